@@ -1,0 +1,274 @@
+"""CPU oracle for one GPU's share of the Mixture-of-Experts layer.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path never does.  It
+shares no code with the HIP library (``routing_schedule_expert_amd``) and never
+imports it.
+
+The arithmetic lives in ``moe_oracle.c`` (plain C, double precision, built with
+gcc); this module only marshals numpy arrays.  Every function names the page
+and section it follows in the C source.
+
+Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
+  schedule, schedule_counting, schedule_rescan  pinned (brute force, closed forms,
+                                                  printed read/counter counts,
+                                                  stable-argsort special case)
+  dispatch                                       pinned (bit copy by definition)
+  expert_ffn_rows, layer_fwd_tokens, combine     pinned (dense FFN special case vs
+                                                  torch fp64, un-permute special case)
+  layer_bwd, bwd_tokens, wgrad_elems             pinned (finite differences, torch
+                                                  autograd, the dw identity)
+  minibatch_floor                                pinned (the printed 2368)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP) into ``oracle/libmoe_oracle.so``."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        p = ctypes.c_void_p
+        i32, i64 = ctypes.c_int, ctypes.c_int64
+        lib.orc_capacity_rows.argtypes = [i32, i32, i32, i32, i32]
+        lib.orc_capacity_rows.restype = i64
+        lib.orc_minibatch_floor.argtypes = [i64] * 5
+        lib.orc_minibatch_floor.restype = i64
+        sched = [i32, i32, i32, i32, i32, i32, p, p, p, p, i64, p, p]
+        lib.orc_schedule.argtypes = sched
+        lib.orc_schedule.restype = i64
+        lib.orc_schedule_rescan.argtypes = sched
+        lib.orc_schedule_rescan.restype = i64
+        lib.orc_schedule_counting.argtypes = [i32] * 7 + [p, p, p, p, i64, p, p]
+        lib.orc_schedule_counting.restype = i64
+        lib.orc_dispatch.argtypes = [i32, i32, p, p, i64, p]
+        lib.orc_dispatch.restype = None
+        lib.orc_expert_ffn_rows.argtypes = [i32, i32, i32, p, p, p, p, p, i64, p, p, p]
+        lib.orc_expert_ffn_rows.restype = None
+        lib.orc_combine_tokens.argtypes = [i32, i32, i32, p, p, p, p, p, i64, p]
+        lib.orc_combine_tokens.restype = None
+        lib.orc_layer_fwd_tokens.argtypes = [i32, i32, i32, i32, i32, p, p, p, p, p, p, i64, p]
+        lib.orc_layer_fwd_tokens.restype = None
+        lib.orc_layer_bwd.argtypes = [i64, i32, i32, i32, i32, i32] + [p] * 10
+        lib.orc_layer_bwd.restype = None
+        lib.orc_bwd_tokens.argtypes = [i32, i32, i32, i32, i32, p, p, p, p, p, p, p, i64, p, p]
+        lib.orc_bwd_tokens.restype = None
+        lib.orc_wgrad_elems.argtypes = [i64, i32, i32, i32, i32, i32, i32] + [p] * 6 + [p, i64, p, p, i64, p]
+        lib.orc_wgrad_elems.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _u16(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bf16 operands are passed as their uint16 bit patterns")
+    return np.ascontiguousarray(a)
+
+
+def capacity_rows(P: int, Np: int, K: int, L: int, pad: int = 256) -> int:
+    """Worst-case dispatched rows: P*Np*K + L*(pad-1)."""
+    return int(_load().orc_capacity_rows(P, Np, K, L, pad))
+
+
+def minibatch_floor(C: int, bm: int, bn: int, H: int, I: int) -> int:
+    """T >= 2*C*bm*bn / min(2I, H), rounded up (Mixture-of-Kittens notes, section 3)."""
+    return int(_load().orc_minibatch_floor(C, bm, bn, H, I))
+
+
+class Schedule:
+    """Result of a schedule: counts [L][P], seg_off [L+1], phi [npad][2],
+    route_row [P][Np][K], npad, and instrumentation stats."""
+
+    def __init__(self, counts, seg_off, phi, route_row, npad, stats):
+        self.counts = counts
+        self.seg_off = seg_off
+        self.phi = phi
+        self.route_row = route_row
+        self.npad = npad
+        self.stats = stats
+
+
+def _schedule_call(fn_name: str, routes: np.ndarray, L: int, base: int, pad: int, NT: int | None):
+    routes = _i32(routes)
+    P, Np, K = routes.shape
+    cap = capacity_rows(P, Np, K, L, pad)
+    counts = np.zeros((L, P), np.int32)
+    seg_off = np.zeros(L + 1, np.int32)
+    phi = np.zeros((max(cap, 1), 2), np.int32)
+    route_row = np.zeros((P, Np, K), np.int32)
+    lib = _load()
+    if fn_name == "counting":
+        stats = np.zeros(2, np.int64)
+        npad = lib.orc_schedule_counting(P, Np, K, L, base, pad, NT, _ptr(routes), _ptr(counts),
+                                         _ptr(seg_off), _ptr(phi), cap, _ptr(route_row), _ptr(stats))
+        st = {"route_reads": int(stats[0]), "counters": int(stats[1])}
+    else:
+        reads = np.zeros(1, np.int64)
+        fn = lib.orc_schedule if fn_name == "plain" else lib.orc_schedule_rescan
+        npad = fn(P, Np, K, L, base, pad, _ptr(routes), _ptr(counts), _ptr(seg_off), _ptr(phi), cap,
+                  _ptr(route_row), _ptr(reads))
+        st = {"route_reads": int(reads[0])}
+    if npad < 0:
+        raise RuntimeError("oracle schedule: capacity exceeded")
+    return Schedule(counts, seg_off, phi[:npad].copy(), route_row, int(npad), st)
+
+
+def schedule(routes: np.ndarray, L: int, base: int = 0, pad: int = 256) -> Schedule:
+    """Plain definition of the pull schedule (position formula, two passes)."""
+    return _schedule_call("plain", routes, L, base, pad, None)
+
+
+def schedule_counting(routes: np.ndarray, L: int, base: int = 0, pad: int = 256, NT: int = 1024) -> Schedule:
+    """The four counting-sort stages with NT logical threads per partition."""
+    return _schedule_call("counting", routes, L, base, pad, NT)
+
+
+def schedule_rescan(routes: np.ndarray, L: int, base: int = 0, pad: int = 256) -> Schedule:
+    """The older per-(expert, peer) rescanning scheduler: lists merged round-robin."""
+    return _schedule_call("rescan", routes, L, base, pad, None)
+
+
+def dispatch(X: np.ndarray, phi: np.ndarray) -> np.ndarray:
+    """Xd[row] = X[phi.part][phi.tok] (bf16 bits), zero rows for padding."""
+    X = _u16(X)
+    P, Np, H = X.shape
+    phi = _i32(phi)
+    npad = phi.shape[0]
+    Xd = np.zeros((npad, H), np.uint16)
+    _load().orc_dispatch(Np, H, _ptr(X), _ptr(phi), npad, _ptr(Xd))
+    return Xd
+
+
+def expert_ffn_rows(seg_off, Xd, W13, W2, rows=None, want=("HU", "A", "Y")):
+    """SwiGLU expert FFN of the listed dispatched rows (default: all rows).
+
+    Returns a dict with the requested double arrays HU [n][2I], A [n][I], Y [n][H]."""
+    Xd, W13, W2 = _u16(Xd), _u16(W13), _u16(W2)
+    seg_off = _i32(seg_off)
+    L, twoI, H = W13.shape
+    I = twoI // 2
+    rows = np.arange(Xd.shape[0], dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    n = rows.shape[0]
+    HU = np.zeros((n, 2 * I)) if "HU" in want else None
+    A = np.zeros((n, I)) if "A" in want else None
+    Y = np.zeros((n, H)) if "Y" in want else None
+    _load().orc_expert_ffn_rows(L, H, I, _ptr(seg_off), _ptr(Xd), _ptr(W13), _ptr(W2), _ptr(rows), n,
+                                _ptr(HU), _ptr(A), _ptr(Y))
+    return {"HU": HU, "A": A, "Y": Y}
+
+
+def combine(route_row, w, Y_rows, yrow_index=None, tokens=None):
+    """out[g] = sum_j w[g][j] * Y[route_row[g][j]] over local slots, ascending j."""
+    route_row = _i32(route_row)
+    P, Np, K = route_row.shape
+    w = np.ascontiguousarray(w, np.float32)
+    Y_rows = np.ascontiguousarray(Y_rows, np.float64)
+    H = Y_rows.shape[1]
+    if yrow_index is None:
+        yrow_index = np.arange(Y_rows.shape[0], dtype=np.int64)
+    yrow_index = np.ascontiguousarray(yrow_index, np.int64)
+    tokens = np.arange(P * Np, dtype=np.int64) if tokens is None else np.ascontiguousarray(tokens, np.int64)
+    out = np.zeros((tokens.shape[0], H))
+    _load().orc_combine_tokens(Np, K, H, _ptr(route_row), _ptr(w), _ptr(Y_rows), _ptr(yrow_index),
+                               _ptr(tokens), tokens.shape[0], _ptr(out))
+    return out
+
+
+def layer_fwd_tokens(routes, w, X, W13, W2, L: int, base: int = 0, tokens=None):
+    """Forward output per token straight from the definition (no schedule)."""
+    routes = _i32(routes)
+    P, Np, K = routes.shape
+    w = np.ascontiguousarray(w, np.float32)
+    X, W13, W2 = _u16(X), _u16(W13), _u16(W2)
+    H = X.shape[-1]
+    I = W13.shape[1] // 2
+    tokens = np.arange(P * Np, dtype=np.int64) if tokens is None else np.ascontiguousarray(tokens, np.int64)
+    out = np.zeros((tokens.shape[0], H))
+    _load().orc_layer_fwd_tokens(K, L, base, H, I, _ptr(routes), _ptr(w), _ptr(X), _ptr(W13), _ptr(W2),
+                                 _ptr(tokens), tokens.shape[0], _ptr(out))
+    return out
+
+
+def layer_bwd(routes, w, X, W13, W2, dOut, L: int, base: int = 0):
+    """Full backward: dict of dX [P][Np][H], dW13 [L][2I][H], dW2 [L][H][I], dw [P][Np][K]."""
+    routes = _i32(routes)
+    P, Np, K = routes.shape
+    w = np.ascontiguousarray(w, np.float32)
+    X, W13, W2, dOut = _u16(X), _u16(W13), _u16(W2), _u16(dOut)
+    H = X.shape[-1]
+    I = W13.shape[1] // 2
+    dX = np.zeros((P, Np, H))
+    dW13 = np.zeros((L, 2 * I, H))
+    dW2 = np.zeros((L, H, I))
+    dw = np.zeros((P, Np, K))
+    _load().orc_layer_bwd(P * Np, K, L, base, H, I, _ptr(routes), _ptr(w), _ptr(X), _ptr(W13), _ptr(W2),
+                          _ptr(dOut), _ptr(dX), _ptr(dW13), _ptr(dW2), _ptr(dw))
+    return {"dX": dX, "dW13": dW13, "dW2": dW2, "dw": dw}
+
+
+def bwd_tokens(routes, w, X, W13, W2, dOut, L: int, base: int, tokens):
+    """dX rows and dw rows of the listed tokens."""
+    routes = _i32(routes)
+    P, Np, K = routes.shape
+    w = np.ascontiguousarray(w, np.float32)
+    X, W13, W2, dOut = _u16(X), _u16(W13), _u16(W2), _u16(dOut)
+    H = X.shape[-1]
+    I = W13.shape[1] // 2
+    tokens = np.ascontiguousarray(tokens, np.int64)
+    dX = np.zeros((tokens.shape[0], H))
+    dw = np.zeros((tokens.shape[0], K))
+    _load().orc_bwd_tokens(K, L, base, H, I, _ptr(routes), _ptr(w), _ptr(X), _ptr(W13), _ptr(W2), _ptr(dOut),
+                           _ptr(tokens), tokens.shape[0], _ptr(dX), _ptr(dw))
+    return dX, dw
+
+
+def wgrad_elems(routes, w, X, W13, W2, dOut, L: int, base: int, expert: int, w13_elems, w2_elems):
+    """Listed elements of dW13[expert] ((n, k) pairs) and dW2[expert] ((m, n) pairs)."""
+    routes = _i32(routes)
+    P, Np, K = routes.shape
+    w = np.ascontiguousarray(w, np.float32)
+    X, W13, W2, dOut = _u16(X), _u16(W13), _u16(W2), _u16(dOut)
+    H = X.shape[-1]
+    I = W13.shape[1] // 2
+    e13 = np.ascontiguousarray(np.asarray(w13_elems, np.int64).reshape(-1, 2))
+    e2 = np.ascontiguousarray(np.asarray(w2_elems, np.int64).reshape(-1, 2))
+    g13 = np.zeros(e13.shape[0])
+    g2 = np.zeros(e2.shape[0])
+    _load().orc_wgrad_elems(P * Np, K, L, base, H, I, expert, _ptr(routes), _ptr(w), _ptr(X), _ptr(W13), _ptr(W2),
+                            _ptr(dOut), _ptr(e13), e13.shape[0], _ptr(g13), _ptr(e2), e2.shape[0], _ptr(g2))
+    return g13, g2
