@@ -1,0 +1,231 @@
+/*
+ * moe.h — C ABI of one GPU's share of a Mixture-of-Experts layer on MI355X
+ * (gfx950): an on-device counting-sort schedule, a row gather, a SwiGLU expert
+ * FFN as a grouped bf16 GEMM, a fixed-order combine, and the backward pass
+ * that reuses the same table.
+ *
+ * Sources:
+ *   [MoK]  "Mixture-of-Kittens: A MoE Megakernel for GB300 NVL72" (reading notes)
+ *   [SOSO] "Scan once, scatter once"
+ *   [BPT]  "Beyond Peak TFLOPs: Why Communication-Compute Overlap Dictates ML
+ *          Productivity Goodput"
+ *
+ * Conventions shared by every call
+ *   - Every pointer is a DEVICE pointer owned by the caller unless the
+ *     argument says "host".  The library allocates no device memory, never
+ *     synchronises the device or the stream, and keeps no state between calls
+ *     (apart from the optional launch trace below).  Calls are asynchronous on
+ *     `stream` (a hipStream_t passed as void*, NULL = the null stream).
+ *   - bf16 tensors are raw bfloat16 (uint16_t storage).  All tensors are dense,
+ *     row-major, in the shapes given; device pointers must be 16-byte aligned.
+ *   - Return value: MOE_OK or a negative MOE_E* code; moe_strerror() names it.
+ *     Arguments are checked on the host before anything is launched; a failed
+ *     check launches nothing and writes nothing.  Device data (route ids, the
+ *     table) is not validated on the host: route ids outside
+ *     [expert_base, expert_base + L) are simply not local (negative "dropped"
+ *     ids included) and are skipped.
+ *   - Results are bitwise reproducible run to run: integer work is exact,
+ *     and every floating-point reduction has a fixed order (no float atomics).
+ *   - Calls that share buffers must be ordered by the caller (same stream or
+ *     events).  Concurrent calls on different buffers are independent.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Error codes. */
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,       /* bad dimension, NULL pointer or misaligned pointer */
+    MOE_ENOSPC = -2,       /* workspace or capacity smaller than required       */
+    MOE_EUNSUPPORTED = -3, /* valid but not supported (e.g. H % 64 != 0)        */
+    MOE_EHIP = -4,         /* a HIP launch or runtime call failed                */
+};
+
+/* Problem description (host struct, read during the call only).
+ *   P            source partitions (the "peers" of [MoK] section 2; here P slices
+ *                of the routing tensor resident in local HBM)
+ *   Np           tokens per partition
+ *   K            top-k slots per token
+ *   E            global experts
+ *   L            local experts: ids [expert_base, expert_base + L)
+ *   expert_base  first local expert id (ep_rank * L for contiguous ownership)
+ *   pad_rows     every expert segment is padded to a multiple of this many rows
+ *                ([SOSO]: 256)
+ *   sched_threads logical scheduler threads per partition ([SOSO]: 1,024).  The
+ *                table does not depend on it (logical threads own contiguous
+ *                route chunks, so the order is the stable one); it is accepted
+ *                for interface fidelity and must be >= 1.
+ *   H, I         hidden size and expert intermediate size (SwiGLU: W13 holds
+ *                gate rows [0, I) and up rows [I, 2I))
+ *   num_batches  moe_schedule only: independent routing tensors per call (>= 1)
+ */
+typedef struct moe_desc {
+    int32_t P, Np, K, E, L, expert_base, pad_rows, sched_threads, H, I, num_batches;
+} moe_desc;
+
+/* One row of the pull table Phi ([MoK] section 2; [BPT] section 2.A): the
+ * partition and token a dispatched row is pulled from; (-1, -1) on padding. */
+typedef struct moe_src {
+    int32_t part;
+    int32_t tok;
+} moe_src;
+
+const char *moe_strerror(int code);
+
+/* Worst-case dispatched rows for `d`: P*Np*K + L*(pad_rows - 1).  Every
+ * row-indexed buffer below (phi, Xd, HU, A, Y, dO_d, dHU, dXd) must hold this
+ * many rows, so that no routing ever needs a host round trip or a dropped
+ * token ([MoK] section 4; [BPT] section 2.B).  Returns -1 for an invalid d. */
+int64_t moe_capacity_rows(const moe_desc *d);
+
+/* Workspace bytes needed by an operation (MOE_OP_*); -1 for an invalid d.  The
+ * workspace is caller-owned scratch: contents on entry are ignored except
+ * where a call says otherwise, and it must not be shared by concurrent calls. */
+enum {
+    MOE_OP_SCHEDULE = 0,
+    MOE_OP_DISPATCH = 1,
+    MOE_OP_EXPERT_FFN = 2,
+    MOE_OP_COMBINE = 3,
+    MOE_OP_LAYER_FWD = 4,
+    MOE_OP_LAYER_BWD = 5,
+};
+int64_t moe_workspace_bytes(const moe_desc *d, int op);
+
+/*
+ * moe_schedule — the counting-sort pull schedule of [MoK] section 2 built on
+ * the device in the four stages of [SOSO] ("The fix is a counting sort"):
+ * count routes per local expert, partition and logical thread; prefix the
+ * counts; pad every expert segment to pad_rows and take its base row; scatter
+ * every route once to Phi[S[l] + p] with
+ *     p = sum_{r'} min(M[l][r'], o) + #{ r' < r : M[l][r'] > o },
+ * o being the route's ordinal among partition r's routes to expert l in flat
+ * (token-major, then slot) order.  Route ids are read twice in total.
+ *
+ * For each batch b in [0, num_batches):
+ *   routes     int32   [nb][P][Np][K]  in: expert id of every slot
+ *   counts     int32   [nb][L][P]      out: M[l][r]
+ *   seg_off    int32   [nb][L+1]       out: S; seg_off[L] = padded rows Npad
+ *   phi        moe_src [nb][cap]       out: rows [0, Npad) written; rows past
+ *                                      Npad are left untouched
+ *   route_row  int32   [nb][P][Np][K]  out: row of each slot, -1 if not local
+ *   ws         >= moe_workspace_bytes(d, MOE_OP_SCHEDULE) bytes
+ * Bit-exact and deterministic.  Npad stays on the device.
+ */
+int moe_schedule(const moe_desc *d, const int32_t *routes, int32_t *counts, int32_t *seg_off,
+                 moe_src *phi, int32_t *route_row, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_dispatch — pull dispatch ([MoK] section 2; [BPT] section 2.A) as a local
+ * gather: Xd[i] = X[phi[i].part][phi[i].tok] bit for bit for i < Npad =
+ * seg_off[L]; padding rows are written as zeros.  Rows >= Npad untouched.
+ *   X        bf16    [P][Np][H]
+ *   phi      moe_src [cap], seg_off int32 [L+1] (from moe_schedule)
+ *   Xd       bf16    [cap][H]
+ * The same call is the backward's reverse-combine gather (dOut -> dO_d).
+ */
+int moe_dispatch(const moe_desc *d, const uint16_t *X, const moe_src *phi, const int32_t *seg_off,
+                 uint16_t *Xd, void *stream);
+
+/*
+ * moe_expert_ffn — SwiGLU expert FFN as grouped GEMMs over the expert
+ * segments ([MoK] sections 3 and 5): for every row i < Npad of segment l
+ *     HU[i] = Xd[i] W13[l]^T            (fp32 accumulate; gate | up)
+ *     A[i]  = silu(HU[i][:I]) * HU[i][I:]   (rounded to bf16)
+ *     Y[i]  = A[i] W2[l]^T              (fp32 accumulate, rounded to bf16)
+ *   Xd   bf16 [cap][H]     W13 bf16 [L][2I][H]     W2 bf16 [L][H][I]
+ *   seg_off int32 [L+1]
+ *   HU   bf16 [cap][2I] or NULL (saved pre-activations for the backward)
+ *   A    bf16 [cap][I]     Y bf16 [cap][H]
+ *   chunk_rows  0: one pass over all rows.  > 0: rows are processed in chunks
+ *               of chunk_rows dispatched rows (a multiple of 256), the down
+ *               projection of chunk c overlapping the gate/up projection of
+ *               chunk c+1 inside one persistent launch (the minibatch T of
+ *               [MoK] section 3).
+ *   ws   >= moe_workspace_bytes(d, MOE_OP_EXPERT_FFN)
+ * Requires H % 256 == 0 and I % 128 == 0 (else MOE_EUNSUPPORTED).
+ */
+int moe_expert_ffn(const moe_desc *d, const uint16_t *Xd, const uint16_t *W13, const uint16_t *W2,
+                   const int32_t *seg_off, uint16_t *HU, uint16_t *A, uint16_t *Y, int32_t chunk_rows,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_combine — push combine ([MoK] section 2) as a local fixed-order sum:
+ *     out[r][t] = sum_{j = 0..K-1, route_row[r][t][j] >= 0} w[r][t][j] * Y[route_row[r][t][j]]
+ * accumulated in fp32 in ascending j and rounded once to bf16; tokens with no
+ * local slot get zeros.  w may be NULL (every weight 1): that is the
+ * backward's reverse-dispatch sum (dXd -> dX).
+ *   Y bf16 [cap][H]   route_row int32 [P][Np][K]   w float [P][Np][K] or NULL
+ *   out bf16 [P][Np][H]
+ */
+int moe_combine(const moe_desc *d, const uint16_t *Y, const int32_t *route_row, const float *w,
+                uint16_t *out, void *stream);
+
+/* Flags of moe_layer_fwd. */
+enum {
+    MOE_PERSISTENT = 1, /* run every stage inside one persistent cooperative launch */
+};
+
+/*
+ * moe_layer_fwd — the whole forward share: schedule, dispatch, expert FFN,
+ * combine.  Outputs as in the four calls above (HU may be NULL).  With
+ * MOE_PERSISTENT set, every stage runs inside one persistent launch whose
+ * workgroups pass device-side barriers between stages ([MoK] section 5,
+ * megakernel fusion); otherwise one launch per stage.  Both give bitwise the
+ * same results.  chunk_rows as in moe_expert_ffn.
+ *   ws >= moe_workspace_bytes(d, MOE_OP_LAYER_FWD)
+ * Uses d->num_batches == 1.
+ */
+int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, const uint16_t *X,
+                  const uint16_t *W13, const uint16_t *W2, int32_t *counts, int32_t *seg_off,
+                  moe_src *phi, int32_t *route_row, uint16_t *Xd, uint16_t *HU, uint16_t *A,
+                  uint16_t *Y, uint16_t *out, int32_t flags, int32_t chunk_rows, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/*
+ * moe_layer_bwd — backward of the forward share, reusing the forward table
+ * ([MoK] section 2: pull reverse-combine, push reverse-dispatch; section 5:
+ * router-weight gradient from the SwiGLU activations and the down-projection
+ * dgrad; [BPT] section 2.C: weight gradients after the data gradients, each
+ * accumulated over the token dimension in one fixed-order pass).
+ *   dOut  bf16 [P][Np][H]           in: gradient of the layer output
+ *   routes, w, phi, route_row, seg_off   from the forward
+ *   Xd bf16 [cap][H], HU bf16 [cap][2I], A bf16 [cap][I]   saved by the forward
+ *   W13, W2                          the forward weights
+ *   dX    bf16  [P][Np][H]   out: sum over local slots of the row gradients
+ *   dW13  float [L][2I][H]   out
+ *   dW2   float [L][H][I]    out
+ *   dw    float [P][Np][K]   out: router-weight gradient, 0 on non-local slots
+ *   ws >= moe_workspace_bytes(d, MOE_OP_LAYER_BWD)
+ * The workspace holds dO_d, dHU, dXd (bf16, cap rows each) and per-row partial
+ * sums.  Every reduction has a fixed order.
+ */
+int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes, const float *w,
+                  const moe_src *phi, const int32_t *route_row, const int32_t *seg_off,
+                  const uint16_t *Xd, const uint16_t *HU, const uint16_t *A, const uint16_t *W13,
+                  const uint16_t *W2, uint16_t *dX, float *dW13, float *dW2, float *dw, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/*
+ * Launch trace (optional, host side).  moe_trace_enable(n) records, for the
+ * next n kernel launches made by this library on any stream, a start and stop
+ * event on the launch's own stream; moe_trace_read copies the finished
+ * records (after the caller has synchronised) into host arrays `kernel`
+ * (a short name per record, each up to 31 characters plus NUL, 32 bytes per
+ * record) and `ms` (elapsed milliseconds), returning the count.
+ * moe_trace_enable(0) stops recording and frees the events.  Not thread safe.
+ */
+int moe_trace_enable(int max_records);
+int moe_trace_read(char *kernel, float *ms, int max_records);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

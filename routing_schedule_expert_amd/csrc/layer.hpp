@@ -1,0 +1,265 @@
+// Layer-level device code: the expert FFN phases, the chunked persistent FFN,
+// the persistent whole-forward launch, and the backward phases.
+//
+//  * Expert FFN ("Mixture-of-Kittens: A MoE Megakernel for GB300 NVL72",
+//    sections 3 and 5): gate/up projection with SwiGLU fused into its
+//    epilogue, then the down projection, over 256-row tiles of the expert
+//    segments.  Npad is read on the device; every persistent workgroup loops
+//    over the tiles of a phase.
+//  * Chunked FFN (section 3, the minibatch T): rows are processed in chunks of
+//    T dispatched rows; phase p runs the gate/up tiles of chunk p together
+//    with the down tiles of chunk p-1, separated by device-wide barriers.
+//  * Persistent forward (section 5, megakernel fusion): schedule, gather, FFN
+//    and combine in one cooperative launch with device-side barriers between
+//    stages, so no host launch sits between them.
+//  * Backward (section 2: pull reverse-combine / push reverse-dispatch; section
+//    5: router-weight gradient from the SwiGLU activations and the down
+//    dgrad; "Beyond Peak TFLOPs" section 2.C: weight gradients after the data
+//    gradients, accumulated over tokens in one fixed-order pass).
+#pragma once
+
+#include "common.hpp"
+#include "gemm.hpp"
+#include "rowops.hpp"
+#include "schedule.hpp"
+
+namespace moe {
+
+struct FfnArgs {
+    const uint16_t *Xd, *W13, *W2;
+    const int32_t *seg_off;
+    uint16_t *HU, *A, *Y;
+    int L, H, I;
+    int32_t chunk_rows;
+    uint32_t *bar;
+};
+
+__device__ __forceinline__ void ffn_gateup_tile(const FfnArgs &a, int mt, int nt, char *lds) {
+    const int H = a.H, I = a.I;
+    const int m0 = mt * kBM;
+    const int l = expert_of(a.seg_off, a.L, m0);
+    const uint16_t *xa = a.Xd + (int64_t)m0 * H;
+    const uint16_t *w = a.W13 + (int64_t)l * 2 * I * H;
+    KOp ak{xa, xa + 128ll * H, H};
+    KOp bk{w + (int64_t)nt * 128 * H, w + ((int64_t)I + nt * 128) * H, H};
+    f32x16 acc[4][4];
+    gemm_mainloop<true, true>(ak, MNOp{}, bk, MNOp{}, H / kBK, true, lds, acc);
+    uint16_t *hu = a.HU ? a.HU + (int64_t)m0 * 2 * I : nullptr;
+    epilogue_swiglu(acc, lds, a.A + (int64_t)m0 * I + nt * 128, I, hu ? hu + nt * 128 : nullptr,
+                    hu ? hu + I + nt * 128 : nullptr, 2ll * I);
+}
+
+__device__ __forceinline__ void ffn_down_tile(const FfnArgs &a, int mt, int nt, char *lds) {
+    const int H = a.H, I = a.I;
+    const int m0 = mt * kBM;
+    const int l = expert_of(a.seg_off, a.L, m0);
+    const uint16_t *aa = a.A + (int64_t)m0 * I;
+    const uint16_t *w = a.W2 + (int64_t)l * H * I + (int64_t)nt * 256 * I;
+    KOp ak{aa, aa + 128ll * I, I};
+    KOp bk{w, w + 128ll * I, I};
+    f32x16 acc[4][4];
+    gemm_mainloop<true, true>(ak, MNOp{}, bk, MNOp{}, I / kBK, false, lds, acc);
+    epilogue_store_bf16(acc, lds, a.Y + (int64_t)m0 * H + nt * 256, H, 256);
+}
+
+// One persistent pass over the tiles of rows [r0, r1) (multiples of 256).
+__device__ __forceinline__ void ffn_gateup_phase(const FfnArgs &a, int r0, int r1, char *lds) {
+    const int mtiles = (r1 - r0) / kBM, ntiles = a.I / 128;
+    const int64_t total = (int64_t)mtiles * ntiles;
+    for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
+        const int64_t lid = logical_tile(it);
+        if (lid >= total) continue;
+        int m, n;
+        grouped_mn(lid, mtiles, ntiles, 4, m, n);
+        ffn_gateup_tile(a, r0 / kBM + m, n, lds);
+    }
+}
+
+__device__ __forceinline__ void ffn_down_phase(const FfnArgs &a, int r0, int r1, char *lds) {
+    const int mtiles = (r1 - r0) / kBM, ntiles = a.H / 256;
+    const int64_t total = (int64_t)mtiles * ntiles;
+    for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
+        const int64_t lid = logical_tile(it);
+        if (lid >= total) continue;
+        int m, n;
+        grouped_mn(lid, mtiles, ntiles, 4, m, n);
+        ffn_down_tile(a, r0 / kBM + m, n, lds);
+    }
+}
+
+// Chunked pipeline: phase p = gate/up of chunk p and down of chunk p-1.
+__device__ __forceinline__ void ffn_chunked_body(const FfnArgs &a, char *lds) {
+    const int npad = a.seg_off[a.L];
+    const int T = a.chunk_rows;
+    const int nchunks = (npad + T - 1) / T;
+    for (int p = 0; p <= nchunks; ++p) {
+        const int gu0 = min(p * T, npad), gu1 = min((p + 1) * T, npad);
+        const int dn0 = p > 0 ? min((p - 1) * T, npad) : 0, dn1 = p > 0 ? gu0 : 0;
+        const int64_t ngu = (int64_t)((gu1 - gu0) / kBM) * (a.I / 128);
+        const int64_t ndn = (int64_t)((dn1 - dn0) / kBM) * (a.H / 256);
+        const int64_t total = ngu + ndn;
+        for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
+            const int64_t lid = logical_tile(it);
+            if (lid >= total) continue;
+            int m, n;
+            if (lid < ngu) {
+                grouped_mn(lid, (gu1 - gu0) / kBM, a.I / 128, 4, m, n);
+                ffn_gateup_tile(a, gu0 / kBM + m, n, lds);
+            } else {
+                grouped_mn(lid - ngu, (dn1 - dn0) / kBM, a.H / 256, 4, m, n);
+                ffn_down_tile(a, dn0 / kBM + m, n, lds);
+            }
+        }
+        grid_barrier(a.bar, gridDim.x);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent forward.
+// ---------------------------------------------------------------------------
+
+struct LayerFwdArgs {
+    SchedArgs sched;
+    FfnArgs ffn;
+    const uint16_t *X;
+    const float *w;
+    uint16_t *out;
+    int Np, K;
+    int64_t ntok, cap;
+};
+
+__device__ __forceinline__ void layer_fwd_persistent_body(const LayerFwdArgs &a, char *lds) {
+    const SchedArgs &s = a.sched;
+    const int nitems = s.P * s.wg_per_part;
+    int32_t *smem = reinterpret_cast<int32_t *>(lds);
+    for (int x = blockIdx.x; x < nitems; x += gridDim.x) sched_count_body(s, smem, x);
+    grid_barrier(a.ffn.bar, gridDim.x);
+    for (int x = blockIdx.x; x < nitems; x += gridDim.x) sched_scatter_body(s, smem, x);
+    grid_barrier(a.ffn.bar, gridDim.x);
+    const int waves = kGemmThreads / kWave;
+    gather_rows_body(a.X, s.phi, s.seg_off + s.L, const_cast<uint16_t *>(a.ffn.Xd), a.Np, a.ffn.H, 0, a.cap,
+                     blockIdx.x * waves + threadIdx.x / kWave, gridDim.x * waves);
+    grid_barrier(a.ffn.bar, gridDim.x);
+    if (a.ffn.chunk_rows > 0) {
+        ffn_chunked_body(a.ffn, lds);
+    } else {
+        const int npad = a.ffn.seg_off[a.ffn.L];
+        ffn_gateup_phase(a.ffn, 0, npad, lds);
+        grid_barrier(a.ffn.bar, gridDim.x);
+        ffn_down_phase(a.ffn, 0, npad, lds);
+        grid_barrier(a.ffn.bar, gridDim.x);
+    }
+    combine_body(a.ffn.Y, s.route_row, a.w, a.out, a.K, a.ffn.H, 0, a.ntok,
+                 blockIdx.x * waves + threadIdx.x / kWave, gridDim.x * waves);
+}
+
+// ---------------------------------------------------------------------------
+// Backward.
+// ---------------------------------------------------------------------------
+
+struct BwdArgs {
+    uint16_t *dOd, *dXd, *dHU;
+    float *wrow, *part;
+    const uint16_t *Xd, *HU, *A, *W13, *W2;
+    const int32_t *seg_off;
+    float *dW13, *dW2;
+    int L, H, I, nparts;
+};
+
+// B2: dA' = dO_d W2[l] (N-contiguous weight), SwiGLU backward in the epilogue.
+__device__ __forceinline__ void bwd_down_phase(const BwdArgs &a, char *lds) {
+    const int H = a.H, I = a.I;
+    const int npad = a.seg_off[a.L];
+    const int mtiles = npad / kBM, ntiles = (I + 255) / 256;
+    const int64_t total = (int64_t)mtiles * ntiles;
+    for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
+        const int64_t lid = logical_tile(it);
+        if (lid >= total) continue;
+        int mt, nt;
+        grouped_mn(lid, mtiles, ntiles, 4, mt, nt);
+        const int m0 = mt * kBM;
+        const int l = expert_of(a.seg_off, a.L, m0);
+        const uint16_t *g = a.dOd + (int64_t)m0 * H;
+        KOp ak{g, g + 128ll * H, H};
+        MNOp bmn{a.W2 + (int64_t)l * H * I + nt * 256, I, I - nt * 256, nullptr};
+        f32x16 acc[4][4];
+        gemm_mainloop<true, false>(ak, MNOp{}, KOp{}, bmn, H / kBK, false, lds, acc);
+        epilogue_swiglu_bwd(acc, a.A + (int64_t)m0 * I, a.HU + (int64_t)m0 * 2 * I, a.wrow + m0,
+                            a.dHU + (int64_t)m0 * 2 * I, a.part + (int64_t)m0 * a.nparts, a.nparts, I, nt * 256, nt);
+    }
+}
+
+// B3: dXd = dHU W13[l] (N-contiguous weight).
+__device__ __forceinline__ void bwd_gateup_phase(const BwdArgs &a, char *lds) {
+    const int H = a.H, I = a.I;
+    const int npad = a.seg_off[a.L];
+    const int mtiles = npad / kBM, ntiles = H / 256;
+    const int64_t total = (int64_t)mtiles * ntiles;
+    for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
+        const int64_t lid = logical_tile(it);
+        if (lid >= total) continue;
+        int mt, nt;
+        grouped_mn(lid, mtiles, ntiles, 4, mt, nt);
+        const int m0 = mt * kBM;
+        const int l = expert_of(a.seg_off, a.L, m0);
+        const uint16_t *g = a.dHU + (int64_t)m0 * 2 * I;
+        KOp ak{g, g + 128ll * 2 * I, 2ll * I};
+        MNOp bmn{a.W13 + (int64_t)l * 2 * I * H + nt * 256, H, H - nt * 256, nullptr};
+        f32x16 acc[4][4];
+        gemm_mainloop<true, false>(ak, MNOp{}, KOp{}, bmn, 2 * I / kBK, false, lds, acc);
+        epilogue_store_bf16(acc, lds, a.dXd + (int64_t)m0 * H + nt * 256, H, 256);
+    }
+}
+
+// B5: per expert, dW2[l] = sum_rows (w dO_d)^T a and dW13[l] = sum_rows dHU^T Xd,
+// reduced over the segment's rows in ascending order inside one workgroup per
+// output tile.  Experts are taken longest segment first.
+__device__ __forceinline__ void wgrad_phase(const BwdArgs &a, char *lds) {
+    const int H = a.H, I = a.I, L = a.L;
+    __shared__ int s_order[256];
+    __syncthreads();
+    if (L <= 256) {
+        for (int l = threadIdx.x; l < L; l += blockDim.x) {
+            const int len = a.seg_off[l + 1] - a.seg_off[l];
+            int rank = 0;
+            for (int q = 0; q < L; ++q) {
+                const int lq = a.seg_off[q + 1] - a.seg_off[q];
+                rank += (lq > len || (lq == len && q < l)) ? 1 : 0;
+            }
+            s_order[rank] = l;
+        }
+    }
+    __syncthreads();
+    const int mt2 = H / 256, nt2 = (I + 255) / 256;      // dW2 [H][I]
+    const int mt13 = 2 * I / 256, nt13 = H / 256;         // dW13 [2I][H]
+    const int per = mt2 * nt2 + mt13 * nt13;
+    const int64_t total = (int64_t)L * per;
+    for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
+        const int64_t lid = logical_tile(it);
+        if (lid >= total) continue;
+        const int pos = (int)(lid / per), in = (int)(lid % per);
+        const int l = L <= 256 ? s_order[pos] : pos;
+        const int S = a.seg_off[l];
+        const int kext = a.seg_off[l + 1] - S;  // padded: padding rows are zero in every operand
+        f32x16 acc[4][4];
+        if (in < mt2 * nt2) {
+            int mt, nt;
+            grouped_mn(in, mt2, nt2, 4, mt, nt);
+            MNOp amn{a.dOd + (int64_t)S * H + mt * 256, H, H - mt * 256, a.wrow + S};
+            MNOp bmn{a.A + (int64_t)S * I + nt * 256, I, I - nt * 256, nullptr};
+            gemm_mainloop<false, false>(KOp{}, amn, KOp{}, bmn, kext / kBK, false, lds, acc);
+            epilogue_store_f32(acc, a.dW2 + (int64_t)l * H * I + (int64_t)mt * 256 * I + nt * 256, I, H - mt * 256,
+                               I - nt * 256);
+        } else {
+            int mt, nt;
+            grouped_mn(in - mt2 * nt2, mt13, nt13, 4, mt, nt);
+            MNOp amn{a.dHU + (int64_t)S * 2 * I + mt * 256, 2ll * I, 2 * I - mt * 256, nullptr};
+            MNOp bmn{a.Xd + (int64_t)S * H + nt * 256, H, H - nt * 256, nullptr};
+            gemm_mainloop<false, false>(KOp{}, amn, KOp{}, bmn, kext / kBK, false, lds, acc);
+            epilogue_store_f32(acc, a.dW13 + (int64_t)l * 2 * I * H + (int64_t)mt * 256 * H + nt * 256, H,
+                               2 * I - mt * 256, H - nt * 256);
+        }
+    }
+}
+
+}  // namespace moe

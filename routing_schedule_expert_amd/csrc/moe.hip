@@ -1,0 +1,583 @@
+// C-ABI entry points and kernels of the MoE layer share (gfx950).
+// The operations, their arguments and error behaviour are documented in
+// include/moe.h; the device code lives in schedule.hpp, rowops.hpp, gemm.hpp
+// and layer.hpp.
+#include <hip/hip_runtime.h>
+
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "common.hpp"
+#include "gemm.hpp"
+#include "layer.hpp"
+#include "rowops.hpp"
+#include "schedule.hpp"
+
+using namespace moe;
+
+// ---------------------------------------------------------------------------
+// Kernels.
+// ---------------------------------------------------------------------------
+
+__global__ void k_zero_u32(uint32_t *p, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void k_sched_count(SchedArgs a) {
+    extern __shared__ int32_t sched_smem[];
+    sched_count_body(a, sched_smem, blockIdx.x);
+}
+
+__global__ __launch_bounds__(256) void k_sched_scatter(SchedArgs a) {
+    extern __shared__ int32_t sched_smem[];
+    sched_scatter_body(a, sched_smem, blockIdx.x);
+}
+
+__global__ __launch_bounds__(256) void k_gather(const uint16_t *src, const moe_src *phi, const int32_t *npad_ptr,
+                                                uint16_t *dst, int Np, int H, int64_t cap) {
+    const int waves = blockDim.x / kWave;
+    gather_rows_body(src, phi, npad_ptr, dst, Np, H, 0, cap, blockIdx.x * waves + threadIdx.x / kWave,
+                     gridDim.x * waves);
+}
+
+__global__ __launch_bounds__(256) void k_combine(const uint16_t *Y, const int32_t *route_row, const float *w,
+                                                 uint16_t *out, int K, int H, int64_t ntok) {
+    const int waves = blockDim.x / kWave;
+    combine_body(Y, route_row, w, out, K, H, 0, ntok, blockIdx.x * waves + threadIdx.x / kWave, gridDim.x * waves);
+}
+
+__global__ __launch_bounds__(256) void k_row_weight(const moe_src *phi, const int32_t *npad_ptr,
+                                                    const int32_t *route_row, const float *w, float *wrow, int Np,
+                                                    int K, int64_t cap) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < cap; i += (int64_t)gridDim.x * blockDim.x)
+        row_weight_body(phi, npad_ptr, route_row, w, wrow, Np, K, i);
+}
+
+__global__ __launch_bounds__(256) void k_dw_finalize(const int32_t *route_row, const float *part, int nparts,
+                                                     float *dw, int64_t nslots) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nslots;
+         i += (int64_t)gridDim.x * blockDim.x)
+        dw_finalize_body(route_row, part, nparts, dw, i);
+}
+
+__global__ __launch_bounds__(256) void k_ffn_gateup(FfnArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+    ffn_gateup_phase(a, 0, a.seg_off[a.L], lds);
+}
+
+__global__ __launch_bounds__(256) void k_ffn_down(FfnArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+    ffn_down_phase(a, 0, a.seg_off[a.L], lds);
+}
+
+__global__ __launch_bounds__(256) void k_ffn_chunked(FfnArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+    ffn_chunked_body(a, lds);
+}
+
+__global__ __launch_bounds__(256) void k_layer_fwd_persistent(LayerFwdArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+    layer_fwd_persistent_body(a, lds);
+}
+
+__global__ __launch_bounds__(256) void k_bwd_down(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+    bwd_down_phase(a, lds);
+}
+
+__global__ __launch_bounds__(256) void k_bwd_gateup(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+    bwd_gateup_phase(a, lds);
+}
+
+__global__ __launch_bounds__(256) void k_wgrad(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+    wgrad_phase(a, lds);
+}
+
+// ---------------------------------------------------------------------------
+// Launch trace.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct TraceRec {
+    char name[32];
+    hipEvent_t start, stop;
+};
+
+std::mutex g_trace_mu;
+std::vector<TraceRec> g_trace;
+int g_trace_cap = 0;
+int g_trace_used = 0;
+
+struct TraceScope {
+    TraceRec *rec = nullptr;
+    hipStream_t stream;
+    TraceScope(const char *name, hipStream_t s) : stream(s) {
+        if (g_trace_used < g_trace_cap) {
+            rec = &g_trace[g_trace_used++];
+            strncpy(rec->name, name, 31);
+            rec->name[31] = 0;
+            (void)hipEventRecord(rec->start, s);
+        }
+    }
+    ~TraceScope() {
+        if (rec) (void)hipEventRecord(rec->stop, stream);
+    }
+};
+
+// Per-device compute-unit count (the persistent grids are sized to it).
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+// Persistent GEMM grid: one workgroup per CU, rounded down to a multiple of 8
+// (one per XCD) so the XCD-aware tile order stays exact.
+int gemm_grid() {
+    int g = device_cus();
+    g -= g % 8;
+    return g > 0 ? g : 8;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_desc(const moe_desc *d, bool need_ffn) {
+    if (!d) return MOE_EINVAL;
+    if (d->P < 1 || d->Np < 1 || d->K < 1 || d->E < 1 || d->L < 1 || d->pad_rows < 1 || d->sched_threads < 1)
+        return MOE_EINVAL;
+    if (d->expert_base < 0 || (int64_t)d->expert_base + d->L > d->E) return MOE_EINVAL;
+    if (d->num_batches < 1) return MOE_EINVAL;
+    const int64_t R = (int64_t)d->Np * d->K;
+    const int64_t cap = (int64_t)d->P * R + (int64_t)d->L * (d->pad_rows - 1);
+    if (R >= (1ll << 31) || cap >= (1ll << 31) - 256) return MOE_EUNSUPPORTED;
+    if (d->L > 4096 || d->P > 4096 || (int64_t)d->L * d->P > 16384) return MOE_EUNSUPPORTED;
+    if (need_ffn) {
+        if (d->H < 1 || d->I < 1) return MOE_EINVAL;
+        if (d->H % 256 || d->I % 128 || d->pad_rows % 256) return MOE_EUNSUPPORTED;
+    }
+    return MOE_OK;
+}
+
+int64_t cap_rows(const moe_desc *d) {
+    return (int64_t)d->P * d->Np * d->K + (int64_t)d->L * (d->pad_rows - 1);
+}
+
+int sched_chunks(const moe_desc *d) { return (int)(((int64_t)d->Np * d->K + kSchedChunk - 1) / kSchedChunk); }
+int sched_wg_per_part(const moe_desc *d) { return (sched_chunks(d) + kSchedWaves - 1) / kSchedWaves; }
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+int64_t sched_ws_bytes(const moe_desc *d) {
+    return align256(4ll * d->num_batches) + 4ll * d->num_batches * d->P * sched_chunks(d) * d->L;
+}
+
+int bwd_nparts(const moe_desc *d) { return 2 * ((d->I + 255) / 256); }
+
+int64_t bwd_ws_bytes(const moe_desc *d) {
+    const int64_t cap = cap_rows(d);
+    return align256(cap * d->H * 2) * 2 + align256(cap * 2ll * d->I * 2) + align256(cap * 4) +
+           align256(cap * 4ll * bwd_nparts(d));
+}
+
+constexpr int64_t kBarrierBytes = 256;
+
+int launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+int launch_schedule(const moe_desc *d, const int32_t *routes, int32_t *counts, int32_t *seg_off, moe_src *phi,
+                    int32_t *route_row, char *ws, hipStream_t s) {
+    SchedArgs a;
+    a.routes = routes;
+    a.counts = counts;
+    a.seg_off = seg_off;
+    a.phi = phi;
+    a.route_row = route_row;
+    a.arrive = reinterpret_cast<uint32_t *>(ws);
+    a.wcnt = reinterpret_cast<int32_t *>(ws + align256(4ll * d->num_batches));
+    a.P = d->P;
+    a.R = d->Np * d->K;
+    a.K = d->K;
+    a.L = d->L;
+    a.base = d->expert_base;
+    a.pad = d->pad_rows;
+    a.nb = d->num_batches;
+    a.W = sched_chunks(d);
+    a.wg_per_part = sched_wg_per_part(d);
+    a.nbits = 32 - __builtin_clz((unsigned)d->L | 1u);
+    a.cap = cap_rows(d);
+    const int wg_per_batch = a.P * a.wg_per_part;
+    const int grid = a.nb >= 8 ? 8 * ((a.nb + 7) / 8) * wg_per_batch : a.nb * wg_per_batch;
+    const size_t lds_count = 4 * (size_t)std::max(kSchedWaves * (a.L + 1), a.P * a.L + a.L + 256);
+    const size_t lds_scatter = 4 * (size_t)(a.L * a.P + a.L + 1 + kSchedWaves * a.L);
+    {
+        TraceScope tr("sched_zero", s);
+        hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(256), 0, s, a.arrive, (int64_t)a.nb);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    {
+        TraceScope tr("sched_count", s);
+        hipLaunchKernelGGL(k_sched_count, dim3(grid), dim3(256), lds_count, s, a);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    {
+        TraceScope tr("sched_scatter", s);
+        hipLaunchKernelGGL(k_sched_scatter, dim3(grid), dim3(256), lds_scatter, s, a);
+    }
+    return launch_status();
+}
+
+int launch_gather(const moe_desc *d, const uint16_t *src, const moe_src *phi, const int32_t *seg_off, uint16_t *dst,
+                  hipStream_t s, const char *name) {
+    const int64_t cap = cap_rows(d);
+    const int grid = (int)std::min<int64_t>((cap + 3) / 4, 16ll * device_cus());
+    TraceScope tr(name, s);
+    hipLaunchKernelGGL(k_gather, dim3(grid), dim3(256), 0, s, src, phi, seg_off + d->L, dst, d->Np, d->H, cap);
+    return launch_status();
+}
+
+int launch_combine(const moe_desc *d, const uint16_t *Y, const int32_t *route_row, const float *w, uint16_t *out,
+                   hipStream_t s, const char *name) {
+    const int64_t ntok = (int64_t)d->P * d->Np;
+    const int grid = (int)std::min<int64_t>((ntok + 3) / 4, 16ll * device_cus());
+    TraceScope tr(name, s);
+    hipLaunchKernelGGL(k_combine, dim3(grid), dim3(256), 0, s, Y, route_row, w, out, d->K, d->H, ntok);
+    return launch_status();
+}
+
+FfnArgs make_ffn_args(const moe_desc *d, const uint16_t *Xd, const uint16_t *W13, const uint16_t *W2,
+                      const int32_t *seg_off, uint16_t *HU, uint16_t *A, uint16_t *Y, int32_t chunk_rows,
+                      uint32_t *bar) {
+    FfnArgs a;
+    a.Xd = Xd;
+    a.W13 = W13;
+    a.W2 = W2;
+    a.seg_off = seg_off;
+    a.HU = HU;
+    a.A = A;
+    a.Y = Y;
+    a.L = d->L;
+    a.H = d->H;
+    a.I = d->I;
+    a.chunk_rows = chunk_rows;
+    a.bar = bar;
+    return a;
+}
+
+int launch_cooperative(const void *fn, int grid, void **args, hipStream_t s) {
+    hipError_t e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kGemmThreads), args, 0, s);
+    return e == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+int launch_ffn(const moe_desc *d, const FfnArgs &a, hipStream_t s) {
+    const int grid = gemm_grid();
+    if (a.chunk_rows <= 0) {
+        {
+            TraceScope tr("ffn_gateup", s);
+            hipLaunchKernelGGL(k_ffn_gateup, dim3(grid), dim3(kGemmThreads), 0, s, a);
+        }
+        if (launch_status() != MOE_OK) return MOE_EHIP;
+        TraceScope tr("ffn_down", s);
+        hipLaunchKernelGGL(k_ffn_down, dim3(grid), dim3(kGemmThreads), 0, s, a);
+        return launch_status();
+    }
+    {
+        TraceScope tr("ffn_barrier_zero", s);
+        hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, a.bar, (int64_t)(kBarrierBytes / 4));
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    FfnArgs copy = a;
+    void *args[] = {&copy};
+    TraceScope tr("ffn_chunked", s);
+    return launch_cooperative(reinterpret_cast<const void *>(k_ffn_chunked), grid, args, s);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI.
+// ---------------------------------------------------------------------------
+
+extern "C" {
+
+const char *moe_strerror(int code) {
+    switch (code) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument (dimension, NULL or misaligned pointer)";
+        case MOE_ENOSPC: return "workspace or capacity too small";
+        case MOE_EUNSUPPORTED: return "unsupported shape";
+        case MOE_EHIP: return "HIP launch or runtime error";
+        default: return "unknown error";
+    }
+}
+
+int64_t moe_capacity_rows(const moe_desc *d) {
+    if (check_desc(d, false) != MOE_OK) return -1;
+    return cap_rows(d);
+}
+
+int64_t moe_workspace_bytes(const moe_desc *d, int op) {
+    const bool ffn = op == MOE_OP_EXPERT_FFN || op == MOE_OP_LAYER_FWD || op == MOE_OP_LAYER_BWD ||
+                     op == MOE_OP_DISPATCH || op == MOE_OP_COMBINE;
+    if (check_desc(d, ffn) != MOE_OK) return -1;
+    switch (op) {
+        case MOE_OP_SCHEDULE: return sched_ws_bytes(d);
+        case MOE_OP_DISPATCH:
+        case MOE_OP_COMBINE: return 0;
+        case MOE_OP_EXPERT_FFN: return kBarrierBytes;
+        case MOE_OP_LAYER_FWD: {
+            moe_desc one = *d;
+            one.num_batches = 1;
+            return kBarrierBytes + sched_ws_bytes(&one);
+        }
+        case MOE_OP_LAYER_BWD: return bwd_ws_bytes(d);
+        default: return -1;
+    }
+}
+
+int moe_schedule(const moe_desc *d, const int32_t *routes, int32_t *counts, int32_t *seg_off, moe_src *phi,
+                 int32_t *route_row, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_desc(d, false);
+    if (rc != MOE_OK) return rc;
+    if (!routes || !counts || !seg_off || !phi || !route_row || !ws) return MOE_EINVAL;
+    if (!aligned16(routes) || !aligned16(counts) || !aligned16(seg_off) || !aligned16(phi) ||
+        !aligned16(route_row) || !aligned16(ws))
+        return MOE_EINVAL;
+    if ((int64_t)ws_bytes < sched_ws_bytes(d)) return MOE_ENOSPC;
+    return launch_schedule(d, routes, counts, seg_off, phi, route_row, static_cast<char *>(ws),
+                           static_cast<hipStream_t>(stream));
+}
+
+int moe_dispatch(const moe_desc *d, const uint16_t *X, const moe_src *phi, const int32_t *seg_off, uint16_t *Xd,
+                 void *stream) {
+    if (!d) return MOE_EINVAL;
+    int rc = check_desc(d, false);
+    if (rc != MOE_OK) return rc;
+    if (d->H < 8 || d->H % 8) return d->H < 1 ? MOE_EINVAL : MOE_EUNSUPPORTED;
+    if (!X || !phi || !seg_off || !Xd) return MOE_EINVAL;
+    if (!aligned16(X) || !aligned16(phi) || !aligned16(Xd)) return MOE_EINVAL;
+    return launch_gather(d, X, phi, seg_off, Xd, static_cast<hipStream_t>(stream), "dispatch");
+}
+
+int moe_combine(const moe_desc *d, const uint16_t *Y, const int32_t *route_row, const float *w, uint16_t *out,
+                void *stream) {
+    if (!d) return MOE_EINVAL;
+    int rc = check_desc(d, false);
+    if (rc != MOE_OK) return rc;
+    if (d->H < 8 || d->H % 8) return d->H < 1 ? MOE_EINVAL : MOE_EUNSUPPORTED;
+    if (!Y || !route_row || !out) return MOE_EINVAL;
+    if (!aligned16(Y) || !aligned16(out)) return MOE_EINVAL;
+    return launch_combine(d, Y, route_row, w, out, static_cast<hipStream_t>(stream), w ? "combine" : "combine_unweighted");
+}
+
+int moe_expert_ffn(const moe_desc *d, const uint16_t *Xd, const uint16_t *W13, const uint16_t *W2,
+                   const int32_t *seg_off, uint16_t *HU, uint16_t *A, uint16_t *Y, int32_t chunk_rows, void *ws,
+                   size_t ws_bytes, void *stream) {
+    int rc = check_desc(d, true);
+    if (rc != MOE_OK) return rc;
+    if (!Xd || !W13 || !W2 || !seg_off || !A || !Y) return MOE_EINVAL;
+    if (!aligned16(Xd) || !aligned16(W13) || !aligned16(W2) || !aligned16(A) || !aligned16(Y) ||
+        (HU && !aligned16(HU)))
+        return MOE_EINVAL;
+    if (chunk_rows < 0 || chunk_rows % 256) return MOE_EINVAL;
+    if (chunk_rows > 0 && (!ws || !aligned16(ws) || ws_bytes < (size_t)kBarrierBytes)) return ws ? MOE_ENOSPC : MOE_EINVAL;
+    FfnArgs a = make_ffn_args(d, Xd, W13, W2, seg_off, HU, A, Y, chunk_rows, static_cast<uint32_t *>(ws));
+    return launch_ffn(d, a, static_cast<hipStream_t>(stream));
+}
+
+int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, const uint16_t *X, const uint16_t *W13,
+                  const uint16_t *W2, int32_t *counts, int32_t *seg_off, moe_src *phi, int32_t *route_row,
+                  uint16_t *Xd, uint16_t *HU, uint16_t *A, uint16_t *Y, uint16_t *out, int32_t flags,
+                  int32_t chunk_rows, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_desc(d, true);
+    if (rc != MOE_OK) return rc;
+    if (d->num_batches != 1) return MOE_EINVAL;
+    if (!routes || !w || !X || !W13 || !W2 || !counts || !seg_off || !phi || !route_row || !Xd || !A || !Y || !out ||
+        !ws)
+        return MOE_EINVAL;
+    const void *ptrs[] = {routes, w, X, W13, W2, counts, seg_off, phi, route_row, Xd, A, Y, out, ws};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MOE_EINVAL;
+    if (HU && !aligned16(HU)) return MOE_EINVAL;
+    if (chunk_rows < 0 || chunk_rows % 256) return MOE_EINVAL;
+    if (flags & ~MOE_PERSISTENT) return MOE_EINVAL;
+    if ((int64_t)ws_bytes < moe_workspace_bytes(d, MOE_OP_LAYER_FWD)) return MOE_ENOSPC;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *wsb = static_cast<char *>(ws);
+    uint32_t *bar = reinterpret_cast<uint32_t *>(wsb);
+    char *sched_ws = wsb + kBarrierBytes;
+    if (flags & MOE_PERSISTENT) {
+        LayerFwdArgs la;
+        SchedArgs &sa = la.sched;
+        sa.routes = routes;
+        sa.counts = counts;
+        sa.seg_off = seg_off;
+        sa.phi = phi;
+        sa.route_row = route_row;
+        sa.arrive = reinterpret_cast<uint32_t *>(sched_ws);
+        sa.wcnt = reinterpret_cast<int32_t *>(sched_ws + align256(4));
+        sa.P = d->P;
+        sa.R = d->Np * d->K;
+        sa.K = d->K;
+        sa.L = d->L;
+        sa.base = d->expert_base;
+        sa.pad = d->pad_rows;
+        sa.nb = 1;
+        sa.W = sched_chunks(d);
+        sa.wg_per_part = sched_wg_per_part(d);
+        sa.nbits = 32 - __builtin_clz((unsigned)d->L | 1u);
+        sa.cap = cap_rows(d);
+        la.ffn = make_ffn_args(d, Xd, W13, W2, seg_off, HU, A, Y, chunk_rows, bar);
+        la.X = X;
+        la.w = w;
+        la.out = out;
+        la.Np = d->Np;
+        la.K = d->K;
+        la.ntok = (int64_t)d->P * d->Np;
+        la.cap = cap_rows(d);
+        {
+            TraceScope tr("layer_zero", s);
+            hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, bar, (int64_t)(kBarrierBytes / 4));
+        }
+        if (launch_status() != MOE_OK) return MOE_EHIP;
+        // the persistent schedule stage counts with at most one arrival word
+        {
+            TraceScope tr("layer_sched_zero", s);
+            hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, sa.arrive, (int64_t)1);
+        }
+        if (launch_status() != MOE_OK) return MOE_EHIP;
+        void *args[] = {&la};
+        TraceScope tr("layer_fwd_persistent", s);
+        return launch_cooperative(reinterpret_cast<const void *>(k_layer_fwd_persistent), gemm_grid(), args, s);
+    }
+    moe_desc one = *d;
+    one.num_batches = 1;
+    rc = launch_schedule(&one, routes, counts, seg_off, phi, route_row, sched_ws, s);
+    if (rc != MOE_OK) return rc;
+    rc = launch_gather(d, X, phi, seg_off, Xd, s, "dispatch");
+    if (rc != MOE_OK) return rc;
+    FfnArgs a = make_ffn_args(d, Xd, W13, W2, seg_off, HU, A, Y, chunk_rows, bar);
+    rc = launch_ffn(d, a, s);
+    if (rc != MOE_OK) return rc;
+    return launch_combine(d, Y, route_row, w, out, s, "combine");
+}
+
+int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes, const float *w, const moe_src *phi,
+                  const int32_t *route_row, const int32_t *seg_off, const uint16_t *Xd, const uint16_t *HU,
+                  const uint16_t *A, const uint16_t *W13, const uint16_t *W2, uint16_t *dX, float *dW13, float *dW2,
+                  float *dw, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_desc(d, true);
+    if (rc != MOE_OK) return rc;
+    if (!dOut || !routes || !w || !phi || !route_row || !seg_off || !Xd || !HU || !A || !W13 || !W2 || !dX || !dW13 ||
+        !dW2 || !dw || !ws)
+        return MOE_EINVAL;
+    const void *ptrs[] = {dOut, phi, Xd, HU, A, W13, W2, dX, dW13, dW2, ws};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MOE_EINVAL;
+    if ((int64_t)ws_bytes < bwd_ws_bytes(d)) return MOE_ENOSPC;
+    (void)routes;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t cap = cap_rows(d);
+    char *p = static_cast<char *>(ws);
+    BwdArgs a;
+    a.dOd = reinterpret_cast<uint16_t *>(p);
+    p += align256(cap * d->H * 2);
+    a.dXd = reinterpret_cast<uint16_t *>(p);
+    p += align256(cap * d->H * 2);
+    a.dHU = reinterpret_cast<uint16_t *>(p);
+    p += align256(cap * 2ll * d->I * 2);
+    a.wrow = reinterpret_cast<float *>(p);
+    p += align256(cap * 4);
+    a.part = reinterpret_cast<float *>(p);
+    a.Xd = Xd;
+    a.HU = HU;
+    a.A = A;
+    a.W13 = W13;
+    a.W2 = W2;
+    a.seg_off = seg_off;
+    a.dW13 = dW13;
+    a.dW2 = dW2;
+    a.L = d->L;
+    a.H = d->H;
+    a.I = d->I;
+    a.nparts = bwd_nparts(d);
+    // B1: reverse-combine gather of the output gradient
+    rc = launch_gather(d, dOut, phi, seg_off, a.dOd, s, "bwd_gather");
+    if (rc != MOE_OK) return rc;
+    {
+        TraceScope tr("bwd_row_weight", s);
+        hipLaunchKernelGGL(k_row_weight, dim3((int)std::min<int64_t>((cap + 255) / 256, 4096)), dim3(256), 0, s, phi,
+                           seg_off + d->L, route_row, w, a.wrow, d->Np, d->K, cap);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    const int grid = gemm_grid();
+    // B2: down-projection dgrad with the SwiGLU backward and dw partials
+    {
+        TraceScope tr("bwd_down", s);
+        hipLaunchKernelGGL(k_bwd_down, dim3(grid), dim3(kGemmThreads), 0, s, a);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    const int64_t nslots = (int64_t)d->P * d->Np * d->K;
+    {
+        TraceScope tr("bwd_dw", s);
+        hipLaunchKernelGGL(k_dw_finalize, dim3((int)std::min<int64_t>((nslots + 255) / 256, 4096)), dim3(256), 0, s,
+                           route_row, a.part, a.nparts, dw, nslots);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    // B3: gate/up dgrad
+    {
+        TraceScope tr("bwd_gateup", s);
+        hipLaunchKernelGGL(k_bwd_gateup, dim3(grid), dim3(kGemmThreads), 0, s, a);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    // B4: reverse-dispatch sum over each token's local slots
+    rc = launch_combine(d, a.dXd, route_row, nullptr, dX, s, "bwd_reverse_dispatch");
+    if (rc != MOE_OK) return rc;
+    // B5: weight gradients, after every data gradient, fixed row order
+    TraceScope tr("bwd_wgrad", s);
+    hipLaunchKernelGGL(k_wgrad, dim3(grid), dim3(kGemmThreads), 0, s, a);
+    return launch_status();
+}
+
+int moe_trace_enable(int max_records) {
+    std::lock_guard<std::mutex> g(g_trace_mu);
+    for (auto &r : g_trace) {
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    g_trace.clear();
+    g_trace_cap = 0;
+    g_trace_used = 0;
+    if (max_records <= 0) return MOE_OK;
+    g_trace.resize(max_records);
+    for (auto &r : g_trace) {
+        if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return MOE_EHIP;
+        r.name[0] = 0;
+    }
+    g_trace_cap = max_records;
+    return MOE_OK;
+}
+
+int moe_trace_read(char *kernel, float *ms, int max_records) {
+    std::lock_guard<std::mutex> g(g_trace_mu);
+    int n = std::min(g_trace_used, max_records);
+    for (int i = 0; i < n; ++i) {
+        float t = -1.f;
+        if (hipEventElapsedTime(&t, g_trace[i].start, g_trace[i].stop) != hipSuccess) t = -1.f;
+        if (kernel) memcpy(kernel + 32 * i, g_trace[i].name, 32);
+        if (ms) ms[i] = t;
+    }
+    return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// Row-streaming kernels: the pull gather, the fixed-order combine, and the two
+// small per-row helpers of the backward.  All are HBM-bound copies: one wave
+// moves one row with 16-byte lane accesses (a row of H bf16 is H/8 chunks),
+// loads are issued before stores so each lane has several in flight.
+//
+//  gather   pull dispatch of "Beyond Peak TFLOPs" section 2.A / the
+//           Mixture-of-Kittens notes section 2: the destination reads each row
+//           through the two-column table {part, tok}; the backward's
+//           reverse-combine is the same gather of dOut.
+//  combine  push combine of the notes' section 2 done locally: per token, the
+//           local slots' rows weighted and summed in ascending slot order in
+//           fp32, rounded once; with no weights it is the reverse-dispatch sum.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kRowUnroll = 4;
+
+// Rows [0, Npad) of dst get src[phi.part][phi.tok] (or zeros on padding).
+// Persistent over rows: Npad is read on the device.
+__device__ void gather_rows_body(const uint16_t *__restrict__ src, const moe_src *__restrict__ phi,
+                                 const int32_t *__restrict__ npad_ptr, uint16_t *__restrict__ dst,
+                                 int Np, int H, int64_t row_begin, int64_t row_end_cap,
+                                 int wave_global, int nwaves) {
+    const int lane = lane_id();
+    const int64_t npad = min((int64_t)*npad_ptr, row_end_cap);
+    const int chunks = H / 8;
+    for (int64_t row = row_begin + wave_global; row < npad; row += nwaves) {
+        const uint2 s = reinterpret_cast<const uint2 *>(phi)[row];
+        const int32_t part = (int32_t)s.x, tok = (int32_t)s.y;
+        u32x4 *out = reinterpret_cast<u32x4 *>(dst + row * (int64_t)H);
+        if (part < 0) {
+            for (int c = lane; c < chunks; c += kWave) out[c] = u32x4{0, 0, 0, 0};
+            continue;
+        }
+        const u32x4 *in = reinterpret_cast<const u32x4 *>(src + ((int64_t)part * Np + tok) * H);
+        int c = lane;
+        for (; c + (kRowUnroll - 1) * kWave < chunks; c += kRowUnroll * kWave) {
+            u32x4 v[kRowUnroll];
+#pragma unroll
+            for (int u = 0; u < kRowUnroll; ++u) v[u] = __builtin_nontemporal_load(in + c + u * kWave);
+#pragma unroll
+            for (int u = 0; u < kRowUnroll; ++u) out[c + u * kWave] = v[u];
+        }
+        for (; c < chunks; c += kWave) out[c] = __builtin_nontemporal_load(in + c);
+    }
+}
+
+// out[g] = sum_{j asc, rows[g][j] >= 0} w[g][j] * Y[rows[g][j]] for tokens g in
+// [g_begin, g_end); one wave per token, kRowUnroll 16-byte chunks per lane in
+// flight.  w == nullptr means every weight is 1.
+__device__ void combine_body(const uint16_t *__restrict__ Y, const int32_t *__restrict__ route_row,
+                             const float *__restrict__ w, uint16_t *__restrict__ out, int K, int H,
+                             int64_t g_begin, int64_t g_end, int wave_global, int nwaves) {
+    const int lane = lane_id();
+    const int chunks = H / 8;
+    for (int64_t g = g_begin + wave_global; g < g_end; g += nwaves) {
+        u32x4 *o = reinterpret_cast<u32x4 *>(out + g * (int64_t)H);
+        for (int c0 = 0; c0 < chunks; c0 += kRowUnroll * kWave) {
+            float acc[kRowUnroll][8];
+#pragma unroll
+            for (int u = 0; u < kRowUnroll; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[u][e] = 0.f;
+            for (int j = 0; j < K; ++j) {
+                const int32_t rw = route_row[g * K + j];
+                if (rw < 0) continue;
+                const float wq = w ? w[g * K + j] : 1.0f;
+                const u32x4 *yr = reinterpret_cast<const u32x4 *>(Y + (int64_t)rw * H);
+                u32x4 v[kRowUnroll];
+#pragma unroll
+                for (int u = 0; u < kRowUnroll; ++u) {
+                    int c = c0 + u * kWave + lane;
+                    v[u] = c < chunks ? __builtin_nontemporal_load(yr + c) : u32x4{0, 0, 0, 0};
+                }
+#pragma unroll
+                for (int u = 0; u < kRowUnroll; ++u)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[u][2 * e] = fmaf(wq, __uint_as_float(v[u][e] << 16), acc[u][2 * e]);
+                        acc[u][2 * e + 1] = fmaf(wq, __uint_as_float(v[u][e] & 0xffff0000u), acc[u][2 * e + 1]);
+                    }
+            }
+#pragma unroll
+            for (int u = 0; u < kRowUnroll; ++u) {
+                int c = c0 + u * kWave + lane;
+                if (c < chunks)
+                    o[c] = u32x4{pack_bf2(acc[u][0], acc[u][1]), pack_bf2(acc[u][2], acc[u][3]),
+                                 pack_bf2(acc[u][4], acc[u][5]), pack_bf2(acc[u][6], acc[u][7])};
+            }
+        }
+    }
+}
+
+// wrow[i] = router weight of the route placed at row i (0 on padding rows).
+__device__ void row_weight_body(const moe_src *__restrict__ phi, const int32_t *__restrict__ npad_ptr,
+                                const int32_t *__restrict__ route_row, const float *__restrict__ w,
+                                float *__restrict__ wrow, int Np, int K, int64_t i) {
+    if (i >= *npad_ptr) return;
+    const uint2 s = reinterpret_cast<const uint2 *>(phi)[i];
+    float v = 0.f;
+    if ((int32_t)s.x >= 0) {
+        const int64_t g = (int64_t)(int32_t)s.x * Np + (int32_t)s.y;
+        for (int j = 0; j < K; ++j)
+            if (route_row[g * K + j] == (int32_t)i) v = w[g * K + j];
+    }
+    wrow[i] = v;
+}
+
+// dw[slot] = sum_q part[row][q] in ascending q (0 for non-local slots).
+__device__ void dw_finalize_body(const int32_t *__restrict__ route_row, const float *__restrict__ part,
+                                 int nparts, float *__restrict__ dw, int64_t slot) {
+    int32_t row = route_row[slot];
+    float s = 0.f;
+    if (row >= 0) {
+        const float *p = part + (int64_t)row * nparts;
+        for (int q = 0; q < nparts; ++q) s += p[q];
+    }
+    dw[slot] = s;
+}
+
+}  // namespace moe

@@ -1,0 +1,253 @@
+// On-device pull schedule: counting sort of routes into padded expert segments.
+//
+// Method ("Mixture-of-Kittens: A MoE Megakernel for GB300 NVL72", section 2,
+// on-device schedule generation; "Scan once, scatter once", section "The fix
+// is a counting sort"):
+//   1. count routes per (local expert, partition, logical thread),
+//   2. prefix the per-thread counts into thread-major offsets,
+//   3. pad every expert segment to pad_rows and take its base row S[l],
+//   4. scatter every route once to Phi[S[l] + p] with the stable cross-rank
+//      position p = sum_r' min(M[l][r'], o) + #{r' < r : M[l][r'] > o}.
+//
+// CDNA4 mapping.  A logical thread is one wavefront that owns a contiguous
+// chunk of kChunk routes of one partition (contiguous ownership is what makes
+// the order stable, so the table does not depend on how many logical threads
+// there are).  Inside a wave, 64 consecutive routes are ranked at once: lanes
+// holding the same local expert find each other with one ballot per bit of the
+// expert id, and a route's rank among them is a masked popcount, so the
+// ordinal o of every route is its index order with no atomics.  Per-wave
+// counters live in LDS.  The last workgroup to finish counting a batch (an
+// integer arrival counter) turns the per-wave counts into exclusive offsets,
+// the per-(expert, partition) counts M and the padded segment offsets S.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kSchedUnroll = 16;                    // route loads in flight per lane
+constexpr int kSchedChunk = kWave * kSchedUnroll;   // routes per logical thread (wave)
+constexpr int kSchedWaves = 4;                      // waves per workgroup
+
+struct SchedArgs {
+    const int32_t *routes;  // [nb][P][R]
+    int32_t *counts;        // [nb][L][P]
+    int32_t *seg_off;       // [nb][L+1]
+    moe_src *phi;           // [nb][cap]
+    int32_t *route_row;     // [nb][P][R]
+    int32_t *wcnt;          // ws: [nb][P][W][L] counts, then exclusive offsets
+    uint32_t *arrive;       // ws: [nb] arrival counters (zero on entry)
+    int32_t P, R, K, L, base, pad, nb, W, wg_per_part, nbits;
+    int64_t cap;
+};
+
+__device__ __forceinline__ int bit_length(uint32_t v) { return 32 - __builtin_clz(v | 1u); }
+
+// Workgroup index -> (batch, partition, first chunk).  For eight or more
+// batches the workgroups of one batch share an XCD (hardware deals workgroup
+// ids round-robin over the 8 XCDs), so its table rows merge in one L2.
+__device__ __forceinline__ bool sched_locate(const SchedArgs &a, int x, int &b, int &r, int &q) {
+    int wg_per_batch = a.P * a.wg_per_part;
+    int k;
+    if (a.nb >= 8) {
+        int xcd = x & 7, s = x >> 3;
+        b = xcd + 8 * (s / wg_per_batch);
+        k = s % wg_per_batch;
+    } else {
+        b = x / wg_per_batch;
+        k = x % wg_per_batch;
+    }
+    if (b >= a.nb) return false;
+    r = k / a.wg_per_part;
+    q = k % a.wg_per_part;
+    return true;
+}
+
+__device__ __forceinline__ uint32_t local_id(int32_t e, int base, int L) {
+    uint32_t l = (uint32_t)(e - base);
+    return l < (uint32_t)L ? l : (uint32_t)L;  // L = not local
+}
+
+// Block-wide exclusive scan of padded segment lengths -> seg_off (one batch).
+__device__ void sched_finalize(const SchedArgs &a, int b, int32_t *s_tot) {
+    const int L = a.L, P = a.P, W = a.W;
+    int32_t *wc = a.wcnt + (int64_t)b * P * W * L;
+    int32_t *cnt = a.counts + (int64_t)b * L * P;
+    // per (partition, expert): exclusive prefix over the partition's chunks
+    for (int pr = threadIdx.x; pr < P * L; pr += blockDim.x) {
+        int r = pr / L, l = pr % L;
+        int32_t *col = wc + (int64_t)r * W * L + l;
+        int32_t acc = 0;
+        int w = 0;
+        for (; w + 8 <= W; w += 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = col[(int64_t)(w + u) * L];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                col[(int64_t)(w + u) * L] = acc;
+                acc += v[u];
+            }
+        }
+        for (; w < W; ++w) {
+            int32_t v = col[(int64_t)w * L];
+            col[(int64_t)w * L] = acc;
+            acc += v;
+        }
+        cnt[l * P + r] = acc;
+        s_tot[pr] = acc;  // [r][l]
+    }
+    __syncthreads();
+    // padded segment lengths, then a block scan over experts
+    int32_t *s_len = s_tot + P * L;  // [L]
+    for (int l = threadIdx.x; l < L; l += blockDim.x) {
+        int32_t t = 0;
+        for (int r = 0; r < P; ++r) t += s_tot[r * L + l];
+        s_len[l] = (t + a.pad - 1) / a.pad * a.pad;
+    }
+    __syncthreads();
+    // each thread sums a contiguous run of experts, then a serial pass over runs
+    int32_t *s_run = s_len + L;  // [blockDim.x]
+    const int per = (L + blockDim.x - 1) / blockDim.x;
+    int lo = threadIdx.x * per, hi = min(L, lo + per);
+    int32_t sum = 0;
+    for (int l = lo; l < hi; ++l) sum += s_len[l];
+    s_run[threadIdx.x] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t acc = 0;
+        for (int i = 0; i < (int)blockDim.x; ++i) {
+            int32_t v = s_run[i];
+            s_run[i] = acc;
+            acc += v;
+        }
+    }
+    __syncthreads();
+    int32_t *so = a.seg_off + (int64_t)b * (L + 1);
+    int32_t acc = s_run[threadIdx.x];
+    for (int l = lo; l < hi; ++l) {
+        so[l] = acc;
+        acc += s_len[l];
+    }
+    if (hi == L && lo < hi) so[L] = acc;
+    if (L == 0 && threadIdx.x == 0) so[0] = 0;
+}
+
+// Stage 1 (+ stages 2 and 3 in the batch's last workgroup).  x is the
+// workgroup's index in the schedule grid (a persistent caller loops over it).
+__device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
+    int b, r, q;
+    if (!sched_locate(a, x, b, r, q)) return;
+    __syncthreads();  // LDS may still be in use by the caller's previous item
+    const int lane = lane_id();
+    const int wv = threadIdx.x / kWave;
+    const int w = q * kSchedWaves + wv;  // chunk (logical thread) index in the partition
+    const int L = a.L;
+    int32_t *cnt = smem + wv * (L + 1);
+    for (int l = lane; l <= L; l += kWave) cnt[l] = 0;
+    __syncthreads();
+    if (w < a.W) {
+        const int32_t *src = a.routes + ((int64_t)b * a.P + r) * a.R;
+        const int64_t lo = (int64_t)w * kSchedChunk;
+        int32_t e[kSchedUnroll];
+#pragma unroll
+        for (int u = 0; u < kSchedUnroll; ++u) {
+            int64_t i = lo + u * kWave + lane;
+            e[u] = i < a.R ? __builtin_nontemporal_load(src + i) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kSchedUnroll; ++u) {
+            uint32_t v = local_id(e[u], a.base, L);
+            uint64_t peers = match_lanes(v, a.nbits);
+            bool leader = (peers & ((1ull << lane) - 1ull)) == 0;  // lowest lane of its group
+            if (leader && v < (uint32_t)L) cnt[v] += __popcll(peers);
+        }
+    }
+    __syncthreads();
+    if (w < a.W) {
+        int32_t *dst = a.wcnt + (((int64_t)b * a.P + r) * a.W + w) * L;
+        for (int l = lane; l < L; l += kWave) dst[l] = cnt[l];
+    }
+    // arrival: the last workgroup of this batch finalises it
+    __shared__ uint32_t s_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t n = __hip_atomic_fetch_add(a.arrive + b, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (n == (uint32_t)(a.P * a.wg_per_part - 1)) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (s_last) {
+        __threadfence();
+        sched_finalize(a, b, smem);
+    }
+}
+
+// Stage 4: scatter every route once.
+__device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
+    int b, r, q;
+    if (!sched_locate(a, x, b, r, q)) return;
+    __syncthreads();
+    const int lane = lane_id();
+    const int wv = threadIdx.x / kWave;
+    const int w = q * kSchedWaves + wv;
+    const int L = a.L, P = a.P;
+    // LDS: M [L][P], S [L+1], per-wave running offsets [4][L]
+    int32_t *sM = smem;
+    int32_t *sS = sM + L * P;
+    int32_t *run = sS + L + 1 + wv * L;
+    const int32_t *cnt = a.counts + (int64_t)b * L * P;
+    const int32_t *so = a.seg_off + (int64_t)b * (L + 1);
+    for (int i = threadIdx.x; i < L * P; i += blockDim.x) sM[i] = cnt[i];
+    for (int i = threadIdx.x; i <= L; i += blockDim.x) sS[i] = so[i];
+    if (w < a.W) {
+        const int32_t *off = a.wcnt + (((int64_t)b * P + r) * a.W + w) * L;
+        for (int l = lane; l < L; l += kWave) run[l] = off[l];
+    }
+    __syncthreads();
+    moe_src *phi = a.phi + (int64_t)b * a.cap;
+    if (w < a.W) {
+        const int32_t *src = a.routes + ((int64_t)b * P + r) * a.R;
+        int32_t *rrow = a.route_row + ((int64_t)b * P + r) * a.R;
+        const int64_t lo = (int64_t)w * kSchedChunk;
+        int32_t e[kSchedUnroll];
+#pragma unroll
+        for (int u = 0; u < kSchedUnroll; ++u) {
+            int64_t i = lo + u * kWave + lane;
+            e[u] = i < a.R ? __builtin_nontemporal_load(src + i) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kSchedUnroll; ++u) {
+            const int64_t i = lo + u * kWave + lane;
+            uint32_t v = local_id(e[u], a.base, L);
+            uint64_t peers = match_lanes(v, a.nbits);
+            int rank = lanes_below(peers);
+            int32_t row = -1;
+            if (v < (uint32_t)L) {
+                const int32_t o = run[v] + rank;
+                const int32_t *Ml = sM + v * P;
+                int32_t p = 0;
+                for (int rr = 0; rr < P; ++rr) {
+                    int32_t m = Ml[rr];
+                    p += min(m, o) + ((rr < r && m > o) ? 1 : 0);
+                }
+                row = sS[v] + p;
+                reinterpret_cast<uint2 *>(phi)[row] = make_uint2((uint32_t)r, (uint32_t)((int32_t)i / a.K));
+            }
+            if (i < a.R) rrow[i] = row;
+            // every lane has read run[v]; now the group's lowest lane advances it
+            if (rank == 0 && v < (uint32_t)L) run[v] += __popcll(peers);
+        }
+    }
+    // padding rows of the segments this workgroup owns: (-1, -1)
+    const int wg_in_batch = r * a.wg_per_part + q;
+    const int nwg = P * a.wg_per_part;
+    for (int l = wg_in_batch; l < L; l += nwg) {
+        int32_t t = 0;
+        for (int rr = 0; rr < P; ++rr) t += sM[l * P + rr];
+        for (int32_t row = sS[l] + t + threadIdx.x; row < sS[l + 1]; row += blockDim.x)
+            reinterpret_cast<uint2 *>(phi)[row] = make_uint2(0xffffffffu, 0xffffffffu);
+    }
+}
+
+}  // namespace moe

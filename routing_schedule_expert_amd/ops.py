@@ -1,0 +1,213 @@
+"""Python binding of the C ABI in include/moe.h (ctypes; argument marshalling only).
+
+Every function has the name of its C entry point and takes torch tensors for
+the device buffers; the stream defaults to torch's current stream on the
+tensors' device.  Each call returns after the launch (asynchronous) and raises
+``MoeError`` if the library returns a negative code.  Every step of the layer
+runs in the HIP library; if ``libmoe.so`` is missing or a device pointer is not
+a CUDA(HIP) tensor, the call fails loudly - there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_ENOSPC, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_OP_SCHEDULE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_LAYER_FWD, MOE_OP_LAYER_BWD = range(6)
+MOE_PERSISTENT = 1
+
+EXPORTED = (
+    "moe_strerror", "moe_capacity_rows", "moe_workspace_bytes", "moe_schedule", "moe_dispatch",
+    "moe_expert_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_bwd", "moe_trace_enable", "moe_trace_read",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {strerror(code)} ({code})")
+        self.code = code
+
+
+class moe_desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("P", "Np", "K", "E", "L", "expert_base", "pad_rows", "sched_threads", "H", "I", "num_batches")]
+
+
+def make_desc(P, Np, K, E, L=None, expert_base=0, pad_rows=256, sched_threads=1024, H=0, I=0, num_batches=1):
+    if L is None:
+        L = E // P
+    return moe_desc(P, Np, K, E, L, expert_base, pad_rows, sched_threads, H, I, num_batches)
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree HIP library (fails loudly when it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with routing_schedule_expert_amd/build.py "
+                          "(or __graft_entry__.build()); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, D = ctypes.c_void_p, ctypes.POINTER(moe_desc)
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_capacity_rows": (i64, [D]),
+        "moe_workspace_bytes": (i64, [D, ctypes.c_int]),
+        "moe_schedule": (ctypes.c_int, [D, P, P, P, P, P, P, sz, P]),
+        "moe_dispatch": (ctypes.c_int, [D, P, P, P, P, P]),
+        "moe_expert_ffn": (ctypes.c_int, [D, P, P, P, P, P, P, P, i32, P, sz, P]),
+        "moe_combine": (ctypes.c_int, [D, P, P, P, P, P]),
+        "moe_layer_fwd": (ctypes.c_int, [D] + [P] * 14 + [i32, i32, P, sz, P]),
+        "moe_layer_bwd": (ctypes.c_int, [D] + [P] * 16 + [sz, P]),
+        "moe_trace_enable": (ctypes.c_int, [ctypes.c_int]),
+        "moe_trace_read": (ctypes.c_int, [P, P, ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().moe_strerror(code).decode()
+
+
+def _check(rc: int, where: str) -> int:
+    if rc != MOE_OK:
+        raise MoeError(rc, where)
+    return rc
+
+
+def _dev(t):
+    """Device pointer of a CUDA(HIP) tensor, or NULL for None."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("device buffers must be CUDA (HIP) torch tensors")
+    if not t.is_contiguous():
+        raise ValueError("device buffers must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, ref: torch.Tensor):
+    if stream is None:
+        stream = torch.cuda.current_stream(ref.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def capacity_rows(d: moe_desc) -> int:
+    n = load().moe_capacity_rows(ctypes.byref(d))
+    if n < 0:
+        raise MoeError(MOE_EINVAL, "moe_capacity_rows")
+    return int(n)
+
+
+def workspace_bytes(d: moe_desc, op: int) -> int:
+    n = load().moe_workspace_bytes(ctypes.byref(d), op)
+    if n < 0:
+        raise MoeError(MOE_EINVAL, "moe_workspace_bytes")
+    return int(n)
+
+
+def moe_schedule(d, routes, counts, seg_off, phi, route_row, ws, stream=None):
+    rc = load().moe_schedule(ctypes.byref(d), _dev(routes), _dev(counts), _dev(seg_off), _dev(phi), _dev(route_row),
+                             _dev(ws), ws.numel() * ws.element_size(), _stream(stream, routes))
+    return _check(rc, "moe_schedule")
+
+
+def moe_dispatch(d, X, phi, seg_off, Xd, stream=None):
+    rc = load().moe_dispatch(ctypes.byref(d), _dev(X), _dev(phi), _dev(seg_off), _dev(Xd), _stream(stream, X))
+    return _check(rc, "moe_dispatch")
+
+
+def moe_expert_ffn(d, Xd, W13, W2, seg_off, HU, A, Y, chunk_rows=0, ws=None, stream=None):
+    rc = load().moe_expert_ffn(ctypes.byref(d), _dev(Xd), _dev(W13), _dev(W2), _dev(seg_off), _dev(HU), _dev(A),
+                               _dev(Y), chunk_rows, _dev(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                               _stream(stream, Xd))
+    return _check(rc, "moe_expert_ffn")
+
+
+def moe_combine(d, Y, route_row, w, out, stream=None):
+    rc = load().moe_combine(ctypes.byref(d), _dev(Y), _dev(route_row), _dev(w), _dev(out), _stream(stream, Y))
+    return _check(rc, "moe_combine")
+
+
+def moe_layer_fwd(d, routes, w, X, W13, W2, counts, seg_off, phi, route_row, Xd, HU, A, Y, out, flags=0,
+                  chunk_rows=0, ws=None, stream=None):
+    rc = load().moe_layer_fwd(ctypes.byref(d), _dev(routes), _dev(w), _dev(X), _dev(W13), _dev(W2), _dev(counts),
+                              _dev(seg_off), _dev(phi), _dev(route_row), _dev(Xd), _dev(HU), _dev(A), _dev(Y),
+                              _dev(out), flags, chunk_rows, _dev(ws), ws.numel() * ws.element_size(),
+                              _stream(stream, X))
+    return _check(rc, "moe_layer_fwd")
+
+
+def moe_layer_bwd(d, dOut, routes, w, phi, route_row, seg_off, Xd, HU, A, W13, W2, dX, dW13, dW2, dw, ws,
+                  stream=None):
+    rc = load().moe_layer_bwd(ctypes.byref(d), _dev(dOut), _dev(routes), _dev(w), _dev(phi), _dev(route_row),
+                              _dev(seg_off), _dev(Xd), _dev(HU), _dev(A), _dev(W13), _dev(W2), _dev(dX), _dev(dW13),
+                              _dev(dW2), _dev(dw), _dev(ws), ws.numel() * ws.element_size(), _stream(stream, dOut))
+    return _check(rc, "moe_layer_bwd")
+
+
+def moe_trace_enable(max_records: int) -> None:
+    _check(load().moe_trace_enable(max_records), "moe_trace_enable")
+
+
+def moe_trace_read(max_records: int = 4096):
+    """[(kernel name, ms)] of the recorded launches (synchronise first)."""
+    names = ctypes.create_string_buffer(32 * max_records)
+    ms = (ctypes.c_float * max_records)()
+    n = load().moe_trace_read(names, ms, max_records)
+    return [(names.raw[32 * i:32 * i + 32].split(b"\0", 1)[0].decode(), float(ms[i])) for i in range(n)]
+
+
+# ---------------------------------------------------------------------------
+# Buffer helpers (device memory via torch; no arithmetic).
+# ---------------------------------------------------------------------------
+
+@dataclass
+class FwdBuffers:
+    counts: torch.Tensor
+    seg_off: torch.Tensor
+    phi: torch.Tensor
+    route_row: torch.Tensor
+    Xd: torch.Tensor
+    HU: torch.Tensor | None
+    A: torch.Tensor
+    Y: torch.Tensor
+    out: torch.Tensor
+    ws: torch.Tensor
+
+
+def alloc_fwd(d: moe_desc, device, save_hu: bool = True) -> FwdBuffers:
+    cap = capacity_rows(d)
+    i32, bf = torch.int32, torch.bfloat16
+    return FwdBuffers(
+        counts=torch.empty((d.L, d.P), dtype=i32, device=device),
+        seg_off=torch.empty(d.L + 1, dtype=i32, device=device),
+        phi=torch.empty((cap, 2), dtype=i32, device=device),
+        route_row=torch.empty((d.P, d.Np, d.K), dtype=i32, device=device),
+        Xd=torch.empty((cap, d.H), dtype=bf, device=device),
+        HU=torch.empty((cap, 2 * d.I), dtype=bf, device=device) if save_hu else None,
+        A=torch.empty((cap, d.I), dtype=bf, device=device),
+        Y=torch.empty((cap, d.H), dtype=bf, device=device),
+        out=torch.empty((d.P, d.Np, d.H), dtype=bf, device=device),
+        ws=torch.empty(max(workspace_bytes(d, MOE_OP_LAYER_FWD), 256), dtype=torch.uint8, device=device),
+    )
+
+
+def layer_fwd(d, routes, w, X, W13, W2, bufs: FwdBuffers, flags=0, chunk_rows=0, stream=None):
+    return moe_layer_fwd(d, routes, w, X, W13, W2, bufs.counts, bufs.seg_off, bufs.phi, bufs.route_row, bufs.Xd,
+                         bufs.HU, bufs.A, bufs.Y, bufs.out, flags, chunk_rows, bufs.ws, stream)

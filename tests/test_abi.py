@@ -1,0 +1,118 @@
+"""The C-ABI library on the host (no GPU needed).
+
+The library must load, export every function include/moe.h declares, size its
+buffers as documented, and reject bad arguments with the documented codes
+before anything is launched (checked with NULL or host-only arguments, so no
+device code ever runs here).
+"""
+import ctypes
+import re
+import os
+
+import pytest
+
+from routing_schedule_expert_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = ops.load()
+    names = declared_functions()
+    assert set(names) == set(ops.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror():
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(ops.strerror(code), str) and ops.strerror(code)
+
+
+def kimi():
+    return ops.make_desc(8, 7168, 8, 384, 48, H=7168, I=2048)
+
+
+def test_capacity_and_workspace_sizes():
+    d = kimi()
+    assert ops.capacity_rows(d) == 8 * 7168 * 8 + 48 * 255 == 470992
+    assert ops.workspace_bytes(d, ops.MOE_OP_DISPATCH) == 0
+    assert ops.workspace_bytes(d, ops.MOE_OP_SCHEDULE) > 0
+    d64 = kimi()
+    d64.num_batches = 64
+    assert ops.workspace_bytes(d64, ops.MOE_OP_SCHEDULE) > 60 * ops.workspace_bytes(d, ops.MOE_OP_SCHEDULE)
+    cap = ops.capacity_rows(d)
+    assert ops.workspace_bytes(d, ops.MOE_OP_LAYER_BWD) >= cap * (7168 * 2 + 4096) * 2
+
+
+@pytest.mark.parametrize("field,value", [
+    ("P", 0), ("Np", 0), ("K", 0), ("E", 0), ("L", 0), ("pad_rows", 0), ("sched_threads", 0),
+    ("num_batches", 0), ("expert_base", -1), ("expert_base", 337),
+])
+def test_invalid_descriptor(field, value):
+    d = kimi()
+    setattr(d, field, value)
+    assert ops.load().moe_capacity_rows(ctypes.byref(d)) == -1
+    assert ops.load().moe_workspace_bytes(ctypes.byref(d), ops.MOE_OP_SCHEDULE) == -1
+
+
+def test_unsupported_shapes():
+    lib = ops.load()
+    for H, I, pad in ((7000, 2048, 256), (7168, 2000, 256), (7168, 2048, 128)):
+        d = ops.make_desc(8, 7168, 8, 384, 48, pad_rows=pad, H=H, I=I)
+        assert lib.moe_workspace_bytes(ctypes.byref(d), ops.MOE_OP_EXPERT_FFN) == -1
+        rc = lib.moe_expert_ffn(ctypes.byref(d), *([None] * 7), 0, None, 0, None)
+        assert rc == ops.MOE_EUNSUPPORTED
+    d = ops.make_desc(8, 7168, 8, 4096 * 8, 4096)  # L*P beyond the supported table size
+    assert lib.moe_capacity_rows(ctypes.byref(d)) == -1
+
+
+def test_null_arguments_rejected_before_launch():
+    lib = ops.load()
+    d = kimi()
+    assert lib.moe_schedule(None, *([None] * 6), 0, None) == ops.MOE_EINVAL
+    assert lib.moe_schedule(ctypes.byref(d), *([None] * 6), 0, None) == ops.MOE_EINVAL
+    assert lib.moe_dispatch(ctypes.byref(d), *([None] * 4), None) == ops.MOE_EINVAL
+    assert lib.moe_combine(ctypes.byref(d), *([None] * 4), None) == ops.MOE_EINVAL
+    assert lib.moe_expert_ffn(ctypes.byref(d), *([None] * 7), 0, None, 0, None) == ops.MOE_EINVAL
+    assert lib.moe_layer_fwd(ctypes.byref(d), *([None] * 14), 0, 0, None, 0, None) == ops.MOE_EINVAL
+    assert lib.moe_layer_bwd(ctypes.byref(d), *([None] * 16), 0, None) == ops.MOE_EINVAL
+
+
+def _fake(addr):
+    # aligned, non-NULL host addresses: every call below fails its host-side
+    # checks before it could launch anything that dereferences them
+    return ctypes.c_void_p(addr)
+
+
+def test_small_workspace_and_misalignment():
+    lib = ops.load()
+    d = kimi()
+    p = [_fake(0x10000 * (i + 1)) for i in range(8)]
+    need = lib.moe_workspace_bytes(ctypes.byref(d), ops.MOE_OP_SCHEDULE)
+    assert lib.moe_schedule(ctypes.byref(d), *p[:6], need - 1, None) == ops.MOE_ENOSPC
+    bad = _fake(0x10004)
+    assert lib.moe_schedule(ctypes.byref(d), bad, *p[1:6], need, None) == ops.MOE_EINVAL
+    # chunk_rows must be a non-negative multiple of 256
+    assert lib.moe_expert_ffn(ctypes.byref(d), *p[:4], None, p[4], p[5], 100, p[6], 256, None) == ops.MOE_EINVAL
+    # the forward layer call takes one routing tensor
+    d2 = kimi()
+    d2.num_batches = 2
+    args = p[:5] + p[:4] + [p[4], None, p[5], p[6], p[7]]
+    assert lib.moe_layer_fwd(ctypes.byref(d2), *args, 0, 0, p[0], 1 << 30, None) == ops.MOE_EINVAL
+    # unknown flag bits
+    assert lib.moe_layer_fwd(ctypes.byref(d), *args, 8, 0, p[0], 1 << 30, None) == ops.MOE_EINVAL
+    # backward workspace too small
+    nbwd = lib.moe_workspace_bytes(ctypes.byref(d), ops.MOE_OP_LAYER_BWD)
+    bargs = [p[i % 8] for i in range(16)]
+    assert lib.moe_layer_bwd(ctypes.byref(d), *bargs, nbwd - 1, None) == ops.MOE_ENOSPC
+
+
+def test_trace_read_empty():
+    assert ops.moe_trace_read(4) == []

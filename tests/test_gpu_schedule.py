@@ -1,0 +1,138 @@
+"""GPU schedule vs the CPU oracle: bit-exact on every output.
+
+The 16 named cases mirror the validation count of 'Scan once, scatter once'
+(realistic and adversarial routings); random cases and batched calls follow.
+Rows of Phi past Npad are never written (checked against a fill pattern).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from routing_schedule_expert_amd import inputs
+from tests.helpers import gpu_schedule
+
+pytestmark = pytest.mark.gpu
+
+
+def check(routes, L, base=0, pad=256, E=None, NT=1024):
+    r = routes if routes.ndim == 4 else routes[None]
+    g = gpu_schedule(r, L, base, pad, E, NT)
+    for b in range(r.shape[0]):
+        s = oracle.schedule(r[b], L, base, pad)
+        np.testing.assert_array_equal(g["counts"][b], s.counts, err_msg=f"counts batch {b}")
+        np.testing.assert_array_equal(g["seg_off"][b], s.seg_off, err_msg=f"seg_off batch {b}")
+        np.testing.assert_array_equal(g["phi"][b][: s.npad], s.phi, err_msg=f"phi batch {b}")
+        assert np.all(g["phi"][b][s.npad:] == -7), "rows past Npad were written"
+        np.testing.assert_array_equal(g["route_row"][b], s.route_row, err_msg=f"route_row batch {b}")
+    return g
+
+
+KIMI = dict(P=8, Np=7168, E=384, K=8)
+
+
+def named_case(name):
+    P, Np, E, K = KIMI["P"], KIMI["Np"], KIMI["E"], KIMI["K"]
+    L = E // P
+    rng = inputs.rng_for(100 + NAMED.index(name))
+    if name == "uniform":
+        return inputs.routes_uniform(rng, P, Np, E, K)[0], L
+    if name == "zipf1.2":
+        return inputs.routes_zipf(rng, P, Np, E, K, 1.2)[0], L
+    if name == "zipf1.5":
+        return inputs.routes_zipf(rng, P, Np, E, K, 1.5)[0], L
+    if name == "hot4":
+        return inputs.routes_hot(rng, P, Np, E, K, L, 0, s=1.5)[0], L
+    if name == "one_expert":
+        return np.full((P, 512, K), 5, np.int32), L
+    if name == "no_local":
+        return (L + rng.integers(0, E - L, size=(P, 1024, K))).astype(np.int32), L
+    if name == "partition_empty":
+        r = inputs.routes_uniform(rng, P, 1024, E, K)[0]
+        r[3] = L + (r[3] % (E - L))
+        return r, L
+    if name in ("at_256", "below_256", "above_256"):
+        # expert l receives 256*(l%3+1) + delta routes, spread over partitions
+        delta = {"at_256": 0, "below_256": -1, "above_256": 1}[name]
+        P2, K2, L2 = 4, 2, 6
+        ids = np.concatenate([np.full(256 * (l % 3 + 1) + delta, l) for l in range(L2)])
+        ids = rng.permutation(ids)
+        n = P2 * K2 * ((ids.size + P2 * K2 - 1) // (P2 * K2))
+        ids = np.concatenate([ids, np.full(n - ids.size, L2 + 1)])
+        return ids.reshape(P2, -1, K2).astype(np.int32), L2
+    if name == "duplicates":
+        r = rng.integers(0, 12, size=(4, 300, 4)).astype(np.int32)
+        r[:, :, 1] = r[:, :, 0]
+        return r, 12
+    if name == "out_of_range":
+        return rng.integers(-5, 30, size=(4, 777, 3)).astype(np.int32), 16
+    if name == "np1":
+        return inputs.routes_uniform(rng, P, 1, E, K)[0], L
+    if name == "k1":
+        return inputs.routes_uniform(rng, P, 4096, E, 1)[0], L
+    if name == "p1":
+        return inputs.routes_uniform(rng, 1, 4096, 64, 8)[0], 64
+    if name == "tiny":
+        return inputs.routes_topk_logits(rng, 2, 256, 8, 2)[0], 4
+    raise KeyError(name)
+
+
+NAMED = ["uniform", "zipf1.2", "zipf1.5", "hot4", "one_expert", "no_local", "partition_empty", "at_256",
+         "below_256", "above_256", "duplicates", "out_of_range", "np1", "k1", "p1", "tiny"]
+
+
+@pytest.mark.parametrize("name", NAMED)
+def test_named_case(name):
+    print(f"[schedule] case {name}", flush=True)
+    routes, L = named_case(name)
+    check(routes, L, E=max(int(routes.max()) + 1, L))
+
+
+def test_random_cases():
+    rng = np.random.default_rng(2024)
+    for i in range(40):
+        P = int(rng.integers(1, 9))
+        Np = int(rng.integers(1, 3000))
+        K = int(rng.integers(1, 9))
+        E = int(rng.integers(1, 200))
+        L = int(rng.integers(1, E + 1))
+        base = int(rng.integers(0, E - L + 1))
+        pad = int(rng.choice([1, 7, 64, 256]))
+        routes = rng.integers(-1, E + 1, size=(P, Np, K)).astype(np.int32)
+        print(f"[schedule] random {i}: P={P} Np={Np} K={K} E={E} L={L} base={base} pad={pad}", flush=True)
+        check(routes, L, base, pad, E)
+
+
+def test_sched_threads_does_not_change_the_table():
+    routes, L = named_case("zipf1.2")
+    a = gpu_schedule(routes, L, NT=1024)
+    b = gpu_schedule(routes, L, NT=37)
+    for k in ("counts", "seg_off", "phi", "route_row"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+@pytest.mark.parametrize("nb", [3, 9])
+def test_batched(nb):
+    rng = inputs.rng_for(77 + nb)
+    r = np.stack([inputs.routes_uniform(rng, 4, 2000, 96, 4)[0] for _ in range(nb)])
+    print(f"[schedule] batched nb={nb}", flush=True)
+    check(r, 24, E=96)
+
+
+def test_batched_kimi_64():
+    rng = inputs.rng_for(64)
+    r = np.stack([inputs.routes_uniform(rng, 8, 7168, 384, 8)[0] for _ in range(64)])
+    print("[schedule] batched kimi nb=64", flush=True)
+    g = gpu_schedule(r, 48)
+    for b in (0, 1, 7, 8, 33, 63):
+        s = oracle.schedule(r[b], 48, 0, 256)
+        np.testing.assert_array_equal(g["phi"][b][: s.npad], s.phi)
+        np.testing.assert_array_equal(g["route_row"][b], s.route_row)
+        np.testing.assert_array_equal(g["seg_off"][b], s.seg_off)
+
+
+def test_repeatable():
+    routes, L = named_case("hot4")
+    a = gpu_schedule(routes, L)
+    b = gpu_schedule(routes, L)
+    for k in ("counts", "seg_off", "phi", "route_row"):
+        np.testing.assert_array_equal(a[k], b[k])
