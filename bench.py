@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of one MI355X's share of the Kimi-shaped MoE layer forward.
+
+One step = one pass of the whole forward hot path through the C ABI
+(moe_layer_fwd: counting-sort schedule, pull gather, SwiGLU grouped GEMMs,
+fixed-order combine) on 8 partitions x 7,168 tokens, 384 experts (48 local),
+top-8, H=7168, I=2048, balanced routing (one local route per token), bf16,
+inputs resident in HBM.  Prints ONE JSON line:
+
+  value      layer-forward TFLOP/s, algorithmic (6*H*I flop per local route)
+  roofline   the dominant kernel (gate/up grouped GEMM + SwiGLU) against the
+             bf16 dense MFMA peak; its duration comes from HIP events recorded
+             on its own stream around every launch in the timed region
+  schedule   the schedule alone on 64 independent routing tensors per call
+             (routes/s and compulsory HBM bytes against 8 TB/s)
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+
+python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+METRIC = "MoE layer fwd TFLOP/s + MFMA util; schedule routes/s (Kimi shape, 1 GPU)"
+
+KIMI = dict(P=8, Np=7168, E=384, K=8, L=48, H=7168, I=2048)
+KERNEL_SOURCES = ("routing_schedule_expert_amd/csrc/gemm.hpp", "routing_schedule_expert_amd/csrc/layer.hpp",
+                  "routing_schedule_expert_amd/csrc/common.hpp")
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, launches_per_step: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_kimi_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def bench_layer(args, torch, ops, inputs, dev):
+    c = KIMI
+    h = inputs.make_layer_inputs_device(5, c["P"], c["Np"], c["E"], c["K"], c["L"], c["H"], c["I"], dev,
+                                        routing="balanced", x_std=1.0)
+    d = ops.make_desc(c["P"], c["Np"], c["K"], c["E"], c["L"], H=c["H"], I=c["I"])
+    routes = torch.from_numpy(h["routes"]).to(dev)
+    w = torch.from_numpy(h["w"]).to(dev)
+    X, W13, W2 = h["X"], h["W13"], h["W2"]
+    bufs = ops.alloc_fwd(d, dev, save_hu=True)
+    local_routes = int(((h["routes"] >= 0) & (h["routes"] < c["L"])).sum())
+    flops = 6.0 * c["H"] * c["I"] * local_routes
+    flops_gateup = 4.0 * c["H"] * c["I"] * local_routes
+    flops_down = 2.0 * c["H"] * c["I"] * local_routes
+    flags = ops.MOE_PERSISTENT if args.persistent else 0
+
+    def step():
+        ops.layer_fwd(d, routes, w, X, W13, W2, bufs, flags=flags, chunk_rows=args.chunk_rows)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ops.moe_trace_enable(args.steps * 16)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    recs = ops.moe_trace_read(args.steps * 16)
+    ops.moe_trace_enable(0)
+    per = {}
+    for name, ms in recs:
+        per.setdefault(name, []).append(ms)
+    stage_ms = {k: float(np.mean(v)) for k, v in per.items()}
+    npad = int(bufs.seg_off[-1].item())
+    return dict(d=d, h=h, bufs=bufs, ms_step=ms_step, stage_ms=stage_ms, flops=flops, flops_gateup=flops_gateup,
+                flops_down=flops_down, local_routes=local_routes, npad=npad, routes=routes, w=w)
+
+
+def bench_schedule(args, torch, ops, inputs, dev, nb, kind="uniform"):
+    c = KIMI
+    rng = inputs.rng_for(2)
+    if kind == "uniform":
+        r = np.stack([inputs.routes_uniform(rng, c["P"], c["Np"], c["E"], c["K"])[0] for _ in range(nb)])
+    else:
+        r = np.stack([inputs.routes_zipf(rng, c["P"], c["Np"], c["E"], c["K"], 1.2)[0] for _ in range(nb)])
+    d = ops.make_desc(c["P"], c["Np"], c["K"], c["E"], c["L"], num_batches=nb)
+    cap = ops.capacity_rows(d)
+    rt = torch.from_numpy(r).to(dev)
+    counts = torch.empty((nb, c["L"], c["P"]), dtype=torch.int32, device=dev)
+    seg_off = torch.empty((nb, c["L"] + 1), dtype=torch.int32, device=dev)
+    phi = torch.empty((nb, cap, 2), dtype=torch.int32, device=dev)
+    route_row = torch.empty_like(rt)
+    ws = torch.empty(ops.workspace_bytes(d, ops.MOE_OP_SCHEDULE), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        ops.moe_schedule(d, rt, counts, seg_off, phi, route_row, ws)
+    reps = max(10, args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        ops.moe_schedule(d, rt, counts, seg_off, phi, route_row, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    routes = nb * c["P"] * c["Np"] * c["K"]
+    npad = seg_off[:, -1].to(torch.int64).sum().item()
+    compulsory = routes * 4 + routes * 4 + npad * 8  # read ids, write route_row, write the table
+    return dict(nb=nb, routing=kind, ms=ms, routes_per_s=routes / (ms / 1e3),
+                compulsory_bytes=compulsory, gbs=compulsory / (ms / 1e3) / 1e9,
+                hbm_frac=compulsory / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, routes=r)
+
+
+def cpu_baseline(L_res, torch, oracle, budget_s: float):
+    """The oracle's per-token forward on a bounded sample of tokens."""
+    c = KIMI
+    h = L_res["h"]
+    ntok = c["P"] * c["Np"]
+    rng = np.random.default_rng(0)
+    # host copies (bf16 bit patterns) of what the oracle reads
+    X = h["X"].view(torch.int16).cpu().numpy().view(np.uint16)
+    W13 = h["W13"].view(torch.int16).cpu().numpy().view(np.uint16)
+    W2 = h["W2"].view(torch.int16).cpu().numpy().view(np.uint16)
+    routes, w = h["routes"], h["w"]
+    # calibrate on a few tokens, then size the sample to about budget_s seconds
+    n = 16
+    t0 = time.perf_counter()
+    oracle.layer_fwd_tokens(routes, w, X, W13, W2, L=c["L"], tokens=rng.choice(ntok, n, replace=False))
+    t1 = time.perf_counter() - t0
+    n = int(min(ntok, max(32, n * budget_s / max(t1, 1e-3))))
+    toks = np.sort(rng.choice(ntok, n, replace=False))
+    t0 = time.perf_counter()
+    oracle.layer_fwd_tokens(routes, w, X, W13, W2, L=c["L"], tokens=toks)
+    dt = time.perf_counter() - t0
+    local = int(((routes.reshape(-1, c["K"])[toks] >= 0) & (routes.reshape(-1, c["K"])[toks] < c["L"])).sum())
+    flops = 6.0 * c["H"] * c["I"] * local
+    # schedule oracle (serial plain definition) on one routing tensor
+    t0 = time.perf_counter()
+    oracle.schedule(routes, c["L"], 0, 256)
+    ts = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"layer forward of {n} of {ntok} tokens ({local} local routes, 6*H*I flop each) "
+                      f"in {dt:.1f} s, fp64 C with OpenMP",
+            "schedule_routes_per_s": c["P"] * c["Np"] * c["K"] / ts,
+            "schedule_sample": "one 458,752-route table, serial plain definition"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--persistent", action="store_true", help="time the persistent single-launch forward")
+    ap.add_argument("--chunk-rows", type=int, default=0, help="minibatch of dispatched rows (multiple of 256)")
+    ap.add_argument("--sched-batches", type=int, default=64)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-schedule", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} (world size {world}) is not "
+              "supported: this build has no multi-GPU path (nothing is sent between GPUs).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import oracle
+    from routing_schedule_expert_amd import inputs, ops
+
+    ops.load()
+    dev = torch.device("cuda:0")
+    print("[bench] layer forward, Kimi shape", file=sys.stderr, flush=True)
+    L_res = bench_layer(args, torch, ops, inputs, dev)
+    ms = L_res["ms_step"]
+    value = L_res["flops"] / (ms / 1e3) / 1e12
+    st = L_res["stage_ms"]
+    k_main = "ffn_gateup" if "ffn_gateup" in st else None
+    roofline = None
+    if k_main:
+        ach = L_res["flops_gateup"] / (st[k_main] / 1e3) / 1e12
+        roofline = {"bound": "mfma", "kernel": k_main, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic(k_main, 1),
+                    "algorithmic_flop_per_launch": L_res["flops_gateup"], "avg_launch_ms": st[k_main]}
+    down = None
+    if "ffn_down" in st:
+        ach = L_res["flops_down"] / (st["ffn_down"] / 1e3) / 1e12
+        down = {"achieved": ach, "frac": ach / PEAK_BF16_TFLOPS, "avg_launch_ms": st["ffn_down"]}
+    sched = None
+    if not args.no_schedule:
+        print("[bench] schedule only, 64 routing tensors per call", file=sys.stderr, flush=True)
+        s64 = bench_schedule(args, torch, ops, inputs, dev, args.sched_batches)
+        s1 = bench_schedule(args, torch, ops, inputs, dev, 1)
+        sched = {"nb": s64["nb"], "routing": "uniform", "routes_per_s": s64["routes_per_s"], "ms": s64["ms"],
+                 "achieved_GBs": s64["gbs"], "peak_GBs": PEAK_HBM_GBS, "frac": s64["hbm_frac"],
+                 "compulsory_bytes_per_call": s64["compulsory_bytes"],
+                 "nb1_ms": s1["ms"], "nb1_routes_per_s": s1["routes_per_s"],
+                 "share_of_layer_nb1": s1["ms"] / ms}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(L_res, torch, oracle, args.cpu_budget)
+    c = KIMI
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "kimi_local_share_fwd", "P": c["P"], "tokens_per_partition": c["Np"],
+                   "experts": c["E"], "local_experts": c["L"], "top_k": c["K"], "H": c["H"], "I": c["I"],
+                   "routing": "balanced", "pad_rows": 256, "dispatched_rows": L_res["npad"],
+                   "local_routes": L_res["local_routes"], "path": "persistent" if args.persistent else "multi-launch",
+                   "chunk_rows": args.chunk_rows},
+        "mfma_util_from_time": value / PEAK_BF16_TFLOPS,
+        "stage_ms": st,
+        "roofline": roofline,
+        "ffn_down": down,
+        "schedule": sched,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -216,6 +216,289 @@ __device__ __forceinline__ void gemm_mainloop(const KOp &ak, const MNOp &amn, co
 }
 
 // ---------------------------------------------------------------------------
+// Deep pipeline for the forward (both operands K-contiguous): NST stages of
+// BKT-deep [256][BKT] A and B tiles, DMA issued NST-1 steps ahead.  Each step
+// waits only for its own stage (s_waitcnt vmcnt(G*(NST-2)), G = DMA
+// instructions per wave per stage; vector memory operations complete in
+// order) and then meets the other waves at a plain s_barrier, so the loads of
+// the next NST-2 stages stay in flight across the barrier.
+// ---------------------------------------------------------------------------
+
+// Byte offset of 16-byte chunk kc (of BKT/8) of row `row` in a [256][BKT]
+// tile.  SW selects the swizzle:
+//   SW = 0   XOR the chunk with a function of the row inside its own row
+//            (row%8 for BKT=64, (row/2)%4 for BKT=32);
+//   SW = 3   "window" swizzle: the rows sharing one 256-byte span (2 rows of
+//            128 B or 4 rows of 64 B) form 16 slots of 16 bytes, and the slot
+//            index is XOR-ed with the span index.  A ds_read_b128 phase of 16
+//            lanes (16 consecutive rows, one chunk) then hits 16 distinct
+//            slots of the 256-byte bank window.
+template <int BKT, int SW>
+__device__ __forceinline__ uint32_t tile_off_t(int row, int kc) {
+    constexpr int cpr = BKT / 8;          // chunks per row
+    constexpr int rps = 16 / cpr;         // rows per 256-byte span
+    if constexpr (SW == 3) {
+        const int span = row / rps;
+        const int slot = (((row % rps) * cpr) | kc) ^ (span & 15);
+        return (uint32_t)(span * 256 + slot * 16);
+    } else if constexpr (BKT == 64) {
+        return (uint32_t)(row * 128 + ((kc ^ (row & 7)) << 4));
+    } else {
+        const int x = SW == 0 ? ((row >> 1) & 3) : SW == 1 ? ((row >> 2) & 3) : (row & 3);
+        return (uint32_t)(row * 64 + ((kc ^ x) << 4));
+    }
+}
+
+// Inverse of tile_off_t for a physical 16-byte slot: the (row, chunk) whose
+// data belongs at physical byte offset `off` of the tile.
+template <int BKT, int SW>
+__device__ __forceinline__ void tile_slot_owner(int off, int &row, int &kc) {
+    constexpr int cpr = BKT / 8;
+    constexpr int rps = 16 / cpr;
+    if constexpr (SW == 3) {
+        const int span = off >> 8;
+        const int logical = ((off >> 4) & 15) ^ (span & 15);
+        row = span * rps + logical / cpr;
+        kc = logical % cpr;
+    } else {
+        row = off / (BKT * 2);
+        const int pc = (off >> 4) % cpr;
+        if constexpr (BKT == 64) {
+            kc = pc ^ (row & 7);
+        } else {
+            const int x = SW == 0 ? ((row >> 1) & 3) : SW == 1 ? ((row >> 2) & 3) : (row & 3);
+            kc = pc ^ x;
+        }
+    }
+}
+
+// One K-contiguous [256][BKT] tile by DMA: each wave's i-th instruction fills
+// a contiguous 1 KiB block, lane L writing physical bytes [16L, 16L+16); the
+// lane fetches the (row, chunk) the swizzle places there.
+template <int BKT, int SW>
+__device__ __forceinline__ void dma_k_t(const KOp &op, int k0, char *tile) {
+    constexpr int blks_per_wave = 256 * BKT * 2 / 1024 / 4;
+    const int t = threadIdx.x, w = t >> 6, L = t & 63;
+#pragma unroll
+    for (int i = 0; i < blks_per_wave; ++i) {
+        const int blk = w * blks_per_wave + i;
+        int row, kc;
+        tile_slot_owner<BKT, SW>(blk * 1024 + L * 16, row, kc);
+        const uint16_t *p = (row < 128 ? op.lo : op.hi) + (int64_t)(row & 127) * op.ld + k0 + kc * 8;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(p), (lds_void_t *)(tile + blk * 1024), 16, 0,
+                                         0);
+    }
+}
+
+template <int BKT, int SW>
+__device__ __forceinline__ void load_frags_t(const char *stage, int s, int arow, const int (&brow)[4], int lane,
+                                             bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+    constexpr int tile_bytes = 256 * BKT * 2;
+    const int kc = 2 * s + (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+        fa[mi] = *reinterpret_cast<const bf16x8 *>(stage + tile_off_t<BKT, SW>(arow + mi * 32, kc));
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+        fb[ni] = *reinterpret_cast<const bf16x8 *>(stage + tile_bytes + tile_off_t<BKT, SW>(brow[ni], kc));
+}
+
+// One stage of BKT/16 sub-steps.  IL = 1 software-pipelines the fragment
+// reads: the 8 ds_reads of sub-step s+1 are interleaved one-for-one with the
+// first 8 of the 16 MFMAs of sub-step s (sched_group_barrier).
+template <int BKT, int SW, int IL>
+__device__ __forceinline__ void compute_stage_t(const char *stage, int arow, const int (&brow)[4], int lane,
+                                                f32x16 (&acc)[4][4]) {
+    constexpr int S = BKT / 16;
+    if constexpr (IL == 0) {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            bf16x8 fa[4], fb[4];
+            load_frags_t<BKT, SW>(stage, s, arow, brow, lane, fa, fb);
+            mfma_block(fa, fb, acc);
+        }
+    } else {
+        bf16x8 fa[2][4], fb[2][4];
+        load_frags_t<BKT, SW>(stage, 0, arow, brow, lane, fa[0], fb[0]);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            if (s + 1 < S) load_frags_t<BKT, SW>(stage, s + 1, arow, brow, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+            mfma_block(fa[s & 1], fb[s & 1], acc);
+            if (s + 1 < S) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 DS read
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            }
+        }
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int BKT, int NST, int SW, int IL = 0>
+__device__ __forceinline__ void gemm_mainloop_deep(const KOp &ak, const KOp &bk, int nk, bool swiglu, char *lds,
+                                                   f32x16 (&acc)[4][4]) {
+    constexpr int tile_bytes = 256 * BKT * 2;
+    constexpr int stage_bytes = 2 * tile_bytes;
+    constexpr int G = 2 * (256 * BKT * 2 / 1024) / 4;  // DMA instructions per wave per stage
+    static_assert(NST >= 2 && NST * stage_bytes <= kGemmLds, "LDS budget");
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+    if (nk <= 0) return;
+    int brow[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) brow[ni] = b_block_row(swiglu, wn, ni) + (lane & 31);
+    const int arow = wm * 128 + (lane & 31);
+    __syncthreads();  // the previous tile's epilogue may still read LDS
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+        if (s < nk) {
+            dma_k_t<BKT, SW>(ak, s * BKT, lds + s * stage_bytes);
+            dma_k_t<BKT, SW>(bk, s * BKT, lds + s * stage_bytes + tile_bytes);
+        }
+    int slot = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + NST - 2 < nk) wait_vm_barrier<G * (NST - 2)>();
+        else wait_vm_barrier<0>();
+        const int ahead = kt + NST - 1;
+        if (ahead < nk) {
+            int as = slot + NST - 1;
+            if (as >= NST) as -= NST;
+            dma_k_t<BKT, SW>(ak, ahead * BKT, lds + as * stage_bytes);
+            dma_k_t<BKT, SW>(bk, ahead * BKT, lds + as * stage_bytes + tile_bytes);
+        }
+        compute_stage_t<BKT, SW, IL>(lds + slot * stage_bytes, arow, brow, lane, acc);
+        if (++slot == NST) slot = 0;
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Wave-grid generalisation: a 256 x 256 tile computed by WM x WN waves, each
+// owning (256/WM) x (256/WN) outputs = MI x NI blocks of 32 x 32.  With 8
+// waves (two per SIMD) one wave's MFMAs cover the other's LDS waits.
+// ---------------------------------------------------------------------------
+template <int WM, int WN>
+struct WaveGrid {
+    static constexpr int NW = WM * WN;
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int MI = 256 / WM / 32;
+    static constexpr int NI = 256 / WN / 32;
+    // B-tile row of block ni for wave column wn.  SwiGLU: rows [0,128) hold
+    // gate columns and [128,256) the matching up columns; each wave takes
+    // NI/2 gate blocks and the same NI/2 up blocks.
+    static __device__ __forceinline__ int brow(bool swiglu, int wn, int ni) {
+        if (swiglu) {
+            constexpr int half = NI / 2;
+            return (ni / half) * 128 + wn * (half * 32) + (ni % half) * 32;
+        }
+        return wn * (NI * 32) + ni * 32;
+    }
+    static __device__ __forceinline__ int row(int wm, int mi, int e, int lane) {
+        return wm * (MI * 32) + mi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+    }
+};
+
+template <int WM, int WN>
+using AccW = f32x16[WaveGrid<WM, WN>::MI][WaveGrid<WM, WN>::NI];
+
+template <int BKT, int SW, int NW>
+__device__ __forceinline__ void dma_k_w(const KOp &op, int k0, char *tile) {
+    constexpr int blks_per_wave = 256 * BKT * 2 / 1024 / NW;
+    const int t = threadIdx.x, w = t >> 6, L = t & 63;
+#pragma unroll
+    for (int i = 0; i < blks_per_wave; ++i) {
+        const int blk = w * blks_per_wave + i;
+        int row, kc;
+        tile_slot_owner<BKT, SW>(blk * 1024 + L * 16, row, kc);
+        const uint16_t *p = (row < 128 ? op.lo : op.hi) + (int64_t)(row & 127) * op.ld + k0 + kc * 8;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(p), (lds_void_t *)(tile + blk * 1024), 16, 0,
+                                         0);
+    }
+}
+
+template <int BKT, int SW, int MI, int NI>
+__device__ __forceinline__ void compute_stage_w(const char *stage, int arow, const int (&brow)[NI], int lane,
+                                                f32x16 (&acc)[MI][NI]) {
+    constexpr int tile_bytes = 256 * BKT * 2;
+#pragma unroll
+    for (int s = 0; s < BKT / 16; ++s) {
+        const int kc = 2 * s + (lane >> 5);
+        bf16x8 fa[MI], fb[NI];
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+            fa[mi] = *reinterpret_cast<const bf16x8 *>(stage + tile_off_t<BKT, SW>(arow + mi * 32, kc));
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+            fb[ni] = *reinterpret_cast<const bf16x8 *>(stage + tile_bytes + tile_off_t<BKT, SW>(brow[ni], kc));
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+    }
+}
+
+template <int WM, int WN, int BKT, int NST, int SW, int LDS_BYTES = kGemmLds>
+__device__ __forceinline__ void gemm_mainloop_w(const KOp &ak, const KOp &bk, int nk, bool swiglu, char *lds,
+                                                AccW<WM, WN> &acc) {
+    using WG = WaveGrid<WM, WN>;
+    constexpr int MI = WG::MI, NI = WG::NI;
+    constexpr int tile_bytes = 256 * BKT * 2;
+    constexpr int stage_bytes = 2 * tile_bytes;
+    constexpr int G = 2 * (tile_bytes / 1024) / WG::NW;  // DMA instructions per wave per stage
+    static_assert(NST >= 2 && NST * stage_bytes <= LDS_BYTES, "LDS budget");
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+    if (nk <= 0) return;
+    int brow[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) brow[ni] = WG::brow(swiglu, wn, ni) + (lane & 31);
+    const int arow = wm * (MI * 32) + (lane & 31);
+    __syncthreads();  // the previous tile's epilogue may still read LDS
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+        if (s < nk) {
+            dma_k_w<BKT, SW, WG::NW>(ak, s * BKT, lds + s * stage_bytes);
+            dma_k_w<BKT, SW, WG::NW>(bk, s * BKT, lds + s * stage_bytes + tile_bytes);
+        }
+    int slot = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+        if (kt + NST - 2 < nk) wait_vm_barrier<G * (NST - 2)>();
+        else wait_vm_barrier<0>();
+        const int ahead = kt + NST - 1;
+        if (ahead < nk) {
+            int as = slot + NST - 1;
+            if (as >= NST) as -= NST;
+            dma_k_w<BKT, SW, WG::NW>(ak, ahead * BKT, lds + as * stage_bytes);
+            dma_k_w<BKT, SW, WG::NW>(bk, ahead * BKT, lds + as * stage_bytes + tile_bytes);
+        }
+        compute_stage_w<BKT, SW, MI, NI>(lds + slot * stage_bytes, arow, brow, lane, acc);
+        if (++slot == NST) slot = 0;
+    }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
 // Tile ordering.
 // ---------------------------------------------------------------------------
 
@@ -281,7 +564,7 @@ __device__ __forceinline__ void flush_tile(const char *lds, int off, uint16_t *d
     }
 }
 
-__device__ __forceinline__ float silu_f(float h) { return h / (1.0f + __expf(-h)); }
+__device__ __forceinline__ float silu_f(float h) { return h * __builtin_amdgcn_rcpf(1.0f + __expf(-h)); }
 
 // Gate/up tile -> A = silu(gate) * up (256 x 128), optional HU (gate and up).
 __device__ __forceinline__ void epilogue_swiglu(f32x16 (&acc)[4][4], char *lds, uint16_t *Aout, int64_t ldA,
@@ -333,6 +616,90 @@ __device__ __forceinline__ void epilogue_store_bf16(f32x16 (&acc)[4][4], char *l
     }
     __syncthreads();
     flush_tile<256>(lds, 0, dst, ld, nvalid);
+}
+
+// Staging for a WM x WN wave grid: wave (wm, wn) writes rows
+// [wm*256/WM, (wm+1)*256/WM), all inside one 128-row half of the staging tile.
+template <int NC, int WM>
+struct LaneStageW {
+    char *base;
+    __device__ __forceinline__ LaneStageW(char *lds, int off, int wm, int lane, int col0) {
+        constexpr int rows_per_wave = 256 / WM;
+        const int r0 = wm * rows_per_wave;
+        base = lds + (r0 >> 7) * kStageBytes + off + (((r0 & 127) + 4 * (lane >> 5)) * NC + col0 + (lane & 31)) * 2;
+    }
+    __device__ __forceinline__ void put(int mi, int e, int c, float v) const {
+        *reinterpret_cast<uint16_t *>(base + ((mi * 32 + 8 * (e >> 2) + (e & 3)) * NC + c) * 2) = f2bf(v);
+    }
+};
+
+template <int WM, int WN>
+__device__ __forceinline__ void epilogue_swiglu_w(AccW<WM, WN> &acc, char *lds, uint16_t *Aout, int64_t ldA, uint16_t *HUg, uint16_t *HUu,
+                                                  int64_t ldHU) {
+    using WG = WaveGrid<WM, WN>;
+    constexpr int MI = WG::MI, half = WG::NI / 2;
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63, wm = wave / WN, wn = wave % WN;
+    const LaneStageW<128, WM> sa(lds, 0, wm, lane, wn * half * 32), sg(lds, 32768, wm, lane, wn * half * 32);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < half; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float h = acc[mi][ni][e], u = acc[mi][ni + half][e];
+                sa.put(mi, e, ni * 32, silu_f(h) * u);
+                if (HUg) sg.put(mi, e, ni * 32, h);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < 256 * 16; c += WG::THREADS) {
+        const int row = c >> 4, cc = (c & 15) * 8;
+        const char *src = lds + (row >> 7) * kStageBytes + ((row & 127) * 128 + cc) * 2;
+        *reinterpret_cast<u32x4 *>(Aout + (int64_t)row * ldA + cc) = *reinterpret_cast<const u32x4 *>(src);
+        if (HUg)
+            *reinterpret_cast<u32x4 *>(HUg + (int64_t)row * ldHU + cc) =
+                *reinterpret_cast<const u32x4 *>(src + 32768);
+    }
+    if (HUg) {
+        __syncthreads();
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+            for (int ni = 0; ni < half; ++ni)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sa.put(mi, e, ni * 32, acc[mi][ni + half][e]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < 256 * 16; c += WG::THREADS) {
+            const int row = c >> 4, cc = (c & 15) * 8;
+            const char *src = lds + (row >> 7) * kStageBytes + ((row & 127) * 128 + cc) * 2;
+            *reinterpret_cast<u32x4 *>(HUu + (int64_t)row * ldHU + cc) = *reinterpret_cast<const u32x4 *>(src);
+        }
+    }
+}
+
+template <int WM, int WN>
+__device__ __forceinline__ void epilogue_store_bf16_w(AccW<WM, WN> &acc, char *lds, uint16_t *dst, int64_t ld, int nvalid) {
+    using WG = WaveGrid<WM, WN>;
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63, wm = wave / WN, wn = wave % WN;
+    const LaneStageW<256, WM> sg(lds, 0, wm, lane, wn * WG::NI * 32);
+#pragma unroll
+    for (int mi = 0; mi < WG::MI; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < WG::NI; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sg.put(mi, e, ni * 32, acc[mi][ni][e]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < 256 * 32; c += WG::THREADS) {
+        const int row = c >> 5, cc = (c & 31) * 8;
+        const char *src = lds + (row >> 7) * kStageBytes + ((row & 127) * 256 + cc) * 2;
+        if (cc < nvalid)
+            *reinterpret_cast<u32x4 *>(dst + (int64_t)row * ld + cc) = *reinterpret_cast<const u32x4 *>(src);
+    }
 }
 
 // fp32 store of a 256 x 256 tile (rows < mvalid, columns < nvalid).

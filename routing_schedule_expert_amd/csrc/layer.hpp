@@ -25,6 +25,11 @@
 
 namespace moe {
 
+// Forward GEMM configuration: 8 waves (4 x 2, two per SIMD) on a 256 x 256
+// tile, 64-deep steps double buffered by DMA, window-swizzled LDS.
+constexpr int kFwdWM = 4, kFwdWN = 2;
+constexpr int kFwdThreads = 64 * kFwdWM * kFwdWN;
+
 struct FfnArgs {
     const uint16_t *Xd, *W13, *W2;
     const int32_t *seg_off;
@@ -42,11 +47,11 @@ __device__ __forceinline__ void ffn_gateup_tile(const FfnArgs &a, int mt, int nt
     const uint16_t *w = a.W13 + (int64_t)l * 2 * I * H;
     KOp ak{xa, xa + 128ll * H, H};
     KOp bk{w + (int64_t)nt * 128 * H, w + ((int64_t)I + nt * 128) * H, H};
-    f32x16 acc[4][4];
-    gemm_mainloop<true, true>(ak, MNOp{}, bk, MNOp{}, H / kBK, true, lds, acc);
+    AccW<kFwdWM, kFwdWN> acc;
+    gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, H / 64, true, lds, acc);
     uint16_t *hu = a.HU ? a.HU + (int64_t)m0 * 2 * I : nullptr;
-    epilogue_swiglu(acc, lds, a.A + (int64_t)m0 * I + nt * 128, I, hu ? hu + nt * 128 : nullptr,
-                    hu ? hu + I + nt * 128 : nullptr, 2ll * I);
+    epilogue_swiglu_w<kFwdWM, kFwdWN>(acc, lds, a.A + (int64_t)m0 * I + nt * 128, I, hu ? hu + nt * 128 : nullptr,
+                                      hu ? hu + I + nt * 128 : nullptr, 2ll * I);
 }
 
 __device__ __forceinline__ void ffn_down_tile(const FfnArgs &a, int mt, int nt, char *lds) {
@@ -57,9 +62,9 @@ __device__ __forceinline__ void ffn_down_tile(const FfnArgs &a, int mt, int nt, 
     const uint16_t *w = a.W2 + (int64_t)l * H * I + (int64_t)nt * 256 * I;
     KOp ak{aa, aa + 128ll * I, I};
     KOp bk{w, w + 128ll * I, I};
-    f32x16 acc[4][4];
-    gemm_mainloop<true, true>(ak, MNOp{}, bk, MNOp{}, I / kBK, false, lds, acc);
-    epilogue_store_bf16(acc, lds, a.Y + (int64_t)m0 * H + nt * 256, H, 256);
+    AccW<kFwdWM, kFwdWN> acc;
+    gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, I / 64, false, lds, acc);
+    epilogue_store_bf16_w<kFwdWM, kFwdWN>(acc, lds, a.Y + (int64_t)m0 * H + nt * 256, H, 256);
 }
 
 // One persistent pass over the tiles of rows [r0, r1) (multiples of 256).
@@ -134,9 +139,11 @@ __device__ __forceinline__ void layer_fwd_persistent_body(const LayerFwdArgs &a,
     int32_t *smem = reinterpret_cast<int32_t *>(lds);
     for (int x = blockIdx.x; x < nitems; x += gridDim.x) sched_count_body(s, smem, x);
     grid_barrier(a.ffn.bar, gridDim.x);
+    if (blockIdx.x == 0) sched_finalize(s, 0, smem);
+    grid_barrier(a.ffn.bar, gridDim.x);
     for (int x = blockIdx.x; x < nitems; x += gridDim.x) sched_scatter_body(s, smem, x);
     grid_barrier(a.ffn.bar, gridDim.x);
-    const int waves = kGemmThreads / kWave;
+    const int waves = blockDim.x / kWave;
     gather_rows_body(a.X, s.phi, s.seg_off + s.L, const_cast<uint16_t *>(a.ffn.Xd), a.Np, a.ffn.H, 0, a.cap,
                      blockIdx.x * waves + threadIdx.x / kWave, gridDim.x * waves);
     grid_barrier(a.ffn.bar, gridDim.x);

@@ -31,6 +31,11 @@ __global__ __launch_bounds__(256) void k_sched_count(SchedArgs a) {
     sched_count_body(a, sched_smem, blockIdx.x);
 }
 
+__global__ __launch_bounds__(256) void k_sched_finalize(SchedArgs a) {
+    extern __shared__ int32_t sched_smem[];
+    sched_finalize(a, blockIdx.x, sched_smem);
+}
+
 __global__ __launch_bounds__(256) void k_sched_scatter(SchedArgs a) {
     extern __shared__ int32_t sched_smem[];
     sched_scatter_body(a, sched_smem, blockIdx.x);
@@ -63,22 +68,22 @@ __global__ __launch_bounds__(256) void k_dw_finalize(const int32_t *route_row, c
         dw_finalize_body(route_row, part, nparts, dw, i);
 }
 
-__global__ __launch_bounds__(256) void k_ffn_gateup(FfnArgs a) {
+__global__ __launch_bounds__(kFwdThreads) void k_ffn_gateup(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
     ffn_gateup_phase(a, 0, a.seg_off[a.L], lds);
 }
 
-__global__ __launch_bounds__(256) void k_ffn_down(FfnArgs a) {
+__global__ __launch_bounds__(kFwdThreads) void k_ffn_down(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
     ffn_down_phase(a, 0, a.seg_off[a.L], lds);
 }
 
-__global__ __launch_bounds__(256) void k_ffn_chunked(FfnArgs a) {
+__global__ __launch_bounds__(kFwdThreads) void k_ffn_chunked(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
     ffn_chunked_body(a, lds);
 }
 
-__global__ __launch_bounds__(256) void k_layer_fwd_persistent(LayerFwdArgs a) {
+__global__ __launch_bounds__(kFwdThreads) void k_layer_fwd_persistent(LayerFwdArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
     layer_fwd_persistent_body(a, lds);
 }
@@ -179,9 +184,7 @@ int sched_wg_per_part(const moe_desc *d) { return (sched_chunks(d) + kSchedWaves
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
-int64_t sched_ws_bytes(const moe_desc *d) {
-    return align256(4ll * d->num_batches) + 4ll * d->num_batches * d->P * sched_chunks(d) * d->L;
-}
+int64_t sched_ws_bytes(const moe_desc *d) { return align256(4ll * d->num_batches * d->P * sched_chunks(d) * d->L); }
 
 int bwd_nparts(const moe_desc *d) { return 2 * ((d->I + 255) / 256); }
 
@@ -195,16 +198,14 @@ constexpr int64_t kBarrierBytes = 256;
 
 int launch_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP; }
 
-int launch_schedule(const moe_desc *d, const int32_t *routes, int32_t *counts, int32_t *seg_off, moe_src *phi,
-                    int32_t *route_row, char *ws, hipStream_t s) {
-    SchedArgs a;
+void fill_sched_args(SchedArgs &a, const moe_desc *d, const int32_t *routes, int32_t *counts, int32_t *seg_off,
+                     moe_src *phi, int32_t *route_row, char *ws, int wpw) {
     a.routes = routes;
     a.counts = counts;
     a.seg_off = seg_off;
     a.phi = phi;
     a.route_row = route_row;
-    a.arrive = reinterpret_cast<uint32_t *>(ws);
-    a.wcnt = reinterpret_cast<int32_t *>(ws + align256(4ll * d->num_batches));
+    a.wcnt = reinterpret_cast<int32_t *>(ws);
     a.P = d->P;
     a.R = d->Np * d->K;
     a.K = d->K;
@@ -213,26 +214,39 @@ int launch_schedule(const moe_desc *d, const int32_t *routes, int32_t *counts, i
     a.pad = d->pad_rows;
     a.nb = d->num_batches;
     a.W = sched_chunks(d);
-    a.wg_per_part = sched_wg_per_part(d);
+    a.wpw = wpw;
+    a.wg_per_part = (a.W + wpw - 1) / wpw;
     a.nbits = 32 - __builtin_clz((unsigned)d->L | 1u);
     a.cap = cap_rows(d);
+}
+
+// LDS (bytes) of the schedule bodies for `wpw` waves per workgroup.
+size_t sched_lds_bytes(const moe_desc *d, int wpw) {
+    const size_t L = d->L, P = d->P;
+    size_t count = wpw * (L + 1), fin = P * L + L + 16, scat = L * P + L + 1 + wpw * L;
+    return 4 * std::max(count, std::max(fin, scat));
+}
+
+int launch_schedule(const moe_desc *d, const int32_t *routes, int32_t *counts, int32_t *seg_off, moe_src *phi,
+                    int32_t *route_row, char *ws, hipStream_t s) {
+    SchedArgs a;
+    fill_sched_args(a, d, routes, counts, seg_off, phi, route_row, ws, kSchedWaves);
     const int wg_per_batch = a.P * a.wg_per_part;
     const int grid = a.nb >= 8 ? 8 * ((a.nb + 7) / 8) * wg_per_batch : a.nb * wg_per_batch;
-    const size_t lds_count = 4 * (size_t)std::max(kSchedWaves * (a.L + 1), a.P * a.L + a.L + 256);
-    const size_t lds_scatter = 4 * (size_t)(a.L * a.P + a.L + 1 + kSchedWaves * a.L);
+    const size_t lds = sched_lds_bytes(d, kSchedWaves);
     {
-        TraceScope tr("sched_zero", s);
-        hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(256), 0, s, a.arrive, (int64_t)a.nb);
+        TraceScope tr("sched_count", s);
+        hipLaunchKernelGGL(k_sched_count, dim3(grid), dim3(64 * kSchedWaves), lds, s, a);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
     {
-        TraceScope tr("sched_count", s);
-        hipLaunchKernelGGL(k_sched_count, dim3(grid), dim3(256), lds_count, s, a);
+        TraceScope tr("sched_finalize", s);
+        hipLaunchKernelGGL(k_sched_finalize, dim3(a.nb), dim3(256), lds, s, a);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
     {
         TraceScope tr("sched_scatter", s);
-        hipLaunchKernelGGL(k_sched_scatter, dim3(grid), dim3(256), lds_scatter, s, a);
+        hipLaunchKernelGGL(k_sched_scatter, dim3(grid), dim3(64 * kSchedWaves), lds, s, a);
     }
     return launch_status();
 }
@@ -275,7 +289,7 @@ FfnArgs make_ffn_args(const moe_desc *d, const uint16_t *Xd, const uint16_t *W13
 }
 
 int launch_cooperative(const void *fn, int grid, void **args, hipStream_t s) {
-    hipError_t e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kGemmThreads), args, 0, s);
+    hipError_t e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kFwdThreads), args, 0, s);
     return e == hipSuccess ? MOE_OK : MOE_EHIP;
 }
 
@@ -284,11 +298,11 @@ int launch_ffn(const moe_desc *d, const FfnArgs &a, hipStream_t s) {
     if (a.chunk_rows <= 0) {
         {
             TraceScope tr("ffn_gateup", s);
-            hipLaunchKernelGGL(k_ffn_gateup, dim3(grid), dim3(kGemmThreads), 0, s, a);
+            hipLaunchKernelGGL(k_ffn_gateup, dim3(grid), dim3(kFwdThreads), 0, s, a);
         }
         if (launch_status() != MOE_OK) return MOE_EHIP;
         TraceScope tr("ffn_down", s);
-        hipLaunchKernelGGL(k_ffn_down, dim3(grid), dim3(kGemmThreads), 0, s, a);
+        hipLaunchKernelGGL(k_ffn_down, dim3(grid), dim3(kFwdThreads), 0, s, a);
         return launch_status();
     }
     {
@@ -418,25 +432,10 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
     char *sched_ws = wsb + kBarrierBytes;
     if (flags & MOE_PERSISTENT) {
         LayerFwdArgs la;
-        SchedArgs &sa = la.sched;
-        sa.routes = routes;
-        sa.counts = counts;
-        sa.seg_off = seg_off;
-        sa.phi = phi;
-        sa.route_row = route_row;
-        sa.arrive = reinterpret_cast<uint32_t *>(sched_ws);
-        sa.wcnt = reinterpret_cast<int32_t *>(sched_ws + align256(4));
-        sa.P = d->P;
-        sa.R = d->Np * d->K;
-        sa.K = d->K;
-        sa.L = d->L;
-        sa.base = d->expert_base;
-        sa.pad = d->pad_rows;
-        sa.nb = 1;
-        sa.W = sched_chunks(d);
-        sa.wg_per_part = sched_wg_per_part(d);
-        sa.nbits = 32 - __builtin_clz((unsigned)d->L | 1u);
-        sa.cap = cap_rows(d);
+        moe_desc one = *d;
+        one.num_batches = 1;
+        if (sched_lds_bytes(&one, kFwdThreads / 64) > (size_t)kGemmLds) return MOE_EUNSUPPORTED;
+        fill_sched_args(la.sched, &one, routes, counts, seg_off, phi, route_row, sched_ws, kFwdThreads / 64);
         la.ffn = make_ffn_args(d, Xd, W13, W2, seg_off, HU, A, Y, chunk_rows, bar);
         la.X = X;
         la.w = w;
@@ -448,12 +447,6 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
         {
             TraceScope tr("layer_zero", s);
             hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, bar, (int64_t)(kBarrierBytes / 4));
-        }
-        if (launch_status() != MOE_OK) return MOE_EHIP;
-        // the persistent schedule stage counts with at most one arrival word
-        {
-            TraceScope tr("layer_sched_zero", s);
-            hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, sa.arrive, (int64_t)1);
         }
         if (launch_status() != MOE_OK) return MOE_EHIP;
         void *args[] = {&la};

@@ -16,9 +16,9 @@
 // holding the same local expert find each other with one ballot per bit of the
 // expert id, and a route's rank among them is a masked popcount, so the
 // ordinal o of every route is its index order with no atomics.  Per-wave
-// counters live in LDS.  The last workgroup to finish counting a batch (an
-// integer arrival counter) turns the per-wave counts into exclusive offsets,
-// the per-(expert, partition) counts M and the padded segment offsets S.
+// counters live in LDS.  A second pass (one workgroup per batch) turns the
+// per-wave counts into exclusive offsets, the per-(expert, partition) counts
+// M and the padded segment offsets S; a third places every route.
 #pragma once
 
 #include "common.hpp"
@@ -27,7 +27,7 @@ namespace moe {
 
 constexpr int kSchedUnroll = 16;                    // route loads in flight per lane
 constexpr int kSchedChunk = kWave * kSchedUnroll;   // routes per logical thread (wave)
-constexpr int kSchedWaves = 4;                      // waves per workgroup
+constexpr int kSchedWaves = 4;                      // waves per workgroup of the standalone kernels
 
 struct SchedArgs {
     const int32_t *routes;  // [nb][P][R]
@@ -36,8 +36,8 @@ struct SchedArgs {
     moe_src *phi;           // [nb][cap]
     int32_t *route_row;     // [nb][P][R]
     int32_t *wcnt;          // ws: [nb][P][W][L] counts, then exclusive offsets
-    uint32_t *arrive;       // ws: [nb] arrival counters (zero on entry)
     int32_t P, R, K, L, base, pad, nb, W, wg_per_part, nbits;
+    int32_t wpw;  // waves per workgroup (chunks handled by one workgroup)
     int64_t cap;
 };
 
@@ -68,14 +68,37 @@ __device__ __forceinline__ uint32_t local_id(int32_t e, int base, int L) {
     return l < (uint32_t)L ? l : (uint32_t)L;  // L = not local
 }
 
-// Block-wide exclusive scan of padded segment lengths -> seg_off (one batch).
-__device__ void sched_finalize(const SchedArgs &a, int b, int32_t *s_tot) {
+// Exclusive prefix sum over the threads of the workgroup, in thread order
+// (wave-level shuffles, then the per-wave totals through LDS).
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *tmp /* >= 16 ints */) {
+    const int lane = lane_id(), w = threadIdx.x >> 6;
+    int32_t x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int32_t y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
+    }
+    __syncthreads();
+    if (lane == kWave - 1) tmp[w] = x;
+    __syncthreads();
+    int32_t base = 0;
+    for (int i = 0; i < w; ++i) base += tmp[i];
+    return base + x - v;
+}
+
+// Stages 2 and 3 for batch b: per (partition, expert) exclusive prefix of the
+// per-chunk counts (in place), M[l][r], and the padded segment offsets S.
+// smem: P*L + L + 16 ints.
+__device__ void sched_finalize(const SchedArgs &a, int b, int32_t *smem) {
     const int L = a.L, P = a.P, W = a.W;
     int32_t *wc = a.wcnt + (int64_t)b * P * W * L;
     int32_t *cnt = a.counts + (int64_t)b * L * P;
-    // per (partition, expert): exclusive prefix over the partition's chunks
+    int32_t *s_tot = smem;          // [P][L]
+    int32_t *s_len = s_tot + P * L; // [L]
+    int32_t *s_tmp = s_len + L;     // [16]
+    __syncthreads();
     for (int pr = threadIdx.x; pr < P * L; pr += blockDim.x) {
-        int r = pr / L, l = pr % L;
+        const int r = pr / L, l = pr % L;
         int32_t *col = wc + (int64_t)r * W * L + l;
         int32_t acc = 0;
         int w = 0;
@@ -90,58 +113,43 @@ __device__ void sched_finalize(const SchedArgs &a, int b, int32_t *s_tot) {
             }
         }
         for (; w < W; ++w) {
-            int32_t v = col[(int64_t)w * L];
+            const int32_t v = col[(int64_t)w * L];
             col[(int64_t)w * L] = acc;
             acc += v;
         }
         cnt[l * P + r] = acc;
-        s_tot[pr] = acc;  // [r][l]
+        s_tot[pr] = acc;
     }
     __syncthreads();
-    // padded segment lengths, then a block scan over experts
-    int32_t *s_len = s_tot + P * L;  // [L]
     for (int l = threadIdx.x; l < L; l += blockDim.x) {
         int32_t t = 0;
         for (int r = 0; r < P; ++r) t += s_tot[r * L + l];
         s_len[l] = (t + a.pad - 1) / a.pad * a.pad;
     }
     __syncthreads();
-    // each thread sums a contiguous run of experts, then a serial pass over runs
-    int32_t *s_run = s_len + L;  // [blockDim.x]
+    // each thread owns a contiguous run of experts; scan the run sums
     const int per = (L + blockDim.x - 1) / blockDim.x;
-    int lo = threadIdx.x * per, hi = min(L, lo + per);
+    const int lo = min(L, (int)threadIdx.x * per), hi = min(L, lo + per);
     int32_t sum = 0;
     for (int l = lo; l < hi; ++l) sum += s_len[l];
-    s_run[threadIdx.x] = sum;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int32_t acc = 0;
-        for (int i = 0; i < (int)blockDim.x; ++i) {
-            int32_t v = s_run[i];
-            s_run[i] = acc;
-            acc += v;
-        }
-    }
-    __syncthreads();
+    int32_t acc = block_exclusive_scan(sum, s_tmp);
     int32_t *so = a.seg_off + (int64_t)b * (L + 1);
-    int32_t acc = s_run[threadIdx.x];
     for (int l = lo; l < hi; ++l) {
         so[l] = acc;
         acc += s_len[l];
     }
-    if (hi == L && lo < hi) so[L] = acc;
-    if (L == 0 && threadIdx.x == 0) so[0] = 0;
+    if (threadIdx.x == blockDim.x - 1) so[L] = acc;  // the last thread's run ends at L
 }
 
-// Stage 1 (+ stages 2 and 3 in the batch's last workgroup).  x is the
-// workgroup's index in the schedule grid (a persistent caller loops over it).
+// Stage 1: per-chunk counts.  x is the workgroup's index in the schedule grid
+// (a persistent caller loops over it).
 __device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
     int b, r, q;
     if (!sched_locate(a, x, b, r, q)) return;
     __syncthreads();  // LDS may still be in use by the caller's previous item
     const int lane = lane_id();
     const int wv = threadIdx.x / kWave;
-    const int w = q * kSchedWaves + wv;  // chunk (logical thread) index in the partition
+    const int w = q * a.wpw + wv;  // chunk (logical thread) index in the partition
     const int L = a.L;
     int32_t *cnt = smem + wv * (L + 1);
     for (int l = lane; l <= L; l += kWave) cnt[l] = 0;
@@ -168,19 +176,6 @@ __device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
         int32_t *dst = a.wcnt + (((int64_t)b * a.P + r) * a.W + w) * L;
         for (int l = lane; l < L; l += kWave) dst[l] = cnt[l];
     }
-    // arrival: the last workgroup of this batch finalises it
-    __shared__ uint32_t s_last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t n = __hip_atomic_fetch_add(a.arrive + b, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (n == (uint32_t)(a.P * a.wg_per_part - 1)) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (s_last) {
-        __threadfence();
-        sched_finalize(a, b, smem);
-    }
 }
 
 // Stage 4: scatter every route once.
@@ -190,7 +185,7 @@ __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
     __syncthreads();
     const int lane = lane_id();
     const int wv = threadIdx.x / kWave;
-    const int w = q * kSchedWaves + wv;
+    const int w = q * a.wpw + wv;
     const int L = a.L, P = a.P;
     // LDS: M [L][P], S [L+1], per-wave running offsets [4][L]
     int32_t *sM = smem;

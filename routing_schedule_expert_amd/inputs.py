@@ -31,10 +31,10 @@ def rng_for(seed: int) -> np.random.Generator:
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns, round to nearest even (NaN kept quiet)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
     nan = np.isnan(x)
+    # finite and infinite inputs cannot overflow 32 bits here (max 0xFF807FFF)
+    r = ((np.where(nan, np.uint32(0), u) + np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))) >> 16).astype(np.uint16)
     if nan.any():
         r[nan] = 0x7FC0
     return r
@@ -167,6 +167,36 @@ def make_layer_inputs(seed: int, P: int, Np: int, E: int, K: int, L: int, H: int
     d = {"routes": routes, "w": w, "X": X, "W13": W13, "W2": W2}
     if with_grad:
         d["dOut"] = normal_bf16(rng, (P, Np, H), x_std)
+    return d
+
+
+def normal_bf16_device(shape, std: float, seed: int, device):
+    """Seeded N(0, std^2) bf16 tensor drawn on the GPU (torch's Philox generator).
+
+    For the multi-GB weight tensors of the full-size configurations; the
+    oracle receives the same values by copying them back to the host."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    t.mul_(std)
+    return t.to(torch.bfloat16)
+
+
+def make_layer_inputs_device(seed: int, P: int, Np: int, E: int, K: int, L: int, H: int, I: int, device,
+                             routing: str = "balanced", base: int = 0, x_std: float = 1.0, w_std: float = 0.02,
+                             s: float = 1.2, with_grad: bool = False):
+    """Routes and router weights on the host (numpy PCG64), dense tensors drawn
+    on the device; returns host routes/w and device X, W13, W2 (and dOut)."""
+    rng = rng_for(seed)
+    routes, w = make_routes(routing, rng, P, Np, E, K, L, base, s)
+    d = {"routes": routes, "w": w,
+         "X": normal_bf16_device((P, Np, H), x_std, seed * 8 + 1, device),
+         "W13": normal_bf16_device((L, 2 * I, H), w_std, seed * 8 + 2, device),
+         "W2": normal_bf16_device((L, H, I), w_std, seed * 8 + 3, device)}
+    if with_grad:
+        d["dOut"] = normal_bf16_device((P, Np, H), x_std, seed * 8 + 4, device)
     return d
 
 
