@@ -126,10 +126,20 @@ def bench_schedule(args, torch, ops, inputs, dev, nb, kind="uniform"):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
+    # per-kernel split from events around each launch (a separate, traced pass)
+    ops.moe_trace_enable(reps * 4)
+    for _ in range(reps):
+        ops.moe_schedule(d, rt, counts, seg_off, phi, route_row, ws)
+    torch.cuda.synchronize()
+    split = {}
+    for name, t in ops.moe_trace_read(reps * 4):
+        split.setdefault(name, []).append(t)
+    ops.moe_trace_enable(0)
+    split = {k: float(np.mean(v)) for k, v in split.items()}
     routes = nb * c["P"] * c["Np"] * c["K"]
     npad = seg_off[:, -1].to(torch.int64).sum().item()
     compulsory = routes * 4 + routes * 4 + npad * 8  # read ids, write route_row, write the table
-    return dict(nb=nb, routing=kind, ms=ms, routes_per_s=routes / (ms / 1e3),
+    return dict(nb=nb, routing=kind, ms=ms, split_ms=split, routes_per_s=routes / (ms / 1e3),
                 compulsory_bytes=compulsory, gbs=compulsory / (ms / 1e3) / 1e9,
                 hbm_frac=compulsory / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, routes=r)
 
@@ -217,6 +227,7 @@ def main():
         s64 = bench_schedule(args, torch, ops, inputs, dev, args.sched_batches)
         s1 = bench_schedule(args, torch, ops, inputs, dev, 1)
         sched = {"nb": s64["nb"], "routing": "uniform", "routes_per_s": s64["routes_per_s"], "ms": s64["ms"],
+                 "kernel_ms": s64["split_ms"],
                  "achieved_GBs": s64["gbs"], "peak_GBs": PEAK_HBM_GBS, "frac": s64["hbm_frac"],
                  "compulsory_bytes_per_call": s64["compulsory_bytes"],
                  "nb1_ms": s1["ms"], "nb1_routes_per_s": s1["routes_per_s"],

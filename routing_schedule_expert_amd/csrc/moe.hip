@@ -27,17 +27,17 @@ __global__ void k_zero_u32(uint32_t *p, int64_t n) {
 }
 
 __global__ __launch_bounds__(256) void k_sched_count(SchedArgs a) {
-    extern __shared__ int32_t sched_smem[];
+    extern __shared__ __attribute__((aligned(16))) int32_t sched_smem[];
     sched_count_body(a, sched_smem, blockIdx.x);
 }
 
 __global__ __launch_bounds__(256) void k_sched_finalize(SchedArgs a) {
-    extern __shared__ int32_t sched_smem[];
+    extern __shared__ __attribute__((aligned(16))) int32_t sched_smem[];
     sched_finalize(a, blockIdx.x, sched_smem);
 }
 
 __global__ __launch_bounds__(256) void k_sched_scatter(SchedArgs a) {
-    extern __shared__ int32_t sched_smem[];
+    extern __shared__ __attribute__((aligned(16))) int32_t sched_smem[];
     sched_scatter_body(a, sched_smem, blockIdx.x);
 }
 
@@ -179,7 +179,13 @@ int64_t cap_rows(const moe_desc *d) {
     return (int64_t)d->P * d->Np * d->K + (int64_t)d->L * (d->pad_rows - 1);
 }
 
-int sched_chunks(const moe_desc *d) { return (int)(((int64_t)d->Np * d->K + kSchedChunk - 1) / kSchedChunk); }
+// 1024-route blocks per logical thread: one for a single routing tensor (most
+// parallelism), four when many tensors are scheduled together (fewer chunks).
+int sched_cb(const moe_desc *d) { return d->num_batches >= 8 ? 4 : 1; }
+int sched_chunks(const moe_desc *d) {
+    const int64_t chunk = (int64_t)kSchedBlock * sched_cb(d);
+    return (int)(((int64_t)d->Np * d->K + chunk - 1) / chunk);
+}
 int sched_wg_per_part(const moe_desc *d) { return (sched_chunks(d) + kSchedWaves - 1) / kSchedWaves; }
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
@@ -215,6 +221,7 @@ void fill_sched_args(SchedArgs &a, const moe_desc *d, const int32_t *routes, int
     a.nb = d->num_batches;
     a.W = sched_chunks(d);
     a.wpw = wpw;
+    a.cb = sched_cb(d);
     a.wg_per_part = (a.W + wpw - 1) / wpw;
     a.nbits = 32 - __builtin_clz((unsigned)d->L | 1u);
     a.cap = cap_rows(d);
@@ -223,7 +230,8 @@ void fill_sched_args(SchedArgs &a, const moe_desc *d, const int32_t *routes, int
 // LDS (bytes) of the schedule bodies for `wpw` waves per workgroup.
 size_t sched_lds_bytes(const moe_desc *d, int wpw) {
     const size_t L = d->L, P = d->P;
-    size_t count = wpw * (L + 1), fin = P * L + L + 16, scat = L * P + L + 1 + wpw * L;
+    const size_t mstride = P <= (size_t)kSchedPMax ? (size_t)kSchedPMax : P;
+    size_t count = wpw * (L + 1), fin = P * L + L + 16, scat = L * mstride + L + 1 + wpw * L;
     return 4 * std::max(count, std::max(fin, scat));
 }
 

@@ -26,8 +26,9 @@
 namespace moe {
 
 constexpr int kSchedUnroll = 16;                    // route loads in flight per lane
-constexpr int kSchedChunk = kWave * kSchedUnroll;   // routes per logical thread (wave)
+constexpr int kSchedBlock = kWave * kSchedUnroll;   // routes ranked per pass of a wave
 constexpr int kSchedWaves = 4;                      // waves per workgroup of the standalone kernels
+constexpr int kSchedPMax = 8;                       // partitions handled by the unrolled position formula
 
 struct SchedArgs {
     const int32_t *routes;  // [nb][P][R]
@@ -38,6 +39,7 @@ struct SchedArgs {
     int32_t *wcnt;          // ws: [nb][P][W][L] counts, then exclusive offsets
     int32_t P, R, K, L, base, pad, nb, W, wg_per_part, nbits;
     int32_t wpw;  // waves per workgroup (chunks handled by one workgroup)
+    int32_t cb;   // 1024-route blocks per chunk (a chunk is one logical thread)
     int64_t cap;
 };
 
@@ -141,8 +143,34 @@ __device__ void sched_finalize(const SchedArgs &a, int b, int32_t *smem) {
     if (threadIdx.x == blockDim.x - 1) so[L] = acc;  // the last thread's run ends at L
 }
 
+// Ranks one block of 1024 consecutive routes (16 steps of 64) of a wave:
+// for every step, the local expert id v of each lane, the mask of lanes with
+// the same v and the lane's rank among them.  Only the loaded ids are needed,
+// so all 16 steps are ranked before any counter is touched.
+struct BlockRank {
+    uint32_t v[kSchedUnroll];
+    uint64_t peers[kSchedUnroll];
+};
+
+__device__ __forceinline__ void rank_block(const SchedArgs &a, const int32_t *src, int32_t lo, int lane,
+                                           BlockRank &br) {
+    int32_t e[kSchedUnroll];
+    const int32_t *sb = src + lo;
+#pragma unroll
+    for (int u = 0; u < kSchedUnroll; ++u) {
+        const int32_t i = lo + u * kWave + lane;
+        e[u] = i < a.R ? __builtin_nontemporal_load(sb + u * kWave + lane) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kSchedUnroll; ++u) {
+        br.v[u] = local_id(e[u], a.base, a.L);
+        br.peers[u] = match_lanes(br.v[u], a.nbits);
+    }
+}
+
 // Stage 1: per-chunk counts.  x is the workgroup's index in the schedule grid
-// (a persistent caller loops over it).
+// (a persistent caller loops over it).  Counting needs no ranks: every local
+// lane adds one to its expert's LDS counter (integer adds, exact in any order).
 __device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
     int b, r, q;
     if (!sched_locate(a, x, b, r, q)) return;
@@ -156,19 +184,21 @@ __device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
     __syncthreads();
     if (w < a.W) {
         const int32_t *src = a.routes + ((int64_t)b * a.P + r) * a.R;
-        const int64_t lo = (int64_t)w * kSchedChunk;
-        int32_t e[kSchedUnroll];
+        for (int blk = 0; blk < a.cb; ++blk) {
+            const int64_t lo = ((int64_t)w * a.cb + blk) * kSchedBlock;
+            if (lo >= a.R) break;
+            int32_t e[kSchedUnroll];
 #pragma unroll
-        for (int u = 0; u < kSchedUnroll; ++u) {
-            int64_t i = lo + u * kWave + lane;
-            e[u] = i < a.R ? __builtin_nontemporal_load(src + i) : -1;
-        }
+            for (int u = 0; u < kSchedUnroll; ++u) {
+                const int64_t i = lo + u * kWave + lane;
+                e[u] = i < a.R ? __builtin_nontemporal_load(src + i) : -1;
+            }
 #pragma unroll
-        for (int u = 0; u < kSchedUnroll; ++u) {
-            uint32_t v = local_id(e[u], a.base, L);
-            uint64_t peers = match_lanes(v, a.nbits);
-            bool leader = (peers & ((1ull << lane) - 1ull)) == 0;  // lowest lane of its group
-            if (leader && v < (uint32_t)L) cnt[v] += __popcll(peers);
+            for (int u = 0; u < kSchedUnroll; ++u) {
+                const uint32_t v = local_id(e[u], a.base, L);
+                if (v < (uint32_t)L)
+                    __hip_atomic_fetch_add(cnt + v, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
         }
     }
     __syncthreads();
@@ -178,7 +208,10 @@ __device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
     }
 }
 
-// Stage 4: scatter every route once.
+// Stage 4: scatter every route once.  The ordinal o of a route is the wave's
+// running count for its expert (starting at the chunk's exclusive offset)
+// plus its rank in the step; the group leader advances the count with an
+// LDS atomic whose returned old value is broadcast to the group.
 __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
     int b, r, q;
     if (!sched_locate(a, x, b, r, q)) return;
@@ -187,13 +220,18 @@ __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
     const int wv = threadIdx.x / kWave;
     const int w = q * a.wpw + wv;
     const int L = a.L, P = a.P;
-    // LDS: M [L][P], S [L+1], per-wave running offsets [4][L]
+    const bool fast = P <= kSchedPMax;
+    const int mstride = fast ? kSchedPMax : P;
+    // LDS: M [L][mstride] (zero-padded), S [L+1], per-wave running offsets [wpw][L]
     int32_t *sM = smem;
-    int32_t *sS = sM + L * P;
+    int32_t *sS = sM + L * mstride;
     int32_t *run = sS + L + 1 + wv * L;
     const int32_t *cnt = a.counts + (int64_t)b * L * P;
     const int32_t *so = a.seg_off + (int64_t)b * (L + 1);
-    for (int i = threadIdx.x; i < L * P; i += blockDim.x) sM[i] = cnt[i];
+    for (int i = threadIdx.x; i < L * mstride; i += blockDim.x) {
+        const int l = i / mstride, rr = i % mstride;
+        sM[i] = rr < P ? cnt[l * P + rr] : 0;
+    }
     for (int i = threadIdx.x; i <= L; i += blockDim.x) sS[i] = so[i];
     if (w < a.W) {
         const int32_t *off = a.wcnt + (((int64_t)b * P + r) * a.W + w) * L;
@@ -204,34 +242,60 @@ __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
     if (w < a.W) {
         const int32_t *src = a.routes + ((int64_t)b * P + r) * a.R;
         int32_t *rrow = a.route_row + ((int64_t)b * P + r) * a.R;
-        const int64_t lo = (int64_t)w * kSchedChunk;
-        int32_t e[kSchedUnroll];
+        const int K = a.K;
+        const int adv_t = kWave / K, adv_j = kWave % K;  // per-step advance of (token, slot)
+        for (int blk = 0; blk < a.cb; ++blk) {
+            const int32_t lo = (w * a.cb + blk) * kSchedBlock;
+            if (lo >= a.R) break;
+            BlockRank br;
+            rank_block(a, src, lo, lane, br);
+            int32_t base[kSchedUnroll];
 #pragma unroll
-        for (int u = 0; u < kSchedUnroll; ++u) {
-            int64_t i = lo + u * kWave + lane;
-            e[u] = i < a.R ? __builtin_nontemporal_load(src + i) : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < kSchedUnroll; ++u) {
-            const int64_t i = lo + u * kWave + lane;
-            uint32_t v = local_id(e[u], a.base, L);
-            uint64_t peers = match_lanes(v, a.nbits);
-            int rank = lanes_below(peers);
-            int32_t row = -1;
-            if (v < (uint32_t)L) {
-                const int32_t o = run[v] + rank;
-                const int32_t *Ml = sM + v * P;
-                int32_t p = 0;
-                for (int rr = 0; rr < P; ++rr) {
-                    int32_t m = Ml[rr];
-                    p += min(m, o) + ((rr < r && m > o) ? 1 : 0);
-                }
-                row = sS[v] + p;
-                reinterpret_cast<uint2 *>(phi)[row] = make_uint2((uint32_t)r, (uint32_t)((int32_t)i / a.K));
+            for (int u = 0; u < kSchedUnroll; ++u) {
+                const int rank = lanes_below(br.peers[u]);
+                int32_t old = 0;
+                if (rank == 0 && br.v[u] < (uint32_t)L)
+                    old = __hip_atomic_fetch_add(run + br.v[u], (int32_t)__popcll(br.peers[u]), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+                const int leader = (int)__builtin_ctzll(br.peers[u]);
+                base[u] = __shfl(old, leader, kWave) + rank;
             }
-            if (i < a.R) rrow[i] = row;
-            // every lane has read run[v]; now the group's lowest lane advances it
-            if (rank == 0 && v < (uint32_t)L) run[v] += __popcll(peers);
+            // (token, slot) of this lane's route in step 0, then advanced by 64 routes per step
+            int32_t t = (lo + lane) / K;
+            int32_t j = (lo + lane) - t * K;
+            const int32_t *M8 = sM;
+            int32_t *rr_blk = rrow + lo;
+#pragma unroll
+            for (int u = 0; u < kSchedUnroll; ++u) {
+                const uint32_t v = br.v[u];
+                int32_t row = -1;
+                if (v < (uint32_t)L) {
+                    const int32_t o = base[u];
+                    int32_t p = 0;
+                    if (fast) {
+                        // min(m, o) + [m > o] = min(m, o + 1): partitions before r
+                        // count up to o + 1, the others up to o (r is wave-uniform)
+                        const int4 m0 = *reinterpret_cast<const int4 *>(M8 + v * kSchedPMax);
+                        const int4 m1 = *reinterpret_cast<const int4 *>(M8 + v * kSchedPMax + 4);
+                        const int32_t m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+                        const int32_t o1 = o + 1;
+#pragma unroll
+                        for (int rr = 0; rr < kSchedPMax; ++rr) p += min(m[rr], rr < r ? o1 : o);
+                    } else {
+                        const int32_t *Ml = sM + v * P;
+                        for (int rr = 0; rr < P; ++rr) p += min(Ml[rr], rr < r ? o + 1 : o);
+                    }
+                    row = sS[v] + p;
+                    reinterpret_cast<uint2 *>(phi)[row] = make_uint2((uint32_t)r, (uint32_t)t);
+                }
+                if (lo + u * kWave + lane < a.R) rr_blk[u * kWave + lane] = row;
+                t += adv_t;
+                j += adv_j;
+                if (j >= K) {
+                    j -= K;
+                    t += 1;
+                }
+            }
         }
     }
     // padding rows of the segments this workgroup owns: (-1, -1)
@@ -239,7 +303,7 @@ __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
     const int nwg = P * a.wg_per_part;
     for (int l = wg_in_batch; l < L; l += nwg) {
         int32_t t = 0;
-        for (int rr = 0; rr < P; ++rr) t += sM[l * P + rr];
+        for (int rr = 0; rr < P; ++rr) t += sM[l * mstride + rr];
         for (int32_t row = sS[l] + t + threadIdx.x; row < sS[l + 1]; row += blockDim.x)
             reinterpret_cast<uint2 *>(phi)[row] = make_uint2(0xffffffffu, 0xffffffffu);
     }
