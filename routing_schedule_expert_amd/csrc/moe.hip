@@ -231,7 +231,7 @@ void fill_sched_args(SchedArgs &a, const moe_desc *d, const int32_t *routes, int
 size_t sched_lds_bytes(const moe_desc *d, int wpw) {
     const size_t L = d->L, P = d->P;
     const size_t mstride = P <= (size_t)kSchedPMax ? (size_t)kSchedPMax : P;
-    size_t count = wpw * (L + 1), fin = P * L + L + 16, scat = L * mstride + L + 1 + wpw * L;
+    size_t count = wpw * (L + 1), fin = P * L + L + 16, scat = L * mstride + L + 1 + wpw * (L + 2 * kSchedBlock);
     return 4 * std::max(count, std::max(fin, scat));
 }
 

@@ -208,10 +208,17 @@ __device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
     }
 }
 
-// Stage 4: scatter every route once.  The ordinal o of a route is the wave's
-// running count for its expert (starting at the chunk's exclusive offset)
-// plus its rank in the step; the group leader advances the count with an
-// LDS atomic whose returned old value is broadcast to the group.
+// Stage 4: scatter every route once.
+//
+// Per 1024-route block of a wave: (A) the local routes are compacted, in
+// index order, into an LDS list (ballot + masked popcount give each local lane
+// its slot; route_row is staged as -1); (B) the list is processed 64 entries
+// at a time: lanes holding the same expert find each other with one ballot
+// per bit of the expert id, the group leader advances the wave's running
+// count for that expert with an LDS atomic (integer, program order) and the
+// returned old value plus the lane's rank in its group is the ordinal o; then
+// p and the row follow and Phi[row] is written; (C) the staged route_row is
+// written back coalesced.  Only local routes pay for ranking and placement.
 __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
     int b, r, q;
     if (!sched_locate(a, x, b, r, q)) return;
@@ -219,13 +226,17 @@ __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
     const int lane = lane_id();
     const int wv = threadIdx.x / kWave;
     const int w = q * a.wpw + wv;
-    const int L = a.L, P = a.P;
+    const int L = a.L, P = a.P, K = a.K;
     const bool fast = P <= kSchedPMax;
     const int mstride = fast ? kSchedPMax : P;
-    // LDS: M [L][mstride] (zero-padded), S [L+1], per-wave running offsets [wpw][L]
+    // LDS: M [L][mstride] (zero-padded), S [L+1], then per wave: running
+    // offsets [L], the compacted list [1024] and the staged route rows [1024]
     int32_t *sM = smem;
     int32_t *sS = sM + L * mstride;
-    int32_t *run = sS + L + 1 + wv * L;
+    int32_t *wave_base = sS + L + 1 + wv * (L + 2 * kSchedBlock);
+    int32_t *run = wave_base;
+    int32_t *list = run + L;
+    int32_t *rowbuf = list + kSchedBlock;
     const int32_t *cnt = a.counts + (int64_t)b * L * P;
     const int32_t *so = a.seg_off + (int64_t)b * (L + 1);
     for (int i = threadIdx.x; i < L * mstride; i += blockDim.x) {
@@ -242,65 +253,71 @@ __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
     if (w < a.W) {
         const int32_t *src = a.routes + ((int64_t)b * P + r) * a.R;
         int32_t *rrow = a.route_row + ((int64_t)b * P + r) * a.R;
-        const int K = a.K;
-        const int adv_t = kWave / K, adv_j = kWave % K;  // per-step advance of (token, slot)
         for (int blk = 0; blk < a.cb; ++blk) {
             const int32_t lo = (w * a.cb + blk) * kSchedBlock;
             if (lo >= a.R) break;
-            BlockRank br;
-            rank_block(a, src, lo, lane, br);
-            int32_t base[kSchedUnroll];
+            // (A) load, compact local routes in index order, stage route_row = -1
+            int32_t e[kSchedUnroll];
 #pragma unroll
             for (int u = 0; u < kSchedUnroll; ++u) {
-                const int rank = lanes_below(br.peers[u]);
-                int32_t old = 0;
-                if (rank == 0 && br.v[u] < (uint32_t)L)
-                    old = __hip_atomic_fetch_add(run + br.v[u], (int32_t)__popcll(br.peers[u]), __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
-                const int leader = (int)__builtin_ctzll(br.peers[u]);
-                base[u] = __shfl(old, leader, kWave) + rank;
+                const int32_t i = lo + u * kWave + lane;
+                e[u] = i < a.R ? __builtin_nontemporal_load(src + i) : -1;
             }
-            // (token, slot) of this lane's route in step 0, then advanced by 64 routes per step
-            int32_t t = (lo + lane) / K;
-            int32_t j = (lo + lane) - t * K;
-            const int32_t *M8 = sM;
-            int32_t *rr_blk = rrow + lo;
+            int nloc = 0;
 #pragma unroll
             for (int u = 0; u < kSchedUnroll; ++u) {
-                const uint32_t v = br.v[u];
-                int32_t row = -1;
-                if (v < (uint32_t)L) {
-                    const int32_t o = base[u];
+                const uint32_t v = local_id(e[u], a.base, L);
+                const bool local = v < (uint32_t)L;
+                const uint64_t lm = ballot(local);
+                rowbuf[u * kWave + lane] = -1;
+                if (local) list[nloc + lanes_below(lm)] = (int32_t)((v << 16) | (uint32_t)(u * kWave + lane));
+                nloc += __popcll(lm);
+            }
+            // (B) rank and place the local routes, 64 at a time
+            const int32_t t0 = lo / K;
+            const int32_t j0 = lo - t0 * K;
+            for (int c0 = 0; c0 < nloc; c0 += kWave) {
+                const bool valid = c0 + lane < nloc;
+                const int32_t ent = valid ? list[c0 + lane] : (int32_t)((uint32_t)L << 16);
+                const uint32_t v = (uint32_t)ent >> 16;
+                const int32_t ib = ent & 0xffff;  // index inside the block
+                const uint64_t peers = match_lanes(v, a.nbits);
+                const int rank = lanes_below(peers);
+                int32_t old = 0;
+                if (rank == 0 && valid)
+                    old = __hip_atomic_fetch_add(run + v, (int32_t)__popcll(peers), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+                const int32_t o = __shfl(old, (int)__builtin_ctzll(peers), kWave) + rank;
+                if (valid) {
                     int32_t p = 0;
                     if (fast) {
                         // min(m, o) + [m > o] = min(m, o + 1): partitions before r
                         // count up to o + 1, the others up to o (r is wave-uniform)
-                        const int4 m0 = *reinterpret_cast<const int4 *>(M8 + v * kSchedPMax);
-                        const int4 m1 = *reinterpret_cast<const int4 *>(M8 + v * kSchedPMax + 4);
+                        const int4 m0 = *reinterpret_cast<const int4 *>(sM + v * kSchedPMax);
+                        const int4 m1 = *reinterpret_cast<const int4 *>(sM + v * kSchedPMax + 4);
                         const int32_t m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-                        const int32_t o1 = o + 1;
 #pragma unroll
-                        for (int rr = 0; rr < kSchedPMax; ++rr) p += min(m[rr], rr < r ? o1 : o);
+                        for (int rr = 0; rr < kSchedPMax; ++rr) p += min(m[rr], rr < r ? o + 1 : o);
                     } else {
                         const int32_t *Ml = sM + v * P;
                         for (int rr = 0; rr < P; ++rr) p += min(Ml[rr], rr < r ? o + 1 : o);
                     }
-                    row = sS[v] + p;
+                    const int32_t row = sS[v] + p;
+                    const int32_t jj = j0 + ib;  // slot offset from token t0, < K + 1024
+                    const int32_t t = t0 + jj / K;
                     reinterpret_cast<uint2 *>(phi)[row] = make_uint2((uint32_t)r, (uint32_t)t);
-                }
-                if (lo + u * kWave + lane < a.R) rr_blk[u * kWave + lane] = row;
-                t += adv_t;
-                j += adv_j;
-                if (j >= K) {
-                    j -= K;
-                    t += 1;
+                    rowbuf[ib] = row;
                 }
             }
+            // (C) route rows of the block, coalesced
+            const int32_t nb_routes = min(kSchedBlock, a.R - lo);
+            for (int k = lane; k < nb_routes; k += kWave) rrow[lo + k] = rowbuf[k];
         }
     }
     // padding rows of the segments this workgroup owns: (-1, -1)
     const int wg_in_batch = r * a.wg_per_part + q;
     const int nwg = P * a.wg_per_part;
+    __syncthreads();
     for (int l = wg_in_batch; l < L; l += nwg) {
         int32_t t = 0;
         for (int rr = 0; rr < P; ++rr) t += sM[l * mstride + rr];
