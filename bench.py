@@ -144,6 +144,96 @@ def bench_schedule(args, torch, ops, inputs, dev, nb, kind="uniform"):
                 hbm_frac=compulsory / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, routes=r)
 
 
+def bench_fwd_bwd(args, torch, ops, inputs, dev):
+    """Adversarial Kimi-shaped forward + backward (Zipf s=1.5 + 4 hot local experts)."""
+    c = KIMI
+    h = inputs.make_layer_inputs_device(6, c["P"], c["Np"], c["E"], c["K"], c["L"], c["H"], c["I"], dev,
+                                        routing="hot", x_std=1.0, s=1.5, with_grad=True)
+    d = ops.make_desc(c["P"], c["Np"], c["K"], c["E"], c["L"], H=c["H"], I=c["I"])
+    routes = torch.from_numpy(h["routes"]).to(dev)
+    w = torch.from_numpy(h["w"]).to(dev)
+    b = ops.alloc_fwd(d, dev, save_hu=True)
+    L, H, I = c["L"], c["H"], c["I"]
+    dX = torch.empty_like(h["X"])
+    dW13 = torch.empty((L, 2 * I, H), dtype=torch.float32, device=dev)
+    dW2 = torch.empty((L, H, I), dtype=torch.float32, device=dev)
+    dw = torch.empty((c["P"], c["Np"], c["K"]), dtype=torch.float32, device=dev)
+    ws = torch.empty(ops.workspace_bytes(d, ops.MOE_OP_LAYER_BWD), dtype=torch.uint8, device=dev)
+    local = int(((h["routes"] >= 0) & (h["routes"] < L)).sum())
+
+    def step():
+        ops.layer_fwd(d, routes, w, h["X"], h["W13"], h["W2"], b)
+        ops.moe_layer_bwd(d, h["dOut"], routes, w, b.phi, b.route_row, b.seg_off, b.Xd, b.HU, b.A, h["W13"],
+                          h["W2"], dX, dW13, dW2, dw, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ops.moe_trace_enable(args.steps * 32)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    per = {}
+    for name, t in ops.moe_trace_read(args.steps * 32):
+        per.setdefault(name, []).append(t)
+    ops.moe_trace_enable(0)
+    st = {k: float(np.mean(v)) for k, v in per.items()}
+    hi = c["H"] * c["I"]
+    fl = 18.0 * hi * local
+    npad = int(b.seg_off[-1].item())
+    return {"metric": "MoE layer fwd+bwd TFLOP/s (Kimi shape, adversarial routing, 1 GPU)",
+            "value": fl / (ms / 1e3) / 1e12, "unit": "TFLOP/s", "ms_per_step": ms, "steps": args.steps,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "kimi_local_share_fwd_bwd", "routing": "zipf1.5+4hot", "local_routes": local,
+                       "dispatched_rows": npad},
+            "stage_ms": st,
+            "kernel_tflops": {k: v for k, v in {
+                "ffn_gateup": 4.0 * hi * local / (st.get("ffn_gateup", 1e9) / 1e3) / 1e12,
+                "ffn_down": 2.0 * hi * local / (st.get("ffn_down", 1e9) / 1e3) / 1e12,
+                "bwd_down": 2.0 * hi * local / (st.get("bwd_down", 1e9) / 1e3) / 1e12,
+                "bwd_gateup": 4.0 * hi * local / (st.get("bwd_gateup", 1e9) / 1e3) / 1e12,
+                "bwd_wgrad": 6.0 * hi * local / (st.get("bwd_wgrad", 1e9) / 1e3) / 1e12}.items()}}
+
+
+def bench_tc_sweep(args, torch, ops, inputs, dev):
+    """Mid configuration (8 x 4096 tokens, 64 experts with 8 local, top-6, H=2048,
+    I=1024): layer forward vs the minibatch of dispatched rows Tc (persistent
+    launch, gate/up of chunk c overlapping the down projection of chunk c-1)."""
+    P, Np, E, K, L, H, I = 8, 4096, 64, 6, 8, 2048, 1024
+    h = inputs.make_layer_inputs_device(4, P, Np, E, K, L, H, I, dev, routing="uniform", x_std=1.0)
+    d = ops.make_desc(P, Np, K, E, L, H=H, I=I)
+    routes = torch.from_numpy(h["routes"]).to(dev)
+    w = torch.from_numpy(h["w"]).to(dev)
+    b = ops.alloc_fwd(d, dev, save_hu=False)
+    local = int(((h["routes"] >= 0) & (h["routes"] < L)).sum())
+    fl = 6.0 * H * I * local
+    rows = []
+    for label, flags, tc in [("multi-launch", 0, 0), ("persistent", ops.MOE_PERSISTENT, 0)] + \
+            [("persistent", ops.MOE_PERSISTENT, t) for t in (256, 512, 1024, 2048, 4096, 8192)]:
+        for _ in range(args.warmup):
+            ops.layer_fwd(d, routes, w, h["X"], h["W13"], h["W2"], b, flags=flags, chunk_rows=tc)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            ops.layer_fwd(d, routes, w, h["X"], h["W13"], h["W2"], b, flags=flags, chunk_rows=tc)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        rows.append({"path": label, "chunk_rows": tc, "ms": ms, "tflops": fl / (ms / 1e3) / 1e12})
+    npad = int(b.seg_off[-1].item())
+    return {"metric": "MoE layer fwd ms vs minibatch Tc (mid shape, 1 GPU)", "unit": "ms",
+            "config": {"workload": "mid_fwd_tc_sweep", "P": P, "tokens_per_partition": Np, "experts": E,
+                       "local_experts": L, "top_k": K, "H": H, "I": I, "local_routes": local,
+                       "dispatched_rows": npad,
+                       "tc_floor_cdna4_256x256": 2 * 256 * 256 * 256 // min(2 * I, H)},
+            "sweep": rows}
+
+
 def cpu_baseline(L_res, torch, oracle, budget_s: float):
     """The oracle's per-token forward on a bounded sample of tokens."""
     c = KIMI
@@ -190,6 +280,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-schedule", action="store_true")
+    ap.add_argument("--workload", default="kimi", choices=["kimi", "kimi_bwd", "mid_tc"],
+                    help="kimi: the contract line (default); kimi_bwd / mid_tc: extra measurements")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -205,6 +297,12 @@ def main():
 
     ops.load()
     dev = torch.device("cuda:0")
+    if args.workload == "kimi_bwd":
+        print(json.dumps(bench_fwd_bwd(args, torch, ops, inputs, dev)), flush=True)
+        return
+    if args.workload == "mid_tc":
+        print(json.dumps(bench_tc_sweep(args, torch, ops, inputs, dev)), flush=True)
+        return
     print("[bench] layer forward, Kimi shape", file=sys.stderr, flush=True)
     L_res = bench_layer(args, torch, ops, inputs, dev)
     ms = L_res["ms_step"]

@@ -702,6 +702,68 @@ __device__ __forceinline__ void epilogue_store_bf16_w(AccW<WM, WN> &acc, char *l
     }
 }
 
+template <int WM, int WN>
+__device__ __forceinline__ void epilogue_store_f32_w(AccW<WM, WN> &acc, float *dst, int64_t ld, int mvalid, int nvalid) {
+    using WG = WaveGrid<WM, WN>;
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63, wm = wave / WN, wn = wave % WN;
+    float *base = dst + (int64_t)WG::row(wm, 0, 0, lane) * ld + wn * (WG::NI * 32) + (lane & 31);
+    const int row0 = WG::row(wm, 0, 0, lane), col0 = wn * (WG::NI * 32) + (lane & 31);
+#pragma unroll
+    for (int mi = 0; mi < WG::MI; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < WG::NI; ++ni) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int dr = mi * 32 + 8 * (e >> 2) + (e & 3);
+                if (row0 + dr < mvalid && col0 + ni * 32 < nvalid) base[(int64_t)dr * ld + ni * 32] = acc[mi][ni][e];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// Down-projection dgrad tile dA' (256 rows x 256 columns of I, columns from
+// n0) -> SwiGLU backward and the router-weight partial sums:
+//   dA = w dA'; dh = dA * u * silu'(h); du = dA * silu(h)  -> dHU (bf16)
+//   part[row][(n0 / 256) * WN + wn] = sum over the wave's columns of dA' * a
+// A, HU, wrow, dHU, part are already offset to the tile's first row.
+template <int WM, int WN>
+__device__ __forceinline__ void epilogue_swiglu_bwd_w(AccW<WM, WN> &acc, const uint16_t *A, const uint16_t *HU,
+                                                      const float *wrow, uint16_t *dHU, float *part, int nparts, int I,
+                                                      int n0) {
+    using WG = WaveGrid<WM, WN>;
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63, wm = wave / WN, wn = wave % WN;
+#pragma unroll
+    for (int mi = 0; mi < WG::MI; ++mi) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = WG::row(wm, mi, e, lane);
+            const float wr = wrow[row];
+            float dot = 0.f;
+#pragma unroll
+            for (int ni = 0; ni < WG::NI; ++ni) {
+                const int col = n0 + wn * (WG::NI * 32) + ni * 32 + (lane & 31);
+                if (col < I) {
+                    const float dap = acc[mi][ni][e];
+                    const float a = bf2f(A[(int64_t)row * I + col]);
+                    const float h = bf2f(HU[(int64_t)row * 2 * I + col]);
+                    const float u = bf2f(HU[(int64_t)row * 2 * I + I + col]);
+                    const float dA = wr * dap;
+                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h));
+                    dHU[(int64_t)row * 2 * I + col] = f2bf(dA * u * sg * (1.0f + h * (1.0f - sg)));
+                    dHU[(int64_t)row * 2 * I + I + col] = f2bf(dA * h * sg);
+                    dot = fmaf(dap, a, dot);
+                }
+            }
+            // fixed-order butterfly over the 32 lanes that share this row
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
+            if ((lane & 31) == 0) part[(int64_t)row * nparts + (n0 / 256) * WN + wn] = dot;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 // fp32 store of a 256 x 256 tile (rows < mvalid, columns < nvalid).
 __device__ __forceinline__ void epilogue_store_f32(f32x16 (&acc)[4][4], float *dst, int64_t ld, int mvalid, int nvalid) {
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63, wm = wave >> 1, wn = wave & 1;

@@ -170,10 +170,19 @@ struct BwdArgs {
     const uint16_t *Xd, *HU, *A, *W13, *W2;
     const int32_t *seg_off;
     float *dW13, *dW2;
+    // transposed operands: weights [L][I][H], [L][H][2I]; activations [.][ldT]
+    uint16_t *W2T, *W13T, *dYT, *AT, *dHUT, *XdT;
+    int64_t ldT;
     int L, H, I, nparts;
 };
 
-// B2: dA' = dO_d W2[l] (N-contiguous weight), SwiGLU backward in the epilogue.
+// A K-contiguous window of up to 256 rows starting at `rows`; when only 128
+// rows exist the upper half repeats the lower one (its results are masked).
+__device__ __forceinline__ KOp rows_window(const uint16_t *rows, int64_t ld, int valid) {
+    return KOp{rows, valid > 128 ? rows + 128 * ld : rows, ld};
+}
+
+// B2: dA' = dO_d W2[l] (as dO_d . W2T[l]^T), SwiGLU backward in the epilogue.
 __device__ __forceinline__ void bwd_down_phase(const BwdArgs &a, char *lds) {
     const int H = a.H, I = a.I;
     const int npad = a.seg_off[a.L];
@@ -187,16 +196,17 @@ __device__ __forceinline__ void bwd_down_phase(const BwdArgs &a, char *lds) {
         const int m0 = mt * kBM;
         const int l = expert_of(a.seg_off, a.L, m0);
         const uint16_t *g = a.dOd + (int64_t)m0 * H;
-        KOp ak{g, g + 128ll * H, H};
-        MNOp bmn{a.W2 + (int64_t)l * H * I + nt * 256, I, I - nt * 256, nullptr};
-        f32x16 acc[4][4];
-        gemm_mainloop<true, false>(ak, MNOp{}, KOp{}, bmn, H / kBK, false, lds, acc);
-        epilogue_swiglu_bwd(acc, a.A + (int64_t)m0 * I, a.HU + (int64_t)m0 * 2 * I, a.wrow + m0,
-                            a.dHU + (int64_t)m0 * 2 * I, a.part + (int64_t)m0 * a.nparts, a.nparts, I, nt * 256, nt);
+        const KOp ak{g, g + 128ll * H, H};
+        const KOp bk = rows_window(a.W2T + ((int64_t)l * I + nt * 256) * H, H, I - nt * 256);
+        AccW<kFwdWM, kFwdWN> acc;
+        gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, H / 64, false, lds, acc);
+        epilogue_swiglu_bwd_w<kFwdWM, kFwdWN>(acc, a.A + (int64_t)m0 * I, a.HU + (int64_t)m0 * 2 * I, a.wrow + m0,
+                                              a.dHU + (int64_t)m0 * 2 * I, a.part + (int64_t)m0 * a.nparts, a.nparts, I,
+                                              nt * 256);
     }
 }
 
-// B3: dXd = dHU W13[l] (N-contiguous weight).
+// B3: dXd = dHU W13[l] (as dHU . W13T[l]^T).
 __device__ __forceinline__ void bwd_gateup_phase(const BwdArgs &a, char *lds) {
     const int H = a.H, I = a.I;
     const int npad = a.seg_off[a.L];
@@ -210,17 +220,17 @@ __device__ __forceinline__ void bwd_gateup_phase(const BwdArgs &a, char *lds) {
         const int m0 = mt * kBM;
         const int l = expert_of(a.seg_off, a.L, m0);
         const uint16_t *g = a.dHU + (int64_t)m0 * 2 * I;
-        KOp ak{g, g + 128ll * 2 * I, 2ll * I};
-        MNOp bmn{a.W13 + (int64_t)l * 2 * I * H + nt * 256, H, H - nt * 256, nullptr};
-        f32x16 acc[4][4];
-        gemm_mainloop<true, false>(ak, MNOp{}, KOp{}, bmn, 2 * I / kBK, false, lds, acc);
-        epilogue_store_bf16(acc, lds, a.dXd + (int64_t)m0 * H + nt * 256, H, 256);
+        const KOp ak{g, g + 128ll * 2 * I, 2ll * I};
+        const KOp bk = rows_window(a.W13T + ((int64_t)l * H + nt * 256) * 2 * I, 2ll * I, 256);
+        AccW<kFwdWM, kFwdWN> acc;
+        gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, 2 * I / 64, false, lds, acc);
+        epilogue_store_bf16_w<kFwdWM, kFwdWN>(acc, lds, a.dXd + (int64_t)m0 * H + nt * 256, H, 256);
     }
 }
 
-// B5: per expert, dW2[l] = sum_rows (w dO_d)^T a and dW13[l] = sum_rows dHU^T Xd,
-// reduced over the segment's rows in ascending order inside one workgroup per
-// output tile.  Experts are taken longest segment first.
+// B5: per expert, dW2[l] = sum_rows (w dO_d)^T a  and  dW13[l] = sum_rows dHU^T Xd,
+// as NT products of the transposed activations over the segment's rows
+// (ascending, inside one workgroup per output tile).  Longest segments first.
 __device__ __forceinline__ void wgrad_phase(const BwdArgs &a, char *lds) {
     const int H = a.H, I = a.I, L = a.L;
     __shared__ int s_order[256];
@@ -237,10 +247,11 @@ __device__ __forceinline__ void wgrad_phase(const BwdArgs &a, char *lds) {
         }
     }
     __syncthreads();
-    const int mt2 = H / 256, nt2 = (I + 255) / 256;      // dW2 [H][I]
-    const int mt13 = 2 * I / 256, nt13 = H / 256;         // dW13 [2I][H]
+    const int mt2 = H / 256, nt2 = (I + 255) / 256;   // dW2 [H][I]
+    const int mt13 = 2 * I / 256, nt13 = H / 256;      // dW13 [2I][H]
     const int per = mt2 * nt2 + mt13 * nt13;
     const int64_t total = (int64_t)L * per;
+    const int64_t ldT = a.ldT;
     for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
         const int64_t lid = logical_tile(it);
         if (lid >= total) continue;
@@ -248,23 +259,23 @@ __device__ __forceinline__ void wgrad_phase(const BwdArgs &a, char *lds) {
         const int l = L <= 256 ? s_order[pos] : pos;
         const int S = a.seg_off[l];
         const int kext = a.seg_off[l + 1] - S;  // padded: padding rows are zero in every operand
-        f32x16 acc[4][4];
+        AccW<kFwdWM, kFwdWN> acc;
         if (in < mt2 * nt2) {
             int mt, nt;
             grouped_mn(in, mt2, nt2, 4, mt, nt);
-            MNOp amn{a.dOd + (int64_t)S * H + mt * 256, H, H - mt * 256, a.wrow + S};
-            MNOp bmn{a.A + (int64_t)S * I + nt * 256, I, I - nt * 256, nullptr};
-            gemm_mainloop<false, false>(KOp{}, amn, KOp{}, bmn, kext / kBK, false, lds, acc);
-            epilogue_store_f32(acc, a.dW2 + (int64_t)l * H * I + (int64_t)mt * 256 * I + nt * 256, I, H - mt * 256,
-                               I - nt * 256);
+            const KOp ak = rows_window(a.dYT + (int64_t)mt * 256 * ldT + S, ldT, 256);
+            const KOp bk = rows_window(a.AT + (int64_t)nt * 256 * ldT + S, ldT, I - nt * 256);
+            gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, kext / 64, false, lds, acc);
+            epilogue_store_f32_w<kFwdWM, kFwdWN>(acc, a.dW2 + (int64_t)l * H * I + (int64_t)mt * 256 * I + nt * 256, I,
+                                                 256, I - nt * 256);
         } else {
             int mt, nt;
             grouped_mn(in - mt2 * nt2, mt13, nt13, 4, mt, nt);
-            MNOp amn{a.dHU + (int64_t)S * 2 * I + mt * 256, 2ll * I, 2 * I - mt * 256, nullptr};
-            MNOp bmn{a.Xd + (int64_t)S * H + nt * 256, H, H - nt * 256, nullptr};
-            gemm_mainloop<false, false>(KOp{}, amn, KOp{}, bmn, kext / kBK, false, lds, acc);
-            epilogue_store_f32(acc, a.dW13 + (int64_t)l * 2 * I * H + (int64_t)mt * 256 * H + nt * 256, H,
-                               2 * I - mt * 256, H - nt * 256);
+            const KOp ak = rows_window(a.dHUT + (int64_t)mt * 256 * ldT + S, ldT, 256);
+            const KOp bk = rows_window(a.XdT + (int64_t)nt * 256 * ldT + S, ldT, 256);
+            gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, kext / 64, false, lds, acc);
+            epilogue_store_f32_w<kFwdWM, kFwdWN>(acc, a.dW13 + (int64_t)l * 2 * I * H + (int64_t)mt * 256 * H + nt * 256,
+                                                 H, 256, 256);
         }
     }
 }

@@ -88,17 +88,23 @@ __global__ __launch_bounds__(kFwdThreads) void k_layer_fwd_persistent(LayerFwdAr
     layer_fwd_persistent_body(a, lds);
 }
 
-__global__ __launch_bounds__(256) void k_bwd_down(BwdArgs a) {
+__global__ __launch_bounds__(256) void k_transpose(TransposeArgs a) {
+    __shared__ uint16_t tile[64][72];
+    const int64_t ntiles = (int64_t)a.B * ((a.R + 63) / 64) * ((a.C + 63) / 64);
+    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) transpose_tile(a, t, tile);
+}
+
+__global__ __launch_bounds__(kFwdThreads) void k_bwd_down(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
     bwd_down_phase(a, lds);
 }
 
-__global__ __launch_bounds__(256) void k_bwd_gateup(BwdArgs a) {
+__global__ __launch_bounds__(kFwdThreads) void k_bwd_gateup(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
     bwd_gateup_phase(a, lds);
 }
 
-__global__ __launch_bounds__(256) void k_wgrad(BwdArgs a) {
+__global__ __launch_bounds__(kFwdThreads) void k_wgrad(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
     wgrad_phase(a, lds);
 }
@@ -194,10 +200,40 @@ int64_t sched_ws_bytes(const moe_desc *d) { return align256(4ll * d->num_batches
 
 int bwd_nparts(const moe_desc *d) { return 2 * ((d->I + 255) / 256); }
 
+// Leading dimension of the transposed activations (rows of length cap, padded
+// to 64 elements so every 16-byte access stays aligned).
+int64_t bwd_ldT(const moe_desc *d) { return (cap_rows(d) + 63) / 64 * 64; }
+
 int64_t bwd_ws_bytes(const moe_desc *d) {
-    const int64_t cap = cap_rows(d);
-    return align256(cap * d->H * 2) * 2 + align256(cap * 2ll * d->I * 2) + align256(cap * 4) +
-           align256(cap * 4ll * bwd_nparts(d));
+    const int64_t cap = cap_rows(d), H = d->H, I = d->I, L = d->L, ldT = bwd_ldT(d);
+    return align256(cap * H * 2) * 2 + align256(cap * 2 * I * 2) + align256(cap * 4) +
+           align256(cap * 4ll * bwd_nparts(d)) + align256(L * I * H * 2) + align256(L * H * 2 * I * 2) +
+           align256(H * ldT * 2) * 2 + align256(I * ldT * 2) + align256(2 * I * ldT * 2);
+}
+
+int launch_transpose(const TransposeArgs &t, hipStream_t s, const char *name) {
+    const int64_t ntiles = (int64_t)t.B * ((t.R + 63) / 64) * ((t.C + 63) / 64);
+    const int grid = (int)std::min<int64_t>(ntiles, 64ll * device_cus());
+    TraceScope tr(name, s);
+    hipLaunchKernelGGL(k_transpose, dim3(grid), dim3(256), 0, s, t);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+TransposeArgs make_transpose(const uint16_t *in, uint16_t *out, int32_t R, int32_t C, int32_t B, int64_t ldi,
+                             int64_t ldo, int64_t bsi, int64_t bso, const float *scale, const int32_t *nrows) {
+    TransposeArgs t;
+    t.in = in;
+    t.out = out;
+    t.scale = scale;
+    t.nrows_ptr = nrows;
+    t.ldi = ldi;
+    t.ldo = ldo;
+    t.bsi = bsi;
+    t.bso = bso;
+    t.R = R;
+    t.C = C;
+    t.B = B;
+    return t;
 }
 
 constexpr int64_t kBarrierBytes = 256;
@@ -488,18 +524,31 @@ int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes
     if ((int64_t)ws_bytes < bwd_ws_bytes(d)) return MOE_ENOSPC;
     (void)routes;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t cap = cap_rows(d);
+    const int64_t cap = cap_rows(d), H = d->H, I = d->I, L = d->L, ldT = bwd_ldT(d);
     char *p = static_cast<char *>(ws);
     BwdArgs a;
     a.dOd = reinterpret_cast<uint16_t *>(p);
-    p += align256(cap * d->H * 2);
+    p += align256(cap * H * 2);
     a.dXd = reinterpret_cast<uint16_t *>(p);
-    p += align256(cap * d->H * 2);
+    p += align256(cap * H * 2);
     a.dHU = reinterpret_cast<uint16_t *>(p);
-    p += align256(cap * 2ll * d->I * 2);
+    p += align256(cap * 2 * I * 2);
     a.wrow = reinterpret_cast<float *>(p);
     p += align256(cap * 4);
     a.part = reinterpret_cast<float *>(p);
+    p += align256(cap * 4ll * bwd_nparts(d));
+    a.W2T = reinterpret_cast<uint16_t *>(p);
+    p += align256(L * I * H * 2);
+    a.W13T = reinterpret_cast<uint16_t *>(p);
+    p += align256(L * H * 2 * I * 2);
+    a.dYT = reinterpret_cast<uint16_t *>(p);
+    p += align256(H * ldT * 2);
+    a.XdT = reinterpret_cast<uint16_t *>(p);
+    p += align256(H * ldT * 2);
+    a.AT = reinterpret_cast<uint16_t *>(p);
+    p += align256(I * ldT * 2);
+    a.dHUT = reinterpret_cast<uint16_t *>(p);
+    a.ldT = ldT;
     a.Xd = Xd;
     a.HU = HU;
     a.A = A;
@@ -512,20 +561,28 @@ int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes
     a.H = d->H;
     a.I = d->I;
     a.nparts = bwd_nparts(d);
+    const int32_t *npad = seg_off + d->L;
     // B1: reverse-combine gather of the output gradient
     rc = launch_gather(d, dOut, phi, seg_off, a.dOd, s, "bwd_gather");
     if (rc != MOE_OK) return rc;
     {
         TraceScope tr("bwd_row_weight", s);
         hipLaunchKernelGGL(k_row_weight, dim3((int)std::min<int64_t>((cap + 255) / 256, 4096)), dim3(256), 0, s, phi,
-                           seg_off + d->L, route_row, w, a.wrow, d->Np, d->K, cap);
+                           npad, route_row, w, a.wrow, d->Np, d->K, cap);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
+    // weights transposed so both operands of every data-gradient GEMM are K-contiguous
+    rc = launch_transpose(make_transpose(W2, a.W2T, (int32_t)H, (int32_t)I, (int32_t)L, I, H, H * I, I * H, nullptr,
+                                         nullptr), s, "bwd_transpose_w2");
+    if (rc != MOE_OK) return rc;
+    rc = launch_transpose(make_transpose(W13, a.W13T, (int32_t)(2 * I), (int32_t)H, (int32_t)L, H, 2 * I, 2 * I * H,
+                                         H * 2 * I, nullptr, nullptr), s, "bwd_transpose_w13");
+    if (rc != MOE_OK) return rc;
     const int grid = gemm_grid();
     // B2: down-projection dgrad with the SwiGLU backward and dw partials
     {
         TraceScope tr("bwd_down", s);
-        hipLaunchKernelGGL(k_bwd_down, dim3(grid), dim3(kGemmThreads), 0, s, a);
+        hipLaunchKernelGGL(k_bwd_down, dim3(grid), dim3(kFwdThreads), 0, s, a);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
     const int64_t nslots = (int64_t)d->P * d->Np * d->K;
@@ -538,15 +595,29 @@ int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes
     // B3: gate/up dgrad
     {
         TraceScope tr("bwd_gateup", s);
-        hipLaunchKernelGGL(k_bwd_gateup, dim3(grid), dim3(kGemmThreads), 0, s, a);
+        hipLaunchKernelGGL(k_bwd_gateup, dim3(grid), dim3(kFwdThreads), 0, s, a);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
     // B4: reverse-dispatch sum over each token's local slots
     rc = launch_combine(d, a.dXd, route_row, nullptr, dX, s, "bwd_reverse_dispatch");
     if (rc != MOE_OK) return rc;
+    // activations transposed (rows [0, Npad)) so the weight gradients reduce
+    // over K-contiguous rows; the router weight is folded into dO_d here
+    rc = launch_transpose(make_transpose(a.dOd, a.dYT, (int32_t)cap, (int32_t)H, 1, H, ldT, 0, 0, a.wrow, npad), s,
+                          "bwd_transpose_dy");
+    if (rc != MOE_OK) return rc;
+    rc = launch_transpose(make_transpose(A, a.AT, (int32_t)cap, (int32_t)I, 1, I, ldT, 0, 0, nullptr, npad), s,
+                          "bwd_transpose_a");
+    if (rc != MOE_OK) return rc;
+    rc = launch_transpose(make_transpose(a.dHU, a.dHUT, (int32_t)cap, (int32_t)(2 * I), 1, 2 * I, ldT, 0, 0, nullptr,
+                                         npad), s, "bwd_transpose_dhu");
+    if (rc != MOE_OK) return rc;
+    rc = launch_transpose(make_transpose(Xd, a.XdT, (int32_t)cap, (int32_t)H, 1, H, ldT, 0, 0, nullptr, npad), s,
+                          "bwd_transpose_xd");
+    if (rc != MOE_OK) return rc;
     // B5: weight gradients, after every data gradient, fixed row order
     TraceScope tr("bwd_wgrad", s);
-    hipLaunchKernelGGL(k_wgrad, dim3(grid), dim3(kGemmThreads), 0, s, a);
+    hipLaunchKernelGGL(k_wgrad, dim3(grid), dim3(kFwdThreads), 0, s, a);
     return launch_status();
 }
 

@@ -121,4 +121,65 @@ __device__ void dw_finalize_body(const int32_t *__restrict__ route_row, const fl
     dw[slot] = s;
 }
 
+// Tiled bf16 transpose: out[b][c][r] = in[b][r][c] * scale[b*rscale + r] (no
+// scale if scale == nullptr), for rows r < nrows and columns c < C.  A
+// workgroup of 256 threads moves one 64 x 64 tile through LDS: rows are read
+// and columns written with 16-byte accesses.  nrows_ptr (device, nullable)
+// caps the rows at run time.
+struct TransposeArgs {
+    const uint16_t *in;
+    uint16_t *out;
+    const float *scale;
+    const int32_t *nrows_ptr;
+    int64_t ldi, ldo, bsi, bso;  // row strides and batch strides (elements)
+    int32_t R, C, B;
+};
+
+__device__ __forceinline__ void transpose_tile(const TransposeArgs &a, int64_t tile, uint16_t (*lds)[72]) {
+    const int ct = (a.C + 63) / 64, rt = (a.R + 63) / 64;
+    const int b = (int)(tile / ((int64_t)ct * rt));
+    const int rem = (int)(tile % ((int64_t)ct * rt));
+    const int r0 = (rem / ct) * 64, c0 = (rem % ct) * 64;
+    int nrows = a.R;
+    if (a.nrows_ptr) nrows = min(nrows, *a.nrows_ptr);
+    if (r0 >= nrows) return;
+    const uint16_t *in = a.in + (int64_t)b * a.bsi;
+    uint16_t *out = a.out + (int64_t)b * a.bso;
+    const int t = threadIdx.x;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int rr = (t >> 3) + 32 * i, cc = (t & 7) * 8;
+        const int r = r0 + rr, c = c0 + cc;
+        u32x4 v = u32x4{0, 0, 0, 0};
+        if (r < nrows && c < a.C) v = *reinterpret_cast<const u32x4 *>(in + (int64_t)r * a.ldi + c);
+        float sc = 1.0f;
+        if (a.scale && r < nrows) sc = a.scale[(int64_t)b * a.R + r];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t x = v[d];
+            if (a.scale) x = pack_bf2(__uint_as_float(x << 16) * sc, __uint_as_float(x & 0xffff0000u) * sc);
+            lds[cc + 2 * d][rr] = (uint16_t)(x & 0xffffu);
+            lds[cc + 2 * d + 1][rr] = (uint16_t)(x >> 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int cc = (t >> 3) + 32 * i, rr = (t & 7) * 8;
+        const int r = r0 + rr, c = c0 + cc;
+        if (c < a.C && r < nrows) {
+            const uint16_t *src = &lds[cc][rr];
+            u32x4 v;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) v[d] = (uint32_t)src[2 * d] | ((uint32_t)src[2 * d + 1] << 16);
+            if (r + 8 <= nrows) {
+                *reinterpret_cast<u32x4 *>(out + (int64_t)c * a.ldo + r) = v;
+            } else {
+                for (int e = 0; r + e < nrows; ++e) out[(int64_t)c * a.ldo + r + e] = src[e];
+            }
+        }
+    }
+}
+
 }  // namespace moe
