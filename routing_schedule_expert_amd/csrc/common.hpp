@@ -41,34 +41,93 @@ __device__ __forceinline__ uint64_t match_lanes(uint32_t v, int nbits) {
 }
 
 // Device-wide barrier for a cooperative (all workgroups resident) launch.
-// `bar` points at zero-initialised uint32 words: [0] arrival count, [1]
-// generation, [2] set to 1 if a wait ever gave up.  Every workgroup calls it
-// the same number of times.  The wait is bounded (about a second of polling):
-// if the grid were not co-resident the kernel finishes with undefined
-// results and bar[2] = 1 instead of hanging the device.
-__device__ __forceinline__ void grid_barrier(uint32_t *bar, uint32_t nblocks) {
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        uint32_t gen = __hip_atomic_load(bar + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-        uint32_t arrived = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (arrived == nblocks - 1) {
-            __hip_atomic_store(bar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(bar + 1, gen + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            for (uint32_t spins = 0;
-                 __hip_atomic_load(bar + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == gen; ++spins) {
-                if (spins > (1u << 24)) {
-                    __hip_atomic_store(bar + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
+//
+// Memory on this part is cached per XCD (each XCD has its own L2), so data
+// written before a barrier by one XCD must be written back from its L2 and
+// the readers' L2 must be invalidated.  Doing that from every workgroup
+// (one agent-scope fence each) costs tens of microseconds per barrier; here one
+// elected workgroup per XCD does it for all workgroups of its XCD:
+//   1. every wave waits for its own stores (s_waitcnt), then the workgroup
+//      arrives at its XCD's counter;
+//   2. the last arrival of an XCD writes back that XCD's L2 (release fence)
+//      and arrives at the device counter; the last XCD publishes the epoch;
+//   3. each XCD's elected workgroup then invalidates its L2 (acquire fence)
+//      and releases its XCD; the other workgroups take an acquire fence too,
+//      which drops their L1 (the shared L2 holds no stale lines by then).
+// Every workgroup counts the barriers it has passed (`epoch`), so all waits are
+// for an exact value and no counter is ever reset: after barrier e the XCD
+// counter of x holds e * (workgroups on x), the device counter e * (XCDs in
+// use), the device epoch and the release word of every XCD hold e.
+// Words of `bar` (zero on entry, 64 words): [0] device arrivals, [1] device
+// epoch, [2] set if a wait gave up, [4] census arrivals, [8+x] arrivals of XCD
+// x, [16+x] release epoch of XCD x, [24+x] workgroups on XCD x, [32] XCDs in
+// use.  Every wait is bounded (about a second): if the grid were not
+// co-resident the kernel finishes with undefined results and bar[2] = 1
+// instead of hanging.  Only thread 0 of a workgroup holds meaningful fields.
+
+__device__ __forceinline__ uint32_t xcc_id() {
+    uint32_t v;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+    return v & 7u;
+}
+
+__device__ __forceinline__ uint32_t ld_agent(uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void spin_until_equal(uint32_t *p, uint32_t want, uint32_t *flag) {
+    for (uint32_t spins = 0; ld_agent(p) != want; ++spins) {
+        if (spins > (1u << 22)) {
+            __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+struct GridBarrier {
+    uint32_t *bar;
+    uint32_t xcc, here, nxcc, epoch;
+
+    // Registers this workgroup's XCD; one fenced barrier publishes the census.
+    __device__ __forceinline__ explicit GridBarrier(uint32_t *b) : bar(b), xcc(0), here(0), nxcc(0), epoch(0) {
+        if (threadIdx.x == 0) {
+            xcc = xcc_id();
+            if (__hip_atomic_fetch_add(bar + 24 + xcc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+                __hip_atomic_fetch_add(bar + 32, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __threadfence();
+            __hip_atomic_fetch_add(bar + 4, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            spin_until_equal(bar + 4, gridDim.x, bar + 2);
+            __threadfence();
+            here = ld_agent(bar + 24 + xcc);
+            nxcc = ld_agent(bar + 32);
+        }
+        __syncthreads();
+    }
+
+    __device__ __forceinline__ void sync() {
+        __builtin_amdgcn_s_waitcnt(0);  // every wave's stores have reached its XCD's L2
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t e = ++epoch;
+            const uint32_t n = __hip_atomic_fetch_add(bar + 8 + xcc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (n == e * here - 1) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // write back this XCD's L2
+                const uint32_t m = __hip_atomic_fetch_add(bar, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                if (m == e * nxcc - 1)
+                    __hip_atomic_store(bar + 1, e, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                else
+                    spin_until_equal(bar + 1, e, bar + 2);
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // invalidate this XCD's L2
+                __hip_atomic_store(bar + 16 + xcc, e, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                spin_until_equal(bar + 16 + xcc, e, bar + 2);
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // invalidate this CU's L1
             }
         }
-        __threadfence();
+        __syncthreads();
     }
-    __syncthreads();
-}
+};
 
 }  // namespace moe
 

@@ -93,7 +93,7 @@ __device__ __forceinline__ void ffn_down_phase(const FfnArgs &a, int r0, int r1,
 }
 
 // Chunked pipeline: phase p = gate/up of chunk p and down of chunk p-1.
-__device__ __forceinline__ void ffn_chunked_body(const FfnArgs &a, char *lds) {
+__device__ __forceinline__ void ffn_chunked_body(const FfnArgs &a, char *lds, GridBarrier &gb) {
     const int npad = a.seg_off[a.L];
     const int T = a.chunk_rows;
     const int nchunks = (npad + T - 1) / T;
@@ -115,7 +115,7 @@ __device__ __forceinline__ void ffn_chunked_body(const FfnArgs &a, char *lds) {
                 ffn_down_tile(a, dn0 / kBM + m, n, lds);
             }
         }
-        grid_barrier(a.bar, gridDim.x);
+        gb.sync();
     }
 }
 
@@ -137,24 +137,25 @@ __device__ __forceinline__ void layer_fwd_persistent_body(const LayerFwdArgs &a,
     const SchedArgs &s = a.sched;
     const int nitems = s.P * s.wg_per_part;
     int32_t *smem = reinterpret_cast<int32_t *>(lds);
+    GridBarrier gb(a.ffn.bar);
     for (int x = blockIdx.x; x < nitems; x += gridDim.x) sched_count_body(s, smem, x);
-    grid_barrier(a.ffn.bar, gridDim.x);
+    gb.sync();
     if (blockIdx.x == 0) sched_finalize(s, 0, smem);
-    grid_barrier(a.ffn.bar, gridDim.x);
+    gb.sync();
     for (int x = blockIdx.x; x < nitems; x += gridDim.x) sched_scatter_body(s, smem, x);
-    grid_barrier(a.ffn.bar, gridDim.x);
+    gb.sync();
     const int waves = blockDim.x / kWave;
     gather_rows_body(a.X, s.phi, s.seg_off + s.L, const_cast<uint16_t *>(a.ffn.Xd), a.Np, a.ffn.H, 0, a.cap,
                      blockIdx.x * waves + threadIdx.x / kWave, gridDim.x * waves);
-    grid_barrier(a.ffn.bar, gridDim.x);
+    gb.sync();
     if (a.ffn.chunk_rows > 0) {
-        ffn_chunked_body(a.ffn, lds);
+        ffn_chunked_body(a.ffn, lds, gb);
     } else {
         const int npad = a.ffn.seg_off[a.ffn.L];
         ffn_gateup_phase(a.ffn, 0, npad, lds);
-        grid_barrier(a.ffn.bar, gridDim.x);
+        gb.sync();
         ffn_down_phase(a.ffn, 0, npad, lds);
-        grid_barrier(a.ffn.bar, gridDim.x);
+        gb.sync();
     }
     combine_body(a.ffn.Y, s.route_row, a.w, a.out, a.K, a.ffn.H, 0, a.ntok,
                  blockIdx.x * waves + threadIdx.x / kWave, gridDim.x * waves);

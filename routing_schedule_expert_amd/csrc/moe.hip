@@ -80,7 +80,8 @@ __global__ __launch_bounds__(kFwdThreads) void k_ffn_down(FfnArgs a) {
 
 __global__ __launch_bounds__(kFwdThreads) void k_ffn_chunked(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
-    ffn_chunked_body(a, lds);
+    GridBarrier gb(a.bar);
+    ffn_chunked_body(a, lds, gb);
 }
 
 __global__ __launch_bounds__(kFwdThreads) void k_layer_fwd_persistent(LayerFwdArgs a) {
