@@ -47,16 +47,36 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, launches_per_step: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_kimi_traffic.json")
+def measured_traffic(kernel: str):
+    """HBM bytes per launch (fetched + written) from the committed rocprofv3
+    counter summary, or None when the kernel sources changed since the
+    counters were taken.  The summary holds `key: value` lines."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_kimi_traffic.md")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
+    rec = {}
+    for ln in open(path):
+        if ":" in ln and not ln.startswith((" ", "#", "|", "`")):
+            k, v = ln.split(":", 1)
+            rec[k.strip()] = v.strip()
     if rec.get("kernel_source_digest") != kernel_source_digest():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    try:
+        return int(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch, dev, mib: int):
+    """One plain elementwise kernel of known traffic (reads and writes `mib`
+    MiB of float32), for scaling the HBM byte counters of a profiled run."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def bench_layer(args, torch, ops, inputs, dev):
@@ -280,6 +300,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-schedule", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the layer steps, run one plain read+write kernel over this many MiB (counter scaling)")
     ap.add_argument("--workload", default="kimi", choices=["kimi", "kimi_bwd", "mid_tc"],
                     help="kimi: the contract line (default); kimi_bwd / mid_tc: extra measurements")
     args = ap.parse_args()
@@ -305,6 +327,8 @@ def main():
         return
     print("[bench] layer forward, Kimi shape", file=sys.stderr, flush=True)
     L_res = bench_layer(args, torch, ops, inputs, dev)
+    if args.copy_calibration_mib > 0:
+        copy_calibration(torch, dev, args.copy_calibration_mib)
     ms = L_res["ms_step"]
     value = L_res["flops"] / (ms / 1e3) / 1e12
     st = L_res["stage_ms"]
@@ -313,7 +337,7 @@ def main():
     if k_main:
         ach = L_res["flops_gateup"] / (st[k_main] / 1e3) / 1e12
         roofline = {"bound": "mfma", "kernel": k_main, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic(k_main, 1),
+                    "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic(k_main),
                     "algorithmic_flop_per_launch": L_res["flops_gateup"], "avg_launch_ms": st[k_main]}
     down = None
     if "ffn_down" in st:
