@@ -430,36 +430,40 @@ __device__ __forceinline__ void dma_k_w(const KOp &op, int k0, char *tile) {
     }
 }
 
-template <int BKT, int SW, int MI, int NI>
-__device__ __forceinline__ void compute_stage_w(const char *stage, int arow, const int (&brow)[NI], int lane,
-                                                f32x16 (&acc)[MI][NI]) {
-    constexpr int tile_bytes = 256 * BKT * 2;
-#pragma unroll
-    for (int s = 0; s < BKT / 16; ++s) {
-        const int kc = 2 * s + (lane >> 5);
-        bf16x8 fa[MI], fb[NI];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-            fa[mi] = *reinterpret_cast<const bf16x8 *>(stage + tile_off_t<BKT, SW>(arow + mi * 32, kc));
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-            fb[ni] = *reinterpret_cast<const bf16x8 *>(stage + tile_bytes + tile_off_t<BKT, SW>(brow[ni], kc));
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
-    }
+// The i-th of this wave's DMA instructions for one K-contiguous [256][BKT]
+// tile (the same 1 KiB blocks dma_k_w fills, one at a time).
+template <int BKT, int SW, int NW>
+__device__ __forceinline__ void dma_blk_w(const KOp &op, int k0, char *tile, int i) {
+    constexpr int blks_per_wave = 256 * BKT * 2 / 1024 / NW;
+    const int t = threadIdx.x, w = t >> 6, L = t & 63;
+    const int blk = w * blks_per_wave + i;
+    int row, kc;
+    tile_slot_owner<BKT, SW>(blk * 1024 + L * 16, row, kc);
+    const uint16_t *p = (row < 128 ? op.lo : op.hi) + (int64_t)(row & 127) * op.ld + k0 + kc * 8;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(p), (lds_void_t *)(tile + blk * 1024), 16, 0, 0);
 }
 
-template <int WM, int WN, int BKT, int NST, int SW, int LDS_BYTES = kGemmLds>
+// Main loop with NST stages of BKT.  The DMA instructions that fill stage
+// kt+NST-1 are not issued in one burst after the barrier: they are spread
+// over the first SPREAD sub-steps of stage kt, one after every few MFMAs
+// (pinned there with sched_group_barrier), so a wave blocked on a full
+// vector-memory queue still has MFMAs of its own in flight and the two waves
+// of a SIMD keep the matrix unit busy.  Measured at the gate/up shape: about
+// 10% faster than the burst.
+template <int WM, int WN, int BKT, int NST, int SW, int LDS_BYTES = kGemmLds, int SPREAD = 2>
 __device__ __forceinline__ void gemm_mainloop_w(const KOp &ak, const KOp &bk, int nk, bool swiglu, char *lds,
                                                 AccW<WM, WN> &acc) {
     using WG = WaveGrid<WM, WN>;
-    constexpr int MI = WG::MI, NI = WG::NI;
+    constexpr int MI = WG::MI, NI = WG::NI, NW = WG::NW;
     constexpr int tile_bytes = 256 * BKT * 2;
     constexpr int stage_bytes = 2 * tile_bytes;
-    constexpr int G = 2 * (tile_bytes / 1024) / WG::NW;  // DMA instructions per wave per stage
+    constexpr int GH = tile_bytes / 1024 / NW;  // DMA instructions per wave per operand per stage
+    constexpr int G = 2 * GH;
+    constexpr int S = BKT / 16;                 // MFMA sub-steps per stage
+    static_assert(SPREAD >= 1 && SPREAD <= S && G % SPREAD == 0, "DMA spread");
+    constexpr int D = G / SPREAD;               // DMA instructions per sub-step
+    static_assert((MI * NI) % D == 0, "DMA slots");
+    constexpr int EVERY = MI * NI / D;          // MFMAs between two DMA instructions
     static_assert(NST >= 2 && NST * stage_bytes <= LDS_BYTES, "LDS budget");
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
     const int wm = wave / WN, wn = wave % WN;
@@ -478,21 +482,47 @@ __device__ __forceinline__ void gemm_mainloop_w(const KOp &ak, const KOp &bk, in
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
         if (s < nk) {
-            dma_k_w<BKT, SW, WG::NW>(ak, s * BKT, lds + s * stage_bytes);
-            dma_k_w<BKT, SW, WG::NW>(bk, s * BKT, lds + s * stage_bytes + tile_bytes);
+            dma_k_w<BKT, SW, NW>(ak, s * BKT, lds + s * stage_bytes);
+            dma_k_w<BKT, SW, NW>(bk, s * BKT, lds + s * stage_bytes + tile_bytes);
         }
     int slot = 0;
     for (int kt = 0; kt < nk; ++kt) {
         if (kt + NST - 2 < nk) wait_vm_barrier<G * (NST - 2)>();
         else wait_vm_barrier<0>();
         const int ahead = kt + NST - 1;
-        if (ahead < nk) {
-            int as = slot + NST - 1;
-            if (as >= NST) as -= NST;
-            dma_k_w<BKT, SW, WG::NW>(ak, ahead * BKT, lds + as * stage_bytes);
-            dma_k_w<BKT, SW, WG::NW>(bk, ahead * BKT, lds + as * stage_bytes + tile_bytes);
+        const bool fill = ahead < nk;
+        int as = slot + NST - 1;
+        if (as >= NST) as -= NST;
+        char *dst = lds + as * stage_bytes;
+        const char *stage = lds + slot * stage_bytes;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int kc = 2 * s + (lane >> 5);
+            bf16x8 fa[MI], fb[NI];
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+                fa[mi] = *reinterpret_cast<const bf16x8 *>(stage + tile_off_t<BKT, SW>(arow + mi * 32, kc));
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+                fb[ni] = *reinterpret_cast<const bf16x8 *>(stage + tile_bytes + tile_off_t<BKT, SW>(brow[ni], kc));
+#pragma unroll
+            for (int q = 0; q < MI * NI; ++q) {
+                acc[q / NI][q % NI] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q / NI], fb[q % NI], acc[q / NI][q % NI], 0, 0, 0);
+                if (s < SPREAD && (q + 1) % EVERY == 0 && fill) {
+                    const int g = s * D + (q + 1) / EVERY - 1;
+                    if (g < GH) dma_blk_w<BKT, SW, NW>(ak, ahead * BKT, dst, g);
+                    else dma_blk_w<BKT, SW, NW>(bk, ahead * BKT, dst + tile_bytes, g - GH);
+                }
+            }
+            if (s < SPREAD) {
+#pragma unroll
+                for (int j = 0; j < D; ++j) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, EVERY, 0);  // EVERY MFMAs
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // then one VMEM read (the DMA)
+                }
+            }
         }
-        compute_stage_w<BKT, SW, MI, NI>(lds + slot * stage_bytes, arow, brow, lane, acc);
         if (++slot == NST) slot = 0;
     }
     __syncthreads();
