@@ -120,18 +120,22 @@ def bench_layer(args, torch, ops, inputs, dev):
                 flops_down=flops_down, local_routes=local_routes, npad=npad, routes=routes, w=w)
 
 
-def bench_schedule(args, torch, ops, inputs, dev, nb, kind="uniform"):
-    c = KIMI
-    rng = inputs.rng_for(2)
+def bench_schedule(args, torch, ops, inputs, dev, nb, kind="uniform", P=8, Np=7168, E=384, K=8, L=48, distinct=8):
+    """The schedule alone on `nb` routing tensors per call.  For nb > distinct
+    the host draws `distinct` tables and repeats them (the tables are
+    independent on the device, so the work is the same)."""
+    rng = inputs.rng_for(2 if kind == "uniform" else 3)
+    nd = min(nb, distinct)
     if kind == "uniform":
-        r = np.stack([inputs.routes_uniform(rng, c["P"], c["Np"], c["E"], c["K"])[0] for _ in range(nb)])
+        base = [inputs.routes_uniform(rng, P, Np, E, K)[0] for _ in range(nd)]
     else:
-        r = np.stack([inputs.routes_zipf(rng, c["P"], c["Np"], c["E"], c["K"], 1.2)[0] for _ in range(nb)])
-    d = ops.make_desc(c["P"], c["Np"], c["K"], c["E"], c["L"], num_batches=nb)
+        base = [inputs.routes_zipf(rng, P, Np, E, K, 1.2)[0] for _ in range(nd)]
+    r = np.stack([base[i % nd] for i in range(nb)])
+    d = ops.make_desc(P, Np, K, E, L, num_batches=nb)
     cap = ops.capacity_rows(d)
     rt = torch.from_numpy(r).to(dev)
-    counts = torch.empty((nb, c["L"], c["P"]), dtype=torch.int32, device=dev)
-    seg_off = torch.empty((nb, c["L"] + 1), dtype=torch.int32, device=dev)
+    counts = torch.empty((nb, L, P), dtype=torch.int32, device=dev)
+    seg_off = torch.empty((nb, L + 1), dtype=torch.int32, device=dev)
     phi = torch.empty((nb, cap, 2), dtype=torch.int32, device=dev)
     route_row = torch.empty_like(rt)
     ws = torch.empty(ops.workspace_bytes(d, ops.MOE_OP_SCHEDULE), dtype=torch.uint8, device=dev)
@@ -156,12 +160,55 @@ def bench_schedule(args, torch, ops, inputs, dev, nb, kind="uniform"):
         split.setdefault(name, []).append(t)
     ops.moe_trace_enable(0)
     split = {k: float(np.mean(v)) for k, v in split.items()}
-    routes = nb * c["P"] * c["Np"] * c["K"]
+    routes = nb * P * Np * K
     npad = seg_off[:, -1].to(torch.int64).sum().item()
     compulsory = routes * 4 + routes * 4 + npad * 8  # read ids, write route_row, write the table
-    return dict(nb=nb, routing=kind, ms=ms, split_ms=split, routes_per_s=routes / (ms / 1e3),
+    two_pass = routes * 4 * 2 + routes * 4 + npad * 8  # as described: the ids are read twice
+    local = int(((r >= 0) & (r < L)).sum())
+    return dict(nb=nb, routing=kind, P=P, Np=Np, E=E, K=K, L=L, ms=ms, split_ms=split,
+                routes_per_s=routes / (ms / 1e3), local_routes=local, dispatched_rows=npad,
                 compulsory_bytes=compulsory, gbs=compulsory / (ms / 1e3) / 1e9,
-                hbm_frac=compulsory / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, routes=r)
+                hbm_frac=compulsory / (ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                two_pass_bytes=two_pass, two_pass_frac=two_pass / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, routes=r)
+
+
+def copy_bandwidth(torch, dev, mib: int = 2048, reps: int = 10) -> float:
+    """Measured device-to-device streaming rate (GB/s, read + write bytes) of
+    one plain elementwise kernel over `mib` MiB, for context beside 8 TB/s."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2.0 * n * 4 / (ms / 1e3) / 1e9
+
+
+def bench_schedule_sweep(args, torch, ops, inputs, dev):
+    """The schedule-only table: Kimi shape (8 partitions x 7,168 tokens, 384
+    experts with 48 local, top-8, rows padded to 256) at 1 and 64 routing
+    tensors per call, uniform and Zipf s=1.2 routing; then 512 tokens per
+    partition, and E in {64, 128, 256, 384} with P = 8 (L = E/8)."""
+    copy_gbs = copy_bandwidth(torch, dev)
+    rows = []
+    cases = [dict(nb=nb, kind=k) for k in ("uniform", "zipf") for nb in (1, 64)]
+    cases += [dict(nb=nb, kind="uniform", Np=512) for nb in (1, 64)]
+    cases += [dict(nb=nb, kind="uniform", E=e, L=e // 8) for e in (64, 128, 256) for nb in (1, 64)]
+    for c in cases:
+        print(f"[bench] schedule {c}", file=sys.stderr, flush=True)
+        res = bench_schedule(args, torch, ops, inputs, dev, **c)
+        res.pop("routes")
+        res["frac_of_copy"] = res["gbs"] / copy_gbs
+        rows.append(res)
+    return {"metric": "schedule routes/s and HBM fraction (compulsory bytes), 1 GPU", "unit": "routes/s",
+            "peak_GBs": PEAK_HBM_GBS, "copy_GBs": copy_gbs, "data": "synthetic", "sweep": rows}
 
 
 def bench_fwd_bwd(args, torch, ops, inputs, dev):
@@ -302,8 +349,8 @@ def main():
     ap.add_argument("--no-schedule", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the layer steps, run one plain read+write kernel over this many MiB (counter scaling)")
-    ap.add_argument("--workload", default="kimi", choices=["kimi", "kimi_bwd", "mid_tc"],
-                    help="kimi: the contract line (default); kimi_bwd / mid_tc: extra measurements")
+    ap.add_argument("--workload", default="kimi", choices=["kimi", "kimi_bwd", "mid_tc", "schedule"],
+                    help="kimi: the contract line (default); kimi_bwd / mid_tc / schedule: extra measurements")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -324,6 +371,9 @@ def main():
         return
     if args.workload == "mid_tc":
         print(json.dumps(bench_tc_sweep(args, torch, ops, inputs, dev)), flush=True)
+        return
+    if args.workload == "schedule":
+        print(json.dumps(bench_schedule_sweep(args, torch, ops, inputs, dev)), flush=True)
         return
     print("[bench] layer forward, Kimi shape", file=sys.stderr, flush=True)
     L_res = bench_layer(args, torch, ops, inputs, dev)
