@@ -2,8 +2,8 @@
 """Benchmark of one MI355X's share of the Kimi-shaped MoE layer forward.
 
 One step = one pass of the whole forward hot path through the C ABI
-(moe_layer_fwd: counting-sort schedule, pull gather, SwiGLU grouped GEMMs,
-fixed-order combine) on 8 partitions x 7,168 tokens, 384 experts (48 local),
+(moe_layer_fwd: counting-sort schedule, pull gather (by default fused into the
+gate/up GEMM's operand loads), SwiGLU grouped GEMMs, fixed-order combine) on 8 partitions x 7,168 tokens, 384 experts (48 local),
 top-8, H=7168, I=2048, balanced routing (one local route per token), bf16,
 inputs resident in HBM.  Prints ONE JSON line:
 
@@ -87,7 +87,7 @@ def bench_layer(args, torch, ops, inputs, dev):
     routes = torch.from_numpy(h["routes"]).to(dev)
     w = torch.from_numpy(h["w"]).to(dev)
     X, W13, W2 = h["X"], h["W13"], h["W2"]
-    bufs = ops.alloc_fwd(d, dev, save_hu=True)
+    bufs = ops.alloc_fwd(d, dev, save_hu=True, save_xd=args.materialize_xd)
     local_routes = int(((h["routes"] >= 0) & (h["routes"] < c["L"])).sum())
     flops = 6.0 * c["H"] * c["I"] * local_routes
     flops_gateup = 4.0 * c["H"] * c["I"] * local_routes
@@ -343,6 +343,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--persistent", action="store_true", help="time the persistent single-launch forward")
     ap.add_argument("--chunk-rows", type=int, default=0, help="minibatch of dispatched rows (multiple of 256)")
+    ap.add_argument("--materialize-xd", action="store_true",
+                    help="write the dispatched rows Xd with a separate gather (default: the gather is fused into the "
+                         "gate/up GEMM's operand loads)")
     ap.add_argument("--sched-batches", type=int, default=64)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -426,7 +429,8 @@ def main():
                    "experts": c["E"], "local_experts": c["L"], "top_k": c["K"], "H": c["H"], "I": c["I"],
                    "routing": "balanced", "pad_rows": 256, "dispatched_rows": L_res["npad"],
                    "local_routes": L_res["local_routes"], "path": "persistent" if args.persistent else "multi-launch",
-                   "chunk_rows": args.chunk_rows},
+                   "chunk_rows": args.chunk_rows,
+                   "dispatch": "separate gather" if args.materialize_xd else "fused into the gate/up operand loads"},
         "mfma_util_from_time": value / PEAK_BF16_TFLOPS,
         "stage_ms": st,
         "roofline": roofline,

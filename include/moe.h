@@ -179,6 +179,12 @@ enum {
  * workgroups pass device-side barriers between stages ([MoK] section 5,
  * megakernel fusion); otherwise one launch per stage.  Both give bitwise the
  * same results.  chunk_rows as in moe_expert_ffn.
+ * Xd may be NULL: the dispatch is then fused into the gate/up GEMM, whose
+ * operand loads pull each row from X through phi ([MoK] section 2, pull
+ * dispatch hidden behind the GEMM), and no dispatched copy is written; every
+ * other output is bitwise the same.  Needs H <= 32768 (else
+ * MOE_EUNSUPPORTED).  moe_layer_bwd needs Xd: a caller that wants the
+ * backward either passes Xd here or fills it later with moe_dispatch.
  *   ws >= moe_workspace_bytes(d, MOE_OP_LAYER_FWD)
  * Uses d->num_batches == 1.
  */

@@ -26,14 +26,25 @@ constexpr int kOpTileBytes = 256 * 64 * 2;    // one [256][64] bf16 operand tile
 constexpr int kStageBytes = 2 * kOpTileBytes;  // A + B
 constexpr int kGemmLds = 2 * kStageBytes;      // 128 KiB
 
-// A K-contiguous operand window: row `i` of the tile starts at
-// (i < 128 ? lo : hi) + (i & 127) * ld (elements), at the current k offset.
-// Every row of a K-contiguous window is valid (tiles never straddle a
-// segment, and N is a multiple of the tile).
+// A K-contiguous operand window of 256 rows.  Contiguous form (rows ==
+// nullptr): row i starts at (i < 128 ? lo : hi) + (i & 127) * ld.  Gathered
+// form: row i is source row rows[i] = (part, tok) of src, i.e. src + (part * np
+// + tok) * ld, and a row with part < 0 (segment padding) reads zeros.  Every
+// row of a window is valid (tiles never straddle a segment, and N is a
+// multiple of the tile).
 struct KOp {
     const uint16_t *lo, *hi;
     int64_t ld;
+    const moe_src *rows;
+    const uint16_t *src;
+    int32_t np;
 };
+
+// Source of the padding rows of a gathered operand: never written, so it
+// stays zero (device globals are zero-initialised when the code object is
+// loaded).  Gathered operands need K <= kZeroRowElems.
+constexpr int kZeroRowElems = 32768;
+__device__ uint16_t g_zero_row[kZeroRowElems];
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -103,37 +114,34 @@ struct WaveGrid {
 template <int WM, int WN>
 using AccW = f32x16[WaveGrid<WM, WN>::MI][WaveGrid<WM, WN>::NI];
 
-// Cache policy of the operand DMA: the default.  (sc0 measured the same at the
-// gate/up shape; the non-temporal policy was about 20% slower because it loses
-// the L2 sharing between the CUs of an XCD.)
-constexpr int kDmaPolicy = 0;
-
+// Source address (at k = 0) of this lane's 16 bytes in its i-th DMA block of
+// one [256][BKT] operand tile: each wave's i-th instruction fills a
+// contiguous 1 KiB block of the tile, lane L writing physical bytes
+// [16L, 16L+16), and the lane fetches the (row, chunk) the swizzle places
+// there.  Computed once per tile; a K step only adds k0.
 template <int BKT, int SW, int NW>
-__device__ __forceinline__ void dma_k_w(const KOp &op, int k0, char *tile) {
-    constexpr int blks_per_wave = 256 * BKT * 2 / 1024 / NW;
-    const int t = threadIdx.x, w = t >> 6, L = t & 63;
-#pragma unroll
-    for (int i = 0; i < blks_per_wave; ++i) {
-        const int blk = w * blks_per_wave + i;
-        int row, kc;
-        tile_slot_owner<BKT, SW>(blk * 1024 + L * 16, row, kc);
-        const uint16_t *p = (row < 128 ? op.lo : op.hi) + (int64_t)(row & 127) * op.ld + k0 + kc * 8;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(p), (lds_void_t *)(tile + blk * 1024), 16, 0,
-                                         kDmaPolicy);
-    }
-}
-
-// The i-th of this wave's DMA instructions for one K-contiguous [256][BKT]
-// tile (the same 1 KiB blocks dma_k_w fills, one at a time).
-template <int BKT, int SW, int NW>
-__device__ __forceinline__ void dma_blk_w(const KOp &op, int k0, char *tile, int i) {
+__device__ __forceinline__ const uint16_t *dma_src_w(const KOp &op, int i) {
     constexpr int blks_per_wave = 256 * BKT * 2 / 1024 / NW;
     const int t = threadIdx.x, w = t >> 6, L = t & 63;
     const int blk = w * blks_per_wave + i;
     int row, kc;
     tile_slot_owner<BKT, SW>(blk * 1024 + L * 16, row, kc);
-    const uint16_t *p = (row < 128 ? op.lo : op.hi) + (int64_t)(row & 127) * op.ld + k0 + kc * 8;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(p), (lds_void_t *)(tile + blk * 1024), 16, 0, kDmaPolicy);
+    const uint16_t *base;
+    if (op.rows) {
+        const uint2 s = reinterpret_cast<const uint2 *>(op.rows)[row];
+        base = (int32_t)s.x >= 0 ? op.src + ((int64_t)(int32_t)s.x * op.np + (int32_t)s.y) * op.ld : g_zero_row;
+    } else {
+        base = (row < 128 ? op.lo : op.hi) + (int64_t)(row & 127) * op.ld;
+    }
+    return base + kc * 8;
+}
+
+template <int BKT, int NW>
+__device__ __forceinline__ void dma_blk_w(const uint16_t *src, int k0, char *tile, int i) {
+    constexpr int blks_per_wave = 256 * BKT * 2 / 1024 / NW;
+    const int blk = (threadIdx.x >> 6) * blks_per_wave + i;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src + k0), (lds_void_t *)(tile + blk * 1024), 16,
+                                     0, 0);
 }
 
 // Main loop with NST stages of BKT.  The DMA instructions that fill stage
@@ -171,12 +179,21 @@ __device__ __forceinline__ void gemm_mainloop_w(const KOp &ak, const KOp &bk, in
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) brow[ni] = WG::brow(swiglu, wn, ni) + (lane & 31);
     const int arow = wm * (MI * 32) + (lane & 31);
+    const uint16_t *asrc[GH], *bsrc[GH];
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+        asrc[i] = dma_src_w<BKT, SW, NW>(ak, i);
+        bsrc[i] = dma_src_w<BKT, SW, NW>(bk, i);
+    }
     __syncthreads();  // the previous tile's epilogue may still read LDS
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
         if (s < nk) {
-            dma_k_w<BKT, SW, NW>(ak, s * BKT, lds + s * stage_bytes);
-            dma_k_w<BKT, SW, NW>(bk, s * BKT, lds + s * stage_bytes + tile_bytes);
+#pragma unroll
+            for (int i = 0; i < GH; ++i) {
+                dma_blk_w<BKT, NW>(asrc[i], s * BKT, lds + s * stage_bytes, i);
+                dma_blk_w<BKT, NW>(bsrc[i], s * BKT, lds + s * stage_bytes + tile_bytes, i);
+            }
         }
     int slot = 0;
     for (int kt = 0; kt < nk; ++kt) {
@@ -204,8 +221,8 @@ __device__ __forceinline__ void gemm_mainloop_w(const KOp &ak, const KOp &bk, in
                     __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q / NI], fb[q % NI], acc[q / NI][q % NI], 0, 0, 0);
                 if (s < SPREAD && (q + 1) % EVERY == 0 && fill) {
                     const int g = s * D + (q + 1) / EVERY - 1;
-                    if (g < GH) dma_blk_w<BKT, SW, NW>(ak, ahead * BKT, dst, g);
-                    else dma_blk_w<BKT, SW, NW>(bk, ahead * BKT, dst + tile_bytes, g - GH);
+                    if (g < GH) dma_blk_w<BKT, NW>(asrc[g], ahead * BKT, dst, g);
+                    else dma_blk_w<BKT, NW>(bsrc[g - GH], ahead * BKT, dst + tile_bytes, g - GH);
                 }
             }
             if (s < SPREAD) {

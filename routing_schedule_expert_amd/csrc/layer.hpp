@@ -30,6 +30,9 @@ namespace moe {
 constexpr int kFwdWM = 4, kFwdWN = 2;
 constexpr int kFwdThreads = 64 * kFwdWM * kFwdWN;
 
+// Xd == nullptr: the gate/up GEMM pulls its A rows straight from X through
+// the table phi (the dispatch fused into the operand loads) and no dispatched
+// copy is written.
 struct FfnArgs {
     const uint16_t *Xd, *W13, *W2;
     const int32_t *seg_off;
@@ -37,15 +40,23 @@ struct FfnArgs {
     int L, H, I;
     int32_t chunk_rows;
     uint32_t *bar;
+    const uint16_t *X;
+    const moe_src *phi;
+    int32_t Np;
 };
 
 __device__ __forceinline__ void ffn_gateup_tile(const FfnArgs &a, int mt, int nt, char *lds) {
     const int H = a.H, I = a.I;
     const int m0 = mt * kBM;
     const int l = expert_of(a.seg_off, a.L, m0);
-    const uint16_t *xa = a.Xd + (int64_t)m0 * H;
     const uint16_t *w = a.W13 + (int64_t)l * 2 * I * H;
-    KOp ak{xa, xa + 128ll * H, H};
+    KOp ak;
+    if (a.Xd) {
+        const uint16_t *xa = a.Xd + (int64_t)m0 * H;
+        ak = KOp{xa, xa + 128ll * H, H, nullptr, nullptr, 0};
+    } else {
+        ak = KOp{nullptr, nullptr, H, a.phi + m0, a.X, a.Np};
+    }
     KOp bk{w + (int64_t)nt * 128 * H, w + ((int64_t)I + nt * 128) * H, H};
     AccW<kFwdWM, kFwdWN> acc;
     gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, H / 64, true, lds, acc);
@@ -145,9 +156,11 @@ __device__ __forceinline__ void layer_fwd_persistent_body(const LayerFwdArgs &a,
     for (int x = blockIdx.x; x < nitems; x += gridDim.x) sched_scatter_body(s, smem, x);
     gb.sync();
     const int waves = blockDim.x / kWave;
-    gather_rows_body(a.X, s.phi, s.seg_off + s.L, const_cast<uint16_t *>(a.ffn.Xd), a.Np, a.ffn.H, 0, a.cap,
-                     blockIdx.x * waves + threadIdx.x / kWave, gridDim.x * waves);
-    gb.sync();
+    if (a.ffn.Xd) {
+        gather_rows_body(a.X, s.phi, s.seg_off + s.L, const_cast<uint16_t *>(a.ffn.Xd), a.Np, a.ffn.H, 0, a.cap,
+                         blockIdx.x * waves + threadIdx.x / kWave, gridDim.x * waves);
+        gb.sync();
+    }
     if (a.ffn.chunk_rows > 0) {
         ffn_chunked_body(a.ffn, lds, gb);
     } else {

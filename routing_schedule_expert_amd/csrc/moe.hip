@@ -316,9 +316,12 @@ int launch_combine(const moe_desc *d, const uint16_t *Y, const int32_t *route_ro
 
 FfnArgs make_ffn_args(const moe_desc *d, const uint16_t *Xd, const uint16_t *W13, const uint16_t *W2,
                       const int32_t *seg_off, uint16_t *HU, uint16_t *A, uint16_t *Y, int32_t chunk_rows,
-                      uint32_t *bar) {
+                      uint32_t *bar, const uint16_t *X = nullptr, const moe_src *phi = nullptr) {
     FfnArgs a;
     a.Xd = Xd;
+    a.X = X;
+    a.phi = phi;
+    a.Np = d->Np;
     a.W13 = W13;
     a.W2 = W2;
     a.seg_off = seg_off;
@@ -461,13 +464,13 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
     int rc = check_desc(d, true);
     if (rc != MOE_OK) return rc;
     if (d->num_batches != 1) return MOE_EINVAL;
-    if (!routes || !w || !X || !W13 || !W2 || !counts || !seg_off || !phi || !route_row || !Xd || !A || !Y || !out ||
-        !ws)
+    if (!routes || !w || !X || !W13 || !W2 || !counts || !seg_off || !phi || !route_row || !A || !Y || !out || !ws)
         return MOE_EINVAL;
-    const void *ptrs[] = {routes, w, X, W13, W2, counts, seg_off, phi, route_row, Xd, A, Y, out, ws};
+    const void *ptrs[] = {routes, w, X, W13, W2, counts, seg_off, phi, route_row, A, Y, out, ws};
     for (const void *p : ptrs)
         if (!aligned16(p)) return MOE_EINVAL;
-    if (HU && !aligned16(HU)) return MOE_EINVAL;
+    if ((HU && !aligned16(HU)) || (Xd && !aligned16(Xd))) return MOE_EINVAL;
+    if (!Xd && d->H > kZeroRowElems) return MOE_EUNSUPPORTED;  // padding rows read the static zero row
     if (chunk_rows < 0 || chunk_rows % 256) return MOE_EINVAL;
     if (flags & ~MOE_PERSISTENT) return MOE_EINVAL;
     if ((int64_t)ws_bytes < moe_workspace_bytes(d, MOE_OP_LAYER_FWD)) return MOE_ENOSPC;
@@ -481,7 +484,7 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
         one.num_batches = 1;
         if (sched_lds_bytes(&one, kFwdThreads / 64) > (size_t)kGemmLds) return MOE_EUNSUPPORTED;
         fill_sched_args(la.sched, &one, routes, counts, seg_off, phi, route_row, sched_ws, kFwdThreads / 64);
-        la.ffn = make_ffn_args(d, Xd, W13, W2, seg_off, HU, A, Y, chunk_rows, bar);
+        la.ffn = make_ffn_args(d, Xd, W13, W2, seg_off, HU, A, Y, chunk_rows, bar, X, phi);
         la.X = X;
         la.w = w;
         la.out = out;
@@ -502,9 +505,11 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
     one.num_batches = 1;
     rc = launch_schedule(&one, routes, counts, seg_off, phi, route_row, sched_ws, s);
     if (rc != MOE_OK) return rc;
-    rc = launch_gather(d, X, phi, seg_off, Xd, s, "dispatch");
-    if (rc != MOE_OK) return rc;
-    FfnArgs a = make_ffn_args(d, Xd, W13, W2, seg_off, HU, A, Y, chunk_rows, bar);
+    if (Xd) {
+        rc = launch_gather(d, X, phi, seg_off, Xd, s, "dispatch");
+        if (rc != MOE_OK) return rc;
+    }
+    FfnArgs a = make_ffn_args(d, Xd, W13, W2, seg_off, HU, A, Y, chunk_rows, bar, X, phi);
     rc = launch_ffn(d, a, s);
     if (rc != MOE_OK) return rc;
     return launch_combine(d, Y, route_row, w, out, s, "combine");

@@ -183,7 +183,7 @@ class FwdBuffers:
     seg_off: torch.Tensor
     phi: torch.Tensor
     route_row: torch.Tensor
-    Xd: torch.Tensor
+    Xd: torch.Tensor | None
     HU: torch.Tensor | None
     A: torch.Tensor
     Y: torch.Tensor
@@ -191,7 +191,9 @@ class FwdBuffers:
     ws: torch.Tensor
 
 
-def alloc_fwd(d: moe_desc, device, save_hu: bool = True) -> FwdBuffers:
+def alloc_fwd(d: moe_desc, device, save_hu: bool = True, save_xd: bool = True) -> FwdBuffers:
+    """Forward buffers.  save_xd=False leaves Xd out: moe_layer_fwd then pulls
+    the gate/up rows straight from X (the dispatch fused into the GEMM loads)."""
     cap = capacity_rows(d)
     i32, bf = torch.int32, torch.bfloat16
     return FwdBuffers(
@@ -199,7 +201,7 @@ def alloc_fwd(d: moe_desc, device, save_hu: bool = True) -> FwdBuffers:
         seg_off=torch.empty(d.L + 1, dtype=i32, device=device),
         phi=torch.empty((cap, 2), dtype=i32, device=device),
         route_row=torch.empty((d.P, d.Np, d.K), dtype=i32, device=device),
-        Xd=torch.empty((cap, d.H), dtype=bf, device=device),
+        Xd=torch.empty((cap, d.H), dtype=bf, device=device) if save_xd else None,
         HU=torch.empty((cap, 2 * d.I), dtype=bf, device=device) if save_hu else None,
         A=torch.empty((cap, d.I), dtype=bf, device=device),
         Y=torch.empty((cap, d.H), dtype=bf, device=device),

@@ -115,5 +115,16 @@ def test_small_workspace_and_misalignment():
     assert lib.moe_layer_bwd(ctypes.byref(d), *bargs, nbwd - 1, None) == ops.MOE_ENOSPC
 
 
+def test_fused_dispatch_needs_zero_row():
+    # Xd = NULL pulls padding rows from a 32768-element zero row: wider H is refused before any launch
+    lib = ops.load()
+    d = ops.make_desc(8, 7168, 8, 384, 48, H=32768 + 256, I=2048)
+    p = [_fake(0x10000 * (i + 1)) for i in range(8)]
+    args = p[:5] + p[:4] + [None, None, p[5], p[6], p[7]]
+    ws = lib.moe_workspace_bytes(ctypes.byref(d), ops.MOE_OP_LAYER_FWD)
+    assert ws > 0
+    assert lib.moe_layer_fwd(ctypes.byref(d), *args, 0, 0, p[0], ws, None) == ops.MOE_EUNSUPPORTED
+
+
 def test_trace_read_empty():
     assert ops.moe_trace_read(4) == []

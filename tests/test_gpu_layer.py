@@ -32,8 +32,8 @@ class Layer:
         self.W2 = up_bf16(self.h["W2"])
         self.dOut = up_bf16(self.h["dOut"]) if grad else None
 
-    def fwd(self, flags=0, chunk_rows=0, save_hu=True):
-        b = ops.alloc_fwd(self.d, dev(), save_hu=save_hu)
+    def fwd(self, flags=0, chunk_rows=0, save_hu=True, save_xd=True):
+        b = ops.alloc_fwd(self.d, dev(), save_hu=save_hu, save_xd=save_xd)
         ops.layer_fwd(self.d, self.routes, self.w, self.X, self.W13, self.W2, b, flags=flags, chunk_rows=chunk_rows)
         torch.cuda.synchronize()
         return b
@@ -106,6 +106,36 @@ def test_forward_paths_agree_bitwise():
         assert digest(b.out) == digest(ref.out)
         assert digest(b.Y[:npad], b.A[:npad], b.HU[:npad]) == digest(ref.Y[:npad], ref.A[:npad], ref.HU[:npad])
         assert digest(b.phi[:npad], b.route_row, b.seg_off) == digest(ref.phi[:npad], ref.route_row, ref.seg_off)
+
+
+def test_forward_fused_dispatch_bitwise():
+    """Xd = NULL: the gate/up GEMM pulls its rows from X through phi; every
+    output must be bitwise the one of the materialised dispatch, on the
+    multi-launch, persistent and chunked paths."""
+    lay = Layer(9, 4, 900, 16, 4, 8, 512, 384, routing="zipf", s=1.2)
+    ref = lay.fwd()
+    npad = int(ref.seg_off[-1])
+    for flags, chunk in ((0, 0), (ops.MOE_PERSISTENT, 0), (0, 512), (ops.MOE_PERSISTENT, 256)):
+        print(f"[layer] fused dispatch flags={flags} chunk_rows={chunk}", flush=True)
+        b = lay.fwd(flags=flags, chunk_rows=chunk, save_xd=False)
+        assert b.Xd is None
+        assert digest(b.out) == digest(ref.out)
+        assert digest(b.Y[:npad], b.A[:npad], b.HU[:npad]) == digest(ref.Y[:npad], ref.A[:npad], ref.HU[:npad])
+        assert digest(b.phi[:npad], b.route_row, b.seg_off) == digest(ref.phi[:npad], ref.route_row, ref.seg_off)
+
+
+def test_fused_dispatch_vs_oracle():
+    lay = Layer(10, 2, 256, 8, 2, 4, 256, 128, routing="topk", x_std=0.02)
+    b = lay.fwd(save_xd=False)
+    h = lay.h
+    s = lay.oracle_schedule()
+    np.testing.assert_array_equal(b.phi[: s.npad].cpu().numpy(), s.phi)
+    r = oracle.expert_ffn_rows(s.seg_off, oracle.dispatch(h["X"], s.phi), h["W13"], h["W2"])
+    real = s.phi[:, 0] >= 0
+    assert rel_l2(f64(b.A[: s.npad])[real], r["A"][real]) <= TOL
+    assert not f64(b.Y[: s.npad])[~real].any()  # padding rows read the zero row
+    out = oracle.layer_fwd_tokens(h["routes"], h["w"], h["X"], h["W13"], h["W2"], L=lay.L)
+    assert rel_l2(f64(b.out).reshape(out.shape), out) <= TOL
 
 
 def test_forward_without_saved_hu():
