@@ -264,6 +264,8 @@ void fill_sched_args(SchedArgs &a, const moe_desc *d, const int32_t *routes, int
     a.cap = cap_rows(d);
 }
 
+constexpr size_t kMaxLds = 160 * 1024;  // LDS of one gfx950 workgroup
+
 // LDS (bytes) of the schedule bodies for `wpw` waves per workgroup.
 size_t sched_lds_bytes(const moe_desc *d, int wpw) {
     const size_t L = d->L, P = d->P;
@@ -279,6 +281,7 @@ int launch_schedule(const moe_desc *d, const int32_t *routes, int32_t *counts, i
     const int wg_per_batch = a.P * a.wg_per_part;
     const int grid = a.nb >= 8 ? 8 * ((a.nb + 7) / 8) * wg_per_batch : a.nb * wg_per_batch;
     const size_t lds = sched_lds_bytes(d, kSchedWaves);
+    if (lds > kMaxLds) return MOE_EUNSUPPORTED;
     {
         TraceScope tr("sched_count", s);
         hipLaunchKernelGGL(k_sched_count, dim3(grid), dim3(64 * kSchedWaves), lds, s, a);

@@ -126,5 +126,15 @@ def test_fused_dispatch_needs_zero_row():
     assert lib.moe_layer_fwd(ctypes.byref(d), *args, 0, 0, p[0], ws, None) == ops.MOE_EUNSUPPORTED
 
 
+def test_schedule_lds_limit():
+    # 4,096 local experts: the scatter's per-expert LDS tables exceed 160 KiB -> refused before any launch
+    lib = ops.load()
+    d = ops.make_desc(4, 1024, 8, 4096, 4096)
+    ws = lib.moe_workspace_bytes(ctypes.byref(d), ops.MOE_OP_SCHEDULE)
+    assert ws > 0
+    p = [_fake(0x10000 * (i + 1)) for i in range(6)]
+    assert lib.moe_schedule(ctypes.byref(d), *p, ws, None) == ops.MOE_EUNSUPPORTED
+
+
 def test_trace_read_empty():
     assert ops.moe_trace_read(4) == []
