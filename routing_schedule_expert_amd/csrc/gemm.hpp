@@ -381,44 +381,83 @@ __device__ __forceinline__ void epilogue_store_f32_w(AccW<WM, WN> &acc, float *d
     }
 }
 
-// Down-projection dgrad tile dA' (256 rows x 256 columns of I, columns from
-// n0) -> SwiGLU backward and the router-weight partial sums:
-//   dA = w dA'; dh = dA * u * silu'(h); du = dA * silu(h)  -> dHU (bf16)
-//   part[row][(n0 / 256) * WN + wn] = sum over the wave's columns of dA' * a
-// A, HU, wrow, dHU, part are already offset to the tile's first row.
+// Down-dgrad tile -> SwiGLU backward.  acc holds dA' = dO_d W2 for 256 rows
+// and the 256 columns [n0, n0+256) of the I activations; with w the row's
+// router weight, h, u the saved gate/up pre-activations and a the activation:
+//   dA = w dA',  dh = dA u s (1 + h (1 - s)),  du = dA h s  (s = sigmoid(h)),
+//   part[row][n0/256] = sum over the tile's columns of dA' a  (the router-
+//   weight gradient's partial dot product, SonicMoE form).
+// The fp32 tile goes through LDS in two 128-row halves (128 KiB each); then
+// every thread takes 8 contiguous columns of one row, so A, h, u are read and
+// dh, du written with 16-byte accesses, and the 32 threads of a row add their
+// partial dots in a fixed butterfly (ascending columns inside a thread).
 template <int WM, int WN>
-__device__ __forceinline__ void epilogue_swiglu_bwd_w(AccW<WM, WN> &acc, const uint16_t *A, const uint16_t *HU,
-                                                      const float *wrow, uint16_t *dHU, float *part, int nparts, int I,
-                                                      int n0) {
+__device__ __forceinline__ void epilogue_swiglu_bwd_w(AccW<WM, WN> &acc, char *lds, const uint16_t *A,
+                                                      const uint16_t *HU, const float *wrow, uint16_t *dHU,
+                                                      float *part, int nparts, int I, int n0) {
     using WG = WaveGrid<WM, WN>;
+    constexpr int NT = WG::THREADS;
+    static_assert((128 * 32) % NT == 0, "every thread runs the same number of chunks");
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63, wm = wave / WN, wn = wave % WN;
+    float *st = reinterpret_cast<float *>(lds);  // [128][256]
+    const int ncols = min(256, I - n0);          // a multiple of 128
+    const int64_t ld2 = 2ll * I;
+    // this wave's rows all lie in one half; each lane writes at compile-time
+    // offsets (< 64 KiB) from one base
+    constexpr int rows_per_wave = 256 / WM;
+    static_assert(rows_per_wave <= 128 && 128 % rows_per_wave == 0, "a wave's rows stay in one half");
+    const int my_half = (wm * rows_per_wave) / 128;
+    float *base = st + ((wm * rows_per_wave) % 128 + 4 * (lane >> 5)) * 256 + wn * (WG::NI * 32) + (lane & 31);
 #pragma unroll
-    for (int mi = 0; mi < WG::MI; ++mi) {
+    for (int half = 0; half < 2; ++half) {
+        __syncthreads();  // the main loop or the previous half is done with LDS
+        if (my_half == half) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int row = WG::row(wm, mi, e, lane);
-            const float wr = wrow[row];
+            for (int mi = 0; mi < WG::MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < WG::NI; ++ni)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        base[(mi * 32 + 8 * (e >> 2) + (e & 3)) * 256 + ni * 32] = acc[mi][ni][e];
+        }
+        __syncthreads();
+        for (int c = t; c < 128 * 32; c += NT) {
+            const int rl = c >> 5, cc = (c & 31) * 8;
+            const int row = 128 * half + rl;
             float dot = 0.f;
+            if (cc < ncols) {
+                const float wr = wrow[row];
+                const float4 d0 = *reinterpret_cast<const float4 *>(st + rl * 256 + cc);
+                const float4 d1 = *reinterpret_cast<const float4 *>(st + rl * 256 + cc + 4);
+                const float dap[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                const u32x4 av = *reinterpret_cast<const u32x4 *>(A + (int64_t)row * I + n0 + cc);
+                const u32x4 hv = *reinterpret_cast<const u32x4 *>(HU + (int64_t)row * ld2 + n0 + cc);
+                const u32x4 uv = *reinterpret_cast<const u32x4 *>(HU + (int64_t)row * ld2 + I + n0 + cc);
+                u32x4 dh, du;
 #pragma unroll
-            for (int ni = 0; ni < WG::NI; ++ni) {
-                const int col = n0 + wn * (WG::NI * 32) + ni * 32 + (lane & 31);
-                if (col < I) {
-                    const float dap = acc[mi][ni][e];
-                    const float a = bf2f(A[(int64_t)row * I + col]);
-                    const float h = bf2f(HU[(int64_t)row * 2 * I + col]);
-                    const float u = bf2f(HU[(int64_t)row * 2 * I + I + col]);
-                    const float dA = wr * dap;
-                    const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h));
-                    dHU[(int64_t)row * 2 * I + col] = f2bf(dA * u * sg * (1.0f + h * (1.0f - sg)));
-                    dHU[(int64_t)row * 2 * I + I + col] = f2bf(dA * h * sg);
-                    dot = fmaf(dap, a, dot);
+                for (int k = 0; k < 4; ++k) {
+                    float rh[2], ru[2];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const float a = __uint_as_float(j ? (av[k] & 0xffff0000u) : (av[k] << 16));
+                        const float h = __uint_as_float(j ? (hv[k] & 0xffff0000u) : (hv[k] << 16));
+                        const float u = __uint_as_float(j ? (uv[k] & 0xffff0000u) : (uv[k] << 16));
+                        const float d = dap[2 * k + j];
+                        const float dA = wr * d;
+                        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-h));
+                        rh[j] = dA * u * sg * (1.0f + h * (1.0f - sg));
+                        ru[j] = dA * h * sg;
+                        dot = fmaf(d, a, dot);
+                    }
+                    dh[k] = pack_bf2(rh[0], rh[1]);
+                    du[k] = pack_bf2(ru[0], ru[1]);
                 }
+                *reinterpret_cast<u32x4 *>(dHU + (int64_t)row * ld2 + n0 + cc) = dh;
+                *reinterpret_cast<u32x4 *>(dHU + (int64_t)row * ld2 + I + n0 + cc) = du;
             }
-            // fixed-order butterfly over the 32 lanes that share this row
 #pragma unroll
             for (int off = 16; off >= 1; off >>= 1) dot += __shfl_xor(dot, off, 64);
-            if ((lane & 31) == 0) part[(int64_t)row * nparts + (n0 / 256) * WN + wn] = dot;
-            __builtin_amdgcn_sched_barrier(0);
+            if ((c & 31) == 0) part[(int64_t)row * nparts + n0 / 256] = dot;
         }
     }
 }

@@ -214,7 +214,7 @@ __device__ __forceinline__ void bwd_down_phase(const BwdArgs &a, char *lds) {
         const KOp bk = rows_window(a.W2T + ((int64_t)l * I + nt * 256) * H, H, I - nt * 256);
         AccW<kFwdWM, kFwdWN> acc;
         gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, H / 64, false, lds, acc);
-        epilogue_swiglu_bwd_w<kFwdWM, kFwdWN>(acc, a.A + (int64_t)m0 * I, a.HU + (int64_t)m0 * 2 * I, a.wrow + m0,
+        epilogue_swiglu_bwd_w<kFwdWM, kFwdWN>(acc, lds, a.A + (int64_t)m0 * I, a.HU + (int64_t)m0 * 2 * I, a.wrow + m0,
                                               a.dHU + (int64_t)m0 * 2 * I, a.part + (int64_t)m0 * a.nparts, a.nparts, I,
                                               nt * 256);
     }

@@ -199,7 +199,7 @@ int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 int64_t sched_ws_bytes(const moe_desc *d) { return align256(4ll * d->num_batches * d->P * sched_chunks(d) * d->L); }
 
-int bwd_nparts(const moe_desc *d) { return 2 * ((d->I + 255) / 256); }
+int bwd_nparts(const moe_desc *d) { return (d->I + 255) / 256; }  // one dw partial per 256-column tile
 
 // Leading dimension of the transposed activations (rows of length cap, padded
 // to 64 elements so every 16-byte access stays aligned).
