@@ -212,10 +212,12 @@ def bench_schedule_sweep(args, torch, ops, inputs, dev):
 
 
 def bench_fwd_bwd(args, torch, ops, inputs, dev):
-    """Adversarial Kimi-shaped forward + backward (Zipf s=1.5 + 4 hot local experts)."""
+    """Kimi-shaped forward + backward: adversarial routing (Zipf s=1.5 + 4 hot
+    local experts taking a quarter of the routes) or balanced routing."""
     c = KIMI
+    routing = args.bwd_routing
     h = inputs.make_layer_inputs_device(6, c["P"], c["Np"], c["E"], c["K"], c["L"], c["H"], c["I"], dev,
-                                        routing="hot", x_std=1.0, s=1.5, with_grad=True)
+                                        routing=routing, x_std=1.0, s=1.5, with_grad=True)
     d = ops.make_desc(c["P"], c["Np"], c["K"], c["E"], c["L"], H=c["H"], I=c["I"])
     routes = torch.from_numpy(h["routes"]).to(dev)
     w = torch.from_numpy(h["w"]).to(dev)
@@ -252,10 +254,11 @@ def bench_fwd_bwd(args, torch, ops, inputs, dev):
     hi = c["H"] * c["I"]
     fl = 18.0 * hi * local
     npad = int(b.seg_off[-1].item())
-    return {"metric": "MoE layer fwd+bwd TFLOP/s (Kimi shape, adversarial routing, 1 GPU)",
+    return {"metric": f"MoE layer fwd+bwd TFLOP/s (Kimi shape, {'adversarial' if routing == 'hot' else routing} routing, 1 GPU)",
             "value": fl / (ms / 1e3) / 1e12, "unit": "TFLOP/s", "ms_per_step": ms, "steps": args.steps,
             "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": "kimi_local_share_fwd_bwd", "routing": "zipf1.5+4hot", "local_routes": local,
+            "config": {"workload": "kimi_local_share_fwd_bwd",
+                       "routing": "zipf1.5+4hot" if routing == "hot" else routing, "local_routes": local,
                        "dispatched_rows": npad},
             "stage_ms": st,
             "kernel_tflops": {k: v for k, v in {
@@ -350,6 +353,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-schedule", action="store_true")
+    ap.add_argument("--bwd-routing", default="hot", choices=["hot", "balanced"],
+                    help="routing of --workload kimi_bwd (default: adversarial)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the layer steps, run one plain read+write kernel over this many MiB (counter scaling)")
     ap.add_argument("--workload", default="kimi", choices=["kimi", "kimi_bwd", "mid_tc", "schedule"],
