@@ -19,6 +19,12 @@ Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
   layer_bwd, bwd_tokens, wgrad_elems             pinned (finite differences, torch
                                                   autograd, the dw identity)
   minibatch_floor                                pinned (the printed 2368)
+  e4m3_value, e4m3_encode, mx_quantize,          pinned (E4M3 closed form per code, encode-
+    mx_quantize_f64, mx_dequantize                 decode identity, ties to even, saturation,
+                                                   scale exponent of the block maximum)
+  mx_expert_ffn_rows, mx_layer_fwd_tokens        pinned (dot products vs numpy on the
+                                                   dequantized operands; token path = rows +
+                                                   combine; close to the bf16 FFN)
 """
 from __future__ import annotations
 
@@ -77,6 +83,14 @@ def _load():
         lib.orc_bwd_tokens.argtypes = [i32, i32, i32, i32, i32, p, p, p, p, p, p, p, i64, p, p]
         lib.orc_bwd_tokens.restype = None
         lib.orc_wgrad_elems.argtypes = [i64, i32, i32, i32, i32, i32, i32] + [p] * 6 + [p, i64, p, p, i64, p]
+        lib.orc_e4m3_value.argtypes = [i32]
+        lib.orc_e4m3_value.restype = ctypes.c_double
+        lib.orc_e4m3_encode.argtypes = [ctypes.c_double]
+        lib.orc_e4m3_encode.restype = i32
+        lib.orc_mx_quantize.argtypes = [p, i64, i32, p, p]
+        lib.orc_mx_quantize_f64.argtypes = [p, i64, i32, p, p]
+        lib.orc_mx_expert_ffn_rows.argtypes = [i32, i32, i32] + [p] * 7 + [p, i64, p, p, p, p]
+        lib.orc_mx_layer_fwd_tokens.argtypes = [i32, i32, i32, i32, i32] + [p] * 8 + [p, i64, p]
         lib.orc_wgrad_elems.restype = None
         _lib = lib
     return _lib
@@ -272,3 +286,99 @@ def wgrad_elems(routes, w, X, W13, W2, dOut, L: int, base: int, expert: int, w13
     _load().orc_wgrad_elems(P * Np, K, L, base, H, I, expert, _ptr(routes), _ptr(w), _ptr(X), _ptr(W13), _ptr(W2),
                             _ptr(dOut), _ptr(e13), e13.shape[0], _ptr(g13), _ptr(e2), e2.shape[0], _ptr(g2))
     return g13, g2
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 (OCP Microscaling: 32-element blocks along the reduction dimension,
+# E8M0 scale 2^(floor(log2 amax) - 8), FP8 E4M3 elements rounded to nearest
+# even and saturated at +-448).
+# ---------------------------------------------------------------------------
+
+def e4m3_value(code: int) -> float:
+    return _load().orc_e4m3_value(int(code))
+
+
+def e4m3_encode(y: float) -> int:
+    return _load().orc_e4m3_encode(float(y))
+
+
+def e4m3_table() -> np.ndarray:
+    """Values of the 256 E4M3 codes (NaN for 0x7F and 0xFF)."""
+    return np.array([e4m3_value(c) for c in range(256)])
+
+
+def mx_quantize(x: np.ndarray):
+    """Row-wise MX quantization of bf16 bits [..., K] -> (codes uint8 [..., K],
+    scale bytes uint8 [..., K/32])."""
+    x = _u16(x)
+    K = x.shape[-1]
+    rows = x.size // K
+    q = np.zeros(x.shape, np.uint8)
+    s = np.zeros(x.shape[:-1] + (K // 32,), np.uint8)
+    _load().orc_mx_quantize(_ptr(x), rows, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def mx_quantize_f64(x: np.ndarray):
+    x = np.ascontiguousarray(x, np.float64)
+    K = x.shape[-1]
+    q = np.zeros(x.shape, np.uint8)
+    s = np.zeros(x.shape[:-1] + (K // 32,), np.uint8)
+    _load().orc_mx_quantize_f64(_ptr(x), x.size // K, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def mx_dequantize(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Double values of MX codes and scale bytes (blocks of 32 along the last axis)."""
+    t = e4m3_table()
+    v = t[np.asarray(q, np.int64)]
+    sc = np.repeat(np.ldexp(1.0, np.asarray(s, np.int64) - 127), 32, axis=-1)
+    return v * sc
+
+
+def mx_dispatch(Xq: np.ndarray, Xs: np.ndarray, phi: np.ndarray):
+    """MX codes and scales of the dispatched rows: row i = X row phi[i]
+    (part * Np + tok); padding rows get code 0 and scale byte 0."""
+    Xq, Xs = np.asarray(Xq, np.uint8), np.asarray(Xs, np.uint8)
+    P, Np, H = Xq.shape
+    phi = _i32(phi)
+    real = phi[:, 0] >= 0
+    src = (phi[:, 0].astype(np.int64) * Np + phi[:, 1]).clip(min=0)
+    q = np.where(real[:, None], Xq.reshape(-1, H)[src], 0).astype(np.uint8)
+    s = np.where(real[:, None], Xs.reshape(-1, H // 32)[src], 0).astype(np.uint8)
+    return q, s
+
+
+def mx_expert_ffn_rows(seg_off, Xdq, Xds, W13q, W13s, W2q, W2s, rows=None):
+    """MXFP8 expert FFN of the listed dispatched rows: dict with A (double
+    [n][I], before quantization), Aq / As (its MX codes and scales) and Y
+    (double [n][H], from the quantized A)."""
+    seg_off = _i32(seg_off)
+    arrs = [np.ascontiguousarray(a, np.uint8) for a in (Xdq, Xds, W13q, W13s, W2q, W2s)]
+    Xdq, Xds, W13q, W13s, W2q, W2s = arrs
+    L, twoI, H = W13q.shape
+    I = twoI // 2
+    rows = np.arange(Xdq.shape[0], dtype=np.int64) if rows is None else np.ascontiguousarray(rows, np.int64)
+    n = rows.shape[0]
+    A = np.zeros((n, I))
+    Aq = np.zeros((n, I), np.uint8)
+    As = np.zeros((n, I // 32), np.uint8)
+    Y = np.zeros((n, H))
+    _load().orc_mx_expert_ffn_rows(L, H, I, _ptr(seg_off), *[_ptr(a) for a in arrs], _ptr(rows), n, _ptr(A),
+                                   _ptr(Aq), _ptr(As), _ptr(Y))
+    return {"A": A, "Aq": Aq, "As": As, "Y": Y}
+
+
+def mx_layer_fwd_tokens(routes, w, Xq, Xs, W13q, W13s, W2q, W2s, L: int, base: int = 0, tokens=None):
+    """MXFP8 forward output per token straight from the definition."""
+    routes = _i32(routes)
+    P, Np, K = routes.shape
+    w = np.ascontiguousarray(w, np.float32)
+    arrs = [np.ascontiguousarray(a, np.uint8) for a in (Xq, Xs, W13q, W13s, W2q, W2s)]
+    H = arrs[0].shape[-1]
+    I = arrs[2].shape[1] // 2
+    tokens = np.arange(P * Np, dtype=np.int64) if tokens is None else np.ascontiguousarray(tokens, np.int64)
+    out = np.zeros((tokens.shape[0], H))
+    _load().orc_mx_layer_fwd_tokens(K, L, base, H, I, _ptr(routes), _ptr(w), *[_ptr(a) for a in arrs],
+                                    _ptr(tokens), tokens.shape[0], _ptr(out))
+    return out

@@ -22,6 +22,10 @@
  *  [BPT]  "Beyond Peak TFLOPs", section 2.A (one two-column pull table
  *         {src_rank, src_idx} serves all four forward/backward phases) and
  *         section 2.C (weight gradients accumulated over tokens in one pass).
+ *  [MoK] section 5 also runs the routed experts in MXFP8 with the activation
+ *         quantization fused into the dispatch loads, the grouped GEMMs and
+ *         SwiGLU; the MX functions at the end of this file follow the OCP
+ *         Microscaling format for that reading (see there).
  *
  * Readings taken where the pages leave a step open (each is listed in the
  * design notes of the repository):
@@ -750,5 +754,203 @@ void orc_wgrad_elems(int64_t ntok, int K, int L, int base, int H, int I, int l,
                 s += (double)w[g * K + j] * widen_bf16(dOut[g * H + m]) * silu(hh) * uu;
             }
         g2[q] = s;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* MXFP8 ([MoK] section 5, mixed precision: routed experts in MXFP8).        */
+/* ------------------------------------------------------------------------ */
+/*
+ * Reading (the pages name MXFP8 and E4M3 for weights and activations but not
+ * the block format): the OCP Microscaling format.  A block is 32 consecutive
+ * elements along the reduction dimension; it shares one E8M0 scale
+ * X = 2^(floor(log2(amax)) - 8) (8 = exponent of the largest E4M3 normal,
+ * 448 = 1.75 * 2^8), stored as the byte e + 127 with e clamped to
+ * [-127, 127]; every element is x / X rounded to FP8 E4M3 (1-4-3, bias 7,
+ * subnormals, no infinities) to nearest, ties to even, saturating at +-448.
+ * An all-zero block gets the byte 0 (X = 2^-127).  The scaling by a power of
+ * two is exact, so the codes of a bf16 input are a fixed function of it.
+ */
+
+/* value of an E4M3 code (the NaN codes 0x7F / 0xFF return NAN) */
+double orc_e4m3_value(int code) {
+    int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    double v = e == 0 ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+    return s ? -v : v;
+}
+
+/* nearest E4M3 code of a finite y, ties to even, saturating at +-448 */
+int orc_e4m3_encode(double y) {
+    int s = signbit(y) ? 1 : 0;
+    double a = fabs(y);
+    if (a >= 448.0) return (s << 7) | 0x7E;
+    int ea;
+    frexp(a, &ea); /* a = f * 2^ea, f in [0.5, 1): floor(log2 a) = ea - 1 */
+    int qexp = a < ldexp(1.0, -6) ? -9 : (ea - 1) - 3; /* exponent of one quantum */
+    double q = nearbyint(ldexp(a, -qexp));              /* default rounding: to nearest even */
+    double mag = ldexp(q, qexp);
+    if (mag >= 448.0) return (s << 7) | 0x7E;
+    if (mag < ldexp(1.0, -6)) return (s << 7) | (int)ldexp(mag, 9); /* subnormal, m = 0..7 */
+    int em;
+    frexp(mag, &em);
+    int E = em - 1;                                      /* mag in [2^E, 2^(E+1)) */
+    int m = (int)(ldexp(mag, -E) * 8.0) - 8;
+    return (s << 7) | ((E + 7) << 3) | m;
+}
+
+/* scale byte and codes of one block of 32 doubles */
+static void mx_block(const double *x, uint8_t *q, uint8_t *sbyte) {
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(x[i]));
+    int se = -127;
+    if (amax > 0.0) {
+        int ea;
+        frexp(amax, &ea);
+        se = (ea - 1) - 8;
+        if (se < -127) se = -127;
+        if (se > 127) se = 127;
+    }
+    *sbyte = (uint8_t)(se + 127);
+    for (int i = 0; i < 32; ++i) q[i] = (uint8_t)orc_e4m3_encode(ldexp(x[i], -se));
+}
+
+/* row-wise MX quantization of bf16 bits [rows][K] (K % 32 == 0):
+ * q [rows][K] codes, s [rows][K/32] scale bytes */
+void orc_mx_quantize(const uint16_t *src, int64_t rows, int K, uint8_t *q, uint8_t *s) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double x[32];
+        for (int b = 0; b < K / 32; ++b) {
+            for (int i = 0; i < 32; ++i) x[i] = widen_bf16(src[r * K + b * 32 + i]);
+            mx_block(x, q + r * K + b * 32, s + r * (K / 32) + b);
+        }
+    }
+}
+
+/* the same for double input (the activations a of the SwiGLU) */
+void orc_mx_quantize_f64(const double *src, int64_t rows, int K, uint8_t *q, uint8_t *s) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int b = 0; b < K / 32; ++b) mx_block(src + r * K + b * 32, q + r * K + b * 32, s + r * (K / 32) + b);
+}
+
+static double mx_value(const uint8_t *q, const uint8_t *s, int64_t i) {
+    return ldexp(orc_e4m3_value(q[i]), (int)s[i / 32] - 127);
+}
+
+/*
+ * MXFP8 expert FFN of listed dispatched rows: Xq/Xs are the MX codes and
+ * scales of the dispatched rows [*][H]; W13q/W13s [L][2I][H] (blocks along
+ * H); W2q/W2s [L][H][I] (blocks along I).  Per row of segment l:
+ *   h, u = dequantized row . dequantized W13[l] rows (double);
+ *   a = silu(h) * u (double, returned in A);
+ *   a is MX-quantized along I (codes Aq [n][I], scales As [n][I/32]);
+ *   y = dequantized a . dequantized W2[l] rows (returned in Y).
+ * Outputs nullable except that Y needs the quantized a.
+ */
+void orc_mx_expert_ffn_rows(int L, int H, int I, const int32_t *seg_off, const uint8_t *Xq,
+                            const uint8_t *Xs, const uint8_t *W13q, const uint8_t *W13s,
+                            const uint8_t *W2q, const uint8_t *W2s, const int64_t *rows, int64_t nrows,
+                            double *A, uint8_t *Aq, uint8_t *As, double *Y) {
+#pragma omp parallel
+    {
+        double *x = (double *)malloc(sizeof(double) * H);
+        double *a = (double *)malloc(sizeof(double) * I);
+        uint8_t *aq = (uint8_t *)malloc(I);
+        uint8_t *as = (uint8_t *)malloc(I / 32);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t qi = 0; qi < nrows; ++qi) {
+            int64_t row = rows[qi];
+            int l = expert_of_row(seg_off, L, row);
+            for (int k = 0; k < H; ++k) x[k] = mx_value(Xq + row * H, Xs + row * (H / 32), k);
+            for (int n = 0; n < I; ++n) {
+                double h = 0.0, u = 0.0;
+                if (l >= 0) {
+                    const uint8_t *gq = W13q + ((int64_t)l * 2 * I + n) * H;
+                    const uint8_t *gs = W13s + ((int64_t)l * 2 * I + n) * (H / 32);
+                    const uint8_t *uq = W13q + ((int64_t)l * 2 * I + I + n) * H;
+                    const uint8_t *us = W13s + ((int64_t)l * 2 * I + I + n) * (H / 32);
+                    for (int k = 0; k < H; ++k) {
+                        h += x[k] * mx_value(gq, gs, k);
+                        u += x[k] * mx_value(uq, us, k);
+                    }
+                }
+                a[n] = silu(h) * u;
+            }
+            orc_mx_quantize_f64(a, 1, I, aq, as);
+            if (A) memcpy(A + qi * I, a, sizeof(double) * I);
+            if (Aq) memcpy(Aq + qi * I, aq, I);
+            if (As) memcpy(As + qi * (I / 32), as, I / 32);
+            if (Y) {
+                for (int m = 0; m < H; ++m) {
+                    double y = 0.0;
+                    if (l >= 0) {
+                        const uint8_t *wq = W2q + ((int64_t)l * H + m) * I;
+                        const uint8_t *ws = W2s + ((int64_t)l * H + m) * (I / 32);
+                        for (int n = 0; n < I; ++n) y += mx_value(aq, as, n) * mx_value(wq, ws, n);
+                    }
+                    Y[qi * H + m] = y;
+                }
+            }
+        }
+        free(x);
+        free(a);
+        free(aq);
+        free(as);
+    }
+}
+
+/*
+ * MXFP8 forward per token straight from the definition (no schedule): as
+ * orc_layer_fwd_tokens with every product taken on MX-dequantized operands
+ * and a MX-quantized before the down projection.  Xq/Xs: [P*Np][H].
+ */
+void orc_mx_layer_fwd_tokens(int K, int L, int base, int H, int I, const int32_t *routes,
+                             const float *w, const uint8_t *Xq, const uint8_t *Xs,
+                             const uint8_t *W13q, const uint8_t *W13s, const uint8_t *W2q,
+                             const uint8_t *W2s, const int64_t *tokens, int64_t ntok, double *out) {
+#pragma omp parallel
+    {
+        double *x = (double *)malloc(sizeof(double) * H);
+        double *a = (double *)malloc(sizeof(double) * I);
+        uint8_t *aq = (uint8_t *)malloc(I);
+        uint8_t *as = (uint8_t *)malloc(I / 32);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t qi = 0; qi < ntok; ++qi) {
+            int64_t g = tokens[qi];
+            double *o = out + qi * H;
+            for (int m = 0; m < H; ++m) o[m] = 0.0;
+            for (int k = 0; k < H; ++k) x[k] = mx_value(Xq + g * H, Xs + g * (H / 32), k);
+            for (int j = 0; j < K; ++j) {
+                int32_t e = routes[g * K + j];
+                if (!is_local(e, base, L)) continue;
+                int l = e - base;
+                for (int n = 0; n < I; ++n) {
+                    double h = 0.0, u = 0.0;
+                    const uint8_t *gq = W13q + ((int64_t)l * 2 * I + n) * H;
+                    const uint8_t *gs = W13s + ((int64_t)l * 2 * I + n) * (H / 32);
+                    const uint8_t *uq = W13q + ((int64_t)l * 2 * I + I + n) * H;
+                    const uint8_t *us = W13s + ((int64_t)l * 2 * I + I + n) * (H / 32);
+                    for (int k = 0; k < H; ++k) {
+                        h += x[k] * mx_value(gq, gs, k);
+                        u += x[k] * mx_value(uq, us, k);
+                    }
+                    a[n] = silu(h) * u;
+                }
+                orc_mx_quantize_f64(a, 1, I, aq, as);
+                double wj = (double)w[g * K + j];
+                for (int m = 0; m < H; ++m) {
+                    const uint8_t *wq = W2q + ((int64_t)l * H + m) * I;
+                    const uint8_t *ws = W2s + ((int64_t)l * H + m) * (I / 32);
+                    double y = 0.0;
+                    for (int n = 0; n < I; ++n) y += mx_value(aq, as, n) * mx_value(wq, ws, n);
+                    o[m] += wj * y;
+                }
+            }
+        }
+        free(x);
+        free(a);
+        free(aq);
+        free(as);
     }
 }
