@@ -269,6 +269,64 @@ def bench_fwd_bwd(args, torch, ops, inputs, dev):
                 "bwd_wgrad": 6.0 * hi * local / (st.get("bwd_wgrad", 1e9) / 1e3) / 1e12}.items()}}
 
 
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA (no sparsity)
+
+
+def bench_layer_mx(args, torch, ops, inputs, dev):
+    """Kimi-shaped forward share with MXFP8 routed experts (moe_layer_fwd_mx):
+    schedule, X quantization, MX gate/up GEMM pulling rows through the table
+    with SwiGLU + quantization of a in its epilogue, MX down GEMM, combine.
+    The weights are quantized once, before the timed region (they do not
+    change between forward steps)."""
+    c = KIMI
+    h = inputs.make_layer_inputs_device(5, c["P"], c["Np"], c["E"], c["K"], c["L"], c["H"], c["I"], dev,
+                                        routing="balanced", x_std=1.0)
+    d = ops.make_desc(c["P"], c["Np"], c["K"], c["E"], c["L"], H=c["H"], I=c["I"])
+    routes = torch.from_numpy(h["routes"]).to(dev)
+    w = torch.from_numpy(h["w"]).to(dev)
+    W13q, W13s = ops.quantize_mx(h["W13"])
+    W2q, W2s = ops.quantize_mx(h["W2"])
+    del h["W13"], h["W2"]
+    bufs = ops.alloc_fwd_mx(d, dev)
+    local = int(((h["routes"] >= 0) & (h["routes"] < c["L"])).sum())
+
+    def step():
+        ops.layer_fwd_mx(d, routes, w, h["X"], W13q, W13s, W2q, W2s, bufs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ops.moe_trace_enable(args.steps * 16)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    per = {}
+    for name, t in ops.moe_trace_read(args.steps * 16):
+        per.setdefault(name, []).append(t)
+    ops.moe_trace_enable(0)
+    st = {k: float(np.mean(v)) for k, v in per.items()}
+    hi = c["H"] * c["I"]
+    fl = 6.0 * hi * local
+    gu = 4.0 * hi * local / (st["mx_gateup"] / 1e3) / 1e12
+    dn = 2.0 * hi * local / (st["mx_down"] / 1e3) / 1e12
+    return {"metric": "MoE layer fwd TFLOP/s, MXFP8 routed experts (Kimi shape, 1 GPU)",
+            "value": fl / (ms / 1e3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "mxfp8-e4m3 (fp32 accumulate), bf16 in/out", "data": "synthetic",
+            "config": {"workload": "kimi_local_share_fwd_mxfp8", "P": c["P"], "tokens_per_partition": c["Np"],
+                       "experts": c["E"], "local_experts": c["L"], "top_k": c["K"], "H": c["H"], "I": c["I"],
+                       "routing": "balanced", "local_routes": local, "weights": "quantized once, outside the step"},
+            "stage_ms": st,
+            "roofline": {"bound": "mfma", "kernel": "mx_gateup", "achieved": gu, "peak": PEAK_FP8_TFLOPS,
+                         "unit": "TFLOP/s", "frac": gu / PEAK_FP8_TFLOPS, "traffic": None,
+                         "algorithmic_flop_per_launch": 4.0 * hi * local, "avg_launch_ms": st["mx_gateup"]},
+            "mx_down": {"achieved": dn, "frac": dn / PEAK_FP8_TFLOPS, "avg_launch_ms": st["mx_down"]}}
+
+
 def bench_tc_sweep(args, torch, ops, inputs, dev):
     """Mid configuration (8 x 4096 tokens, 64 experts with 8 local, top-6, H=2048,
     I=1024): layer forward vs the minibatch of dispatched rows Tc (persistent
@@ -357,8 +415,8 @@ def main():
                     help="routing of --workload kimi_bwd (default: adversarial)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the layer steps, run one plain read+write kernel over this many MiB (counter scaling)")
-    ap.add_argument("--workload", default="kimi", choices=["kimi", "kimi_bwd", "mid_tc", "schedule"],
-                    help="kimi: the contract line (default); kimi_bwd / mid_tc / schedule: extra measurements")
+    ap.add_argument("--workload", default="kimi", choices=["kimi", "kimi_bwd", "mid_tc", "schedule", "kimi_mx"],
+                    help="kimi: the contract line (default); kimi_bwd / mid_tc / schedule / kimi_mx: extra measurements")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -379,6 +437,9 @@ def main():
         return
     if args.workload == "mid_tc":
         print(json.dumps(bench_tc_sweep(args, torch, ops, inputs, dev)), flush=True)
+        return
+    if args.workload == "kimi_mx":
+        print(json.dumps(bench_layer_mx(args, torch, ops, inputs, dev)), flush=True)
         return
     if args.workload == "schedule":
         print(json.dumps(bench_schedule_sweep(args, torch, ops, inputs, dev)), flush=True)

@@ -195,6 +195,52 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
                   size_t ws_bytes, void *stream);
 
 /*
+ * MXFP8 routed experts ([MoK] section 5, mixed precision).  Format (the OCP
+ * Microscaling reading of "MXFP8"): blocks of 32 consecutive elements along
+ * the reduction dimension share one E8M0 scale byte b (scale 2^(b - 127),
+ * b = floor(log2 max|x|) - 8 + 127 clamped to [0, 254]; 0 for an all-zero
+ * block); every element is the FP8 E4M3 code (1-4-3, bias 7) of x / scale,
+ * rounded to nearest with ties to even and saturated at +-448.
+ *
+ * moe_quantize_mx — row-wise MX quantization of a bf16 matrix.
+ *   src     bf16 [rows][K], K a multiple of 32, 16-byte aligned
+ *   q       out: uint8 codes [rows][K], 16-byte aligned
+ *   scales  out: uint8 scale bytes [rows][K/32]
+ * Used for the weights (W13 [L][2I][H] as 2IL rows of H, W2 [L][H][I] as HL
+ * rows of I) once per weight update, and inside moe_layer_fwd_mx for X.
+ * Errors: MOE_EINVAL for a NULL or misaligned pointer, rows < 0 or K not a
+ * positive multiple of 32.
+ */
+int moe_quantize_mx(const uint16_t *src, int64_t rows, int32_t K, uint8_t *q, uint8_t *scales,
+                    void *stream);
+
+/*
+ * moe_layer_fwd_mx — the forward share with MXFP8 routed experts: schedule as
+ * in moe_schedule; X quantized row-wise (codes Xq [P*Np][H], scales Xs
+ * [P*Np][H/32]); the gate/up GEMM pulls each dispatched row's codes from Xq
+ * through phi ([MoK] section 2, pull dispatch; padding rows read zeros),
+ * accumulates in fp32 and in its epilogue computes a = silu(h) * u and
+ * quantizes it (codes Aq [cap][I], scales As [cap][I/32]); the down GEMM
+ * multiplies the MX codes of a and W2 into Y (bf16 [cap][H]); the combine is
+ * moe_combine's.
+ *   W13q, W13s  MX codes [L][2I][H] and scales [L][2I][H/32] of W13 (rows
+ *               [0,I) gate, [I,2I) up), e.g. from moe_quantize_mx
+ *   W2q, W2s    MX codes [L][H][I] and scales [L][H][I/32] of W2
+ *   counts, seg_off, phi, route_row   out, as in moe_schedule
+ *   Xq, Xs, Aq, As, Y, out            out (Xq, Aq, Y, out 16-byte aligned;
+ *                                     Xs, As, W13s, W2s 4-byte aligned)
+ *   ws >= moe_workspace_bytes(d, MOE_OP_LAYER_FWD)
+ * Needs H a multiple of 128 and H <= 65536 (MOE_EUNSUPPORTED otherwise),
+ * d->num_batches == 1.  Every float reduction has a fixed order, so repeated
+ * calls give bitwise the same outputs.
+ */
+int moe_layer_fwd_mx(const moe_desc *d, const int32_t *routes, const float *w, const uint16_t *X,
+                     const uint8_t *W13q, const uint8_t *W13s, const uint8_t *W2q, const uint8_t *W2s,
+                     int32_t *counts, int32_t *seg_off, moe_src *phi, int32_t *route_row, uint8_t *Xq,
+                     uint8_t *Xs, uint8_t *Aq, uint8_t *As, uint16_t *Y, uint16_t *out, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/*
  * moe_layer_bwd — backward of the forward share, reusing the forward table
  * ([MoK] section 2: pull reverse-combine, push reverse-dispatch; section 5:
  * router-weight gradient from the SwiGLU activations and the down-projection

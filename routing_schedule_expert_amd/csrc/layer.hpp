@@ -20,6 +20,7 @@
 
 #include "common.hpp"
 #include "gemm.hpp"
+#include "mx.hpp"
 #include "rowops.hpp"
 #include "schedule.hpp"
 
@@ -127,6 +128,81 @@ __device__ __forceinline__ void ffn_chunked_body(const FfnArgs &a, char *lds, Gr
             }
         }
         gb.sync();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 expert FFN.
+// ---------------------------------------------------------------------------
+
+struct MxFfnArgs {
+    const uint8_t *Xq, *Xs;  // MX codes [P*Np][H] and scale bytes [P*Np][H/32] of X
+    const moe_src *phi;      // the pull table: dispatched row -> X row
+    int32_t Np;
+    const uint8_t *W13q, *W13s, *W2q, *W2s;  // [L][2I][H] (+/32), [L][H][I] (+/32)
+    const int32_t *seg_off;
+    uint8_t *Aq, *As;  // MX codes [cap][I] and scale bytes [cap][I/32] of a
+    uint16_t *Y;       // bf16 [cap][H]
+    int L, H, I;
+};
+
+__device__ __forceinline__ const uint16_t *as_u16(const uint8_t *p) { return reinterpret_cast<const uint16_t *>(p); }
+
+__device__ __forceinline__ void mx_gateup_tile(const MxFfnArgs &a, int mt, int nt, char *lds) {
+    const int H = a.H, I = a.I;
+    const int m0 = mt * kBM;
+    const int l = expert_of(a.seg_off, a.L, m0);
+    const KOp ak{nullptr, nullptr, H / 2, a.phi + m0, as_u16(a.Xq), a.Np};
+    const SOp as{nullptr, nullptr, H / 32, a.phi + m0, a.Xs, a.Np};
+    const uint8_t *w = a.W13q + (int64_t)l * 2 * I * H;
+    const uint8_t *ws = a.W13s + (int64_t)l * 2 * I * (H / 32);
+    const KOp bk{as_u16(w + (int64_t)nt * 128 * H), as_u16(w + ((int64_t)I + nt * 128) * H), H / 2, nullptr, nullptr, 0};
+    const SOp bs{ws + (int64_t)nt * 128 * (H / 32), ws + ((int64_t)I + nt * 128) * (H / 32), H / 32, nullptr, nullptr,
+                 0};
+    AccW<kFwdWM, kFwdWN> acc;
+    gemm_mainloop_mx<kFwdWM, kFwdWN>(ak, bk, as, bs, H / 128, true, lds, acc);
+    epilogue_swiglu_mx<kFwdWM, kFwdWN>(acc, lds, a.Aq + (int64_t)m0 * I + nt * 128, I,
+                                       a.As + (int64_t)m0 * (I / 32) + nt * 4, I / 32);
+}
+
+__device__ __forceinline__ void mx_down_tile(const MxFfnArgs &a, int mt, int nt, char *lds) {
+    const int H = a.H, I = a.I;
+    const int m0 = mt * kBM;
+    const int l = expert_of(a.seg_off, a.L, m0);
+    const uint8_t *aq = a.Aq + (int64_t)m0 * I;
+    const uint8_t *asc = a.As + (int64_t)m0 * (I / 32);
+    const KOp ak{as_u16(aq), as_u16(aq + 128ll * I), I / 2, nullptr, nullptr, 0};
+    const SOp as{asc, asc + 128ll * (I / 32), I / 32, nullptr, nullptr, 0};
+    const uint8_t *w = a.W2q + ((int64_t)l * H + nt * 256) * I;
+    const uint8_t *ws = a.W2s + ((int64_t)l * H + nt * 256) * (I / 32);
+    const KOp bk{as_u16(w), as_u16(w + 128ll * I), I / 2, nullptr, nullptr, 0};
+    const SOp bs{ws, ws + 128ll * (I / 32), I / 32, nullptr, nullptr, 0};
+    AccW<kFwdWM, kFwdWN> acc;
+    gemm_mainloop_mx<kFwdWM, kFwdWN>(ak, bk, as, bs, I / 128, false, lds, acc);
+    epilogue_store_bf16_w<kFwdWM, kFwdWN>(acc, lds, a.Y + (int64_t)m0 * H + nt * 256, H, 256);
+}
+
+__device__ __forceinline__ void mx_gateup_phase(const MxFfnArgs &a, char *lds) {
+    const int mtiles = a.seg_off[a.L] / kBM, ntiles = a.I / 128;
+    const int64_t total = (int64_t)mtiles * ntiles;
+    for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
+        const int64_t lid = logical_tile(it);
+        if (lid >= total) continue;
+        int m, n;
+        grouped_mn(lid, mtiles, ntiles, 4, m, n);
+        mx_gateup_tile(a, m, n, lds);
+    }
+}
+
+__device__ __forceinline__ void mx_down_phase(const MxFfnArgs &a, char *lds) {
+    const int mtiles = a.seg_off[a.L] / kBM, ntiles = a.H / 256;
+    const int64_t total = (int64_t)mtiles * ntiles;
+    for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
+        const int64_t lid = logical_tile(it);
+        if (lid >= total) continue;
+        int m, n;
+        grouped_mn(lid, mtiles, ntiles, 4, m, n);
+        mx_down_tile(a, m, n, lds);
     }
 }
 

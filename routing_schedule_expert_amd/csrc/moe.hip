@@ -89,6 +89,22 @@ __global__ __launch_bounds__(kFwdThreads) void k_layer_fwd_persistent(LayerFwdAr
     layer_fwd_persistent_body(a, lds);
 }
 
+__global__ __launch_bounds__(256) void k_mx_quantize(const uint16_t *src, int64_t nblocks, int K, uint8_t *q,
+                                                    uint8_t *s) {
+    for (int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; b < nblocks; b += (int64_t)gridDim.x * blockDim.x)
+        mx_quantize_block_bf16(src, K, q, s, b);
+}
+
+__global__ __launch_bounds__(kFwdThreads) void k_mx_gateup(MxFfnArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+    mx_gateup_phase(a, lds);
+}
+
+__global__ __launch_bounds__(kFwdThreads) void k_mx_down(MxFfnArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+    mx_down_phase(a, lds);
+}
+
 __global__ __launch_bounds__(256) void k_transpose(TransposeArgs a) {
     __shared__ uint16_t tile[64][72];
     const int64_t ntiles = (int64_t)a.B * ((a.R + 63) / 64) * ((a.C + 63) / 64);
@@ -367,6 +383,18 @@ int launch_ffn(const moe_desc *d, const FfnArgs &a, hipStream_t s) {
     return launch_cooperative(reinterpret_cast<const void *>(k_ffn_chunked), grid, args, s);
 }
 
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+int launch_mx_quantize(const uint16_t *src, int64_t rows, int32_t K, uint8_t *q, uint8_t *sc, hipStream_t s,
+                       const char *name) {
+    const int64_t nblocks = rows * (K / 32);
+    if (nblocks == 0) return MOE_OK;
+    const int grid = (int)std::min<int64_t>((nblocks + 255) / 256, 16ll * device_cus());
+    TraceScope tr(name, s);
+    hipLaunchKernelGGL(k_mx_quantize, dim3(grid), dim3(256), 0, s, src, nblocks, (int)K, q, sc);
+    return launch_status();
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -628,6 +656,67 @@ int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes
     TraceScope tr("bwd_wgrad", s);
     hipLaunchKernelGGL(k_wgrad, dim3(grid), dim3(kFwdThreads), 0, s, a);
     return launch_status();
+}
+
+int moe_quantize_mx(const uint16_t *src, int64_t rows, int32_t K, uint8_t *q, uint8_t *scales, void *stream) {
+    if (rows < 0 || K <= 0 || K % 32) return MOE_EINVAL;
+    if (rows == 0) return MOE_OK;
+    if (!src || !q || !scales || !aligned16(src) || !aligned16(q)) return MOE_EINVAL;
+    return launch_mx_quantize(src, rows, K, q, scales, static_cast<hipStream_t>(stream), "mx_quantize");
+}
+
+int moe_layer_fwd_mx(const moe_desc *d, const int32_t *routes, const float *w, const uint16_t *X,
+                     const uint8_t *W13q, const uint8_t *W13s, const uint8_t *W2q, const uint8_t *W2s,
+                     int32_t *counts, int32_t *seg_off, moe_src *phi, int32_t *route_row, uint8_t *Xq,
+                     uint8_t *Xs, uint8_t *Aq, uint8_t *As, uint16_t *Y, uint16_t *out, void *ws,
+                     size_t ws_bytes, void *stream) {
+    int rc = check_desc(d, true);
+    if (rc != MOE_OK) return rc;
+    if (d->num_batches != 1) return MOE_EINVAL;
+    const void *a16[] = {routes, w, X, W13q, W2q, counts, seg_off, phi, route_row, Xq, Aq, Y, out, ws};
+    for (const void *p : a16)
+        if (!p || !aligned16(p)) return MOE_EINVAL;
+    const void *a4[] = {W13s, W2s, Xs, As};
+    for (const void *p : a4)
+        if (!p || !aligned4(p)) return MOE_EINVAL;
+    if (d->H % 128 || d->H > 2 * kZeroRowElems) return MOE_EUNSUPPORTED;
+    if ((int64_t)ws_bytes < moe_workspace_bytes(d, MOE_OP_LAYER_FWD)) return MOE_ENOSPC;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *sched_ws = static_cast<char *>(ws) + kBarrierBytes;
+    moe_desc one = *d;
+    one.num_batches = 1;
+    rc = launch_schedule(&one, routes, counts, seg_off, phi, route_row, sched_ws, s);
+    if (rc != MOE_OK) return rc;
+    rc = launch_mx_quantize(X, (int64_t)d->P * d->Np, d->H, Xq, Xs, s, "mx_quantize_x");
+    if (rc != MOE_OK) return rc;
+    MxFfnArgs a;
+    a.Xq = Xq;
+    a.Xs = Xs;
+    a.phi = phi;
+    a.Np = d->Np;
+    a.W13q = W13q;
+    a.W13s = W13s;
+    a.W2q = W2q;
+    a.W2s = W2s;
+    a.seg_off = seg_off;
+    a.Aq = Aq;
+    a.As = As;
+    a.Y = Y;
+    a.L = d->L;
+    a.H = d->H;
+    a.I = d->I;
+    const int grid = gemm_grid();
+    {
+        TraceScope tr("mx_gateup", s);
+        hipLaunchKernelGGL(k_mx_gateup, dim3(grid), dim3(kFwdThreads), 0, s, a);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    {
+        TraceScope tr("mx_down", s);
+        hipLaunchKernelGGL(k_mx_down, dim3(grid), dim3(kFwdThreads), 0, s, a);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    return launch_combine(d, Y, route_row, w, out, s, "combine");
 }
 
 int moe_trace_enable(int max_records) {

@@ -1,0 +1,317 @@
+// MXFP8 routed experts ("Mixture-of-Kittens: A MoE Megakernel for GB300
+// NVL72", section 5, mixed precision: the routed experts run in MXFP8 with
+// the activation quantization fused into the dispatch loads, the grouped GEMMs
+// and SwiGLU).
+//
+// Format (OCP Microscaling, the reading of "MXFP8"): blocks of 32 consecutive
+// elements along the reduction dimension share an E8M0 scale
+// 2^(floor(log2 amax) - 8), stored as a byte (exponent + 127, clamped to
+// [-127, 127]; an all-zero block gets 0); each element is x / scale rounded to
+// FP8 E4M3 (bias 7, subnormals, no infinities) to nearest, ties to even,
+// saturating at +-448.  Codes are stored row-major [rows][K] and scale bytes
+// [rows][K/32].
+//
+// GEMM: gfx950's v_mfma_scale_f32_32x32x64_f8f6f4 multiplies 32 x 64 blocks of
+// E4M3 codes with one scale per lane.  Lane l holds row l % 32; its bytes
+// 0-15 are 16 elements of the first 32-element K block of the instruction and
+// bytes 16-31 16 elements of the second, the two lane halves splitting each
+// block; lane l supplies the scale of block l / 32 of its row in the byte the
+// op_sel immediate names (checked on the hardware with controlled inputs).
+// A 256 x 256 tile with 128-deep K steps therefore moves exactly the bytes of
+// the bf16 tile with 64-deep steps (the same DMA and LDS swizzle) for twice
+// the flops.
+#pragma once
+
+#include "common.hpp"
+#include "gemm.hpp"
+
+namespace moe {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// E4M3 code of a finite float, nearest with ties to even, saturating at 448
+// (branch-free: every case is computed and selected).
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+    const uint32_t s = __float_as_uint(y) >> 31;
+    const float a = fabsf(y);
+    // one quantum: 2^(E-3) for a normal value (E = floor(log2 a) >= -6), 2^-9 below
+    const int E = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;
+    const int qexp = a < 0.015625f ? -9 : E - 3;
+    const float q = __builtin_rintf(__builtin_amdgcn_ldexpf(a, -qexp));  // exact scaling, round to even
+    const float mag = __builtin_amdgcn_ldexpf(q, qexp);
+    const uint32_t b = __float_as_uint(mag);
+    const uint32_t normal = ((((b >> 23) & 0xff) - 127 + 7) << 3) | ((b >> 20) & 7u);
+    uint32_t code = mag < 0.015625f ? (uint32_t)q : normal;  // subnormal: m = q in 0..7
+    code = (a >= 448.0f || mag >= 448.0f) ? 0x7Eu : code;
+    return (s << 7) | code;
+}
+
+// Block exponent: floor(log2 amax) - 8 clamped to [-127, 127]; -127 for 0.
+__device__ __forceinline__ int mx_block_exp(float amax) {
+    if (!(amax > 0.0f)) return -127;
+    const uint32_t b = __float_as_uint(amax);
+    int e = (int)(b >> 23) - 127;
+    if ((b >> 23) == 0) e = -127 - (__builtin_clz(b & 0x7fffffu) - 9);  // fp32 subnormal
+    const int se = e - 8;
+    return se < -127 ? -127 : (se > 127 ? 127 : se);
+}
+
+// Codes of 32 values v (fp32) into 8 words, with the block's scale byte.
+__device__ __forceinline__ uint32_t mx_quantize32(const float (&v)[32], uint32_t (&w)[8]) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const int se = mx_block_exp(amax);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x |= e4m3_encode(__builtin_amdgcn_ldexpf(v[4 * k + j], -se)) << (8 * j);
+        w[k] = x;
+    }
+    return (uint32_t)(se + 127);
+}
+
+// Row-wise quantization of bf16 [rows][K]: block b (of rows * K / 32) per call.
+__device__ __forceinline__ void mx_quantize_block_bf16(const uint16_t *src, int K, uint8_t *q, uint8_t *s,
+                                                       int64_t b) {
+    const int64_t row = b / (K / 32), blk = b % (K / 32);
+    const u32x4 *in = reinterpret_cast<const u32x4 *>(src + row * K + blk * 32);
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const u32x4 x = in[c];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            v[8 * c + 2 * d] = __uint_as_float(x[d] << 16);
+            v[8 * c + 2 * d + 1] = __uint_as_float(x[d] & 0xffff0000u);
+        }
+    }
+    uint32_t w[8];
+    const uint32_t sb = mx_quantize32(v, w);
+    u32x4 *out = reinterpret_cast<u32x4 *>(q + row * K + blk * 32);
+    out[0] = u32x4{w[0], w[1], w[2], w[3]};
+    out[1] = u32x4{w[4], w[5], w[6], w[7]};
+    s[row * (K / 32) + blk] = (uint8_t)sb;
+}
+
+// Scale rows of an MX operand window, parallel to a KOp: row i's scale bytes
+// start at (rows ? gathered row : (i < 128 ? lo : hi) + (i & 127) * ld).
+struct SOp {
+    const uint8_t *lo, *hi;
+    int64_t ld;  // bytes per row = K / 32
+    const moe_src *rows;
+    const uint8_t *src;
+    int32_t np;
+};
+
+// A padding row of a gathered operand reads zero codes (the zero row), so any
+// scale serves it: it takes source row 0's.
+__device__ __forceinline__ const uint32_t *mx_scale_row(const SOp &op, int row) {
+    const uint8_t *base;
+    if (op.rows) {
+        const uint2 s = reinterpret_cast<const uint2 *>(op.rows)[row];
+        const int64_t src_row = (int32_t)s.x >= 0 ? (int64_t)(int32_t)s.x * op.np + (int32_t)s.y : 0;
+        base = op.src + src_row * op.ld;
+    } else {
+        base = (row < 128 ? op.lo : op.hi) + (int64_t)(row & 127) * op.ld;
+    }
+    return reinterpret_cast<const uint32_t *>(base);
+}
+
+// dma_src_w for an MX operand tile, kept out of line: inlined into the MX
+// main loop together with a gathered operand, its branch makes this
+// compiler's CFG simplification crash.  It runs once per tile and lane.
+template <int NW>
+__device__ __attribute__((noinline)) const uint16_t *mx_dma_src(const KOp &op, int i) {
+    return dma_src_w<64, 3, NW>(op, i);
+}
+
+template <int OPSEL>
+__device__ __forceinline__ f32x16 mfma_mx(const i32x8 &a, const i32x8 &b, const f32x16 &c, uint32_t sa, uint32_t sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPSEL, (int)sa, OPSEL, (int)sb);
+}
+
+// Two 16-byte chunks of an operand tile row as one MFMA fragment.
+__device__ __forceinline__ i32x8 mx_frag(const char *tile, int row, int c0, int c1) {
+    const u32x4 x = *reinterpret_cast<const u32x4 *>(tile + tile_off_t<64, 3>(row, c0));
+    const u32x4 y = *reinterpret_cast<const u32x4 *>(tile + tile_off_t<64, 3>(row, c1));
+    return i32x8{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+}
+
+// One 64-deep sub-step S (0 or 1) of an MX step: fragment reads and the
+// MI x NI MFMAs (op_sel S*2 picks this sub-step's scale byte); in sub-step 0
+// one DMA instruction of the next stage follows every EVERY MFMAs.
+template <int WM, int WN, int S, int EVERY, int GH, bool FILL>
+__device__ __forceinline__ void mx_substep(const char *stage, int arow, const int (&brow)[WaveGrid<WM, WN>::NI], int h,
+                                           const uint32_t (&ca)[WaveGrid<WM, WN>::MI],
+                                           const uint32_t (&cb)[WaveGrid<WM, WN>::NI], AccW<WM, WN> &acc,
+                                           const uint16_t *const (&asrc)[GH], const uint16_t *const (&bsrc)[GH],
+                                           int k0, char *dst) {
+    using WG = WaveGrid<WM, WN>;
+    constexpr int MI = WG::MI, NI = WG::NI, NW = WG::NW;
+    constexpr int tile_bytes = 256 * 128;
+    i32x8 fa[MI], fb[NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) fa[mi] = mx_frag(stage, arow + mi * 32, 4 * S + h, 4 * S + 2 + h);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) fb[ni] = mx_frag(stage + tile_bytes, brow[ni], 4 * S + h, 4 * S + 2 + h);
+#pragma unroll
+    for (int q = 0; q < MI * NI; ++q) {
+        const int mi = q / NI, ni = q % NI;
+        acc[mi][ni] = mfma_mx<2 * S>(fa[mi], fb[ni], acc[mi][ni], ca[mi], cb[ni]);
+        if constexpr (S == 0 && FILL) {
+            if ((q + 1) % EVERY == 0) {
+                const int g = (q + 1) / EVERY - 1;
+                const bool isa = g < GH;
+                dma_blk_w<64, NW>(isa ? asrc[g] : bsrc[g - GH], k0, isa ? dst : dst + tile_bytes, isa ? g : g - GH);
+            }
+        }
+    }
+    if constexpr (S == 0 && FILL) {
+#pragma unroll
+        for (int j = 0; j < 2 * GH; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, EVERY, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+    }
+}
+
+// One 128-deep K step kt on stage `slot`: wait for the stage, take this
+// step's scale words, and with FILL spread the next stage's DMA over
+// sub-step 0 and load the next step's scale words after it.
+template <int WM, int WN, int EVERY, int GH, bool FILL>
+__device__ __forceinline__ void mx_step(char *lds, int slot, int kt, int arow, const int (&brow)[WaveGrid<WM, WN>::NI],
+                                        int h, uint32_t (&sa)[WaveGrid<WM, WN>::MI],
+                                        uint32_t (&sb)[WaveGrid<WM, WN>::NI],
+                                        const uint32_t *const (&sarow)[WaveGrid<WM, WN>::MI],
+                                        const uint32_t *const (&sbrow)[WaveGrid<WM, WN>::NI], AccW<WM, WN> &acc,
+                                        const uint16_t *const (&asrc)[GH], const uint16_t *const (&bsrc)[GH]) {
+    using WG = WaveGrid<WM, WN>;
+    constexpr int MI = WG::MI, NI = WG::NI;
+    constexpr int stage_bytes = 2 * 256 * 128;
+    wait_vm_barrier<0>();
+    char *dst = lds + (slot ^ 1) * stage_bytes;
+    const char *stage = lds + slot * stage_bytes;
+    uint32_t ca[MI], cb[NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) ca[mi] = sa[mi] >> (8 * h);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) cb[ni] = sb[ni] >> (8 * h);
+    mx_substep<WM, WN, 0, EVERY, GH, FILL>(stage, arow, brow, h, ca, cb, acc, asrc, bsrc, (kt + 1) * 64, dst);
+    // after sub-step 0, so the pinned vector-memory slots there are the DMA's
+    if constexpr (FILL) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) sa[mi] = sarow[mi][kt + 1];
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) sb[ni] = sbrow[ni][kt + 1];
+    }
+    mx_substep<WM, WN, 1, EVERY, GH, FILL>(stage, arow, brow, h, ca, cb, acc, asrc, bsrc, (kt + 1) * 64, dst);
+}
+
+// MX main loop: 256 x 256 tile, K steps of 128 codes (one [256][128]-byte
+// operand tile each, the bf16 loop's DMA and swizzle), two 64-deep MFMA
+// sub-steps per step, double buffered.  ak/bk address the codes as 16-bit
+// units (ld = K / 2); as/bs the scale bytes.  The next stage's DMA is spread
+// over the first sub-step's MFMAs; the scale words of step kt+1 are loaded
+// during step kt.
+template <int WM, int WN>
+__device__ __forceinline__ void gemm_mainloop_mx(const KOp &ak, const KOp &bk, const SOp &as, const SOp &bs, int nk,
+                                                 bool swiglu, char *lds, AccW<WM, WN> &acc) {
+    using WG = WaveGrid<WM, WN>;
+    constexpr int MI = WG::MI, NI = WG::NI, NW = WG::NW;
+    constexpr int tile_bytes = 256 * 128;
+    constexpr int stage_bytes = 2 * tile_bytes;
+    constexpr int GH = tile_bytes / 1024 / NW;
+    constexpr int G = 2 * GH;
+    static_assert((MI * NI) % G == 0, "DMA slots in one sub-step");
+    constexpr int EVERY = MI * NI / G;
+    static_assert(2 * stage_bytes <= kGemmLds, "LDS budget");
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int wm = wave / WN, wn = wave % WN, h = lane >> 5;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+    if (nk <= 0) return;
+    int brow[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) brow[ni] = WG::brow(swiglu, wn, ni) + (lane & 31);
+    const int arow = wm * (MI * 32) + (lane & 31);
+    const uint16_t *asrc[GH], *bsrc[GH];
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+        asrc[i] = mx_dma_src<NW>(ak, i);
+        bsrc[i] = mx_dma_src<NW>(bk, i);
+    }
+    const uint32_t *sarow[MI], *sbrow[NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) sarow[mi] = mx_scale_row(as, arow + mi * 32);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) sbrow[ni] = mx_scale_row(bs, brow[ni]);
+    uint32_t sa[MI], sb[NI];  // this step's scale words, shifted to this lane's half
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) sa[mi] = sarow[mi][0];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) sb[ni] = sbrow[ni][0];
+    __syncthreads();  // the previous tile's epilogue may still read LDS
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+        dma_blk_w<64, NW>(asrc[i], 0, lds, i);
+        dma_blk_w<64, NW>(bsrc[i], 0, lds + tile_bytes, i);
+    }
+    int slot = 0;
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+        mx_step<WM, WN, EVERY, GH, true>(lds, slot, kt, arow, brow, h, sa, sb, sarow, sbrow, acc, asrc, bsrc);
+        slot ^= 1;
+    }
+    mx_step<WM, WN, EVERY, GH, false>(lds, slot, nk - 1, arow, brow, h, sa, sb, sarow, sbrow, acc, asrc, bsrc);
+    __syncthreads();
+}
+
+// Gate/up tile -> a = silu(gate) * up (256 rows x 128 columns), MX-quantized
+// along the columns: codes Aq[row][0..128) and 4 scale bytes per row.  The fp32
+// tile goes through LDS (128 KiB); then every thread quantizes whole 32-column
+// blocks of a row.
+template <int WM, int WN>
+__device__ __forceinline__ void epilogue_swiglu_mx(AccW<WM, WN> &acc, char *lds, uint8_t *Aq, int64_t ldq,
+                                                   uint8_t *As, int64_t lds_row) {
+    using WG = WaveGrid<WM, WN>;
+    constexpr int NT = WG::THREADS, half = WG::NI / 2;
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63, wm = wave / WN, wn = wave % WN;
+    float *st = reinterpret_cast<float *>(lds);  // [256][128]
+    __syncthreads();
+    float *base = st + (wm * (WG::MI * 32) + 4 * (lane >> 5)) * 128 + wn * (half * 32) + (lane & 31);
+#pragma unroll
+    for (int mi = 0; mi < WG::MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < half; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                base[(mi * 32 + 8 * (e >> 2) + (e & 3)) * 128 + ni * 32] =
+                    silu_f(acc[mi][ni][e]) * acc[mi][ni + half][e];
+    __syncthreads();
+    for (int b = t; b < 256 * 4; b += NT) {
+        const int row = b >> 2, blk = b & 3;
+        float v[32];
+        const float4 *src = reinterpret_cast<const float4 *>(st + row * 128 + blk * 32);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float4 x = src[c];
+            v[4 * c] = x.x;
+            v[4 * c + 1] = x.y;
+            v[4 * c + 2] = x.z;
+            v[4 * c + 3] = x.w;
+        }
+        uint32_t w[8];
+        const uint32_t sb = mx_quantize32(v, w);
+        u32x4 *out = reinterpret_cast<u32x4 *>(Aq + row * ldq + blk * 32);
+        out[0] = u32x4{w[0], w[1], w[2], w[3]};
+        out[1] = u32x4{w[4], w[5], w[6], w[7]};
+        As[row * lds_row + blk] = (uint8_t)sb;
+    }
+}
+
+}  // namespace moe

@@ -25,6 +25,8 @@ MOE_PERSISTENT = 1
 EXPORTED = (
     "moe_strerror", "moe_capacity_rows", "moe_workspace_bytes", "moe_schedule", "moe_dispatch",
     "moe_expert_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_bwd", "moe_trace_enable", "moe_trace_read",
+    "moe_quantize_mx",
+    "moe_layer_fwd_mx",
 )
 
 
@@ -68,6 +70,8 @@ def load() -> ctypes.CDLL:
         "moe_expert_ffn": (ctypes.c_int, [D, P, P, P, P, P, P, P, i32, P, sz, P]),
         "moe_combine": (ctypes.c_int, [D, P, P, P, P, P]),
         "moe_layer_fwd": (ctypes.c_int, [D] + [P] * 14 + [i32, i32, P, sz, P]),
+        "moe_quantize_mx": (ctypes.c_int, [P, i64, i32, P, P, P]),
+        "moe_layer_fwd_mx": (ctypes.c_int, [D] + [P] * 18 + [sz, P]),
         "moe_layer_bwd": (ctypes.c_int, [D] + [P] * 16 + [sz, P]),
         "moe_trace_enable": (ctypes.c_int, [ctypes.c_int]),
         "moe_trace_read": (ctypes.c_int, [P, P, ctypes.c_int]),
@@ -213,3 +217,72 @@ def alloc_fwd(d: moe_desc, device, save_hu: bool = True, save_xd: bool = True) -
 def layer_fwd(d, routes, w, X, W13, W2, bufs: FwdBuffers, flags=0, chunk_rows=0, stream=None):
     return moe_layer_fwd(d, routes, w, X, W13, W2, bufs.counts, bufs.seg_off, bufs.phi, bufs.route_row, bufs.Xd,
                          bufs.HU, bufs.A, bufs.Y, bufs.out, flags, chunk_rows, bufs.ws, stream)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 routed experts.
+# ---------------------------------------------------------------------------
+
+def moe_quantize_mx(src, q, scales, stream=None):
+    """Row-wise MX quantization of a bf16 tensor [..., K] into codes (uint8,
+    same shape) and scale bytes (uint8 [..., K/32])."""
+    K = src.shape[-1]
+    rows = src.numel() // K if K else 0
+    rc = load().moe_quantize_mx(_dev(src), rows, K, _dev(q), _dev(scales), _stream(stream, src))
+    return _check(rc, "moe_quantize_mx")
+
+
+def quantize_mx(src, stream=None):
+    """Allocate and fill (codes, scales) for a bf16 tensor [..., K]."""
+    q = torch.empty(src.shape, dtype=torch.uint8, device=src.device)
+    s = torch.empty(src.shape[:-1] + (src.shape[-1] // 32,), dtype=torch.uint8, device=src.device)
+    moe_quantize_mx(src, q, s, stream)
+    return q, s
+
+
+def moe_layer_fwd_mx(d, routes, w, X, W13q, W13s, W2q, W2s, counts, seg_off, phi, route_row, Xq, Xs, Aq, As, Y, out,
+                     ws, stream=None):
+    rc = load().moe_layer_fwd_mx(ctypes.byref(d), _dev(routes), _dev(w), _dev(X), _dev(W13q), _dev(W13s), _dev(W2q),
+                                 _dev(W2s), _dev(counts), _dev(seg_off), _dev(phi), _dev(route_row), _dev(Xq),
+                                 _dev(Xs), _dev(Aq), _dev(As), _dev(Y), _dev(out), _dev(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream, X))
+    return _check(rc, "moe_layer_fwd_mx")
+
+
+@dataclass
+class MxFwdBuffers:
+    counts: torch.Tensor
+    seg_off: torch.Tensor
+    phi: torch.Tensor
+    route_row: torch.Tensor
+    Xq: torch.Tensor
+    Xs: torch.Tensor
+    Aq: torch.Tensor
+    As: torch.Tensor
+    Y: torch.Tensor
+    out: torch.Tensor
+    ws: torch.Tensor
+
+
+def alloc_fwd_mx(d: moe_desc, device) -> MxFwdBuffers:
+    cap = capacity_rows(d)
+    i32, u8 = torch.int32, torch.uint8
+    ntok = d.P * d.Np
+    return MxFwdBuffers(
+        counts=torch.empty((d.L, d.P), dtype=i32, device=device),
+        seg_off=torch.empty(d.L + 1, dtype=i32, device=device),
+        phi=torch.empty((cap, 2), dtype=i32, device=device),
+        route_row=torch.empty((d.P, d.Np, d.K), dtype=i32, device=device),
+        Xq=torch.empty((d.P, d.Np, d.H), dtype=u8, device=device),
+        Xs=torch.empty((d.P, d.Np, d.H // 32), dtype=u8, device=device),
+        Aq=torch.empty((cap, d.I), dtype=u8, device=device),
+        As=torch.empty((cap, d.I // 32), dtype=u8, device=device),
+        Y=torch.empty((cap, d.H), dtype=torch.bfloat16, device=device),
+        out=torch.empty((d.P, d.Np, d.H), dtype=torch.bfloat16, device=device),
+        ws=torch.empty(max(workspace_bytes(d, MOE_OP_LAYER_FWD), 256), dtype=torch.uint8, device=device),
+    )
+
+
+def layer_fwd_mx(d, routes, w, X, W13q, W13s, W2q, W2s, bufs: MxFwdBuffers, stream=None):
+    return moe_layer_fwd_mx(d, routes, w, X, W13q, W13s, W2q, W2s, bufs.counts, bufs.seg_off, bufs.phi,
+                            bufs.route_row, bufs.Xq, bufs.Xs, bufs.Aq, bufs.As, bufs.Y, bufs.out, bufs.ws, stream)

@@ -136,5 +136,23 @@ def test_schedule_lds_limit():
     assert lib.moe_schedule(ctypes.byref(d), *p, ws, None) == ops.MOE_EUNSUPPORTED
 
 
+def test_mx_arguments_rejected_before_launch():
+    lib = ops.load()
+    p = [_fake(0x10000 * (i + 1)) for i in range(20)]
+    assert lib.moe_quantize_mx(p[0], 4, 48, p[1], p[2], None) == ops.MOE_EINVAL  # K not a multiple of 32
+    assert lib.moe_quantize_mx(p[0], -1, 64, p[1], p[2], None) == ops.MOE_EINVAL
+    assert lib.moe_quantize_mx(_fake(0x10008), 4, 64, p[1], p[2], None) == ops.MOE_EINVAL  # misaligned
+    assert lib.moe_quantize_mx(None, 0, 64, None, None, None) == ops.MOE_OK  # nothing to do
+    d = kimi()
+    ws = lib.moe_workspace_bytes(ctypes.byref(d), ops.MOE_OP_LAYER_FWD)
+    args = p[:18]  # 17 operands and the workspace
+    assert lib.moe_layer_fwd_mx(ctypes.byref(d), *args[:5], None, *args[6:], ws, None) == ops.MOE_EINVAL
+    assert lib.moe_layer_fwd_mx(ctypes.byref(d), *args[:3], _fake(0x10004), *args[4:], ws, None) == ops.MOE_EINVAL
+    assert lib.moe_layer_fwd_mx(ctypes.byref(d), *args, ws - 1, None) == ops.MOE_ENOSPC
+    d2 = ops.make_desc(8, 7168, 8, 384, 48, H=65536 + 256, I=2048)  # rows wider than the zero row for padding
+    ws2 = lib.moe_workspace_bytes(ctypes.byref(d2), ops.MOE_OP_LAYER_FWD)
+    assert lib.moe_layer_fwd_mx(ctypes.byref(d2), *args, ws2, None) == ops.MOE_EUNSUPPORTED
+
+
 def test_trace_read_empty():
     assert ops.moe_trace_read(4) == []

@@ -1,0 +1,200 @@
+"""MXFP8 routed experts on the GPU vs the CPU oracle (OCP microscaling reading
+of the Mixture-of-Kittens notes, section 5).
+
+Quantization of bf16 inputs (X, W13, W2) is a fixed function of the input, so
+codes and scale bytes must match the oracle bit for bit.  The activation a is
+computed in fp32 on the GPU and in fp64 by the oracle before it is quantized,
+so its codes may differ where a value sits on a rounding boundary: they must
+agree for almost every element, and their dequantized values within rel-L2
+1e-2.  Y and the combined output must be within rel-L2 1e-2 of the oracle's MX
+path; padding rows exactly zero; repeated runs bitwise identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from routing_schedule_expert_amd import inputs, ops
+from tests.helpers import dev, f64, rel_l2, up, up_bf16
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+def bf16_bits(x):
+    return inputs.bf16_bits(np.asarray(x, np.float32))
+
+
+def edge_rows(rng, K):
+    """Rows that exercise the quantizer's corner cases, 32-element blocks."""
+    rows = [rng.standard_normal(K) * 3]
+    z = rng.standard_normal(K)
+    z[:32] = 0.0                                   # all-zero block
+    z[32:64] = -0.0
+    rows.append(z)
+    rows.append(rng.standard_normal(K) * 1e-39)   # bf16 subnormals
+    s = rng.standard_normal(K)
+    s[::32] = 1.9375 * np.sign(s[::32] + 1e-9)    # maxima with mantissa > 1.75: saturation
+    rows.append(s)
+    m = rng.standard_normal(K) * 1e-4
+    m[5::32] = 1e4                                 # tiny elements under a large maximum
+    rows.append(m)
+    t = np.zeros(K)
+    t[:] = 1.0625                                  # ties at 1.0625 * 2^8 after scaling: to even
+    t[::32] = 1.0
+    rows.append(t)
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("K", [32, 256, 7168])
+def test_quantize_bit_exact(K):
+    rng = np.random.default_rng(K)
+    x = np.concatenate([edge_rows(rng, K), rng.standard_normal((57, K)).astype(np.float32) * 0.02])
+    xb = bf16_bits(x)
+    q_ref, s_ref = oracle.mx_quantize(xb)
+    src = up_bf16(xb)
+    q, s = ops.quantize_mx(src)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(s.cpu().numpy(), s_ref)
+
+
+def test_quantize_large_bit_exact():
+    rng = np.random.default_rng(9)
+    xb = bf16_bits(rng.standard_normal((2048, 2048)).astype(np.float32))
+    q_ref, s_ref = oracle.mx_quantize(xb)
+    q, s = ops.quantize_mx(up_bf16(xb))
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(s.cpu().numpy(), s_ref)
+
+
+class MxLayer:
+    def __init__(self, seed, P, Np, E, K, L, H, I, routing="uniform", s=1.2):
+        self.h = inputs.make_layer_inputs(seed, P, Np, E, K, L, H, I, routing=routing, x_std=1.0, s=s)
+        self.P, self.Np, self.K, self.L, self.H, self.I = P, Np, K, L, H, I
+        self.d = ops.make_desc(P, Np, K, E, L, H=H, I=I)
+        self.routes, self.w = up(self.h["routes"]), up(self.h["w"])
+        self.X = up_bf16(self.h["X"])
+        self.W13q, self.W13s = ops.quantize_mx(up_bf16(self.h["W13"]))
+        self.W2q, self.W2s = ops.quantize_mx(up_bf16(self.h["W2"]))
+
+    def fwd(self):
+        b = ops.alloc_fwd_mx(self.d, dev())
+        ops.layer_fwd_mx(self.d, self.routes, self.w, self.X, self.W13q, self.W13s, self.W2q, self.W2s, b)
+        torch.cuda.synchronize()
+        return b
+
+
+def check_mx_full(lay: MxLayer, b):
+    h = lay.h
+    s = oracle.schedule(h["routes"], lay.L, 0, 256)
+    np.testing.assert_array_equal(b.phi[: s.npad].cpu().numpy(), s.phi)
+    np.testing.assert_array_equal(b.route_row.cpu().numpy(), s.route_row)
+    Xq, Xs = oracle.mx_quantize(h["X"])
+    np.testing.assert_array_equal(b.Xq.cpu().numpy(), Xq)
+    np.testing.assert_array_equal(b.Xs.cpu().numpy(), Xs)
+    W13q, W13s = oracle.mx_quantize(h["W13"])
+    W2q, W2s = oracle.mx_quantize(h["W2"])
+    np.testing.assert_array_equal(lay.W13q.cpu().numpy(), W13q)
+    np.testing.assert_array_equal(lay.W2s.cpu().numpy(), W2s)
+    Xdq, Xds = oracle.mx_dispatch(Xq, Xs, s.phi)
+    r = oracle.mx_expert_ffn_rows(s.seg_off, Xdq, Xds, W13q, W13s, W2q, W2s)
+    real = s.phi[:, 0] >= 0
+    Aq, As = b.Aq[: s.npad].cpu().numpy(), b.As[: s.npad].cpu().numpy()
+    same = (Aq[real] == r["Aq"][real]).mean()
+    print(f"[mx] a codes equal to the oracle's: {same:.5f}", flush=True)
+    assert same >= 0.98
+    a_gpu = oracle.mx_dequantize(Aq, As)
+    a_ref = oracle.mx_dequantize(r["Aq"], r["As"])
+    assert rel_l2(a_gpu[real], a_ref[real]) <= TOL
+    Y = f64(b.Y[: s.npad])
+    err = rel_l2(Y[real], r["Y"][real])
+    print(f"[mx] Y rel-L2 {err:.2e}", flush=True)
+    assert err <= TOL
+    assert not Y[~real].any()
+    assert not a_gpu[~real].any()
+    out = oracle.mx_layer_fwd_tokens(h["routes"], h["w"], Xq, Xs, W13q, W13s, W2q, W2s, L=lay.L)
+    err = rel_l2(f64(b.out).reshape(out.shape), out)
+    print(f"[mx] out rel-L2 {err:.2e}", flush=True)
+    assert err <= TOL
+
+
+def test_mx_tiny_forward():
+    print("[mx] tiny forward", flush=True)
+    lay = MxLayer(1, 2, 256, 8, 2, 4, 256, 128, routing="topk")
+    check_mx_full(lay, lay.fwd())
+
+
+def test_mx_small_forward_multi_tile():
+    print("[mx] small forward, several tiles and ragged segments", flush=True)
+    lay = MxLayer(3, 4, 700, 12, 3, 6, 512, 256, routing="zipf", s=1.2)
+    check_mx_full(lay, lay.fwd())
+
+
+def test_mx_repeat_bitwise():
+    lay = MxLayer(8, 4, 500, 16, 4, 8, 512, 256, routing="zipf")
+    a, b = lay.fwd(), lay.fwd()
+    npad = int(a.seg_off[-1])  # rows past Npad are never written
+    assert torch.equal(a.out, b.out)
+    assert torch.equal(a.Y[:npad], b.Y[:npad]) and torch.equal(a.Aq[:npad], b.Aq[:npad])
+    assert torch.equal(a.As[:npad], b.As[:npad])
+
+
+def test_mx_kimi_sampled():
+    """Kimi-shaped share (8 x 7,168 tokens, 384 experts with 48 local, top-8,
+    H=7168, I=2048, balanced routing): X codes of sampled rows bit-exact,
+    a and Y of rows of four experts, out of 256 tokens."""
+    print("[mx] Kimi shape", flush=True)
+    c = dict(P=8, Np=7168, E=384, K=8, L=48, H=7168, I=2048)
+    h = inputs.make_layer_inputs_device(5, c["P"], c["Np"], c["E"], c["K"], c["L"], c["H"], c["I"], dev(),
+                                        routing="balanced", x_std=1.0)
+    d = ops.make_desc(c["P"], c["Np"], c["K"], c["E"], c["L"], H=c["H"], I=c["I"])
+    W13q, W13s = ops.quantize_mx(h["W13"])
+    W2q, W2s = ops.quantize_mx(h["W2"])
+    routes, w = torch.from_numpy(h["routes"]).to(dev()), torch.from_numpy(h["w"]).to(dev())
+    b = ops.alloc_fwd_mx(d, dev())
+    ops.layer_fwd_mx(d, routes, w, h["X"], W13q, W13s, W2q, W2s, b)
+    torch.cuda.synchronize()
+    s = oracle.schedule(h["routes"], c["L"], 0, 256)
+    np.testing.assert_array_equal(b.phi[: s.npad].cpu().numpy(), s.phi)
+    host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    X = host(h["X"])
+    rng = np.random.default_rng(3)
+    toks = np.sort(rng.choice(c["P"] * c["Np"], 256, replace=False))
+    Xq_ref, Xs_ref = oracle.mx_quantize(X.reshape(-1, c["H"])[toks])
+    np.testing.assert_array_equal(b.Xq.view(-1, c["H"])[torch.from_numpy(toks).to(dev())].cpu().numpy(), Xq_ref)
+    np.testing.assert_array_equal(b.Xs.view(-1, c["H"] // 32)[torch.from_numpy(toks).to(dev())].cpu().numpy(),
+                                  Xs_ref)
+    # weights: the codes the GPU made are the oracle's (checked on two experts' rows)
+    W13 = host(h["W13"])
+    W2 = host(h["W2"])
+    for l in (0, 47):
+        q, sc = oracle.mx_quantize(W13[l])
+        np.testing.assert_array_equal(W13q[l].cpu().numpy(), q)
+        np.testing.assert_array_equal(W13s[l].cpu().numpy(), sc)
+    W13q_h, W13s_h = W13q.cpu().numpy(), W13s.cpu().numpy()
+    W2q_h, W2s_h = W2q.cpu().numpy(), W2s.cpu().numpy()
+    Xq_all, Xs_all = b.Xq.cpu().numpy(), b.Xs.cpu().numpy()  # bit-exact on the sample above
+    Xdq, Xds = oracle.mx_dispatch(Xq_all, Xs_all, s.phi)
+    seg = np.diff(s.seg_off)
+    sample = []
+    for l in sorted({int(np.argmax(seg)), 0, 17, 47}):
+        real = np.arange(s.seg_off[l], s.seg_off[l + 1])
+        real = real[s.phi[real, 0] >= 0]
+        sample.append(rng.choice(real, 32, replace=False))
+    rows = np.sort(np.concatenate(sample))
+    r = oracle.mx_expert_ffn_rows(s.seg_off, Xdq, Xds, W13q_h, W13s_h, W2q_h, W2s_h, rows=rows)
+    ridx = torch.from_numpy(rows).to(dev())
+    Aq, As = b.Aq[ridx].cpu().numpy(), b.As[ridx].cpu().numpy()
+    same = (Aq == r["Aq"]).mean()
+    print(f"[mx] Kimi a codes equal: {same:.5f}", flush=True)
+    assert same >= 0.98
+    assert rel_l2(oracle.mx_dequantize(Aq, As), oracle.mx_dequantize(r["Aq"], r["As"])) <= TOL
+    err = rel_l2(f64(b.Y[ridx]), r["Y"])
+    print(f"[mx] Kimi Y rel-L2 {err:.2e}", flush=True)
+    assert err <= TOL
+    out_ref = oracle.mx_layer_fwd_tokens(h["routes"], h["w"], Xq_all, Xs_all, W13q_h, W13s_h, W2q_h, W2s_h,
+                                         L=c["L"], tokens=toks)
+    err = rel_l2(f64(b.out.view(-1, c["H"])[torch.from_numpy(toks).to(dev())]), out_ref)
+    print(f"[mx] Kimi out rel-L2 {err:.2e}", flush=True)
+    assert err <= TOL
