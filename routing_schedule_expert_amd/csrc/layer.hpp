@@ -148,6 +148,7 @@ struct MxFfnArgs {
 
 __device__ __forceinline__ const uint16_t *as_u16(const uint8_t *p) { return reinterpret_cast<const uint16_t *>(p); }
 
+template <int SG>
 __device__ __forceinline__ void mx_gateup_tile(const MxFfnArgs &a, int mt, int nt, char *lds) {
     const int H = a.H, I = a.I;
     const int m0 = mt * kBM;
@@ -160,11 +161,12 @@ __device__ __forceinline__ void mx_gateup_tile(const MxFfnArgs &a, int mt, int n
     const SOp bs{ws + (int64_t)nt * 128 * (H / 32), ws + ((int64_t)I + nt * 128) * (H / 32), H / 32, nullptr, nullptr,
                  0};
     AccW<kFwdWM, kFwdWN> acc;
-    gemm_mainloop_mx<kFwdWM, kFwdWN>(ak, bk, as, bs, H / 128, true, lds, acc);
+    gemm_mainloop_mx<kFwdWM, kFwdWN, SG>(ak, bk, as, bs, H / 128, true, lds, acc);
     epilogue_swiglu_mx<kFwdWM, kFwdWN>(acc, lds, a.Aq + (int64_t)m0 * I + nt * 128, I,
                                        a.As + (int64_t)m0 * (I / 32) + nt * 4, I / 32);
 }
 
+template <int SG>
 __device__ __forceinline__ void mx_down_tile(const MxFfnArgs &a, int mt, int nt, char *lds) {
     const int H = a.H, I = a.I;
     const int m0 = mt * kBM;
@@ -178,10 +180,11 @@ __device__ __forceinline__ void mx_down_tile(const MxFfnArgs &a, int mt, int nt,
     const KOp bk{as_u16(w), as_u16(w + 128ll * I), I / 2, nullptr, nullptr, 0};
     const SOp bs{ws, ws + 128ll * (I / 32), I / 32, nullptr, nullptr, 0};
     AccW<kFwdWM, kFwdWN> acc;
-    gemm_mainloop_mx<kFwdWM, kFwdWN>(ak, bk, as, bs, I / 128, false, lds, acc);
+    gemm_mainloop_mx<kFwdWM, kFwdWN, SG>(ak, bk, as, bs, I / 128, false, lds, acc);
     epilogue_store_bf16_w<kFwdWM, kFwdWN>(acc, lds, a.Y + (int64_t)m0 * H + nt * 256, H, 256);
 }
 
+template <int SG>
 __device__ __forceinline__ void mx_gateup_phase(const MxFfnArgs &a, char *lds) {
     const int mtiles = a.seg_off[a.L] / kBM, ntiles = a.I / 128;
     const int64_t total = (int64_t)mtiles * ntiles;
@@ -190,10 +193,11 @@ __device__ __forceinline__ void mx_gateup_phase(const MxFfnArgs &a, char *lds) {
         if (lid >= total) continue;
         int m, n;
         grouped_mn(lid, mtiles, ntiles, 4, m, n);
-        mx_gateup_tile(a, m, n, lds);
+        mx_gateup_tile<SG>(a, m, n, lds);
     }
 }
 
+template <int SG>
 __device__ __forceinline__ void mx_down_phase(const MxFfnArgs &a, char *lds) {
     const int mtiles = a.seg_off[a.L] / kBM, ntiles = a.H / 256;
     const int64_t total = (int64_t)mtiles * ntiles;
@@ -202,7 +206,7 @@ __device__ __forceinline__ void mx_down_phase(const MxFfnArgs &a, char *lds) {
         if (lid >= total) continue;
         int m, n;
         grouped_mn(lid, mtiles, ntiles, 4, m, n);
-        mx_down_tile(a, m, n, lds);
+        mx_down_tile<SG>(a, m, n, lds);
     }
 }
 

@@ -95,14 +95,16 @@ __global__ __launch_bounds__(256) void k_mx_quantize(const uint16_t *src, int64_
         mx_quantize_block_bf16(src, K, q, s, b);
 }
 
+template <int SG>
 __global__ __launch_bounds__(kFwdThreads) void k_mx_gateup(MxFfnArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
-    mx_gateup_phase(a, lds);
+    __shared__ __attribute__((aligned(16))) char lds[kMxLds];
+    mx_gateup_phase<SG>(a, lds);
 }
 
+template <int SG>
 __global__ __launch_bounds__(kFwdThreads) void k_mx_down(MxFfnArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
-    mx_down_phase(a, lds);
+    __shared__ __attribute__((aligned(16))) char lds[kMxLds];
+    mx_down_phase<SG>(a, lds);
 }
 
 __global__ __launch_bounds__(256) void k_transpose(TransposeArgs a) {
@@ -708,12 +710,19 @@ int moe_layer_fwd_mx(const moe_desc *d, const int32_t *routes, const float *w, c
     const int grid = gemm_grid();
     {
         TraceScope tr("mx_gateup", s);
-        hipLaunchKernelGGL(k_mx_gateup, dim3(grid), dim3(kFwdThreads), 0, s, a);
+        // scale rows of H / 32 bytes: 16-byte scale DMAs when they are 16-byte aligned
+        if (d->H % 512 == 0 && aligned16(Xs) && aligned16(W13s))
+            hipLaunchKernelGGL(k_mx_gateup<4>, dim3(grid), dim3(kFwdThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(k_mx_gateup<1>, dim3(grid), dim3(kFwdThreads), 0, s, a);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
     {
         TraceScope tr("mx_down", s);
-        hipLaunchKernelGGL(k_mx_down, dim3(grid), dim3(kFwdThreads), 0, s, a);
+        if (d->I % 512 == 0 && aligned16(As) && aligned16(W2s))
+            hipLaunchKernelGGL(k_mx_down<4>, dim3(grid), dim3(kFwdThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(k_mx_down<1>, dim3(grid), dim3(kFwdThreads), 0, s, a);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
     return launch_combine(d, Y, route_row, w, out, s, "combine");

@@ -107,7 +107,7 @@ struct SOp {
 
 // A padding row of a gathered operand reads zero codes (the zero row), so any
 // scale serves it: it takes source row 0's.
-__device__ __forceinline__ const uint32_t *mx_scale_row(const SOp &op, int row) {
+__device__ __forceinline__ const uint8_t *mx_scale_row(const SOp &op, int row) {
     const uint8_t *base;
     if (op.rows) {
         const uint2 s = reinterpret_cast<const uint2 *>(op.rows)[row];
@@ -116,7 +116,7 @@ __device__ __forceinline__ const uint32_t *mx_scale_row(const SOp &op, int row) 
     } else {
         base = (row < 128 ? op.lo : op.hi) + (int64_t)(row & 127) * op.ld;
     }
-    return reinterpret_cast<const uint32_t *>(base);
+    return base;
 }
 
 // dma_src_w for an MX operand tile, kept out of line: inlined into the MX
@@ -177,56 +177,82 @@ __device__ __forceinline__ void mx_substep(const char *stage, int arow, const in
     }
 }
 
-// One 128-deep K step kt on stage `slot`: wait for the stage, take this
-// step's scale words, and with FILL spread the next stage's DMA over
-// sub-step 0 and load the next step's scale words after it.
-template <int WM, int WN, int EVERY, int GH, bool FILL>
-__device__ __forceinline__ void mx_step(char *lds, int slot, int kt, int arow, const int (&brow)[WaveGrid<WM, WN>::NI],
-                                        int h, uint32_t (&sa)[WaveGrid<WM, WN>::MI],
-                                        uint32_t (&sb)[WaveGrid<WM, WN>::NI],
-                                        const uint32_t *const (&sarow)[WaveGrid<WM, WN>::MI],
-                                        const uint32_t *const (&sbrow)[WaveGrid<WM, WN>::NI], AccW<WM, WN> &acc,
-                                        const uint16_t *const (&asrc)[GH], const uint16_t *const (&bsrc)[GH]) {
+// LDS of an MX GEMM: two 64 KiB stages of operand codes, then the scale
+// words in two buffers of SG-step groups: [2][A, B][256 rows][SG] u32.
+constexpr int kMxScaleBytes = 2 * 2 * 256 * 16;
+constexpr int kMxLds = kGemmLds + kMxScaleBytes;
+
+// Scale group buffer b (0/1) of operand o (0 = A, 1 = B).
+template <int SG>
+__device__ __forceinline__ char *mx_scale_buf(char *lds, int b, int o) {
+    return lds + kGemmLds + b * (2 * 256 * 4 * SG) + o * (256 * 4 * SG);
+}
+
+// This wave's gather DMA of one scale group: lane = operand row (waves 0-3
+// the A rows 64w + lane, waves 4-7 the B rows), SG consecutive step words.
+template <int SG>
+__device__ __forceinline__ void mx_scale_dma(const uint32_t *ssrc, int step, char *lds, int b) {
+    const int w = threadIdx.x >> 6;
+    const void *src = reinterpret_cast<const void *>(ssrc + step);
+    lds_void_t *dst = (lds_void_t *)(mx_scale_buf<SG>(lds, b, w >> 2) + (w & 3) * (64 * 4 * SG));
+    if constexpr (SG == 4)
+        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
+
+// One 128-deep K step kt on stage `slot`: wait for the stage; on the first
+// step of an SG-step group that has a successor, fetch that group's scale
+// words (their buffer was last read in the previous group, which every wave
+// has left by this barrier); read this step's scale words from LDS; and with
+// FILL spread the next stage's DMA over sub-step 0.  The scale fetch comes
+// before the sub-steps so that its branch does not split them: the MFMA / DMA
+// interleave is pinned only within one basic block.
+template <int WM, int WN, int EVERY, int GH, int SG, bool FILL>
+__device__ __forceinline__ void mx_step(char *lds, int slot, int kt, int nk, int arow,
+                                        const int (&brow)[WaveGrid<WM, WN>::NI], int h, const uint32_t *ssrc,
+                                        AccW<WM, WN> &acc, const uint16_t *const (&asrc)[GH],
+                                        const uint16_t *const (&bsrc)[GH]) {
     using WG = WaveGrid<WM, WN>;
     constexpr int MI = WG::MI, NI = WG::NI;
     constexpr int stage_bytes = 2 * 256 * 128;
     wait_vm_barrier<0>();
+    const int grp = kt / SG, j = kt % SG;
+    if (FILL && j == 0 && kt + SG < nk) mx_scale_dma<SG>(ssrc, kt + SG, lds, (grp + 1) & 1);
     char *dst = lds + (slot ^ 1) * stage_bytes;
     const char *stage = lds + slot * stage_bytes;
+    const uint32_t *swa = reinterpret_cast<const uint32_t *>(mx_scale_buf<SG>(lds, grp & 1, 0));
+    const uint32_t *swb = reinterpret_cast<const uint32_t *>(mx_scale_buf<SG>(lds, grp & 1, 1));
     uint32_t ca[MI], cb[NI];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) ca[mi] = sa[mi] >> (8 * h);
+    for (int mi = 0; mi < MI; ++mi) ca[mi] = swa[(arow + mi * 32) * SG + j] >> (8 * h);
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) cb[ni] = sb[ni] >> (8 * h);
+    for (int ni = 0; ni < NI; ++ni) cb[ni] = swb[brow[ni] * SG + j] >> (8 * h);
     mx_substep<WM, WN, 0, EVERY, GH, FILL>(stage, arow, brow, h, ca, cb, acc, asrc, bsrc, (kt + 1) * 64, dst);
-    // after sub-step 0, so the pinned vector-memory slots there are the DMA's
-    if constexpr (FILL) {
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi) sa[mi] = sarow[mi][kt + 1];
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) sb[ni] = sbrow[ni][kt + 1];
-    }
     mx_substep<WM, WN, 1, EVERY, GH, FILL>(stage, arow, brow, h, ca, cb, acc, asrc, bsrc, (kt + 1) * 64, dst);
 }
 
 // MX main loop: 256 x 256 tile, K steps of 128 codes (one [256][128]-byte
 // operand tile each, the bf16 loop's DMA and swizzle), two 64-deep MFMA
 // sub-steps per step, double buffered.  ak/bk address the codes as 16-bit
-// units (ld = K / 2); as/bs the scale bytes.  The next stage's DMA is spread
-// over the first sub-step's MFMAs; the scale words of step kt+1 are loaded
-// during step kt.
-template <int WM, int WN>
+// units (ld = K / 2); as/bs the scale bytes.  Scale words reach LDS by a
+// gather DMA (lane = operand row, SG steps' words per lane) rather than by
+// per-lane loads: a 4-byte load per lane, row and step costs three times the
+// vector-memory requests of the operand tiles.  SG = 4 (16-byte lanes) needs
+// nk % 4 == 0 and 16-byte aligned scale rows, SG = 1 4-byte aligned ones.
+// Needs 8 waves (4 x 64 rows per operand); lds holds kMxLds bytes.
+template <int WM, int WN, int SG>
 __device__ __forceinline__ void gemm_mainloop_mx(const KOp &ak, const KOp &bk, const SOp &as, const SOp &bs, int nk,
                                                  bool swiglu, char *lds, AccW<WM, WN> &acc) {
     using WG = WaveGrid<WM, WN>;
     constexpr int MI = WG::MI, NI = WG::NI, NW = WG::NW;
+    static_assert(NW == 8, "one scale DMA per wave: waves 0-3 A rows, 4-7 B rows");
+    static_assert(SG == 1 || SG == 4, "scale DMA lanes of 4 or 16 bytes");
     constexpr int tile_bytes = 256 * 128;
-    constexpr int stage_bytes = 2 * tile_bytes;
     constexpr int GH = tile_bytes / 1024 / NW;
     constexpr int G = 2 * GH;
     static_assert((MI * NI) % G == 0, "DMA slots in one sub-step");
     constexpr int EVERY = MI * NI / G;
-    static_assert(2 * stage_bytes <= kGemmLds, "LDS budget");
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
     const int wm = wave / WN, wn = wave % WN, h = lane >> 5;
 #pragma unroll
@@ -246,17 +272,10 @@ __device__ __forceinline__ void gemm_mainloop_mx(const KOp &ak, const KOp &bk, c
         asrc[i] = mx_dma_src<NW>(ak, i);
         bsrc[i] = mx_dma_src<NW>(bk, i);
     }
-    const uint32_t *sarow[MI], *sbrow[NI];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) sarow[mi] = mx_scale_row(as, arow + mi * 32);
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) sbrow[ni] = mx_scale_row(bs, brow[ni]);
-    uint32_t sa[MI], sb[NI];  // this step's scale words, shifted to this lane's half
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) sa[mi] = sarow[mi][0];
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) sb[ni] = sbrow[ni][0];
+    const uint32_t *ssrc = reinterpret_cast<const uint32_t *>(
+        wave < 4 ? mx_scale_row(as, 64 * wave + lane) : mx_scale_row(bs, 64 * (wave - 4) + lane));
     __syncthreads();  // the previous tile's epilogue may still read LDS
+    mx_scale_dma<SG>(ssrc, 0, lds, 0);
 #pragma unroll
     for (int i = 0; i < GH; ++i) {
         dma_blk_w<64, NW>(asrc[i], 0, lds, i);
@@ -264,10 +283,10 @@ __device__ __forceinline__ void gemm_mainloop_mx(const KOp &ak, const KOp &bk, c
     }
     int slot = 0;
     for (int kt = 0; kt + 1 < nk; ++kt) {
-        mx_step<WM, WN, EVERY, GH, true>(lds, slot, kt, arow, brow, h, sa, sb, sarow, sbrow, acc, asrc, bsrc);
+        mx_step<WM, WN, EVERY, GH, SG, true>(lds, slot, kt, nk, arow, brow, h, ssrc, acc, asrc, bsrc);
         slot ^= 1;
     }
-    mx_step<WM, WN, EVERY, GH, false>(lds, slot, nk - 1, arow, brow, h, sa, sb, sarow, sbrow, acc, asrc, bsrc);
+    mx_step<WM, WN, EVERY, GH, SG, false>(lds, slot, nk - 1, nk, arow, brow, h, ssrc, acc, asrc, bsrc);
     __syncthreads();
 }
 
