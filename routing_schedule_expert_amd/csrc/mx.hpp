@@ -201,35 +201,55 @@ __device__ __forceinline__ void mx_scale_dma(const uint32_t *ssrc, int step, cha
         __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
 }
 
+// This lane's scale words of step kt (A rows arow + 32 mi, B rows brow[ni]),
+// shifted so that op_sel 0 / 2 pick its lane half's block of each sub-step.
+template <int WM, int WN, int SG>
+__device__ __forceinline__ void mx_read_scales(char *lds, int kt, int arow, const int (&brow)[WaveGrid<WM, WN>::NI],
+                                               int h, uint32_t (&ca)[WaveGrid<WM, WN>::MI],
+                                               uint32_t (&cb)[WaveGrid<WM, WN>::NI]) {
+    const int grp = kt / SG, j = kt % SG;
+    const uint32_t *swa = reinterpret_cast<const uint32_t *>(mx_scale_buf<SG>(lds, grp & 1, 0));
+    const uint32_t *swb = reinterpret_cast<const uint32_t *>(mx_scale_buf<SG>(lds, grp & 1, 1));
+#pragma unroll
+    for (int mi = 0; mi < WaveGrid<WM, WN>::MI; ++mi) ca[mi] = swa[(arow + mi * 32) * SG + j] >> (8 * h);
+#pragma unroll
+    for (int ni = 0; ni < WaveGrid<WM, WN>::NI; ++ni) cb[ni] = swb[brow[ni] * SG + j] >> (8 * h);
+}
+
 // One 128-deep K step kt on stage `slot`: wait for the stage; on the first
 // step of an SG-step group that has a successor, fetch that group's scale
 // words (their buffer was last read in the previous group, which every wave
-// has left by this barrier); read this step's scale words from LDS; and with
-// FILL spread the next stage's DMA over sub-step 0.  The scale fetch comes
-// before the sub-steps so that its branch does not split them: the MFMA / DMA
-// interleave is pinned only within one basic block.
+// has left by this barrier); with FILL spread the next stage's DMA over
+// sub-step 0.  The scale fetch comes before the sub-steps so that its branch
+// does not split them: the MFMA / DMA interleave is pinned only within one
+// basic block.  ca / cb hold this step's scale words on entry when SG > 1
+// (read one step ahead, between the sub-steps: step kt + 1's group is in LDS
+// since step kt's barrier) and the next step's on return; with SG = 1 the
+// next group is this step's DMA, so the words are read after the barrier.
 template <int WM, int WN, int EVERY, int GH, int SG, bool FILL>
 __device__ __forceinline__ void mx_step(char *lds, int slot, int kt, int nk, int arow,
                                         const int (&brow)[WaveGrid<WM, WN>::NI], int h, const uint32_t *ssrc,
+                                        uint32_t (&ca)[WaveGrid<WM, WN>::MI], uint32_t (&cb)[WaveGrid<WM, WN>::NI],
                                         AccW<WM, WN> &acc, const uint16_t *const (&asrc)[GH],
                                         const uint16_t *const (&bsrc)[GH]) {
     using WG = WaveGrid<WM, WN>;
     constexpr int MI = WG::MI, NI = WG::NI;
     constexpr int stage_bytes = 2 * 256 * 128;
     wait_vm_barrier<0>();
-    const int grp = kt / SG, j = kt % SG;
-    if (FILL && j == 0 && kt + SG < nk) mx_scale_dma<SG>(ssrc, kt + SG, lds, (grp + 1) & 1);
+    if (FILL && kt % SG == 0 && kt + SG < nk) mx_scale_dma<SG>(ssrc, kt + SG, lds, (kt / SG + 1) & 1);
     char *dst = lds + (slot ^ 1) * stage_bytes;
     const char *stage = lds + slot * stage_bytes;
-    const uint32_t *swa = reinterpret_cast<const uint32_t *>(mx_scale_buf<SG>(lds, grp & 1, 0));
-    const uint32_t *swb = reinterpret_cast<const uint32_t *>(mx_scale_buf<SG>(lds, grp & 1, 1));
-    uint32_t ca[MI], cb[NI];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) ca[mi] = swa[(arow + mi * 32) * SG + j] >> (8 * h);
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) cb[ni] = swb[brow[ni] * SG + j] >> (8 * h);
+    if constexpr (SG == 1) mx_read_scales<WM, WN, SG>(lds, kt, arow, brow, h, ca, cb);
     mx_substep<WM, WN, 0, EVERY, GH, FILL>(stage, arow, brow, h, ca, cb, acc, asrc, bsrc, (kt + 1) * 64, dst);
+    uint32_t na[MI], nb[NI];
+    if constexpr (SG > 1 && FILL) mx_read_scales<WM, WN, SG>(lds, kt + 1, arow, brow, h, na, nb);
     mx_substep<WM, WN, 1, EVERY, GH, FILL>(stage, arow, brow, h, ca, cb, acc, asrc, bsrc, (kt + 1) * 64, dst);
+    if constexpr (SG > 1 && FILL) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) ca[mi] = na[mi];
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) cb[ni] = nb[ni];
+    }
 }
 
 // MX main loop: 256 x 256 tile, K steps of 128 codes (one [256][128]-byte
@@ -281,12 +301,17 @@ __device__ __forceinline__ void gemm_mainloop_mx(const KOp &ak, const KOp &bk, c
         dma_blk_w<64, NW>(asrc[i], 0, lds, i);
         dma_blk_w<64, NW>(bsrc[i], 0, lds + tile_bytes, i);
     }
+    uint32_t ca[MI], cb[NI];
+    if constexpr (SG > 1) {  // step 0's words: wait for the first group
+        wait_vm_barrier<0>();
+        mx_read_scales<WM, WN, SG>(lds, 0, arow, brow, h, ca, cb);
+    }
     int slot = 0;
     for (int kt = 0; kt + 1 < nk; ++kt) {
-        mx_step<WM, WN, EVERY, GH, SG, true>(lds, slot, kt, nk, arow, brow, h, ssrc, acc, asrc, bsrc);
+        mx_step<WM, WN, EVERY, GH, SG, true>(lds, slot, kt, nk, arow, brow, h, ssrc, ca, cb, acc, asrc, bsrc);
         slot ^= 1;
     }
-    mx_step<WM, WN, EVERY, GH, SG, false>(lds, slot, nk - 1, nk, arow, brow, h, ssrc, acc, asrc, bsrc);
+    mx_step<WM, WN, EVERY, GH, SG, false>(lds, slot, nk - 1, nk, arow, brow, h, ssrc, ca, cb, acc, asrc, bsrc);
     __syncthreads();
 }
 
