@@ -25,6 +25,10 @@ Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
   mx_expert_ffn_rows, mx_layer_fwd_tokens        pinned (dot products vs numpy on the
                                                    dequantized operands; token path = rows +
                                                    combine; close to the bf16 FFN)
+  macrobatch_schedules, ring_walk                pinned (one macrobatch = the whole table;
+                                                   every local route in exactly one window;
+                                                   closed forms of the reversed ring's
+                                                   residency and replay count)
 """
 from __future__ import annotations
 
@@ -382,3 +386,35 @@ def mx_layer_fwd_tokens(routes, w, Xq, Xs, W13q, W13s, W2q, W2s, L: int, base: i
     _load().orc_mx_layer_fwd_tokens(K, L, base, H, I, _ptr(routes), _ptr(w), *[_ptr(a) for a in arrs],
                                     _ptr(tokens), tokens.shape[0], _ptr(out))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Macrobatch ring ("Beyond Peak TFLOPs" section 2.B; Mixture-of-Kittens notes,
+# section 4).  The ring changes where rows live and in which order
+# macrobatches run, not what the layer computes: its outputs are those of
+# layer_fwd_tokens / layer_bwd.
+# ---------------------------------------------------------------------------
+
+def macrobatch_schedules(routes: np.ndarray, L: int, mb_tokens: int, base: int = 0, pad: int = 256):
+    """One table per macrobatch: macrobatch m is tokens [m*mb_tokens,
+    (m+1)*mb_tokens) of every partition, scheduled on its own (its Phi holds
+    the token's index inside the window)."""
+    P, Np, K = routes.shape
+    assert Np % mb_tokens == 0
+    return [schedule(np.ascontiguousarray(routes[:, m * mb_tokens:(m + 1) * mb_tokens]), L, base, pad)
+            for m in range(Np // mb_tokens)]
+
+
+def ring_walk(M: int, S: int, reverse: bool = True):
+    """The forward's walk over M macrobatches through S ring slots, as a plain
+    simulation: walk step i takes macrobatch M-1-i (reverse) or i and slot
+    i % S, evicting the slot's previous occupant.  Returns the walk
+    [(m, slot)], the macrobatches still resident afterwards {m: slot}, and the
+    ones the backward (token order m = 0, 1, ...) must replay."""
+    walk = [((M - 1 - i) if reverse else i, i % S) for i in range(M)]
+    resident = {}
+    for m, slot in walk:
+        resident = {k: v for k, v in resident.items() if v != slot}
+        resident[m] = slot
+    replay = [m for m in range(M) if m not in resident]
+    return walk, resident, replay
