@@ -265,6 +265,73 @@ int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes
                   size_t ws_bytes, void *stream);
 
 /*
+ * Macrobatch ring ([BPT] section 2.B and [MoK] section 4: a fixed ring of
+ * token buffers through which macrobatches cycle with no host sync and no
+ * dropped token; combine of one macrobatch interleaved with the dispatch of
+ * the next; the forward walks the ring in reverse so the activations the
+ * backward needs first are the ones still resident).
+ *
+ * The Np tokens of every partition are cut into M = Np / mb_tokens
+ * macrobatches: macrobatch m is tokens [m*mb_tokens, (m+1)*mb_tokens) of each
+ * of the P partitions.  Each macrobatch has its own pull table, its expert
+ * segments padded to pad_rows, in a ring slot of
+ *   capm = moe_ring_capacity_rows(d, mb_tokens) = P*mb_tokens*K + L*(pad_rows-1)
+ * rows.  Both calls need mb_tokens to divide Np, ring_slots >= 1,
+ * d->num_batches == 1 and H <= 65536 (padding rows read a static zero row);
+ * otherwise MOE_EINVAL / MOE_EUNSUPPORTED.  -1 from the two size queries
+ * means such an invalid d or mb_tokens.
+ */
+int64_t moe_ring_capacity_rows(const moe_desc *d, int32_t mb_tokens);
+/* op = MOE_OP_LAYER_FWD or MOE_OP_LAYER_BWD (the two calls below). */
+int64_t moe_ring_workspace_bytes(const moe_desc *d, int32_t mb_tokens, int op);
+
+/*
+ * moe_layer_fwd_ring — the layer forward through the ring.
+ *   routes, w, X, W13, W2   as moe_layer_fwd
+ *   counts    out: int32 [M][L][P]      per-macrobatch counts
+ *   seg_off   out: int32 [M][L+1]       per-macrobatch segment offsets (rows of its slot)
+ *   phi       out: moe_src [M][capm]    per-macrobatch pull tables; tok is the
+ *                                       token's index inside the macrobatch
+ *   route_row out: int32 [P][Np][K]     row of each route inside its macrobatch's
+ *                                       slot, -1 for non-local slots
+ *   HU        out: bf16 [ring_slots][capm][2I]  the ring: saved pre-activations
+ *   A         out: bf16 [ring_slots][capm][I]   and activations
+ *   Y         scratch: bf16 [capm][H]   one macrobatch's expert outputs
+ *   out       out: bf16 [P][Np][H]      bitwise equal to moe_layer_fwd's
+ *   ws >= moe_ring_workspace_bytes(d, mb_tokens, MOE_OP_LAYER_FWD)
+ * All M tables come from one batched schedule launch.  The walk is
+ * m = M-1, ..., 0: macrobatch m uses slot (M-1-m) % ring_slots; each step is
+ * one launch holding the gate/up tiles of m (the dispatch fused into their
+ * operand loads) together with the combine of m+1, then the down GEMM of m;
+ * a last launch combines macrobatch 0.  On return slot (M-1-m) % ring_slots
+ * holds macrobatch m for every m < min(ring_slots, M).
+ */
+int moe_layer_fwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots, const int32_t *routes,
+                       const float *w, const uint16_t *X, const uint16_t *W13, const uint16_t *W2, int32_t *counts,
+                       int32_t *seg_off, moe_src *phi, int32_t *route_row, uint16_t *HU, uint16_t *A, uint16_t *Y,
+                       uint16_t *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_layer_bwd_ring — the backward of moe_layer_fwd_ring, with the same
+ * d, mb_tokens and ring_slots, and phi, route_row, seg_off, HU, A as that
+ * call left them (X, W13, W2 unchanged since).
+ *   dOut, w, X, W13, W2   as moe_layer_bwd (X replaces the saved Xd)
+ *   dX, dW13, dW2, dw     out, as moe_layer_bwd
+ *   ws >= moe_ring_workspace_bytes(d, mb_tokens, MOE_OP_LAYER_BWD)
+ * Macrobatches are taken in token order m = 0, 1, ...: those still in the
+ * ring (m < ring_slots) use their slot; the others are replayed (their
+ * gate/up GEMM recomputed from X into the workspace, bitwise the forward's
+ * values).  dX and dw are bitwise equal to moe_layer_bwd's; the weight
+ * gradients are summed per macrobatch and added in ascending m (a fixed
+ * order, so reproducible, but rounded differently from moe_layer_bwd's
+ * single pass).
+ */
+int moe_layer_bwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots, const uint16_t *dOut,
+                       const float *w, const uint16_t *X, const uint16_t *W13, const uint16_t *W2, const moe_src *phi,
+                       const int32_t *route_row, const int32_t *seg_off, const uint16_t *HU, const uint16_t *A,
+                       uint16_t *dX, float *dW13, float *dW2, float *dw, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Launch trace (optional, host side).  moe_trace_enable(n) records, for the
  * next n kernel launches made by this library on any stream, a start and stop
  * event on the launch's own stream; moe_trace_read copies the finished

@@ -361,8 +361,12 @@ __device__ __forceinline__ void epilogue_store_bf16_w(AccW<WM, WN> &acc, char *l
     }
 }
 
+// fp32 tile store of the rows < mvalid and columns < nvalid; with accumulate
+// each element is added to what dst holds (one fp32 add per call, so a
+// sequence of calls sums in call order).
 template <int WM, int WN>
-__device__ __forceinline__ void epilogue_store_f32_w(AccW<WM, WN> &acc, float *dst, int64_t ld, int mvalid, int nvalid) {
+__device__ __forceinline__ void epilogue_store_f32_w(AccW<WM, WN> &acc, float *dst, int64_t ld, int mvalid, int nvalid,
+                                                     bool accumulate = false) {
     using WG = WaveGrid<WM, WN>;
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63, wm = wave / WN, wn = wave % WN;
     float *base = dst + (int64_t)WG::row(wm, 0, 0, lane) * ld + wn * (WG::NI * 32) + (lane & 31);
@@ -374,7 +378,10 @@ __device__ __forceinline__ void epilogue_store_f32_w(AccW<WM, WN> &acc, float *d
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int dr = mi * 32 + 8 * (e >> 2) + (e & 3);
-                if (row0 + dr < mvalid && col0 + ni * 32 < nvalid) base[(int64_t)dr * ld + ni * 32] = acc[mi][ni][e];
+                if (row0 + dr < mvalid && col0 + ni * 32 < nvalid) {
+                    float *o = base + (int64_t)dr * ld + ni * 32;
+                    *o = accumulate ? *o + acc[mi][ni][e] : acc[mi][ni][e];
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }

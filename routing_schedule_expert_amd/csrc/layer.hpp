@@ -211,6 +211,51 @@ __device__ __forceinline__ void mx_down_phase(const MxFfnArgs &a, char *lds) {
 }
 
 // ---------------------------------------------------------------------------
+// Macrobatch ring ("Beyond Peak TFLOPs" section 2.B; the Mixture-of-Kittens
+// notes, section 4): the combine of one macrobatch runs in the same launch as
+// the gate/up GEMM of the next, so a slot's rows are consumed while the next
+// macrobatch's rows are produced.
+// ---------------------------------------------------------------------------
+
+// The combine of one token window (tpp tokens in each of the partitions,
+// tstride apart); Y == nullptr: nothing to combine.
+struct WindowCombine {
+    const uint16_t *Y;
+    const int32_t *route_row;  // at the window's first token of partition 0
+    const float *w;
+    uint16_t *out;
+    int K, H, tpp;
+    int64_t ntok, tstride;
+};
+
+constexpr int kCombineItem = 64;  // tokens per combine work item (8 per wave)
+
+// Work items: the gate/up tiles of `a` then the combine items of `c`.  Each
+// workgroup takes whole items, so the HBM-bound combine fills the CUs the
+// last round of MFMA tiles leaves idle.
+__device__ __forceinline__ void ring_gateup_combine_body(const FfnArgs &a, const WindowCombine &c, char *lds) {
+    const int npad = a.seg_off[a.L];
+    const int mtiles = npad / kBM, ntiles = a.I / 128;
+    const int64_t ngu = (int64_t)mtiles * ntiles;
+    const int64_t ncb = c.Y ? (c.ntok + kCombineItem - 1) / kCombineItem : 0;
+    const int64_t total = ngu + ncb;
+    const int waves = blockDim.x / kWave;
+    for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
+        const int64_t lid = logical_tile(it);
+        if (lid >= total) continue;
+        if (lid < ngu) {
+            int m, n;
+            grouped_mn(lid, mtiles, ntiles, 4, m, n);
+            ffn_gateup_tile(a, m, n, lds);
+        } else {
+            const int64_t g0 = (lid - ngu) * kCombineItem;
+            combine_body(c.Y, c.route_row, c.w, c.out, c.K, c.H, g0, min(g0 + kCombineItem, c.ntok),
+                         threadIdx.x / kWave, waves, c.tpp, c.tstride);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Persistent forward.
 // ---------------------------------------------------------------------------
 
@@ -268,6 +313,7 @@ struct BwdArgs {
     uint16_t *W2T, *W13T, *dYT, *AT, *dHUT, *XdT;
     int64_t ldT;
     int L, H, I, nparts;
+    int accumulate;  // B5 adds to dW13 / dW2 instead of overwriting them
 };
 
 // A K-contiguous window of up to 256 rows starting at `rows`; when only 128
@@ -361,7 +407,7 @@ __device__ __forceinline__ void wgrad_phase(const BwdArgs &a, char *lds) {
             const KOp bk = rows_window(a.AT + (int64_t)nt * 256 * ldT + S, ldT, I - nt * 256);
             gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, kext / 64, false, lds, acc);
             epilogue_store_f32_w<kFwdWM, kFwdWN>(acc, a.dW2 + (int64_t)l * H * I + (int64_t)mt * 256 * I + nt * 256, I,
-                                                 256, I - nt * 256);
+                                                 256, I - nt * 256, a.accumulate);
         } else {
             int mt, nt;
             grouped_mn(in - mt2 * nt2, mt13, nt13, 4, mt, nt);
@@ -369,7 +415,7 @@ __device__ __forceinline__ void wgrad_phase(const BwdArgs &a, char *lds) {
             const KOp bk = rows_window(a.XdT + (int64_t)nt * 256 * ldT + S, ldT, 256);
             gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, kext / 64, false, lds, acc);
             epilogue_store_f32_w<kFwdWM, kFwdWN>(acc, a.dW13 + (int64_t)l * 2 * I * H + (int64_t)mt * 256 * H + nt * 256,
-                                                 H, 256, 256);
+                                                 H, 256, 256, a.accumulate);
         }
     }
 }

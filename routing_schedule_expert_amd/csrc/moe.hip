@@ -49,9 +49,11 @@ __global__ __launch_bounds__(256) void k_gather(const uint16_t *src, const moe_s
 }
 
 __global__ __launch_bounds__(256) void k_combine(const uint16_t *Y, const int32_t *route_row, const float *w,
-                                                 uint16_t *out, int K, int H, int64_t ntok) {
+                                                 uint16_t *out, int K, int H, int64_t ntok, int tpp,
+                                                 int64_t tstride) {
     const int waves = blockDim.x / kWave;
-    combine_body(Y, route_row, w, out, K, H, 0, ntok, blockIdx.x * waves + threadIdx.x / kWave, gridDim.x * waves);
+    combine_body(Y, route_row, w, out, K, H, 0, ntok, blockIdx.x * waves + threadIdx.x / kWave, gridDim.x * waves,
+                 tpp, tstride);
 }
 
 __global__ __launch_bounds__(256) void k_row_weight(const moe_src *phi, const int32_t *npad_ptr,
@@ -62,10 +64,15 @@ __global__ __launch_bounds__(256) void k_row_weight(const moe_src *phi, const in
 }
 
 __global__ __launch_bounds__(256) void k_dw_finalize(const int32_t *route_row, const float *part, int nparts,
-                                                     float *dw, int64_t nslots) {
+                                                     float *dw, int64_t nslots, int spp, int64_t sstride) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nslots;
          i += (int64_t)gridDim.x * blockDim.x)
-        dw_finalize_body(route_row, part, nparts, dw, i);
+        dw_finalize_body(route_row, part, nparts, dw, i, spp, sstride);
+}
+
+__global__ __launch_bounds__(kFwdThreads) void k_ring_gateup_combine(FfnArgs a, WindowCombine c) {
+    __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+    ring_gateup_combine_body(a, c, lds);
 }
 
 __global__ __launch_bounds__(kFwdThreads) void k_ffn_gateup(FfnArgs a) {
@@ -280,6 +287,8 @@ void fill_sched_args(SchedArgs &a, const moe_desc *d, const int32_t *routes, int
     a.wg_per_part = (a.W + wpw - 1) / wpw;
     a.nbits = 32 - __builtin_clz((unsigned)d->L | 1u);
     a.cap = cap_rows(d);
+    a.pstride = a.R;
+    a.bstride = (int64_t)a.P * a.R;
 }
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS of one gfx950 workgroup
@@ -292,10 +301,14 @@ size_t sched_lds_bytes(const moe_desc *d, int wpw) {
     return 4 * std::max(count, std::max(fin, scat));
 }
 
+// pstride / bstride > 0: the tables are token windows of one routing tensor
+// (SchedArgs); 0 keeps whole tensors.
 int launch_schedule(const moe_desc *d, const int32_t *routes, int32_t *counts, int32_t *seg_off, moe_src *phi,
-                    int32_t *route_row, char *ws, hipStream_t s) {
+                    int32_t *route_row, char *ws, hipStream_t s, int64_t pstride = 0, int64_t bstride = 0) {
     SchedArgs a;
     fill_sched_args(a, d, routes, counts, seg_off, phi, route_row, ws, kSchedWaves);
+    if (pstride > 0) a.pstride = pstride;
+    if (bstride > 0) a.bstride = bstride;
     const int wg_per_batch = a.P * a.wg_per_part;
     const int grid = a.nb >= 8 ? 8 * ((a.nb + 7) / 8) * wg_per_batch : a.nb * wg_per_batch;
     const size_t lds = sched_lds_bytes(d, kSchedWaves);
@@ -317,21 +330,28 @@ int launch_schedule(const moe_desc *d, const int32_t *routes, int32_t *counts, i
     return launch_status();
 }
 
+// np_stride > 0: source rows part * np_stride + tok (a token window of a
+// larger [P][np_stride] array, src pointing at the window's first token).
 int launch_gather(const moe_desc *d, const uint16_t *src, const moe_src *phi, const int32_t *seg_off, uint16_t *dst,
-                  hipStream_t s, const char *name) {
+                  hipStream_t s, const char *name, int np_stride = 0) {
     const int64_t cap = cap_rows(d);
     const int grid = (int)std::min<int64_t>((cap + 3) / 4, 16ll * device_cus());
     TraceScope tr(name, s);
-    hipLaunchKernelGGL(k_gather, dim3(grid), dim3(256), 0, s, src, phi, seg_off + d->L, dst, d->Np, d->H, cap);
+    hipLaunchKernelGGL(k_gather, dim3(grid), dim3(256), 0, s, src, phi, seg_off + d->L, dst,
+                       np_stride > 0 ? np_stride : d->Np, d->H, cap);
     return launch_status();
 }
 
+// tstride > d->Np: the d->Np tokens of each partition are a window of a
+// [P][tstride] token array (route_row, w, out pointing at its first token).
 int launch_combine(const moe_desc *d, const uint16_t *Y, const int32_t *route_row, const float *w, uint16_t *out,
-                   hipStream_t s, const char *name) {
+                   hipStream_t s, const char *name, int64_t tstride = 0) {
     const int64_t ntok = (int64_t)d->P * d->Np;
     const int grid = (int)std::min<int64_t>((ntok + 3) / 4, 16ll * device_cus());
+    const int tpp = tstride > d->Np ? d->Np : 0;
     TraceScope tr(name, s);
-    hipLaunchKernelGGL(k_combine, dim3(grid), dim3(256), 0, s, Y, route_row, w, out, d->K, d->H, ntok);
+    hipLaunchKernelGGL(k_combine, dim3(grid), dim3(256), 0, s, Y, route_row, w, out, d->K, d->H, ntok, tpp,
+                       tpp ? tstride : (int64_t)0);
     return launch_status();
 }
 
@@ -548,23 +568,18 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
     return launch_combine(d, Y, route_row, w, out, s, "combine");
 }
 
-int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes, const float *w, const moe_src *phi,
-                  const int32_t *route_row, const int32_t *seg_off, const uint16_t *Xd, const uint16_t *HU,
-                  const uint16_t *A, const uint16_t *W13, const uint16_t *W2, uint16_t *dX, float *dW13, float *dW2,
-                  float *dw, void *ws, size_t ws_bytes, void *stream) {
-    int rc = check_desc(d, true);
-    if (rc != MOE_OK) return rc;
-    if (!dOut || !routes || !w || !phi || !route_row || !seg_off || !Xd || !HU || !A || !W13 || !W2 || !dX || !dW13 ||
-        !dW2 || !dw || !ws)
-        return MOE_EINVAL;
-    const void *ptrs[] = {dOut, phi, Xd, HU, A, W13, W2, dX, dW13, dW2, ws};
-    for (const void *p : ptrs)
-        if (!aligned16(p)) return MOE_EINVAL;
-    if ((int64_t)ws_bytes < bwd_ws_bytes(d)) return MOE_ENOSPC;
-    (void)routes;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+// The backward of one table's rows.  d describes the tokens the table covers
+// (a window of tstride tokens per partition when tstride > d->Np: dOut, w,
+// route_row, dX and dw then point at the window's first token).  With
+// weights_ready the transposed weights are already in the workspace; with
+// accumulate the weight gradients are added to dW13 / dW2.
+int bwd_core(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const float *w, const moe_src *phi,
+             const int32_t *route_row, const int32_t *seg_off, const uint16_t *Xd, const uint16_t *HU,
+             const uint16_t *A, const uint16_t *W13, const uint16_t *W2, uint16_t *dX, float *dW13, float *dW2,
+             float *dw, char *ws, bool weights_ready, bool accumulate, hipStream_t s) {
     const int64_t cap = cap_rows(d), H = d->H, I = d->I, L = d->L, ldT = bwd_ldT(d);
-    char *p = static_cast<char *>(ws);
+    const bool window = tstride > d->Np;
+    char *p = ws;
     BwdArgs a;
     a.dOd = reinterpret_cast<uint16_t *>(p);
     p += align256(cap * H * 2);
@@ -600,23 +615,27 @@ int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes
     a.H = d->H;
     a.I = d->I;
     a.nparts = bwd_nparts(d);
+    a.accumulate = accumulate ? 1 : 0;
     const int32_t *npad = seg_off + d->L;
+    const int np_stride = window ? (int)tstride : d->Np;
     // B1: reverse-combine gather of the output gradient
-    rc = launch_gather(d, dOut, phi, seg_off, a.dOd, s, "bwd_gather");
+    int rc = launch_gather(d, dOut, phi, seg_off, a.dOd, s, "bwd_gather", np_stride);
     if (rc != MOE_OK) return rc;
     {
         TraceScope tr("bwd_row_weight", s);
         hipLaunchKernelGGL(k_row_weight, dim3((int)std::min<int64_t>((cap + 255) / 256, 4096)), dim3(256), 0, s, phi,
-                           npad, route_row, w, a.wrow, d->Np, d->K, cap);
+                           npad, route_row, w, a.wrow, np_stride, d->K, cap);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
-    // weights transposed so both operands of every data-gradient GEMM are K-contiguous
-    rc = launch_transpose(make_transpose(W2, a.W2T, (int32_t)H, (int32_t)I, (int32_t)L, I, H, H * I, I * H, nullptr,
-                                         nullptr), s, "bwd_transpose_w2");
-    if (rc != MOE_OK) return rc;
-    rc = launch_transpose(make_transpose(W13, a.W13T, (int32_t)(2 * I), (int32_t)H, (int32_t)L, H, 2 * I, 2 * I * H,
-                                         H * 2 * I, nullptr, nullptr), s, "bwd_transpose_w13");
-    if (rc != MOE_OK) return rc;
+    if (!weights_ready) {
+        // weights transposed so both operands of every data-gradient GEMM are K-contiguous
+        rc = launch_transpose(make_transpose(W2, a.W2T, (int32_t)H, (int32_t)I, (int32_t)L, I, H, H * I, I * H,
+                                             nullptr, nullptr), s, "bwd_transpose_w2");
+        if (rc != MOE_OK) return rc;
+        rc = launch_transpose(make_transpose(W13, a.W13T, (int32_t)(2 * I), (int32_t)H, (int32_t)L, H, 2 * I,
+                                             2 * I * H, H * 2 * I, nullptr, nullptr), s, "bwd_transpose_w13");
+        if (rc != MOE_OK) return rc;
+    }
     const int grid = gemm_grid();
     // B2: down-projection dgrad with the SwiGLU backward and dw partials
     {
@@ -628,7 +647,8 @@ int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes
     {
         TraceScope tr("bwd_dw", s);
         hipLaunchKernelGGL(k_dw_finalize, dim3((int)std::min<int64_t>((nslots + 255) / 256, 4096)), dim3(256), 0, s,
-                           route_row, a.part, a.nparts, dw, nslots);
+                           route_row, a.part, a.nparts, dw, nslots, window ? d->Np * d->K : 0,
+                           window ? tstride * d->K : (int64_t)0);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
     // B3: gate/up dgrad
@@ -638,7 +658,7 @@ int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
     // B4: reverse-dispatch sum over each token's local slots
-    rc = launch_combine(d, a.dXd, route_row, nullptr, dX, s, "bwd_reverse_dispatch");
+    rc = launch_combine(d, a.dXd, route_row, nullptr, dX, s, "bwd_reverse_dispatch", window ? tstride : 0);
     if (rc != MOE_OK) return rc;
     // activations transposed (rows [0, Npad)) so the weight gradients reduce
     // over K-contiguous rows; the router weight is folded into dO_d here
@@ -658,6 +678,24 @@ int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes
     TraceScope tr("bwd_wgrad", s);
     hipLaunchKernelGGL(k_wgrad, dim3(grid), dim3(kFwdThreads), 0, s, a);
     return launch_status();
+}
+
+int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes, const float *w, const moe_src *phi,
+                  const int32_t *route_row, const int32_t *seg_off, const uint16_t *Xd, const uint16_t *HU,
+                  const uint16_t *A, const uint16_t *W13, const uint16_t *W2, uint16_t *dX, float *dW13, float *dW2,
+                  float *dw, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_desc(d, true);
+    if (rc != MOE_OK) return rc;
+    if (!dOut || !routes || !w || !phi || !route_row || !seg_off || !Xd || !HU || !A || !W13 || !W2 || !dX || !dW13 ||
+        !dW2 || !dw || !ws)
+        return MOE_EINVAL;
+    const void *ptrs[] = {dOut, phi, Xd, HU, A, W13, W2, dX, dW13, dW2, ws};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return MOE_EINVAL;
+    if ((int64_t)ws_bytes < bwd_ws_bytes(d)) return MOE_ENOSPC;
+    (void)routes;
+    return bwd_core(d, 0, dOut, w, phi, route_row, seg_off, Xd, HU, A, W13, W2, dX, dW13, dW2, dw,
+                    static_cast<char *>(ws), false, false, static_cast<hipStream_t>(stream));
 }
 
 int moe_quantize_mx(const uint16_t *src, int64_t rows, int32_t K, uint8_t *q, uint8_t *scales, void *stream) {
@@ -726,6 +764,166 @@ int moe_layer_fwd_mx(const moe_desc *d, const int32_t *routes, const float *w, c
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
     return launch_combine(d, Y, route_row, w, out, s, "combine");
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Macrobatch ring.
+// ---------------------------------------------------------------------------
+
+// Checks shared by the ring calls; dm describes one macrobatch (Np =
+// mb_tokens) with num_batches = M macrobatches.
+int ring_check(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots, moe_desc &dm, int &M) {
+    int rc = check_desc(d, true);
+    if (rc != MOE_OK) return rc;
+    if (d->num_batches != 1 || mb_tokens < 1 || d->Np % mb_tokens || ring_slots < 1) return MOE_EINVAL;
+    if (d->H > kZeroRowElems) return MOE_EUNSUPPORTED;  // padding rows read the static zero row
+    dm = *d;
+    dm.Np = mb_tokens;
+    M = d->Np / mb_tokens;
+    dm.num_batches = M;
+    return check_desc(&dm, true);
+}
+
+int64_t ring_bwd_extra_bytes(const moe_desc *d1) {
+    const int64_t cap = cap_rows(d1);
+    return align256(cap * 2 * d1->I * 2) + align256(cap * d1->I * 2) + align256(cap * d1->H * 2);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_ring_capacity_rows(const moe_desc *d, int32_t mb_tokens) {
+    moe_desc dm;
+    int M;
+    if (ring_check(d, mb_tokens, 1, dm, M) != MOE_OK) return -1;
+    dm.num_batches = 1;
+    return cap_rows(&dm);
+}
+
+int64_t moe_ring_workspace_bytes(const moe_desc *d, int32_t mb_tokens, int op) {
+    moe_desc dm;
+    int M;
+    if (ring_check(d, mb_tokens, 1, dm, M) != MOE_OK) return -1;
+    moe_desc d1 = dm;
+    d1.num_batches = 1;
+    if (op == MOE_OP_LAYER_FWD) return kBarrierBytes + sched_ws_bytes(&dm);
+    if (op == MOE_OP_LAYER_BWD) return bwd_ws_bytes(&d1) + ring_bwd_extra_bytes(&d1);
+    return -1;
+}
+
+int moe_layer_fwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots, const int32_t *routes,
+                       const float *w, const uint16_t *X, const uint16_t *W13, const uint16_t *W2, int32_t *counts,
+                       int32_t *seg_off, moe_src *phi, int32_t *route_row, uint16_t *HU, uint16_t *A, uint16_t *Y,
+                       uint16_t *out, void *ws, size_t ws_bytes, void *stream) {
+    moe_desc dm;
+    int M;
+    int rc = ring_check(d, mb_tokens, ring_slots, dm, M);
+    if (rc != MOE_OK) return rc;
+    const void *ptrs[] = {routes, w, X, W13, W2, counts, seg_off, phi, route_row, HU, A, Y, out, ws};
+    for (const void *p : ptrs)
+        if (!p || !aligned16(p)) return MOE_EINVAL;
+    if ((int64_t)ws_bytes < moe_ring_workspace_bytes(d, mb_tokens, MOE_OP_LAYER_FWD)) return MOE_ENOSPC;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *wsb = static_cast<char *>(ws);
+    uint32_t *bar = reinterpret_cast<uint32_t *>(wsb);
+    const int64_t B = mb_tokens, K = d->K, H = d->H, I = d->I, L = d->L, Np = d->Np;
+    // every macrobatch's table in one batched schedule: table m is token window m
+    rc = launch_schedule(&dm, routes, counts, seg_off, phi, route_row, wsb + kBarrierBytes, s, Np * K, B * K);
+    if (rc != MOE_OK) return rc;
+    moe_desc d1 = dm;
+    d1.num_batches = 1;
+    const int64_t capm = cap_rows(&d1);
+    const int grid = gemm_grid();
+    // reversed ring: the last macrobatch first, so the first ones stay resident
+    for (int i = 0; i < M; ++i) {
+        const int m = M - 1 - i, slot = i % ring_slots;
+        FfnArgs fa = make_ffn_args(&d1, nullptr, W13, W2, seg_off + (int64_t)m * (L + 1),
+                                   HU + (int64_t)slot * capm * 2 * I, A + (int64_t)slot * capm * I, Y, 0, bar,
+                                   X + (int64_t)m * B * H, phi + (int64_t)m * capm);
+        fa.Np = d->Np;  // partition stride of X
+        WindowCombine wc{};  // Y == nullptr: no combine in the first launch
+        if (i > 0) {  // the combine of the macrobatch walked before this one
+            const int64_t t0 = (int64_t)(m + 1) * B;
+            wc.Y = Y;
+            wc.route_row = route_row + t0 * K;
+            wc.w = w + t0 * K;
+            wc.out = out + t0 * H;
+        }
+        wc.K = d->K;
+        wc.H = d->H;
+        wc.tpp = (int)B;
+        wc.ntok = (int64_t)d->P * B;
+        wc.tstride = Np;
+        {
+            TraceScope tr("ring_gateup_combine", s);
+            hipLaunchKernelGGL(k_ring_gateup_combine, dim3(grid), dim3(kFwdThreads), 0, s, fa, wc);
+        }
+        if (launch_status() != MOE_OK) return MOE_EHIP;
+        {
+            TraceScope tr("ring_down", s);
+            hipLaunchKernelGGL(k_ffn_down, dim3(grid), dim3(kFwdThreads), 0, s, fa);
+        }
+        if (launch_status() != MOE_OK) return MOE_EHIP;
+    }
+    return launch_combine(&d1, Y, route_row, w, out, s, "ring_combine", Np);  // macrobatch 0
+}
+
+int moe_layer_bwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots, const uint16_t *dOut,
+                       const float *w, const uint16_t *X, const uint16_t *W13, const uint16_t *W2, const moe_src *phi,
+                       const int32_t *route_row, const int32_t *seg_off, const uint16_t *HU, const uint16_t *A,
+                       uint16_t *dX, float *dW13, float *dW2, float *dw, void *ws, size_t ws_bytes, void *stream) {
+    moe_desc dm;
+    int M;
+    int rc = ring_check(d, mb_tokens, ring_slots, dm, M);
+    if (rc != MOE_OK) return rc;
+    const void *ptrs[] = {dOut, w, X, W13, W2, phi, route_row, seg_off, HU, A, dX, dW13, dW2, dw, ws};
+    for (const void *p : ptrs)
+        if (!p || !aligned16(p)) return MOE_EINVAL;
+    if ((int64_t)ws_bytes < moe_ring_workspace_bytes(d, mb_tokens, MOE_OP_LAYER_BWD)) return MOE_ENOSPC;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    moe_desc d1 = dm;
+    d1.num_batches = 1;
+    const int64_t capm = cap_rows(&d1), B = mb_tokens, K = d->K, H = d->H, I = d->I, L = d->L, Np = d->Np;
+    char *core_ws = static_cast<char *>(ws);
+    char *p = core_ws + bwd_ws_bytes(&d1);
+    uint16_t *HUr = reinterpret_cast<uint16_t *>(p);
+    p += align256(capm * 2 * I * 2);
+    uint16_t *Ar = reinterpret_cast<uint16_t *>(p);
+    p += align256(capm * I * 2);
+    uint16_t *Xd = reinterpret_cast<uint16_t *>(p);
+    for (int m = 0; m < M; ++m) {
+        const int64_t t0 = (int64_t)m * B;
+        const int32_t *so = seg_off + (int64_t)m * (L + 1);
+        const moe_src *ph = phi + (int64_t)m * capm;
+        const uint16_t *hu, *aa;
+        if (m < ring_slots) {  // still in the ring: walked among the forward's last ring_slots
+            const int64_t slot = (M - 1 - m) % ring_slots;
+            hu = HU + slot * capm * 2 * I;
+            aa = A + slot * capm * I;
+        } else {  // replay: the forward's gate/up of this macrobatch, from X through its table
+            FfnArgs fa = make_ffn_args(&d1, nullptr, W13, W2, so, HUr, Ar, nullptr, 0, nullptr, X + t0 * H, ph);
+            fa.Np = d->Np;
+            {
+                TraceScope tr("ring_replay_gateup", s);
+                hipLaunchKernelGGL(k_ffn_gateup, dim3(gemm_grid()), dim3(kFwdThreads), 0, s, fa);
+            }
+            if (launch_status() != MOE_OK) return MOE_EHIP;
+            hu = HUr;
+            aa = Ar;
+        }
+        // the dispatched rows of X, for the gate/up weight gradient
+        rc = launch_gather(&d1, X + t0 * H, ph, so, Xd, s, "ring_bwd_gather_x", (int)Np);
+        if (rc != MOE_OK) return rc;
+        rc = bwd_core(&d1, Np, dOut + t0 * H, w + t0 * K, ph, route_row + t0 * K, so, Xd, hu, aa, W13, W2,
+                      dX + t0 * H, dW13, dW2, dw + t0 * K, core_ws, m > 0, m > 0, s);
+        if (rc != MOE_OK) return rc;
+    }
+    return MOE_OK;
 }
 
 int moe_trace_enable(int max_records) {

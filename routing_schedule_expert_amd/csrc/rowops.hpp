@@ -48,15 +48,26 @@ __device__ void gather_rows_body(const uint16_t *__restrict__ src, const moe_src
     }
 }
 
+// Token g' of a window of tpp tokens in each partition, partitions tstride
+// tokens apart, as an index into the whole [P][tstride] token array
+// (tpp == 0: the identity).
+__device__ __forceinline__ int64_t window_token(int64_t g, int tpp, int64_t tstride) {
+    return tpp ? (g / tpp) * tstride + g % tpp : g;
+}
+
 // out[g] = sum_{j asc, rows[g][j] >= 0} w[g][j] * Y[rows[g][j]] for tokens g in
-// [g_begin, g_end); one wave per token, kRowUnroll 16-byte chunks per lane in
-// flight.  w == nullptr means every weight is 1.
+// [g_begin, g_end) (through window_token when tpp > 0: route_row, w and out
+// then point at the window's first token of partition 0); one wave per token,
+// kRowUnroll 16-byte chunks per lane in flight.  w == nullptr means every
+// weight is 1.
 __device__ void combine_body(const uint16_t *__restrict__ Y, const int32_t *__restrict__ route_row,
                              const float *__restrict__ w, uint16_t *__restrict__ out, int K, int H,
-                             int64_t g_begin, int64_t g_end, int wave_global, int nwaves) {
+                             int64_t g_begin, int64_t g_end, int wave_global, int nwaves, int tpp = 0,
+                             int64_t tstride = 0) {
     const int lane = lane_id();
     const int chunks = H / 8;
-    for (int64_t g = g_begin + wave_global; g < g_end; g += nwaves) {
+    for (int64_t gw = g_begin + wave_global; gw < g_end; gw += nwaves) {
+        const int64_t g = window_token(gw, tpp, tstride);
         u32x4 *o = reinterpret_cast<u32x4 *>(out + g * (int64_t)H);
         for (int c0 = 0; c0 < chunks; c0 += kRowUnroll * kWave) {
             float acc[kRowUnroll][8];
@@ -109,9 +120,13 @@ __device__ void row_weight_body(const moe_src *__restrict__ phi, const int32_t *
     wrow[i] = v;
 }
 
-// dw[slot] = sum_q part[row][q] in ascending q (0 for non-local slots).
+// dw[slot] = sum_q part[row][q] in ascending q (0 for non-local slots); slot
+// is mapped like a token by window_token, in units of slots (tpp K per
+// partition, tstride K apart).
 __device__ void dw_finalize_body(const int32_t *__restrict__ route_row, const float *__restrict__ part,
-                                 int nparts, float *__restrict__ dw, int64_t slot) {
+                                 int nparts, float *__restrict__ dw, int64_t slot_w, int spp = 0,
+                                 int64_t sstride = 0) {
+    const int64_t slot = window_token(slot_w, spp, sstride);
     int32_t row = route_row[slot];
     float s = 0.f;
     if (row >= 0) {

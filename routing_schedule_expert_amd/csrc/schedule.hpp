@@ -31,16 +31,20 @@ constexpr int kSchedWaves = 4;                      // waves per workgroup of th
 constexpr int kSchedPMax = 8;                       // partitions handled by the unrolled position formula
 
 struct SchedArgs {
-    const int32_t *routes;  // [nb][P][R]
+    const int32_t *routes;  // table b, partition r: R routes at b * bstride + r * pstride
     int32_t *counts;        // [nb][L][P]
     int32_t *seg_off;       // [nb][L+1]
     moe_src *phi;           // [nb][cap]
-    int32_t *route_row;     // [nb][P][R]
+    int32_t *route_row;     // same layout as routes
     int32_t *wcnt;          // ws: [nb][P][W][L] counts, then exclusive offsets
     int32_t P, R, K, L, base, pad, nb, W, wg_per_part, nbits;
     int32_t wpw;  // waves per workgroup (chunks handled by one workgroup)
     int32_t cb;   // 1024-route blocks per chunk (a chunk is one logical thread)
     int64_t cap;
+    // Element strides between tables and between partitions of a table: P * R
+    // and R for nb whole routing tensors; B * K and Np * K when the tables are
+    // the token windows [m B, (m + 1) B) of one [P][Np][K] tensor (macrobatches).
+    int64_t bstride, pstride;
 };
 
 __device__ __forceinline__ int bit_length(uint32_t v) { return 32 - __builtin_clz(v | 1u); }
@@ -183,7 +187,7 @@ __device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
     for (int l = lane; l <= L; l += kWave) cnt[l] = 0;
     __syncthreads();
     if (w < a.W) {
-        const int32_t *src = a.routes + ((int64_t)b * a.P + r) * a.R;
+        const int32_t *src = a.routes + (int64_t)b * a.bstride + (int64_t)r * a.pstride;
         for (int blk = 0; blk < a.cb; ++blk) {
             const int64_t lo = ((int64_t)w * a.cb + blk) * kSchedBlock;
             if (lo >= a.R) break;
@@ -251,8 +255,8 @@ __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
     __syncthreads();
     moe_src *phi = a.phi + (int64_t)b * a.cap;
     if (w < a.W) {
-        const int32_t *src = a.routes + ((int64_t)b * P + r) * a.R;
-        int32_t *rrow = a.route_row + ((int64_t)b * P + r) * a.R;
+        const int32_t *src = a.routes + (int64_t)b * a.bstride + (int64_t)r * a.pstride;
+        int32_t *rrow = a.route_row + (int64_t)b * a.bstride + (int64_t)r * a.pstride;
         for (int blk = 0; blk < a.cb; ++blk) {
             const int32_t lo = (w * a.cb + blk) * kSchedBlock;
             if (lo >= a.R) break;

@@ -27,6 +27,7 @@ EXPORTED = (
     "moe_expert_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_bwd", "moe_trace_enable", "moe_trace_read",
     "moe_quantize_mx",
     "moe_layer_fwd_mx",
+    "moe_ring_capacity_rows", "moe_ring_workspace_bytes", "moe_layer_fwd_ring", "moe_layer_bwd_ring",
 )
 
 
@@ -73,6 +74,10 @@ def load() -> ctypes.CDLL:
         "moe_quantize_mx": (ctypes.c_int, [P, i64, i32, P, P, P]),
         "moe_layer_fwd_mx": (ctypes.c_int, [D] + [P] * 18 + [sz, P]),
         "moe_layer_bwd": (ctypes.c_int, [D] + [P] * 16 + [sz, P]),
+        "moe_ring_capacity_rows": (i64, [D, i32]),
+        "moe_ring_workspace_bytes": (i64, [D, i32, ctypes.c_int]),
+        "moe_layer_fwd_ring": (ctypes.c_int, [D, i32, i32] + [P] * 14 + [sz, P]),
+        "moe_layer_bwd_ring": (ctypes.c_int, [D, i32, i32] + [P] * 15 + [sz, P]),
         "moe_trace_enable": (ctypes.c_int, [ctypes.c_int]),
         "moe_trace_read": (ctypes.c_int, [P, P, ctypes.c_int]),
     }
@@ -286,3 +291,78 @@ def alloc_fwd_mx(d: moe_desc, device) -> MxFwdBuffers:
 def layer_fwd_mx(d, routes, w, X, W13q, W13s, W2q, W2s, bufs: MxFwdBuffers, stream=None):
     return moe_layer_fwd_mx(d, routes, w, X, W13q, W13s, W2q, W2s, bufs.counts, bufs.seg_off, bufs.phi,
                             bufs.route_row, bufs.Xq, bufs.Xs, bufs.Aq, bufs.As, bufs.Y, bufs.out, bufs.ws, stream)
+
+
+# ---------------------------------------------------------------------------
+# Macrobatch ring.
+# ---------------------------------------------------------------------------
+
+def ring_capacity_rows(d: moe_desc, mb_tokens: int) -> int:
+    n = load().moe_ring_capacity_rows(ctypes.byref(d), mb_tokens)
+    if n < 0:
+        raise MoeError(MOE_EINVAL, "moe_ring_capacity_rows")
+    return int(n)
+
+
+def ring_workspace_bytes(d: moe_desc, mb_tokens: int, op: int) -> int:
+    n = load().moe_ring_workspace_bytes(ctypes.byref(d), mb_tokens, op)
+    if n < 0:
+        raise MoeError(MOE_EINVAL, "moe_ring_workspace_bytes")
+    return int(n)
+
+
+def moe_layer_fwd_ring(d, mb_tokens, ring_slots, routes, w, X, W13, W2, counts, seg_off, phi, route_row, HU, A, Y,
+                       out, ws, stream=None):
+    rc = load().moe_layer_fwd_ring(ctypes.byref(d), mb_tokens, ring_slots, _dev(routes), _dev(w), _dev(X), _dev(W13),
+                                   _dev(W2), _dev(counts), _dev(seg_off), _dev(phi), _dev(route_row), _dev(HU),
+                                   _dev(A), _dev(Y), _dev(out), _dev(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream, X))
+    return _check(rc, "moe_layer_fwd_ring")
+
+
+def moe_layer_bwd_ring(d, mb_tokens, ring_slots, dOut, w, X, W13, W2, phi, route_row, seg_off, HU, A, dX, dW13, dW2,
+                       dw, ws, stream=None):
+    rc = load().moe_layer_bwd_ring(ctypes.byref(d), mb_tokens, ring_slots, _dev(dOut), _dev(w), _dev(X), _dev(W13),
+                                   _dev(W2), _dev(phi), _dev(route_row), _dev(seg_off), _dev(HU), _dev(A), _dev(dX),
+                                   _dev(dW13), _dev(dW2), _dev(dw), _dev(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream, dOut))
+    return _check(rc, "moe_layer_bwd_ring")
+
+
+@dataclass
+class RingBuffers:
+    mb_tokens: int
+    slots: int
+    counts: torch.Tensor     # [M][L][P]
+    seg_off: torch.Tensor    # [M][L+1]
+    phi: torch.Tensor        # [M][capm][2]
+    route_row: torch.Tensor  # [P][Np][K]
+    HU: torch.Tensor         # [slots][capm][2I]
+    A: torch.Tensor          # [slots][capm][I]
+    Y: torch.Tensor          # [capm][H]
+    out: torch.Tensor
+    ws: torch.Tensor
+
+
+def alloc_ring(d: moe_desc, mb_tokens: int, slots: int, device) -> RingBuffers:
+    capm = ring_capacity_rows(d, mb_tokens)
+    M = d.Np // mb_tokens
+    i32, bf = torch.int32, torch.bfloat16
+    return RingBuffers(
+        mb_tokens=mb_tokens, slots=slots,
+        counts=torch.empty((M, d.L, d.P), dtype=i32, device=device),
+        seg_off=torch.empty((M, d.L + 1), dtype=i32, device=device),
+        phi=torch.empty((M, capm, 2), dtype=i32, device=device),
+        route_row=torch.empty((d.P, d.Np, d.K), dtype=i32, device=device),
+        HU=torch.empty((slots, capm, 2 * d.I), dtype=bf, device=device),
+        A=torch.empty((slots, capm, d.I), dtype=bf, device=device),
+        Y=torch.empty((capm, d.H), dtype=bf, device=device),
+        out=torch.empty((d.P, d.Np, d.H), dtype=bf, device=device),
+        ws=torch.empty(max(ring_workspace_bytes(d, mb_tokens, MOE_OP_LAYER_FWD), 256), dtype=torch.uint8,
+                       device=device),
+    )
+
+
+def layer_fwd_ring(d, routes, w, X, W13, W2, r: RingBuffers, stream=None):
+    return moe_layer_fwd_ring(d, r.mb_tokens, r.slots, routes, w, X, W13, W2, r.counts, r.seg_off, r.phi,
+                              r.route_row, r.HU, r.A, r.Y, r.out, r.ws, stream)

@@ -154,5 +154,33 @@ def test_mx_arguments_rejected_before_launch():
     assert lib.moe_layer_fwd_mx(ctypes.byref(d2), *args, ws2, None) == ops.MOE_EUNSUPPORTED
 
 
+def test_ring_sizes_and_arguments_rejected_before_launch():
+    lib = ops.load()
+    d = kimi()
+    assert ops.ring_capacity_rows(d, 1024) == 8 * 1024 * 8 + 48 * 255
+    assert ops.ring_capacity_rows(d, 7168) == ops.capacity_rows(d)
+    for bad in (0, -1, 1000, 7169):  # must divide Np
+        assert lib.moe_ring_capacity_rows(ctypes.byref(d), bad) == -1
+    assert lib.moe_ring_workspace_bytes(ctypes.byref(d), 1024, ops.MOE_OP_SCHEDULE) == -1
+    wf = ops.ring_workspace_bytes(d, 1024, ops.MOE_OP_LAYER_FWD)
+    wb = ops.ring_workspace_bytes(d, 1024, ops.MOE_OP_LAYER_BWD)
+    capm = ops.ring_capacity_rows(d, 1024)
+    assert wb >= capm * (7168 * 3 + 2048 * 3) * 2  # per-slot dO_d, dXd, Xd, dHU, replayed HU and A
+    p = [_fake(0x10000 * (i + 1)) for i in range(20)]
+    fwd = p[:14]  # 13 operands and the workspace
+    bwd = p[:15]  # 14 operands and the workspace
+    for mb, slots in ((1000, 2), (0, 2), (1024, 0)):
+        assert lib.moe_layer_fwd_ring(ctypes.byref(d), mb, slots, *fwd, wf, None) == ops.MOE_EINVAL
+        assert lib.moe_layer_bwd_ring(ctypes.byref(d), mb, slots, *bwd, wb, None) == ops.MOE_EINVAL
+    assert lib.moe_layer_fwd_ring(ctypes.byref(d), 1024, 2, *fwd[:4], None, *fwd[5:], wf, None) == ops.MOE_EINVAL
+    assert lib.moe_layer_fwd_ring(ctypes.byref(d), 1024, 2, *fwd[:9], _fake(0x10004), *fwd[10:], wf,
+                                  None) == ops.MOE_EINVAL
+    assert lib.moe_layer_fwd_ring(ctypes.byref(d), 1024, 2, *fwd, wf - 1, None) == ops.MOE_ENOSPC
+    assert lib.moe_layer_bwd_ring(ctypes.byref(d), 1024, 2, *bwd[:14], None, wb, None) == ops.MOE_EINVAL
+    assert lib.moe_layer_bwd_ring(ctypes.byref(d), 1024, 2, *bwd, wb - 1, None) == ops.MOE_ENOSPC
+    d2 = ops.make_desc(8, 7168, 8, 384, 48, H=65536 + 256, I=2048)
+    assert lib.moe_layer_fwd_ring(ctypes.byref(d2), 1024, 2, *fwd, 1 << 40, None) == ops.MOE_EUNSUPPORTED
+
+
 def test_trace_read_empty():
     assert ops.moe_trace_read(4) == []
