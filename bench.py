@@ -269,6 +269,99 @@ def bench_fwd_bwd(args, torch, ops, inputs, dev):
                 "bwd_wgrad": 6.0 * hi * local / (st.get("bwd_wgrad", 1e9) / 1e3) / 1e12}.items()}}
 
 
+def bench_ring(args, torch, ops, inputs, dev):
+    """Kimi-shaped share (balanced routing) through the macrobatch ring
+    (moe_layer_fwd_ring / moe_layer_bwd_ring) for several (tokens per
+    partition per macrobatch, ring slots) settings, beside the ring-less path
+    on the same inputs: forward and forward + backward time, dispatched rows
+    (each macrobatch pads its own segments), replayed macrobatches and the
+    bytes of the row buffers each path keeps."""
+    c = KIMI
+    h = inputs.make_layer_inputs_device(7, c["P"], c["Np"], c["E"], c["K"], c["L"], c["H"], c["I"], dev,
+                                        routing="balanced", x_std=1.0, with_grad=True)
+    d = ops.make_desc(c["P"], c["Np"], c["K"], c["E"], c["L"], H=c["H"], I=c["I"])
+    routes = torch.from_numpy(h["routes"]).to(dev)
+    w = torch.from_numpy(h["w"]).to(dev)
+    L, H, I = c["L"], c["H"], c["I"]
+    local = int(((h["routes"] >= 0) & (h["routes"] < L)).sum())
+    hi = H * I
+    grads = {"dX": torch.empty_like(h["X"]),
+             "dW13": torch.empty((L, 2 * I, H), dtype=torch.float32, device=dev),
+             "dW2": torch.empty((L, H, I), dtype=torch.float32, device=dev),
+             "dw": torch.empty((c["P"], c["Np"], c["K"]), dtype=torch.float32, device=dev)}
+
+    def timed(step, steps):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ops.moe_trace_enable(steps * 64)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        per = {}
+        for name, t in ops.moe_trace_read(steps * 64):
+            per.setdefault(name, []).append(t)
+        ops.moe_trace_enable(0)
+        return e0.elapsed_time(e1) / steps, {k: float(np.sum(v)) / steps for k, v in per.items()}
+
+    res = []
+    # ring-less: fused dispatch for the forward alone; the backward needs the dispatched rows
+    b = ops.alloc_fwd(d, dev, save_hu=True, save_xd=True)
+    bf = ops.alloc_fwd(d, dev, save_hu=True, save_xd=False)
+    ws = torch.empty(ops.workspace_bytes(d, ops.MOE_OP_LAYER_BWD), dtype=torch.uint8, device=dev)
+    fwd_ms, fwd_st = timed(lambda: ops.layer_fwd(d, routes, w, h["X"], h["W13"], h["W2"], bf), args.steps)
+
+    def std_step():
+        ops.layer_fwd(d, routes, w, h["X"], h["W13"], h["W2"], b)
+        ops.moe_layer_bwd(d, h["dOut"], routes, w, b.phi, b.route_row, b.seg_off, b.Xd, b.HU, b.A, h["W13"],
+                          h["W2"], grads["dX"], grads["dW13"], grads["dW2"], grads["dw"], ws)
+
+    fb_ms, _ = timed(std_step, max(2, args.steps // 2))
+    cap = ops.capacity_rows(d)
+    res.append({"mb_tokens": c["Np"], "slots": None, "macrobatches": 1, "fwd_ms": fwd_ms, "fwd_bwd_ms": fb_ms,
+                "dispatched_rows": int(b.seg_off[-1].item()), "replays": 0,
+                "row_buffer_gb": cap * (H + 2 * I + I + H) * 2 / 1e9, "fwd_stage_ms": fwd_st})
+    del b, bf, ws
+    torch.cuda.empty_cache()
+    for item in args.ring.split(","):
+        B, S = (int(x) for x in item.split(":"))
+        M = c["Np"] // B
+        print(f"[bench] ring, {M} macrobatches of {B} tokens per partition, {S} slots", file=sys.stderr, flush=True)
+        r = ops.alloc_ring(d, B, S, dev)
+        ws = torch.empty(ops.ring_workspace_bytes(d, B, ops.MOE_OP_LAYER_BWD), dtype=torch.uint8, device=dev)
+        fwd_ms, fwd_st = timed(lambda: ops.layer_fwd_ring(d, routes, w, h["X"], h["W13"], h["W2"], r), args.steps)
+
+        def ring_step():
+            ops.layer_fwd_ring(d, routes, w, h["X"], h["W13"], h["W2"], r)
+            ops.moe_layer_bwd_ring(d, B, S, h["dOut"], w, h["X"], h["W13"], h["W2"], r.phi, r.route_row, r.seg_off,
+                                   r.HU, r.A, grads["dX"], grads["dW13"], grads["dW2"], grads["dw"], ws)
+
+        fb_ms, fb_st = timed(ring_step, max(2, args.steps // 2))
+        capm = ops.ring_capacity_rows(d, B)
+        res.append({"mb_tokens": B, "slots": S, "macrobatches": M, "fwd_ms": fwd_ms, "fwd_bwd_ms": fb_ms,
+                    "dispatched_rows": int(r.seg_off[:, -1].sum().item()), "replays": max(0, M - S),
+                    "row_buffer_gb": (S * capm * 3 * I + capm * H) * 2 / 1e9, "fwd_stage_ms": fwd_st,
+                    "replay_gateup_ms": fb_st.get("ring_replay_gateup", 0.0)})
+        del r, ws
+        torch.cuda.empty_cache()
+    head = res[1] if len(res) > 1 else res[0]
+    for x in res:
+        x["fwd_tflops"] = 6.0 * hi * local / (x["fwd_ms"] / 1e3) / 1e12
+        x["fwd_bwd_tflops"] = 18.0 * hi * local / (x["fwd_bwd_ms"] / 1e3) / 1e12
+    return {"metric": "MoE layer fwd TFLOP/s through the macrobatch ring (Kimi shape, 1 GPU)",
+            "value": head["fwd_tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": head["fwd_ms"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "kimi_local_share_ring", "P": c["P"], "tokens_per_partition": c["Np"],
+                       "experts": c["E"], "local_experts": L, "top_k": c["K"], "H": H, "I": I,
+                       "routing": "balanced", "local_routes": local, "mb_tokens": head["mb_tokens"],
+                       "ring_slots": head["slots"]},
+            "sweep": res}
+
+
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA (no sparsity)
 
 
@@ -415,8 +508,12 @@ def main():
                     help="routing of --workload kimi_bwd (default: adversarial)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the layer steps, run one plain read+write kernel over this many MiB (counter scaling)")
-    ap.add_argument("--workload", default="kimi", choices=["kimi", "kimi_bwd", "mid_tc", "schedule", "kimi_mx"],
-                    help="kimi: the contract line (default); kimi_bwd / mid_tc / schedule / kimi_mx: extra measurements")
+    ap.add_argument("--workload", default="kimi",
+                    choices=["kimi", "kimi_bwd", "mid_tc", "schedule", "kimi_mx", "kimi_ring"],
+                    help="kimi: the contract line (default); kimi_bwd / mid_tc / schedule / kimi_mx / kimi_ring: extra "
+                         "measurements")
+    ap.add_argument("--ring", default="3584:1,3584:2,1024:2,1024:7",
+                    help="--workload kimi_ring: comma list of tokens-per-partition-per-macrobatch:slots")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -440,6 +537,9 @@ def main():
         return
     if args.workload == "kimi_mx":
         print(json.dumps(bench_layer_mx(args, torch, ops, inputs, dev)), flush=True)
+        return
+    if args.workload == "kimi_ring":
+        print(json.dumps(bench_ring(args, torch, ops, inputs, dev)), flush=True)
         return
     if args.workload == "schedule":
         print(json.dumps(bench_schedule_sweep(args, torch, ops, inputs, dev)), flush=True)
