@@ -363,7 +363,10 @@ __device__ __forceinline__ void epilogue_store_bf16_w(AccW<WM, WN> &acc, char *l
 
 // fp32 tile store of the rows < mvalid and columns < nvalid; with accumulate
 // each element is added to what dst holds (one fp32 add per call, so a
-// sequence of calls sums in call order).
+// sequence of calls sums in call order).  The old values of one mi block are
+// all loaded before any of its stores: interleaved load / store pairs through
+// one pointer cannot be reordered by the compiler and would wait out a full
+// memory latency per element.
 template <int WM, int WN>
 __device__ __forceinline__ void epilogue_store_f32_w(AccW<WM, WN> &acc, float *dst, int64_t ld, int mvalid, int nvalid,
                                                      bool accumulate = false) {
@@ -373,15 +376,27 @@ __device__ __forceinline__ void epilogue_store_f32_w(AccW<WM, WN> &acc, float *d
     const int row0 = WG::row(wm, 0, 0, lane), col0 = wn * (WG::NI * 32) + (lane & 31);
 #pragma unroll
     for (int mi = 0; mi < WG::MI; ++mi) {
+        if (accumulate) {
+            float old[WG::NI][16];
+#pragma unroll
+            for (int ni = 0; ni < WG::NI; ++ni)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int dr = mi * 32 + 8 * (e >> 2) + (e & 3);
+                    const bool ok = row0 + dr < mvalid && col0 + ni * 32 < nvalid;
+                    old[ni][e] = ok ? base[(int64_t)dr * ld + ni * 32] : 0.f;
+                }
+#pragma unroll
+            for (int ni = 0; ni < WG::NI; ++ni)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[mi][ni][e] = old[ni][e] + acc[mi][ni][e];
+        }
 #pragma unroll
         for (int ni = 0; ni < WG::NI; ++ni) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int dr = mi * 32 + 8 * (e >> 2) + (e & 3);
-                if (row0 + dr < mvalid && col0 + ni * 32 < nvalid) {
-                    float *o = base + (int64_t)dr * ld + ni * 32;
-                    *o = accumulate ? *o + acc[mi][ni][e] : acc[mi][ni][e];
-                }
+                if (row0 + dr < mvalid && col0 + ni * 32 < nvalid) base[(int64_t)dr * ld + ni * 32] = acc[mi][ni][e];
             }
             __builtin_amdgcn_sched_barrier(0);
         }
