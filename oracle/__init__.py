@@ -25,6 +25,10 @@ Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
   mx_expert_ffn_rows, mx_layer_fwd_tokens        pinned (dot products vs numpy on the
                                                    dequantized operands; token path = rows +
                                                    combine; close to the bf16 FFN)
+  shared_ffn_tokens, layer_fwd_tokens_shared     pinned (dense SwiGLU vs torch fp64 with no
+                                                   local routes; zero shared weights leave the
+                                                   routed output; the routed part stays linear
+                                                   in w)
   macrobatch_schedules, ring_walk                pinned (one macrobatch = the whole table;
                                                    every local route in exactly one window;
                                                    closed forms of the reversed ring's
@@ -418,3 +422,25 @@ def ring_walk(M: int, S: int, reverse: bool = True):
         resident[m] = slot
     replay = [m for m in range(M) if m not in resident]
     return walk, resident, replay
+
+
+# ---------------------------------------------------------------------------
+# Shared expert ("Beyond Peak TFLOPs" section 2.C; Mixture-of-Kittens notes,
+# section 5): a dense SwiGLU expert applied to every token, its output added to
+# the routed combine.
+# ---------------------------------------------------------------------------
+
+def shared_ffn_tokens(X, W13s, W2s, tokens=None):
+    """S[g] = W2s (silu(W1s x_g) * (W3s x_g)) for the listed tokens (default all),
+    as the single-expert FFN over the token rows in their own order."""
+    X = _u16(X)
+    H = X.shape[-1]
+    Xr = np.ascontiguousarray(X.reshape(-1, H))
+    seg = np.array([0, Xr.shape[0]], np.int32)
+    return expert_ffn_rows(seg, Xr, _u16(W13s)[None], _u16(W2s)[None], rows=tokens, want=("Y",))["Y"]
+
+
+def layer_fwd_tokens_shared(routes, w, X, W13, W2, W13s, W2s, L: int, base: int = 0, tokens=None):
+    """Layer output with a shared expert: routed combine + shared FFN, per token."""
+    return (layer_fwd_tokens(routes, w, X, W13, W2, L=L, base=base, tokens=tokens)
+            + shared_ffn_tokens(X, W13s, W2s, tokens=tokens))
