@@ -266,7 +266,7 @@ def bench_fwd_bwd(args, torch, ops, inputs, dev):
                 "ffn_down": 2.0 * hi * local / (st.get("ffn_down", 1e9) / 1e3) / 1e12,
                 "bwd_down": 2.0 * hi * local / (st.get("bwd_down", 1e9) / 1e3) / 1e12,
                 "bwd_gateup": 4.0 * hi * local / (st.get("bwd_gateup", 1e9) / 1e3) / 1e12,
-                "bwd_wgrad": 6.0 * hi * local / (st.get("bwd_wgrad", 1e9) / 1e3) / 1e12}.items()}}
+                "bwd_wgrad_rdispatch": 6.0 * hi * local / (st.get("bwd_wgrad_rdispatch", 1e9) / 1e3) / 1e12}.items()}}
 
 
 def bench_ring(args, torch, ops, inputs, dev):

@@ -95,6 +95,7 @@ enum {
     MOE_OP_COMBINE = 3,
     MOE_OP_LAYER_FWD = 4,
     MOE_OP_LAYER_BWD = 5,
+    MOE_OP_LAYER_FWD_SHARED = 6,
 };
 int64_t moe_workspace_bytes(const moe_desc *d, int op);
 
@@ -193,6 +194,35 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
                   moe_src *phi, int32_t *route_row, uint16_t *Xd, uint16_t *HU, uint16_t *A,
                   uint16_t *Y, uint16_t *out, int32_t flags, int32_t chunk_rows, void *ws,
                   size_t ws_bytes, void *stream);
+
+/*
+ * moe_layer_fwd_shared — the layer forward with a shared expert: a dense
+ * SwiGLU FFN over every token beside the routed experts ([BPT] section 2.C:
+ * the shared expert computed while the first routed rows are pulled; [MoK]
+ * section 5: the shared expert stays bf16).  Per token g,
+ *   out[g] = bf16( sum_{j asc, local} w[g][j] * Y[route_row[g][j]] + S[g] ),
+ *   S = W2s (silu(W1s x) * (W3s x))  rounded to bf16 once (Ys).
+ *   Is     shared intermediate size, a multiple of 128
+ *   W13s   bf16 [2 Is][H]   gate rows [0, Is), up rows [Is, 2 Is)
+ *   W2s    bf16 [H][Is]
+ *   HUs    bf16 [ntokp][2 Is] out, nullable: saved shared pre-activations
+ *   As     bf16 [ntokp][Is]   out: shared activations
+ *   Ys     bf16 [ntokp][H]    out: S; rows past P*Np are zero
+ *   with ntokp = P*Np rounded up to a multiple of 256.  The routed arguments
+ *   are those of moe_layer_fwd with Xd = NULL (the dispatch fused into the
+ *   gate/up operand loads).
+ *   ws >= moe_workspace_bytes(d, MOE_OP_LAYER_FWD_SHARED)
+ * Launches: the schedule, one gate/up launch holding the shared and the
+ * routed tiles, one down launch holding both, the combine adding S.  The
+ * routed rows (HU, A, Y) are bitwise those of moe_layer_fwd.  Errors as
+ * moe_layer_fwd, and MOE_EINVAL for Is < 1, MOE_EUNSUPPORTED for Is % 128
+ * or H > 65536.
+ */
+int moe_layer_fwd_shared(const moe_desc *d, int32_t Is, const int32_t *routes, const float *w, const uint16_t *X,
+                         const uint16_t *W13, const uint16_t *W2, const uint16_t *W13s, const uint16_t *W2s,
+                         int32_t *counts, int32_t *seg_off, moe_src *phi, int32_t *route_row, uint16_t *HU,
+                         uint16_t *A, uint16_t *Y, uint16_t *HUs, uint16_t *As, uint16_t *Ys, uint16_t *out, void *ws,
+                         size_t ws_bytes, void *stream);
 
 /*
  * MXFP8 routed experts ([MoK] section 5, mixed precision).  Format (the OCP

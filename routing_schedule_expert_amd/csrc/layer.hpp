@@ -211,6 +211,51 @@ __device__ __forceinline__ void mx_down_phase(const MxFfnArgs &a, char *lds) {
 }
 
 // ---------------------------------------------------------------------------
+// Shared expert ("Beyond Peak TFLOPs" section 2.C; the Mixture-of-Kittens
+// notes, section 5: a dense bf16 expert over every token).  It is one more
+// grouped GEMM with a single segment whose table is the identity over the
+// tokens, and its tiles share the routed GEMM's launches: the two work lists
+// are concatenated, shared tiles first, so neither waits for the other's
+// tail.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void dual_gateup_body(const FfnArgs &s, const FfnArgs &r, char *lds) {
+    const int ms = s.seg_off[s.L] / kBM, ns = s.I / 128;
+    const int mr = r.seg_off[r.L] / kBM, nr = r.I / 128;
+    const int64_t ts = (int64_t)ms * ns, total = ts + (int64_t)mr * nr;
+    for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
+        const int64_t lid = logical_tile(it);
+        if (lid >= total) continue;
+        int m, n;
+        if (lid < ts) {
+            grouped_mn(lid, ms, ns, 4, m, n);
+            ffn_gateup_tile(s, m, n, lds);
+        } else {
+            grouped_mn(lid - ts, mr, nr, 4, m, n);
+            ffn_gateup_tile(r, m, n, lds);
+        }
+    }
+}
+
+__device__ __forceinline__ void dual_down_body(const FfnArgs &s, const FfnArgs &r, char *lds) {
+    const int ms = s.seg_off[s.L] / kBM, nt = s.H / 256;
+    const int mr = r.seg_off[r.L] / kBM;
+    const int64_t ts = (int64_t)ms * nt, total = ts + (int64_t)mr * nt;
+    for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
+        const int64_t lid = logical_tile(it);
+        if (lid >= total) continue;
+        int m, n;
+        if (lid < ts) {
+            grouped_mn(lid, ms, nt, 4, m, n);
+            ffn_down_tile(s, m, n, lds);
+        } else {
+            grouped_mn(lid - ts, mr, nt, 4, m, n);
+            ffn_down_tile(r, m, n, lds);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Macrobatch ring ("Beyond Peak TFLOPs" section 2.B; the Mixture-of-Kittens
 // notes, section 4): the combine of one macrobatch runs in the same launch as
 // the gate/up GEMM of the next, so a slot's rows are consumed while the next
@@ -371,7 +416,10 @@ __device__ __forceinline__ void bwd_gateup_phase(const BwdArgs &a, char *lds) {
 // B5: per expert, dW2[l] = sum_rows (w dO_d)^T a  and  dW13[l] = sum_rows dHU^T Xd,
 // as NT products of the transposed activations over the segment's rows
 // (ascending, inside one workgroup per output tile).  Longest segments first.
-__device__ __forceinline__ void wgrad_phase(const BwdArgs &a, char *lds) {
+// The reverse-dispatch sum `c` (B4, HBM-bound) shares the launch as 64-token
+// work items after the tiles ("Beyond Peak TFLOPs" section 2.C: the deferred
+// weight gradients overlap the last reverse-dispatch rounds).
+__device__ __forceinline__ void wgrad_phase(const BwdArgs &a, const WindowCombine &c, char *lds) {
     const int H = a.H, I = a.I, L = a.L;
     __shared__ int s_order[256];
     __syncthreads();
@@ -390,11 +438,19 @@ __device__ __forceinline__ void wgrad_phase(const BwdArgs &a, char *lds) {
     const int mt2 = H / 256, nt2 = (I + 255) / 256;   // dW2 [H][I]
     const int mt13 = 2 * I / 256, nt13 = H / 256;      // dW13 [2I][H]
     const int per = mt2 * nt2 + mt13 * nt13;
-    const int64_t total = (int64_t)L * per;
+    const int64_t ntiles = (int64_t)L * per;
+    const int64_t ncb = c.Y ? (c.ntok + kCombineItem - 1) / kCombineItem : 0;
+    const int64_t total = ntiles + ncb;
     const int64_t ldT = a.ldT;
     for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
         const int64_t lid = logical_tile(it);
         if (lid >= total) continue;
+        if (lid >= ntiles) {
+            const int64_t g0 = (lid - ntiles) * kCombineItem;
+            combine_body(c.Y, c.route_row, c.w, c.out, c.K, c.H, g0, min(g0 + kCombineItem, c.ntok),
+                         threadIdx.x / kWave, blockDim.x / kWave, c.tpp, c.tstride);
+            continue;
+        }
         const int pos = (int)(lid / per), in = (int)(lid % per);
         const int l = L <= 256 ? s_order[pos] : pos;
         const int S = a.seg_off[l];

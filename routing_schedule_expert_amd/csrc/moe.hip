@@ -50,10 +50,33 @@ __global__ __launch_bounds__(256) void k_gather(const uint16_t *src, const moe_s
 
 __global__ __launch_bounds__(256) void k_combine(const uint16_t *Y, const int32_t *route_row, const float *w,
                                                  uint16_t *out, int K, int H, int64_t ntok, int tpp,
-                                                 int64_t tstride) {
+                                                 int64_t tstride, const uint16_t *S) {
     const int waves = blockDim.x / kWave;
     combine_body(Y, route_row, w, out, K, H, 0, ntok, blockIdx.x * waves + threadIdx.x / kWave, gridDim.x * waves,
-                 tpp, tstride);
+                 tpp, tstride, S);
+}
+
+// The shared expert's table: row g < ntok pulls token g (partition g / Np,
+// token g % Np), rows [ntok, ntokp) are padding; one segment [0, ntokp).
+__global__ __launch_bounds__(256) void k_identity_table(moe_src *phi, int32_t *seg_off, int Np, int64_t ntok,
+                                                        int64_t ntokp) {
+    for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < ntokp; g += (int64_t)gridDim.x * blockDim.x)
+        reinterpret_cast<int2 *>(phi)[g] =
+            g < ntok ? make_int2((int)(g / Np), (int)(g % Np)) : make_int2(-1, -1);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        seg_off[0] = 0;
+        seg_off[1] = (int32_t)ntokp;
+    }
+}
+
+__global__ __launch_bounds__(kFwdThreads) void k_dual_gateup(FfnArgs sh, FfnArgs r) {
+    __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+    dual_gateup_body(sh, r, lds);
+}
+
+__global__ __launch_bounds__(kFwdThreads) void k_dual_down(FfnArgs sh, FfnArgs r) {
+    __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
+    dual_down_body(sh, r, lds);
 }
 
 __global__ __launch_bounds__(256) void k_row_weight(const moe_src *phi, const int32_t *npad_ptr,
@@ -130,9 +153,9 @@ __global__ __launch_bounds__(kFwdThreads) void k_bwd_gateup(BwdArgs a) {
     bwd_gateup_phase(a, lds);
 }
 
-__global__ __launch_bounds__(kFwdThreads) void k_wgrad(BwdArgs a) {
+__global__ __launch_bounds__(kFwdThreads) void k_wgrad(BwdArgs a, WindowCombine c) {
     __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
-    wgrad_phase(a, lds);
+    wgrad_phase(a, c, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -211,6 +234,10 @@ int64_t cap_rows(const moe_desc *d) {
     return (int64_t)d->P * d->Np * d->K + (int64_t)d->L * (d->pad_rows - 1);
 }
 
+// Rows of the shared expert's buffers: every token, rounded up to a tile.
+int64_t shared_rows(const moe_desc *d) { return ((int64_t)d->P * d->Np + 255) / 256 * 256; }
+
+
 // 1024-route blocks per logical thread: one for a single routing tensor (most
 // parallelism), four when many tensors are scheduled together (fewer chunks).
 int sched_cb(const moe_desc *d) { return d->num_batches >= 8 ? 4 : 1; }
@@ -221,6 +248,9 @@ int sched_chunks(const moe_desc *d) {
 int sched_wg_per_part(const moe_desc *d) { return (sched_chunks(d) + kSchedWaves - 1) / kSchedWaves; }
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace of the shared expert's identity table: 2 offsets, then the rows.
+int64_t shared_table_bytes(const moe_desc *d) { return 256 + align256(shared_rows(d) * 8); }
 
 int64_t sched_ws_bytes(const moe_desc *d) { return align256(4ll * d->num_batches * d->P * sched_chunks(d) * d->L); }
 
@@ -344,14 +374,15 @@ int launch_gather(const moe_desc *d, const uint16_t *src, const moe_src *phi, co
 
 // tstride > d->Np: the d->Np tokens of each partition are a window of a
 // [P][tstride] token array (route_row, w, out pointing at its first token).
+// S (nullable): the shared expert's output rows [P*Np][H], added per token.
 int launch_combine(const moe_desc *d, const uint16_t *Y, const int32_t *route_row, const float *w, uint16_t *out,
-                   hipStream_t s, const char *name, int64_t tstride = 0) {
+                   hipStream_t s, const char *name, int64_t tstride = 0, const uint16_t *S = nullptr) {
     const int64_t ntok = (int64_t)d->P * d->Np;
     const int grid = (int)std::min<int64_t>((ntok + 3) / 4, 16ll * device_cus());
     const int tpp = tstride > d->Np ? d->Np : 0;
     TraceScope tr(name, s);
     hipLaunchKernelGGL(k_combine, dim3(grid), dim3(256), 0, s, Y, route_row, w, out, d->K, d->H, ntok, tpp,
-                       tpp ? tstride : (int64_t)0);
+                       tpp ? tstride : (int64_t)0, S);
     return launch_status();
 }
 
@@ -443,7 +474,7 @@ int64_t moe_capacity_rows(const moe_desc *d) {
 
 int64_t moe_workspace_bytes(const moe_desc *d, int op) {
     const bool ffn = op == MOE_OP_EXPERT_FFN || op == MOE_OP_LAYER_FWD || op == MOE_OP_LAYER_BWD ||
-                     op == MOE_OP_DISPATCH || op == MOE_OP_COMBINE;
+                     op == MOE_OP_DISPATCH || op == MOE_OP_COMBINE || op == MOE_OP_LAYER_FWD_SHARED;
     if (check_desc(d, ffn) != MOE_OK) return -1;
     switch (op) {
         case MOE_OP_SCHEDULE: return sched_ws_bytes(d);
@@ -456,6 +487,11 @@ int64_t moe_workspace_bytes(const moe_desc *d, int op) {
             return kBarrierBytes + sched_ws_bytes(&one);
         }
         case MOE_OP_LAYER_BWD: return bwd_ws_bytes(d);
+        case MOE_OP_LAYER_FWD_SHARED: {
+            moe_desc one = *d;
+            one.num_batches = 1;
+            return kBarrierBytes + sched_ws_bytes(&one) + shared_table_bytes(d);
+        }
         default: return -1;
     }
 }
@@ -657,9 +693,6 @@ int bwd_core(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const flo
         hipLaunchKernelGGL(k_bwd_gateup, dim3(grid), dim3(kFwdThreads), 0, s, a);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
-    // B4: reverse-dispatch sum over each token's local slots
-    rc = launch_combine(d, a.dXd, route_row, nullptr, dX, s, "bwd_reverse_dispatch", window ? tstride : 0);
-    if (rc != MOE_OK) return rc;
     // activations transposed (rows [0, Npad)) so the weight gradients reduce
     // over K-contiguous rows; the router weight is folded into dO_d here
     rc = launch_transpose(make_transpose(a.dOd, a.dYT, (int32_t)cap, (int32_t)H, 1, H, ldT, 0, 0, a.wrow, npad), s,
@@ -674,10 +707,73 @@ int bwd_core(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const flo
     rc = launch_transpose(make_transpose(Xd, a.XdT, (int32_t)cap, (int32_t)H, 1, H, ldT, 0, 0, nullptr, npad), s,
                           "bwd_transpose_xd");
     if (rc != MOE_OK) return rc;
-    // B5: weight gradients, after every data gradient, fixed row order
-    TraceScope tr("bwd_wgrad", s);
-    hipLaunchKernelGGL(k_wgrad, dim3(grid), dim3(kFwdThreads), 0, s, a);
+    // B5: weight gradients, after every data gradient, fixed row order, in one
+    // launch with B4, the reverse-dispatch sum over each token's local slots
+    WindowCombine rd{};
+    rd.Y = a.dXd;
+    rd.route_row = route_row;
+    rd.w = nullptr;
+    rd.out = dX;
+    rd.K = d->K;
+    rd.H = d->H;
+    rd.tpp = window ? d->Np : 0;
+    rd.ntok = (int64_t)d->P * d->Np;
+    rd.tstride = window ? tstride : 0;
+    TraceScope tr("bwd_wgrad_rdispatch", s);
+    hipLaunchKernelGGL(k_wgrad, dim3(grid), dim3(kFwdThreads), 0, s, a, rd);
     return launch_status();
+}
+
+int moe_layer_fwd_shared(const moe_desc *d, int32_t Is, const int32_t *routes, const float *w, const uint16_t *X,
+                         const uint16_t *W13, const uint16_t *W2, const uint16_t *W13s, const uint16_t *W2s,
+                         int32_t *counts, int32_t *seg_off, moe_src *phi, int32_t *route_row, uint16_t *HU,
+                         uint16_t *A, uint16_t *Y, uint16_t *HUs, uint16_t *As, uint16_t *Ys, uint16_t *out, void *ws,
+                         size_t ws_bytes, void *stream) {
+    int rc = check_desc(d, true);
+    if (rc != MOE_OK) return rc;
+    if (d->num_batches != 1 || Is < 1) return MOE_EINVAL;
+    if (Is % 128) return MOE_EUNSUPPORTED;
+    if (d->H > kZeroRowElems) return MOE_EUNSUPPORTED;  // padding rows read the static zero row
+    const void *ptrs[] = {routes, w, X, W13, W2, W13s, W2s, counts, seg_off, phi, route_row, A, Y, As, Ys, out, ws};
+    for (const void *p : ptrs)
+        if (!p || !aligned16(p)) return MOE_EINVAL;
+    if ((HU && !aligned16(HU)) || (HUs && !aligned16(HUs))) return MOE_EINVAL;
+    if ((int64_t)ws_bytes < moe_workspace_bytes(d, MOE_OP_LAYER_FWD_SHARED)) return MOE_ENOSPC;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *wsb = static_cast<char *>(ws);
+    uint32_t *bar = reinterpret_cast<uint32_t *>(wsb);
+    moe_desc one = *d;
+    one.num_batches = 1;
+    char *sched_ws = wsb + kBarrierBytes;
+    char *tbl = sched_ws + sched_ws_bytes(&one);
+    int32_t *seg_s = reinterpret_cast<int32_t *>(tbl);
+    moe_src *phi_s = reinterpret_cast<moe_src *>(tbl + 256);
+    const int64_t ntok = (int64_t)d->P * d->Np, ntokp = shared_rows(d);
+    {
+        TraceScope tr("shared_table", s);
+        hipLaunchKernelGGL(k_identity_table, dim3((int)std::min<int64_t>((ntokp + 255) / 256, 1024)), dim3(256), 0, s,
+                           phi_s, seg_s, d->Np, ntok, ntokp);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    rc = launch_schedule(&one, routes, counts, seg_off, phi, route_row, sched_ws, s);
+    if (rc != MOE_OK) return rc;
+    FfnArgs fr = make_ffn_args(d, nullptr, W13, W2, seg_off, HU, A, Y, 0, bar, X, phi);
+    moe_desc ds = *d;
+    ds.L = 1;
+    ds.I = Is;
+    FfnArgs fs = make_ffn_args(&ds, nullptr, W13s, W2s, seg_s, HUs, As, Ys, 0, bar, X, phi_s);
+    const int grid = gemm_grid();
+    {
+        TraceScope tr("shared_routed_gateup", s);
+        hipLaunchKernelGGL(k_dual_gateup, dim3(grid), dim3(kFwdThreads), 0, s, fs, fr);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    {
+        TraceScope tr("shared_routed_down", s);
+        hipLaunchKernelGGL(k_dual_down, dim3(grid), dim3(kFwdThreads), 0, s, fs, fr);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    return launch_combine(d, Y, route_row, w, out, s, "combine_shared", 0, Ys);
 }
 
 int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes, const float *w, const moe_src *phi,

@@ -55,15 +55,16 @@ __device__ __forceinline__ int64_t window_token(int64_t g, int tpp, int64_t tstr
     return tpp ? (g / tpp) * tstride + g % tpp : g;
 }
 
-// out[g] = sum_{j asc, rows[g][j] >= 0} w[g][j] * Y[rows[g][j]] for tokens g in
-// [g_begin, g_end) (through window_token when tpp > 0: route_row, w and out
-// then point at the window's first token of partition 0); one wave per token,
-// kRowUnroll 16-byte chunks per lane in flight.  w == nullptr means every
-// weight is 1.
+// out[g] = sum_{j asc, rows[g][j] >= 0} w[g][j] * Y[rows[g][j]] (+ S[g]) for
+// tokens g in [g_begin, g_end) (through window_token when tpp > 0: route_row,
+// w and out then point at the window's first token of partition 0); one wave
+// per token, kRowUnroll 16-byte chunks per lane in flight.  w == nullptr means
+// every weight is 1.  S (nullable, [tokens][H]) is the shared expert's output,
+// added after the slots, before the one rounding.
 __device__ void combine_body(const uint16_t *__restrict__ Y, const int32_t *__restrict__ route_row,
                              const float *__restrict__ w, uint16_t *__restrict__ out, int K, int H,
                              int64_t g_begin, int64_t g_end, int wave_global, int nwaves, int tpp = 0,
-                             int64_t tstride = 0) {
+                             int64_t tstride = 0, const uint16_t *__restrict__ S = nullptr) {
     const int lane = lane_id();
     const int chunks = H / 8;
     for (int64_t gw = g_begin + wave_global; gw < g_end; gw += nwaves) {
@@ -93,6 +94,19 @@ __device__ void combine_body(const uint16_t *__restrict__ Y, const int32_t *__re
                         acc[u][2 * e] = fmaf(wq, __uint_as_float(v[u][e] << 16), acc[u][2 * e]);
                         acc[u][2 * e + 1] = fmaf(wq, __uint_as_float(v[u][e] & 0xffff0000u), acc[u][2 * e + 1]);
                     }
+            }
+            if (S) {
+                const u32x4 *sr = reinterpret_cast<const u32x4 *>(S + g * (int64_t)H);
+#pragma unroll
+                for (int u = 0; u < kRowUnroll; ++u) {
+                    int c = c0 + u * kWave + lane;
+                    const u32x4 v = c < chunks ? __builtin_nontemporal_load(sr + c) : u32x4{0, 0, 0, 0};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[u][2 * e] += __uint_as_float(v[e] << 16);
+                        acc[u][2 * e + 1] += __uint_as_float(v[e] & 0xffff0000u);
+                    }
+                }
             }
 #pragma unroll
             for (int u = 0; u < kRowUnroll; ++u) {

@@ -19,7 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOSPC, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3, -4
-MOE_OP_SCHEDULE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_LAYER_FWD, MOE_OP_LAYER_BWD = range(6)
+(MOE_OP_SCHEDULE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_LAYER_FWD, MOE_OP_LAYER_BWD,
+ MOE_OP_LAYER_FWD_SHARED) = range(7)
 MOE_PERSISTENT = 1
 
 EXPORTED = (
@@ -28,6 +29,7 @@ EXPORTED = (
     "moe_quantize_mx",
     "moe_layer_fwd_mx",
     "moe_ring_capacity_rows", "moe_ring_workspace_bytes", "moe_layer_fwd_ring", "moe_layer_bwd_ring",
+    "moe_layer_fwd_shared",
 )
 
 
@@ -74,6 +76,7 @@ def load() -> ctypes.CDLL:
         "moe_quantize_mx": (ctypes.c_int, [P, i64, i32, P, P, P]),
         "moe_layer_fwd_mx": (ctypes.c_int, [D] + [P] * 18 + [sz, P]),
         "moe_layer_bwd": (ctypes.c_int, [D] + [P] * 16 + [sz, P]),
+        "moe_layer_fwd_shared": (ctypes.c_int, [D, i32] + [P] * 19 + [sz, P]),
         "moe_ring_capacity_rows": (i64, [D, i32]),
         "moe_ring_workspace_bytes": (i64, [D, i32, ctypes.c_int]),
         "moe_layer_fwd_ring": (ctypes.c_int, [D, i32, i32] + [P] * 14 + [sz, P]),
@@ -366,3 +369,43 @@ def alloc_ring(d: moe_desc, mb_tokens: int, slots: int, device) -> RingBuffers:
 def layer_fwd_ring(d, routes, w, X, W13, W2, r: RingBuffers, stream=None):
     return moe_layer_fwd_ring(d, r.mb_tokens, r.slots, routes, w, X, W13, W2, r.counts, r.seg_off, r.phi,
                               r.route_row, r.HU, r.A, r.Y, r.out, r.ws, stream)
+
+
+# ---------------------------------------------------------------------------
+# Shared expert.
+# ---------------------------------------------------------------------------
+
+def moe_layer_fwd_shared(d, Is, routes, w, X, W13, W2, W13s, W2s, counts, seg_off, phi, route_row, HU, A, Y, HUs, As,
+                         Ys, out, ws, stream=None):
+    rc = load().moe_layer_fwd_shared(ctypes.byref(d), Is, _dev(routes), _dev(w), _dev(X), _dev(W13), _dev(W2),
+                                     _dev(W13s), _dev(W2s), _dev(counts), _dev(seg_off), _dev(phi), _dev(route_row),
+                                     _dev(HU), _dev(A), _dev(Y), _dev(HUs), _dev(As), _dev(Ys), _dev(out), _dev(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream, X))
+    return _check(rc, "moe_layer_fwd_shared")
+
+
+@dataclass
+class SharedBuffers:
+    Is: int
+    HUs: torch.Tensor | None
+    As: torch.Tensor
+    Ys: torch.Tensor
+    ws: torch.Tensor
+
+
+def alloc_shared(d: moe_desc, Is: int, device, save_hu: bool = False) -> SharedBuffers:
+    ntokp = (d.P * d.Np + 255) // 256 * 256
+    bf = torch.bfloat16
+    return SharedBuffers(
+        Is=Is,
+        HUs=torch.empty((ntokp, 2 * Is), dtype=bf, device=device) if save_hu else None,
+        As=torch.empty((ntokp, Is), dtype=bf, device=device),
+        Ys=torch.empty((ntokp, d.H), dtype=bf, device=device),
+        ws=torch.empty(workspace_bytes(d, MOE_OP_LAYER_FWD_SHARED), dtype=torch.uint8, device=device),
+    )
+
+
+def layer_fwd_shared(d, routes, w, X, W13, W2, W13s, W2s, bufs: FwdBuffers, sh: SharedBuffers, stream=None):
+    """Forward with a shared expert; bufs.Xd is not used (fused dispatch)."""
+    return moe_layer_fwd_shared(d, sh.Is, routes, w, X, W13, W2, W13s, W2s, bufs.counts, bufs.seg_off, bufs.phi,
+                                bufs.route_row, bufs.HU, bufs.A, bufs.Y, sh.HUs, sh.As, sh.Ys, bufs.out, sh.ws, stream)
