@@ -362,6 +362,68 @@ def bench_ring(args, torch, ops, inputs, dev):
             "sweep": res}
 
 
+def bench_shared(args, torch, ops, inputs, dev):
+    """Kimi-shaped forward share with a shared expert (Is = --shared-is):
+    moe_layer_fwd_shared (shared tiles inside the routed GEMM launches, the
+    shared output added by the combine) beside the same work in separate
+    launches (the routed forward, the shared expert as its own grouped GEMM,
+    then an elementwise add)."""
+    c = KIMI
+    Is = args.shared_is
+    h = inputs.make_layer_inputs_device(5, c["P"], c["Np"], c["E"], c["K"], c["L"], c["H"], c["I"], dev,
+                                        routing="balanced", x_std=1.0)
+    W13s = inputs.normal_bf16_device((2 * Is, c["H"]), 0.02, 91, dev)
+    W2s = inputs.normal_bf16_device((c["H"], Is), 0.02, 92, dev)
+    d = ops.make_desc(c["P"], c["Np"], c["K"], c["E"], c["L"], H=c["H"], I=c["I"])
+    routes = torch.from_numpy(h["routes"]).to(dev)
+    w = torch.from_numpy(h["w"]).to(dev)
+    ntok = c["P"] * c["Np"]
+    assert ntok % 256 == 0
+    local = int(((h["routes"] >= 0) & (h["routes"] < c["L"])).sum())
+    b = ops.alloc_fwd(d, dev, save_hu=True, save_xd=False)
+    sh = ops.alloc_shared(d, Is, dev)
+    ds = ops.make_desc(1, ntok, 1, 1, 1, H=c["H"], I=Is)
+    seg_s = torch.tensor([0, ntok], dtype=torch.int32, device=dev)
+    Xrows = h["X"].view(ntok, c["H"])
+    ws_s = torch.empty(max(ops.workspace_bytes(ds, ops.MOE_OP_EXPERT_FFN), 256), dtype=torch.uint8, device=dev)
+
+    def timed(step):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ops.moe_trace_enable(args.steps * 16)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        per = {}
+        for name, t in ops.moe_trace_read(args.steps * 16):
+            per.setdefault(name, []).append(t)
+        ops.moe_trace_enable(0)
+        return e0.elapsed_time(e1) / args.steps, {k: float(np.mean(v)) for k, v in per.items()}
+
+    ms_f, st_f = timed(lambda: ops.layer_fwd_shared(d, routes, w, h["X"], h["W13"], h["W2"], W13s, W2s, b, sh))
+
+    def separate():
+        ops.layer_fwd(d, routes, w, h["X"], h["W13"], h["W2"], b)
+        ops.moe_expert_ffn(ds, Xrows, W13s, W2s, seg_s, None, sh.As, sh.Ys, 0, ws_s)
+        b.out.view(ntok, c["H"]).add_(sh.Ys[:ntok])
+
+    ms_s, st_s = timed(separate)
+    fl = 6.0 * c["H"] * c["I"] * local + 6.0 * c["H"] * Is * ntok
+    return {"metric": "MoE layer fwd TFLOP/s with a shared expert (Kimi shape, 1 GPU)",
+            "value": fl / (ms_f / 1e3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_f, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "kimi_local_share_fwd_shared_expert", "P": c["P"],
+                       "tokens_per_partition": c["Np"], "experts": c["E"], "local_experts": c["L"], "top_k": c["K"],
+                       "H": c["H"], "I": c["I"], "shared_I": Is, "routing": "balanced", "local_routes": local},
+            "stage_ms": st_f,
+            "separate_launches": {"ms_per_step": ms_s, "tflops": fl / (ms_s / 1e3) / 1e12, "stage_ms": st_s}}
+
+
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA (no sparsity)
 
 
@@ -509,9 +571,10 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the layer steps, run one plain read+write kernel over this many MiB (counter scaling)")
     ap.add_argument("--workload", default="kimi",
-                    choices=["kimi", "kimi_bwd", "mid_tc", "schedule", "kimi_mx", "kimi_ring"],
-                    help="kimi: the contract line (default); kimi_bwd / mid_tc / schedule / kimi_mx / kimi_ring: extra "
-                         "measurements")
+                    choices=["kimi", "kimi_bwd", "mid_tc", "schedule", "kimi_mx", "kimi_ring", "kimi_shared"],
+                    help="kimi: the contract line (default); kimi_bwd / mid_tc / schedule / kimi_mx / kimi_ring / "
+                         "kimi_shared: extra measurements")
+    ap.add_argument("--shared-is", type=int, default=2048, help="--workload kimi_shared: shared intermediate size")
     ap.add_argument("--ring", default="3584:1,3584:2,1024:2,1024:7",
                     help="--workload kimi_ring: comma list of tokens-per-partition-per-macrobatch:slots")
     args = ap.parse_args()
@@ -540,6 +603,9 @@ def main():
         return
     if args.workload == "kimi_ring":
         print(json.dumps(bench_ring(args, torch, ops, inputs, dev)), flush=True)
+        return
+    if args.workload == "kimi_shared":
+        print(json.dumps(bench_shared(args, torch, ops, inputs, dev)), flush=True)
         return
     if args.workload == "schedule":
         print(json.dumps(bench_schedule_sweep(args, torch, ops, inputs, dev)), flush=True)
