@@ -238,9 +238,11 @@ int64_t cap_rows(const moe_desc *d) {
 int64_t shared_rows(const moe_desc *d) { return ((int64_t)d->P * d->Np + 255) / 256 * 256; }
 
 
-// 1024-route blocks per logical thread: one for a single routing tensor (most
-// parallelism), four when many tensors are scheduled together (fewer chunks).
-int sched_cb(const moe_desc *d) { return d->num_batches >= 8 ? 4 : 1; }
+// Blocks of kSchedBlock routes per logical thread: 1,024 routes for a single
+// routing tensor (most parallelism), 4,096 when many tensors are scheduled
+// together (fewer chunks).
+int sched_cb(const moe_desc *d) { return (d->num_batches >= 8 ? 4096 : 1024) / kSchedBlock; }
+static_assert(1024 % kSchedBlock == 0, "a logical thread holds whole blocks");
 int sched_chunks(const moe_desc *d) {
     const int64_t chunk = (int64_t)kSchedBlock * sched_cb(d);
     return (int)(((int64_t)d->Np * d->K + chunk - 1) / chunk);
@@ -323,11 +325,15 @@ void fill_sched_args(SchedArgs &a, const moe_desc *d, const int32_t *routes, int
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS of one gfx950 workgroup
 
-// LDS (bytes) of the schedule bodies for `wpw` waves per workgroup.
-size_t sched_lds_bytes(const moe_desc *d, int wpw) {
+// LDS (bytes) of each schedule body for `wpw` waves per workgroup (stage 0
+// count, 1 finalize, 2 scatter; -1: the largest, for a caller running all three).
+size_t sched_lds_bytes(const moe_desc *d, int wpw, int stage = -1) {
     const size_t L = d->L, P = d->P;
     const size_t mstride = P <= (size_t)kSchedPMax ? (size_t)kSchedPMax : P;
     size_t count = wpw * (L + 1), fin = P * L + L + 16, scat = L * mstride + L + 1 + wpw * (L + 2 * kSchedBlock);
+    if (stage == 0) return 4 * count;
+    if (stage == 1) return 4 * fin;
+    if (stage == 2) return 4 * scat;
     return 4 * std::max(count, std::max(fin, scat));
 }
 
@@ -341,21 +347,22 @@ int launch_schedule(const moe_desc *d, const int32_t *routes, int32_t *counts, i
     if (bstride > 0) a.bstride = bstride;
     const int wg_per_batch = a.P * a.wg_per_part;
     const int grid = a.nb >= 8 ? 8 * ((a.nb + 7) / 8) * wg_per_batch : a.nb * wg_per_batch;
-    const size_t lds = sched_lds_bytes(d, kSchedWaves);
-    if (lds > kMaxLds) return MOE_EUNSUPPORTED;
+    if (sched_lds_bytes(d, kSchedWaves) > kMaxLds) return MOE_EUNSUPPORTED;
     {
         TraceScope tr("sched_count", s);
-        hipLaunchKernelGGL(k_sched_count, dim3(grid), dim3(64 * kSchedWaves), lds, s, a);
+        hipLaunchKernelGGL(k_sched_count, dim3(grid), dim3(64 * kSchedWaves), sched_lds_bytes(d, kSchedWaves, 0), s,
+                           a);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
     {
         TraceScope tr("sched_finalize", s);
-        hipLaunchKernelGGL(k_sched_finalize, dim3(a.nb), dim3(256), lds, s, a);
+        hipLaunchKernelGGL(k_sched_finalize, dim3(a.nb), dim3(256), sched_lds_bytes(d, kSchedWaves, 1), s, a);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
     {
         TraceScope tr("sched_scatter", s);
-        hipLaunchKernelGGL(k_sched_scatter, dim3(grid), dim3(64 * kSchedWaves), lds, s, a);
+        hipLaunchKernelGGL(k_sched_scatter, dim3(grid), dim3(64 * kSchedWaves), sched_lds_bytes(d, kSchedWaves, 2),
+                           s, a);
     }
     return launch_status();
 }
