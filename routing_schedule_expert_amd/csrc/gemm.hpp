@@ -12,9 +12,10 @@
 // K-contiguous ([mn][k]); their [256][64] bf16 tiles go global -> LDS by
 // direct DMA (global_load_lds_dwordx4), double buffered (2 x 64 KiB), with a
 // 256-byte window XOR swizzle that keeps the 16-lane phases of ds_read_b128
-// conflict-free.  The backward feeds transposed copies so every product has
-// this form.  No float atomics: each output element is reduced over K inside
-// one workgroup in ascending K.
+// conflict-free.  The backward's operands that lie MN-contiguous (the weights
+// along their rows, the activations over their rows) use the same loop with
+// transposing LDS reads (gemm_mainloop_x).  No float atomics: each output
+// element is reduced over K inside one workgroup in ascending K.
 #pragma once
 
 #include "common.hpp"
@@ -235,6 +236,272 @@ __device__ __forceinline__ void gemm_mainloop_w(const KOp &ak, const KOp &bk, in
         }
         if (++slot == NST) slot = 0;
     }
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Operands stored MN-contiguous ([k][mn]): the backward's products need
+// W2[l] and W13[l] along their rows, and the weight gradients reduce over the
+// rows of the activations; instead of transposed copies in HBM, such an
+// operand's [64][256] tile is moved to LDS as it lies (512-byte k rows) and
+// its MFMA fragments are built with the transposing LDS read
+// (ds_read_b64_tr_b16): within each 16-lane group, lane 4j + c points at 4
+// consecutive mn values of k row j, and lane i receives, from the lanes
+// 4j + i/4 (j = 0..3), their (i%4)-th values, i.e. the 4 k values of column
+// i.  Two such reads give a lane its 8 k values of one column.
+//
+// T tile layout: k row r at r * 512 bytes; its 16-byte chunk c at physical
+// chunk c ^ (4 * (r & 3)), so the 4 rows a 16-lane group reads fall in 4
+// different 64-byte quarters of the 256-byte bank window.
+// ---------------------------------------------------------------------------
+
+// An MN-contiguous operand window: element (k, mn) at base + k * ld + mn, for
+// mn < valid (128 or 256); columns past `valid` repeat the first ones (their
+// results are masked by the caller).
+struct TOp {
+    const uint16_t *base;
+    int64_t ld;
+    int valid;
+};
+
+__device__ __forceinline__ uint32_t ttile_off(int r, int c) { return (uint32_t)(r * 512 + ((c ^ (4 * (r & 3))) << 4)); }
+
+// Source (at k = 0) of this lane's 16 bytes in its i-th DMA block of a T
+// tile: block b covers k rows 2b, 2b+1; lane L writes physical chunk L % 32 of
+// row 2b + L / 32 and fetches the logical chunk the swizzle puts there.
+template <int NW>
+__device__ __forceinline__ const uint16_t *dma_src_t(const TOp &op, int i) {
+    constexpr int blks_per_wave = 32 / NW;
+    const int t = threadIdx.x, w = t >> 6, L = t & 63;
+    const int r = 2 * (w * blks_per_wave + i) + (L >> 5);
+    int c = (L & 31) ^ (4 * (r & 3));
+    if (c * 8 >= op.valid) c -= op.valid / 8;
+    return op.base + (int64_t)r * op.ld + c * 8;
+}
+
+// This wave's i-th 1 KiB DMA block of a [256][64]-sized operand tile, from a
+// per-lane source already advanced to the K step.
+template <int NW>
+__device__ __forceinline__ void dma_blk_x(const uint16_t *src, char *tile, int i) {
+    const int blk = (threadIdx.x >> 6) * (32 / NW) + i;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(src), (lds_void_t *)(tile + blk * 1024), 16, 0, 0);
+}
+
+// LDS byte address of a generic pointer into this workgroup's LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)(const char *)p;
+}
+
+// The two transposing-read addresses of a T-operand fragment for MFMA block
+// base `mnb` (a multiple of 32) and sub-step s: this lane's column
+// mnb + lane % 32, k rows 16 s + 8 (lane / 32) + 0..3 and + 4..7.
+__device__ __forceinline__ void t_frag_addr(const char *tile, int mnb, int s, int lane, uint32_t &a0, uint32_t &a1) {
+    const int h2 = lane >> 5, g = (lane >> 4) & 1, q = lane & 15, j = q >> 2, cq = q & 3;
+    const int c = (mnb >> 3) + 2 * g + (cq >> 1);
+    a0 = lds_addr(tile + ttile_off(16 * s + 8 * h2 + j, c) + (cq & 1) * 8);
+    a1 = lds_addr(tile + ttile_off(16 * s + 8 * h2 + 4 + j, c) + (cq & 1) * 8);
+}
+
+// N transposing LDS reads (ds_read_b64_tr_b16) and a wait for them, in one
+// asm block, so the results are complete when it ends.  Issued as compiler
+// builtins, each such read made the compiler wait for every outstanding DMA
+// into LDS first (it cannot tell that they target the other stage), which
+// serialised the next stage's loads with this one's MFMAs.
+template <int N>
+__device__ __forceinline__ void tr_reads(const uint32_t (&ad)[N], uint64_t (&o)[N]);
+template <>
+__device__ __forceinline__ void tr_reads<4>(const uint32_t (&ad)[4], uint64_t (&o)[4]) {
+    asm volatile("ds_read_b64_tr_b16 %0, %4\n\t"
+                 "ds_read_b64_tr_b16 %1, %5\n\t"
+                 "ds_read_b64_tr_b16 %2, %6\n\t"
+                 "ds_read_b64_tr_b16 %3, %7\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+                 : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]));
+}
+
+template <>
+__device__ __forceinline__ void tr_reads<8>(const uint32_t (&ad)[8], uint64_t (&o)[8]) {
+    asm volatile("ds_read_b64_tr_b16 %0, %8\n\t"
+                 "ds_read_b64_tr_b16 %1, %9\n\t"
+                 "ds_read_b64_tr_b16 %2, %10\n\t"
+                 "ds_read_b64_tr_b16 %3, %11\n\t"
+                 "ds_read_b64_tr_b16 %4, %12\n\t"
+                 "ds_read_b64_tr_b16 %5, %13\n\t"
+                 "ds_read_b64_tr_b16 %6, %14\n\t"
+                 "ds_read_b64_tr_b16 %7, %15\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+                 : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]));
+}
+
+template <>
+__device__ __forceinline__ void tr_reads<12>(const uint32_t (&ad)[12], uint64_t (&o)[12]) {
+    asm volatile("ds_read_b64_tr_b16 %0, %12\n\t"
+                 "ds_read_b64_tr_b16 %1, %13\n\t"
+                 "ds_read_b64_tr_b16 %2, %14\n\t"
+                 "ds_read_b64_tr_b16 %3, %15\n\t"
+                 "ds_read_b64_tr_b16 %4, %16\n\t"
+                 "ds_read_b64_tr_b16 %5, %17\n\t"
+                 "ds_read_b64_tr_b16 %6, %18\n\t"
+                 "ds_read_b64_tr_b16 %7, %19\n\t"
+                 "ds_read_b64_tr_b16 %8, %20\n\t"
+                 "ds_read_b64_tr_b16 %9, %21\n\t"
+                 "ds_read_b64_tr_b16 %10, %22\n\t"
+                 "ds_read_b64_tr_b16 %11, %23\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11])
+                 : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]), "v"(ad[8]), "v"(ad[9]), "v"(ad[10]), "v"(ad[11]));
+}
+
+// Fragment from two transposing reads: 4 k values each, low then high.
+__device__ __forceinline__ bf16x8 tr_frag(uint64_t lo, uint64_t hi) {
+    typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+    const u64x2 v = {lo, hi};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// An operand of the general main loop: K-contiguous (KOp) or MN-contiguous (TOp).
+template <bool T>
+struct OpOf {
+    using type = KOp;
+};
+template <>
+struct OpOf<true> {
+    using type = TOp;
+};
+
+// One K step of gemm_mainloop_x on stage `slot`; with FILL the next stage's
+// DMA (sources already advanced by the caller) is spread over the first two
+// sub-steps.  FILL is a template flag so no branch splits the pinned
+// MFMA / DMA interleave.
+template <int WM, int WN, bool AT, bool BT, bool FILL, int GH>
+__device__ __forceinline__ void x_step(char *lds, int slot, int lane, int arow, const int (&brow)[WaveGrid<WM, WN>::NI],
+                                       const uint16_t *const (&asrc)[GH], const uint16_t *const (&bsrc)[GH],
+                                       int64_t ao, int64_t bo, AccW<WM, WN> &acc) {
+    using WG = WaveGrid<WM, WN>;
+    constexpr int MI = WG::MI, NI = WG::NI, NW = WG::NW;
+    constexpr int BKT = 64, SW = 3, SPREAD = 2;
+    constexpr int tile_bytes = 256 * BKT * 2, stage_bytes = 2 * tile_bytes;
+    constexpr int G = 2 * GH, S = BKT / 16, D = G / SPREAD;
+    static_assert((MI * NI) % D == 0, "DMA slots");
+    constexpr int EVERY = MI * NI / D;
+    wait_vm_barrier<0>();
+    char *dst = lds + (slot ^ 1) * stage_bytes;
+    const char *stage = lds + slot * stage_bytes;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int kc = 2 * s + (lane >> 5);
+        bf16x8 fa[MI], fb[NI];
+        if constexpr (!AT) {
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+                fa[mi] = *reinterpret_cast<const bf16x8 *>(stage + tile_off_t<BKT, SW>(arow + mi * 32, kc));
+        }
+        if constexpr (!BT) {
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+                fb[ni] = *reinterpret_cast<const bf16x8 *>(stage + tile_bytes + tile_off_t<BKT, SW>(brow[ni], kc));
+        }
+        if constexpr (AT || BT) {  // every transposing read of the sub-step in one batch
+            constexpr int NA = AT ? 2 * MI : 0, NB = BT ? 2 * NI : 0;
+            uint32_t ad[NA + NB];
+            uint64_t o[NA + NB];
+            if constexpr (AT) {
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) t_frag_addr(stage, arow + mi * 32, s, lane, ad[2 * mi], ad[2 * mi + 1]);
+            }
+            if constexpr (BT) {
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni)
+                    t_frag_addr(stage + tile_bytes, brow[ni], s, lane, ad[NA + 2 * ni], ad[NA + 2 * ni + 1]);
+            }
+            tr_reads<NA + NB>(ad, o);
+            if constexpr (AT) {
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi) fa[mi] = tr_frag(o[2 * mi], o[2 * mi + 1]);
+            }
+            if constexpr (BT) {
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni) fb[ni] = tr_frag(o[NA + 2 * ni], o[NA + 2 * ni + 1]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < MI * NI; ++q) {
+            acc[q / NI][q % NI] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q / NI], fb[q % NI], acc[q / NI][q % NI], 0, 0, 0);
+            if constexpr (FILL) {
+                if (s < SPREAD && (q + 1) % EVERY == 0) {
+                    const int g = s * D + (q + 1) / EVERY - 1;
+                    if (g < GH) dma_blk_x<NW>(asrc[g] + ao, dst, g);
+                    else dma_blk_x<NW>(bsrc[g - GH] + bo, dst + tile_bytes, g - GH);
+                }
+            }
+        }
+        if constexpr (FILL) {
+            if (s < SPREAD) {
+#pragma unroll
+                for (int j = 0; j < D; ++j) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, EVERY, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+            }
+        }
+    }
+}
+
+// gemm_mainloop_w (K step 64, two stages, window swizzle, DMA spread over
+// two sub-steps) with either operand MN-contiguous: AT / BT select TOp
+// operands.  A K-contiguous operand's DMA moves k0 elements along its rows, an
+// MN-contiguous one's k0 rows.  The MFMA inputs, and so the results, are
+// those of the same product with transposed copies.
+template <int WM, int WN, bool AT, bool BT>
+__device__ __forceinline__ void gemm_mainloop_x(const typename OpOf<AT>::type &ak, const typename OpOf<BT>::type &bk,
+                                                int nk, bool swiglu, char *lds, AccW<WM, WN> &acc) {
+    using WG = WaveGrid<WM, WN>;
+    constexpr int MI = WG::MI, NI = WG::NI, NW = WG::NW;
+    constexpr int BKT = 64, SW = 3;
+    constexpr int tile_bytes = 256 * BKT * 2;
+    constexpr int GH = tile_bytes / 1024 / NW;
+    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+    const int wm = wave / WN, wn = wave % WN;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+    if (nk <= 0) return;
+    int brow[NI];  // block base (T) or this lane's row (K-contiguous) of each B block
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) brow[ni] = WG::brow(swiglu, wn, ni) + (BT ? 0 : (lane & 31));
+    const int arow = wm * (MI * 32) + (AT ? 0 : (lane & 31));
+    const uint16_t *asrc[GH], *bsrc[GH];
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+        if constexpr (AT) asrc[i] = dma_src_t<NW>(ak, i);
+        else asrc[i] = dma_src_w<BKT, SW, NW>(ak, i);
+        if constexpr (BT) bsrc[i] = dma_src_t<NW>(bk, i);
+        else bsrc[i] = dma_src_w<BKT, SW, NW>(bk, i);
+    }
+    int64_t astep, bstep;  // elements per K step
+    if constexpr (AT) astep = BKT * ak.ld;
+    else astep = BKT;
+    if constexpr (BT) bstep = BKT * bk.ld;
+    else bstep = BKT;
+    __syncthreads();  // the previous tile's epilogue may still read LDS
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+        dma_blk_x<NW>(asrc[i], lds, i);
+        dma_blk_x<NW>(bsrc[i], lds + tile_bytes, i);
+    }
+    int slot = 0;
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+        x_step<WM, WN, AT, BT, true, GH>(lds, slot, lane, arow, brow, asrc, bsrc, (int64_t)(kt + 1) * astep,
+                                         (int64_t)(kt + 1) * bstep, acc);
+        slot ^= 1;
+    }
+    x_step<WM, WN, AT, BT, false, GH>(lds, slot, lane, arow, brow, asrc, bsrc, 0, 0, acc);
     __syncthreads();
 }
 

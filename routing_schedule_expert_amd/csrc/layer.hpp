@@ -348,26 +348,28 @@ __device__ __forceinline__ void layer_fwd_persistent_body(const LayerFwdArgs &a,
 // Backward.
 // ---------------------------------------------------------------------------
 
+// The weights and the row activations are read as they lie: the data
+// gradients take W2[l] and W13[l] as MN-contiguous operands, the weight
+// gradients take the activation rows as MN-contiguous operands on both sides
+// (their K is the row index), so no transposed copy is made.
+// Data-gradient GEMMs: their B operand is MN-contiguous, and each of its
+// fragments takes two transposing LDS reads against one plain read for a
+// K-contiguous fragment, so the wave grid is 2 x 4 (4 A blocks, 2 B blocks
+// per wave) rather than the forward's 4 x 2: 8 LDS reads per sub-step, not 10.
+constexpr int kBwdWM = 2, kBwdWN = 4;
+
 struct BwdArgs {
     uint16_t *dOd, *dXd, *dHU;
+    uint16_t *dOw;  // dO_d rows times the row's router weight (B5's dW2 operand)
     float *wrow, *part;
     const uint16_t *Xd, *HU, *A, *W13, *W2;
     const int32_t *seg_off;
     float *dW13, *dW2;
-    // transposed operands: weights [L][I][H], [L][H][2I]; activations [.][ldT]
-    uint16_t *W2T, *W13T, *dYT, *AT, *dHUT, *XdT;
-    int64_t ldT;
     int L, H, I, nparts;
     int accumulate;  // B5 adds to dW13 / dW2 instead of overwriting them
 };
 
-// A K-contiguous window of up to 256 rows starting at `rows`; when only 128
-// rows exist the upper half repeats the lower one (its results are masked).
-__device__ __forceinline__ KOp rows_window(const uint16_t *rows, int64_t ld, int valid) {
-    return KOp{rows, valid > 128 ? rows + 128 * ld : rows, ld};
-}
-
-// B2: dA' = dO_d W2[l] (as dO_d . W2T[l]^T), SwiGLU backward in the epilogue.
+// B2: dA' = dO_d W2[l], SwiGLU backward in the epilogue.
 __device__ __forceinline__ void bwd_down_phase(const BwdArgs &a, char *lds) {
     const int H = a.H, I = a.I;
     const int npad = a.seg_off[a.L];
@@ -382,16 +384,16 @@ __device__ __forceinline__ void bwd_down_phase(const BwdArgs &a, char *lds) {
         const int l = expert_of(a.seg_off, a.L, m0);
         const uint16_t *g = a.dOd + (int64_t)m0 * H;
         const KOp ak{g, g + 128ll * H, H};
-        const KOp bk = rows_window(a.W2T + ((int64_t)l * I + nt * 256) * H, H, I - nt * 256);
-        AccW<kFwdWM, kFwdWN> acc;
-        gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, H / 64, false, lds, acc);
-        epilogue_swiglu_bwd_w<kFwdWM, kFwdWN>(acc, lds, a.A + (int64_t)m0 * I, a.HU + (int64_t)m0 * 2 * I, a.wrow + m0,
+        const TOp bk{a.W2 + (int64_t)l * H * I + nt * 256, I, min(256, I - nt * 256)};  // [k = h][i]
+        AccW<kBwdWM, kBwdWN> acc;
+        gemm_mainloop_x<kBwdWM, kBwdWN, false, true>(ak, bk, H / 64, false, lds, acc);
+        epilogue_swiglu_bwd_w<kBwdWM, kBwdWN>(acc, lds, a.A + (int64_t)m0 * I, a.HU + (int64_t)m0 * 2 * I, a.wrow + m0,
                                               a.dHU + (int64_t)m0 * 2 * I, a.part + (int64_t)m0 * a.nparts, a.nparts, I,
                                               nt * 256);
     }
 }
 
-// B3: dXd = dHU W13[l] (as dHU . W13T[l]^T).
+// B3: dXd = dHU W13[l].
 __device__ __forceinline__ void bwd_gateup_phase(const BwdArgs &a, char *lds) {
     const int H = a.H, I = a.I;
     const int npad = a.seg_off[a.L];
@@ -406,16 +408,16 @@ __device__ __forceinline__ void bwd_gateup_phase(const BwdArgs &a, char *lds) {
         const int l = expert_of(a.seg_off, a.L, m0);
         const uint16_t *g = a.dHU + (int64_t)m0 * 2 * I;
         const KOp ak{g, g + 128ll * 2 * I, 2ll * I};
-        const KOp bk = rows_window(a.W13T + ((int64_t)l * H + nt * 256) * 2 * I, 2ll * I, 256);
-        AccW<kFwdWM, kFwdWN> acc;
-        gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, 2 * I / 64, false, lds, acc);
-        epilogue_store_bf16_w<kFwdWM, kFwdWN>(acc, lds, a.dXd + (int64_t)m0 * H + nt * 256, H, 256);
+        const TOp bk{a.W13 + (int64_t)l * 2 * I * H + nt * 256, H, 256};  // [k = j][h]
+        AccW<kBwdWM, kBwdWN> acc;
+        gemm_mainloop_x<kBwdWM, kBwdWN, false, true>(ak, bk, 2 * I / 64, false, lds, acc);
+        epilogue_store_bf16_w<kBwdWM, kBwdWN>(acc, lds, a.dXd + (int64_t)m0 * H + nt * 256, H, 256);
     }
 }
 
 // B5: per expert, dW2[l] = sum_rows (w dO_d)^T a  and  dW13[l] = sum_rows dHU^T Xd,
-// as NT products of the transposed activations over the segment's rows
-// (ascending, inside one workgroup per output tile).  Longest segments first.
+// both operands the segment's activation rows read MN-contiguous (K = row,
+// ascending, inside one workgroup per output tile).  Longest segments first.
 // The reverse-dispatch sum `c` (B4, HBM-bound) shares the launch as 64-token
 // work items after the tiles ("Beyond Peak TFLOPs" section 2.C: the deferred
 // weight gradients overlap the last reverse-dispatch rounds).
@@ -441,7 +443,6 @@ __device__ __forceinline__ void wgrad_phase(const BwdArgs &a, const WindowCombin
     const int64_t ntiles = (int64_t)L * per;
     const int64_t ncb = c.Y ? (c.ntok + kCombineItem - 1) / kCombineItem : 0;
     const int64_t total = ntiles + ncb;
-    const int64_t ldT = a.ldT;
     for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
         const int64_t lid = logical_tile(it);
         if (lid >= total) continue;
@@ -459,17 +460,17 @@ __device__ __forceinline__ void wgrad_phase(const BwdArgs &a, const WindowCombin
         if (in < mt2 * nt2) {
             int mt, nt;
             grouped_mn(in, mt2, nt2, 4, mt, nt);
-            const KOp ak = rows_window(a.dYT + (int64_t)mt * 256 * ldT + S, ldT, 256);
-            const KOp bk = rows_window(a.AT + (int64_t)nt * 256 * ldT + S, ldT, I - nt * 256);
-            gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, kext / 64, false, lds, acc);
+            const TOp ak{a.dOw + (int64_t)S * H + mt * 256, H, 256};
+            const TOp bk{a.A + (int64_t)S * I + nt * 256, I, min(256, I - nt * 256)};
+            gemm_mainloop_x<kFwdWM, kFwdWN, true, true>(ak, bk, kext / 64, false, lds, acc);
             epilogue_store_f32_w<kFwdWM, kFwdWN>(acc, a.dW2 + (int64_t)l * H * I + (int64_t)mt * 256 * I + nt * 256, I,
                                                  256, I - nt * 256, a.accumulate);
         } else {
             int mt, nt;
             grouped_mn(in - mt2 * nt2, mt13, nt13, 4, mt, nt);
-            const KOp ak = rows_window(a.dHUT + (int64_t)mt * 256 * ldT + S, ldT, 256);
-            const KOp bk = rows_window(a.XdT + (int64_t)nt * 256 * ldT + S, ldT, 256);
-            gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, kext / 64, false, lds, acc);
+            const TOp ak{a.dHU + (int64_t)S * 2 * I + mt * 256, 2ll * I, 256};
+            const TOp bk{a.Xd + (int64_t)S * H + nt * 256, H, 256};
+            gemm_mainloop_x<kFwdWM, kFwdWN, true, true>(ak, bk, kext / 64, false, lds, acc);
             epilogue_store_f32_w<kFwdWM, kFwdWN>(acc, a.dW13 + (int64_t)l * 2 * I * H + (int64_t)mt * 256 * H + nt * 256,
                                                  H, 256, 256, a.accumulate);
         }

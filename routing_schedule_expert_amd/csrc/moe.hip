@@ -48,6 +48,14 @@ __global__ __launch_bounds__(256) void k_gather(const uint16_t *src, const moe_s
                      gridDim.x * waves);
 }
 
+__global__ __launch_bounds__(256) void k_gather_scaled(const uint16_t *src, const moe_src *phi,
+                                                       const int32_t *npad_ptr, const float *wrow, uint16_t *dst,
+                                                       uint16_t *dst_w, int Np, int H, int64_t cap) {
+    const int waves = blockDim.x / kWave;
+    gather_rows_scaled_body(src, phi, npad_ptr, wrow, dst, dst_w, Np, H, cap, blockIdx.x * waves + threadIdx.x / kWave,
+                            gridDim.x * waves);
+}
+
 __global__ __launch_bounds__(256) void k_combine(const uint16_t *Y, const int32_t *route_row, const float *w,
                                                  uint16_t *out, int K, int H, int64_t ntok, int tpp,
                                                  int64_t tstride, const uint16_t *S) {
@@ -135,12 +143,6 @@ template <int SG>
 __global__ __launch_bounds__(kFwdThreads) void k_mx_down(MxFfnArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kMxLds];
     mx_down_phase<SG>(a, lds);
-}
-
-__global__ __launch_bounds__(256) void k_transpose(TransposeArgs a) {
-    __shared__ uint16_t tile[64][72];
-    const int64_t ntiles = (int64_t)a.B * ((a.R + 63) / 64) * ((a.C + 63) / 64);
-    for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) transpose_tile(a, t, tile);
 }
 
 __global__ __launch_bounds__(kFwdThreads) void k_bwd_down(BwdArgs a) {
@@ -258,40 +260,12 @@ int64_t sched_ws_bytes(const moe_desc *d) { return align256(4ll * d->num_batches
 
 int bwd_nparts(const moe_desc *d) { return (d->I + 255) / 256; }  // one dw partial per 256-column tile
 
-// Leading dimension of the transposed activations (rows of length cap, padded
-// to 64 elements so every 16-byte access stays aligned).
-int64_t bwd_ldT(const moe_desc *d) { return (cap_rows(d) + 63) / 64 * 64; }
-
+// Backward workspace: dO_d, dXd, dO_d * w (bf16 [cap][H] each), dHU (bf16
+// [cap][2I]), the row weights and the dw partials (fp32).
 int64_t bwd_ws_bytes(const moe_desc *d) {
-    const int64_t cap = cap_rows(d), H = d->H, I = d->I, L = d->L, ldT = bwd_ldT(d);
-    return align256(cap * H * 2) * 2 + align256(cap * 2 * I * 2) + align256(cap * 4) +
-           align256(cap * 4ll * bwd_nparts(d)) + align256(L * I * H * 2) + align256(L * H * 2 * I * 2) +
-           align256(H * ldT * 2) * 2 + align256(I * ldT * 2) + align256(2 * I * ldT * 2);
-}
-
-int launch_transpose(const TransposeArgs &t, hipStream_t s, const char *name) {
-    const int64_t ntiles = (int64_t)t.B * ((t.R + 63) / 64) * ((t.C + 63) / 64);
-    const int grid = (int)std::min<int64_t>(ntiles, 64ll * device_cus());
-    TraceScope tr(name, s);
-    hipLaunchKernelGGL(k_transpose, dim3(grid), dim3(256), 0, s, t);
-    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
-}
-
-TransposeArgs make_transpose(const uint16_t *in, uint16_t *out, int32_t R, int32_t C, int32_t B, int64_t ldi,
-                             int64_t ldo, int64_t bsi, int64_t bso, const float *scale, const int32_t *nrows) {
-    TransposeArgs t;
-    t.in = in;
-    t.out = out;
-    t.scale = scale;
-    t.nrows_ptr = nrows;
-    t.ldi = ldi;
-    t.ldo = ldo;
-    t.bsi = bsi;
-    t.bso = bso;
-    t.R = R;
-    t.C = C;
-    t.B = B;
-    return t;
+    const int64_t cap = cap_rows(d), H = d->H, I = d->I;
+    return align256(cap * H * 2) * 3 + align256(cap * 2 * I * 2) + align256(cap * 4) +
+           align256(cap * 4ll * bwd_nparts(d));
 }
 
 constexpr int64_t kBarrierBytes = 256;
@@ -611,16 +585,19 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
     return launch_combine(d, Y, route_row, w, out, s, "combine");
 }
 
+}  // extern "C"
+
+namespace {
+
 // The backward of one table's rows.  d describes the tokens the table covers
 // (a window of tstride tokens per partition when tstride > d->Np: dOut, w,
 // route_row, dX and dw then point at the window's first token).  With
-// weights_ready the transposed weights are already in the workspace; with
 // accumulate the weight gradients are added to dW13 / dW2.
 int bwd_core(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const float *w, const moe_src *phi,
              const int32_t *route_row, const int32_t *seg_off, const uint16_t *Xd, const uint16_t *HU,
              const uint16_t *A, const uint16_t *W13, const uint16_t *W2, uint16_t *dX, float *dW13, float *dW2,
-             float *dw, char *ws, bool weights_ready, bool accumulate, hipStream_t s) {
-    const int64_t cap = cap_rows(d), H = d->H, I = d->I, L = d->L, ldT = bwd_ldT(d);
+             float *dw, char *ws, bool accumulate, hipStream_t s) {
+    const int64_t cap = cap_rows(d), H = d->H, I = d->I;
     const bool window = tstride > d->Np;
     char *p = ws;
     BwdArgs a;
@@ -628,24 +605,13 @@ int bwd_core(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const flo
     p += align256(cap * H * 2);
     a.dXd = reinterpret_cast<uint16_t *>(p);
     p += align256(cap * H * 2);
+    a.dOw = reinterpret_cast<uint16_t *>(p);
+    p += align256(cap * H * 2);
     a.dHU = reinterpret_cast<uint16_t *>(p);
     p += align256(cap * 2 * I * 2);
     a.wrow = reinterpret_cast<float *>(p);
     p += align256(cap * 4);
     a.part = reinterpret_cast<float *>(p);
-    p += align256(cap * 4ll * bwd_nparts(d));
-    a.W2T = reinterpret_cast<uint16_t *>(p);
-    p += align256(L * I * H * 2);
-    a.W13T = reinterpret_cast<uint16_t *>(p);
-    p += align256(L * H * 2 * I * 2);
-    a.dYT = reinterpret_cast<uint16_t *>(p);
-    p += align256(H * ldT * 2);
-    a.XdT = reinterpret_cast<uint16_t *>(p);
-    p += align256(H * ldT * 2);
-    a.AT = reinterpret_cast<uint16_t *>(p);
-    p += align256(I * ldT * 2);
-    a.dHUT = reinterpret_cast<uint16_t *>(p);
-    a.ldT = ldT;
     a.Xd = Xd;
     a.HU = HU;
     a.A = A;
@@ -661,24 +627,20 @@ int bwd_core(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const flo
     a.accumulate = accumulate ? 1 : 0;
     const int32_t *npad = seg_off + d->L;
     const int np_stride = window ? (int)tstride : d->Np;
-    // B1: reverse-combine gather of the output gradient
-    int rc = launch_gather(d, dOut, phi, seg_off, a.dOd, s, "bwd_gather", np_stride);
-    if (rc != MOE_OK) return rc;
     {
         TraceScope tr("bwd_row_weight", s);
         hipLaunchKernelGGL(k_row_weight, dim3((int)std::min<int64_t>((cap + 255) / 256, 4096)), dim3(256), 0, s, phi,
                            npad, route_row, w, a.wrow, np_stride, d->K, cap);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
-    if (!weights_ready) {
-        // weights transposed so both operands of every data-gradient GEMM are K-contiguous
-        rc = launch_transpose(make_transpose(W2, a.W2T, (int32_t)H, (int32_t)I, (int32_t)L, I, H, H * I, I * H,
-                                             nullptr, nullptr), s, "bwd_transpose_w2");
-        if (rc != MOE_OK) return rc;
-        rc = launch_transpose(make_transpose(W13, a.W13T, (int32_t)(2 * I), (int32_t)H, (int32_t)L, H, 2 * I,
-                                             2 * I * H, H * 2 * I, nullptr, nullptr), s, "bwd_transpose_w13");
-        if (rc != MOE_OK) return rc;
+    // B1: reverse-combine gather of the output gradient, and its rows times w
+    {
+        const int grid = (int)std::min<int64_t>((cap + 3) / 4, 16ll * device_cus());
+        TraceScope tr("bwd_gather", s);
+        hipLaunchKernelGGL(k_gather_scaled, dim3(grid), dim3(256), 0, s, dOut, phi, npad, a.wrow, a.dOd, a.dOw,
+                           np_stride, d->H, cap);
     }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
     const int grid = gemm_grid();
     // B2: down-projection dgrad with the SwiGLU backward and dw partials
     {
@@ -700,20 +662,6 @@ int bwd_core(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const flo
         hipLaunchKernelGGL(k_bwd_gateup, dim3(grid), dim3(kFwdThreads), 0, s, a);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
-    // activations transposed (rows [0, Npad)) so the weight gradients reduce
-    // over K-contiguous rows; the router weight is folded into dO_d here
-    rc = launch_transpose(make_transpose(a.dOd, a.dYT, (int32_t)cap, (int32_t)H, 1, H, ldT, 0, 0, a.wrow, npad), s,
-                          "bwd_transpose_dy");
-    if (rc != MOE_OK) return rc;
-    rc = launch_transpose(make_transpose(A, a.AT, (int32_t)cap, (int32_t)I, 1, I, ldT, 0, 0, nullptr, npad), s,
-                          "bwd_transpose_a");
-    if (rc != MOE_OK) return rc;
-    rc = launch_transpose(make_transpose(a.dHU, a.dHUT, (int32_t)cap, (int32_t)(2 * I), 1, 2 * I, ldT, 0, 0, nullptr,
-                                         npad), s, "bwd_transpose_dhu");
-    if (rc != MOE_OK) return rc;
-    rc = launch_transpose(make_transpose(Xd, a.XdT, (int32_t)cap, (int32_t)H, 1, H, ldT, 0, 0, nullptr, npad), s,
-                          "bwd_transpose_xd");
-    if (rc != MOE_OK) return rc;
     // B5: weight gradients, after every data gradient, fixed row order, in one
     // launch with B4, the reverse-dispatch sum over each token's local slots
     WindowCombine rd{};
@@ -730,6 +678,10 @@ int bwd_core(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const flo
     hipLaunchKernelGGL(k_wgrad, dim3(grid), dim3(kFwdThreads), 0, s, a, rd);
     return launch_status();
 }
+
+}  // namespace
+
+extern "C" {
 
 int moe_layer_fwd_shared(const moe_desc *d, int32_t Is, const int32_t *routes, const float *w, const uint16_t *X,
                          const uint16_t *W13, const uint16_t *W2, const uint16_t *W13s, const uint16_t *W2s,
@@ -798,7 +750,7 @@ int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes
     if ((int64_t)ws_bytes < bwd_ws_bytes(d)) return MOE_ENOSPC;
     (void)routes;
     return bwd_core(d, 0, dOut, w, phi, route_row, seg_off, Xd, HU, A, W13, W2, dX, dW13, dW2, dw,
-                    static_cast<char *>(ws), false, false, static_cast<hipStream_t>(stream));
+                    static_cast<char *>(ws), false, static_cast<hipStream_t>(stream));
 }
 
 int moe_quantize_mx(const uint16_t *src, int64_t rows, int32_t K, uint8_t *q, uint8_t *scales, void *stream) {
@@ -1023,7 +975,7 @@ int moe_layer_bwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots,
         rc = launch_gather(&d1, X + t0 * H, ph, so, Xd, s, "ring_bwd_gather_x", (int)Np);
         if (rc != MOE_OK) return rc;
         rc = bwd_core(&d1, Np, dOut + t0 * H, w + t0 * K, ph, route_row + t0 * K, so, Xd, hu, aa, W13, W2,
-                      dX + t0 * H, dW13, dW2, dw + t0 * K, core_ws, m > 0, m > 0, s);
+                      dX + t0 * H, dW13, dW2, dw + t0 * K, core_ws, m > 0, s);
         if (rc != MOE_OK) return rc;
     }
     return MOE_OK;

@@ -55,6 +55,49 @@ __device__ __forceinline__ int64_t window_token(int64_t g, int tpp, int64_t tstr
     return tpp ? (g / tpp) * tstride + g % tpp : g;
 }
 
+// The backward's reverse-combine gather: rows [0, Npad) of dst get
+// src[phi.part][phi.tok] (zeros on padding) and rows of dst_w the same row
+// times wrow[row], each element rounded once to bf16 (the weight gradient's
+// operand, so the router weight is applied once per row, not per product).
+__device__ void gather_rows_scaled_body(const uint16_t *__restrict__ src, const moe_src *__restrict__ phi,
+                                        const int32_t *__restrict__ npad_ptr, const float *__restrict__ wrow,
+                                        uint16_t *__restrict__ dst, uint16_t *__restrict__ dst_w, int Np, int H,
+                                        int64_t row_end_cap, int wave_global, int nwaves) {
+    const int lane = lane_id();
+    const int64_t npad = min((int64_t)*npad_ptr, row_end_cap);
+    const int chunks = H / 8;
+    for (int64_t row = wave_global; row < npad; row += nwaves) {
+        const uint2 s = reinterpret_cast<const uint2 *>(phi)[row];
+        const int32_t part = (int32_t)s.x, tok = (int32_t)s.y;
+        u32x4 *out = reinterpret_cast<u32x4 *>(dst + row * (int64_t)H);
+        u32x4 *outw = reinterpret_cast<u32x4 *>(dst_w + row * (int64_t)H);
+        if (part < 0) {
+            for (int c = lane; c < chunks; c += kWave) out[c] = outw[c] = u32x4{0, 0, 0, 0};
+            continue;
+        }
+        const float sc = wrow[row];
+        const u32x4 *in = reinterpret_cast<const u32x4 *>(src + ((int64_t)part * Np + tok) * H);
+        for (int c0 = lane; c0 < chunks; c0 += kRowUnroll * kWave) {
+            u32x4 v[kRowUnroll];
+#pragma unroll
+            for (int u = 0; u < kRowUnroll; ++u)
+                if (c0 + u * kWave < chunks) v[u] = __builtin_nontemporal_load(in + c0 + u * kWave);
+#pragma unroll
+            for (int u = 0; u < kRowUnroll; ++u) {
+                const int c = c0 + u * kWave;
+                if (c < chunks) {
+                    out[c] = v[u];
+                    u32x4 x;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        x[e] = pack_bf2(__uint_as_float(v[u][e] << 16) * sc, __uint_as_float(v[u][e] & 0xffff0000u) * sc);
+                    outw[c] = x;
+                }
+            }
+        }
+    }
+}
+
 // out[g] = sum_{j asc, rows[g][j] >= 0} w[g][j] * Y[rows[g][j]] (+ S[g]) for
 // tokens g in [g_begin, g_end) (through window_token when tpp > 0: route_row,
 // w and out then point at the window's first token of partition 0); one wave
@@ -148,67 +191,6 @@ __device__ void dw_finalize_body(const int32_t *__restrict__ route_row, const fl
         for (int q = 0; q < nparts; ++q) s += p[q];
     }
     dw[slot] = s;
-}
-
-// Tiled bf16 transpose: out[b][c][r] = in[b][r][c] * scale[b*rscale + r] (no
-// scale if scale == nullptr), for rows r < nrows and columns c < C.  A
-// workgroup of 256 threads moves one 64 x 64 tile through LDS: rows are read
-// and columns written with 16-byte accesses.  nrows_ptr (device, nullable)
-// caps the rows at run time.
-struct TransposeArgs {
-    const uint16_t *in;
-    uint16_t *out;
-    const float *scale;
-    const int32_t *nrows_ptr;
-    int64_t ldi, ldo, bsi, bso;  // row strides and batch strides (elements)
-    int32_t R, C, B;
-};
-
-__device__ __forceinline__ void transpose_tile(const TransposeArgs &a, int64_t tile, uint16_t (*lds)[72]) {
-    const int ct = (a.C + 63) / 64, rt = (a.R + 63) / 64;
-    const int b = (int)(tile / ((int64_t)ct * rt));
-    const int rem = (int)(tile % ((int64_t)ct * rt));
-    const int r0 = (rem / ct) * 64, c0 = (rem % ct) * 64;
-    int nrows = a.R;
-    if (a.nrows_ptr) nrows = min(nrows, *a.nrows_ptr);
-    if (r0 >= nrows) return;
-    const uint16_t *in = a.in + (int64_t)b * a.bsi;
-    uint16_t *out = a.out + (int64_t)b * a.bso;
-    const int t = threadIdx.x;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int rr = (t >> 3) + 32 * i, cc = (t & 7) * 8;
-        const int r = r0 + rr, c = c0 + cc;
-        u32x4 v = u32x4{0, 0, 0, 0};
-        if (r < nrows && c < a.C) v = *reinterpret_cast<const u32x4 *>(in + (int64_t)r * a.ldi + c);
-        float sc = 1.0f;
-        if (a.scale && r < nrows) sc = a.scale[(int64_t)b * a.R + r];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            uint32_t x = v[d];
-            if (a.scale) x = pack_bf2(__uint_as_float(x << 16) * sc, __uint_as_float(x & 0xffff0000u) * sc);
-            lds[cc + 2 * d][rr] = (uint16_t)(x & 0xffffu);
-            lds[cc + 2 * d + 1][rr] = (uint16_t)(x >> 16);
-        }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int cc = (t >> 3) + 32 * i, rr = (t & 7) * 8;
-        const int r = r0 + rr, c = c0 + cc;
-        if (c < a.C && r < nrows) {
-            const uint16_t *src = &lds[cc][rr];
-            u32x4 v;
-#pragma unroll
-            for (int d = 0; d < 4; ++d) v[d] = (uint32_t)src[2 * d] | ((uint32_t)src[2 * d + 1] << 16);
-            if (r + 8 <= nrows) {
-                *reinterpret_cast<u32x4 *>(out + (int64_t)c * a.ldo + r) = v;
-            } else {
-                for (int e = 0; r + e < nrows; ++e) out[(int64_t)c * a.ldo + r + e] = src[e];
-            }
-        }
-    }
 }
 
 }  // namespace moe
