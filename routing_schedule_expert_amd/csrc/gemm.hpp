@@ -145,100 +145,6 @@ __device__ __forceinline__ void dma_blk_w(const uint16_t *src, int k0, char *til
                                      0, 0);
 }
 
-// Main loop with NST stages of BKT.  The DMA instructions that fill stage
-// kt+NST-1 are not issued in one burst after the barrier: they are spread
-// over the first SPREAD sub-steps of stage kt, one after every few MFMAs
-// (pinned there with sched_group_barrier), so a wave blocked on a full
-// vector-memory queue still has MFMAs of its own in flight and the two waves
-// of a SIMD keep the matrix unit busy.  Measured at the gate/up shape: about
-// 10% faster than the burst.
-template <int WM, int WN, int BKT, int NST, int SW, int LDS_BYTES = kGemmLds, int SPREAD = 2>
-__device__ __forceinline__ void gemm_mainloop_w(const KOp &ak, const KOp &bk, int nk, bool swiglu, char *lds,
-                                                AccW<WM, WN> &acc) {
-    using WG = WaveGrid<WM, WN>;
-    constexpr int MI = WG::MI, NI = WG::NI, NW = WG::NW;
-    constexpr int tile_bytes = 256 * BKT * 2;
-    constexpr int stage_bytes = 2 * tile_bytes;
-    constexpr int GH = tile_bytes / 1024 / NW;  // DMA instructions per wave per operand per stage
-    constexpr int G = 2 * GH;
-    constexpr int S = BKT / 16;                 // MFMA sub-steps per stage
-    static_assert(SPREAD >= 1 && SPREAD <= S && G % SPREAD == 0, "DMA spread");
-    constexpr int D = G / SPREAD;               // DMA instructions per sub-step
-    static_assert((MI * NI) % D == 0, "DMA slots");
-    constexpr int EVERY = MI * NI / D;          // MFMAs between two DMA instructions
-    static_assert(NST >= 2 && NST * stage_bytes <= LDS_BYTES, "LDS budget");
-    const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-    const int wm = wave / WN, wn = wave % WN;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
-    if (nk <= 0) return;
-    int brow[NI];
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) brow[ni] = WG::brow(swiglu, wn, ni) + (lane & 31);
-    const int arow = wm * (MI * 32) + (lane & 31);
-    const uint16_t *asrc[GH], *bsrc[GH];
-#pragma unroll
-    for (int i = 0; i < GH; ++i) {
-        asrc[i] = dma_src_w<BKT, SW, NW>(ak, i);
-        bsrc[i] = dma_src_w<BKT, SW, NW>(bk, i);
-    }
-    __syncthreads();  // the previous tile's epilogue may still read LDS
-#pragma unroll
-    for (int s = 0; s < NST - 1; ++s)
-        if (s < nk) {
-#pragma unroll
-            for (int i = 0; i < GH; ++i) {
-                dma_blk_w<BKT, NW>(asrc[i], s * BKT, lds + s * stage_bytes, i);
-                dma_blk_w<BKT, NW>(bsrc[i], s * BKT, lds + s * stage_bytes + tile_bytes, i);
-            }
-        }
-    int slot = 0;
-    for (int kt = 0; kt < nk; ++kt) {
-        if (kt + NST - 2 < nk) wait_vm_barrier<G * (NST - 2)>();
-        else wait_vm_barrier<0>();
-        const int ahead = kt + NST - 1;
-        const bool fill = ahead < nk;
-        int as = slot + NST - 1;
-        if (as >= NST) as -= NST;
-        char *dst = lds + as * stage_bytes;
-        const char *stage = lds + slot * stage_bytes;
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-            const int kc = 2 * s + (lane >> 5);
-            bf16x8 fa[MI], fb[NI];
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-                fa[mi] = *reinterpret_cast<const bf16x8 *>(stage + tile_off_t<BKT, SW>(arow + mi * 32, kc));
-#pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
-                fb[ni] = *reinterpret_cast<const bf16x8 *>(stage + tile_bytes + tile_off_t<BKT, SW>(brow[ni], kc));
-#pragma unroll
-            for (int q = 0; q < MI * NI; ++q) {
-                acc[q / NI][q % NI] =
-                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[q / NI], fb[q % NI], acc[q / NI][q % NI], 0, 0, 0);
-                if (s < SPREAD && (q + 1) % EVERY == 0 && fill) {
-                    const int g = s * D + (q + 1) / EVERY - 1;
-                    if (g < GH) dma_blk_w<BKT, NW>(asrc[g], ahead * BKT, dst, g);
-                    else dma_blk_w<BKT, NW>(bsrc[g - GH], ahead * BKT, dst + tile_bytes, g - GH);
-                }
-            }
-            if (s < SPREAD) {
-#pragma unroll
-                for (int j = 0; j < D; ++j) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, EVERY, 0);  // EVERY MFMAs
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // then one VMEM read (the DMA)
-                }
-            }
-        }
-        if (++slot == NST) slot = 0;
-    }
-    __syncthreads();
-}
-
 // ---------------------------------------------------------------------------
 // Operands stored MN-contiguous ([k][mn]): the backward's products need
 // W2[l] and W13[l] along their rows, and the weight gradients reduce over the
@@ -450,11 +356,17 @@ __device__ __forceinline__ void x_step(char *lds, int slot, int lane, int arow, 
     }
 }
 
-// gemm_mainloop_w (K step 64, two stages, window swizzle, DMA spread over
-// two sub-steps) with either operand MN-contiguous: AT / BT select TOp
-// operands.  A K-contiguous operand's DMA moves k0 elements along its rows, an
-// MN-contiguous one's k0 rows.  The MFMA inputs, and so the results, are
-// those of the same product with transposed copies.
+// The bf16 main loop: K steps of 64, two stages double buffered in 128 KiB,
+// the window swizzle for K-contiguous operands.  The DMA instructions that
+// fill the next stage are not issued in one burst after the barrier: they are
+// spread over the MFMAs of the first two of the four 16-deep sub-steps
+// (pinned with sched_group_barrier), so a wave blocked on a full
+// vector-memory queue still has MFMAs of its own in flight and the two waves
+// of a SIMD keep the matrix unit busy (about 10% faster than the burst at the
+// gate/up shape).  Either operand may be MN-contiguous (AT / BT select TOp):
+// a K-contiguous operand's DMA moves 64 elements along its rows per step, an
+// MN-contiguous one's 64 rows; the MFMA inputs, and so the results, are those
+// of the same product with transposed copies.
 template <int WM, int WN, bool AT, bool BT>
 __device__ __forceinline__ void gemm_mainloop_x(const typename OpOf<AT>::type &ak, const typename OpOf<BT>::type &bk,
                                                 int nk, bool swiglu, char *lds, AccW<WM, WN> &acc) {

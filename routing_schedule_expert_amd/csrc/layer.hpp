@@ -60,7 +60,7 @@ __device__ __forceinline__ void ffn_gateup_tile(const FfnArgs &a, int mt, int nt
     }
     KOp bk{w + (int64_t)nt * 128 * H, w + ((int64_t)I + nt * 128) * H, H};
     AccW<kFwdWM, kFwdWN> acc;
-    gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, H / 64, true, lds, acc);
+    gemm_mainloop_x<kFwdWM, kFwdWN, false, false>(ak, bk, H / 64, true, lds, acc);
     uint16_t *hu = a.HU ? a.HU + (int64_t)m0 * 2 * I : nullptr;
     epilogue_swiglu_w<kFwdWM, kFwdWN>(acc, lds, a.A + (int64_t)m0 * I + nt * 128, I, hu ? hu + nt * 128 : nullptr,
                                       hu ? hu + I + nt * 128 : nullptr, 2ll * I);
@@ -75,7 +75,7 @@ __device__ __forceinline__ void ffn_down_tile(const FfnArgs &a, int mt, int nt, 
     KOp ak{aa, aa + 128ll * I, I};
     KOp bk{w, w + 128ll * I, I};
     AccW<kFwdWM, kFwdWN> acc;
-    gemm_mainloop_w<kFwdWM, kFwdWN, 64, 2, 3>(ak, bk, I / 64, false, lds, acc);
+    gemm_mainloop_x<kFwdWM, kFwdWN, false, false>(ak, bk, I / 64, false, lds, acc);
     epilogue_store_bf16_w<kFwdWM, kFwdWN>(acc, lds, a.Y + (int64_t)m0 * H + nt * 256, H, 256);
 }
 
