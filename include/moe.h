@@ -285,8 +285,10 @@ int moe_layer_fwd_mx(const moe_desc *d, const int32_t *routes, const float *w, c
  *   dW2   float [L][H][I]    out
  *   dw    float [P][Np][K]   out: router-weight gradient, 0 on non-local slots
  *   ws >= moe_workspace_bytes(d, MOE_OP_LAYER_BWD)
- * The workspace holds dO_d, dHU, dXd (bf16, cap rows each) and per-row partial
- * sums.  Every reduction has a fixed order.
+ * The workspace holds dO_d, dO_d times the row's router weight, dXd, dHU
+ * (bf16, cap rows each), the row weights and per-row partial sums; the weights
+ * and the saved activations are read where they lie (no transposed copies).
+ * Every reduction has a fixed order.
  */
 int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes, const float *w,
                   const moe_src *phi, const int32_t *route_row, const int32_t *seg_off,
