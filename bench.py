@@ -327,21 +327,22 @@ def bench_ring(args, torch, ops, inputs, dev):
     del b, bf, ws
     torch.cuda.empty_cache()
     for item in args.ring.split(","):
-        B, S = (int(x) for x in item.split(":"))
+        B, S, G = (int(x) for x in (item.split(":") + ["1"])[:3])
         M = c["Np"] // B
-        print(f"[bench] ring, {M} macrobatches of {B} tokens per partition, {S} slots", file=sys.stderr, flush=True)
+        print(f"[bench] ring, {M} macrobatches of {B} tokens per partition, {S} slots, weight gradients in groups "
+              f"of {G}", file=sys.stderr, flush=True)
         r = ops.alloc_ring(d, B, S, dev)
-        ws = torch.empty(ops.ring_workspace_bytes(d, B, ops.MOE_OP_LAYER_BWD), dtype=torch.uint8, device=dev)
+        ws = torch.empty(ops.ring_workspace_bytes(d, B, ops.MOE_OP_LAYER_BWD, G), dtype=torch.uint8, device=dev)
         fwd_ms, fwd_st = timed(lambda: ops.layer_fwd_ring(d, routes, w, h["X"], h["W13"], h["W2"], r), args.steps)
 
         def ring_step():
             ops.layer_fwd_ring(d, routes, w, h["X"], h["W13"], h["W2"], r)
             ops.moe_layer_bwd_ring(d, B, S, h["dOut"], w, h["X"], h["W13"], h["W2"], r.phi, r.route_row, r.seg_off,
-                                   r.HU, r.A, grads["dX"], grads["dW13"], grads["dW2"], grads["dw"], ws)
+                                   r.HU, r.A, grads["dX"], grads["dW13"], grads["dW2"], grads["dw"], ws, wgrad_group=G)
 
         fb_ms, fb_st = timed(ring_step, max(2, args.steps // 2))
         capm = ops.ring_capacity_rows(d, B)
-        res.append({"mb_tokens": B, "slots": S, "macrobatches": M, "fwd_ms": fwd_ms, "fwd_bwd_ms": fb_ms,
+        res.append({"mb_tokens": B, "slots": S, "wgrad_group": G, "macrobatches": M, "fwd_ms": fwd_ms, "fwd_bwd_ms": fb_ms,
                     "dispatched_rows": int(r.seg_off[:, -1].sum().item()), "replays": max(0, M - S),
                     "row_buffer_gb": (S * capm * 3 * I + capm * H) * 2 / 1e9, "fwd_stage_ms": fwd_st,
                     "replay_gateup_ms": fb_st.get("ring_replay_gateup", 0.0)})
@@ -575,8 +576,8 @@ def main():
                     help="kimi: the contract line (default); kimi_bwd / mid_tc / schedule / kimi_mx / kimi_ring / "
                          "kimi_shared: extra measurements")
     ap.add_argument("--shared-is", type=int, default=2048, help="--workload kimi_shared: shared intermediate size")
-    ap.add_argument("--ring", default="3584:1,3584:2,1024:2,1024:7",
-                    help="--workload kimi_ring: comma list of tokens-per-partition-per-macrobatch:slots")
+    ap.add_argument("--ring", default="3584:1:1,3584:2:1,3584:2:2,1024:2:1,1024:2:7,1024:7:7",
+                    help="--workload kimi_ring: comma list of tokens-per-partition-per-macrobatch:slots[:wgrad group]")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -314,8 +314,9 @@ int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes
  * means such an invalid d or mb_tokens.
  */
 int64_t moe_ring_capacity_rows(const moe_desc *d, int32_t mb_tokens);
-/* op = MOE_OP_LAYER_FWD or MOE_OP_LAYER_BWD (the two calls below). */
-int64_t moe_ring_workspace_bytes(const moe_desc *d, int32_t mb_tokens, int op);
+/* op = MOE_OP_LAYER_FWD or MOE_OP_LAYER_BWD (the two calls below);
+ * wgrad_group (1..16) matters for the backward only. */
+int64_t moe_ring_workspace_bytes(const moe_desc *d, int32_t mb_tokens, int32_t wgrad_group, int op);
 
 /*
  * moe_layer_fwd_ring — the layer forward through the ring.
@@ -347,21 +348,30 @@ int moe_layer_fwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots,
  * moe_layer_bwd_ring — the backward of moe_layer_fwd_ring, with the same
  * d, mb_tokens and ring_slots, and phi, route_row, seg_off, HU, A as that
  * call left them (X, W13, W2 unchanged since).
+ *   wgrad_group           1..16: macrobatches whose weight gradients are
+ *                         summed in one pass ([BPT] section 2.C: wgrads
+ *                         deferred after the dgrads, accumulated over the
+ *                         token dimension in one pass; wgrad_group >= M gives
+ *                         a single pass over all macrobatches)
  *   dOut, w, X, W13, W2   as moe_layer_bwd (X replaces the saved Xd)
  *   dX, dW13, dW2, dw     out, as moe_layer_bwd
- *   ws >= moe_ring_workspace_bytes(d, mb_tokens, MOE_OP_LAYER_BWD)
+ *   ws >= moe_ring_workspace_bytes(d, mb_tokens, wgrad_group, MOE_OP_LAYER_BWD)
+ *        (it keeps the weight-gradient rows of min(wgrad_group, M) macrobatches)
  * Macrobatches are taken in token order m = 0, 1, ...: those still in the
  * ring (m < ring_slots) use their slot; the others are replayed (their
  * gate/up GEMM recomputed from X into the workspace, bitwise the forward's
- * values).  dX and dw are bitwise equal to moe_layer_bwd's; the weight
- * gradients are summed per macrobatch and added in ascending m (a fixed
- * order, so reproducible, but rounded differently from moe_layer_bwd's
- * single pass).
+ * values).  dX and dw are bitwise equal to moe_layer_bwd's.  The weight
+ * gradients of a group are one K loop per output tile over the group's
+ * macrobatches in ascending m, and groups are added in ascending order (a
+ * fixed order, so reproducible, but rounded differently from moe_layer_bwd's
+ * single table).  Errors as moe_layer_fwd_ring, and MOE_EINVAL for a
+ * wgrad_group outside 1..16.
  */
-int moe_layer_bwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots, const uint16_t *dOut,
-                       const float *w, const uint16_t *X, const uint16_t *W13, const uint16_t *W2, const moe_src *phi,
-                       const int32_t *route_row, const int32_t *seg_off, const uint16_t *HU, const uint16_t *A,
-                       uint16_t *dX, float *dW13, float *dW2, float *dw, void *ws, size_t ws_bytes, void *stream);
+int moe_layer_bwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots, int32_t wgrad_group,
+                       const uint16_t *dOut, const float *w, const uint16_t *X, const uint16_t *W13,
+                       const uint16_t *W2, const moe_src *phi, const int32_t *route_row, const int32_t *seg_off,
+                       const uint16_t *HU, const uint16_t *A, uint16_t *dX, float *dW13, float *dW2, float *dw,
+                       void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Launch trace (optional, host side).  moe_trace_enable(n) records, for the

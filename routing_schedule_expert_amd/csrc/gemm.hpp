@@ -367,9 +367,11 @@ __device__ __forceinline__ void x_step(char *lds, int slot, int lane, int arow, 
 // a K-contiguous operand's DMA moves 64 elements along its rows per step, an
 // MN-contiguous one's 64 rows; the MFMA inputs, and so the results, are those
 // of the same product with transposed copies.
+// With zero == false the products are added to what acc holds (a K loop
+// continued over another range of rows).
 template <int WM, int WN, bool AT, bool BT>
 __device__ __forceinline__ void gemm_mainloop_x(const typename OpOf<AT>::type &ak, const typename OpOf<BT>::type &bk,
-                                                int nk, bool swiglu, char *lds, AccW<WM, WN> &acc) {
+                                                int nk, bool swiglu, char *lds, AccW<WM, WN> &acc, bool zero = true) {
     using WG = WaveGrid<WM, WN>;
     constexpr int MI = WG::MI, NI = WG::NI, NW = WG::NW;
     constexpr int BKT = 64, SW = 3;
@@ -377,12 +379,14 @@ __device__ __forceinline__ void gemm_mainloop_x(const typename OpOf<AT>::type &a
     constexpr int GH = tile_bytes / 1024 / NW;
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
     const int wm = wave / WN, wn = wave % WN;
+    if (zero) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
+            for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+                for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+    }
     if (nk <= 0) return;
     int brow[NI];  // block base (T) or this lane's row (K-contiguous) of each B block
 #pragma unroll

@@ -358,15 +358,15 @@ __device__ __forceinline__ void layer_fwd_persistent_body(const LayerFwdArgs &a,
 // per wave) rather than the forward's 4 x 2: 8 LDS reads per sub-step, not 10.
 constexpr int kBwdWM = 2, kBwdWN = 4;
 
+// The data-gradient GEMMs of one table (B2, B3).
 struct BwdArgs {
-    uint16_t *dOd, *dXd, *dHU;
-    uint16_t *dOw;  // dO_d rows times the row's router weight (B5's dW2 operand)
-    float *wrow, *part;
-    const uint16_t *Xd, *HU, *A, *W13, *W2;
+    const uint16_t *dOd;
+    uint16_t *dXd, *dHU;
+    const float *wrow;
+    float *part;
+    const uint16_t *HU, *A, *W13, *W2;
     const int32_t *seg_off;
-    float *dW13, *dW2;
     int L, H, I, nparts;
-    int accumulate;  // B5 adds to dW13 / dW2 instead of overwriting them
 };
 
 // B2: dA' = dO_d W2[l], SwiGLU backward in the epilogue.
@@ -415,22 +415,85 @@ __device__ __forceinline__ void bwd_gateup_phase(const BwdArgs &a, char *lds) {
     }
 }
 
-// B5: per expert, dW2[l] = sum_rows (w dO_d)^T a  and  dW13[l] = sum_rows dHU^T Xd,
-// both operands the segment's activation rows read MN-contiguous (K = row,
-// ascending, inside one workgroup per output tile).  Longest segments first.
-// The reverse-dispatch sum `c` (B4, HBM-bound) shares the launch as 64-token
-// work items after the tiles ("Beyond Peak TFLOPs" section 2.C: the deferred
-// weight gradients overlap the last reverse-dispatch rounds).
-__device__ __forceinline__ void wgrad_phase(const BwdArgs &a, const WindowCombine &c, char *lds) {
+// B5 operands: the activation rows of G tables (the backward of one table,
+// or of a group of macrobatches whose weight gradients are taken together).
+// Table g's buffers are at fixed strides from table 0's (kernel arguments are
+// not indexed at run time, which would copy them to scratch); its A rows are
+// either in a ring slot (bit g of a_in_ring) or at A + g * a_stride.
+constexpr int kMaxWgradGroup = 16;
+struct WgradArgs {
+    const uint16_t *dOw, *dHU, *Xd, *A;
+    int64_t stride;           // elements between consecutive tables' dOw, dHU, Xd and A buffers
+    const int32_t *seg_off;   // table g: seg_off + g * (L + 1)
+    const uint16_t *A_ring;   // ring slots of A, slot_elems apart
+    int64_t slot_elems;
+    int ring_slots, m0, M;    // table g is macrobatch m0 + g, in slot (M - 1 - m) % ring_slots
+    uint32_t a_in_ring;
+    int G;
+    float *dW13, *dW2;
+    int L, H, I;
+    int accumulate;  // add to dW13 / dW2 instead of overwriting them
+};
+
+__device__ __forceinline__ const uint16_t *wgrad_A(const WgradArgs &a, int g) {
+    if ((a.a_in_ring >> g) & 1u)
+        return a.A_ring + (int64_t)((a.M - 1 - (a.m0 + g)) % a.ring_slots) * a.slot_elems;
+    return a.A + g * a.stride;
+}
+
+// One output tile of dW2[l] (W2) or dW13[l]: the K loop over the expert's rows
+// of every table of the group, then the fp32 store.
+template <bool W2>
+__device__ __forceinline__ void wgrad_tile(const WgradArgs &a, int l, int mt, int nt, char *lds) {
     const int H = a.H, I = a.I, L = a.L;
+    AccW<kFwdWM, kFwdWN> acc;
+    for (int g = 0; g < a.G; ++g) {
+        const int32_t *so = a.seg_off + g * (L + 1);
+        const int S = so[l];
+        const int kext = so[l + 1] - S;  // padded: padding rows are zero in every operand
+        const int64_t off = g * a.stride;
+        if constexpr (W2) {
+            const TOp ak{a.dOw + off + (int64_t)S * H + mt * 256, H, 256};
+            const TOp bk{wgrad_A(a, g) + (int64_t)S * I + nt * 256, I, min(256, I - nt * 256)};
+            gemm_mainloop_x<kFwdWM, kFwdWN, true, true>(ak, bk, kext / 64, false, lds, acc, g == 0);
+        } else {
+            const TOp ak{a.dHU + off + (int64_t)S * 2 * I + mt * 256, 2ll * I, 256};
+            const TOp bk{a.Xd + off + (int64_t)S * H + nt * 256, H, 256};
+            gemm_mainloop_x<kFwdWM, kFwdWN, true, true>(ak, bk, kext / 64, false, lds, acc, g == 0);
+        }
+    }
+    if constexpr (W2)
+        epilogue_store_f32_w<kFwdWM, kFwdWN>(acc, a.dW2 + (int64_t)l * H * I + (int64_t)mt * 256 * I + nt * 256, I, 256,
+                                             I - nt * 256, a.accumulate);
+    else
+        epilogue_store_f32_w<kFwdWM, kFwdWN>(acc, a.dW13 + (int64_t)l * 2 * I * H + (int64_t)mt * 256 * H + nt * 256, H,
+                                             256, 256, a.accumulate);
+}
+
+// B5: per expert, dW2[l] = sum_rows (w dO_d)^T a  and  dW13[l] = sum_rows dHU^T Xd,
+// both operands the segment's activation rows read MN-contiguous (K = row).
+// The K loop of an output tile runs over the expert's rows of table 0, then
+// table 1, ... in ascending row order inside one workgroup, so the weight
+// gradients of a group of tables take one pass ("Beyond Peak TFLOPs"
+// section 2.C: deferred weight gradients accumulated over the token dimension
+// in one pass).  Longest experts first.  The reverse-dispatch sum `c` (B4,
+// HBM-bound) shares the launch as 64-token work items after the tiles (the
+// deferred weight gradients overlap the last reverse-dispatch rounds).
+__device__ __forceinline__ void wgrad_phase(const WgradArgs &a, const WindowCombine &c, char *lds) {
+    const int H = a.H, I = a.I, L = a.L, G = a.G;
     __shared__ int s_order[256];
     __syncthreads();
     if (L <= 256) {
         for (int l = threadIdx.x; l < L; l += blockDim.x) {
-            const int len = a.seg_off[l + 1] - a.seg_off[l];
+            auto total = [&](int e) {
+                int n = 0;
+                for (int g = 0; g < G; ++g) n += a.seg_off[g * (L + 1) + e + 1] - a.seg_off[g * (L + 1) + e];
+                return n;
+            };
+            const int len = total(l);
             int rank = 0;
             for (int q = 0; q < L; ++q) {
-                const int lq = a.seg_off[q + 1] - a.seg_off[q];
+                const int lq = total(q);
                 rank += (lq > len || (lq == len && q < l)) ? 1 : 0;
             }
             s_order[rank] = l;
@@ -454,25 +517,13 @@ __device__ __forceinline__ void wgrad_phase(const BwdArgs &a, const WindowCombin
         }
         const int pos = (int)(lid / per), in = (int)(lid % per);
         const int l = L <= 256 ? s_order[pos] : pos;
-        const int S = a.seg_off[l];
-        const int kext = a.seg_off[l + 1] - S;  // padded: padding rows are zero in every operand
-        AccW<kFwdWM, kFwdWN> acc;
+        int mt, nt;
         if (in < mt2 * nt2) {
-            int mt, nt;
             grouped_mn(in, mt2, nt2, 4, mt, nt);
-            const TOp ak{a.dOw + (int64_t)S * H + mt * 256, H, 256};
-            const TOp bk{a.A + (int64_t)S * I + nt * 256, I, min(256, I - nt * 256)};
-            gemm_mainloop_x<kFwdWM, kFwdWN, true, true>(ak, bk, kext / 64, false, lds, acc);
-            epilogue_store_f32_w<kFwdWM, kFwdWN>(acc, a.dW2 + (int64_t)l * H * I + (int64_t)mt * 256 * I + nt * 256, I,
-                                                 256, I - nt * 256, a.accumulate);
+            wgrad_tile<true>(a, l, mt, nt, lds);
         } else {
-            int mt, nt;
             grouped_mn(in - mt2 * nt2, mt13, nt13, 4, mt, nt);
-            const TOp ak{a.dHU + (int64_t)S * 2 * I + mt * 256, 2ll * I, 256};
-            const TOp bk{a.Xd + (int64_t)S * H + nt * 256, H, 256};
-            gemm_mainloop_x<kFwdWM, kFwdWN, true, true>(ak, bk, kext / 64, false, lds, acc);
-            epilogue_store_f32_w<kFwdWM, kFwdWN>(acc, a.dW13 + (int64_t)l * 2 * I * H + (int64_t)mt * 256 * H + nt * 256,
-                                                 H, 256, 256, a.accumulate);
+            wgrad_tile<false>(a, l, mt, nt, lds);
         }
     }
 }

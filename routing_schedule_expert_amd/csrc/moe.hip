@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kFwdThreads) void k_bwd_gateup(BwdArgs a) {
     bwd_gateup_phase(a, lds);
 }
 
-__global__ __launch_bounds__(kFwdThreads) void k_wgrad(BwdArgs a, WindowCombine c) {
+__global__ __launch_bounds__(kFwdThreads) void k_wgrad(WgradArgs a, WindowCombine c) {
     __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
     wgrad_phase(a, c, lds);
 }
@@ -589,55 +589,67 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
 
 namespace {
 
-// The backward of one table's rows.  d describes the tokens the table covers
-// (a window of tstride tokens per partition when tstride > d->Np: dOut, w,
-// route_row, dX and dw then point at the window's first token).  With
-// accumulate the weight gradients are added to dW13 / dW2.
-int bwd_core(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const float *w, const moe_src *phi,
-             const int32_t *route_row, const int32_t *seg_off, const uint16_t *Xd, const uint16_t *HU,
-             const uint16_t *A, const uint16_t *W13, const uint16_t *W2, uint16_t *dX, float *dW13, float *dW2,
-             float *dw, char *ws, bool accumulate, hipStream_t s) {
+// Per-table backward buffers: the gathered output gradient and its rows times
+// w, the row gradients, the row weights and the dw partials.
+struct BwdBufs {
+    uint16_t *dOd, *dOw, *dXd, *dHU;
+    float *wrow, *part;
+};
+
+BwdBufs carve_bwd(char *p, const moe_desc *d) {
     const int64_t cap = cap_rows(d), H = d->H, I = d->I;
-    const bool window = tstride > d->Np;
-    char *p = ws;
-    BwdArgs a;
-    a.dOd = reinterpret_cast<uint16_t *>(p);
+    BwdBufs b;
+    b.dOd = reinterpret_cast<uint16_t *>(p);
     p += align256(cap * H * 2);
-    a.dXd = reinterpret_cast<uint16_t *>(p);
+    b.dXd = reinterpret_cast<uint16_t *>(p);
     p += align256(cap * H * 2);
-    a.dOw = reinterpret_cast<uint16_t *>(p);
+    b.dOw = reinterpret_cast<uint16_t *>(p);
     p += align256(cap * H * 2);
-    a.dHU = reinterpret_cast<uint16_t *>(p);
+    b.dHU = reinterpret_cast<uint16_t *>(p);
     p += align256(cap * 2 * I * 2);
-    a.wrow = reinterpret_cast<float *>(p);
+    b.wrow = reinterpret_cast<float *>(p);
     p += align256(cap * 4);
-    a.part = reinterpret_cast<float *>(p);
-    a.Xd = Xd;
+    b.part = reinterpret_cast<float *>(p);
+    return b;
+}
+
+// The data gradients of one table's rows (B1, B2, dw, B3).  d describes the
+// tokens the table covers (a window of tstride tokens per partition when
+// tstride > d->Np: dOut, w, route_row and dw then point at the window's first
+// token).
+int bwd_dgrad(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const float *w, const moe_src *phi,
+              const int32_t *route_row, const int32_t *seg_off, const uint16_t *HU, const uint16_t *A,
+              const uint16_t *W13, const uint16_t *W2, float *dw, const BwdBufs &bb, hipStream_t s) {
+    const int64_t cap = cap_rows(d);
+    const bool window = tstride > d->Np;
+    BwdArgs a;
+    a.dOd = bb.dOd;
+    a.dXd = bb.dXd;
+    a.dHU = bb.dHU;
+    a.wrow = bb.wrow;
+    a.part = bb.part;
     a.HU = HU;
     a.A = A;
     a.W13 = W13;
     a.W2 = W2;
     a.seg_off = seg_off;
-    a.dW13 = dW13;
-    a.dW2 = dW2;
     a.L = d->L;
     a.H = d->H;
     a.I = d->I;
     a.nparts = bwd_nparts(d);
-    a.accumulate = accumulate ? 1 : 0;
     const int32_t *npad = seg_off + d->L;
     const int np_stride = window ? (int)tstride : d->Np;
     {
         TraceScope tr("bwd_row_weight", s);
         hipLaunchKernelGGL(k_row_weight, dim3((int)std::min<int64_t>((cap + 255) / 256, 4096)), dim3(256), 0, s, phi,
-                           npad, route_row, w, a.wrow, np_stride, d->K, cap);
+                           npad, route_row, w, bb.wrow, np_stride, d->K, cap);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
     // B1: reverse-combine gather of the output gradient, and its rows times w
     {
         const int grid = (int)std::min<int64_t>((cap + 3) / 4, 16ll * device_cus());
         TraceScope tr("bwd_gather", s);
-        hipLaunchKernelGGL(k_gather_scaled, dim3(grid), dim3(256), 0, s, dOut, phi, npad, a.wrow, a.dOd, a.dOw,
+        hipLaunchKernelGGL(k_gather_scaled, dim3(grid), dim3(256), 0, s, dOut, phi, npad, bb.wrow, bb.dOd, bb.dOw,
                            np_stride, d->H, cap);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
@@ -652,20 +664,22 @@ int bwd_core(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const flo
     {
         TraceScope tr("bwd_dw", s);
         hipLaunchKernelGGL(k_dw_finalize, dim3((int)std::min<int64_t>((nslots + 255) / 256, 4096)), dim3(256), 0, s,
-                           route_row, a.part, a.nparts, dw, nslots, window ? d->Np * d->K : 0,
+                           route_row, bb.part, a.nparts, dw, nslots, window ? d->Np * d->K : 0,
                            window ? tstride * d->K : (int64_t)0);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
     // B3: gate/up dgrad
-    {
-        TraceScope tr("bwd_gateup", s);
-        hipLaunchKernelGGL(k_bwd_gateup, dim3(grid), dim3(kFwdThreads), 0, s, a);
-    }
-    if (launch_status() != MOE_OK) return MOE_EHIP;
-    // B5: weight gradients, after every data gradient, fixed row order, in one
-    // launch with B4, the reverse-dispatch sum over each token's local slots
+    TraceScope tr("bwd_gateup", s);
+    hipLaunchKernelGGL(k_bwd_gateup, dim3(grid), dim3(kFwdThreads), 0, s, a);
+    return launch_status();
+}
+
+// B4 of one table: the reverse-dispatch sum of its tokens' row gradients.
+WindowCombine reverse_dispatch(const moe_desc *d, int64_t tstride, const uint16_t *dXd, const int32_t *route_row,
+                               uint16_t *dX) {
+    const bool window = tstride > d->Np;
     WindowCombine rd{};
-    rd.Y = a.dXd;
+    rd.Y = dXd;
     rd.route_row = route_row;
     rd.w = nullptr;
     rd.out = dX;
@@ -674,9 +688,42 @@ int bwd_core(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const flo
     rd.tpp = window ? d->Np : 0;
     rd.ntok = (int64_t)d->P * d->Np;
     rd.tstride = window ? tstride : 0;
+    return rd;
+}
+
+// B5 over the tables of `wa`, in one launch with the reverse dispatch `rd`
+// (Y == nullptr: none).
+int launch_wgrad(const WgradArgs &wa, const WindowCombine &rd, hipStream_t s) {
     TraceScope tr("bwd_wgrad_rdispatch", s);
-    hipLaunchKernelGGL(k_wgrad, dim3(grid), dim3(kFwdThreads), 0, s, a, rd);
+    hipLaunchKernelGGL(k_wgrad, dim3(gemm_grid()), dim3(kFwdThreads), 0, s, wa, rd);
     return launch_status();
+}
+
+// B5 arguments for table 0 at the given buffers; more tables follow at
+// `stride` elements (set by the caller).
+WgradArgs wgrad_args(const moe_desc *d, const uint16_t *dOw, const uint16_t *A, const uint16_t *dHU,
+                     const uint16_t *Xd, const int32_t *seg_off, float *dW13, float *dW2, bool accumulate) {
+    WgradArgs wa{};
+    wa.dOw = dOw;
+    wa.A = A;
+    wa.dHU = dHU;
+    wa.Xd = Xd;
+    wa.seg_off = seg_off;
+    wa.stride = 0;
+    wa.A_ring = nullptr;
+    wa.slot_elems = 0;
+    wa.ring_slots = 1;
+    wa.m0 = 0;
+    wa.M = 1;
+    wa.a_in_ring = 0;
+    wa.G = 1;
+    wa.dW13 = dW13;
+    wa.dW2 = dW2;
+    wa.L = d->L;
+    wa.H = d->H;
+    wa.I = d->I;
+    wa.accumulate = accumulate ? 1 : 0;
+    return wa;
 }
 
 }  // namespace
@@ -749,8 +796,12 @@ int moe_layer_bwd(const moe_desc *d, const uint16_t *dOut, const int32_t *routes
         if (!aligned16(p)) return MOE_EINVAL;
     if ((int64_t)ws_bytes < bwd_ws_bytes(d)) return MOE_ENOSPC;
     (void)routes;
-    return bwd_core(d, 0, dOut, w, phi, route_row, seg_off, Xd, HU, A, W13, W2, dX, dW13, dW2, dw,
-                    static_cast<char *>(ws), false, static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const BwdBufs bb = carve_bwd(static_cast<char *>(ws), d);
+    rc = bwd_dgrad(d, 0, dOut, w, phi, route_row, seg_off, HU, A, W13, W2, dw, bb, s);
+    if (rc != MOE_OK) return rc;
+    const WgradArgs wa = wgrad_args(d, bb.dOw, A, bb.dHU, Xd, seg_off, dW13, dW2, false);
+    return launch_wgrad(wa, reverse_dispatch(d, 0, bb.dXd, route_row, dX), s);
 }
 
 int moe_quantize_mx(const uint16_t *src, int64_t rows, int32_t K, uint8_t *q, uint8_t *scales, void *stream) {
@@ -843,10 +894,15 @@ int ring_check(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots, moe_des
     return check_desc(&dm, true);
 }
 
-int64_t ring_bwd_extra_bytes(const moe_desc *d1) {
-    const int64_t cap = cap_rows(d1);
-    return align256(cap * 2 * d1->I * 2) + align256(cap * d1->I * 2) + align256(cap * d1->H * 2);
+// Ring backward workspace: the per-table buffers (BwdBufs) of one macrobatch,
+// whose dO_d * w and dHU are then kept for each of the G macrobatches of a
+// weight-gradient group together with their X rows and replayed HU, A.
+int64_t ring_group_slot_bytes(const moe_desc *d1) {
+    const int64_t cap = cap_rows(d1), H = d1->H, I = d1->I;
+    return align256(cap * H * 2) * 2 + align256(cap * 2 * I * 2) * 2 + align256(cap * I * 2);
 }
+
+int64_t ring_bwd_bytes(const moe_desc *d1, int G) { return bwd_ws_bytes(d1) + G * ring_group_slot_bytes(d1); }
 
 }  // namespace
 
@@ -860,15 +916,15 @@ int64_t moe_ring_capacity_rows(const moe_desc *d, int32_t mb_tokens) {
     return cap_rows(&dm);
 }
 
-int64_t moe_ring_workspace_bytes(const moe_desc *d, int32_t mb_tokens, int op) {
+int64_t moe_ring_workspace_bytes(const moe_desc *d, int32_t mb_tokens, int32_t wgrad_group, int op) {
     moe_desc dm;
     int M;
     if (ring_check(d, mb_tokens, 1, dm, M) != MOE_OK) return -1;
     moe_desc d1 = dm;
     d1.num_batches = 1;
     if (op == MOE_OP_LAYER_FWD) return kBarrierBytes + sched_ws_bytes(&dm);
-    if (op == MOE_OP_LAYER_BWD) return bwd_ws_bytes(&d1) + ring_bwd_extra_bytes(&d1);
-    return -1;
+    if (op != MOE_OP_LAYER_BWD || wgrad_group < 1 || wgrad_group > kMaxWgradGroup) return -1;
+    return ring_bwd_bytes(&d1, std::min(wgrad_group, M));
 }
 
 int moe_layer_fwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots, const int32_t *routes,
@@ -882,7 +938,7 @@ int moe_layer_fwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots,
     const void *ptrs[] = {routes, w, X, W13, W2, counts, seg_off, phi, route_row, HU, A, Y, out, ws};
     for (const void *p : ptrs)
         if (!p || !aligned16(p)) return MOE_EINVAL;
-    if ((int64_t)ws_bytes < moe_ring_workspace_bytes(d, mb_tokens, MOE_OP_LAYER_FWD)) return MOE_ENOSPC;
+    if ((int64_t)ws_bytes < moe_ring_workspace_bytes(d, mb_tokens, 1, MOE_OP_LAYER_FWD)) return MOE_ENOSPC;
     hipStream_t s = static_cast<hipStream_t>(stream);
     char *wsb = static_cast<char *>(ws);
     uint32_t *bar = reinterpret_cast<uint32_t *>(wsb);
@@ -928,30 +984,50 @@ int moe_layer_fwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots,
     return launch_combine(&d1, Y, route_row, w, out, s, "ring_combine", Np);  // macrobatch 0
 }
 
-int moe_layer_bwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots, const uint16_t *dOut,
-                       const float *w, const uint16_t *X, const uint16_t *W13, const uint16_t *W2, const moe_src *phi,
-                       const int32_t *route_row, const int32_t *seg_off, const uint16_t *HU, const uint16_t *A,
-                       uint16_t *dX, float *dW13, float *dW2, float *dw, void *ws, size_t ws_bytes, void *stream) {
+int moe_layer_bwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots, int32_t wgrad_group,
+                       const uint16_t *dOut, const float *w, const uint16_t *X, const uint16_t *W13,
+                       const uint16_t *W2, const moe_src *phi, const int32_t *route_row, const int32_t *seg_off,
+                       const uint16_t *HU, const uint16_t *A, uint16_t *dX, float *dW13, float *dW2, float *dw,
+                       void *ws, size_t ws_bytes, void *stream) {
     moe_desc dm;
     int M;
     int rc = ring_check(d, mb_tokens, ring_slots, dm, M);
     if (rc != MOE_OK) return rc;
+    if (wgrad_group < 1 || wgrad_group > kMaxWgradGroup) return MOE_EINVAL;
     const void *ptrs[] = {dOut, w, X, W13, W2, phi, route_row, seg_off, HU, A, dX, dW13, dW2, dw, ws};
     for (const void *p : ptrs)
         if (!p || !aligned16(p)) return MOE_EINVAL;
-    if ((int64_t)ws_bytes < moe_ring_workspace_bytes(d, mb_tokens, MOE_OP_LAYER_BWD)) return MOE_ENOSPC;
+    const int G = std::min<int>(wgrad_group, M);
+    if ((int64_t)ws_bytes < moe_ring_workspace_bytes(d, mb_tokens, wgrad_group, MOE_OP_LAYER_BWD)) return MOE_ENOSPC;
     hipStream_t s = static_cast<hipStream_t>(stream);
     moe_desc d1 = dm;
     d1.num_batches = 1;
     const int64_t capm = cap_rows(&d1), B = mb_tokens, K = d->K, H = d->H, I = d->I, L = d->L, Np = d->Np;
-    char *core_ws = static_cast<char *>(ws);
-    char *p = core_ws + bwd_ws_bytes(&d1);
-    uint16_t *HUr = reinterpret_cast<uint16_t *>(p);
-    p += align256(capm * 2 * I * 2);
-    uint16_t *Ar = reinterpret_cast<uint16_t *>(p);
-    p += align256(capm * I * 2);
-    uint16_t *Xd = reinterpret_cast<uint16_t *>(p);
+    BwdBufs bb = carve_bwd(static_cast<char *>(ws), &d1);
+    char *slots = static_cast<char *>(ws) + bwd_ws_bytes(&d1);
+    struct Slot {
+        uint16_t *dOw, *Xd, *dHU, *HUr, *Ar;
+    };
+    auto slot_of = [&](int j) {
+        char *p = slots + j * ring_group_slot_bytes(&d1);
+        Slot sl;
+        sl.dOw = reinterpret_cast<uint16_t *>(p);
+        p += align256(capm * H * 2);
+        sl.Xd = reinterpret_cast<uint16_t *>(p);
+        p += align256(capm * H * 2);
+        sl.dHU = reinterpret_cast<uint16_t *>(p);
+        p += align256(capm * 2 * I * 2);
+        sl.HUr = reinterpret_cast<uint16_t *>(p);
+        p += align256(capm * 2 * I * 2);
+        sl.Ar = reinterpret_cast<uint16_t *>(p);
+        return sl;
+    };
+    const Slot s0 = slot_of(0);
+    const int64_t slot_stride = ring_group_slot_bytes(&d1) / 2;  // elements between two slots' buffers
+    uint32_t a_in_ring = 0;
     for (int m = 0; m < M; ++m) {
+        const int j = m % G;  // this macrobatch's place in its weight-gradient group
+        const Slot sl = slot_of(j);
         const int64_t t0 = (int64_t)m * B;
         const int32_t *so = seg_off + (int64_t)m * (L + 1);
         const moe_src *ph = phi + (int64_t)m * capm;
@@ -961,22 +1037,51 @@ int moe_layer_bwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots,
             hu = HU + slot * capm * 2 * I;
             aa = A + slot * capm * I;
         } else {  // replay: the forward's gate/up of this macrobatch, from X through its table
-            FfnArgs fa = make_ffn_args(&d1, nullptr, W13, W2, so, HUr, Ar, nullptr, 0, nullptr, X + t0 * H, ph);
+            FfnArgs fa = make_ffn_args(&d1, nullptr, W13, W2, so, sl.HUr, sl.Ar, nullptr, 0, nullptr, X + t0 * H, ph);
             fa.Np = d->Np;
             {
                 TraceScope tr("ring_replay_gateup", s);
                 hipLaunchKernelGGL(k_ffn_gateup, dim3(gemm_grid()), dim3(kFwdThreads), 0, s, fa);
             }
             if (launch_status() != MOE_OK) return MOE_EHIP;
-            hu = HUr;
-            aa = Ar;
+            hu = sl.HUr;
+            aa = sl.Ar;
         }
         // the dispatched rows of X, for the gate/up weight gradient
-        rc = launch_gather(&d1, X + t0 * H, ph, so, Xd, s, "ring_bwd_gather_x", (int)Np);
+        rc = launch_gather(&d1, X + t0 * H, ph, so, sl.Xd, s, "ring_bwd_gather_x", (int)Np);
         if (rc != MOE_OK) return rc;
-        rc = bwd_core(&d1, Np, dOut + t0 * H, w + t0 * K, ph, route_row + t0 * K, so, Xd, hu, aa, W13, W2,
-                      dX + t0 * H, dW13, dW2, dw + t0 * K, core_ws, m > 0, s);
+        bb.dOw = sl.dOw;
+        bb.dHU = sl.dHU;
+        rc = bwd_dgrad(&d1, Np, dOut + t0 * H, w + t0 * K, ph, route_row + t0 * K, so, hu, aa, W13, W2, dw + t0 * K,
+                       bb, s);
         if (rc != MOE_OK) return rc;
+        if (m < ring_slots) a_in_ring |= 1u << j;
+        const WindowCombine rd = reverse_dispatch(&d1, Np, bb.dXd, route_row + t0 * K, dX + t0 * H);
+        if (j == G - 1 || m == M - 1) {
+            // the group's weight gradients in one pass (added in ascending group
+            // order), with this macrobatch's reverse dispatch
+            const int m0 = m - j;
+            WgradArgs wa = wgrad_args(&d1, s0.dOw, s0.Ar, s0.dHU, s0.Xd, seg_off + (int64_t)m0 * (L + 1), dW13, dW2,
+                                      m0 > 0);
+            wa.stride = slot_stride;
+            wa.A_ring = A;
+            wa.slot_elems = capm * I;
+            wa.ring_slots = ring_slots;
+            wa.m0 = m0;
+            wa.M = M;
+            wa.a_in_ring = a_in_ring;
+            wa.G = j + 1;
+            rc = launch_wgrad(wa, rd, s);
+            if (rc != MOE_OK) return rc;
+            a_in_ring = 0;
+        } else {
+            TraceScope tr("bwd_reverse_dispatch", s);
+            const int64_t ntok = rd.ntok;
+            const int grid = (int)std::min<int64_t>((ntok + 3) / 4, 16ll * device_cus());
+            hipLaunchKernelGGL(k_combine, dim3(grid), dim3(256), 0, s, rd.Y, rd.route_row, rd.w, rd.out, rd.K, rd.H,
+                               ntok, rd.tpp, rd.tstride, (const uint16_t *)nullptr);
+            if (launch_status() != MOE_OK) return MOE_EHIP;
+        }
     }
     return MOE_OK;
 }

@@ -78,9 +78,9 @@ def load() -> ctypes.CDLL:
         "moe_layer_bwd": (ctypes.c_int, [D] + [P] * 16 + [sz, P]),
         "moe_layer_fwd_shared": (ctypes.c_int, [D, i32] + [P] * 19 + [sz, P]),
         "moe_ring_capacity_rows": (i64, [D, i32]),
-        "moe_ring_workspace_bytes": (i64, [D, i32, ctypes.c_int]),
+        "moe_ring_workspace_bytes": (i64, [D, i32, i32, ctypes.c_int]),
         "moe_layer_fwd_ring": (ctypes.c_int, [D, i32, i32] + [P] * 14 + [sz, P]),
-        "moe_layer_bwd_ring": (ctypes.c_int, [D, i32, i32] + [P] * 15 + [sz, P]),
+        "moe_layer_bwd_ring": (ctypes.c_int, [D, i32, i32, i32] + [P] * 15 + [sz, P]),
         "moe_trace_enable": (ctypes.c_int, [ctypes.c_int]),
         "moe_trace_read": (ctypes.c_int, [P, P, ctypes.c_int]),
     }
@@ -307,8 +307,8 @@ def ring_capacity_rows(d: moe_desc, mb_tokens: int) -> int:
     return int(n)
 
 
-def ring_workspace_bytes(d: moe_desc, mb_tokens: int, op: int) -> int:
-    n = load().moe_ring_workspace_bytes(ctypes.byref(d), mb_tokens, op)
+def ring_workspace_bytes(d: moe_desc, mb_tokens: int, op: int, wgrad_group: int = 1) -> int:
+    n = load().moe_ring_workspace_bytes(ctypes.byref(d), mb_tokens, wgrad_group, op)
     if n < 0:
         raise MoeError(MOE_EINVAL, "moe_ring_workspace_bytes")
     return int(n)
@@ -324,8 +324,9 @@ def moe_layer_fwd_ring(d, mb_tokens, ring_slots, routes, w, X, W13, W2, counts, 
 
 
 def moe_layer_bwd_ring(d, mb_tokens, ring_slots, dOut, w, X, W13, W2, phi, route_row, seg_off, HU, A, dX, dW13, dW2,
-                       dw, ws, stream=None):
-    rc = load().moe_layer_bwd_ring(ctypes.byref(d), mb_tokens, ring_slots, _dev(dOut), _dev(w), _dev(X), _dev(W13),
+                       dw, ws, stream=None, wgrad_group=1):
+    rc = load().moe_layer_bwd_ring(ctypes.byref(d), mb_tokens, ring_slots, wgrad_group, _dev(dOut), _dev(w), _dev(X),
+                                   _dev(W13),
                                    _dev(W2), _dev(phi), _dev(route_row), _dev(seg_off), _dev(HU), _dev(A), _dev(dX),
                                    _dev(dW13), _dev(dW2), _dev(dw), _dev(ws), ws.numel() * ws.element_size(),
                                    _stream(stream, dOut))

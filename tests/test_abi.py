@@ -161,9 +161,14 @@ def test_ring_sizes_and_arguments_rejected_before_launch():
     assert ops.ring_capacity_rows(d, 7168) == ops.capacity_rows(d)
     for bad in (0, -1, 1000, 7169):  # must divide Np
         assert lib.moe_ring_capacity_rows(ctypes.byref(d), bad) == -1
-    assert lib.moe_ring_workspace_bytes(ctypes.byref(d), 1024, ops.MOE_OP_SCHEDULE) == -1
+    assert lib.moe_ring_workspace_bytes(ctypes.byref(d), 1024, 1, ops.MOE_OP_SCHEDULE) == -1
+    for bad_group in (0, 17):
+        assert lib.moe_ring_workspace_bytes(ctypes.byref(d), 1024, bad_group, ops.MOE_OP_LAYER_BWD) == -1
     wf = ops.ring_workspace_bytes(d, 1024, ops.MOE_OP_LAYER_FWD)
     wb = ops.ring_workspace_bytes(d, 1024, ops.MOE_OP_LAYER_BWD)
+    # each macrobatch of a weight-gradient group keeps its own rows; 7 macrobatches at most
+    w3, w7, w9 = (ops.ring_workspace_bytes(d, 1024, ops.MOE_OP_LAYER_BWD, g) for g in (3, 7, 9))
+    assert wb < w3 < w7 == w9
     capm = ops.ring_capacity_rows(d, 1024)
     assert wb >= capm * (7168 * 3 + 2048 * 3) * 2  # per-slot dO_d, dXd, Xd, dHU, replayed HU and A
     p = [_fake(0x10000 * (i + 1)) for i in range(20)]
@@ -171,13 +176,15 @@ def test_ring_sizes_and_arguments_rejected_before_launch():
     bwd = p[:15]  # 14 operands and the workspace
     for mb, slots in ((1000, 2), (0, 2), (1024, 0)):
         assert lib.moe_layer_fwd_ring(ctypes.byref(d), mb, slots, *fwd, wf, None) == ops.MOE_EINVAL
-        assert lib.moe_layer_bwd_ring(ctypes.byref(d), mb, slots, *bwd, wb, None) == ops.MOE_EINVAL
+        assert lib.moe_layer_bwd_ring(ctypes.byref(d), mb, slots, 1, *bwd, wb, None) == ops.MOE_EINVAL
     assert lib.moe_layer_fwd_ring(ctypes.byref(d), 1024, 2, *fwd[:4], None, *fwd[5:], wf, None) == ops.MOE_EINVAL
     assert lib.moe_layer_fwd_ring(ctypes.byref(d), 1024, 2, *fwd[:9], _fake(0x10004), *fwd[10:], wf,
                                   None) == ops.MOE_EINVAL
     assert lib.moe_layer_fwd_ring(ctypes.byref(d), 1024, 2, *fwd, wf - 1, None) == ops.MOE_ENOSPC
-    assert lib.moe_layer_bwd_ring(ctypes.byref(d), 1024, 2, *bwd[:14], None, wb, None) == ops.MOE_EINVAL
-    assert lib.moe_layer_bwd_ring(ctypes.byref(d), 1024, 2, *bwd, wb - 1, None) == ops.MOE_ENOSPC
+    assert lib.moe_layer_bwd_ring(ctypes.byref(d), 1024, 2, 1, *bwd[:14], None, wb, None) == ops.MOE_EINVAL
+    assert lib.moe_layer_bwd_ring(ctypes.byref(d), 1024, 2, 1, *bwd, wb - 1, None) == ops.MOE_ENOSPC
+    assert lib.moe_layer_bwd_ring(ctypes.byref(d), 1024, 2, 0, *bwd, 1 << 40, None) == ops.MOE_EINVAL
+    assert lib.moe_layer_bwd_ring(ctypes.byref(d), 1024, 2, 3, *bwd, w3 - 1, None) == ops.MOE_ENOSPC
     d2 = ops.make_desc(8, 7168, 8, 384, 48, H=65536 + 256, I=2048)
     assert lib.moe_layer_fwd_ring(ctypes.byref(d2), 1024, 2, *fwd, 1 << 40, None) == ops.MOE_EUNSUPPORTED
 

@@ -30,7 +30,7 @@ def ring_fwd(lay: Layer, B: int, S: int) -> ops.RingBuffers:
     return r
 
 
-def ring_bwd(lay: Layer, r: ops.RingBuffers):
+def ring_bwd(lay: Layer, r: ops.RingBuffers, G: int = 1):
     d, L, H, I = lay.d, lay.L, lay.H, lay.I
     g = {
         "dX": torch.empty_like(lay.X),
@@ -38,10 +38,10 @@ def ring_bwd(lay: Layer, r: ops.RingBuffers):
         "dW2": torch.empty((L, H, I), dtype=torch.float32, device=dev()),
         "dw": torch.empty((lay.P, lay.Np, lay.K), dtype=torch.float32, device=dev()),
     }
-    ws = torch.empty(ops.ring_workspace_bytes(d, r.mb_tokens, ops.MOE_OP_LAYER_BWD), dtype=torch.uint8,
+    ws = torch.empty(ops.ring_workspace_bytes(d, r.mb_tokens, ops.MOE_OP_LAYER_BWD, G), dtype=torch.uint8,
                      device=dev())
     ops.moe_layer_bwd_ring(d, r.mb_tokens, r.slots, lay.dOut, lay.w, lay.X, lay.W13, lay.W2, r.phi, r.route_row,
-                           r.seg_off, r.HU, r.A, g["dX"], g["dW13"], g["dW2"], g["dw"], ws)
+                           r.seg_off, r.HU, r.A, g["dX"], g["dW13"], g["dW2"], g["dw"], ws, wgrad_group=G)
     torch.cuda.synchronize()
     return g
 
@@ -103,12 +103,13 @@ def test_ring_forward_ragged_and_nonlocal():
     check_resident_slots(lay, r, std, 96, 2)
 
 
-@pytest.mark.parametrize("B,S", [(512, 1), (128, 1), (128, 4), (64, 3)])
-def test_ring_backward(B, S):
-    print(f"[ring] backward B={B} S={S}", flush=True)
+@pytest.mark.parametrize("B,S,G", [(512, 1, 1), (128, 1, 1), (128, 4, 1), (64, 3, 1), (128, 1, 4), (64, 3, 3),
+                                   (64, 2, 16)])
+def test_ring_backward(B, S, G):
+    print(f"[ring] backward B={B} S={S} G={G}", flush=True)
     lay = Layer(12, 4, 512, 16, 4, 8, 256, 256, routing="zipf", x_std=1.0)
     r = ring_fwd(lay, B, S)
-    g = ring_bwd(lay, r)
+    g = ring_bwd(lay, r, G)
     std = lay.fwd()
     gs = lay.bwd(std)
     assert torch.equal(g["dX"], gs["dX"])
@@ -118,7 +119,7 @@ def test_ring_backward(B, S):
         print(f"[ring] {name} vs single pass rel-L2 {err:.2e}", flush=True)
         assert err <= 1e-5
     check_bwd_full(lay, g)
-    g2 = ring_bwd(lay, r)  # the slots are read only: a second backward is bitwise the first
+    g2 = ring_bwd(lay, r, G)  # the slots are read only: a second backward is bitwise the first
     for name in g:
         assert torch.equal(g[name], g2[name]), name
 
@@ -128,7 +129,8 @@ def test_ring_kimi_shape():
     H=7168, I=2048, balanced routing) in 7 macrobatches of 1,024 tokens per
     partition through 2 slots: tables bit-exact, output bitwise the ring-less
     forward's, the backward's dX and dw bitwise the ring-less backward's, the
-    weight gradients within 1e-5 of the single pass."""
+    weight gradients (one pass over all 7 macrobatches) within 1e-5 of the
+    single table."""
     print("[ring] Kimi shape, 7 macrobatches, 2 slots", flush=True)
     c = dict(P=8, Np=7168, E=384, K=8, L=48, H=7168, I=2048)
     h = inputs.make_layer_inputs_device(5, c["P"], c["Np"], c["E"], c["K"], c["L"], c["H"], c["I"], dev(),
@@ -153,9 +155,9 @@ def test_ring_kimi_shape():
     dW13 = torch.empty((c["L"], 2 * c["I"], c["H"]), dtype=torch.float32, device=dev())
     dW2 = torch.empty((c["L"], c["H"], c["I"]), dtype=torch.float32, device=dev())
     dw = torch.empty((c["P"], c["Np"], c["K"]), dtype=torch.float32, device=dev())
-    ws = torch.empty(ops.ring_workspace_bytes(d, B, ops.MOE_OP_LAYER_BWD), dtype=torch.uint8, device=dev())
+    ws = torch.empty(ops.ring_workspace_bytes(d, B, ops.MOE_OP_LAYER_BWD, 7), dtype=torch.uint8, device=dev())
     ops.moe_layer_bwd_ring(d, B, S, h["dOut"], w, h["X"], h["W13"], h["W2"], r.phi, r.route_row, r.seg_off, r.HU,
-                           r.A, dX, dW13, dW2, dw, ws)
+                           r.A, dX, dW13, dW2, dw, ws, wgrad_group=7)
     torch.cuda.synchronize()
     del ws, r
     gs = {"dX": torch.empty_like(dX), "dW13": torch.empty_like(dW13), "dW2": torch.empty_like(dW2),
