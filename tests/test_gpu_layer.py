@@ -138,6 +138,26 @@ def test_fused_dispatch_vs_oracle():
     assert rel_l2(f64(b.out).reshape(out.shape), out) <= TOL
 
 
+def test_fused_dispatch_widest_rows():
+    """H = 32768, the widest row the fused dispatch supports (padding rows
+    read a static zero row of that many elements): bitwise the materialised
+    path, padding rows zero, output vs the oracle."""
+    print("[layer] fused dispatch, H = 32768", flush=True)
+    lay = Layer(14, 2, 64, 8, 2, 4, 32768, 128, routing="topk", x_std=0.02, grad=False)
+    a = lay.fwd(save_xd=True)
+    b = lay.fwd(save_xd=False)
+    s = lay.oracle_schedule()
+    assert torch.equal(a.out, b.out)
+    assert torch.equal(a.Y[: s.npad], b.Y[: s.npad])
+    real = s.phi[:, 0] >= 0
+    assert (~real).any() and not f64(b.Y[: s.npad])[~real].any()
+    h = lay.h
+    out = oracle.layer_fwd_tokens(h["routes"], h["w"], h["X"], h["W13"], h["W2"], L=lay.L)
+    err = rel_l2(f64(b.out).reshape(out.shape), out)
+    print(f"[layer] H=32768 out rel-L2 {err:.2e}", flush=True)
+    assert err <= TOL
+
+
 def test_forward_without_saved_hu():
     lay = Layer(5, 2, 300, 8, 2, 4, 256, 128)
     a = lay.fwd(save_hu=True)

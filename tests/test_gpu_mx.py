@@ -131,6 +131,14 @@ def test_mx_small_forward_multi_tile():
     check_mx_full(lay, lay.fwd())
 
 
+def test_mx_widest_rows():
+    """H = 65536 codes, the widest MX row (padding rows read the static zero
+    row as bytes): full check against the oracle's MX path."""
+    print("[mx] H = 65536", flush=True)
+    lay = MxLayer(15, 2, 64, 8, 2, 4, 65536, 128, routing="topk")
+    check_mx_full(lay, lay.fwd())
+
+
 def test_mx_repeat_bitwise():
     lay = MxLayer(8, 4, 500, 16, 4, 8, 512, 256, routing="zipf")
     a, b = lay.fwd(), lay.fwd()
