@@ -17,7 +17,6 @@ constexpr int kWave = 64;
 
 // Round-to-nearest-even float -> bf16 bits (v_cvt_pk_bf16_f32; NaN stays NaN).
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
-__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
     return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
 }

@@ -47,8 +47,6 @@ struct SchedArgs {
     int64_t bstride, pstride;
 };
 
-__device__ __forceinline__ int bit_length(uint32_t v) { return 32 - __builtin_clz(v | 1u); }
-
 // Workgroup index -> (batch, partition, first chunk).  For eight or more
 // batches the workgroups of one batch share an XCD (hardware deals workgroup
 // ids round-robin over the 8 XCDs), so its table rows merge in one L2.
@@ -145,31 +143,6 @@ __device__ void sched_finalize(const SchedArgs &a, int b, int32_t *smem) {
         acc += s_len[l];
     }
     if (threadIdx.x == blockDim.x - 1) so[L] = acc;  // the last thread's run ends at L
-}
-
-// Ranks one block of 1024 consecutive routes (16 steps of 64) of a wave:
-// for every step, the local expert id v of each lane, the mask of lanes with
-// the same v and the lane's rank among them.  Only the loaded ids are needed,
-// so all 16 steps are ranked before any counter is touched.
-struct BlockRank {
-    uint32_t v[kSchedUnroll];
-    uint64_t peers[kSchedUnroll];
-};
-
-__device__ __forceinline__ void rank_block(const SchedArgs &a, const int32_t *src, int32_t lo, int lane,
-                                           BlockRank &br) {
-    int32_t e[kSchedUnroll];
-    const int32_t *sb = src + lo;
-#pragma unroll
-    for (int u = 0; u < kSchedUnroll; ++u) {
-        const int32_t i = lo + u * kWave + lane;
-        e[u] = i < a.R ? __builtin_nontemporal_load(sb + u * kWave + lane) : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kSchedUnroll; ++u) {
-        br.v[u] = local_id(e[u], a.base, a.L);
-        br.peers[u] = match_lanes(br.v[u], a.nbits);
-    }
 }
 
 // Stage 1: per-chunk counts.  x is the workgroup's index in the schedule grid
