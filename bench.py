@@ -518,6 +518,86 @@ def bench_tc_sweep(args, torch, ops, inputs, dev):
             "sweep": rows}
 
 
+def bench_vendor_gemm(args, torch, ops, inputs, dev):
+    """Context for the grouped GEMMs: the vendor BLAS (torch -> hipBLASLt) on
+    the same shapes in the same process, next to this library's gate/up and
+    down launches of the Kimi-shaped layer forward.  The vendor products are
+    plain GEMMs (no SwiGLU, no gather, no HU copy), so they bound from above
+    what a library GEMM of these shapes reaches on this machine:
+      batched_nn     48 experts x 1,280 rows: X[l] (1280 x 7168) @ W[l] (7168 x 4096),
+                     one weight per expert, torch.bmm (weights stored K x N);
+      per_expert_nt  the same, as 48 products X[l] @ W[l]^T with W[l] stored
+                     4096 x 7168 (the layout of W13: both operands K-contiguous);
+      dense_nt       61,440 x 7168 @ (4096 x 7168)^T, one weight for all rows;
+      down_*         the down projection shapes (K = 2048, N = 7168)."""
+    print("[bench] this library's layer forward", file=sys.stderr, flush=True)
+    L_res = bench_layer(args, torch, ops, inputs, dev)
+    st = L_res["stage_ms"]
+    ours = {"ffn_gateup": {"ms": st["ffn_gateup"], "tflops": L_res["flops_gateup"] / st["ffn_gateup"] / 1e9},
+            "ffn_down": {"ms": st["ffn_down"], "tflops": L_res["flops_down"] / st["ffn_down"] / 1e9}}
+    del L_res
+    torch.cuda.empty_cache()
+    c = KIMI
+    L, Mb, H, I = c["L"], 1280, c["H"], c["I"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+
+    def randn(*shape, std):
+        return (torch.randn(*shape, device=dev, generator=g, dtype=torch.float32) * std).to(torch.bfloat16)
+
+    def timed(fn, flops):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        return {"ms": ms, "tflops": flops / ms / 1e9}
+
+    vendor = {}
+    fl_gu = 2.0 * L * Mb * H * 2 * I
+    fl_dn = 2.0 * L * Mb * I * H
+    print("[bench] vendor gate/up shapes", file=sys.stderr, flush=True)
+    Xb = randn(L, Mb, H, std=1.0)
+    Wkn = randn(L, H, 2 * I, std=0.02)  # stored K x N: bmm takes it without a transposed view
+    vendor["batched_nn"] = timed(lambda: torch.bmm(Xb, Wkn), fl_gu)
+    del Wkn
+    Wnk = randn(L, 2 * I, H, std=0.02)
+    outs = torch.empty(L, Mb, 2 * I, device=dev, dtype=torch.bfloat16)
+
+    def per_expert():
+        for l in range(L):
+            torch.matmul(Xb[l], Wnk[l].t(), out=outs[l])
+
+    vendor["per_expert_nt"] = timed(per_expert, fl_gu)
+    Xflat = Xb.view(L * Mb, H)
+    vendor["dense_nt"] = timed(lambda: torch.matmul(Xflat, Wnk[0].t()), fl_gu)
+    del Xb, Wnk, outs, Xflat
+    torch.cuda.empty_cache()
+    print("[bench] vendor down shapes", file=sys.stderr, flush=True)
+    Ab = randn(L, Mb, I, std=1.0)
+    W2kn = randn(L, I, H, std=0.02)
+    vendor["down_batched_nn"] = timed(lambda: torch.bmm(Ab, W2kn), fl_dn)
+    del W2kn
+    W2nk = randn(L, H, I, std=0.02)
+    outd = torch.empty(L, Mb, H, device=dev, dtype=torch.bfloat16)
+
+    def per_expert_down():
+        for l in range(L):
+            torch.matmul(Ab[l], W2nk[l].t(), out=outd[l])
+
+    vendor["down_per_expert_nt"] = timed(per_expert_down, fl_dn)
+    return {"metric": "grouped GEMM TFLOP/s vs the vendor BLAS on the same shapes (Kimi share, 1 GPU)",
+            "unit": "TFLOP/s", "steps": args.steps, "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "kimi_gemm_vendor_context", "experts": L, "rows_per_expert": Mb, "H": H, "I": I},
+            "this_library": ours, "vendor_blas": vendor,
+            "torch": torch.__version__, "hip": torch.version.hip}
+
+
 def cpu_baseline(L_res, torch, oracle, budget_s: float):
     """The oracle's per-token forward on a bounded sample of tokens."""
     c = KIMI
@@ -572,9 +652,11 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the layer steps, run one plain read+write kernel over this many MiB (counter scaling)")
     ap.add_argument("--workload", default="kimi",
-                    choices=["kimi", "kimi_bwd", "mid_tc", "schedule", "kimi_mx", "kimi_ring", "kimi_shared"],
+                    choices=["kimi", "kimi_bwd", "mid_tc", "schedule", "kimi_mx", "kimi_ring", "kimi_shared",
+                             "vendor_gemm"],
                     help="kimi: the contract line (default); kimi_bwd / mid_tc / schedule / kimi_mx / kimi_ring / "
-                         "kimi_shared: extra measurements")
+                         "kimi_shared: extra measurements; vendor_gemm: the vendor BLAS on the grouped GEMMs' "
+                         "shapes, for context")
     ap.add_argument("--shared-is", type=int, default=2048, help="--workload kimi_shared: shared intermediate size")
     ap.add_argument("--ring", default="3584:1:1,3584:2:1,3584:2:2,1024:2:1,1024:2:7,1024:7:7",
                     help="--workload kimi_ring: comma list of tokens-per-partition-per-macrobatch:slots[:wgrad group]")
@@ -610,6 +692,9 @@ def main():
         return
     if args.workload == "schedule":
         print(json.dumps(bench_schedule_sweep(args, torch, ops, inputs, dev)), flush=True)
+        return
+    if args.workload == "vendor_gemm":
+        print(json.dumps(bench_vendor_gemm(args, torch, ops, inputs, dev)), flush=True)
         return
     print("[bench] layer forward, Kimi shape", file=sys.stderr, flush=True)
     L_res = bench_layer(args, torch, ops, inputs, dev)
