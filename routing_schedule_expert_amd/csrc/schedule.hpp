@@ -185,17 +185,86 @@ __device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
     }
 }
 
-// Stage 4: scatter every route once.
-//
-// Per 1024-route block of a wave: (A) the local routes are compacted, in
-// index order, into an LDS list (ballot + masked popcount give each local lane
-// its slot; route_row is staged as -1); (B) the list is processed 64 entries
-// at a time: lanes holding the same expert find each other with one ballot
-// per bit of the expert id, the group leader advances the wave's running
-// count for that expert with an LDS atomic (integer, program order) and the
-// returned old value plus the lane's rank in its group is the ordinal o; then
-// p and the row follow and Phi[row] is written; (C) the staged route_row is
-// written back coalesced.  Only local routes pay for ranking and placement.
+// Places the routes of one block of kSchedBlock routes starting at route lo
+// of partition r: lane l holds the local ids v[u] (L = not local) of routes
+// lo + u * 64 + l.  (A) the local routes are compacted, in index order, into
+// an LDS list (ballot + masked popcount give each local lane its slot;
+// route_row is staged as -1); (B) the list is processed 64 entries at a time:
+// lanes holding the same expert find each other with one ballot per bit of
+// the expert id, the group leader advances the wave's running count for that
+// expert with an LDS atomic (integer, program order) and the returned old
+// value plus the lane's rank in its group is the ordinal o; then p and the row
+// follow and Phi[row] is written; (C) the staged route_row is written back
+// coalesced.  Only local routes pay for ranking and placement.
+__device__ __forceinline__ void place_block(const SchedArgs &a, const uint32_t (&v)[kSchedUnroll], int32_t lo, int r,
+                                            const int32_t *sM, const int32_t *sS, int32_t *run, int32_t *list,
+                                            int32_t *rowbuf, moe_src *phi, int32_t *rrow) {
+    const int lane = lane_id();
+    const int L = a.L, P = a.P, K = a.K;
+    const bool fast = P <= kSchedPMax;
+    int nloc = 0;
+#pragma unroll
+    for (int u = 0; u < kSchedUnroll; ++u) {
+        const bool local = v[u] < (uint32_t)L;
+        const uint64_t lm = ballot(local);
+        rowbuf[u * kWave + lane] = -1;
+        if (local) list[nloc + lanes_below(lm)] = (int32_t)((v[u] << 16) | (uint32_t)(u * kWave + lane));
+        nloc += __popcll(lm);
+    }
+    const int32_t t0 = lo / K;
+    const int32_t j0 = lo - t0 * K;
+    for (int c0 = 0; c0 < nloc; c0 += kWave) {
+        const bool valid = c0 + lane < nloc;
+        const int32_t ent = valid ? list[c0 + lane] : (int32_t)((uint32_t)L << 16);
+        const uint32_t e = (uint32_t)ent >> 16;
+        const int32_t ib = ent & 0xffff;  // index inside the block
+        const uint64_t peers = match_lanes(e, a.nbits);
+        const int rank = lanes_below(peers);
+        int32_t old = 0;
+        if (rank == 0 && valid)
+            old = __hip_atomic_fetch_add(run + e, (int32_t)__popcll(peers), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int32_t o = __shfl(old, (int)__builtin_ctzll(peers), kWave) + rank;
+        if (valid) {
+            int32_t p = 0;
+            if (fast) {
+                // min(m, o) + [m > o] = min(m, o + 1): partitions before r
+                // count up to o + 1, the others up to o (r is wave-uniform)
+                const int4 m0 = *reinterpret_cast<const int4 *>(sM + e * kSchedPMax);
+                const int4 m1 = *reinterpret_cast<const int4 *>(sM + e * kSchedPMax + 4);
+                const int32_t m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+                for (int rr = 0; rr < kSchedPMax; ++rr) p += min(m[rr], rr < r ? o + 1 : o);
+            } else {
+                const int32_t *Ml = sM + e * P;
+                for (int rr = 0; rr < P; ++rr) p += min(Ml[rr], rr < r ? o + 1 : o);
+            }
+            const int32_t row = sS[e] + p;
+            const int32_t jj = j0 + ib;  // slot offset from token t0, < K + 1024
+            const int32_t t = t0 + jj / K;
+            if ((uint32_t)row < (uint32_t)a.cap)  // always true for a consistent table
+                reinterpret_cast<uint2 *>(phi)[row] = make_uint2((uint32_t)r, (uint32_t)t);
+            rowbuf[ib] = row;
+        }
+    }
+    // (C) route rows of the block, coalesced
+    const int32_t nb_routes = min(kSchedBlock, a.R - lo);
+    for (int k = lane; k < nb_routes; k += kWave) rrow[lo + k] = rowbuf[k];
+}
+
+// Padding rows (-1, -1) of segments l = first, first + step, ... < L.
+__device__ __forceinline__ void pad_segments(const SchedArgs &a, const int32_t *sM, int mstride, const int32_t *sS,
+                                             moe_src *phi, int first, int step) {
+    for (int l = first; l < a.L; l += step) {
+        int32_t t = 0;
+        for (int rr = 0; rr < a.P; ++rr) t += sM[l * mstride + rr];
+        const int32_t hi = min(sS[l + 1], (int32_t)a.cap);  // sS[l + 1] <= cap for a consistent table
+        for (int32_t row = max(sS[l] + t, 0) + threadIdx.x; row < hi; row += blockDim.x)
+            reinterpret_cast<uint2 *>(phi)[row] = make_uint2(0xffffffffu, 0xffffffffu);
+    }
+}
+
+// Stage 4: place every route once (place_block per block of the chunk).
 __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
     int b, r, q;
     if (!sched_locate(a, x, b, r, q)) return;
@@ -203,9 +272,8 @@ __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
     const int lane = lane_id();
     const int wv = threadIdx.x / kWave;
     const int w = q * a.wpw + wv;
-    const int L = a.L, P = a.P, K = a.K;
-    const bool fast = P <= kSchedPMax;
-    const int mstride = fast ? kSchedPMax : P;
+    const int L = a.L, P = a.P;
+    const int mstride = P <= kSchedPMax ? kSchedPMax : P;
     // LDS: M [L][mstride] (zero-padded), S [L+1], then per wave: running
     // offsets [L], the compacted list [1024] and the staged route rows [1024]
     int32_t *sM = smem;
@@ -233,74 +301,21 @@ __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
         for (int blk = 0; blk < a.cb; ++blk) {
             const int32_t lo = (w * a.cb + blk) * kSchedBlock;
             if (lo >= a.R) break;
-            // (A) load, compact local routes in index order, stage route_row = -1
             int32_t e[kSchedUnroll];
 #pragma unroll
             for (int u = 0; u < kSchedUnroll; ++u) {
                 const int32_t i = lo + u * kWave + lane;
                 e[u] = i < a.R ? __builtin_nontemporal_load(src + i) : -1;
             }
-            int nloc = 0;
+            uint32_t v[kSchedUnroll];
 #pragma unroll
-            for (int u = 0; u < kSchedUnroll; ++u) {
-                const uint32_t v = local_id(e[u], a.base, L);
-                const bool local = v < (uint32_t)L;
-                const uint64_t lm = ballot(local);
-                rowbuf[u * kWave + lane] = -1;
-                if (local) list[nloc + lanes_below(lm)] = (int32_t)((v << 16) | (uint32_t)(u * kWave + lane));
-                nloc += __popcll(lm);
-            }
-            // (B) rank and place the local routes, 64 at a time
-            const int32_t t0 = lo / K;
-            const int32_t j0 = lo - t0 * K;
-            for (int c0 = 0; c0 < nloc; c0 += kWave) {
-                const bool valid = c0 + lane < nloc;
-                const int32_t ent = valid ? list[c0 + lane] : (int32_t)((uint32_t)L << 16);
-                const uint32_t v = (uint32_t)ent >> 16;
-                const int32_t ib = ent & 0xffff;  // index inside the block
-                const uint64_t peers = match_lanes(v, a.nbits);
-                const int rank = lanes_below(peers);
-                int32_t old = 0;
-                if (rank == 0 && valid)
-                    old = __hip_atomic_fetch_add(run + v, (int32_t)__popcll(peers), __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_WORKGROUP);
-                const int32_t o = __shfl(old, (int)__builtin_ctzll(peers), kWave) + rank;
-                if (valid) {
-                    int32_t p = 0;
-                    if (fast) {
-                        // min(m, o) + [m > o] = min(m, o + 1): partitions before r
-                        // count up to o + 1, the others up to o (r is wave-uniform)
-                        const int4 m0 = *reinterpret_cast<const int4 *>(sM + v * kSchedPMax);
-                        const int4 m1 = *reinterpret_cast<const int4 *>(sM + v * kSchedPMax + 4);
-                        const int32_t m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-#pragma unroll
-                        for (int rr = 0; rr < kSchedPMax; ++rr) p += min(m[rr], rr < r ? o + 1 : o);
-                    } else {
-                        const int32_t *Ml = sM + v * P;
-                        for (int rr = 0; rr < P; ++rr) p += min(Ml[rr], rr < r ? o + 1 : o);
-                    }
-                    const int32_t row = sS[v] + p;
-                    const int32_t jj = j0 + ib;  // slot offset from token t0, < K + 1024
-                    const int32_t t = t0 + jj / K;
-                    reinterpret_cast<uint2 *>(phi)[row] = make_uint2((uint32_t)r, (uint32_t)t);
-                    rowbuf[ib] = row;
-                }
-            }
-            // (C) route rows of the block, coalesced
-            const int32_t nb_routes = min(kSchedBlock, a.R - lo);
-            for (int k = lane; k < nb_routes; k += kWave) rrow[lo + k] = rowbuf[k];
+            for (int u = 0; u < kSchedUnroll; ++u) v[u] = local_id(e[u], a.base, L);
+            place_block(a, v, lo, r, sM, sS, run, list, rowbuf, phi, rrow);
         }
     }
-    // padding rows of the segments this workgroup owns: (-1, -1)
-    const int wg_in_batch = r * a.wg_per_part + q;
-    const int nwg = P * a.wg_per_part;
+    // padding rows of the segments this workgroup owns
     __syncthreads();
-    for (int l = wg_in_batch; l < L; l += nwg) {
-        int32_t t = 0;
-        for (int rr = 0; rr < P; ++rr) t += sM[l * mstride + rr];
-        for (int32_t row = sS[l] + t + threadIdx.x; row < sS[l + 1]; row += blockDim.x)
-            reinterpret_cast<uint2 *>(phi)[row] = make_uint2(0xffffffffu, 0xffffffffu);
-    }
+    pad_segments(a, sM, mstride, sS, phi, r * a.wg_per_part + q, P * a.wg_per_part);
 }
 
 }  // namespace moe

@@ -3,6 +3,7 @@
 The 16 named cases mirror the validation count of 'Scan once, scatter once'
 (realistic and adversarial routings); random cases and batched calls follow.
 Rows of Phi past Npad are never written (checked against a fill pattern).
+The workspace starts as a garbage pattern: nothing in it may be assumed clear.
 """
 import numpy as np
 import pytest
@@ -136,3 +137,30 @@ def test_repeatable():
     b = gpu_schedule(routes, L)
     for k in ("counts", "seg_off", "phi", "route_row"):
         np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_many_local_experts():
+    """300 local experts (9-bit expert ids in the lane matching), a nonzero base."""
+    rng = inputs.rng_for(301)
+    routes = rng.integers(-1, 640, size=(3, 700, 4)).astype(np.int32)
+    print("[schedule] L=300", flush=True)
+    check(routes, 300, base=20, E=640)
+
+
+def test_many_partitions():
+    """64 partitions x 110 local experts: the position formula's general loop
+    (more partitions than the unrolled 8), M staged at a stride of 64."""
+    rng = inputs.rng_for(302)
+    routes = rng.integers(0, 220, size=(64, 96, 2)).astype(np.int32)
+    print("[schedule] P=64 L=110", flush=True)
+    check(routes, 110, E=220)
+
+
+@pytest.mark.parametrize("nb", [8, 24])
+def test_batched_ragged_tables(nb):
+    """Eight or more tables (workgroups of a table kept on one XCD), partitions
+    whose route counts are not multiples of a logical thread's chunk."""
+    rng = inputs.rng_for(303 + nb)
+    r = np.stack([inputs.routes_zipf(rng, 5, 3333, 80, 3, 1.3)[0] for _ in range(nb)])
+    print(f"[schedule] batched ragged nb={nb}", flush=True)
+    check(r, 40, base=8, E=80)
