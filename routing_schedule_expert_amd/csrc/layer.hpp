@@ -294,7 +294,7 @@ __device__ __forceinline__ void ring_gateup_combine_body(const FfnArgs &a, const
             ffn_gateup_tile(a, m, n, lds);
         } else {
             const int64_t g0 = (lid - ngu) * kCombineItem;
-            combine_body(c.Y, c.route_row, c.w, c.out, c.K, c.H, g0, min(g0 + kCombineItem, c.ntok),
+            combine_body<kRowUnrollWide>(c.Y, c.route_row, c.w, c.out, c.K, c.H, g0, min(g0 + kCombineItem, c.ntok),
                          threadIdx.x / kWave, waves, c.tpp, c.tstride);
         }
     }
@@ -340,7 +340,7 @@ __device__ __forceinline__ void layer_fwd_persistent_body(const LayerFwdArgs &a,
         ffn_down_phase(a.ffn, 0, npad, lds);
         gb.sync();
     }
-    combine_body(a.ffn.Y, s.route_row, a.w, a.out, a.K, a.ffn.H, 0, a.ntok,
+    combine_body<kRowUnrollWide>(a.ffn.Y, s.route_row, a.w, a.out, a.K, a.ffn.H, 0, a.ntok,
                  blockIdx.x * waves + threadIdx.x / kWave, gridDim.x * waves);
 }
 
@@ -511,7 +511,7 @@ __device__ __forceinline__ void wgrad_phase(const WgradArgs &a, const WindowComb
         if (lid >= total) continue;
         if (lid >= ntiles) {
             const int64_t g0 = (lid - ntiles) * kCombineItem;
-            combine_body(c.Y, c.route_row, c.w, c.out, c.K, c.H, g0, min(g0 + kCombineItem, c.ntok),
+            combine_body<kRowUnrollWide>(c.Y, c.route_row, c.w, c.out, c.K, c.H, g0, min(g0 + kCombineItem, c.ntok),
                          threadIdx.x / kWave, blockDim.x / kWave, c.tpp, c.tstride);
             continue;
         }

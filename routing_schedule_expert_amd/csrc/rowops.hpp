@@ -17,6 +17,7 @@
 namespace moe {
 
 constexpr int kRowUnroll = 4;
+constexpr int kRowUnrollWide = 8;
 
 // Rows [0, Npad) of dst get src[phi.part][phi.tok] (or zeros on padding).
 // Persistent over rows: Npad is read on the device.
@@ -101,9 +102,14 @@ __device__ void gather_rows_scaled_body(const uint16_t *__restrict__ src, const 
 // out[g] = sum_{j asc, rows[g][j] >= 0} w[g][j] * Y[rows[g][j]] (+ S[g]) for
 // tokens g in [g_begin, g_end) (through window_token when tpp > 0: route_row,
 // w and out then point at the window's first token of partition 0); one wave
-// per token, kRowUnroll 16-byte chunks per lane in flight.  w == nullptr means
-// every weight is 1.  S (nullable, [tokens][H]) is the shared expert's output,
-// added after the slots, before the one rounding.
+// per token, U 16-byte chunks per lane in flight.  w == nullptr means every
+// weight is 1.  S (nullable, [tokens][H]) is the shared expert's output, added
+// after the slots, before the one rounding.
+// U trades registers for bytes in flight: the standalone combine kernel keeps
+// many waves per CU and U = kRowUnroll; a combine that runs inside a GEMM
+// kernel (eight waves per CU) takes U = kRowUnrollWide, a whole 7,168-wide
+// row per wave, so the CU still keeps enough row loads in flight.
+template <int U = kRowUnroll>
 __device__ void combine_body(const uint16_t *__restrict__ Y, const int32_t *__restrict__ route_row,
                              const float *__restrict__ w, uint16_t *__restrict__ out, int K, int H,
                              int64_t g_begin, int64_t g_end, int wave_global, int nwaves, int tpp = 0,
@@ -113,10 +119,10 @@ __device__ void combine_body(const uint16_t *__restrict__ Y, const int32_t *__re
     for (int64_t gw = g_begin + wave_global; gw < g_end; gw += nwaves) {
         const int64_t g = window_token(gw, tpp, tstride);
         u32x4 *o = reinterpret_cast<u32x4 *>(out + g * (int64_t)H);
-        for (int c0 = 0; c0 < chunks; c0 += kRowUnroll * kWave) {
-            float acc[kRowUnroll][8];
+        for (int c0 = 0; c0 < chunks; c0 += U * kWave) {
+            float acc[U][8];
 #pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u)
+            for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[u][e] = 0.f;
             for (int j = 0; j < K; ++j) {
@@ -124,14 +130,14 @@ __device__ void combine_body(const uint16_t *__restrict__ Y, const int32_t *__re
                 if (rw < 0) continue;
                 const float wq = w ? w[g * K + j] : 1.0f;
                 const u32x4 *yr = reinterpret_cast<const u32x4 *>(Y + (int64_t)rw * H);
-                u32x4 v[kRowUnroll];
+                u32x4 v[U];
 #pragma unroll
-                for (int u = 0; u < kRowUnroll; ++u) {
+                for (int u = 0; u < U; ++u) {
                     int c = c0 + u * kWave + lane;
                     v[u] = c < chunks ? __builtin_nontemporal_load(yr + c) : u32x4{0, 0, 0, 0};
                 }
 #pragma unroll
-                for (int u = 0; u < kRowUnroll; ++u)
+                for (int u = 0; u < U; ++u)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         acc[u][2 * e] = fmaf(wq, __uint_as_float(v[u][e] << 16), acc[u][2 * e]);
@@ -141,7 +147,7 @@ __device__ void combine_body(const uint16_t *__restrict__ Y, const int32_t *__re
             if (S) {
                 const u32x4 *sr = reinterpret_cast<const u32x4 *>(S + g * (int64_t)H);
 #pragma unroll
-                for (int u = 0; u < kRowUnroll; ++u) {
+                for (int u = 0; u < U; ++u) {
                     int c = c0 + u * kWave + lane;
                     const u32x4 v = c < chunks ? __builtin_nontemporal_load(sr + c) : u32x4{0, 0, 0, 0};
 #pragma unroll
@@ -152,7 +158,7 @@ __device__ void combine_body(const uint16_t *__restrict__ Y, const int32_t *__re
                 }
             }
 #pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u) {
+            for (int u = 0; u < U; ++u) {
                 int c = c0 + u * kWave + lane;
                 if (c < chunks)
                     o[c] = u32x4{pack_bf2(acc[u][0], acc[u][1]), pack_bf2(acc[u][2], acc[u][3]),
