@@ -247,9 +247,11 @@ __device__ __forceinline__ void place_block(const SchedArgs &a, const uint32_t (
             rowbuf[ib] = row;
         }
     }
-    // (C) route rows of the block, coalesced
+    // (C) route rows of the block, coalesced; streamed past L2 (nontemporal) so
+    // the partly written lines of Phi, which other partitions' workgroups fill
+    // in, stay there longer
     const int32_t nb_routes = min(kSchedBlock, a.R - lo);
-    for (int k = lane; k < nb_routes; k += kWave) rrow[lo + k] = rowbuf[k];
+    for (int k = lane; k < nb_routes; k += kWave) __builtin_nontemporal_store(rowbuf[k], rrow + lo + k);
 }
 
 // Padding rows (-1, -1) of segments l = first, first + step, ... < L.
