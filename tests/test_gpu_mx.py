@@ -69,10 +69,10 @@ def test_quantize_large_bit_exact():
 
 
 class MxLayer:
-    def __init__(self, seed, P, Np, E, K, L, H, I, routing="uniform", s=1.2):
-        self.h = inputs.make_layer_inputs(seed, P, Np, E, K, L, H, I, routing=routing, x_std=1.0, s=s)
-        self.P, self.Np, self.K, self.L, self.H, self.I = P, Np, K, L, H, I
-        self.d = ops.make_desc(P, Np, K, E, L, H=H, I=I)
+    def __init__(self, seed, P, Np, E, K, L, H, I, routing="uniform", s=1.2, base=0):
+        self.h = inputs.make_layer_inputs(seed, P, Np, E, K, L, H, I, routing=routing, base=base, x_std=1.0, s=s)
+        self.P, self.Np, self.K, self.L, self.H, self.I, self.base = P, Np, K, L, H, I, base
+        self.d = ops.make_desc(P, Np, K, E, L, expert_base=base, H=H, I=I)
         self.routes, self.w = up(self.h["routes"]), up(self.h["w"])
         self.X = up_bf16(self.h["X"])
         self.W13q, self.W13s = ops.quantize_mx(up_bf16(self.h["W13"]))
@@ -87,7 +87,7 @@ class MxLayer:
 
 def check_mx_full(lay: MxLayer, b):
     h = lay.h
-    s = oracle.schedule(h["routes"], lay.L, 0, 256)
+    s = oracle.schedule(h["routes"], lay.L, lay.base, 256)
     np.testing.assert_array_equal(b.phi[: s.npad].cpu().numpy(), s.phi)
     np.testing.assert_array_equal(b.route_row.cpu().numpy(), s.route_row)
     Xq, Xs = oracle.mx_quantize(h["X"])
@@ -113,7 +113,7 @@ def check_mx_full(lay: MxLayer, b):
     assert err <= TOL
     assert not Y[~real].any()
     assert not a_gpu[~real].any()
-    out = oracle.mx_layer_fwd_tokens(h["routes"], h["w"], Xq, Xs, W13q, W13s, W2q, W2s, L=lay.L)
+    out = oracle.mx_layer_fwd_tokens(h["routes"], h["w"], Xq, Xs, W13q, W13s, W2q, W2s, L=lay.L, base=lay.base)
     err = rel_l2(f64(b.out).reshape(out.shape), out)
     print(f"[mx] out rel-L2 {err:.2e}", flush=True)
     assert err <= TOL
@@ -128,6 +128,18 @@ def test_mx_tiny_forward():
 def test_mx_small_forward_multi_tile():
     print("[mx] small forward, several tiles and ragged segments", flush=True)
     lay = MxLayer(3, 4, 700, 12, 3, 6, 512, 256, routing="zipf", s=1.2)
+    check_mx_full(lay, lay.fwd())
+
+
+def test_mx_nonzero_base_and_dropped_ids():
+    """Local experts [5, 11) of 24 and dropped (-1) slots: tables, codes and
+    outputs against the oracle's MX path with the same expert base."""
+    print("[mx] expert base 5, dropped ids", flush=True)
+    lay = MxLayer(17, 3, 300, 24, 3, 6, 256, 128, routing="zipf", base=5)
+    rt = lay.h["routes"].copy()
+    rt[:, ::5, 1] = -1
+    lay.h["routes"] = rt
+    lay.routes = up(rt)
     check_mx_full(lay, lay.fwd())
 
 

@@ -62,6 +62,29 @@ def test_shared_forward(P, Np, Is):
     assert torch.equal(b.out, b2.out) and torch.equal(sh.Ys, sh2.Ys)
 
 
+def test_shared_nonzero_base_and_dropped_ids():
+    """Local experts [6, 10) of 12 with dropped (-1) slots: routed rows bitwise
+    the routed-only path's, the output within rel-L2 1e-2 of the oracle."""
+    print("[shared] expert base 6, dropped ids", flush=True)
+    lay = Layer(25, 3, 200, 12, 3, 4, 256, 128, routing="zipf", base=6, x_std=1.0, grad=False)
+    rt = lay.h["routes"].copy()
+    rt[:, ::3, 0] = -1
+    lay.h["routes"] = rt
+    lay.routes = up(rt)
+    w13s, w2s = shared_weights(26, 256, 128)
+    b, sh = run_shared(lay, up_bf16(w13s), up_bf16(w2s), 128)
+    std = lay.fwd(save_xd=False)
+    npad = int(std.seg_off[-1])
+    for name in ("HU", "A", "Y"):
+        assert torch.equal(getattr(b, name)[:npad], getattr(std, name)[:npad]), name
+    h = lay.h
+    out = oracle.layer_fwd_tokens_shared(h["routes"], h["w"], h["X"], h["W13"], h["W2"], w13s, w2s, L=lay.L,
+                                         base=lay.base)
+    err = rel_l2(f64(b.out).reshape(out.shape), out)
+    print(f"[shared] out rel-L2 {err:.2e}", flush=True)
+    assert err <= TOL
+
+
 def test_shared_only_tokens_without_local_routes():
     """No local route anywhere: the output is the shared expert alone."""
     lay = Layer(23, 2, 128, 8, 2, 4, 256, 128, routing="topk", x_std=1.0, grad=False)
