@@ -230,3 +230,33 @@ def test_mid_forward_sampled():
     out = oracle.layer_fwd_tokens(lay.h["routes"], lay.h["w"], lay.h["X"], lay.h["W13"], lay.h["W2"], L=lay.L,
                                   tokens=toks)
     assert rel_l2(f64(b.out).reshape(-1, lay.H)[toks], out) <= TOL
+
+
+def test_random_shapes_forward_backward():
+    """Seeded random shapes within the supported constraints (H a multiple of
+    256, I of 128), routing kinds, expert bases and dropped slots: the full
+    forward checks (tables bit-exact, rows and outputs vs the oracle, padding
+    and non-local tokens exactly zero) and the full backward checks."""
+    rng = np.random.default_rng(4242)
+    for i in range(10):
+        P = int(rng.integers(1, 5))
+        Np = int(rng.integers(40, 500))
+        E = int(rng.integers(4, 24))
+        K = int(rng.integers(1, min(4, E) + 1))
+        L = int(rng.integers(1, E + 1))
+        base = int(rng.integers(0, E - L + 1))
+        H = int(rng.choice([256, 512, 768]))
+        I = int(rng.choice([128, 256, 384]))
+        routing = str(rng.choice(["uniform", "zipf", "topk"]))
+        drop = bool(rng.random() < 0.5)
+        print(f"[layer] random {i}: P={P} Np={Np} E={E} K={K} L={L} base={base} H={H} I={I} {routing}"
+              f"{' dropped slots' if drop else ''}", flush=True)
+        lay = Layer(100 + i, P, Np, E, K, L, H, I, routing=routing, base=base, x_std=1.0)
+        if drop:
+            rt = lay.h["routes"].copy()
+            rt[:, ::3, 0] = -1
+            lay.h["routes"] = rt
+            lay.routes = up(rt)
+        b = lay.fwd()
+        check_fwd_full(lay, b)
+        check_bwd_full(lay, lay.bwd(b))
