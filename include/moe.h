@@ -107,7 +107,10 @@ int64_t moe_workspace_bytes(const moe_desc *d, int op);
  * every route once to Phi[S[l] + p] with
  *     p = sum_{r'} min(M[l][r'], o) + #{ r' < r : M[l][r'] > o },
  * o being the route's ordinal among partition r's routes to expert l in flat
- * (token-major, then slot) order.  Route ids are read twice in total.
+ * (token-major, then slot) order.  Route ids are read once as int32; the count
+ * stage leaves each route's local id as one byte in the workspace and the
+ * scatter reads those (with more than 255 local experts it reads the int32 ids
+ * again).
  *
  * For each batch b in [0, num_batches):
  *   routes     int32   [nb][P][Np][K]  in: expert id of every slot

@@ -256,7 +256,14 @@ int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 // Workspace of the shared expert's identity table: 2 offsets, then the rows.
 int64_t shared_table_bytes(const moe_desc *d) { return 256 + align256(shared_rows(d) * 8); }
 
-int64_t sched_ws_bytes(const moe_desc *d) { return align256(4ll * d->num_batches * d->P * sched_chunks(d) * d->L); }
+// Schedule workspace: per-chunk counts, then (L <= 255) every route's local id
+// as a byte in blocks of kSchedBlock (SchedArgs::ids8).
+int64_t sched_counts_bytes(const moe_desc *d) { return align256(4ll * d->num_batches * d->P * sched_chunks(d) * d->L); }
+int64_t sched_nblk(const moe_desc *d) { return ((int64_t)d->Np * d->K + kSchedBlock - 1) / kSchedBlock; }
+int64_t sched_ws_bytes(const moe_desc *d) {
+    const int64_t ids = d->L <= 255 ? align256((int64_t)d->num_batches * d->P * sched_nblk(d) * kSchedBlock) : 0;
+    return sched_counts_bytes(d) + ids;
+}
 
 int bwd_nparts(const moe_desc *d) { return (d->I + 255) / 256; }  // one dw partial per 256-column tile
 
@@ -295,6 +302,8 @@ void fill_sched_args(SchedArgs &a, const moe_desc *d, const int32_t *routes, int
     a.cap = cap_rows(d);
     a.pstride = a.R;
     a.bstride = (int64_t)a.P * a.R;
+    a.ids8 = d->L <= 255 ? reinterpret_cast<uint8_t *>(ws + sched_counts_bytes(d)) : nullptr;
+    a.nblk = (int32_t)sched_nblk(d);
 }
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS of one gfx950 workgroup

@@ -18,7 +18,10 @@
 // ordinal o of every route is its index order with no atomics.  Per-wave
 // counters live in LDS.  A second pass (one workgroup per batch) turns the
 // per-wave counts into exclusive offsets, the per-(expert, partition) counts
-// M and the padded segment offsets S; a third places every route.
+// M and the padded segment offsets S; a third places every route.  The count
+// stage also leaves every route's local id as one byte, so the scatter reads
+// a quarter of the ids' bytes the second time (the pages' design reads the
+// ids twice).
 #pragma once
 
 #include "common.hpp"
@@ -45,7 +48,18 @@ struct SchedArgs {
     // and R for nb whole routing tensors; B * K and Np * K when the tables are
     // the token windows [m B, (m + 1) B) of one [P][Np][K] tensor (macrobatches).
     int64_t bstride, pstride;
+    // Local ids of every route as bytes, written by the count stage and read
+    // by the scatter instead of the 4-byte ids (nullptr when L > 255: the
+    // scatter then reads the ids again).  Block k of partition r of table b
+    // is 1,024 bytes at ((b * P + r) * nblk + k) * 1024, lane l's 16 ids (its
+    // routes lo + u * 64 + l) one 16-byte word at l * 16.
+    uint8_t *ids8;
+    int32_t nblk;  // blocks of kSchedBlock routes per partition
 };
+
+__device__ __forceinline__ uint8_t *ids8_block(const SchedArgs &a, int b, int r, int64_t blk) {
+    return a.ids8 + (((int64_t)b * a.P + r) * a.nblk + blk) * kSchedBlock;
+}
 
 // Workgroup index -> (batch, partition, first chunk).  For eight or more
 // batches the workgroups of one batch share an XCD (hardware deals workgroup
@@ -170,12 +184,16 @@ __device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
                 const int64_t i = lo + u * kWave + lane;
                 e[u] = i < a.R ? __builtin_nontemporal_load(src + i) : -1;
             }
+            u32x4 word = {0u, 0u, 0u, 0u};
 #pragma unroll
             for (int u = 0; u < kSchedUnroll; ++u) {
                 const uint32_t v = local_id(e[u], a.base, L);
+                word[u >> 2] |= v << (8 * (u & 3));
                 if (v < (uint32_t)L)
                     __hip_atomic_fetch_add(cnt + v, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             }
+            if (a.ids8)
+                *reinterpret_cast<u32x4 *>(ids8_block(a, b, r, (int64_t)w * a.cb + blk) + lane * 16) = word;
         }
     }
     __syncthreads();
@@ -303,15 +321,22 @@ __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
         for (int blk = 0; blk < a.cb; ++blk) {
             const int32_t lo = (w * a.cb + blk) * kSchedBlock;
             if (lo >= a.R) break;
-            int32_t e[kSchedUnroll];
-#pragma unroll
-            for (int u = 0; u < kSchedUnroll; ++u) {
-                const int32_t i = lo + u * kWave + lane;
-                e[u] = i < a.R ? __builtin_nontemporal_load(src + i) : -1;
-            }
             uint32_t v[kSchedUnroll];
+            if (a.ids8) {  // the count stage's bytes: a quarter of the ids' traffic
+                const u32x4 word = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4 *>(ids8_block(a, b, r, w * a.cb + blk) + lane * 16));
 #pragma unroll
-            for (int u = 0; u < kSchedUnroll; ++u) v[u] = local_id(e[u], a.base, L);
+                for (int u = 0; u < kSchedUnroll; ++u) v[u] = (word[u >> 2] >> (8 * (u & 3))) & 0xffu;
+            } else {
+                int32_t e[kSchedUnroll];
+#pragma unroll
+                for (int u = 0; u < kSchedUnroll; ++u) {
+                    const int32_t i = lo + u * kWave + lane;
+                    e[u] = i < a.R ? __builtin_nontemporal_load(src + i) : -1;
+                }
+#pragma unroll
+                for (int u = 0; u < kSchedUnroll; ++u) v[u] = local_id(e[u], a.base, L);
+            }
             place_block(a, v, lo, r, sM, sS, run, list, rowbuf, phi, rrow);
         }
     }

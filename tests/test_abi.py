@@ -46,8 +46,16 @@ def test_capacity_and_workspace_sizes():
     assert ops.workspace_bytes(d, ops.MOE_OP_SCHEDULE) > 0
     d64 = kimi()
     d64.num_batches = 64
-    # per-chunk counters for every batch: at least one int per (batch, partition, expert)
-    assert ops.workspace_bytes(d64, ops.MOE_OP_SCHEDULE) >= 64 * 8 * 48 * 4 > ops.workspace_bytes(d, ops.MOE_OP_SCHEDULE) / 4
+    routes = 8 * 7168 * 8
+    # per-chunk counters (at least one int per batch, partition and expert) and
+    # one byte per route for the scatter's second read of the local ids
+    assert ops.workspace_bytes(d, ops.MOE_OP_SCHEDULE) >= 8 * 48 * 4 + routes
+    assert ops.workspace_bytes(d64, ops.MOE_OP_SCHEDULE) >= 64 * (8 * 48 * 4 + routes)
+    # more than 255 local experts: no byte copy (the scatter reads the ids again),
+    # so one more local expert takes less workspace
+    w255 = ops.workspace_bytes(ops.make_desc(8, 7168, 8, 2048, 255), ops.MOE_OP_SCHEDULE)
+    w256 = ops.workspace_bytes(ops.make_desc(8, 7168, 8, 2048, 256), ops.MOE_OP_SCHEDULE)
+    assert 0 < w256 < w255 and w255 >= routes
     cap = ops.capacity_rows(d)
     assert ops.workspace_bytes(d, ops.MOE_OP_LAYER_BWD) >= cap * (7168 * 2 + 4096) * 2
 
