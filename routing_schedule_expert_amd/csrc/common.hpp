@@ -29,12 +29,26 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
 
 // Mask of the lanes holding the same value v (0 <= v < 2^nbits); inactive
-// lanes must not call.  Built from one ballot per bit.
+// lanes must not call.  Built from one ballot per bit: a lane keeps the
+// ballot of its bit value (the ballot, or its complement where its bit is 0).
 __device__ __forceinline__ uint64_t match_lanes(uint32_t v, int nbits) {
     uint64_t peers = __ballot(1);
     for (int b = 0; b < nbits; ++b) {
-        uint64_t m = __ballot((v >> b) & 1u);
-        peers &= ((v >> b) & 1u) ? m : ~m;
+        const uint64_t flip = (uint64_t)((v >> b) & 1u) - 1ull;  // 0 where the bit is 1, all ones where 0
+        peers &= __ballot((v >> b) & 1u) ^ flip;
+    }
+    return peers;
+}
+
+// The same with the bit count fixed at compile time (the loop unrolled);
+// bits of v at or above NB must be zero.
+template <int NB>
+__device__ __forceinline__ uint64_t match_lanes_n(uint32_t v) {
+    uint64_t peers = __ballot(1);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const uint64_t flip = (uint64_t)((v >> b) & 1u) - 1ull;
+        peers &= __ballot((v >> b) & 1u) ^ flip;
     }
     return peers;
 }

@@ -119,21 +119,17 @@ __device__ void sched_finalize(const SchedArgs &a, int b, int32_t *smem) {
         const int r = pr / L, l = pr % L;
         int32_t *col = wc + (int64_t)r * W * L + l;
         int32_t acc = 0;
-        int w = 0;
-        for (; w + 8 <= W; w += 8) {
-            int32_t v[8];
+        // batches of 16 chunks, loads first (predicated), so a column costs one
+        // memory round trip per 16 chunks
+        for (int w = 0; w < W; w += 16) {
+            int32_t v[16];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = col[(int64_t)(w + u) * L];
+            for (int u = 0; u < 16; ++u) v[u] = w + u < W ? col[(int64_t)(w + u) * L] : 0;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                col[(int64_t)(w + u) * L] = acc;
+            for (int u = 0; u < 16; ++u) {
+                if (w + u < W) col[(int64_t)(w + u) * L] = acc;
                 acc += v[u];
             }
-        }
-        for (; w < W; ++w) {
-            const int32_t v = col[(int64_t)w * L];
-            col[(int64_t)w * L] = acc;
-            acc += v;
         }
         cnt[l * P + r] = acc;
         s_tot[pr] = acc;
@@ -175,15 +171,21 @@ __device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
     __syncthreads();
     if (w < a.W) {
         const int32_t *src = a.routes + (int64_t)b * a.bstride + (int64_t)r * a.pstride;
-        for (int blk = 0; blk < a.cb; ++blk) {
-            const int64_t lo = ((int64_t)w * a.cb + blk) * kSchedBlock;
-            if (lo >= a.R) break;
-            int32_t e[kSchedUnroll];
+        // the next block's ids are loaded while this one is counted
+        auto load_block = [&](int64_t lo, int32_t (&e)[kSchedUnroll]) {
 #pragma unroll
             for (int u = 0; u < kSchedUnroll; ++u) {
                 const int64_t i = lo + u * kWave + lane;
                 e[u] = i < a.R ? __builtin_nontemporal_load(src + i) : -1;
             }
+        };
+        int32_t e[kSchedUnroll];
+        load_block((int64_t)w * a.cb * kSchedBlock, e);
+        for (int blk = 0; blk < a.cb; ++blk) {
+            const int64_t lo = ((int64_t)w * a.cb + blk) * kSchedBlock;
+            if (lo >= a.R) break;
+            int32_t en[kSchedUnroll];
+            if (blk + 1 < a.cb) load_block(lo + kSchedBlock, en);
             u32x4 word = {0u, 0u, 0u, 0u};
 #pragma unroll
             for (int u = 0; u < kSchedUnroll; ++u) {
@@ -194,6 +196,8 @@ __device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
             }
             if (a.ids8)
                 *reinterpret_cast<u32x4 *>(ids8_block(a, b, r, (int64_t)w * a.cb + blk) + lane * 16) = word;
+#pragma unroll
+            for (int u = 0; u < kSchedUnroll; ++u) e[u] = en[u];
         }
     }
     __syncthreads();
@@ -206,37 +210,42 @@ __device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
 // Places the routes of one block of kSchedBlock routes starting at route lo
 // of partition r: lane l holds the local ids v[u] (L = not local) of routes
 // lo + u * 64 + l.  (A) the local routes are compacted, in index order, into
-// an LDS list (ballot + masked popcount give each local lane its slot;
-// route_row is staged as -1); (B) the list is processed 64 entries at a time:
-// lanes holding the same expert find each other with one ballot per bit of
-// the expert id, the group leader advances the wave's running count for that
-// expert with an LDS atomic (integer, program order) and the returned old
-// value plus the lane's rank in its group is the ordinal o; then p and the row
-// follow and Phi[row] is written; (C) the staged route_row is written back
-// coalesced.  Only local routes pay for ranking and placement.
-__device__ __forceinline__ void place_block(const SchedArgs &a, const uint32_t (&v)[kSchedUnroll], int32_t lo, int r,
-                                            const int32_t *sM, const int32_t *sS, int32_t *run, int32_t *list,
-                                            int32_t *rowbuf, moe_src *phi, int32_t *rrow) {
+// an LDS list (ballot + masked popcount give each local lane its slot); (B)
+// the list is processed 64 entries at a time: lanes holding the same expert
+// find each other with one ballot per bit of the expert id, the group leader
+// advances the wave's running count for that expert with an LDS atomic
+// (integer, program order) and the returned old value plus the lane's rank in
+// its group is the ordinal o; then p and the row follow, Phi[row] is written
+// and the row is staged in LDS at the route's place; (C) each lane writes its
+// routes' rows, coalesced (-1 for the routes that are not local, which never
+// touch LDS).  Only local routes pay for ranking and placement.  NB: bits of
+// the expert ids ranked by an unrolled match (0: a runtime loop over a.nbits).
+template <int NB>
+__device__ __forceinline__ void place_block_n(const SchedArgs &a, const uint32_t (&v)[kSchedUnroll], int32_t lo,
+                                              int r, const int32_t *sM, const int32_t *sS, int32_t *run,
+                                              int32_t *list, int32_t *rowbuf, moe_src *phi, int32_t *rrow) {
     const int lane = lane_id();
-    const int L = a.L, P = a.P, K = a.K;
+    const int L = a.L, P = a.P;
+    const uint32_t K = (uint32_t)a.K;
     const bool fast = P <= kSchedPMax;
     int nloc = 0;
 #pragma unroll
     for (int u = 0; u < kSchedUnroll; ++u) {
         const bool local = v[u] < (uint32_t)L;
         const uint64_t lm = ballot(local);
-        rowbuf[u * kWave + lane] = -1;
         if (local) list[nloc + lanes_below(lm)] = (int32_t)((v[u] << 16) | (uint32_t)(u * kWave + lane));
         nloc += __popcll(lm);
     }
-    const int32_t t0 = lo / K;
-    const int32_t j0 = lo - t0 * K;
+    const uint32_t t0 = (uint32_t)lo / K;  // lo >= 0
+    const uint32_t j0 = (uint32_t)lo - t0 * K;
     for (int c0 = 0; c0 < nloc; c0 += kWave) {
         const bool valid = c0 + lane < nloc;
         const int32_t ent = valid ? list[c0 + lane] : (int32_t)((uint32_t)L << 16);
         const uint32_t e = (uint32_t)ent >> 16;
         const int32_t ib = ent & 0xffff;  // index inside the block
-        const uint64_t peers = match_lanes(e, a.nbits);
+        uint64_t peers;
+        if constexpr (NB > 0) peers = match_lanes_n<NB>(e);
+        else peers = match_lanes(e, a.nbits);
         const int rank = lanes_below(peers);
         int32_t old = 0;
         if (rank == 0 && valid)
@@ -258,10 +267,10 @@ __device__ __forceinline__ void place_block(const SchedArgs &a, const uint32_t (
                 for (int rr = 0; rr < P; ++rr) p += min(Ml[rr], rr < r ? o + 1 : o);
             }
             const int32_t row = sS[e] + p;
-            const int32_t jj = j0 + ib;  // slot offset from token t0, < K + 1024
-            const int32_t t = t0 + jj / K;
+            const uint32_t jj = j0 + (uint32_t)ib;  // slot offset from token t0, < K + 1024
+            const uint32_t t = t0 + jj / K;
             if ((uint32_t)row < (uint32_t)a.cap)  // always true for a consistent table
-                reinterpret_cast<uint2 *>(phi)[row] = make_uint2((uint32_t)r, (uint32_t)t);
+                reinterpret_cast<uint2 *>(phi)[row] = make_uint2((uint32_t)r, t);
             rowbuf[ib] = row;
         }
     }
@@ -269,7 +278,20 @@ __device__ __forceinline__ void place_block(const SchedArgs &a, const uint32_t (
     // the partly written lines of Phi, which other partitions' workgroups fill
     // in, stay there longer
     const int32_t nb_routes = min(kSchedBlock, a.R - lo);
-    for (int k = lane; k < nb_routes; k += kWave) __builtin_nontemporal_store(rowbuf[k], rrow + lo + k);
+    int32_t rows[kSchedUnroll];
+#pragma unroll
+    for (int u = 0; u < kSchedUnroll; ++u) rows[u] = v[u] < (uint32_t)L ? rowbuf[u * kWave + lane] : -1;
+#pragma unroll
+    for (int u = 0; u < kSchedUnroll; ++u)
+        if (u * kWave + lane < nb_routes) __builtin_nontemporal_store(rows[u], rrow + lo + u * kWave + lane);
+}
+
+__device__ __forceinline__ void place_block(const SchedArgs &a, const uint32_t (&v)[kSchedUnroll], int32_t lo, int r,
+                                            const int32_t *sM, const int32_t *sS, int32_t *run, int32_t *list,
+                                            int32_t *rowbuf, moe_src *phi, int32_t *rrow) {
+    if (a.nbits <= 6) place_block_n<6>(a, v, lo, r, sM, sS, run, list, rowbuf, phi, rrow);
+    else if (a.nbits <= 9) place_block_n<9>(a, v, lo, r, sM, sS, run, list, rowbuf, phi, rrow);
+    else place_block_n<0>(a, v, lo, r, sM, sS, run, list, rowbuf, phi, rrow);
 }
 
 // Padding rows (-1, -1) of segments l = first, first + step, ... < L.
