@@ -425,24 +425,33 @@ __device__ __forceinline__ void gemm_mainloop_x(const typename OpOf<AT>::type &a
 // Tile ordering.
 // ---------------------------------------------------------------------------
 
+// Tile numbers fit in 32 bits (the host rejects larger shapes), so the
+// divisions below are 32-bit ones: a 64-bit division is a long software
+// sequence paid between every two tiles.
+
 // Round-robin XCD placement: in each round of G = gridDim.x concurrent tiles,
 // XCD x%8 gets a contiguous run of G/8 logical tiles, so tiles that share
 // operands (same M tile, neighbouring N tiles) meet in one L2.
-__device__ __forceinline__ int64_t logical_tile(int64_t it) {
-    const int64_t G = gridDim.x;
-    const int64_t round = it / G, x = it % G;
-    return round * G + (x & 7) * (G >> 3) + (x >> 3);
+__device__ __forceinline__ int64_t logical_tile(int64_t it64) {
+    const uint32_t it = (uint32_t)it64, G = gridDim.x;
+    const uint32_t round = it / G, x = it - round * G;
+    return (int64_t)(round * G + (x & 7) * (G >> 3) + (x >> 3));
 }
 
 // Grouped order inside a (mtiles x ntiles) grid: GM M tiles sweep all N tiles.
-__device__ __forceinline__ void grouped_mn(int64_t lid, int mtiles, int ntiles, int GM, int &m, int &n) {
-    const int64_t per = (int64_t)GM * ntiles;
-    const int g = (int)(lid / per);
-    const int first = g * GM;
+template <int GM>
+__device__ __forceinline__ void grouped_mn(int64_t lid64, int mtiles, int ntiles, int &m, int &n) {
+    const uint32_t lid = (uint32_t)lid64, per = (uint32_t)(GM * ntiles);
+    const uint32_t g = lid / per, in = lid - g * per;
+    const int first = (int)g * GM;
     const int gm = min(GM, mtiles - first);
-    const int in = (int)(lid % per);
-    m = first + in % gm;
-    n = in / gm;
+    if (gm == GM) {  // a full group: constant divisor
+        m = first + (int)(in % GM);
+        n = (int)(in / GM);
+    } else {
+        m = first + (int)(in % (uint32_t)gm);
+        n = (int)(in / (uint32_t)gm);
+    }
 }
 
 __device__ __forceinline__ int expert_of(const int32_t *seg_off, int L, int row) {
@@ -460,8 +469,7 @@ __device__ __forceinline__ int expert_of(const int32_t *seg_off, int L, int row)
 
 __device__ __forceinline__ float silu_f(float h) { return h * __builtin_amdgcn_rcpf(1.0f + __expf(-h)); }
 
-// Staging for a WM x WN wave grid: wave (wm, wn) writes rows
-// [wm*256/WM, (wm+1)*256/WM), all inside one 128-row half of the staging tile.
+// One 16-bit LDS write per value, chunks in place (read with SWZ = false).
 template <int NC, int WM>
 struct LaneStageW {
     char *base;
@@ -474,6 +482,80 @@ struct LaneStageW {
         *reinterpret_cast<uint16_t *>(base + ((mi * 32 + 8 * (e >> 2) + (e & 3)) * NC + c) * 2) = f2bf(v);
     }
 };
+
+// Staging of bf16 values for a WM x WN wave grid: wave (wm, wn) writes rows
+// [wm*256/WM, (wm+1)*256/WM), all inside one 128-row half (one 64 KiB stage)
+// of the 256-row staging tile.  Lanes 2k and 2k+1 hold adjacent columns; for
+// two consecutive rows e, e+1 of an accumulator block they trade one value
+// (one DPP exchange), so the even lane writes both columns of row e and the
+// odd lane both columns of row e+1 as one dword: half the LDS writes of one
+// 16-bit write per value, and no two lanes share a dword.  The 16-byte chunks of a staged row are permuted by XOR with
+// 4 * stage_swz(row): the four rows one write instruction touches (r, r+1,
+// r+4, r+5) then sit in four different 64-byte bank groups.  Readers find
+// column chunk q of row r at chunk q ^ (4 * stage_swz(r)).
+__device__ __forceinline__ int stage_swz(int row) { return (row & 1) | ((row >> 1) & 2); }
+
+__device__ __forceinline__ float dpp_swap_pair(float v) {  // value of lane ^ 1
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+template <int NC, int WM>
+struct PairStageW {
+    char *rowbase;
+    int col0, sw, odd;
+    __device__ __forceinline__ PairStageW(char *lds, int off, int wm, int lane, int col0_) {
+        constexpr int rows_per_wave = 256 / WM;
+        static_assert(rows_per_wave % 32 == 0, "row blocks of 32");
+        const int r0 = wm * rows_per_wave, hi = lane >> 5;
+        odd = lane & 1;
+        rowbase = lds + (r0 >> 7) * kStageBytes + off + ((r0 & 127) + 4 * hi + odd) * NC * 2;
+        col0 = col0_ + (lane & 30);
+        sw = 4 * (odd | (hi << 1));
+    }
+    // v0, v1: this lane's values of rows e and e+1 (e even) of block (mi, c)
+    __device__ __forceinline__ void put2(int mi, int e, int c, float v0, float v1) const {
+        const float recv = dpp_swap_pair(odd ? v0 : v1);
+        const uint32_t w = odd ? pack_bf2(recv, v1) : pack_bf2(v0, recv);
+        const int col = col0 + c;
+        *reinterpret_cast<uint32_t *>(rowbase + (mi * 32 + 8 * (e >> 2) + (e & 3)) * NC * 2 +
+                                      (((col >> 3) ^ sw) << 4) + (col & 7) * 2) = w;
+    }
+};
+
+// Copy of a staged 256 x NC bf16 area (chunks placed as PairStageW writes
+// them) to rows of dst; columns from ncols on are not written.  A thread keeps
+// one 16-byte column chunk for all its rows and issues a batch of LDS reads
+// before the batch's stores (one LDS round trip per batch, not per chunk).
+// tt is the thread index passed through an empty asm by the caller: the
+// addresses, the same for every tile, are then not hoisted out of the tile
+// loop to stay live (and spill) across the next tile's K loop.
+template <int NC, int THREADS, bool SWZ = true>
+__device__ __forceinline__ void copy_staged(const char *area, uint16_t *dst, int64_t ld, int ncols, int tt) {
+    constexpr int CPR = NC / 8, RSTEP = THREADS / CPR, kIt = 256 / RSTEP, kBatch = 8;
+    static_assert(kIt % kBatch == 0, "whole batches");
+    const int q = tt % CPR, r0 = tt / CPR;
+#pragma unroll
+    for (int b = 0; b < kIt; b += kBatch) {
+        u32x4 v[kBatch];
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const int row = r0 + (b + i) * RSTEP;
+            v[i] = *reinterpret_cast<const u32x4 *>(area + (row >> 7) * kStageBytes + (row & 127) * (NC * 2) +
+                                                    ((SWZ ? q ^ (4 * stage_swz(row)) : q) << 4));
+        }
+        if (q * 8 < ncols) {
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                *reinterpret_cast<u32x4 *>(dst + (int64_t)(r0 + (b + i) * RSTEP) * ld + q * 8) = v[i];
+        }
+    }
+}
+
+__device__ __forceinline__ int opaque_tid() {
+    int tt = threadIdx.x;
+    asm volatile("" : "+v"(tt));
+    return tt;
+}
 
 template <int WM, int WN>
 __device__ __forceinline__ void epilogue_swiglu_w(AccW<WM, WN> &acc, char *lds, uint16_t *Aout, int64_t ldA, uint16_t *HUg, uint16_t *HUu,
@@ -495,15 +577,10 @@ __device__ __forceinline__ void epilogue_swiglu_w(AccW<WM, WN> &acc, char *lds, 
         __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < 256 * 16; c += WG::THREADS) {
-        const int row = c >> 4, cc = (c & 15) * 8;
-        const char *src = lds + (row >> 7) * kStageBytes + ((row & 127) * 128 + cc) * 2;
-        *reinterpret_cast<u32x4 *>(Aout + (int64_t)row * ldA + cc) = *reinterpret_cast<const u32x4 *>(src);
-        if (HUg)
-            *reinterpret_cast<u32x4 *>(HUg + (int64_t)row * ldHU + cc) =
-                *reinterpret_cast<const u32x4 *>(src + 32768);
-    }
+    const int tt = opaque_tid();
+    copy_staged<128, WG::THREADS, false>(lds, Aout, ldA, 128, tt);
     if (HUg) {
+        copy_staged<128, WG::THREADS, false>(lds + 32768, HUg, ldHU, 128, tt);
         __syncthreads();
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
@@ -514,11 +591,7 @@ __device__ __forceinline__ void epilogue_swiglu_w(AccW<WM, WN> &acc, char *lds, 
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
-        for (int c = threadIdx.x; c < 256 * 16; c += WG::THREADS) {
-            const int row = c >> 4, cc = (c & 15) * 8;
-            const char *src = lds + (row >> 7) * kStageBytes + ((row & 127) * 128 + cc) * 2;
-            *reinterpret_cast<u32x4 *>(HUu + (int64_t)row * ldHU + cc) = *reinterpret_cast<const u32x4 *>(src);
-        }
+        copy_staged<128, WG::THREADS, false>(lds, HUu, ldHU, 128, tt);
     }
 }
 
@@ -526,22 +599,17 @@ template <int WM, int WN>
 __device__ __forceinline__ void epilogue_store_bf16_w(AccW<WM, WN> &acc, char *lds, uint16_t *dst, int64_t ld, int nvalid) {
     using WG = WaveGrid<WM, WN>;
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63, wm = wave / WN, wn = wave % WN;
-    const LaneStageW<256, WM> sg(lds, 0, wm, lane, wn * WG::NI * 32);
+    const PairStageW<256, WM> sg(lds, 0, wm, lane, wn * WG::NI * 32);
 #pragma unroll
     for (int mi = 0; mi < WG::MI; ++mi) {
 #pragma unroll
         for (int ni = 0; ni < WG::NI; ++ni)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sg.put(mi, e, ni * 32, acc[mi][ni][e]);
+            for (int e = 0; e < 16; e += 2) sg.put2(mi, e, ni * 32, acc[mi][ni][e], acc[mi][ni][e + 1]);
         __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < 256 * 32; c += WG::THREADS) {
-        const int row = c >> 5, cc = (c & 31) * 8;
-        const char *src = lds + (row >> 7) * kStageBytes + ((row & 127) * 256 + cc) * 2;
-        if (cc < nvalid)
-            *reinterpret_cast<u32x4 *>(dst + (int64_t)row * ld + cc) = *reinterpret_cast<const u32x4 *>(src);
-    }
+    copy_staged<256, WG::THREADS>(lds, dst, ld, nvalid, opaque_tid());
 }
 
 // fp32 tile store of the rows < mvalid and columns < nvalid; with accumulate

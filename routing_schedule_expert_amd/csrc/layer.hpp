@@ -87,7 +87,7 @@ __device__ __forceinline__ void ffn_gateup_phase(const FfnArgs &a, int r0, int r
         const int64_t lid = logical_tile(it);
         if (lid >= total) continue;
         int m, n;
-        grouped_mn(lid, mtiles, ntiles, 4, m, n);
+        grouped_mn<4>(lid, mtiles, ntiles, m, n);
         ffn_gateup_tile(a, r0 / kBM + m, n, lds);
     }
 }
@@ -99,7 +99,7 @@ __device__ __forceinline__ void ffn_down_phase(const FfnArgs &a, int r0, int r1,
         const int64_t lid = logical_tile(it);
         if (lid >= total) continue;
         int m, n;
-        grouped_mn(lid, mtiles, ntiles, 4, m, n);
+        grouped_mn<4>(lid, mtiles, ntiles, m, n);
         ffn_down_tile(a, r0 / kBM + m, n, lds);
     }
 }
@@ -120,10 +120,10 @@ __device__ __forceinline__ void ffn_chunked_body(const FfnArgs &a, char *lds, Gr
             if (lid >= total) continue;
             int m, n;
             if (lid < ngu) {
-                grouped_mn(lid, (gu1 - gu0) / kBM, a.I / 128, 4, m, n);
+                grouped_mn<4>(lid, (gu1 - gu0) / kBM, a.I / 128, m, n);
                 ffn_gateup_tile(a, gu0 / kBM + m, n, lds);
             } else {
-                grouped_mn(lid - ngu, (dn1 - dn0) / kBM, a.H / 256, 4, m, n);
+                grouped_mn<4>(lid - ngu, (dn1 - dn0) / kBM, a.H / 256, m, n);
                 ffn_down_tile(a, dn0 / kBM + m, n, lds);
             }
         }
@@ -192,7 +192,7 @@ __device__ __forceinline__ void mx_gateup_phase(const MxFfnArgs &a, char *lds) {
         const int64_t lid = logical_tile(it);
         if (lid >= total) continue;
         int m, n;
-        grouped_mn(lid, mtiles, ntiles, 4, m, n);
+        grouped_mn<4>(lid, mtiles, ntiles, m, n);
         mx_gateup_tile<SG>(a, m, n, lds);
     }
 }
@@ -205,7 +205,7 @@ __device__ __forceinline__ void mx_down_phase(const MxFfnArgs &a, char *lds) {
         const int64_t lid = logical_tile(it);
         if (lid >= total) continue;
         int m, n;
-        grouped_mn(lid, mtiles, ntiles, 4, m, n);
+        grouped_mn<4>(lid, mtiles, ntiles, m, n);
         mx_down_tile<SG>(a, m, n, lds);
     }
 }
@@ -228,10 +228,10 @@ __device__ __forceinline__ void dual_gateup_body(const FfnArgs &s, const FfnArgs
         if (lid >= total) continue;
         int m, n;
         if (lid < ts) {
-            grouped_mn(lid, ms, ns, 4, m, n);
+            grouped_mn<4>(lid, ms, ns, m, n);
             ffn_gateup_tile(s, m, n, lds);
         } else {
-            grouped_mn(lid - ts, mr, nr, 4, m, n);
+            grouped_mn<4>(lid - ts, mr, nr, m, n);
             ffn_gateup_tile(r, m, n, lds);
         }
     }
@@ -246,10 +246,10 @@ __device__ __forceinline__ void dual_down_body(const FfnArgs &s, const FfnArgs &
         if (lid >= total) continue;
         int m, n;
         if (lid < ts) {
-            grouped_mn(lid, ms, nt, 4, m, n);
+            grouped_mn<4>(lid, ms, nt, m, n);
             ffn_down_tile(s, m, n, lds);
         } else {
-            grouped_mn(lid - ts, mr, nt, 4, m, n);
+            grouped_mn<4>(lid - ts, mr, nt, m, n);
             ffn_down_tile(r, m, n, lds);
         }
     }
@@ -290,7 +290,7 @@ __device__ __forceinline__ void ring_gateup_combine_body(const FfnArgs &a, const
         if (lid >= total) continue;
         if (lid < ngu) {
             int m, n;
-            grouped_mn(lid, mtiles, ntiles, 4, m, n);
+            grouped_mn<4>(lid, mtiles, ntiles, m, n);
             ffn_gateup_tile(a, m, n, lds);
         } else {
             const int64_t g0 = (lid - ngu) * kCombineItem;
@@ -379,7 +379,7 @@ __device__ __forceinline__ void bwd_down_phase(const BwdArgs &a, char *lds) {
         const int64_t lid = logical_tile(it);
         if (lid >= total) continue;
         int mt, nt;
-        grouped_mn(lid, mtiles, ntiles, 4, mt, nt);
+        grouped_mn<4>(lid, mtiles, ntiles, mt, nt);
         const int m0 = mt * kBM;
         const int l = expert_of(a.seg_off, a.L, m0);
         const uint16_t *g = a.dOd + (int64_t)m0 * H;
@@ -403,7 +403,7 @@ __device__ __forceinline__ void bwd_gateup_phase(const BwdArgs &a, char *lds) {
         const int64_t lid = logical_tile(it);
         if (lid >= total) continue;
         int mt, nt;
-        grouped_mn(lid, mtiles, ntiles, 4, mt, nt);
+        grouped_mn<4>(lid, mtiles, ntiles, mt, nt);
         const int m0 = mt * kBM;
         const int l = expert_of(a.seg_off, a.L, m0);
         const uint16_t *g = a.dHU + (int64_t)m0 * 2 * I;
@@ -515,14 +515,14 @@ __device__ __forceinline__ void wgrad_phase(const WgradArgs &a, const WindowComb
                          threadIdx.x / kWave, blockDim.x / kWave, c.tpp, c.tstride);
             continue;
         }
-        const int pos = (int)(lid / per), in = (int)(lid % per);
+        const int pos = (int)((uint32_t)lid / (uint32_t)per), in = (int)((uint32_t)lid - (uint32_t)pos * (uint32_t)per);
         const int l = L <= 256 ? s_order[pos] : pos;
         int mt, nt;
         if (in < mt2 * nt2) {
-            grouped_mn(in, mt2, nt2, 4, mt, nt);
+            grouped_mn<4>(in, mt2, nt2, mt, nt);
             wgrad_tile<true>(a, l, mt, nt, lds);
         } else {
-            grouped_mn(in - mt2 * nt2, mt13, nt13, 4, mt, nt);
+            grouped_mn<4>(in - mt2 * nt2, mt13, nt13, mt, nt);
             wgrad_tile<false>(a, l, mt, nt, lds);
         }
     }

@@ -228,6 +228,11 @@ int check_desc(const moe_desc *d, bool need_ffn) {
     if (need_ffn) {
         if (d->H < 1 || d->I < 1) return MOE_EINVAL;
         if (d->H % 256 || d->I % 128 || d->pad_rows % 256) return MOE_EUNSUPPORTED;
+        // the GEMM launches number their tiles with 32-bit integers (far past
+        // any shape whose buffers fit in device memory)
+        const int64_t row_tiles = cap / 256 + 1, col_tiles = d->H / 128 + 2 * (int64_t)d->I / 128 + 2;
+        const int64_t wgrad_tiles = (int64_t)d->L * (d->H / 256) * 3 * (d->I / 256 + 1);
+        if (row_tiles * col_tiles + wgrad_tiles >= (1ll << 30)) return MOE_EUNSUPPORTED;
     }
     return MOE_OK;
 }
@@ -749,6 +754,8 @@ int moe_layer_fwd_shared(const moe_desc *d, int32_t Is, const int32_t *routes, c
     if (d->num_batches != 1 || Is < 1) return MOE_EINVAL;
     if (Is % 128) return MOE_EUNSUPPORTED;
     if (d->H > kZeroRowElems) return MOE_EUNSUPPORTED;  // padding rows read the static zero row
+    if (((int64_t)d->P * d->Np / 256 + 1) * (Is / 128 + d->H / 256 + 1) >= (1ll << 30))
+        return MOE_EUNSUPPORTED;  // 32-bit tile numbers
     const void *ptrs[] = {routes, w, X, W13, W2, W13s, W2s, counts, seg_off, phi, route_row, A, Y, As, Ys, out, ws};
     for (const void *p : ptrs)
         if (!p || !aligned16(p)) return MOE_EINVAL;
