@@ -153,7 +153,10 @@ int moe_dispatch(const moe_desc *d, const uint16_t *X, const moe_src *phi, const
  *               chunk c+1 inside one persistent launch (the minibatch T of
  *               [MoK] section 3).
  *   ws   >= moe_workspace_bytes(d, MOE_OP_EXPERT_FFN)
- * Requires H % 256 == 0 and I % 128 == 0 (else MOE_EUNSUPPORTED).
+ * Requires H % 256 == 0 and I % 128 == 0 (else MOE_EUNSUPPORTED).  The
+ * GEMM launches number their 256-row tiles with 32-bit integers: shapes whose
+ * tile counts come near 2^30 (weights of petabytes) are MOE_EUNSUPPORTED for
+ * every call that runs a GEMM.
  */
 int moe_expert_ffn(const moe_desc *d, const uint16_t *Xd, const uint16_t *W13, const uint16_t *W2,
                    const int32_t *seg_off, uint16_t *HU, uint16_t *A, uint16_t *Y, int32_t chunk_rows,
@@ -218,8 +221,8 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
  * Launches: the schedule, one gate/up launch holding the shared and the
  * routed tiles, one down launch holding both, the combine adding S.  The
  * routed rows (HU, A, Y) are bitwise those of moe_layer_fwd.  Errors as
- * moe_layer_fwd, and MOE_EINVAL for Is < 1, MOE_EUNSUPPORTED for Is % 128
- * or H > 65536.
+ * moe_layer_fwd, and MOE_EINVAL for Is < 1, MOE_EUNSUPPORTED for Is % 128,
+ * H > 65536 or shared tile counts past 32-bit tile numbers.
  */
 int moe_layer_fwd_shared(const moe_desc *d, int32_t Is, const int32_t *routes, const float *w, const uint16_t *X,
                          const uint16_t *W13, const uint16_t *W2, const uint16_t *W13s, const uint16_t *W2s,

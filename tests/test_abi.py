@@ -80,6 +80,13 @@ def test_unsupported_shapes():
         assert rc == ops.MOE_EUNSUPPORTED
     d = ops.make_desc(8, 7168, 8, 4096 * 8, 4096)  # L*P beyond the supported table size
     assert lib.moe_capacity_rows(ctypes.byref(d)) == -1
+    # GEMM tiles are numbered with 32-bit integers: a shape with ~4e10 weight-
+    # gradient tiles is refused (its weights alone would be petabytes)
+    big = ops.make_desc(8, 7168, 8, 384, 48, H=1 << 22, I=1 << 22)
+    assert lib.moe_workspace_bytes(ctypes.byref(big), ops.MOE_OP_LAYER_BWD) == -1
+    assert lib.moe_expert_ffn(ctypes.byref(big), *([None] * 7), 0, None, 0, None) == ops.MOE_EUNSUPPORTED
+    ok = ops.make_desc(8, 7168, 8, 384, 48, H=1 << 15, I=1 << 14)
+    assert lib.moe_workspace_bytes(ctypes.byref(ok), ops.MOE_OP_LAYER_BWD) > 0
 
 
 def test_null_arguments_rejected_before_launch():
