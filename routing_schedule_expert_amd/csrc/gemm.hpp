@@ -523,12 +523,13 @@ struct PairStageW {
 };
 
 // Copy of a staged 256 x NC bf16 area (chunks placed as PairStageW writes
-// them) to rows of dst; columns from ncols on are not written.  A thread keeps
-// one 16-byte column chunk for all its rows and issues a batch of LDS reads
-// before the batch's stores (one LDS round trip per batch, not per chunk).
-// tt is the thread index passed through an empty asm by the caller: the
-// addresses, the same for every tile, are then not hoisted out of the tile
-// loop to stay live (and spill) across the next tile's K loop.
+// them, or in place with SWZ = false) to rows of dst; columns from ncols on
+// (a multiple of 8) are not written.  A thread keeps one 16-byte column chunk
+// for all its rows and issues a batch of LDS reads before the batch's stores
+// (one LDS round trip per batch, not per chunk).  tt is the thread index
+// passed through an empty asm by the caller: the addresses, the same for
+// every tile, are then not hoisted out of the tile loop to stay live (and
+// spill) across the next tile's K loop.
 template <int NC, int THREADS, bool SWZ = true>
 __device__ __forceinline__ void copy_staged(const char *area, uint16_t *dst, int64_t ld, int ncols, int tt) {
     constexpr int CPR = NC / 8, RSTEP = THREADS / CPR, kIt = 256 / RSTEP, kBatch = 8;
