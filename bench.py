@@ -665,7 +665,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU's share of the layer; --gpus {args.gpus} (world size {world}) is not "
-              "supported: this build has no multi-GPU path (nothing is sent between GPUs).", file=sys.stderr)
+              "supported: this library has no multi-GPU path (nothing is sent between GPUs).", file=sys.stderr)
         sys.exit(2)
 
     import torch
