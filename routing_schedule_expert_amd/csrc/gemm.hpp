@@ -350,8 +350,13 @@ __device__ __forceinline__ void x_step(char *lds, int slot, int lane, int arow, 
             if (s < SPREAD) {
 #pragma unroll
                 for (int j = 0; j < D; ++j) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, EVERY, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    if constexpr (!AT && !BT) {  // each DMA ahead of its MFMA: the first right after the barrier
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, EVERY, 0);
+                    } else {
+                        __builtin_amdgcn_sched_group_barrier(0x008, EVERY, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                    }
                 }
             }
         }
@@ -367,7 +372,10 @@ __device__ __forceinline__ void x_step(char *lds, int slot, int lane, int arow, 
 // unit busy.  At the gate/up shape this is about 10% faster than the burst
 // and 3.5% faster than spreading the DMAs over two sub-steps (over all four:
 // 10% slower), the stage's loads then start as early as the barrier allows.
-// With both operands MN-contiguous the two-sub-step spread stays 2% faster.  Either operand may be MN-contiguous (AT / BT select TOp):
+// With both operands MN-contiguous the two-sub-step spread stays 2% faster.
+// With both operands K-contiguous (the forward GEMMs) each DMA goes ahead of
+// its MFMA, the first one right after the barrier (gate/up 0.7-1.5% faster;
+// the down dgrad, one MN-contiguous operand, 2.8% slower that way).  Either operand may be MN-contiguous (AT / BT select TOp):
 // a K-contiguous operand's DMA moves 64 elements along its rows per step, an
 // MN-contiguous one's 64 rows; the MFMA inputs, and so the results, are those
 // of the same product with transposed copies.
