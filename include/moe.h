@@ -23,7 +23,8 @@
  *     check launches nothing and writes nothing.  Device data (route ids, the
  *     table) is not validated on the host: route ids outside
  *     [expert_base, expert_base + L) are simply not local (negative "dropped"
- *     ids included) and are skipped.
+ *     ids included) and are skipped; those outside [0, E) are also counted on
+ *     the device (MOE_WS_INVALID_IDS below).
  *   - Results are bitwise reproducible run to run: integer work is exact,
  *     and every floating-point reduction has a fixed order (no float atomics).
  *   - Calls that share buffers must be ordered by the caller (same stream or
@@ -98,6 +99,43 @@ enum {
     MOE_OP_LAYER_FWD_SHARED = 6,
 };
 int64_t moe_workspace_bytes(const moe_desc *d, int op);
+
+/*
+ * Status words the library leaves in a caller's workspace.  Nothing is read
+ * back to the host by the library (it never synchronises); a caller that
+ * wants them copies the words after the call has finished.
+ *
+ *   MOE_WS_INVALID_IDS     int32 per routing table: the number of route ids
+ *                          outside [0, E) the schedule saw (negative "dropped"
+ *                          ids included).  Such ids are never local and are
+ *                          skipped ([MoK] section 2 places only the local
+ *                          routes); the count lets a caller detect a corrupt
+ *                          routing tensor without a host round trip.  Written
+ *                          by every call that runs the schedule: num_batches
+ *                          words for moe_schedule, one for moe_layer_fwd,
+ *                          moe_layer_fwd_mx and moe_layer_fwd_shared, and one
+ *                          per macrobatch (M words) for moe_layer_fwd_ring.
+ *   MOE_WS_BARRIER_STATUS  uint32: 0 after a call whose device-wide waits all
+ *                          completed, 1 if one gave up.  Only the persistent
+ *                          and chunked paths (moe_layer_fwd with
+ *                          MOE_PERSISTENT or chunk_rows > 0, moe_expert_ffn
+ *                          with chunk_rows > 0) wait across workgroups: they
+ *                          clear the word, and every wait is bounded (about a
+ *                          second of spinning) so that a grid whose workgroups
+ *                          were not all resident ends instead of hanging.  When
+ *                          the word is 1 the outputs of that call are
+ *                          undefined.  Other calls leave it untouched.
+ *
+ * moe_workspace_field returns the byte offset of `field` in the workspace of
+ * operation `op` (moe_workspace_bytes), or -1 if d is invalid or op has no
+ * such field.  moe_layer_fwd_mx uses MOE_OP_LAYER_FWD's offsets, and so does
+ * moe_layer_fwd_ring (its workspace is laid out the same way).
+ */
+enum {
+    MOE_WS_INVALID_IDS = 0,
+    MOE_WS_BARRIER_STATUS = 1,
+};
+int64_t moe_workspace_field(const moe_desc *d, int op, int field);
 
 /*
  * moe_schedule — the counting-sort pull schedule of [MoK] section 2 built on

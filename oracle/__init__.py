@@ -19,6 +19,7 @@ Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
   layer_bwd, bwd_tokens, wgrad_elems             pinned (finite differences, torch
                                                   autograd, the dw identity)
   minibatch_floor                                pinned (the printed 2368)
+  invalid_ids                                    pinned (brute force on tiny inputs)
   e4m3_value, e4m3_encode, mx_quantize,          pinned (E4M3 closed form per code, encode-
     mx_quantize_f64, mx_dequantize                 decode identity, ties to even, saturation,
                                                    scale exponent of the block maximum)
@@ -78,6 +79,8 @@ def _load():
         lib.orc_schedule_rescan.restype = i64
         lib.orc_schedule_counting.argtypes = [i32] * 7 + [p, p, p, p, i64, p, p]
         lib.orc_schedule_counting.restype = i64
+        lib.orc_invalid_ids.argtypes = [i64, i32, p]
+        lib.orc_invalid_ids.restype = i64
         lib.orc_dispatch.argtypes = [i32, i32, p, p, i64, p]
         lib.orc_dispatch.restype = None
         lib.orc_expert_ffn_rows.argtypes = [i32, i32, i32, p, p, p, p, p, i64, p, p, p]
@@ -90,14 +93,14 @@ def _load():
         lib.orc_layer_bwd.restype = None
         lib.orc_bwd_tokens.argtypes = [i32, i32, i32, i32, i32, p, p, p, p, p, p, p, i64, p, p]
         lib.orc_bwd_tokens.restype = None
-        lib.orc_wgrad_elems.argtypes = [i64, i32, i32, i32, i32, i32, i32] + [p] * 6 + [p, i64, p, p, i64, p]
+        lib.orc_wgrad_elems.argtypes = [i64, i32, i32, i32, i32, i32, i32] + [p] * 6 + [p, i64, p, p, i64, p, p, p]
         lib.orc_e4m3_value.argtypes = [i32]
         lib.orc_e4m3_value.restype = ctypes.c_double
         lib.orc_e4m3_encode.argtypes = [ctypes.c_double]
         lib.orc_e4m3_encode.restype = i32
         lib.orc_mx_quantize.argtypes = [p, i64, i32, p, p]
         lib.orc_mx_quantize_f64.argtypes = [p, i64, i32, p, p]
-        lib.orc_mx_expert_ffn_rows.argtypes = [i32, i32, i32] + [p] * 7 + [p, i64, p, p, p, p]
+        lib.orc_mx_expert_ffn_rows.argtypes = [i32, i32, i32] + [p] * 7 + [p, i64, p, p, p, p, p, p]
         lib.orc_mx_layer_fwd_tokens.argtypes = [i32, i32, i32, i32, i32] + [p] * 8 + [p, i64, p]
         lib.orc_wgrad_elems.restype = None
         _lib = lib
@@ -183,6 +186,12 @@ def schedule_counting(routes: np.ndarray, L: int, base: int = 0, pad: int = 256,
 def schedule_rescan(routes: np.ndarray, L: int, base: int = 0, pad: int = 256) -> Schedule:
     """The older per-(expert, peer) rescanning scheduler: lists merged round-robin."""
     return _schedule_call("rescan", routes, L, base, pad, None)
+
+
+def invalid_ids(routes: np.ndarray, E: int) -> int:
+    """Number of route ids outside [0, E) (never local; counted on the device)."""
+    routes = _i32(routes)
+    return int(_load().orc_invalid_ids(routes.size, E, _ptr(routes)))
 
 
 def dispatch(X: np.ndarray, phi: np.ndarray) -> np.ndarray:
@@ -279,8 +288,11 @@ def bwd_tokens(routes, w, X, W13, W2, dOut, L: int, base: int, tokens):
     return dX, dw
 
 
-def wgrad_elems(routes, w, X, W13, W2, dOut, L: int, base: int, expert: int, w13_elems, w2_elems):
-    """Listed elements of dW13[expert] ((n, k) pairs) and dW2[expert] ((m, n) pairs)."""
+def wgrad_elems(routes, w, X, W13, W2, dOut, L: int, base: int, expert: int, w13_elems, w2_elems,
+                with_abs: bool = False):
+    """Listed elements of dW13[expert] ((n, k) pairs) and dW2[expert] ((m, n)
+    pairs); with_abs also returns, per element, the sum of its terms' absolute
+    values (the scale of the error that roundings of the terms can cause)."""
     routes = _i32(routes)
     P, Np, K = routes.shape
     w = np.ascontiguousarray(w, np.float32)
@@ -291,9 +303,12 @@ def wgrad_elems(routes, w, X, W13, W2, dOut, L: int, base: int, expert: int, w13
     e2 = np.ascontiguousarray(np.asarray(w2_elems, np.int64).reshape(-1, 2))
     g13 = np.zeros(e13.shape[0])
     g2 = np.zeros(e2.shape[0])
+    a13 = np.zeros(e13.shape[0]) if with_abs else None
+    a2 = np.zeros(e2.shape[0]) if with_abs else None
     _load().orc_wgrad_elems(P * Np, K, L, base, H, I, expert, _ptr(routes), _ptr(w), _ptr(X), _ptr(W13), _ptr(W2),
-                            _ptr(dOut), _ptr(e13), e13.shape[0], _ptr(g13), _ptr(e2), e2.shape[0], _ptr(g2))
-    return g13, g2
+                            _ptr(dOut), _ptr(e13), e13.shape[0], _ptr(g13), _ptr(e2), e2.shape[0], _ptr(g2),
+                            _ptr(a13), _ptr(a2))
+    return (g13, g2, a13, a2) if with_abs else (g13, g2)
 
 
 # ---------------------------------------------------------------------------
@@ -357,10 +372,12 @@ def mx_dispatch(Xq: np.ndarray, Xs: np.ndarray, phi: np.ndarray):
     return q, s
 
 
-def mx_expert_ffn_rows(seg_off, Xdq, Xds, W13q, W13s, W2q, W2s, rows=None):
+def mx_expert_ffn_rows(seg_off, Xdq, Xds, W13q, W13s, W2q, W2s, rows=None, with_hu=False):
     """MXFP8 expert FFN of the listed dispatched rows: dict with A (double
     [n][I], before quantization), Aq / As (its MX codes and scales) and Y
-    (double [n][H], from the quantized A)."""
+    (double [n][H], from the quantized A).  with_hu adds HU (double [n][2I]:
+    h then u) and HUabs (the sums of the magnitudes of the terms of each h and
+    u, which scale any accumulation error in them)."""
     seg_off = _i32(seg_off)
     arrs = [np.ascontiguousarray(a, np.uint8) for a in (Xdq, Xds, W13q, W13s, W2q, W2s)]
     Xdq, Xds, W13q, W13s, W2q, W2s = arrs
@@ -372,9 +389,14 @@ def mx_expert_ffn_rows(seg_off, Xdq, Xds, W13q, W13s, W2q, W2s, rows=None):
     Aq = np.zeros((n, I), np.uint8)
     As = np.zeros((n, I // 32), np.uint8)
     Y = np.zeros((n, H))
+    HU = np.zeros((n, 2 * I)) if with_hu else None
+    HUabs = np.zeros((n, 2 * I)) if with_hu else None
     _load().orc_mx_expert_ffn_rows(L, H, I, _ptr(seg_off), *[_ptr(a) for a in arrs], _ptr(rows), n, _ptr(A),
-                                   _ptr(Aq), _ptr(As), _ptr(Y))
-    return {"A": A, "Aq": Aq, "As": As, "Y": Y}
+                                   _ptr(Aq), _ptr(As), _ptr(Y), _ptr(HU), _ptr(HUabs))
+    r = {"A": A, "Aq": Aq, "As": As, "Y": Y}
+    if with_hu:
+        r["HU"], r["HUabs"] = HU, HUabs
+    return r
 
 
 def mx_layer_fwd_tokens(routes, w, Xq, Xs, W13q, W13s, W2q, W2s, L: int, base: int = 0, tokens=None):

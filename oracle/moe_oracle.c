@@ -289,6 +289,17 @@ int64_t orc_schedule_counting(int P, int Np, int K, int L, int base, int pad, in
 /* each (expert, peer) token list in scan order and merges the lists round-   */
 /* robin (round o visits peers 0..P-1 and takes item o where it exists).      */
 /* It never evaluates the position formula, so it is an independent check.   */
+/* Route ids outside [0, E) in a routing tensor of n ids.  The schedule
+ * places only local routes ([MoK] section 2); an id that names no expert at
+ * all (a negative "dropped" slot, or one past the last expert) is counted so
+ * a caller can tell a corrupt routing tensor from a merely non-local one. */
+int64_t orc_invalid_ids(int64_t n, int E, const int32_t *routes) {
+    int64_t bad = 0;
+    for (int64_t i = 0; i < n; ++i)
+        if (routes[i] < 0 || routes[i] >= E) ++bad;
+    return bad;
+}
+
 /* ------------------------------------------------------------------------ */
 
 int64_t orc_schedule_rescan(int P, int Np, int K, int L, int base, int pad,
@@ -707,20 +718,52 @@ void orc_bwd_tokens(int K, int L, int base, int H, int I, const int32_t *routes,
     }
 }
 
+/* Selected elements of the weight gradients of local expert l ([BPT]
+ * section 2.C: sums over the token dimension):
+ *   dW13[l][nn][k] = sum over routes to l of d{h,u}[n] * x[k]   (n = nn mod I;
+ *                    dh for gate rows nn < I, du for up rows),
+ *   dW2[l][m][n]   = sum over routes to l of w * dOut[m] * a[n],
+ * routes taken in ascending (token, slot) order.  The per-route quantities of
+ * a column n (h, u and dA' = W2[:, n] . dOut) are computed once per route and
+ * shared by every requested element of that column; each element's sum still
+ * runs over the routes in that order.  a13 / a2 (nullable) receive the sums
+ * of the terms' absolute values: a rounding of relative size e in every term
+ * moves the sum by at most e times that, which bounds the error of a result
+ * computed from rounded intermediates. */
 void orc_wgrad_elems(int64_t ntok, int K, int L, int base, int H, int I, int l,
                      const int32_t *routes, const float *w, const uint16_t *X,
                      const uint16_t *W13, const uint16_t *W2, const uint16_t *dOut,
                      const int64_t *w13_elems, int64_t n13, double *g13,
-                     const int64_t *w2_elems, int64_t n2, double *g2) {
+                     const int64_t *w2_elems, int64_t n2, double *g2,
+                     double *a13, double *a2) {
     const uint16_t *w13 = W13 + (int64_t)l * 2 * I * H;
     const uint16_t *w2 = W2 + (int64_t)l * H * I;
     (void)L;
-    /* dW13[l][n][k] = sum_routes d{h,u}[n] * x[k] */
-#pragma omp parallel for schedule(dynamic, 1)
+    /* the distinct columns n and, per column, its requested elements */
+    int *cnt = (int *)calloc((size_t)I + 1, sizeof(int));
+    for (int64_t q = 0; q < n13; ++q) cnt[(w13_elems[2 * q] % I) + 1]++;
+    for (int64_t q = 0; q < n2; ++q) cnt[w2_elems[2 * q + 1] + 1]++;
+    for (int n = 0; n < I; ++n) cnt[n + 1] += cnt[n];
+    int64_t *items = (int64_t *)malloc((size_t)(n13 + n2 + 1) * sizeof(int64_t));
+    int *fill = (int *)calloc((size_t)I, sizeof(int));
+    /* item >= 0: a dW13 element; item < 0: dW2 element -item - 1 */
     for (int64_t q = 0; q < n13; ++q) {
-        int64_t nn = w13_elems[2 * q], kk = w13_elems[2 * q + 1];
-        int n = (int)(nn < I ? nn : nn - I);
-        double s = 0.0;
+        int n = (int)(w13_elems[2 * q] % I);
+        items[cnt[n] + fill[n]++] = q;
+    }
+    for (int64_t q = 0; q < n2; ++q) {
+        int n = (int)w2_elems[2 * q + 1];
+        items[cnt[n] + fill[n]++] = -q - 1;
+    }
+    for (int64_t q = 0; q < n13; ++q) g13[q] = 0.0;
+    for (int64_t q = 0; q < n2; ++q) g2[q] = 0.0;
+    if (a13)
+        for (int64_t q = 0; q < n13; ++q) a13[q] = 0.0;
+    if (a2)
+        for (int64_t q = 0; q < n2; ++q) a2[q] = 0.0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int n = 0; n < I; ++n) {
+        if (cnt[n + 1] == cnt[n]) continue;
         for (int64_t g = 0; g < ntok; ++g)
             for (int j = 0; j < K; ++j) {
                 if (routes[g * K + j] != base + l) continue;
@@ -731,30 +774,26 @@ void orc_wgrad_elems(int64_t ntok, int K, int L, int base, int H, int I, int l,
                     uu += xk * widen_bf16(w13[(int64_t)(I + n) * H + k]);
                     d += widen_bf16(dOut[g * H + k]) * widen_bf16(w2[(int64_t)k * I + n]);
                 }
-                double dA = (double)w[g * K + j] * d;
-                double grad = nn < I ? dA * uu * silu_grad(hh) : dA * silu(hh);
-                s += grad * widen_bf16(X[g * H + kk]);
-            }
-        g13[q] = s;
-    }
-    /* dW2[l][m][n] = sum_routes w * dOut[m] * a[n] */
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t q = 0; q < n2; ++q) {
-        int64_t m = w2_elems[2 * q], n = w2_elems[2 * q + 1];
-        double s = 0.0;
-        for (int64_t g = 0; g < ntok; ++g)
-            for (int j = 0; j < K; ++j) {
-                if (routes[g * K + j] != base + l) continue;
-                double hh = 0.0, uu = 0.0;
-                for (int k = 0; k < H; ++k) {
-                    double xk = widen_bf16(X[g * H + k]);
-                    hh += xk * widen_bf16(w13[(int64_t)n * H + k]);
-                    uu += xk * widen_bf16(w13[(int64_t)(I + n) * H + k]);
+                double wr = (double)w[g * K + j];
+                double dA = wr * d;
+                for (int c = cnt[n]; c < cnt[n + 1]; ++c) {
+                    int64_t it = items[c];
+                    if (it >= 0) {
+                        int64_t nn = w13_elems[2 * it], kk = w13_elems[2 * it + 1];
+                        double grad = nn < I ? dA * uu * silu_grad(hh) : dA * silu(hh);
+                        double t = grad * widen_bf16(X[g * H + kk]);
+                        g13[it] += t;
+                        if (a13) a13[it] += fabs(t);
+                    } else {
+                        int64_t q = -it - 1, m = w2_elems[2 * q];
+                        double t = wr * widen_bf16(dOut[g * H + m]) * silu(hh) * uu;
+                        g2[q] += t;
+                        if (a2) a2[q] += fabs(t);
+                    }
                 }
-                s += (double)w[g * K + j] * widen_bf16(dOut[g * H + m]) * silu(hh) * uu;
             }
-        g2[q] = s;
     }
+    free(cnt); free(items); free(fill);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -851,7 +890,7 @@ static double mx_value(const uint8_t *q, const uint8_t *s, int64_t i) {
 void orc_mx_expert_ffn_rows(int L, int H, int I, const int32_t *seg_off, const uint8_t *Xq,
                             const uint8_t *Xs, const uint8_t *W13q, const uint8_t *W13s,
                             const uint8_t *W2q, const uint8_t *W2s, const int64_t *rows, int64_t nrows,
-                            double *A, uint8_t *Aq, uint8_t *As, double *Y) {
+                            double *A, uint8_t *Aq, uint8_t *As, double *Y, double *HUv, double *HUabs) {
 #pragma omp parallel
     {
         double *x = (double *)malloc(sizeof(double) * H);
@@ -864,18 +903,31 @@ void orc_mx_expert_ffn_rows(int L, int H, int I, const int32_t *seg_off, const u
             int l = expert_of_row(seg_off, L, row);
             for (int k = 0; k < H; ++k) x[k] = mx_value(Xq + row * H, Xs + row * (H / 32), k);
             for (int n = 0; n < I; ++n) {
-                double h = 0.0, u = 0.0;
+                double h = 0.0, u = 0.0, habs = 0.0, uabs = 0.0;
                 if (l >= 0) {
                     const uint8_t *gq = W13q + ((int64_t)l * 2 * I + n) * H;
                     const uint8_t *gs = W13s + ((int64_t)l * 2 * I + n) * (H / 32);
                     const uint8_t *uq = W13q + ((int64_t)l * 2 * I + I + n) * H;
                     const uint8_t *us = W13s + ((int64_t)l * 2 * I + I + n) * (H / 32);
                     for (int k = 0; k < H; ++k) {
-                        h += x[k] * mx_value(gq, gs, k);
-                        u += x[k] * mx_value(uq, us, k);
+                        double th = x[k] * mx_value(gq, gs, k), tu = x[k] * mx_value(uq, us, k);
+                        h += th;
+                        u += tu;
+                        habs += fabs(th);
+                        uabs += fabs(tu);
                     }
                 }
                 a[n] = silu(h) * u;
+                /* h, u and the sums of their terms' magnitudes (the scale of
+                 * any accumulation error in h and u), gate then up */
+                if (HUv) {
+                    HUv[qi * 2 * I + n] = h;
+                    HUv[qi * 2 * I + I + n] = u;
+                }
+                if (HUabs) {
+                    HUabs[qi * 2 * I + n] = habs;
+                    HUabs[qi * 2 * I + I + n] = uabs;
+                }
             }
             orc_mx_quantize_f64(a, 1, I, aq, as);
             if (A) memcpy(A + qi * I, a, sizeof(double) * I);

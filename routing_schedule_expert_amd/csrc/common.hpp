@@ -76,7 +76,8 @@ __device__ __forceinline__ uint64_t match_lanes_n(uint32_t v) {
 // x, [16+x] release epoch of XCD x, [24+x] workgroups on XCD x, [32] XCDs in
 // use.  Every wait is bounded (about a second): if the grid were not
 // co-resident the kernel finishes with undefined results and bar[2] = 1
-// instead of hanging.  Only thread 0 of a workgroup holds meaningful fields.
+// instead of hanging (bar[2] is the caller-visible MOE_WS_BARRIER_STATUS
+// word).  Only thread 0 of a workgroup holds meaningful fields.
 
 __device__ __forceinline__ uint32_t xcc_id() {
     uint32_t v;

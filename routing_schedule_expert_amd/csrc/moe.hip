@@ -261,13 +261,20 @@ int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 // Workspace of the shared expert's identity table: 2 offsets, then the rows.
 int64_t shared_table_bytes(const moe_desc *d) { return 256 + align256(shared_rows(d) * 8); }
 
-// Schedule workspace: per-chunk counts, then (L <= 255) every route's local id
-// as a byte in blocks of kSchedBlock (SchedArgs::ids8).
+// Schedule workspace: the per-table count of route ids outside [0, E) (int32
+// [nb], at byte 0, documented in moe.h), the per-chunk counts, the per-chunk
+// invalid-id counts, then (L <= 255) every route's local id as a byte in
+// blocks of kSchedBlock (SchedArgs::ids8).
+int64_t sched_invalid_bytes(const moe_desc *d) { return align256(4ll * d->num_batches); }
 int64_t sched_counts_bytes(const moe_desc *d) { return align256(4ll * d->num_batches * d->P * sched_chunks(d) * d->L); }
+int64_t sched_winv_bytes(const moe_desc *d) { return align256(4ll * d->num_batches * d->P * sched_chunks(d)); }
 int64_t sched_nblk(const moe_desc *d) { return ((int64_t)d->Np * d->K + kSchedBlock - 1) / kSchedBlock; }
+int64_t sched_ids8_offset(const moe_desc *d) {
+    return sched_invalid_bytes(d) + sched_counts_bytes(d) + sched_winv_bytes(d);
+}
 int64_t sched_ws_bytes(const moe_desc *d) {
     const int64_t ids = d->L <= 255 ? align256((int64_t)d->num_batches * d->P * sched_nblk(d) * kSchedBlock) : 0;
-    return sched_counts_bytes(d) + ids;
+    return sched_ids8_offset(d) + ids;
 }
 
 int bwd_nparts(const moe_desc *d) { return (d->I + 255) / 256; }  // one dw partial per 256-column tile
@@ -291,7 +298,10 @@ void fill_sched_args(SchedArgs &a, const moe_desc *d, const int32_t *routes, int
     a.seg_off = seg_off;
     a.phi = phi;
     a.route_row = route_row;
-    a.wcnt = reinterpret_cast<int32_t *>(ws);
+    a.invalid_ids = reinterpret_cast<int32_t *>(ws);
+    a.wcnt = reinterpret_cast<int32_t *>(ws + sched_invalid_bytes(d));
+    a.winv = reinterpret_cast<int32_t *>(ws + sched_invalid_bytes(d) + sched_counts_bytes(d));
+    a.E = d->E;
     a.P = d->P;
     a.R = d->Np * d->K;
     a.K = d->K;
@@ -307,7 +317,7 @@ void fill_sched_args(SchedArgs &a, const moe_desc *d, const int32_t *routes, int
     a.cap = cap_rows(d);
     a.pstride = a.R;
     a.bstride = (int64_t)a.P * a.R;
-    a.ids8 = d->L <= 255 ? reinterpret_cast<uint8_t *>(ws + sched_counts_bytes(d)) : nullptr;
+    a.ids8 = d->L <= 255 ? reinterpret_cast<uint8_t *>(ws + sched_ids8_offset(d)) : nullptr;
     a.nblk = (int32_t)sched_nblk(d);
 }
 
@@ -318,7 +328,7 @@ constexpr size_t kMaxLds = 160 * 1024;  // LDS of one gfx950 workgroup
 size_t sched_lds_bytes(const moe_desc *d, int wpw, int stage = -1) {
     const size_t L = d->L, P = d->P;
     const size_t mstride = P <= (size_t)kSchedPMax ? (size_t)kSchedPMax : P;
-    size_t count = wpw * (L + 1), fin = P * L + L + 16, scat = L * mstride + L + 1 + wpw * (L + 2 * kSchedBlock);
+    size_t count = wpw * (L + 1), fin = P * L + L + 17, scat = L * mstride + L + 1 + wpw * (L + 2 * kSchedBlock);
     if (stage == 0) return 4 * count;
     if (stage == 1) return 4 * fin;
     if (stage == 2) return 4 * scat;
@@ -489,6 +499,23 @@ int64_t moe_workspace_bytes(const moe_desc *d, int op) {
         }
         default: return -1;
     }
+}
+
+int64_t moe_workspace_field(const moe_desc *d, int op, int field) {
+    if (moe_workspace_bytes(d, op) < 0) return -1;
+    // barrier words (LAYER_FWD, EXPERT_FFN) at byte 0, word 2 the give-up
+    // flag; the schedule's workspace after them (LAYER_FWD, LAYER_FWD_SHARED)
+    // or alone (SCHEDULE), its invalid-id counts at its byte 0
+    if (field == MOE_WS_INVALID_IDS) {
+        if (op == MOE_OP_SCHEDULE) return 0;
+        if (op == MOE_OP_LAYER_FWD || op == MOE_OP_LAYER_FWD_SHARED) return kBarrierBytes;
+        return -1;
+    }
+    if (field == MOE_WS_BARRIER_STATUS) {
+        if (op == MOE_OP_LAYER_FWD || op == MOE_OP_EXPERT_FFN) return 8;
+        return -1;
+    }
+    return -1;
 }
 
 int moe_schedule(const moe_desc *d, const int32_t *routes, int32_t *counts, int32_t *seg_off, moe_src *phi,

@@ -40,7 +40,14 @@ struct SchedArgs {
     moe_src *phi;           // [nb][cap]
     int32_t *route_row;     // same layout as routes
     int32_t *wcnt;          // ws: [nb][P][W][L] counts, then exclusive offsets
+    // Route ids outside [0, E): per chunk (ws, [nb][P][W], written by the
+    // count stage) and per table (ws, [nb], their sum, written by the
+    // finalize).  Such ids are never local; the sum lets a caller detect a
+    // corrupt routing tensor without a host round trip.
+    int32_t *winv;
+    int32_t *invalid_ids;
     int32_t P, R, K, L, base, pad, nb, W, wg_per_part, nbits;
+    int32_t E;
     int32_t wpw;  // waves per workgroup (chunks handled by one workgroup)
     int32_t cb;   // 1024-route blocks per chunk (a chunk is one logical thread)
     int64_t cap;
@@ -106,7 +113,7 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *tmp 
 
 // Stages 2 and 3 for batch b: per (partition, expert) exclusive prefix of the
 // per-chunk counts (in place), M[l][r], and the padded segment offsets S.
-// smem: P*L + L + 16 ints.
+// smem: P*L + L + 17 ints.
 __device__ void sched_finalize(const SchedArgs &a, int b, int32_t *smem) {
     const int L = a.L, P = a.P, W = a.W;
     int32_t *wc = a.wcnt + (int64_t)b * P * W * L;
@@ -114,7 +121,16 @@ __device__ void sched_finalize(const SchedArgs &a, int b, int32_t *smem) {
     int32_t *s_tot = smem;          // [P][L]
     int32_t *s_len = s_tot + P * L; // [L]
     int32_t *s_tmp = s_len + L;     // [16]
+    int32_t *s_inv = s_tmp + 16;    // [1]
     __syncthreads();
+    if (threadIdx.x == 0) *s_inv = 0;
+    __syncthreads();
+    {  // ids outside [0, E) over the table's chunks (integer sum, exact in any order)
+        const int32_t *wi = a.winv + (int64_t)b * P * W;
+        int32_t n = 0;
+        for (int i = threadIdx.x; i < P * W; i += blockDim.x) n += wi[i];
+        if (n) __hip_atomic_fetch_add(s_inv, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     for (int pr = threadIdx.x; pr < P * L; pr += blockDim.x) {
         const int r = pr / L, l = pr % L;
         int32_t *col = wc + (int64_t)r * W * L + l;
@@ -153,6 +169,8 @@ __device__ void sched_finalize(const SchedArgs &a, int b, int32_t *smem) {
         acc += s_len[l];
     }
     if (threadIdx.x == blockDim.x - 1) so[L] = acc;  // the last thread's run ends at L
+    __syncthreads();
+    if (threadIdx.x == 0) a.invalid_ids[b] = *s_inv;
 }
 
 // Stage 1: per-chunk counts.  x is the workgroup's index in the schedule grid
@@ -181,6 +199,7 @@ __device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
         };
         int32_t e[kSchedUnroll];
         load_block((int64_t)w * a.cb * kSchedBlock, e);
+        int32_t ninv = 0;
         for (int blk = 0; blk < a.cb; ++blk) {
             const int64_t lo = ((int64_t)w * a.cb + blk) * kSchedBlock;
             if (lo >= a.R) break;
@@ -193,17 +212,22 @@ __device__ void sched_count_body(const SchedArgs &a, int32_t *smem, int x) {
                 word[u >> 2] |= v << (8 * (u & 3));
                 if (v < (uint32_t)L)
                     __hip_atomic_fetch_add(cnt + v, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                // ids outside [0, E) among the routes that exist (past R the
+                // loads filled -1)
+                ninv += (lo + u * kWave + lane < a.R && (uint32_t)e[u] >= (uint32_t)a.E) ? 1 : 0;
             }
             if (a.ids8)
                 *reinterpret_cast<u32x4 *>(ids8_block(a, b, r, (int64_t)w * a.cb + blk) + lane * 16) = word;
 #pragma unroll
             for (int u = 0; u < kSchedUnroll; ++u) e[u] = en[u];
         }
+        if (ninv) __hip_atomic_fetch_add(cnt + L, ninv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     __syncthreads();
     if (w < a.W) {
         int32_t *dst = a.wcnt + (((int64_t)b * a.P + r) * a.W + w) * L;
         for (int l = lane; l < L; l += kWave) dst[l] = cnt[l];
+        if (lane == 0) a.winv[((int64_t)b * a.P + r) * a.W + w] = cnt[L];
     }
 }
 
@@ -341,8 +365,11 @@ __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
         const int32_t *src = a.routes + (int64_t)b * a.bstride + (int64_t)r * a.pstride;
         int32_t *rrow = a.route_row + (int64_t)b * a.bstride + (int64_t)r * a.pstride;
         for (int blk = 0; blk < a.cb; ++blk) {
-            const int32_t lo = (w * a.cb + blk) * kSchedBlock;
-            if (lo >= a.R) break;
+            // 64-bit before the bound check: near R = 2^31 the block start of
+            // a trailing block would not fit in 32 bits
+            const int64_t lo64 = ((int64_t)w * a.cb + blk) * kSchedBlock;
+            if (lo64 >= a.R) break;
+            const int32_t lo = (int32_t)lo64;  // < R < 2^31
             uint32_t v[kSchedUnroll];
             if (a.ids8) {  // the count stage's bytes: a quarter of the ids' traffic
                 const u32x4 word = __builtin_nontemporal_load(
@@ -353,7 +380,7 @@ __device__ void sched_scatter_body(const SchedArgs &a, int32_t *smem, int x) {
                 int32_t e[kSchedUnroll];
 #pragma unroll
                 for (int u = 0; u < kSchedUnroll; ++u) {
-                    const int32_t i = lo + u * kWave + lane;
+                    const int64_t i = lo64 + u * kWave + lane;
                     e[u] = i < a.R ? __builtin_nontemporal_load(src + i) : -1;
                 }
 #pragma unroll

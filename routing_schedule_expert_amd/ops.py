@@ -22,9 +22,11 @@ MOE_OK, MOE_EINVAL, MOE_ENOSPC, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3, -4
 (MOE_OP_SCHEDULE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_LAYER_FWD, MOE_OP_LAYER_BWD,
  MOE_OP_LAYER_FWD_SHARED) = range(7)
 MOE_PERSISTENT = 1
+MOE_WS_INVALID_IDS, MOE_WS_BARRIER_STATUS = 0, 1
 
 EXPORTED = (
-    "moe_strerror", "moe_capacity_rows", "moe_workspace_bytes", "moe_schedule", "moe_dispatch",
+    "moe_strerror", "moe_capacity_rows", "moe_workspace_bytes", "moe_workspace_field", "moe_schedule",
+    "moe_dispatch",
     "moe_expert_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_bwd", "moe_trace_enable", "moe_trace_read",
     "moe_quantize_mx",
     "moe_layer_fwd_mx",
@@ -68,6 +70,7 @@ def load() -> ctypes.CDLL:
         "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "moe_capacity_rows": (i64, [D]),
         "moe_workspace_bytes": (i64, [D, ctypes.c_int]),
+        "moe_workspace_field": (i64, [D, ctypes.c_int, ctypes.c_int]),
         "moe_schedule": (ctypes.c_int, [D, P, P, P, P, P, P, sz, P]),
         "moe_dispatch": (ctypes.c_int, [D, P, P, P, P, P]),
         "moe_expert_ffn": (ctypes.c_int, [D, P, P, P, P, P, P, P, i32, P, sz, P]),
@@ -131,6 +134,19 @@ def workspace_bytes(d: moe_desc, op: int) -> int:
     if n < 0:
         raise MoeError(MOE_EINVAL, "moe_workspace_bytes")
     return int(n)
+
+
+def workspace_field(d: moe_desc, op: int, field: int) -> int:
+    """Byte offset of a status word (MOE_WS_*) in op's workspace; -1 if op has none."""
+    return int(load().moe_workspace_field(ctypes.byref(d), op, field))
+
+
+def read_ws_words(ws: torch.Tensor, offset: int, n: int = 1) -> list:
+    """The n int32 words at byte `offset` of a workspace tensor (synchronises
+    the tensor's stream by copying to the host)."""
+    if offset < 0:
+        raise ValueError("no such workspace field")
+    return [int(v) for v in ws[offset:offset + 4 * n].cpu().view(torch.int32).tolist()]
 
 
 def moe_schedule(d, routes, counts, seg_off, phi, route_row, ws, stream=None):

@@ -34,6 +34,47 @@ def rel_l2(got, ref) -> float:
     return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
 
 
+def rows_rel_l2(got, ref) -> np.ndarray:
+    """Per-row rel-L2 (rows = first axis).  A row whose reference is all zero
+    scores 0 if the result row is all zero too, else infinity."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    got = got.reshape(got.shape[0], -1)
+    ref = ref.reshape(ref.shape[0], -1)
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    safe = np.where(den > 0, den, 1.0)
+    return np.where(den > 0, num / safe, np.where(num > 0, np.inf, 0.0))
+
+
+def assert_rows(name, got, ref, tol, ids=None):
+    """Every row within rel-L2 tol of its reference row; prints the worst row
+    (its index in `ids` when given) and the aggregate rel-L2."""
+    rel = rows_rel_l2(got, ref)
+    if rel.size == 0:
+        return
+    i = int(np.argmax(rel))
+    where = int(ids[i]) if ids is not None else i
+    print(f"    {name}: {rel.size} rows, worst row {where} rel-L2 {rel[i]:.2e}, "
+          f"aggregate {rel_l2(got, ref):.2e}", flush=True)
+    assert rel[i] <= tol, f"{name}: row {where} rel-L2 {rel[i]:.3e} > {tol}"
+
+
+def assert_elems(name, got, ref, tol):
+    """Scalars (dot products that may cancel): |got - ref| <= tol * max(|ref|,
+    rms(ref)) for every element; prints the worst one."""
+    got = np.asarray(got, np.float64).reshape(-1)
+    ref = np.asarray(ref, np.float64).reshape(-1)
+    if ref.size == 0:
+        return
+    floor = np.sqrt(np.mean(ref * ref))
+    scale = np.maximum(np.abs(ref), floor if floor > 0 else 1.0)
+    err = np.abs(got - ref) / scale
+    i = int(np.argmax(err))
+    print(f"    {name}: {ref.size} elements, worst {i} scaled error {err[i]:.2e}", flush=True)
+    assert err[i] <= tol, f"{name}: element {i} got {got[i]!r} want {ref[i]!r} (scaled error {err[i]:.3e})"
+
+
 def digest(*tensors) -> str:
     h = hashlib.sha256()
     for t in tensors:
@@ -57,5 +98,6 @@ def gpu_schedule(routes: np.ndarray, L: int, base: int = 0, pad: int = 256, E: i
     ws = torch.full((ops.workspace_bytes(d, ops.MOE_OP_SCHEDULE),), 0x5A, dtype=torch.uint8, device=dev())
     ops.moe_schedule(d, rt, counts, seg_off, phi, route_row, ws)
     torch.cuda.synchronize()
+    inv = ops.read_ws_words(ws, ops.workspace_field(d, ops.MOE_OP_SCHEDULE, ops.MOE_WS_INVALID_IDS), nb)
     return {"counts": counts.cpu().numpy(), "seg_off": seg_off.cpu().numpy(), "phi": phi.cpu().numpy(),
-            "route_row": route_row.cpu().numpy(), "cap": cap}
+            "route_row": route_row.cpu().numpy(), "cap": cap, "invalid": inv, "E": E}

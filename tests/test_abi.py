@@ -206,3 +206,37 @@ def test_ring_sizes_and_arguments_rejected_before_launch():
 
 def test_trace_read_empty():
     assert ops.moe_trace_read(4) == []
+
+
+def test_workspace_fields():
+    """Status words: the invalid-id counts sit at the start of the schedule's
+    workspace (after the 256 barrier bytes in the layer forward), the barrier
+    give-up word at byte 8 of the calls that wait across workgroups."""
+    d = kimi()
+    f = ops.workspace_field
+    assert f(d, ops.MOE_OP_SCHEDULE, ops.MOE_WS_INVALID_IDS) == 0
+    assert f(d, ops.MOE_OP_LAYER_FWD, ops.MOE_WS_INVALID_IDS) == 256
+    assert f(d, ops.MOE_OP_LAYER_FWD_SHARED, ops.MOE_WS_INVALID_IDS) == 256
+    assert f(d, ops.MOE_OP_LAYER_FWD, ops.MOE_WS_BARRIER_STATUS) == 8
+    assert f(d, ops.MOE_OP_EXPERT_FFN, ops.MOE_WS_BARRIER_STATUS) == 8
+    for op, field in ((ops.MOE_OP_SCHEDULE, ops.MOE_WS_BARRIER_STATUS), (ops.MOE_OP_DISPATCH, 0),
+                      (ops.MOE_OP_LAYER_BWD, 0), (ops.MOE_OP_LAYER_FWD, 7)):
+        assert f(d, op, field) == -1
+    for op in (ops.MOE_OP_SCHEDULE, ops.MOE_OP_LAYER_FWD):
+        off = f(d, op, ops.MOE_WS_INVALID_IDS)
+        assert 0 <= off and off + 4 <= ops.workspace_bytes(d, op)
+    bad = kimi()
+    bad.P = 0
+    assert f(bad, ops.MOE_OP_SCHEDULE, ops.MOE_WS_INVALID_IDS) == -1
+
+
+def test_route_count_bound():
+    """Routes per partition up to the 32-bit capacity bound are accepted (the
+    schedule indexes its blocks with 64-bit starts), one more is not."""
+    lib = ops.load()
+    # P = 1, K = 1, L = 1, pad 256: cap = Np + 255 must stay below 2^31 - 256
+    ok = ops.make_desc(1, 2**31 - 1024, 1, 2, 1)
+    assert lib.moe_capacity_rows(ctypes.byref(ok)) == 2**31 - 1024 + 255
+    assert lib.moe_workspace_bytes(ctypes.byref(ok), ops.MOE_OP_SCHEDULE) > 2**31 - 1024
+    over = ops.make_desc(1, 2**31 - 511, 1, 2, 1)
+    assert lib.moe_capacity_rows(ctypes.byref(over)) == -1

@@ -18,7 +18,9 @@ pytestmark = pytest.mark.gpu
 def check(routes, L, base=0, pad=256, E=None, NT=1024):
     r = routes if routes.ndim == 4 else routes[None]
     g = gpu_schedule(r, L, base, pad, E, NT)
+    E_used = g["E"]
     for b in range(r.shape[0]):
+        assert g["invalid"][b] == oracle.invalid_ids(r[b], E_used), f"invalid-id count batch {b}"
         s = oracle.schedule(r[b], L, base, pad)
         np.testing.assert_array_equal(g["counts"][b], s.counts, err_msg=f"counts batch {b}")
         np.testing.assert_array_equal(g["seg_off"][b], s.seg_off, err_msg=f"seg_off batch {b}")
@@ -85,7 +87,10 @@ NAMED = ["uniform", "zipf1.2", "zipf1.5", "hot4", "one_expert", "no_local", "par
 def test_named_case(name):
     print(f"[schedule] case {name}", flush=True)
     routes, L = named_case(name)
-    check(routes, L, E=max(int(routes.max()) + 1, L))
+    # out_of_range: ids in [-5, 30) against 20 experts, so both negative and
+    # too-large ids reach the invalid-id count
+    E = 20 if name == "out_of_range" else max(int(routes.max()) + 1, L)
+    check(routes, L, E=E)
 
 
 def test_random_cases():
@@ -122,9 +127,12 @@ def test_batched(nb):
 def test_batched_kimi_64():
     rng = inputs.rng_for(64)
     r = np.stack([inputs.routes_uniform(rng, 8, 7168, 384, 8)[0] for _ in range(64)])
+    r[5, 2, 100, 3] = -1   # one dropped slot and one id past the last expert
+    r[63, 7, 7000, 0] = 384
     print("[schedule] batched kimi nb=64", flush=True)
-    g = gpu_schedule(r, 48)
-    for b in (0, 1, 7, 8, 33, 63):
+    g = gpu_schedule(r, 48, E=384)
+    assert [b for b in range(64) if g["invalid"][b]] == [5, 63] and g["invalid"][5] == g["invalid"][63] == 1
+    for b in (0, 1, 5, 7, 8, 33, 63):
         s = oracle.schedule(r[b], 48, 0, 256)
         np.testing.assert_array_equal(g["phi"][b][: s.npad], s.phi)
         np.testing.assert_array_equal(g["route_row"][b], s.route_row)

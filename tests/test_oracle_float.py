@@ -156,6 +156,11 @@ def test_backward_matches_torch_autograd():
             g13, g2 = oracle.wgrad_elems(d["routes"], d["w"], d["X"], d["W13"], d["W2"], d["dOut"], L, base, l, e13, e2)
             np.testing.assert_allclose(g13, [g["dW13"][l][n, k] for n, k in e13], rtol=1e-10, atol=1e-14)
             np.testing.assert_allclose(g2, [g["dW2"][l][m, n] for m, n in e2], rtol=1e-10, atol=1e-14)
+            # the absolute-term sums bound the results, and the same call returns the same sums
+            h13, h2, a13, a2 = oracle.wgrad_elems(d["routes"], d["w"], d["X"], d["W13"], d["W2"], d["dOut"], L, base,
+                                                  l, e13, e2, with_abs=True)
+            assert np.array_equal(h13, g13) and np.array_equal(h2, g2)
+            assert np.all(a13 >= np.abs(g13) * (1 - 1e-12)) and np.all(a2 >= np.abs(g2) * (1 - 1e-12))
 
 
 def _loss(d, X=None, W13=None, W2=None, w=None, L=3, base=0):
@@ -218,3 +223,18 @@ def test_dw_is_inner_product_with_expert_output():
                 row = s.route_row[r, t, j]
                 ref = 0.0 if row < 0 else float(dOut[r, t] @ Y[row])
                 assert abs(g["dw"][r, t, j] - ref) <= 1e-10 * max(1e-12, abs(ref)) + 1e-15
+
+
+def test_wgrad_abs_sums_single_route():
+    """With a single route to an expert each element is one term, so its
+    absolute-term sum is exactly its magnitude."""
+    rng = np.random.default_rng(31)
+    P, Np, K, E, L, H, I = 1, 3, 1, 4, 4, 16, 8
+    d = inputs.make_layer_inputs(31, P, Np, E, K, L, H, I, routing="uniform", x_std=1.0, with_grad=True)
+    routes = np.array([[[0], [1], [1]]], np.int32)
+    e13 = [(int(rng.integers(0, 2 * I)), int(rng.integers(0, H))) for _ in range(6)]
+    e2 = [(int(rng.integers(0, H)), int(rng.integers(0, I))) for _ in range(6)]
+    g13, g2, a13, a2 = oracle.wgrad_elems(routes, d["w"], d["X"], d["W13"], d["W2"], d["dOut"], L, 0, 0, e13, e2,
+                                          with_abs=True)
+    np.testing.assert_array_equal(a13, np.abs(g13))
+    np.testing.assert_array_equal(a2, np.abs(g2))

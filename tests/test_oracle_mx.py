@@ -140,3 +140,29 @@ def test_mx_forward_close_to_bf16_forward():
     out = oracle.layer_fwd_tokens(h["routes"], h["w"], h["X"], h["W13"], h["W2"], L=L)
     err = np.linalg.norm(out_mx - out) / np.linalg.norm(out)
     assert 1e-3 < err < 0.1  # quantization error of three 3-bit-mantissa operands, not zero
+
+
+def test_mx_rows_pre_activations():
+    """with_hu: a = silu(h) * u from the returned h and u, the returned A and
+    codes unchanged, and each magnitude sum at least |h| or |u|; a row whose
+    X codes are a single nonzero element has sums equal to |h| and |u|."""
+    h = inputs.make_layer_inputs(12, 2, 64, 8, 2, 4, 256, 128, routing="topk", x_std=1.0)
+    s = oracle.schedule(h["routes"], 4, 0, 256)
+    Xq, Xs = oracle.mx_quantize(h["X"])
+    W13q, W13s = oracle.mx_quantize(h["W13"])
+    W2q, W2s = oracle.mx_quantize(h["W2"])
+    Xdq, Xds = oracle.mx_dispatch(Xq, Xs, s.phi)
+    plain = oracle.mx_expert_ffn_rows(s.seg_off, Xdq, Xds, W13q, W13s, W2q, W2s)
+    r = oracle.mx_expert_ffn_rows(s.seg_off, Xdq, Xds, W13q, W13s, W2q, W2s, with_hu=True)
+    for k in ("A", "Aq", "As", "Y"):
+        assert np.array_equal(plain[k], r[k])
+    I = 128
+    hh, uu = r["HU"][:, :I], r["HU"][:, I:]
+    np.testing.assert_allclose(hh / (1 + np.exp(-hh)) * uu, r["A"], rtol=1e-12, atol=1e-300)
+    assert np.all(r["HUabs"] >= np.abs(r["HU"]) * (1 - 1e-12))
+    one = Xdq.copy()
+    real = np.nonzero(s.phi[:, 0] >= 0)[0][0]
+    one[real] = 0
+    one[real, 5] = Xdq[real, 5] if Xdq[real, 5] & 0x7f else 0x38
+    r1 = oracle.mx_expert_ffn_rows(s.seg_off, one, Xds, W13q, W13s, W2q, W2s, rows=[real], with_hu=True)
+    np.testing.assert_array_equal(r1["HUabs"], np.abs(r1["HU"]))

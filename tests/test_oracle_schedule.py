@@ -227,3 +227,17 @@ def test_capacity_bound_is_reached():
     routes.reshape(-1)[:] = np.repeat(np.arange(L), 5)
     s = oracle.schedule(routes, L, 0, pad)
     assert s.npad == 32 == oracle.capacity_rows(P, Np, K, L, pad)
+
+
+def test_invalid_ids_brute_force():
+    """The oracle's count of ids outside [0, E) equals a per-id Python count
+    on random tiny tensors that mix valid, negative and too-large ids."""
+    rng = np.random.default_rng(77)
+    for _ in range(50):
+        P, Np, K, E = (int(rng.integers(1, 4)), int(rng.integers(1, 20)), int(rng.integers(1, 4)),
+                       int(rng.integers(1, 9)))
+        routes = rng.integers(-3, E + 3, size=(P, Np, K)).astype(np.int32)
+        want = sum(1 for e in routes.reshape(-1).tolist() if not (0 <= e < E))
+        assert oracle.invalid_ids(routes, E) == want
+    assert oracle.invalid_ids(np.zeros((2, 3, 2), np.int32), 1) == 0
+    assert oracle.invalid_ids(np.full((1, 4, 2), -1, np.int32), 8) == 8
