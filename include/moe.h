@@ -240,6 +240,30 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
                   size_t ws_bytes, void *stream);
 
 /*
+ * moe_layer_fwd_noalloc — moe_layer_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same call and the same results, without the
+ * workspace argument.  Its workspace is a static device array inside the
+ * library, MOE_NOALLOC_SCRATCH_BYTES per GPU, which every GPU the library runs
+ * on holds until the process ends.  The call allocates and frees nothing
+ * (its first call on a device looks up that device's copy of the array).
+ *   status  nullable device int32[2] (4-byte aligned): on completion [0] the
+ *           MOE_WS_INVALID_IDS count of this call, [1] its
+ *           MOE_WS_BARRIER_STATUS word (0 when the call does not wait across
+ *           workgroups)
+ * Errors: those of moe_layer_fwd, and MOE_ENOSPC when
+ * moe_workspace_bytes(d, MOE_OP_LAYER_FWD) exceeds MOE_NOALLOC_SCRATCH_BYTES
+ * (nothing is launched then).  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (different streams, or different host
+ * threads, not ordered by the caller) race and give undefined results.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (4 << 20)
+int moe_layer_fwd_noalloc(const moe_desc *d, const int32_t *routes, const float *w, const uint16_t *X,
+                          const uint16_t *W13, const uint16_t *W2, int32_t *counts, int32_t *seg_off, moe_src *phi,
+                          int32_t *route_row, uint16_t *Xd, uint16_t *HU, uint16_t *A, uint16_t *Y, uint16_t *out,
+                          int32_t flags, int32_t chunk_rows, int32_t *status, void *stream);
+
+/*
  * moe_layer_fwd_shared — the layer forward with a shared expert: a dense
  * SwiGLU FFN over every token beside the routed experts ([BPT] section 2.C:
  * the shared expert computed while the first routed rows are pulled; [MoK]

@@ -453,6 +453,41 @@ int launch_mx_quantize(const uint16_t *src, int64_t rows, int32_t K, uint8_t *q,
     return launch_status();
 }
 
+// Workspace of moe_layer_fwd_noalloc: a static device array, one copy per GPU
+// the library runs on, held until the process ends.  Host code never passes
+// `scratch` itself to a kernel (in host code the name is only a stand-in for
+// the symbol): the device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+constexpr int64_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "whole 256-byte workspace blocks");
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {};
+
+int scratch_for_current_device(char **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+    if (dev < 0 || dev >= 64) return MOE_EUNSUPPORTED;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<char *>(g_scratch_ptr[dev]);
+    return MOE_OK;
+}
+
+// status[0] = the invalid-id count, status[1] = the barrier word when the
+// call waited across workgroups (else 0: the word is left from earlier calls).
+__global__ void k_copy_status(const char *ws, int64_t inv_off, int64_t bar_off, int waited, int32_t *status) {
+    if (threadIdx.x == 0) {
+        status[0] = *reinterpret_cast<const int32_t *>(ws + inv_off);
+        status[1] = waited ? *reinterpret_cast<const int32_t *>(ws + bar_off) : 0;
+    }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -566,6 +601,29 @@ int moe_expert_ffn(const moe_desc *d, const uint16_t *Xd, const uint16_t *W13, c
     if (chunk_rows > 0 && (!ws || !aligned16(ws) || ws_bytes < (size_t)kBarrierBytes)) return ws ? MOE_ENOSPC : MOE_EINVAL;
     FfnArgs a = make_ffn_args(d, Xd, W13, W2, seg_off, HU, A, Y, chunk_rows, static_cast<uint32_t *>(ws));
     return launch_ffn(d, a, static_cast<hipStream_t>(stream));
+}
+
+int moe_layer_fwd_noalloc(const moe_desc *d, const int32_t *routes, const float *w, const uint16_t *X,
+                          const uint16_t *W13, const uint16_t *W2, int32_t *counts, int32_t *seg_off, moe_src *phi,
+                          int32_t *route_row, uint16_t *Xd, uint16_t *HU, uint16_t *A, uint16_t *Y, uint16_t *out,
+                          int32_t flags, int32_t chunk_rows, int32_t *status, void *stream) {
+    int rc = check_desc(d, true);
+    if (rc != MOE_OK) return rc;
+    if (moe_workspace_bytes(d, MOE_OP_LAYER_FWD) > kScratchBytes) return MOE_ENOSPC;
+    if (status && ((uintptr_t)status & 3u)) return MOE_EINVAL;
+    char *ws = nullptr;
+    rc = scratch_for_current_device(&ws);
+    if (rc != MOE_OK) return rc;
+    rc = moe_layer_fwd(d, routes, w, X, W13, W2, counts, seg_off, phi, route_row, Xd, HU, A, Y, out, flags,
+                       chunk_rows, ws, (size_t)kScratchBytes, stream);
+    if (rc != MOE_OK || !status) return rc;
+    const int waited = (flags & MOE_PERSISTENT) || chunk_rows > 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TraceScope tr("noalloc_status", s);
+    hipLaunchKernelGGL(k_copy_status, dim3(1), dim3(64), 0, s, ws,
+                       moe_workspace_field(d, MOE_OP_LAYER_FWD, MOE_WS_INVALID_IDS),
+                       moe_workspace_field(d, MOE_OP_LAYER_FWD, MOE_WS_BARRIER_STATUS), waited, status);
+    return launch_status();
 }
 
 int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, const uint16_t *X, const uint16_t *W13,

@@ -31,8 +31,9 @@ EXPORTED = (
     "moe_quantize_mx",
     "moe_layer_fwd_mx",
     "moe_ring_capacity_rows", "moe_ring_workspace_bytes", "moe_layer_fwd_ring", "moe_layer_bwd_ring",
-    "moe_layer_fwd_shared",
+    "moe_layer_fwd_shared", "moe_layer_fwd_noalloc",
 )
+MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
 class MoeError(RuntimeError):
@@ -76,6 +77,7 @@ def load() -> ctypes.CDLL:
         "moe_expert_ffn": (ctypes.c_int, [D, P, P, P, P, P, P, P, i32, P, sz, P]),
         "moe_combine": (ctypes.c_int, [D, P, P, P, P, P]),
         "moe_layer_fwd": (ctypes.c_int, [D] + [P] * 14 + [i32, i32, P, sz, P]),
+        "moe_layer_fwd_noalloc": (ctypes.c_int, [D] + [P] * 14 + [i32, i32, P, P]),
         "moe_quantize_mx": (ctypes.c_int, [P, i64, i32, P, P, P]),
         "moe_layer_fwd_mx": (ctypes.c_int, [D] + [P] * 18 + [sz, P]),
         "moe_layer_bwd": (ctypes.c_int, [D] + [P] * 16 + [sz, P]),
@@ -179,6 +181,15 @@ def moe_layer_fwd(d, routes, w, X, W13, W2, counts, seg_off, phi, route_row, Xd,
                               _dev(out), flags, chunk_rows, _dev(ws), ws.numel() * ws.element_size(),
                               _stream(stream, X))
     return _check(rc, "moe_layer_fwd")
+
+
+def moe_layer_fwd_noalloc(d, routes, w, X, W13, W2, counts, seg_off, phi, route_row, Xd, HU, A, Y, out, flags=0,
+                          chunk_rows=0, status=None, stream=None):
+    rc = load().moe_layer_fwd_noalloc(ctypes.byref(d), _dev(routes), _dev(w), _dev(X), _dev(W13), _dev(W2),
+                                      _dev(counts), _dev(seg_off), _dev(phi), _dev(route_row), _dev(Xd), _dev(HU),
+                                      _dev(A), _dev(Y), _dev(out), flags, chunk_rows, _dev(status),
+                                      _stream(stream, X))
+    return _check(rc, "moe_layer_fwd_noalloc")
 
 
 def moe_layer_bwd(d, dOut, routes, w, phi, route_row, seg_off, Xd, HU, A, W13, W2, dX, dW13, dW2, dw, ws,
