@@ -116,6 +116,12 @@ __global__ __launch_bounds__(kFwdThreads) void k_ffn_down(FfnArgs a) {
     ffn_down_phase(a, 0, a.seg_off[a.L], lds);
 }
 
+// Wide-tile down projection: 8 waves, all 160 KiB of LDS, one workgroup per CU.
+__global__ __launch_bounds__(kWideThreads) void k_ffn_down_w(FfnArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kWideLds];
+    wide_down_phase(a, lds);
+}
+
 __global__ __launch_bounds__(kFwdThreads) void k_ffn_chunked(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
     GridBarrier gb(a.bar);
@@ -233,6 +239,9 @@ int check_desc(const moe_desc *d, bool need_ffn) {
         const int64_t row_tiles = cap / 256 + 1, col_tiles = d->H / 128 + 2 * (int64_t)d->I / 128 + 2;
         const int64_t wgrad_tiles = (int64_t)d->L * (d->H / 256) * 3 * (d->I / 256 + 1);
         if (row_tiles * col_tiles + wgrad_tiles >= (1ll << 30)) return MOE_EUNSUPPORTED;
+        // the wide down tiles address 384 rows of W2 and 256 rows of A with
+        // 32-bit byte offsets below 1 GiB
+        if (768ll * d->I >= (1ll << 30)) return MOE_EUNSUPPORTED;
     }
     return MOE_OK;
 }
@@ -427,7 +436,7 @@ int launch_ffn(const moe_desc *d, const FfnArgs &a, hipStream_t s) {
         }
         if (launch_status() != MOE_OK) return MOE_EHIP;
         TraceScope tr("ffn_down", s);
-        hipLaunchKernelGGL(k_ffn_down, dim3(grid), dim3(kFwdThreads), 0, s, a);
+        hipLaunchKernelGGL(k_ffn_down_w, dim3(grid), dim3(kWideThreads), 0, s, a);
         return launch_status();
     }
     {
@@ -1078,7 +1087,7 @@ int moe_layer_fwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots,
         if (launch_status() != MOE_OK) return MOE_EHIP;
         {
             TraceScope tr("ring_down", s);
-            hipLaunchKernelGGL(k_ffn_down, dim3(grid), dim3(kFwdThreads), 0, s, fa);
+            hipLaunchKernelGGL(k_ffn_down_w, dim3(grid), dim3(kWideThreads), 0, s, fa);
         }
         if (launch_status() != MOE_OK) return MOE_EHIP;
     }
