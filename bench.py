@@ -37,7 +37,7 @@ METRIC = "MoE layer fwd TFLOP/s + MFMA util; schedule routes/s (Kimi shape, 1 GP
 
 KIMI = dict(P=8, Np=7168, E=384, K=8, L=48, H=7168, I=2048)
 KERNEL_SOURCES = ("routing_schedule_expert_amd/csrc/gemm.hpp", "routing_schedule_expert_amd/csrc/layer.hpp",
-                  "routing_schedule_expert_amd/csrc/common.hpp")
+                  "routing_schedule_expert_amd/csrc/common.hpp", "routing_schedule_expert_amd/csrc/wide.hpp")
 
 
 def kernel_source_digest() -> str:
@@ -47,11 +47,11 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch (fetched + written) from the committed rocprofv3
-    counter summary, or None when the kernel sources changed since the
-    counters were taken.  The summary holds `key: value` lines."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_kimi_traffic.md")
+def profile_fields(name: str):
+    """`key: value` lines of a committed rocprofv3 summary under profiles/, or
+    None when it is missing or the kernel sources changed since the counters
+    were taken (its kernel_source_digest no longer matches)."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     rec = {}
@@ -61,10 +61,44 @@ def measured_traffic(kernel: str):
             rec[k.strip()] = v.strip()
     if rec.get("kernel_source_digest") != kernel_source_digest():
         return None
+    return rec
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch (fetched + written) from the committed counter
+    summary, or None when it is stale."""
+    rec = profile_fields(f"{kernel}_kimi_traffic.md")
     try:
-        return int(rec["hbm_bytes_per_launch"])
+        return int(rec["hbm_bytes_per_launch"]) if rec else None
     except (KeyError, ValueError):
         return None
+
+
+def measured_mfma_counters():
+    """MFMA busy fraction and engine clock of the grouped GEMMs from the
+    committed counter summary (SQ_VALU_MFMA_BUSY_CYCLES over active cycles x
+    SIMDs, GRBM_GUI_ACTIVE per XCD over the dispatch time), or None when it is
+    stale.  Counters cannot be read inside the timed run itself."""
+    rec = profile_fields("ffn_gemm_kimi_mfma_util.md")
+    if not rec:
+        return None
+    out = {"source": "profiles/ffn_gemm_kimi_mfma_util.md"}
+    for k in ("gateup_mfma_busy", "gateup_clock_ghz", "down_mfma_busy", "down_clock_ghz"):
+        try:
+            out[k] = float(rec[k])
+        except (KeyError, ValueError):
+            return None
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def copy_calibration(torch, dev, mib: int):
@@ -626,7 +660,8 @@ def cpu_baseline(L_res, torch, oracle, budget_s: float):
     oracle.schedule(routes, c["L"], 0, 256)
     ts = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"layer forward of {n} of {ntok} tokens ({local} local routes, 6*H*I flop each) "
                       f"in {dt:.1f} s, fp64 C with OpenMP",
             "schedule_routes_per_s": c["P"] * c["Np"] * c["K"] / ts,
@@ -750,6 +785,7 @@ def main():
                    "chunk_rows": args.chunk_rows,
                    "dispatch": "separate gather" if args.materialize_xd else "fused into the gate/up operand loads"},
         "mfma_util_from_time": value / PEAK_BF16_TFLOPS,
+        "mfma_counters": measured_mfma_counters(),
         "stage_ms": st,
         "roofline": roofline,
         "ffn_down": down,

@@ -46,6 +46,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
+# MOE_ORACLE_LIB names another build of moe_oracle.c to load instead (the
+# sanitizer build of oracle/sanitize.sh); it is used as it is, never rebuilt.
+_LIB_OVERRIDE = os.environ.get("MOE_ORACLE_LIB")
 
 
 def build(force: bool = True) -> str:
@@ -63,9 +66,12 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        lib = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            lib = ctypes.CDLL(_LIB)
         p = ctypes.c_void_p
         i32, i64 = ctypes.c_int, ctypes.c_int64
         lib.orc_capacity_rows.argtypes = [i32, i32, i32, i32, i32]
