@@ -26,6 +26,11 @@ Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
   mx_expert_ffn_rows, mx_layer_fwd_tokens        pinned (dot products vs numpy on the
                                                    dequantized operands; token path = rows +
                                                    combine; close to the bf16 FFN)
+  mx_weights_t, mx_bwd_tokens, mx_wgrad_elems    pinned (matrix-form numpy composition on
+                                                   dequantized operands at tiny shapes; within
+                                                   the format's error of the bf16 backward;
+                                                   exact scaling by powers of two of dOut;
+                                                   zero dOut, non-local tokens)
   shared_ffn_tokens, layer_fwd_tokens_shared     pinned (dense SwiGLU vs torch fp64 with no
                                                    local routes; zero shared weights leave the
                                                    routed output; the routed part stays linear
@@ -109,6 +114,10 @@ def _load():
         lib.orc_mx_expert_ffn_rows.argtypes = [i32, i32, i32] + [p] * 7 + [p, i64, p, p, p, p, p, p]
         lib.orc_mx_layer_fwd_tokens.argtypes = [i32, i32, i32, i32, i32] + [p] * 8 + [p, i64, p]
         lib.orc_wgrad_elems.restype = None
+        lib.orc_mx_bwd_tokens.argtypes = [i32, i32, i32, i32, i32] + [p] * 11 + [p, i64, p, p, p]
+        lib.orc_mx_bwd_tokens.restype = None
+        lib.orc_mx_wgrad_elems.argtypes = [i32, i32, i32, i32, i32, i32] + [p] * 12 + [p, i64, p, p, i64, p, p, p]
+        lib.orc_mx_wgrad_elems.restype = None
         _lib = lib
     return _lib
 
@@ -418,6 +427,70 @@ def mx_layer_fwd_tokens(routes, w, Xq, Xs, W13q, W13s, W2q, W2s, L: int, base: i
     _load().orc_mx_layer_fwd_tokens(K, L, base, H, I, _ptr(routes), _ptr(w), *[_ptr(a) for a in arrs],
                                     _ptr(tokens), tokens.shape[0], _ptr(out))
     return out
+
+
+def mx_transpose_quantize(W: np.ndarray):
+    """MX quantization of bf16 bits [..., R, C] along R: codes [..., C, R] and
+    scale bytes [..., C, R/32] (each column of W quantized in blocks of 32
+    consecutive rows)."""
+    return mx_quantize(np.ascontiguousarray(np.swapaxes(_u16(W), -1, -2)))
+
+
+def mx_weights_t(W13: np.ndarray, W2: np.ndarray):
+    """The backward's MX weights: W2 columns along H ([L][I][H]) for the down
+    dgrad, W13 columns along 2I ([L][H][2I]) for the gate/up dgrad."""
+    W2tq, W2ts = mx_transpose_quantize(W2)
+    W13tq, W13ts = mx_transpose_quantize(W13)
+    return {"W2tq": W2tq, "W2ts": W2ts, "W13tq": W13tq, "W13ts": W13ts}
+
+
+def mx_bwd_tokens(routes, w, Xq, Xs, W13q, W13s, wt, dOut, L: int, base: int = 0, tokens=None,
+                  with_abs: bool = False):
+    """MXFP8 backward, token side: dX rows (double [n][H]) and dw rows ([n][K])
+    of the listed tokens.  Xq/Xs, W13q/W13s are the forward's MX operands; wt
+    is mx_weights_t(W13, W2).  with_abs also returns the sums |dA'[i] a[i]|."""
+    routes = _i32(routes)
+    P, Np, K = routes.shape
+    w = np.ascontiguousarray(w, np.float32)
+    Xq, Xs, W13q, W13s = (np.ascontiguousarray(a, np.uint8) for a in (Xq, Xs, W13q, W13s))
+    t = [np.ascontiguousarray(wt[k], np.uint8) for k in ("W2tq", "W2ts", "W13tq", "W13ts")]
+    dOut = _u16(dOut)
+    H = Xq.shape[-1]
+    I = W13q.shape[1] // 2
+    tokens = np.arange(P * Np, dtype=np.int64) if tokens is None else np.ascontiguousarray(tokens, np.int64)
+    n = tokens.shape[0]
+    dX = np.zeros((n, H))
+    dw = np.zeros((n, K))
+    dwabs = np.zeros((n, K)) if with_abs else None
+    _load().orc_mx_bwd_tokens(K, L, base, H, I, _ptr(routes), _ptr(w), _ptr(Xq), _ptr(Xs), _ptr(W13q), _ptr(W13s),
+                              *[_ptr(a) for a in t], _ptr(dOut), _ptr(tokens), n, _ptr(dX), _ptr(dw), _ptr(dwabs))
+    return (dX, dw, dwabs) if with_abs else (dX, dw)
+
+
+def mx_wgrad_elems(sched, routes, w, X, Xq, Xs, W13q, W13s, wt, dOut, expert: int, w13_elems, w2_elems,
+                   with_abs: bool = False):
+    """Listed elements of the MX backward's dW13[expert] ((nn, k) pairs) and
+    dW2[expert] ((m, i) pairs); sched is oracle.schedule(routes, ...) of the
+    same routing (its table fixes the row blocks).  with_abs also returns the
+    sums of the terms' magnitudes."""
+    routes = _i32(routes)
+    P, Np, K = routes.shape
+    w = np.ascontiguousarray(w, np.float32)
+    X, dOut = _u16(X), _u16(dOut)
+    Xq, Xs, W13q, W13s = (np.ascontiguousarray(a, np.uint8) for a in (Xq, Xs, W13q, W13s))
+    W2tq, W2ts = (np.ascontiguousarray(wt[k], np.uint8) for k in ("W2tq", "W2ts"))
+    L, twoI, H = W13q.shape
+    I = twoI // 2
+    e13 = np.ascontiguousarray(np.asarray(w13_elems, np.int64).reshape(-1, 2))
+    e2 = np.ascontiguousarray(np.asarray(w2_elems, np.int64).reshape(-1, 2))
+    g13, g2 = np.zeros(e13.shape[0]), np.zeros(e2.shape[0])
+    a13 = np.zeros(e13.shape[0]) if with_abs else None
+    a2 = np.zeros(e2.shape[0]) if with_abs else None
+    _load().orc_mx_wgrad_elems(Np, K, L, H, I, expert, _ptr(_i32(sched.seg_off)), _ptr(_i32(sched.phi)),
+                               _ptr(_i32(sched.route_row)), _ptr(w), _ptr(X), _ptr(Xq), _ptr(Xs), _ptr(W13q),
+                               _ptr(W13s), _ptr(W2tq), _ptr(W2ts), _ptr(dOut), _ptr(e13), e13.shape[0], _ptr(g13),
+                               _ptr(e2), e2.shape[0], _ptr(g2), _ptr(a13), _ptr(a2))
+    return (g13, g2, a13, a2) if with_abs else (g13, g2)
 
 
 # ---------------------------------------------------------------------------

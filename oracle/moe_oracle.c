@@ -1006,3 +1006,272 @@ void orc_mx_layer_fwd_tokens(int K, int L, int base, int H, int I, const int32_t
         free(as);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* MXFP8 backward ([BPT] section 3 and [MoK] section 6 report an MXFP8       */
+/* backward; neither spells out its quantization).                           */
+/* ------------------------------------------------------------------------ */
+/*
+ * Reading: every product of the backward takes MX operands, each blocked
+ * along that product's own reduction dimension and quantized from the value
+ * the bf16 backward uses at that point:
+ *   down dgrad     dA'[i] = sum_k dO[k] W2[l][k][i]   (over H): the row of
+ *                  dOut along H, the column i of W2[l] along H;
+ *   gate/up dgrad  dXd[k] = sum_n dHU[n] W13[l][n][k] (over 2I): the dHU row
+ *                  along 2I, the column k of W13[l] along 2I;
+ *   dW2[l][m][i]   = sum_r (w dO)[r][m] a[r][i]      (over the expert's
+ *                  dispatched rows): both columns along the rows;
+ *   dW13[l][n][k]  = sum_r dHU[r][n] Xd[r][k]         (over the rows): both
+ *                  columns along the rows.
+ * Row blocks are 32 consecutive dispatched rows (segments start at multiples
+ * of 256, so no block straddles two experts); padding rows are zero.  The
+ * elementwise steps are those of the bf16 backward: a is what the forward's
+ * down projection consumed (its MX codes, dequantized), dw = dA' . a,
+ * dA = w dA', dh = dA u silu'(h), du = dA silu(h), with h and u as the
+ * forward saves them (bf16).  Where a code depends on a value that the
+ * kernels hold in bf16 (h and u, dHU, w dO), that value is rounded as they
+ * round it (to float, then to bf16, ties to even) before it is used, so both
+ * sides quantize the same number; everything else stays double.
+ */
+
+/* float rounding of v, then bf16 with ties to even (finite v) */
+static double round_bf16_f32(double v) {
+    float f = (float)v;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* the 256 E4M3 values, so dequantizing a row costs one lookup per element */
+static double e4m3_tab[256];
+static int e4m3_tab_ready;
+static void e4m3_tab_init(void) {
+    if (e4m3_tab_ready) return;
+    for (int c = 0; c < 256; ++c) e4m3_tab[c] = orc_e4m3_value(c);
+    e4m3_tab_ready = 1;
+}
+
+/* dequantized MX row: out[k] = value(q[k]) * 2^(s[k/32] - 127) */
+static void mx_row(const uint8_t *q, const uint8_t *s, int K, double *out) {
+    for (int b = 0; b < K / 32; ++b) {
+        double sc = ldexp(1.0, (int)s[b] - 127);
+        for (int i = 0; i < 32; ++i) out[b * 32 + i] = e4m3_tab[q[b * 32 + i]] * sc;
+    }
+}
+
+/* MX quantize-then-dequantize of n doubles (n % 32 == 0) in place */
+static void mx_roundtrip(double *x, int64_t n) {
+    uint8_t q[32], s;
+    for (int64_t b = 0; b < n / 32; ++b) {
+        mx_block(x + b * 32, q, &s);
+        double sc = ldexp(1.0, (int)s - 127);
+        for (int i = 0; i < 32; ++i) x[b * 32 + i] = e4m3_tab[q[i]] * sc;
+    }
+}
+
+/*
+ * Token side of the MX backward for the listed tokens: dX[q] (the sum over
+ * the token's local slots j ascending of the gate/up dgrad row) and dw[q][j]
+ * (0 for slots that are not local).  The forward quantities of each route are
+ * recomputed as orc_mx_layer_fwd_tokens computes them.  Weights: W13q/W13s
+ * [L][2I][H] (forward, blocks along H); W2tq/W2ts [L][I][H] (column i of W2[l],
+ * blocks along H); W13tq/W13ts [L][H][2I] (column k of W13[l], blocks along
+ * 2I).  dwabs (nullable) gets the sum of |dA'[i] a[i]| per slot.
+ */
+void orc_mx_bwd_tokens(int K, int L, int base, int H, int I, const int32_t *routes, const float *w,
+                       const uint8_t *Xq, const uint8_t *Xs, const uint8_t *W13q, const uint8_t *W13s,
+                       const uint8_t *W2tq, const uint8_t *W2ts, const uint8_t *W13tq, const uint8_t *W13ts,
+                       const uint16_t *dOut, const int64_t *tokens, int64_t ntok, double *dX, double *dw,
+                       double *dwabs) {
+    e4m3_tab_init();
+#pragma omp parallel
+    {
+        double *x = (double *)malloc(sizeof(double) * H);
+        double *go = (double *)malloc(sizeof(double) * H);
+        double *wr = (double *)malloc(sizeof(double) * (H > 2 * I ? H : 2 * I));
+        double *h = (double *)malloc(sizeof(double) * I);
+        double *u = (double *)malloc(sizeof(double) * I);
+        double *a = (double *)malloc(sizeof(double) * I);
+        double *dhu = (double *)malloc(sizeof(double) * 2 * I);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t q = 0; q < ntok; ++q) {
+            int64_t g = tokens[q];
+            double *dx = dX + q * H;
+            for (int k = 0; k < H; ++k) {
+                dx[k] = 0.0;
+                go[k] = widen_bf16(dOut[g * H + k]);
+            }
+            mx_row(Xq + g * H, Xs + g * (H / 32), H, x);
+            mx_roundtrip(go, H); /* dO along H */
+            for (int j = 0; j < K; ++j) {
+                int32_t e = routes[g * K + j];
+                dw[q * K + j] = 0.0;
+                if (dwabs) dwabs[q * K + j] = 0.0;
+                if (!is_local(e, base, L)) continue;
+                int l = e - base;
+                /* forward of this route: h, u, a (MX codes, dequantized) */
+                for (int n = 0; n < I; ++n) {
+                    double hh = 0.0, uu = 0.0;
+                    mx_row(W13q + ((int64_t)l * 2 * I + n) * H, W13s + ((int64_t)l * 2 * I + n) * (H / 32), H, wr);
+                    for (int k = 0; k < H; ++k) hh += x[k] * wr[k];
+                    mx_row(W13q + ((int64_t)l * 2 * I + I + n) * H, W13s + ((int64_t)l * 2 * I + I + n) * (H / 32),
+                           H, wr);
+                    for (int k = 0; k < H; ++k) uu += x[k] * wr[k];
+                    a[n] = silu(hh) * uu;
+                    h[n] = round_bf16_f32(hh); /* as saved */
+                    u[n] = round_bf16_f32(uu);
+                }
+                mx_roundtrip(a, I);
+                /* down dgrad, router-weight gradient, SwiGLU backward */
+                double wj = (double)w[g * K + j], dot = 0.0, dabs = 0.0;
+                for (int i = 0; i < I; ++i) {
+                    double d = 0.0;
+                    mx_row(W2tq + ((int64_t)l * I + i) * H, W2ts + ((int64_t)l * I + i) * (H / 32), H, wr);
+                    for (int k = 0; k < H; ++k) d += go[k] * wr[k];
+                    dot += d * a[i];
+                    dabs += fabs(d * a[i]);
+                    double dA = wj * d;
+                    dhu[i] = round_bf16_f32(dA * u[i] * silu_grad(h[i]));
+                    dhu[I + i] = round_bf16_f32(dA * silu(h[i]));
+                }
+                dw[q * K + j] = dot;
+                if (dwabs) dwabs[q * K + j] = dabs;
+                /* gate/up dgrad on dHU quantized along 2I */
+                mx_roundtrip(dhu, 2 * I);
+                for (int k = 0; k < H; ++k) {
+                    double s = 0.0;
+                    mx_row(W13tq + ((int64_t)l * H + k) * 2 * I, W13ts + ((int64_t)l * H + k) * (2 * I / 32), 2 * I,
+                           wr);
+                    for (int n = 0; n < 2 * I; ++n) s += dhu[n] * wr[n];
+                    dx[k] += s;
+                }
+            }
+        }
+        free(x); free(go); free(wr); free(h); free(u); free(a); free(dhu);
+    }
+}
+
+/*
+ * Weight gradients of local expert l in the MX backward, listed elements:
+ * dW13[l][nn][k] (pairs (nn, k), nn in [0, 2I)) and dW2[l][m][i] (pairs
+ * (m, i)), each a sum over the segment's dispatched rows [seg_off[l],
+ * seg_off[l+1]) in ascending order of the products of two columns quantized
+ * along the rows (reading above).  Row r holds the route phi[r] = (part, tok)
+ * of slot j with route_row[part*Np + tok][j] == r (padding rows: zero).  Each
+ * distinct column is quantized once and shared by its elements.  a13 / a2
+ * (nullable) get the sums of the terms' magnitudes.
+ */
+void orc_mx_wgrad_elems(int Np, int K, int L, int H, int I, int l, const int32_t *seg_off, const int32_t *phi,
+                        const int32_t *route_row, const float *w, const uint16_t *X, const uint8_t *Xq,
+                        const uint8_t *Xs, const uint8_t *W13q, const uint8_t *W13s, const uint8_t *W2tq,
+                        const uint8_t *W2ts, const uint16_t *dOut, const int64_t *w13_elems, int64_t n13,
+                        double *g13, const int64_t *w2_elems, int64_t n2, double *g2, double *a13, double *a2) {
+    e4m3_tab_init();
+    (void)L;
+    const int64_t s0 = seg_off[l], nr = (int64_t)seg_off[l + 1] - s0;
+    /* per row: token and router weight (-1 / 0 for padding) */
+    int64_t *tok = (int64_t *)malloc(sizeof(int64_t) * (nr + 1));
+    double *wrow = (double *)malloc(sizeof(double) * (nr + 1));
+    for (int64_t r = 0; r < nr; ++r) {
+        tok[r] = -1;
+        wrow[r] = 0.0;
+        int32_t p = phi[2 * (s0 + r)], t = phi[2 * (s0 + r) + 1];
+        if (p < 0) continue;
+        int64_t g = (int64_t)p * Np + t;
+        tok[r] = g;
+        for (int j = 0; j < K; ++j)
+            if (route_row[g * K + j] == s0 + r) wrow[r] = (double)w[g * K + j];
+    }
+    /* which forward columns n (of I) each row needs: a's 32-blocks of the dW2
+     * elements' i, and the i = nn mod I of the dW13 elements */
+    char *need_a = (char *)calloc((size_t)I, 1), *need_d = (char *)calloc((size_t)I, 1);
+    for (int64_t q = 0; q < n2; ++q) {
+        int64_t b = w2_elems[2 * q + 1] / 32;
+        for (int i = 0; i < 32; ++i) need_a[b * 32 + i] = 1;
+    }
+    for (int64_t q = 0; q < n13; ++q) need_d[w13_elems[2 * q] % I] = 1;
+    /* per row and needed column: a (dequantized MX), dHU (gate, up) as bf16 */
+    double *A = (double *)calloc((size_t)(nr * I + 1), sizeof(double));
+    double *DH = (double *)calloc((size_t)(nr * 2 * I + 1), sizeof(double));
+#pragma omp parallel
+    {
+        double *x = (double *)malloc(sizeof(double) * H);
+        double *go = (double *)malloc(sizeof(double) * H);
+        double *wr = (double *)malloc(sizeof(double) * H);
+        double *a = (double *)malloc(sizeof(double) * I);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < nr; ++r) {
+            if (tok[r] < 0) continue;
+            int64_t g = tok[r];
+            mx_row(Xq + g * H, Xs + g * (H / 32), H, x);
+            for (int k = 0; k < H; ++k) go[k] = widen_bf16(dOut[g * H + k]);
+            mx_roundtrip(go, H);
+            for (int n = 0; n < I; ++n) {
+                a[n] = 0.0;
+                if (!need_a[n] && !need_d[n]) continue;
+                double hh = 0.0, uu = 0.0;
+                mx_row(W13q + ((int64_t)l * 2 * I + n) * H, W13s + ((int64_t)l * 2 * I + n) * (H / 32), H, wr);
+                for (int k = 0; k < H; ++k) hh += x[k] * wr[k];
+                mx_row(W13q + ((int64_t)l * 2 * I + I + n) * H, W13s + ((int64_t)l * 2 * I + I + n) * (H / 32), H,
+                       wr);
+                for (int k = 0; k < H; ++k) uu += x[k] * wr[k];
+                a[n] = silu(hh) * uu;
+                if (need_d[n]) {
+                    double d = 0.0;
+                    mx_row(W2tq + ((int64_t)l * I + n) * H, W2ts + ((int64_t)l * I + n) * (H / 32), H, wr);
+                    for (int k = 0; k < H; ++k) d += go[k] * wr[k];
+                    double hb = round_bf16_f32(hh), ub = round_bf16_f32(uu), dA = wrow[r] * d;
+                    DH[r * 2 * I + n] = round_bf16_f32(dA * ub * silu_grad(hb));
+                    DH[r * 2 * I + I + n] = round_bf16_f32(dA * silu(hb));
+                }
+            }
+            /* a's codes: only whole needed blocks are meaningful */
+            for (int b = 0; b < I / 32; ++b) {
+                if (!need_a[b * 32]) continue;
+                mx_roundtrip(a + b * 32, 32);
+                for (int i = 0; i < 32; ++i) A[r * I + b * 32 + i] = a[b * 32 + i];
+            }
+        }
+        free(x); free(go); free(wr); free(a);
+    }
+    /* the elements: each pair of columns quantized along the rows */
+#pragma omp parallel
+    {
+        double *c1 = (double *)malloc(sizeof(double) * (nr + 1));
+        double *c2 = (double *)malloc(sizeof(double) * (nr + 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t q = 0; q < n13 + n2; ++q) {
+            if (q < n13) {
+                int64_t nn = w13_elems[2 * q], k = w13_elems[2 * q + 1];
+                for (int64_t r = 0; r < nr; ++r) {
+                    c1[r] = DH[r * 2 * I + nn];
+                    c2[r] = tok[r] < 0 ? 0.0 : widen_bf16(X[tok[r] * H + k]);
+                }
+            } else {
+                int64_t e = q - n13, m = w2_elems[2 * e], i = w2_elems[2 * e + 1];
+                for (int64_t r = 0; r < nr; ++r) {
+                    c1[r] = tok[r] < 0 ? 0.0 : round_bf16_f32(wrow[r] * widen_bf16(dOut[tok[r] * H + m]));
+                    c2[r] = A[r * I + i];
+                }
+            }
+            mx_roundtrip(c1, nr);
+            mx_roundtrip(c2, nr);
+            double s = 0.0, sa = 0.0;
+            for (int64_t r = 0; r < nr; ++r) {
+                s += c1[r] * c2[r];
+                sa += fabs(c1[r] * c2[r]);
+            }
+            if (q < n13) {
+                g13[q] = s;
+                if (a13) a13[q] = sa;
+            } else {
+                g2[q - n13] = s;
+                if (a2) a2[q - n13] = sa;
+            }
+        }
+        free(c1); free(c2);
+    }
+    free(tok); free(wrow); free(need_a); free(need_d); free(A); free(DH);
+}
