@@ -97,6 +97,7 @@ enum {
     MOE_OP_LAYER_FWD = 4,
     MOE_OP_LAYER_BWD = 5,
     MOE_OP_LAYER_FWD_SHARED = 6,
+    MOE_OP_LAYER_BWD_MX = 7,
 };
 int64_t moe_workspace_bytes(const moe_desc *d, int op);
 
@@ -134,6 +135,23 @@ int64_t moe_workspace_bytes(const moe_desc *d, int op);
 enum {
     MOE_WS_INVALID_IDS = 0,
     MOE_WS_BARRIER_STATUS = 1,
+    /* inspection of moe_layer_bwd_mx (op MOE_OP_LAYER_BWD_MX), with
+     * ldt = moe_capacity_rows rounded up to a multiple of 512 and only the rows
+     * below seg_off[L] (the columns below it for the [C][ldt] buffers) written
+     * by the last call: */
+    MOE_WS_MX_DHU = 2,     /* bf16 [cap][2I]: dHU (gate then up columns)       */
+    MOE_WS_MX_DO_Q = 3,    /* [cap][H]:   dO_d row codes (along H)             */
+    MOE_WS_MX_DO_S = 4,    /* [cap][H/32]                                      */
+    MOE_WS_MX_DHU_Q = 5,   /* [cap][2I]:  dHU row codes (along 2I)             */
+    MOE_WS_MX_DHU_S = 6,   /* [cap][2I/32]                                     */
+    MOE_WS_MX_DOWT_Q = 7,  /* [H][ldt]:   (dO_d w) column codes (along rows)   */
+    MOE_WS_MX_DOWT_S = 8,  /* [H][ldt/32]                                      */
+    MOE_WS_MX_AT_Q = 9,    /* [I][ldt]:   a column codes                       */
+    MOE_WS_MX_AT_S = 10,   /* [I][ldt/32]                                      */
+    MOE_WS_MX_XDT_Q = 11,  /* [H][ldt]:   Xd column codes                      */
+    MOE_WS_MX_XDT_S = 12,  /* [H][ldt/32]                                      */
+    MOE_WS_MX_DHUT_Q = 13, /* [2I][ldt]:  dHU column codes                     */
+    MOE_WS_MX_DHUT_S = 14, /* [2I][ldt/32]                                     */
 };
 int64_t moe_workspace_field(const moe_desc *d, int op, int field);
 
@@ -327,6 +345,9 @@ int moe_quantize_mx(const uint16_t *src, int64_t rows, int32_t K, uint8_t *q, ui
  *   counts, seg_off, phi, route_row   out, as in moe_schedule
  *   Xq, Xs, Aq, As, Y, out            out (Xq, Aq, Y, out 16-byte aligned;
  *                                     Xs, As, W13s, W2s 4-byte aligned)
+ *   HU          nullable out: bf16 [cap][2I], h then u rounded once from the
+ *               fp32 accumulators (16-byte aligned), what moe_layer_bwd_mx
+ *               needs besides Aq / As
  *   ws >= moe_workspace_bytes(d, MOE_OP_LAYER_FWD)
  * Needs H a multiple of 128 and H <= 65536 (MOE_EUNSUPPORTED otherwise),
  * d->num_batches == 1.  Every float reduction has a fixed order, so repeated
@@ -335,7 +356,54 @@ int moe_quantize_mx(const uint16_t *src, int64_t rows, int32_t K, uint8_t *q, ui
 int moe_layer_fwd_mx(const moe_desc *d, const int32_t *routes, const float *w, const uint16_t *X,
                      const uint8_t *W13q, const uint8_t *W13s, const uint8_t *W2q, const uint8_t *W2s,
                      int32_t *counts, int32_t *seg_off, moe_src *phi, int32_t *route_row, uint8_t *Xq,
-                     uint8_t *Xs, uint8_t *Aq, uint8_t *As, uint16_t *Y, uint16_t *out, void *ws,
+                     uint8_t *Xs, uint8_t *Aq, uint8_t *As, uint16_t *HU, uint16_t *Y, uint16_t *out, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/*
+ * moe_quantize_mx_t — MX quantization of the columns of bf16 matrices:
+ * src [batch][R][C] -> q [batch][C][R] codes, scales [batch][C][R/32], each
+ * column of src in blocks of 32 consecutive rows (the format above, blocked
+ * along R).  The backward's weights: W2 [L][H][I] (R = H) for the down dgrad,
+ * W13 [L][2I][H] (R = 2I) for the gate/up dgrad, once per weight update.
+ * Needs R a multiple of 32 and C of 8; src and q 16-byte aligned.
+ * Errors: MOE_EINVAL for bad sizes or pointers.
+ */
+int moe_quantize_mx_t(const uint16_t *src, int64_t batch, int32_t R, int32_t C, uint8_t *q, uint8_t *scales,
+                      void *stream);
+
+/*
+ * moe_layer_bwd_mx — backward of moe_layer_fwd_mx with MXFP8 products ([BPT]
+ * section 3 and [MoK] section 6 report an MXFP8 backward; [MoK] section 5
+ * fuses the quantization into the loads, the GEMMs and SwiGLU).  Reading:
+ * every product takes MX operands blocked along its own reduction dimension,
+ * quantized from the value the bf16 backward (moe_layer_bwd) uses there:
+ *   dA' = dO_d . W2[l]    over H:  dO_d rows, W2 columns (W2tq);
+ *   dXd = dHU . W13[l]    over 2I: dHU rows, W13 columns (W13tq);
+ *   dW2[l]  = (w dO_d)^T a, dW13[l] = dHU^T Xd, over the expert's dispatched
+ *   rows: both operands quantized along the rows in blocks of 32 rows.
+ * a is the forward's Aq / As (dequantized exactly); h and u its saved HU;
+ * dw = dA' . a, dA = w dA', dh = dA u silu'(h), du = dA silu(h) in fp32;
+ * dHU, dO_d w, dXd and dX are rounded to bf16 once, dW13 / dW2 / dw are fp32.
+ *   dOut  bf16 [P][Np][H]   in
+ *   w, phi, route_row, seg_off   from the forward
+ *   X     bf16 [P][Np][H]   the forward's input (its rows are pulled through
+ *                           phi and quantized along the dispatched rows)
+ *   HU    bf16 [cap][2I], Aq [cap][I], As [cap][I/32]   saved by the forward
+ *   W13tq, W13ts  MX codes [L][H][2I] and scales [L][H][2I/32] (moe_quantize_mx_t
+ *                 of W13 with R = 2I, C = H)
+ *   W2tq, W2ts    MX codes [L][I][H] and scales [L][I][H/32] (R = H, C = I)
+ *   dX, dW13, dW2, dw   out, as in moe_layer_bwd
+ *   ws >= moe_workspace_bytes(d, MOE_OP_LAYER_BWD_MX): moe_layer_bwd's buffers,
+ *   then the row-quantized dO_d and dHU and the four row-blocked operands of
+ *   the weight gradients, stored transposed.
+ * Pointers: dOut, X, phi, HU, Aq, W13tq, W2tq, dX, ws 16-byte aligned; the
+ * others 4-byte aligned.  d->num_batches == 1.  Every reduction has a fixed
+ * order, so repeated calls give bitwise the same outputs.
+ */
+int moe_layer_bwd_mx(const moe_desc *d, const uint16_t *dOut, const float *w, const uint16_t *X, const moe_src *phi,
+                     const int32_t *route_row, const int32_t *seg_off, const uint16_t *HU, const uint8_t *Aq,
+                     const uint8_t *As, const uint8_t *W13tq, const uint8_t *W13ts, const uint8_t *W2tq,
+                     const uint8_t *W2ts, uint16_t *dX, float *dW13, float *dW2, float *dw, void *ws,
                      size_t ws_bytes, void *stream);
 
 /*

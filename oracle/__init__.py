@@ -6,8 +6,11 @@ shares no code with the HIP library (``routing_schedule_expert_amd``) and never
 imports it.
 
 The arithmetic lives in ``moe_oracle.c`` (plain C, double precision, built with
-gcc); this module only marshals numpy arrays.  Every function names the page
-and section it follows in the C source.
+gcc); this module marshals numpy arrays, except ``mx_layer_bwd``, which writes
+the MXFP8 backward a second time in matrix form (numpy fp64 products on
+dequantized operands, per expert segment), fast enough for full experts at
+the Kimi shape, and pinned against the C loops.  Every function names the page
+and section it follows.
 
 Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
   schedule, schedule_counting, schedule_rescan  pinned (brute force, closed forms,
@@ -26,11 +29,11 @@ Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
   mx_expert_ffn_rows, mx_layer_fwd_tokens        pinned (dot products vs numpy on the
                                                    dequantized operands; token path = rows +
                                                    combine; close to the bf16 FFN)
-  mx_weights_t, mx_bwd_tokens, mx_wgrad_elems    pinned (matrix-form numpy composition on
-                                                   dequantized operands at tiny shapes; within
-                                                   the format's error of the bf16 backward;
-                                                   exact scaling by powers of two of dOut;
-                                                   zero dOut, non-local tokens)
+  mx_weights_t, mx_bwd_tokens, mx_wgrad_elems,   pinned (the C loops and the matrix form agree
+    mx_layer_bwd                                   to 1e-12 at tiny shapes; within the format's
+                                                   error of the bf16 backward; exact scaling by
+                                                   powers of two of dOut; zero dOut, non-local
+                                                   tokens)
   shared_ffn_tokens, layer_fwd_tokens_shared     pinned (dense SwiGLU vs torch fp64 with no
                                                    local routes; zero shared weights leave the
                                                    routed output; the routed part stays linear
@@ -491,6 +494,98 @@ def mx_wgrad_elems(sched, routes, w, X, Xq, Xs, W13q, W13s, wt, dOut, expert: in
                                _ptr(W13s), _ptr(W2tq), _ptr(W2ts), _ptr(dOut), _ptr(e13), e13.shape[0], _ptr(g13),
                                _ptr(e2), e2.shape[0], _ptr(g2), _ptr(a13), _ptr(a2))
     return (g13, g2, a13, a2) if with_abs else (g13, g2)
+
+
+def _bf16_via_f32(x):
+    """Round doubles to float, then to bf16 with ties to even (the rounding
+    the kernels apply to the values they keep in bf16)."""
+    f = np.asarray(x, np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    return u.view(np.float32).astype(np.float64)
+
+
+def _bf16_values(b):
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _colq(M):
+    """MX codes and scales of the columns of M [rows][C] along the rows
+    (codes [C][rows], scales [C][rows/32])."""
+    return mx_quantize_f64(np.ascontiguousarray(np.asarray(M, np.float64).T))
+
+
+def mx_layer_bwd(routes, w, X, W13, W2, dOut, L: int, base: int = 0, experts=None):
+    """The MXFP8 backward in matrix form (the reading of moe_oracle.c's MXFP8
+    backward section): per local expert segment of oracle.schedule's table,
+    the forward (h, u from the MX codes of X and W13; a = silu(h) u, its row
+    codes), then dA' = dO . W2 (dO rows along H, W2 columns along H),
+    dw = dA' . a, dHU = bf16(w dA' u silu'(h), w dA' silu(h)) with h, u as
+    bf16, dXd = dHU . W13 (dHU rows along 2I, W13 columns along 2I), and the
+    weight gradients from column codes along the segment's rows:
+    dW2 = (bf16(w dO))^T a, dW13 = dHU^T Xd.  experts (default all) limits
+    the segments computed; the token side (dX, dw) sums only their rows.
+    Returns dict: 'sched', 'dX' [P*Np][H], 'dw' [P*Np][K], and per computed
+    expert l a dict 'seg'[l] with rows, HU (double, exact), a (dequantized
+    codes; a_exact before quantization; HUabs the sums of the magnitudes of
+    h's and u's terms), dAp, dHU (bf16 values), dHUq/dHUs (row codes), dXd, the column
+    codes dHUT, aT, XdT, dOwT (each (codes [C][rows], scales)) and dW13, dW2.
+    Dense numpy products in double; for shapes whose segments fit in memory."""
+    routes = _i32(routes)
+    P, Np, K = routes.shape
+    X, W13, W2, dOut = _u16(X), _u16(W13), _u16(W2), _u16(dOut)
+    H = X.shape[-1]
+    I = W13.shape[1] // 2
+    w = np.asarray(w, np.float32).reshape(-1, K)
+    s = schedule(routes, L, base)
+    rr = s.route_row.reshape(-1, K)
+    Xdeq = mx_dequantize(*mx_quantize(X)).reshape(-1, H)
+    dOq = mx_dequantize(*mx_quantize(dOut)).reshape(-1, H)
+    dOv = _bf16_values(dOut).reshape(-1, H)
+    Xv = _bf16_values(X).reshape(-1, H)
+    dX = np.zeros((P * Np, H))
+    dw = np.zeros((P * Np, K))
+    seg = {}
+    for l in (range(L) if experts is None else experts):
+        r0, r1 = int(s.seg_off[l]), int(s.seg_off[l + 1])
+        if r1 == r0:
+            continue
+        rows = np.arange(r0, r1)
+        ph = s.phi[rows]
+        re = ph[:, 0] >= 0
+        g = np.where(re, ph[:, 0].astype(np.int64) * Np + ph[:, 1], 0)
+        slot = np.full(rows.size, -1, np.int64)
+        tk, jk = np.nonzero((rr >= r0) & (rr < r1))
+        slot[rr[tk, jk] - r0] = jk
+        wr = np.where(re, w[g, np.maximum(slot, 0)].astype(np.float64), 0.0)
+        W13deq = mx_dequantize(*mx_quantize(W13[l]))                       # [2I][H]
+        W2t = mx_dequantize(*mx_transpose_quantize(W2[l]))                 # [I][H]
+        W13t = mx_dequantize(*mx_transpose_quantize(W13[l]))               # [H][2I]
+        Xg = np.where(re[:, None], Xdeq[g], 0.0)
+        HU = Xg @ W13deq.T
+        hh, uu = HU[:, :I], HU[:, I:]
+        a_exact = hh / (1.0 + np.exp(-hh)) * uu
+        Aq, As = mx_quantize_f64(a_exact)
+        a = mx_dequantize(Aq, As)
+        hb, ub = _bf16_via_f32(hh), _bf16_via_f32(uu)
+        dAp = np.where(re[:, None], dOq[g], 0.0) @ W2t.T
+        dA = wr[:, None] * dAp
+        sg = 1.0 / (1.0 + np.exp(-hb))
+        dHU = np.concatenate([_bf16_via_f32(dA * ub * sg * (1.0 + hb * (1.0 - sg))), _bf16_via_f32(dA * hb * sg)], 1)
+        dHUq, dHUs = mx_quantize_f64(dHU)
+        dXd = mx_dequantize(dHUq, dHUs) @ W13t.T
+        dwr = (dAp * a).sum(1)
+        for k in np.nonzero(re)[0]:
+            dX[g[k]] += dXd[k]
+            dw[g[k], slot[k]] = dwr[k]
+        dOw = np.where(re[:, None], _bf16_via_f32(wr[:, None] * dOv[g]), 0.0)
+        XdT, dOwT, aT, dHUT = (_colq(M) for M in (np.where(re[:, None], Xv[g], 0.0), dOw, a, dHU))
+        seg[l] = {"rows": rows, "HU": HU, "HUabs": np.abs(Xg) @ np.abs(W13deq).T, "a_exact": a_exact, "a": a,
+                  "Aq": Aq, "As": As, "dAp": dAp, "dHU": dHU, "dHUq": dHUq,
+                  "dHUs": dHUs, "dXd": dXd, "XdT": XdT, "dOwT": dOwT, "aT": aT, "dHUT": dHUT, "W13t": W13t,
+                  "dW2": mx_dequantize(*dOwT) @ mx_dequantize(*aT).T,
+                  "dW13": mx_dequantize(*dHUT) @ mx_dequantize(*XdT).T}
+    return {"sched": s, "dX": dX, "dw": dw, "seg": seg}
 
 
 # ---------------------------------------------------------------------------

@@ -667,6 +667,21 @@ __device__ __forceinline__ void epilogue_store_f32_w(AccW<WM, WN> &acc, float *d
     }
 }
 
+// The activation a as the down-dgrad epilogue reads it: load() fetches 8
+// consecutive columns of one row (col a multiple of 8), at() unpacks value i
+// of them where it is used.  Bf16 rows [rows][ld].
+struct ARowsBf16 {
+    const uint16_t *p;
+    int64_t ld;
+    using Raw = u32x4;
+    __device__ __forceinline__ Raw load(int row, int col) const {
+        return *reinterpret_cast<const u32x4 *>(p + (int64_t)row * ld + col);
+    }
+    __device__ __forceinline__ static float at(const Raw &v, int i) {
+        return __uint_as_float((i & 1) ? (v[i >> 1] & 0xffff0000u) : (v[i >> 1] << 16));
+    }
+};
+
 // Down-dgrad tile -> SwiGLU backward.  acc holds dA' = dO_d W2 for 256 rows
 // and the 256 columns [n0, n0+256) of the I activations; with w the row's
 // router weight, h, u the saved gate/up pre-activations and a the activation:
@@ -677,8 +692,8 @@ __device__ __forceinline__ void epilogue_store_f32_w(AccW<WM, WN> &acc, float *d
 // every thread takes 8 contiguous columns of one row, so A, h, u are read and
 // dh, du written with 16-byte accesses, and the 32 threads of a row add their
 // partial dots in a fixed butterfly (ascending columns inside a thread).
-template <int WM, int WN>
-__device__ __forceinline__ void epilogue_swiglu_bwd_w(AccW<WM, WN> &acc, char *lds, const uint16_t *A,
+template <int WM, int WN, class ARows>
+__device__ __forceinline__ void epilogue_swiglu_bwd_w(AccW<WM, WN> &acc, char *lds, const ARows &A,
                                                       const uint16_t *HU, const float *wrow, uint16_t *dHU,
                                                       float *part, int nparts, int I, int n0) {
     using WG = WaveGrid<WM, WN>;
@@ -716,7 +731,7 @@ __device__ __forceinline__ void epilogue_swiglu_bwd_w(AccW<WM, WN> &acc, char *l
                 const float4 d0 = *reinterpret_cast<const float4 *>(st + rl * 256 + cc);
                 const float4 d1 = *reinterpret_cast<const float4 *>(st + rl * 256 + cc + 4);
                 const float dap[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
-                const u32x4 av = *reinterpret_cast<const u32x4 *>(A + (int64_t)row * I + n0 + cc);
+                const typename ARows::Raw av = A.load(row, n0 + cc);
                 const u32x4 hv = *reinterpret_cast<const u32x4 *>(HU + (int64_t)row * ld2 + n0 + cc);
                 const u32x4 uv = *reinterpret_cast<const u32x4 *>(HU + (int64_t)row * ld2 + I + n0 + cc);
                 u32x4 dh, du;
@@ -725,7 +740,7 @@ __device__ __forceinline__ void epilogue_swiglu_bwd_w(AccW<WM, WN> &acc, char *l
                     float rh[2], ru[2];
 #pragma unroll
                     for (int j = 0; j < 2; ++j) {
-                        const float a = __uint_as_float(j ? (av[k] & 0xffff0000u) : (av[k] << 16));
+                        const float a = ARows::at(av, 2 * k + j);
                         const float h = __uint_as_float(j ? (hv[k] & 0xffff0000u) : (hv[k] << 16));
                         const float u = __uint_as_float(j ? (uv[k] & 0xffff0000u) : (uv[k] << 16));
                         const float d = dap[2 * k + j];

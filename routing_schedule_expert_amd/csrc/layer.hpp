@@ -177,6 +177,7 @@ struct MxFfnArgs {
     const uint8_t *W13q, *W13s, *W2q, *W2s;  // [L][2I][H] (+/32), [L][H][I] (+/32)
     const int32_t *seg_off;
     uint8_t *Aq, *As;  // MX codes [cap][I] and scale bytes [cap][I/32] of a
+    uint16_t *HU;      // nullable: bf16 [cap][2I], h then u (saved for the backward)
     uint16_t *Y;       // bf16 [cap][H]
     int L, H, I;
 };
@@ -197,8 +198,10 @@ __device__ __forceinline__ void mx_gateup_tile(const MxFfnArgs &a, int mt, int n
                  0};
     AccW<kFwdWM, kFwdWN> acc;
     gemm_mainloop_mx<kFwdWM, kFwdWN, SG>(ak, bk, as, bs, H / 128, true, lds, acc);
+    uint16_t *hu = a.HU ? a.HU + (int64_t)m0 * 2 * I + nt * 128 : nullptr;
     epilogue_swiglu_mx<kFwdWM, kFwdWN>(acc, lds, a.Aq + (int64_t)m0 * I + nt * 128, I,
-                                       a.As + (int64_t)m0 * (I / 32) + nt * 4, I / 32);
+                                       a.As + (int64_t)m0 * (I / 32) + nt * 4, I / 32, hu, hu ? hu + I : nullptr,
+                                       2ll * I);
 }
 
 template <int SG>
@@ -422,7 +425,7 @@ __device__ __forceinline__ void bwd_down_phase(const BwdArgs &a, char *lds) {
         const TOp bk{a.W2 + (int64_t)l * H * I + nt * 256, I, min(256, I - nt * 256)};  // [k = h][i]
         AccW<kBwdWM, kBwdWN> acc;
         gemm_mainloop_x<kBwdWM, kBwdWN, false, true>(ak, bk, H / 64, false, lds, acc);
-        epilogue_swiglu_bwd_w<kBwdWM, kBwdWN>(acc, lds, a.A + (int64_t)m0 * I, a.HU + (int64_t)m0 * 2 * I, a.wrow + m0,
+        epilogue_swiglu_bwd_w<kBwdWM, kBwdWN>(acc, lds, ARowsBf16{a.A + (int64_t)m0 * I, I}, a.HU + (int64_t)m0 * 2 * I, a.wrow + m0,
                                               a.dHU + (int64_t)m0 * 2 * I, a.part + (int64_t)m0 * a.nparts, a.nparts, I,
                                               nt * 256);
     }
@@ -514,15 +517,15 @@ __device__ __forceinline__ void wgrad_tile(const WgradArgs &a, int l, int mt, in
 // in one pass).  Longest experts first.  The reverse-dispatch sum `c` (B4,
 // HBM-bound) shares the launch as 64-token work items after the tiles (the
 // deferred weight gradients overlap the last reverse-dispatch rounds).
-__device__ __forceinline__ void wgrad_phase(const WgradArgs &a, const WindowCombine &c, char *lds) {
-    const int H = a.H, I = a.I, L = a.L, G = a.G;
-    __shared__ int s_order[256];
+// s_order[rank] = the local expert with the rank-th most rows over G tables
+// (ties by ascending id); only for L <= 256.
+__device__ __forceinline__ void experts_by_rows(const int32_t *seg_off, int L, int G, int *s_order) {
     __syncthreads();
     if (L <= 256) {
         for (int l = threadIdx.x; l < L; l += blockDim.x) {
             auto total = [&](int e) {
                 int n = 0;
-                for (int g = 0; g < G; ++g) n += a.seg_off[g * (L + 1) + e + 1] - a.seg_off[g * (L + 1) + e];
+                for (int g = 0; g < G; ++g) n += seg_off[g * (L + 1) + e + 1] - seg_off[g * (L + 1) + e];
                 return n;
             };
             const int len = total(l);
@@ -535,6 +538,12 @@ __device__ __forceinline__ void wgrad_phase(const WgradArgs &a, const WindowComb
         }
     }
     __syncthreads();
+}
+
+__device__ __forceinline__ void wgrad_phase(const WgradArgs &a, const WindowCombine &c, char *lds) {
+    const int H = a.H, I = a.I, L = a.L, G = a.G;
+    __shared__ int s_order[256];
+    experts_by_rows(a.seg_off, L, G, s_order);
     const int mt2 = H / 256, nt2 = (I + 255) / 256;   // dW2 [H][I]
     const int mt13 = 2 * I / 256, nt13 = H / 256;      // dW13 [2I][H]
     const int per = mt2 * nt2 + mt13 * nt13;

@@ -12,6 +12,7 @@
 #include "common.hpp"
 #include "gemm.hpp"
 #include "layer.hpp"
+#include "mxbwd.hpp"
 #include "rowops.hpp"
 #include "schedule.hpp"
 
@@ -149,6 +150,33 @@ template <int SG>
 __global__ __launch_bounds__(kFwdThreads) void k_mx_down(MxFfnArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kMxLds];
     mx_down_phase<SG>(a, lds);
+}
+
+__global__ __launch_bounds__(256) void k_mx_quantize_rows(const uint16_t *src, const int32_t *nrows, int K, uint8_t *q,
+                                                         uint8_t *s) {
+    mx_quantize_rows_body(src, nrows, K, q, s);
+}
+
+__global__ __launch_bounds__(kColqThreads) void k_mx_colq(ColQArgs a) {
+    __shared__ __attribute__((aligned(16))) float st[kColqLds / 4];
+    mx_colq_body(a, st);
+}
+
+template <int SG>
+__global__ __launch_bounds__(kFwdThreads) void k_mx_bwd_down(MxBwdArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kMxLds];
+    mx_bwd_down_phase<SG>(a, lds);
+}
+
+template <int SG>
+__global__ __launch_bounds__(kFwdThreads) void k_mx_bwd_gateup(MxBwdArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kMxLds];
+    mx_bwd_gateup_phase<SG>(a, lds);
+}
+
+__global__ __launch_bounds__(kFwdThreads) void k_mx_wgrad(MxWgradArgs a, WindowCombine c) {
+    __shared__ __attribute__((aligned(16))) char lds[kMxLds];
+    mx_wgrad_phase(a, c, lds);
 }
 
 __global__ __launch_bounds__(kFwdThreads) void k_bwd_down(BwdArgs a) {
@@ -294,6 +322,47 @@ int64_t bwd_ws_bytes(const moe_desc *d) {
     const int64_t cap = cap_rows(d), H = d->H, I = d->I;
     return align256(cap * H * 2) * 3 + align256(cap * 2 * I * 2) + align256(cap * 4) +
            align256(cap * 4ll * bwd_nparts(d));
+}
+
+// MX backward workspace, after the bf16 backward's buffers: the row-quantized
+// dO_d and dHU, and the four column-quantized operands of the weight
+// gradients stored transposed with mx_ldt codes per row.
+int64_t mx_ldt(const moe_desc *d) { return (cap_rows(d) + 511) / 512 * 512; }
+
+// The MX buffers in carving order (the workspace fields MOE_WS_MX_*_Q / _S
+// name them in this order from MOE_WS_MX_DHU_Q on).
+enum MxBuf { kDOq, kDOs, kDHUq, kDHUs, kDOwTq, kDOwTs, kATq, kATs, kXdTq, kXdTs, kDHUTq, kDHUTs, kMxBufs };
+static_assert(MOE_WS_MX_DHUT_S - MOE_WS_MX_DO_Q + 1 == kMxBufs, "one workspace field per MX buffer");
+
+// Byte offsets of the MX buffers after the bf16 backward's; returns the total.
+int64_t mx_bwd_offsets(const moe_desc *d, int64_t (&off)[kMxBufs]) {
+    const int64_t cap = cap_rows(d), H = d->H, I = d->I, ldt = mx_ldt(d);
+    const int64_t bytes[kMxBufs] = {cap * H,     cap * H / 32,     cap * 2 * I,     cap * 2 * I / 32,
+                                    H * ldt,     H * ldt / 32,     I * ldt,         I * ldt / 32,
+                                    H * ldt,     H * ldt / 32,     2 * I * ldt,     2 * I * ldt / 32};
+    int64_t o = bwd_ws_bytes(d);
+    for (int i = 0; i < kMxBufs; ++i) {
+        off[i] = o;
+        o += align256(bytes[i]);
+    }
+    return o;
+}
+
+struct MxBwdBufs {
+    uint8_t *b[kMxBufs];
+};
+
+MxBwdBufs carve_mx_bwd(char *ws, const moe_desc *d) {
+    int64_t off[kMxBufs];
+    mx_bwd_offsets(d, off);
+    MxBwdBufs m;
+    for (int i = 0; i < kMxBufs; ++i) m.b[i] = reinterpret_cast<uint8_t *>(ws + off[i]);
+    return m;
+}
+
+int64_t mx_bwd_ws_bytes(const moe_desc *d) {
+    int64_t off[kMxBufs];
+    return mx_bwd_offsets(d, off);
 }
 
 constexpr int64_t kBarrierBytes = 256;
@@ -523,7 +592,8 @@ int64_t moe_capacity_rows(const moe_desc *d) {
 
 int64_t moe_workspace_bytes(const moe_desc *d, int op) {
     const bool ffn = op == MOE_OP_EXPERT_FFN || op == MOE_OP_LAYER_FWD || op == MOE_OP_LAYER_BWD ||
-                     op == MOE_OP_DISPATCH || op == MOE_OP_COMBINE || op == MOE_OP_LAYER_FWD_SHARED;
+                     op == MOE_OP_DISPATCH || op == MOE_OP_COMBINE || op == MOE_OP_LAYER_FWD_SHARED ||
+                     op == MOE_OP_LAYER_BWD_MX;
     if (check_desc(d, ffn) != MOE_OK) return -1;
     switch (op) {
         case MOE_OP_SCHEDULE: return sched_ws_bytes(d);
@@ -536,6 +606,7 @@ int64_t moe_workspace_bytes(const moe_desc *d, int op) {
             return kBarrierBytes + sched_ws_bytes(&one);
         }
         case MOE_OP_LAYER_BWD: return bwd_ws_bytes(d);
+        case MOE_OP_LAYER_BWD_MX: return mx_bwd_ws_bytes(d);
         case MOE_OP_LAYER_FWD_SHARED: {
             moe_desc one = *d;
             one.num_batches = 1;
@@ -558,6 +629,13 @@ int64_t moe_workspace_field(const moe_desc *d, int op, int field) {
     if (field == MOE_WS_BARRIER_STATUS) {
         if (op == MOE_OP_LAYER_FWD || op == MOE_OP_EXPERT_FFN) return 8;
         return -1;
+    }
+    if (op == MOE_OP_LAYER_BWD_MX) {
+        // the bf16 backward's dHU follows dO_d, dXd and dO_d w
+        if (field == MOE_WS_MX_DHU) return 3 * align256(cap_rows(d) * d->H * 2);
+        int64_t off[kMxBufs];
+        mx_bwd_offsets(d, off);
+        if (field >= MOE_WS_MX_DO_Q && field < MOE_WS_MX_DO_Q + kMxBufs) return off[field - MOE_WS_MX_DO_Q];
     }
     return -1;
 }
@@ -721,6 +799,27 @@ BwdBufs carve_bwd(char *p, const moe_desc *d) {
     return b;
 }
 
+// The row weights and B1 of one table: the reverse-combine gather of the
+// output gradient (dO_d) and its rows times w (dO_d w).
+int bwd_gather(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const float *w, const moe_src *phi,
+               const int32_t *route_row, const int32_t *seg_off, const BwdBufs &bb, hipStream_t s) {
+    const int64_t cap = cap_rows(d);
+    const bool window = tstride > d->Np;
+    const int32_t *npad = seg_off + d->L;
+    const int np_stride = window ? (int)tstride : d->Np;
+    {
+        TraceScope tr("bwd_row_weight", s);
+        hipLaunchKernelGGL(k_row_weight, dim3((int)std::min<int64_t>((cap + 255) / 256, 4096)), dim3(256), 0, s, phi,
+                           npad, route_row, w, bb.wrow, np_stride, d->K, cap);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    const int grid = (int)std::min<int64_t>((cap + 3) / 4, 16ll * device_cus());
+    TraceScope tr("bwd_gather", s);
+    hipLaunchKernelGGL(k_gather_scaled, dim3(grid), dim3(256), 0, s, dOut, phi, npad, bb.wrow, bb.dOd, bb.dOw,
+                       np_stride, d->H, cap);
+    return launch_status();
+}
+
 // The data gradients of one table's rows (B1, B2, dw, B3).  d describes the
 // tokens the table covers (a window of tstride tokens per partition when
 // tstride > d->Np: dOut, w, route_row and dw then point at the window's first
@@ -745,22 +844,8 @@ int bwd_dgrad(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const fl
     a.H = d->H;
     a.I = d->I;
     a.nparts = bwd_nparts(d);
-    const int32_t *npad = seg_off + d->L;
-    const int np_stride = window ? (int)tstride : d->Np;
-    {
-        TraceScope tr("bwd_row_weight", s);
-        hipLaunchKernelGGL(k_row_weight, dim3((int)std::min<int64_t>((cap + 255) / 256, 4096)), dim3(256), 0, s, phi,
-                           npad, route_row, w, bb.wrow, np_stride, d->K, cap);
-    }
-    if (launch_status() != MOE_OK) return MOE_EHIP;
-    // B1: reverse-combine gather of the output gradient, and its rows times w
-    {
-        const int grid = (int)std::min<int64_t>((cap + 3) / 4, 16ll * device_cus());
-        TraceScope tr("bwd_gather", s);
-        hipLaunchKernelGGL(k_gather_scaled, dim3(grid), dim3(256), 0, s, dOut, phi, npad, bb.wrow, bb.dOd, bb.dOw,
-                           np_stride, d->H, cap);
-    }
-    if (launch_status() != MOE_OK) return MOE_EHIP;
+    int rc = bwd_gather(d, tstride, dOut, w, phi, route_row, seg_off, bb, s);
+    if (rc != MOE_OK) return rc;
     const int grid = gemm_grid();
     // B2: down-projection dgrad with the SwiGLU backward and dw partials
     {
@@ -924,7 +1009,7 @@ int moe_quantize_mx(const uint16_t *src, int64_t rows, int32_t K, uint8_t *q, ui
 int moe_layer_fwd_mx(const moe_desc *d, const int32_t *routes, const float *w, const uint16_t *X,
                      const uint8_t *W13q, const uint8_t *W13s, const uint8_t *W2q, const uint8_t *W2s,
                      int32_t *counts, int32_t *seg_off, moe_src *phi, int32_t *route_row, uint8_t *Xq,
-                     uint8_t *Xs, uint8_t *Aq, uint8_t *As, uint16_t *Y, uint16_t *out, void *ws,
+                     uint8_t *Xs, uint8_t *Aq, uint8_t *As, uint16_t *HU, uint16_t *Y, uint16_t *out, void *ws,
                      size_t ws_bytes, void *stream) {
     int rc = check_desc(d, true);
     if (rc != MOE_OK) return rc;
@@ -932,6 +1017,7 @@ int moe_layer_fwd_mx(const moe_desc *d, const int32_t *routes, const float *w, c
     const void *a16[] = {routes, w, X, W13q, W2q, counts, seg_off, phi, route_row, Xq, Aq, Y, out, ws};
     for (const void *p : a16)
         if (!p || !aligned16(p)) return MOE_EINVAL;
+    if (HU && !aligned16(HU)) return MOE_EINVAL;
     const void *a4[] = {W13s, W2s, Xs, As};
     for (const void *p : a4)
         if (!p || !aligned4(p)) return MOE_EINVAL;
@@ -957,6 +1043,7 @@ int moe_layer_fwd_mx(const moe_desc *d, const int32_t *routes, const float *w, c
     a.seg_off = seg_off;
     a.Aq = Aq;
     a.As = As;
+    a.HU = HU;
     a.Y = Y;
     a.L = d->L;
     a.H = d->H;
@@ -980,6 +1067,186 @@ int moe_layer_fwd_mx(const moe_desc *d, const int32_t *routes, const float *w, c
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
     return launch_combine(d, Y, route_row, w, out, s, "combine");
+}
+
+}  // extern "C"
+
+namespace {
+
+int launch_colq(const ColQArgs &a, int64_t max_tiles, hipStream_t s, const char *name) {
+    if (max_tiles <= 0) return MOE_OK;
+    const int grid = (int)std::min<int64_t>(max_tiles, 8ll * device_cus());
+    TraceScope tr(name, s);
+    hipLaunchKernelGGL(k_mx_colq, dim3(grid), dim3(kColqThreads), 0, s, a);
+    return launch_status();
+}
+
+int64_t colq_tiles(int64_t rows, int64_t cols, int64_t batch) {
+    return (rows + kColqRows - 1) / kColqRows * ((cols + kColqCols - 1) / kColqCols) * batch;
+}
+
+// Column quantization of the dispatched rows [rows < *npad][C] of a table,
+// into [C][ldt] codes: from bf16 rows (src, ld; gathered through phi when
+// given) or from MX codes (q, s [cap][C]).
+ColQArgs colq_rows(const uint16_t *src, int64_t ld, const moe_src *phi, int32_t Np, const uint8_t *srcq,
+                   const uint8_t *srcs, const int32_t *npad, int64_t cap, int C, uint8_t *q, uint8_t *sc,
+                   int64_t ldt) {
+    ColQArgs a{};
+    a.src = src;
+    a.ld = ld;
+    a.in_bstride = 0;
+    a.phi = phi;
+    a.Np = Np;
+    a.srcq = srcq;
+    a.srcs = srcs;
+    a.nrows = npad;
+    a.R = cap;
+    a.C = C;
+    a.batch = 1;
+    a.q = q;
+    a.s = sc;
+    a.ldq = ldt;
+    a.out_bstride = 0;
+    return a;
+}
+
+int launch_quantize_rows(const uint16_t *src, const int32_t *npad, int64_t cap, int K, uint8_t *q, uint8_t *sc,
+                         hipStream_t s, const char *name) {
+    const int grid = (int)std::min<int64_t>((cap * (K / 32) + 255) / 256, 16ll * device_cus());
+    TraceScope tr(name, s);
+    hipLaunchKernelGGL(k_mx_quantize_rows, dim3(grid), dim3(256), 0, s, src, npad, K, q, sc);
+    return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_quantize_mx_t(const uint16_t *src, int64_t batch, int32_t R, int32_t C, uint8_t *q, uint8_t *scales,
+                      void *stream) {
+    if (batch < 0 || R <= 0 || C <= 0 || R % 32 || C % 8) return MOE_EINVAL;
+    if (batch == 0) return MOE_OK;
+    if (!src || !q || !scales || !aligned16(src) || !aligned16(q)) return MOE_EINVAL;
+    if (batch > (1ll << 30) / std::max<int64_t>(1, colq_tiles(R, C, 1))) return MOE_EUNSUPPORTED;
+    ColQArgs a{};
+    a.src = src;
+    a.ld = C;
+    a.in_bstride = (int64_t)R * C;
+    a.R = R;
+    a.C = C;
+    a.batch = (int)batch;
+    a.q = q;
+    a.s = scales;
+    a.ldq = R;
+    a.out_bstride = (int64_t)R * C;
+    return launch_colq(a, colq_tiles(R, C, batch), static_cast<hipStream_t>(stream), "mx_quantize_t");
+}
+
+int moe_layer_bwd_mx(const moe_desc *d, const uint16_t *dOut, const float *w, const uint16_t *X, const moe_src *phi,
+                     const int32_t *route_row, const int32_t *seg_off, const uint16_t *HU, const uint8_t *Aq,
+                     const uint8_t *As, const uint8_t *W13tq, const uint8_t *W13ts, const uint8_t *W2tq,
+                     const uint8_t *W2ts, uint16_t *dX, float *dW13, float *dW2, float *dw, void *ws,
+                     size_t ws_bytes, void *stream) {
+    int rc = check_desc(d, true);
+    if (rc != MOE_OK) return rc;
+    if (d->num_batches != 1) return MOE_EINVAL;
+    const void *a16[] = {dOut, X, phi, HU, Aq, W13tq, W2tq, dX, ws};
+    for (const void *p : a16)
+        if (!p || !aligned16(p)) return MOE_EINVAL;
+    const void *a4[] = {w, route_row, seg_off, As, W13ts, W2ts, dW13, dW2, dw};
+    for (const void *p : a4)
+        if (!p || !aligned4(p)) return MOE_EINVAL;
+    if ((int64_t)ws_bytes < mx_bwd_ws_bytes(d)) return MOE_ENOSPC;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t cap = cap_rows(d), ldt = mx_ldt(d);
+    const int H = d->H, I = d->I;
+    const BwdBufs bb = carve_bwd(static_cast<char *>(ws), d);
+    const MxBwdBufs mx = carve_mx_bwd(static_cast<char *>(ws), d);
+    uint8_t *const *mb = mx.b;
+    const int32_t *npad = seg_off + d->L;
+    rc = bwd_gather(d, 0, dOut, w, phi, route_row, seg_off, bb, s);
+    if (rc != MOE_OK) return rc;
+    rc = launch_quantize_rows(bb.dOd, npad, cap, H, mb[kDOq], mb[kDOs], s, "mx_bwd_quantize_dO");
+    if (rc != MOE_OK) return rc;
+    MxBwdArgs a;
+    a.dOq = mb[kDOq];
+    a.dOs = mb[kDOs];
+    a.W2tq = W2tq;
+    a.W2ts = W2ts;
+    a.Aq = Aq;
+    a.As = As;
+    a.HU = HU;
+    a.wrow = bb.wrow;
+    a.dHU = bb.dHU;
+    a.part = bb.part;
+    a.dHUq = mb[kDHUq];
+    a.dHUs = mb[kDHUs];
+    a.W13tq = W13tq;
+    a.W13ts = W13ts;
+    a.dXd = bb.dXd;
+    a.seg_off = seg_off;
+    a.L = d->L;
+    a.H = H;
+    a.I = I;
+    a.nparts = bwd_nparts(d);
+    const int grid = gemm_grid();
+    {
+        // B2; scale rows of H / 32 bytes: 16-byte scale DMAs when aligned
+        TraceScope tr("mx_bwd_down", s);
+        if (H % 512 == 0 && aligned16(W2ts))
+            hipLaunchKernelGGL(k_mx_bwd_down<4>, dim3(grid), dim3(kFwdThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(k_mx_bwd_down<1>, dim3(grid), dim3(kFwdThreads), 0, s, a);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    const int64_t nslots = (int64_t)d->P * d->Np * d->K;
+    {
+        TraceScope tr("bwd_dw", s);
+        hipLaunchKernelGGL(k_dw_finalize, dim3((int)std::min<int64_t>((nslots + 255) / 256, 4096)), dim3(256), 0, s,
+                           route_row, bb.part, a.nparts, dw, nslots, 0, (int64_t)0);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    rc = launch_quantize_rows(bb.dHU, npad, cap, 2 * I, mb[kDHUq], mb[kDHUs], s, "mx_bwd_quantize_dHU");
+    if (rc != MOE_OK) return rc;
+    {
+        TraceScope tr("mx_bwd_gateup", s);
+        if ((2 * I) % 512 == 0 && aligned16(W13ts))
+            hipLaunchKernelGGL(k_mx_bwd_gateup<4>, dim3(grid), dim3(kFwdThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL(k_mx_bwd_gateup<1>, dim3(grid), dim3(kFwdThreads), 0, s, a);
+    }
+    if (launch_status() != MOE_OK) return MOE_EHIP;
+    // the weight gradients' operands, quantized along the rows
+    const ColQArgs jobs[4] = {
+        colq_rows(bb.dOw, H, nullptr, 0, nullptr, nullptr, npad, cap, H, mb[kDOwTq], mb[kDOwTs], ldt),
+        colq_rows(nullptr, 0, nullptr, 0, Aq, As, npad, cap, I, mb[kATq], mb[kATs], ldt),
+        colq_rows(X, H, phi, d->Np, nullptr, nullptr, npad, cap, H, mb[kXdTq], mb[kXdTs], ldt),
+        colq_rows(bb.dHU, 2 * I, nullptr, 0, nullptr, nullptr, npad, cap, 2 * I, mb[kDHUTq], mb[kDHUTs], ldt)};
+    const char *names[4] = {"mx_bwd_colq_dOw", "mx_bwd_colq_a", "mx_bwd_colq_Xd", "mx_bwd_colq_dHU"};
+    for (int j = 0; j < 4; ++j) {
+        rc = launch_colq(jobs[j], colq_tiles(cap, jobs[j].C, 1), s, names[j]);
+        if (rc != MOE_OK) return rc;
+    }
+    MxWgradArgs wa;
+    wa.dOwTq = mb[kDOwTq];
+    wa.dOwTs = mb[kDOwTs];
+    wa.aTq = mb[kATq];
+    wa.aTs = mb[kATs];
+    wa.dHUTq = mb[kDHUTq];
+    wa.dHUTs = mb[kDHUTs];
+    wa.XdTq = mb[kXdTq];
+    wa.XdTs = mb[kXdTs];
+    wa.ld_t = ldt;
+    wa.seg_off = seg_off;
+    wa.dW13 = dW13;
+    wa.dW2 = dW2;
+    wa.L = d->L;
+    wa.H = H;
+    wa.I = I;
+    TraceScope tr("mx_bwd_wgrad_rdispatch", s);
+    hipLaunchKernelGGL(k_mx_wgrad, dim3(grid), dim3(kFwdThreads), 0, s, wa,
+                       reverse_dispatch(d, 0, bb.dXd, route_row, dX));
+    return launch_status();
 }
 
 }  // extern "C"

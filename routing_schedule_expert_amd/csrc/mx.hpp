@@ -318,10 +318,12 @@ __device__ __forceinline__ void gemm_mainloop_mx(const KOp &ak, const KOp &bk, c
 // Gate/up tile -> a = silu(gate) * up (256 rows x 128 columns), MX-quantized
 // along the columns: codes Aq[row][0..128) and 4 scale bytes per row.  The fp32
 // tile goes through LDS (128 KiB); then every thread quantizes whole 32-column
-// blocks of a row.
+// blocks of a row.  With HUg set, h and u are also stored as bf16 (the
+// backward's saved pre-activations): gate columns at HUg, up at HUu.
 template <int WM, int WN>
 __device__ __forceinline__ void epilogue_swiglu_mx(AccW<WM, WN> &acc, char *lds, uint8_t *Aq, int64_t ldq,
-                                                   uint8_t *As, int64_t lds_row) {
+                                                   uint8_t *As, int64_t lds_row, uint16_t *HUg, uint16_t *HUu,
+                                                   int64_t ldHU) {
     using WG = WaveGrid<WM, WN>;
     constexpr int NT = WG::THREADS, half = WG::NI / 2;
     const int t = threadIdx.x, wave = t >> 6, lane = t & 63, wm = wave / WN, wn = wave % WN;
@@ -355,6 +357,25 @@ __device__ __forceinline__ void epilogue_swiglu_mx(AccW<WM, WN> &acc, char *lds,
         out[0] = u32x4{w[0], w[1], w[2], w[3]};
         out[1] = u32x4{w[4], w[5], w[6], w[7]};
         As[row * lds_row + blk] = (uint8_t)sb;
+    }
+    if (HUg) {
+        const LaneStageW<128, WM> sg(lds, 0, wm, lane, wn * half * 32), su(lds, 32768, wm, lane, wn * half * 32);
+        __syncthreads();  // every thread is done reading the fp32 tile
+#pragma unroll
+        for (int mi = 0; mi < WG::MI; ++mi) {
+#pragma unroll
+            for (int ni = 0; ni < half; ++ni)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    sg.put(mi, e, ni * 32, acc[mi][ni][e]);
+                    su.put(mi, e, ni * 32, acc[mi][ni + half][e]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        const int tt = opaque_tid();
+        copy_staged<128, NT, false>(lds, HUg, ldHU, 128, tt);
+        copy_staged<128, NT, false>(lds + 32768, HUu, ldHU, 128, tt);
     }
 }
 

@@ -13,6 +13,7 @@ import ctypes
 import os
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -20,16 +21,18 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOSPC, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3, -4
 (MOE_OP_SCHEDULE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_LAYER_FWD, MOE_OP_LAYER_BWD,
- MOE_OP_LAYER_FWD_SHARED) = range(7)
+ MOE_OP_LAYER_FWD_SHARED, MOE_OP_LAYER_BWD_MX) = range(8)
 MOE_PERSISTENT = 1
 MOE_WS_INVALID_IDS, MOE_WS_BARRIER_STATUS = 0, 1
+(MOE_WS_MX_DHU, MOE_WS_MX_DO_Q, MOE_WS_MX_DO_S, MOE_WS_MX_DHU_Q, MOE_WS_MX_DHU_S, MOE_WS_MX_DOWT_Q, MOE_WS_MX_DOWT_S,
+ MOE_WS_MX_AT_Q, MOE_WS_MX_AT_S, MOE_WS_MX_XDT_Q, MOE_WS_MX_XDT_S, MOE_WS_MX_DHUT_Q, MOE_WS_MX_DHUT_S) = range(2, 15)
 
 EXPORTED = (
     "moe_strerror", "moe_capacity_rows", "moe_workspace_bytes", "moe_workspace_field", "moe_schedule",
     "moe_dispatch",
     "moe_expert_ffn", "moe_combine", "moe_layer_fwd", "moe_layer_bwd", "moe_trace_enable", "moe_trace_read",
-    "moe_quantize_mx",
-    "moe_layer_fwd_mx",
+    "moe_quantize_mx", "moe_quantize_mx_t",
+    "moe_layer_fwd_mx", "moe_layer_bwd_mx",
     "moe_ring_capacity_rows", "moe_ring_workspace_bytes", "moe_layer_fwd_ring", "moe_layer_bwd_ring",
     "moe_layer_fwd_shared", "moe_layer_fwd_noalloc",
 )
@@ -79,7 +82,9 @@ def load() -> ctypes.CDLL:
         "moe_layer_fwd": (ctypes.c_int, [D] + [P] * 14 + [i32, i32, P, sz, P]),
         "moe_layer_fwd_noalloc": (ctypes.c_int, [D] + [P] * 14 + [i32, i32, P, P]),
         "moe_quantize_mx": (ctypes.c_int, [P, i64, i32, P, P, P]),
-        "moe_layer_fwd_mx": (ctypes.c_int, [D] + [P] * 18 + [sz, P]),
+        "moe_quantize_mx_t": (ctypes.c_int, [P, i64, i32, i32, P, P, P]),
+        "moe_layer_fwd_mx": (ctypes.c_int, [D] + [P] * 19 + [sz, P]),
+        "moe_layer_bwd_mx": (ctypes.c_int, [D] + [P] * 18 + [sz, P]),
         "moe_layer_bwd": (ctypes.c_int, [D] + [P] * 16 + [sz, P]),
         "moe_layer_fwd_shared": (ctypes.c_int, [D, i32] + [P] * 19 + [sz, P]),
         "moe_ring_capacity_rows": (i64, [D, i32]),
@@ -275,13 +280,40 @@ def quantize_mx(src, stream=None):
     return q, s
 
 
-def moe_layer_fwd_mx(d, routes, w, X, W13q, W13s, W2q, W2s, counts, seg_off, phi, route_row, Xq, Xs, Aq, As, Y, out,
-                     ws, stream=None):
+def moe_quantize_mx_t(src, q, scales, stream=None):
+    """MX quantization of the columns of bf16 [..., R, C] along R into codes
+    uint8 [..., C, R] and scale bytes uint8 [..., C, R/32]."""
+    R, C = src.shape[-2], src.shape[-1]
+    batch = src.numel() // (R * C) if R * C else 0
+    rc = load().moe_quantize_mx_t(_dev(src), batch, R, C, _dev(q), _dev(scales), _stream(stream, src))
+    return _check(rc, "moe_quantize_mx_t")
+
+
+def quantize_mx_t(src, stream=None):
+    """Allocate and fill (codes, scales) of src's columns along its rows."""
+    R, C = src.shape[-2], src.shape[-1]
+    q = torch.empty(src.shape[:-2] + (C, R), dtype=torch.uint8, device=src.device)
+    s = torch.empty(src.shape[:-2] + (C, R // 32), dtype=torch.uint8, device=src.device)
+    moe_quantize_mx_t(src, q, s, stream)
+    return q, s
+
+
+def moe_layer_fwd_mx(d, routes, w, X, W13q, W13s, W2q, W2s, counts, seg_off, phi, route_row, Xq, Xs, Aq, As, HU, Y,
+                     out, ws, stream=None):
     rc = load().moe_layer_fwd_mx(ctypes.byref(d), _dev(routes), _dev(w), _dev(X), _dev(W13q), _dev(W13s), _dev(W2q),
                                  _dev(W2s), _dev(counts), _dev(seg_off), _dev(phi), _dev(route_row), _dev(Xq),
-                                 _dev(Xs), _dev(Aq), _dev(As), _dev(Y), _dev(out), _dev(ws),
+                                 _dev(Xs), _dev(Aq), _dev(As), _dev(HU), _dev(Y), _dev(out), _dev(ws),
                                  ws.numel() * ws.element_size(), _stream(stream, X))
     return _check(rc, "moe_layer_fwd_mx")
+
+
+def moe_layer_bwd_mx(d, dOut, w, X, phi, route_row, seg_off, HU, Aq, As, W13tq, W13ts, W2tq, W2ts, dX, dW13, dW2, dw,
+                     ws, stream=None):
+    rc = load().moe_layer_bwd_mx(ctypes.byref(d), _dev(dOut), _dev(w), _dev(X), _dev(phi), _dev(route_row),
+                                 _dev(seg_off), _dev(HU), _dev(Aq), _dev(As), _dev(W13tq), _dev(W13ts), _dev(W2tq),
+                                 _dev(W2ts), _dev(dX), _dev(dW13), _dev(dW2), _dev(dw), _dev(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream, dOut))
+    return _check(rc, "moe_layer_bwd_mx")
 
 
 @dataclass
@@ -294,12 +326,14 @@ class MxFwdBuffers:
     Xs: torch.Tensor
     Aq: torch.Tensor
     As: torch.Tensor
+    HU: torch.Tensor | None
     Y: torch.Tensor
     out: torch.Tensor
     ws: torch.Tensor
 
 
-def alloc_fwd_mx(d: moe_desc, device) -> MxFwdBuffers:
+def alloc_fwd_mx(d: moe_desc, device, save_hu: bool = False) -> MxFwdBuffers:
+    """MX forward buffers; save_hu keeps h and u (bf16) for moe_layer_bwd_mx."""
     cap = capacity_rows(d)
     i32, u8 = torch.int32, torch.uint8
     ntok = d.P * d.Np
@@ -312,6 +346,7 @@ def alloc_fwd_mx(d: moe_desc, device) -> MxFwdBuffers:
         Xs=torch.empty((d.P, d.Np, d.H // 32), dtype=u8, device=device),
         Aq=torch.empty((cap, d.I), dtype=u8, device=device),
         As=torch.empty((cap, d.I // 32), dtype=u8, device=device),
+        HU=torch.empty((cap, 2 * d.I), dtype=torch.bfloat16, device=device) if save_hu else None,
         Y=torch.empty((cap, d.H), dtype=torch.bfloat16, device=device),
         out=torch.empty((d.P, d.Np, d.H), dtype=torch.bfloat16, device=device),
         ws=torch.empty(max(workspace_bytes(d, MOE_OP_LAYER_FWD), 256), dtype=torch.uint8, device=device),
@@ -320,7 +355,56 @@ def alloc_fwd_mx(d: moe_desc, device) -> MxFwdBuffers:
 
 def layer_fwd_mx(d, routes, w, X, W13q, W13s, W2q, W2s, bufs: MxFwdBuffers, stream=None):
     return moe_layer_fwd_mx(d, routes, w, X, W13q, W13s, W2q, W2s, bufs.counts, bufs.seg_off, bufs.phi,
-                            bufs.route_row, bufs.Xq, bufs.Xs, bufs.Aq, bufs.As, bufs.Y, bufs.out, bufs.ws, stream)
+                            bufs.route_row, bufs.Xq, bufs.Xs, bufs.Aq, bufs.As, bufs.HU, bufs.Y, bufs.out, bufs.ws,
+                            stream)
+
+
+@dataclass
+class MxBwdGrads:
+    dX: torch.Tensor
+    dW13: torch.Tensor
+    dW2: torch.Tensor
+    dw: torch.Tensor
+    ws: torch.Tensor
+
+
+def alloc_bwd_mx(d: moe_desc, device) -> MxBwdGrads:
+    return MxBwdGrads(
+        dX=torch.empty((d.P, d.Np, d.H), dtype=torch.bfloat16, device=device),
+        dW13=torch.empty((d.L, 2 * d.I, d.H), dtype=torch.float32, device=device),
+        dW2=torch.empty((d.L, d.H, d.I), dtype=torch.float32, device=device),
+        dw=torch.empty((d.P, d.Np, d.K), dtype=torch.float32, device=device),
+        ws=torch.empty(workspace_bytes(d, MOE_OP_LAYER_BWD_MX), dtype=torch.uint8, device=device),
+    )
+
+
+def mx_bwd_views(d: moe_desc, ws: torch.Tensor) -> dict:
+    """Views of moe_layer_bwd_mx's workspace buffers (the MOE_WS_MX_* fields):
+    dHU bf16 [cap][2I]; row codes / scales (DO, DHU) [cap][C] / [cap][C/32];
+    column codes / scales (DOWT, AT, XDT, DHUT) [C][ldt] / [C][ldt/32]."""
+    cap = capacity_rows(d)
+    ldt = (cap + 511) // 512 * 512
+    H, I2 = d.H, 2 * d.I
+
+    def at(field, shape, dtype=torch.uint8):
+        off = workspace_field(d, MOE_OP_LAYER_BWD_MX, field)
+        n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+        return ws[off:off + n].view(dtype).view(shape)
+
+    v = {"dHU": at(MOE_WS_MX_DHU, (cap, I2), torch.bfloat16)}
+    for nm, f, C in (("DO", MOE_WS_MX_DO_Q, H), ("DHU", MOE_WS_MX_DHU_Q, I2)):
+        v[nm] = (at(f, (cap, C)), at(f + 1, (cap, C // 32)))
+    for nm, f, C in (("DOWT", MOE_WS_MX_DOWT_Q, H), ("AT", MOE_WS_MX_AT_Q, d.I), ("XDT", MOE_WS_MX_XDT_Q, H),
+                     ("DHUT", MOE_WS_MX_DHUT_Q, I2)):
+        v[nm] = (at(f, (C, ldt)), at(f + 1, (C, ldt // 32)))
+    return v
+
+
+def layer_bwd_mx(d, dOut, w, X, fwd: MxFwdBuffers, W13t, W2t, g: MxBwdGrads, stream=None):
+    """moe_layer_bwd_mx on a forward's buffers; W13t / W2t are the (codes,
+    scales) of quantize_mx_t(W13) and quantize_mx_t(W2)."""
+    return moe_layer_bwd_mx(d, dOut, w, X, fwd.phi, fwd.route_row, fwd.seg_off, fwd.HU, fwd.Aq, fwd.As, W13t[0],
+                            W13t[1], W2t[0], W2t[1], g.dX, g.dW13, g.dW2, g.dw, g.ws, stream)
 
 
 # ---------------------------------------------------------------------------

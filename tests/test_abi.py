@@ -160,13 +160,43 @@ def test_mx_arguments_rejected_before_launch():
     assert lib.moe_quantize_mx(None, 0, 64, None, None, None) == ops.MOE_OK  # nothing to do
     d = kimi()
     ws = lib.moe_workspace_bytes(ctypes.byref(d), ops.MOE_OP_LAYER_FWD)
-    args = p[:18]  # 17 operands and the workspace
+    args = p[:19]  # 18 operands and the workspace
     assert lib.moe_layer_fwd_mx(ctypes.byref(d), *args[:5], None, *args[6:], ws, None) == ops.MOE_EINVAL
     assert lib.moe_layer_fwd_mx(ctypes.byref(d), *args[:3], _fake(0x10004), *args[4:], ws, None) == ops.MOE_EINVAL
     assert lib.moe_layer_fwd_mx(ctypes.byref(d), *args, ws - 1, None) == ops.MOE_ENOSPC
     d2 = ops.make_desc(8, 7168, 8, 384, 48, H=65536 + 256, I=2048)  # rows wider than the zero row for padding
     ws2 = lib.moe_workspace_bytes(ctypes.byref(d2), ops.MOE_OP_LAYER_FWD)
     assert lib.moe_layer_fwd_mx(ctypes.byref(d2), *args, ws2, None) == ops.MOE_EUNSUPPORTED
+    # HU (operand 15) is optional but must be 16-byte aligned when given
+    assert lib.moe_layer_fwd_mx(ctypes.byref(d), *args[:15], _fake(0x10008), *args[16:], ws, None) == ops.MOE_EINVAL
+
+
+def test_mx_backward_arguments_and_workspace():
+    lib = ops.load()
+    p = [_fake(0x10000 * (i + 1)) for i in range(20)]
+    # column quantization: R a multiple of 32, C of 8, aligned pointers
+    assert lib.moe_quantize_mx_t(p[0], 2, 48, 64, p[1], p[2], None) == ops.MOE_EINVAL
+    assert lib.moe_quantize_mx_t(p[0], 2, 64, 60, p[1], p[2], None) == ops.MOE_EINVAL
+    assert lib.moe_quantize_mx_t(p[0], -1, 64, 64, p[1], p[2], None) == ops.MOE_EINVAL
+    assert lib.moe_quantize_mx_t(_fake(0x10008), 1, 64, 64, p[1], p[2], None) == ops.MOE_EINVAL
+    assert lib.moe_quantize_mx_t(None, 0, 64, 64, None, None, None) == ops.MOE_OK
+    d = kimi()
+    cap = ops.capacity_rows(d)
+    wb = ops.workspace_bytes(d, ops.MOE_OP_LAYER_BWD)
+    wm = ops.workspace_bytes(d, ops.MOE_OP_LAYER_BWD_MX)
+    H, I = 7168, 2048
+    ldt = (cap + 511) // 512 * 512
+    # the bf16 backward's buffers, the row-quantized dO_d and dHU, the four
+    # transposed column-quantized operands; codes plus a scale byte per 32
+    assert wm - wb >= (cap * (H + 2 * I) + ldt * (2 * H + 3 * I)) * 33 // 32
+    assert wm - wb <= (cap * (H + 2 * I) + ldt * (2 * H + 3 * I)) * 33 // 32 + 12 * 256
+    bwd = p[:18]  # 17 operands and the workspace
+    assert lib.moe_layer_bwd_mx(ctypes.byref(d), *bwd, wm - 1, None) == ops.MOE_ENOSPC
+    for i in range(18):
+        assert lib.moe_layer_bwd_mx(ctypes.byref(d), *bwd[:i], None, *bwd[i + 1:], wm, None) == ops.MOE_EINVAL, i
+    assert lib.moe_layer_bwd_mx(ctypes.byref(d), _fake(0x10008), *bwd[1:], wm, None) == ops.MOE_EINVAL
+    d2 = ops.make_desc(8, 7168, 8, 384, 48, H=7168, I=2048, num_batches=2)
+    assert lib.moe_layer_bwd_mx(ctypes.byref(d2), *bwd, wm, None) == ops.MOE_EINVAL
 
 
 def test_ring_sizes_and_arguments_rejected_before_launch():

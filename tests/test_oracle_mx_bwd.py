@@ -3,10 +3,11 @@ TFLOPs" section 3 and the Mixture-of-Kittens notes section 6 report; reading:
 every backward product on MX operands blocked along its own reduction
 dimension, the elementwise steps those of the bf16 backward).
 
-The oracle computes per token and per weight-gradient element with C loops.
-Here the same backward is composed in matrix form with numpy products on
-dequantized operands, column quantization done by transposing (pins that a
-transposed operand, a wrong block axis or a dropped term shows up); the
+The oracle computes the backward twice: per token and per weight-gradient
+element with C loops, and in matrix form with numpy products on dequantized
+operands per expert segment, column quantization done by transposing.  The
+two must agree to 1e-12 (pins that a transposed operand, a wrong block axis
+or a dropped term shows up in either); the
 result must lie within the format's error of the bf16 backward oracle (pinned
 by autograd and finite differences); scaling dOut by a power of two scales
 every gradient by exactly that power (the block scales absorb it); zero dOut
@@ -20,12 +21,6 @@ import oracle
 from routing_schedule_expert_amd import inputs
 
 
-def bf16_via_f32(x):
-    """Round to float, then to bf16 (torch's conversion, ties to even)."""
-    t = torch.from_numpy(np.asarray(x, np.float64)).to(torch.float32).to(torch.bfloat16)
-    return t.to(torch.float64).numpy()
-
-
 def bf16_values(bits):
     return inputs.bf16_to_f32(bits).astype(np.float64)
 
@@ -34,68 +29,17 @@ def deq(qs):
     return oracle.mx_dequantize(*qs)
 
 
-def colq(M):
-    """Dequantized MX quantization of M [rows][C] along the rows."""
-    if M.shape[0] == 0:
-        return M
-    return deq(oracle.mx_quantize_f64(np.ascontiguousarray(M.T))).T
-
-
 def matrix_form(h, L, base=0):
-    """The MX backward composed from whole-segment matrix products."""
-    routes, w, X, W13, W2, dOut = (h[k] for k in ("routes", "w", "X", "W13", "W2", "dOut"))
-    P, Np, K = routes.shape
-    H = X.shape[-1]
-    I = W13.shape[1] // 2
-    s = oracle.schedule(routes, L, base)
-    Xdeq = deq(oracle.mx_quantize(X)).reshape(-1, H)
-    W13deq = deq(oracle.mx_quantize(W13))
-    wt = oracle.mx_weights_t(W13, W2)
-    W2t = deq((wt["W2tq"], wt["W2ts"]))      # [L][I][H]
-    W13t = deq((wt["W13tq"], wt["W13ts"]))   # [L][H][2I]
-    dOq = deq(oracle.mx_quantize(dOut)).reshape(-1, H)
-    dO = bf16_values(dOut).reshape(-1, H)
-    Xv = bf16_values(X).reshape(-1, H)
-    real = s.phi[:, 0] >= 0
-    g = np.where(real, s.phi[:, 0].astype(np.int64) * Np + s.phi[:, 1], 0)
-    rr = s.route_row.reshape(-1, K)
-    wrow = np.zeros(s.npad)
-    slot_of = np.full((s.npad, 2), -1, np.int64)
-    for t in range(P * Np):
-        for j in range(K):
-            if rr[t, j] >= 0:
-                wrow[rr[t, j]] = w.reshape(-1, K)[t, j]
-                slot_of[rr[t, j]] = (t, j)
-    dX = np.zeros((P * Np, H))
-    dw = np.zeros((P * Np, K))
+    """The oracle's matrix form (numpy products per expert segment), its
+    weight gradients assembled into [L][...] arrays."""
+    r = oracle.mx_layer_bwd(h["routes"], h["w"], h["X"], h["W13"], h["W2"], h["dOut"], L, base)
+    H = h["X"].shape[-1]
+    I = h["W13"].shape[1] // 2
     dW13 = np.zeros((L, 2 * I, H))
     dW2 = np.zeros((L, H, I))
-    for l in range(L):
-        r0, r1 = int(s.seg_off[l]), int(s.seg_off[l + 1])
-        if r1 == r0:
-            continue
-        rows = np.arange(r0, r1)
-        re = real[rows][:, None]
-        gg = g[rows]
-        HU = np.where(re, Xdeq[gg], 0.0) @ W13deq[l].T
-        hh, uu = HU[:, :I], HU[:, I:]
-        a = deq(oracle.mx_quantize_f64(hh / (1 + np.exp(-hh)) * uu))
-        hb, ub = bf16_via_f32(hh), bf16_via_f32(uu)
-        dAp = np.where(re, dOq[gg], 0.0) @ W2t[l].T
-        dA = wrow[rows, None] * dAp
-        sg = 1.0 / (1.0 + np.exp(-hb))
-        dHU = np.concatenate([bf16_via_f32(dA * ub * sg * (1 + hb * (1 - sg))), bf16_via_f32(dA * hb * sg)], 1)
-        dXd = deq(oracle.mx_quantize_f64(dHU)) @ W13t[l].T
-        dwr = (dAp * a).sum(1)
-        for k, r in enumerate(rows):
-            t, j = slot_of[r]
-            if t >= 0:
-                dX[t] += dXd[k]
-                dw[t, j] = dwr[k]
-        dOw = np.where(re, bf16_via_f32(wrow[rows, None] * dO[gg]), 0.0)
-        dW2[l] = colq(dOw).T @ colq(a)
-        dW13[l] = colq(dHU).T @ colq(np.where(re, Xv[gg], 0.0))
-    return {"dX": dX, "dw": dw, "dW13": dW13, "dW2": dW2}
+    for l, sg in r["seg"].items():
+        dW13[l], dW2[l] = sg["dW13"], sg["dW2"]
+    return {"dX": r["dX"], "dw": r["dw"], "dW13": dW13, "dW2": dW2}
 
 
 def oracle_full(h, L, base=0):
@@ -138,6 +82,16 @@ CASES = {
     "ragged_base": lambda: case(2, Np=37, E=12, K=3, L=5, base=3, H=96, I=32),
     "hot_empty": lambda: case(3, Np=150, E=16, K=2, L=6, H=64, I=96, hot_empty=True),
 }
+
+
+def test_bf16_rounding_helper_matches_torch():
+    """The matrix form's float-then-bf16 rounding against torch's conversion,
+    on random values and on exact bf16 midpoints (ties to even)."""
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        (np.arange(1, 2000) * 2 + 1) * 2.0 ** -9 + 1.0])  # odd multiples of half a bf16 ulp near 1..9
+    ref = torch.from_numpy(x).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle._bf16_via_f32(x), ref)
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
