@@ -517,6 +517,95 @@ def bench_layer_mx(args, torch, ops, inputs, dev):
             "mx_down": {"achieved": dn, "frac": dn / PEAK_FP8_TFLOPS, "avg_launch_ms": st["mx_down"]}}
 
 
+def timed_steps(args, torch, ops, step, ntrace=64):
+    """ms per call of step() over args.steps calls after args.warmup, and the
+    mean launch time of every traced kernel."""
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ops.moe_trace_enable(args.steps * ntrace)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    per = {}
+    for name, t in ops.moe_trace_read(args.steps * ntrace):
+        per.setdefault(name, []).append(t)
+    ops.moe_trace_enable(0)
+    return ms, {k: float(np.mean(v)) for k, v in per.items()}
+
+
+def bench_fwd_bwd_mx(args, torch, ops, inputs, dev):
+    """Kimi-shaped forward + backward with MXFP8 routed experts
+    (moe_layer_fwd_mx saving h and u, then moe_layer_bwd_mx), beside the bf16
+    forward + backward on the same inputs in the same process.  Weights are
+    quantized before the timed region, both row-wise (forward) and column-wise
+    (backward), as a training step would after each weight update."""
+    c = KIMI
+    routing = args.bwd_routing
+    h = inputs.make_layer_inputs_device(6, c["P"], c["Np"], c["E"], c["K"], c["L"], c["H"], c["I"], dev,
+                                        routing=routing, x_std=1.0, s=1.5, with_grad=True)
+    d = ops.make_desc(c["P"], c["Np"], c["K"], c["E"], c["L"], H=c["H"], I=c["I"])
+    routes = torch.from_numpy(h["routes"]).to(dev)
+    w = torch.from_numpy(h["w"]).to(dev)
+    L, H, I = c["L"], c["H"], c["I"]
+    local = int(((h["routes"] >= 0) & (h["routes"] < L)).sum())
+    W13q, W13s = ops.quantize_mx(h["W13"])
+    W2q, W2s = ops.quantize_mx(h["W2"])
+    W13t, W2t = ops.quantize_mx_t(h["W13"]), ops.quantize_mx_t(h["W2"])
+    fm = ops.alloc_fwd_mx(d, dev, save_hu=True)
+    gm = ops.alloc_bwd_mx(d, dev)
+
+    def fwd_mx():
+        ops.layer_fwd_mx(d, routes, w, h["X"], W13q, W13s, W2q, W2s, fm)
+
+    def bwd_mx():
+        ops.layer_bwd_mx(d, h["dOut"], w, h["X"], fm, W13t, W2t, gm)
+
+    ms_fm, st_fm = timed_steps(args, torch, ops, fwd_mx)
+    ms_bm, st_bm = timed_steps(args, torch, ops, bwd_mx)
+    del fm, gm
+    torch.cuda.empty_cache()
+    b = ops.alloc_fwd(d, dev, save_hu=True)
+    dX = torch.empty_like(h["X"])
+    dW13 = torch.empty((L, 2 * I, H), dtype=torch.float32, device=dev)
+    dW2 = torch.empty((L, H, I), dtype=torch.float32, device=dev)
+    dw = torch.empty((c["P"], c["Np"], c["K"]), dtype=torch.float32, device=dev)
+    ws = torch.empty(ops.workspace_bytes(d, ops.MOE_OP_LAYER_BWD), dtype=torch.uint8, device=dev)
+
+    def fwd_bf16():
+        ops.layer_fwd(d, routes, w, h["X"], h["W13"], h["W2"], b)
+
+    def bwd_bf16():
+        ops.moe_layer_bwd(d, h["dOut"], routes, w, b.phi, b.route_row, b.seg_off, b.Xd, b.HU, b.A, h["W13"],
+                          h["W2"], dX, dW13, dW2, dw, ws)
+
+    ms_fb, _ = timed_steps(args, torch, ops, fwd_bf16)
+    ms_bb, st_bb = timed_steps(args, torch, ops, bwd_bf16)
+    hi = H * I
+    ms = ms_fm + ms_bm
+    fl = 18.0 * hi * local
+    tf = lambda flop, key, st: flop / (st[key] / 1e3) / 1e12 if key in st else None
+    return {"metric": f"MoE layer fwd+bwd TFLOP/s, MXFP8 routed experts (Kimi shape, "
+                      f"{'adversarial' if routing == 'hot' else routing} routing, 1 GPU)",
+            "value": fl / (ms / 1e3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "mxfp8-e4m3 (fp32 accumulate), bf16 in/out", "data": "synthetic",
+            "config": {"workload": "kimi_local_share_fwd_bwd_mxfp8",
+                       "routing": "zipf1.5+4hot" if routing == "hot" else routing, "local_routes": local,
+                       "weights": "quantized row- and column-wise once, outside the step"},
+            "ms": {"fwd_mx": ms_fm, "bwd_mx": ms_bm, "fwd_bf16": ms_fb, "bwd_bf16": ms_bb},
+            "speedup_vs_bf16": {"fwd": ms_fb / ms_fm, "bwd": ms_bb / ms_bm, "fwd_bwd": (ms_fb + ms_bb) / ms},
+            "stage_ms_fwd_mx": st_fm, "stage_ms_bwd_mx": st_bm, "stage_ms_bwd_bf16": st_bb,
+            "kernel_tflops": {k: v for k, v in {
+                "mx_bwd_down": tf(2.0 * hi * local, "mx_bwd_down", st_bm),
+                "mx_bwd_gateup": tf(4.0 * hi * local, "mx_bwd_gateup", st_bm),
+                "mx_bwd_wgrad_rdispatch": tf(6.0 * hi * local, "mx_bwd_wgrad_rdispatch", st_bm)}.items()}}
+
+
 def bench_tc_sweep(args, torch, ops, inputs, dev):
     """Mid configuration (8 x 4096 tokens, 64 experts with 8 local, top-6, H=2048,
     I=1024): layer forward vs the minibatch of dispatched rows Tc (persistent
@@ -687,11 +776,11 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the layer steps, run one plain read+write kernel over this many MiB (counter scaling)")
     ap.add_argument("--workload", default="kimi",
-                    choices=["kimi", "kimi_bwd", "mid_tc", "schedule", "kimi_mx", "kimi_ring", "kimi_shared",
-                             "vendor_gemm"],
-                    help="kimi: the contract line (default); kimi_bwd / mid_tc / schedule / kimi_mx / kimi_ring / "
-                         "kimi_shared: extra measurements; vendor_gemm: the vendor BLAS on the grouped GEMMs' "
-                         "shapes, for context")
+                    choices=["kimi", "kimi_bwd", "mid_tc", "schedule", "kimi_mx", "kimi_mx_bwd", "kimi_ring",
+                             "kimi_shared", "vendor_gemm"],
+                    help="kimi: the contract line (default); kimi_bwd / mid_tc / schedule / kimi_mx / kimi_mx_bwd / "
+                         "kimi_ring / kimi_shared: extra measurements; vendor_gemm: the vendor BLAS on the grouped "
+                         "GEMMs' shapes, for context")
     ap.add_argument("--shared-is", type=int, default=2048, help="--workload kimi_shared: shared intermediate size")
     ap.add_argument("--ring", default="3584:1:1,3584:2:1,3584:2:2,1024:2:1,1024:2:7,1024:7:7",
                     help="--workload kimi_ring: comma list of tokens-per-partition-per-macrobatch:slots[:wgrad group]")
@@ -715,6 +804,9 @@ def main():
         return
     if args.workload == "mid_tc":
         print(json.dumps(bench_tc_sweep(args, torch, ops, inputs, dev)), flush=True)
+        return
+    if args.workload == "kimi_mx_bwd":
+        print(json.dumps(bench_fwd_bwd_mx(args, torch, ops, inputs, dev)), flush=True)
         return
     if args.workload == "kimi_mx":
         print(json.dumps(bench_layer_mx(args, torch, ops, inputs, dev)), flush=True)
