@@ -135,23 +135,24 @@ int64_t moe_workspace_bytes(const moe_desc *d, int op);
 enum {
     MOE_WS_INVALID_IDS = 0,
     MOE_WS_BARRIER_STATUS = 1,
-    /* inspection of moe_layer_bwd_mx (op MOE_OP_LAYER_BWD_MX), with
-     * ldt = moe_capacity_rows rounded up to a multiple of 512 and only the rows
-     * below seg_off[L] (the columns below it for the [C][ldt] buffers) written
-     * by the last call: */
+    /* inspection of moe_layer_bwd_mx (op MOE_OP_LAYER_BWD_MX); only the rows
+     * below seg_off[L] are written by a call.  The column-code buffers are
+     * segment-major: local expert l (rows [S, S + n), S = seg_off[l],
+     * n = seg_off[l+1] - S) owns a [C][n] block of codes at byte C * S and a
+     * [C][n/32] block of scale bytes at byte C * S / 32. */
     MOE_WS_MX_DHU = 2,     /* bf16 [cap][2I]: dHU (gate then up columns)       */
     MOE_WS_MX_DO_Q = 3,    /* [cap][H]:   dO_d row codes (along H)             */
     MOE_WS_MX_DO_S = 4,    /* [cap][H/32]                                      */
     MOE_WS_MX_DHU_Q = 5,   /* [cap][2I]:  dHU row codes (along 2I)             */
     MOE_WS_MX_DHU_S = 6,   /* [cap][2I/32]                                     */
-    MOE_WS_MX_DOWT_Q = 7,  /* [H][ldt]:   (dO_d w) column codes (along rows)   */
-    MOE_WS_MX_DOWT_S = 8,  /* [H][ldt/32]                                      */
-    MOE_WS_MX_AT_Q = 9,    /* [I][ldt]:   a column codes                       */
-    MOE_WS_MX_AT_S = 10,   /* [I][ldt/32]                                      */
-    MOE_WS_MX_XDT_Q = 11,  /* [H][ldt]:   Xd column codes                      */
-    MOE_WS_MX_XDT_S = 12,  /* [H][ldt/32]                                      */
-    MOE_WS_MX_DHUT_Q = 13, /* [2I][ldt]:  dHU column codes                     */
-    MOE_WS_MX_DHUT_S = 14, /* [2I][ldt/32]                                     */
+    MOE_WS_MX_DOWT_Q = 7,  /* C = H:  (dO_d w) column codes (along the rows)   */
+    MOE_WS_MX_DOWT_S = 8,  /*         their scale bytes                        */
+    MOE_WS_MX_AT_Q = 9,    /* C = I:  a column codes                           */
+    MOE_WS_MX_AT_S = 10,   /*                                                  */
+    MOE_WS_MX_XDT_Q = 11,  /* C = H:  Xd column codes                          */
+    MOE_WS_MX_XDT_S = 12,  /*                                                  */
+    MOE_WS_MX_DHUT_Q = 13, /* C = 2I: dHU column codes                         */
+    MOE_WS_MX_DHUT_S = 14, /*                                                  */
 };
 int64_t moe_workspace_field(const moe_desc *d, int op, int field);
 
@@ -393,9 +394,11 @@ int moe_quantize_mx_t(const uint16_t *src, int64_t batch, int32_t R, int32_t C, 
  *                 of W13 with R = 2I, C = H)
  *   W2tq, W2ts    MX codes [L][I][H] and scales [L][I][H/32] (R = H, C = I)
  *   dX, dW13, dW2, dw   out, as in moe_layer_bwd
- *   ws >= moe_workspace_bytes(d, MOE_OP_LAYER_BWD_MX): moe_layer_bwd's buffers,
- *   then the row-quantized dO_d and dHU and the four row-blocked operands of
- *   the weight gradients, stored transposed.
+ *   ws >= moe_workspace_bytes(d, MOE_OP_LAYER_BWD_MX): dXd and dHU (bf16), the
+ *   row weights and dw partials, the row codes of dO_d and dHU, and the four
+ *   row-blocked operands of the weight gradients stored transposed per expert
+ *   segment (the MOE_WS_MX_* fields).  dO_d itself is never written: one pass
+ *   pulls the rows of dOut through phi and writes both of its encodings.
  * Pointers: dOut, X, phi, HU, Aq, W13tq, W2tq, dX, ws 16-byte aligned; the
  * others 4-byte aligned.  d->num_batches == 1.  Every reduction has a fixed
  * order, so repeated calls give bitwise the same outputs.

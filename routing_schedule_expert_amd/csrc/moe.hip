@@ -152,11 +152,6 @@ __global__ __launch_bounds__(kFwdThreads) void k_mx_down(MxFfnArgs a) {
     mx_down_phase<SG>(a, lds);
 }
 
-__global__ __launch_bounds__(256) void k_mx_quantize_rows(const uint16_t *src, const int32_t *nrows, int K, uint8_t *q,
-                                                         uint8_t *s) {
-    mx_quantize_rows_body(src, nrows, K, q, s);
-}
-
 __global__ __launch_bounds__(kColqThreads) void k_mx_colq(ColQArgs a) {
     __shared__ __attribute__((aligned(16))) float st[kColqLds / 4];
     mx_colq_body(a, st);
@@ -326,21 +321,26 @@ int64_t bwd_ws_bytes(const moe_desc *d) {
 
 // MX backward workspace, after the bf16 backward's buffers: the row-quantized
 // dO_d and dHU, and the four column-quantized operands of the weight
-// gradients stored transposed with mx_ldt codes per row.
-int64_t mx_ldt(const moe_desc *d) { return (cap_rows(d) + 511) / 512 * 512; }
+// gradients, transposed per expert segment (C codes per dispatched row).
 
 // The MX buffers in carving order (the workspace fields MOE_WS_MX_*_Q / _S
 // name them in this order from MOE_WS_MX_DHU_Q on).
 enum MxBuf { kDOq, kDOs, kDHUq, kDHUs, kDOwTq, kDOwTs, kATq, kATs, kXdTq, kXdTs, kDHUTq, kDHUTs, kMxBufs };
 static_assert(MOE_WS_MX_DHUT_S - MOE_WS_MX_DO_Q + 1 == kMxBufs, "one workspace field per MX buffer");
 
-// Byte offsets of the MX buffers after the bf16 backward's; returns the total.
+// The MX backward's bf16 / fp32 buffers: dXd [cap][H], dHU [cap][2I] (bf16),
+// the row weights and the dw partials (fp32), at these offsets.
+int64_t mx_dhu_offset(const moe_desc *d) { return align256(cap_rows(d) * d->H * 2); }
+int64_t mx_wrow_offset(const moe_desc *d) { return mx_dhu_offset(d) + align256(cap_rows(d) * 2 * d->I * 2); }
+int64_t mx_part_offset(const moe_desc *d) { return mx_wrow_offset(d) + align256(cap_rows(d) * 4); }
+
+// Byte offsets of the MX code buffers after those; returns the total.
 int64_t mx_bwd_offsets(const moe_desc *d, int64_t (&off)[kMxBufs]) {
-    const int64_t cap = cap_rows(d), H = d->H, I = d->I, ldt = mx_ldt(d);
-    const int64_t bytes[kMxBufs] = {cap * H,     cap * H / 32,     cap * 2 * I,     cap * 2 * I / 32,
-                                    H * ldt,     H * ldt / 32,     I * ldt,         I * ldt / 32,
-                                    H * ldt,     H * ldt / 32,     2 * I * ldt,     2 * I * ldt / 32};
-    int64_t o = bwd_ws_bytes(d);
+    const int64_t cap = cap_rows(d), H = d->H, I = d->I;
+    const int64_t bytes[kMxBufs] = {cap * H, cap * H / 32, cap * 2 * I, cap * 2 * I / 32,
+                                    cap * H, cap * H / 32, cap * I,     cap * I / 32,
+                                    cap * H, cap * H / 32, cap * 2 * I, cap * 2 * I / 32};
+    int64_t o = mx_part_offset(d) + align256(cap * 4ll * bwd_nparts(d));
     for (int i = 0; i < kMxBufs; ++i) {
         off[i] = o;
         o += align256(bytes[i]);
@@ -632,7 +632,7 @@ int64_t moe_workspace_field(const moe_desc *d, int op, int field) {
     }
     if (op == MOE_OP_LAYER_BWD_MX) {
         // the bf16 backward's dHU follows dO_d, dXd and dO_d w
-        if (field == MOE_WS_MX_DHU) return 3 * align256(cap_rows(d) * d->H * 2);
+        if (field == MOE_WS_MX_DHU) return mx_dhu_offset(d);
         int64_t off[kMxBufs];
         mx_bwd_offsets(d, off);
         if (field >= MOE_WS_MX_DO_Q && field < MOE_WS_MX_DO_Q + kMxBufs) return off[field - MOE_WS_MX_DO_Q];
@@ -799,6 +799,17 @@ BwdBufs carve_bwd(char *p, const moe_desc *d) {
     return b;
 }
 
+// The router weight of every dispatched row of one table.
+int launch_row_weight(const moe_desc *d, int64_t tstride, const float *w, const moe_src *phi,
+                      const int32_t *route_row, const int32_t *seg_off, float *wrow, hipStream_t s) {
+    const int64_t cap = cap_rows(d);
+    const int np_stride = tstride > d->Np ? (int)tstride : d->Np;
+    TraceScope tr("bwd_row_weight", s);
+    hipLaunchKernelGGL(k_row_weight, dim3((int)std::min<int64_t>((cap + 255) / 256, 4096)), dim3(256), 0, s, phi,
+                       seg_off + d->L, route_row, w, wrow, np_stride, d->K, cap);
+    return launch_status();
+}
+
 // The row weights and B1 of one table: the reverse-combine gather of the
 // output gradient (dO_d) and its rows times w (dO_d w).
 int bwd_gather(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const float *w, const moe_src *phi,
@@ -807,12 +818,7 @@ int bwd_gather(const moe_desc *d, int64_t tstride, const uint16_t *dOut, const f
     const bool window = tstride > d->Np;
     const int32_t *npad = seg_off + d->L;
     const int np_stride = window ? (int)tstride : d->Np;
-    {
-        TraceScope tr("bwd_row_weight", s);
-        hipLaunchKernelGGL(k_row_weight, dim3((int)std::min<int64_t>((cap + 255) / 256, 4096)), dim3(256), 0, s, phi,
-                           npad, route_row, w, bb.wrow, np_stride, d->K, cap);
-    }
-    if (launch_status() != MOE_OK) return MOE_EHIP;
+    if (launch_row_weight(d, tstride, w, phi, route_row, seg_off, bb.wrow, s) != MOE_OK) return MOE_EHIP;
     const int grid = (int)std::min<int64_t>((cap + 3) / 4, 16ll * device_cus());
     TraceScope tr("bwd_gather", s);
     hipLaunchKernelGGL(k_gather_scaled, dim3(grid), dim3(256), 0, s, dOut, phi, npad, bb.wrow, bb.dOd, bb.dOw,
@@ -1086,11 +1092,11 @@ int64_t colq_tiles(int64_t rows, int64_t cols, int64_t batch) {
 }
 
 // Column quantization of the dispatched rows [rows < *npad][C] of a table,
-// into [C][ldt] codes: from bf16 rows (src, ld; gathered through phi when
-// given) or from MX codes (q, s [cap][C]).
+// segment-major: from bf16 rows (src, ld; gathered through phi when given)
+// or from MX codes (q, s [cap][C]).
 ColQArgs colq_rows(const uint16_t *src, int64_t ld, const moe_src *phi, int32_t Np, const uint8_t *srcq,
-                   const uint8_t *srcs, const int32_t *npad, int64_t cap, int C, uint8_t *q, uint8_t *sc,
-                   int64_t ldt) {
+                   const uint8_t *srcs, const int32_t *seg_off, int L, int64_t cap, int C, uint8_t *q,
+                   uint8_t *sc) {
     ColQArgs a{};
     a.src = src;
     a.ld = ld;
@@ -1099,23 +1105,17 @@ ColQArgs colq_rows(const uint16_t *src, int64_t ld, const moe_src *phi, int32_t 
     a.Np = Np;
     a.srcq = srcq;
     a.srcs = srcs;
-    a.nrows = npad;
+    a.nrows = seg_off + L;
+    a.seg_off = seg_off;
+    a.L = L;
     a.R = cap;
     a.C = C;
     a.batch = 1;
     a.q = q;
     a.s = sc;
-    a.ldq = ldt;
+    a.ldq = 0;
     a.out_bstride = 0;
     return a;
-}
-
-int launch_quantize_rows(const uint16_t *src, const int32_t *npad, int64_t cap, int K, uint8_t *q, uint8_t *sc,
-                         hipStream_t s, const char *name) {
-    const int grid = (int)std::min<int64_t>((cap * (K / 32) + 255) / 256, 16ll * device_cus());
-    TraceScope tr(name, s);
-    hipLaunchKernelGGL(k_mx_quantize_rows, dim3(grid), dim3(256), 0, s, src, npad, K, q, sc);
-    return launch_status();
 }
 
 }  // namespace
@@ -1158,15 +1158,26 @@ int moe_layer_bwd_mx(const moe_desc *d, const uint16_t *dOut, const float *w, co
         if (!p || !aligned4(p)) return MOE_EINVAL;
     if ((int64_t)ws_bytes < mx_bwd_ws_bytes(d)) return MOE_ENOSPC;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int64_t cap = cap_rows(d), ldt = mx_ldt(d);
+    const int64_t cap = cap_rows(d);
     const int H = d->H, I = d->I;
-    const BwdBufs bb = carve_bwd(static_cast<char *>(ws), d);
-    const MxBwdBufs mx = carve_mx_bwd(static_cast<char *>(ws), d);
+    char *wsb = static_cast<char *>(ws);
+    BwdBufs bb{};
+    bb.dXd = reinterpret_cast<uint16_t *>(wsb);
+    bb.dHU = reinterpret_cast<uint16_t *>(wsb + mx_dhu_offset(d));
+    bb.wrow = reinterpret_cast<float *>(wsb + mx_wrow_offset(d));
+    bb.part = reinterpret_cast<float *>(wsb + mx_part_offset(d));
+    const MxBwdBufs mx = carve_mx_bwd(wsb, d);
     uint8_t *const *mb = mx.b;
-    const int32_t *npad = seg_off + d->L;
-    rc = bwd_gather(d, 0, dOut, w, phi, route_row, seg_off, bb, s);
+    rc = launch_row_weight(d, 0, w, phi, route_row, seg_off, bb.wrow, s);
     if (rc != MOE_OK) return rc;
-    rc = launch_quantize_rows(bb.dOd, npad, cap, H, mb[kDOq], mb[kDOs], s, "mx_bwd_quantize_dO");
+    // B1 fused with both encodings of dO_d: the rows of dOut pulled through
+    // phi, their row codes for the down dgrad and the column codes of
+    // bf16(dO_d w) for dW2, in one read
+    ColQArgs qo = colq_rows(dOut, H, phi, d->Np, nullptr, nullptr, seg_off, d->L, cap, H, mb[kDOwTq], mb[kDOwTs]);
+    qo.wrow = bb.wrow;
+    qo.rq = mb[kDOq];
+    qo.rs = mb[kDOs];
+    rc = launch_colq(qo, colq_tiles(cap, H, 1), s, "mx_bwd_gather_quantize_dO");
     if (rc != MOE_OK) return rc;
     MxBwdArgs a;
     a.dOq = mb[kDOq];
@@ -1206,7 +1217,12 @@ int moe_layer_bwd_mx(const moe_desc *d, const uint16_t *dOut, const float *w, co
                            route_row, bb.part, a.nparts, dw, nslots, 0, (int64_t)0);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
-    rc = launch_quantize_rows(bb.dHU, npad, cap, 2 * I, mb[kDHUq], mb[kDHUs], s, "mx_bwd_quantize_dHU");
+    // dHU: row codes for the gate/up dgrad and column codes for dW13, one read
+    ColQArgs qh = colq_rows(bb.dHU, 2 * I, nullptr, 0, nullptr, nullptr, seg_off, d->L, cap, 2 * I, mb[kDHUTq],
+                            mb[kDHUTs]);
+    qh.rq = mb[kDHUq];
+    qh.rs = mb[kDHUs];
+    rc = launch_colq(qh, colq_tiles(cap, 2 * I, 1), s, "mx_bwd_quantize_dHU");
     if (rc != MOE_OK) return rc;
     {
         TraceScope tr("mx_bwd_gateup", s);
@@ -1216,17 +1232,13 @@ int moe_layer_bwd_mx(const moe_desc *d, const uint16_t *dOut, const float *w, co
             hipLaunchKernelGGL(k_mx_bwd_gateup<1>, dim3(grid), dim3(kFwdThreads), 0, s, a);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
-    // the weight gradients' operands, quantized along the rows
-    const ColQArgs jobs[4] = {
-        colq_rows(bb.dOw, H, nullptr, 0, nullptr, nullptr, npad, cap, H, mb[kDOwTq], mb[kDOwTs], ldt),
-        colq_rows(nullptr, 0, nullptr, 0, Aq, As, npad, cap, I, mb[kATq], mb[kATs], ldt),
-        colq_rows(X, H, phi, d->Np, nullptr, nullptr, npad, cap, H, mb[kXdTq], mb[kXdTs], ldt),
-        colq_rows(bb.dHU, 2 * I, nullptr, 0, nullptr, nullptr, npad, cap, 2 * I, mb[kDHUTq], mb[kDHUTs], ldt)};
-    const char *names[4] = {"mx_bwd_colq_dOw", "mx_bwd_colq_a", "mx_bwd_colq_Xd", "mx_bwd_colq_dHU"};
-    for (int j = 0; j < 4; ++j) {
-        rc = launch_colq(jobs[j], colq_tiles(cap, jobs[j].C, 1), s, names[j]);
-        if (rc != MOE_OK) return rc;
-    }
+    // the other two weight-gradient operands, quantized along the rows
+    rc = launch_colq(colq_rows(nullptr, 0, nullptr, 0, Aq, As, seg_off, d->L, cap, I, mb[kATq], mb[kATs]),
+                     colq_tiles(cap, I, 1), s, "mx_bwd_colq_a");
+    if (rc != MOE_OK) return rc;
+    rc = launch_colq(colq_rows(X, H, phi, d->Np, nullptr, nullptr, seg_off, d->L, cap, H, mb[kXdTq], mb[kXdTs]),
+                     colq_tiles(cap, H, 1), s, "mx_bwd_colq_Xd");
+    if (rc != MOE_OK) return rc;
     MxWgradArgs wa;
     wa.dOwTq = mb[kDOwTq];
     wa.dOwTs = mb[kDOwTs];
@@ -1236,7 +1248,6 @@ int moe_layer_bwd_mx(const moe_desc *d, const uint16_t *dOut, const float *w, co
     wa.dHUTs = mb[kDHUTs];
     wa.XdTq = mb[kXdTq];
     wa.XdTs = mb[kXdTs];
-    wa.ld_t = ldt;
     wa.seg_off = seg_off;
     wa.dW13 = dW13;
     wa.dW2 = dW2;

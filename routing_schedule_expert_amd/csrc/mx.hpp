@@ -29,21 +29,16 @@ namespace moe {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// E4M3 code of a finite float, nearest with ties to even, saturating at 448
-// (branch-free: every case is computed and selected).
-__device__ __forceinline__ uint32_t e4m3_encode(float y) {
-    const uint32_t s = __float_as_uint(y) >> 31;
-    const float a = fabsf(y);
-    // one quantum: 2^(E-3) for a normal value (E = floor(log2 a) >= -6), 2^-9 below
-    const int E = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;
-    const int qexp = a < 0.015625f ? -9 : E - 3;
-    const float q = __builtin_rintf(__builtin_amdgcn_ldexpf(a, -qexp));  // exact scaling, round to even
-    const float mag = __builtin_amdgcn_ldexpf(q, qexp);
-    const uint32_t b = __float_as_uint(mag);
-    const uint32_t normal = ((((b >> 23) & 0xff) - 127 + 7) << 3) | ((b >> 20) & 7u);
-    uint32_t code = mag < 0.015625f ? (uint32_t)q : normal;  // subnormal: m = q in 0..7
-    code = (a >= 448.0f || mag >= 448.0f) ? 0x7Eu : code;
-    return (s << 7) | code;
+// E4M3 codes of four finite floats, packed in order into one word: nearest
+// with ties to even, saturating at +-448.  gfx950 converts to the OCP E4M3
+// format in hardware (round to nearest even, with subnormals); a value past
+// 448 is clamped to 448 first, which is where saturating rounding takes it.
+__device__ __forceinline__ float e4m3_clamp(float y) { return fminf(fmaxf(y, -448.0f), 448.0f); }
+
+__device__ __forceinline__ uint32_t e4m3_encode4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), w, true);
+    return (uint32_t)w;
 }
 
 // Block exponent: floor(log2 amax) - 8 clamped to [-127, 127]; -127 for 0.
@@ -63,12 +58,9 @@ __device__ __forceinline__ uint32_t mx_quantize32(const float (&v)[32], uint32_t
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
     const int se = mx_block_exp(amax);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        uint32_t x = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x |= e4m3_encode(__builtin_amdgcn_ldexpf(v[4 * k + j], -se)) << (8 * j);
-        w[k] = x;
-    }
+    for (int k = 0; k < 8; ++k)
+        w[k] = e4m3_encode4(__builtin_amdgcn_ldexpf(v[4 * k], -se), __builtin_amdgcn_ldexpf(v[4 * k + 1], -se),
+                            __builtin_amdgcn_ldexpf(v[4 * k + 2], -se), __builtin_amdgcn_ldexpf(v[4 * k + 3], -se));
     return (uint32_t)(se + 127);
 }
 

@@ -13,8 +13,9 @@
 //   dW2[l]  = (w dO_d)^T a              over the expert's rows;
 //   dW13[l] = dHU^T Xd                  over the expert's rows:
 // the four row-dimension operands are quantized along the rows in blocks of
-// 32 dispatched rows and stored transposed ([C][ld_t]), so every MX product
-// reads both operands K-contiguous through the forward's scaled-MFMA loop.
+// 32 dispatched rows and stored transposed per expert segment ([C][rows of
+// the segment]), so every MX product reads both operands K-contiguous through
+// the forward's scaled-MFMA loop.
 // The SwiGLU backward and dw stay those of the bf16 path, with a read from
 // the forward's MX codes (exactly: an E4M3 value times a power of two is an
 // fp32 number).
@@ -59,21 +60,21 @@ struct ARowsMx {
 // Quantization passes.
 // ---------------------------------------------------------------------------
 
-// Row quantization of bf16 [rows][K] for the rows below *nrows (the
-// dispatched rows of a table): one 32-element block per thread.
-__device__ __forceinline__ void mx_quantize_rows_body(const uint16_t *src, const int32_t *nrows, int K, uint8_t *q,
-                                                      uint8_t *s) {
-    const int64_t nblocks = (int64_t)(*nrows) * (K / 32);
-    for (int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; b < nblocks; b += (int64_t)gridDim.x * blockDim.x)
-        mx_quantize_block_bf16(src, K, q, s, b);
-}
-
-// Column quantization: out[c][r] = codes of column c of a [R][C] source in
-// blocks of 32 consecutive rows (scale bytes [c][r / 32]), for batch b at
-// b * out_bstride codes (b * out_bstride / 32 scale bytes).  Sources:
+// Column quantization: the codes of column c of a [R][C] source in blocks
+// of 32 consecutive rows.  Outputs: without seg_off, out[c][r] with ldq codes
+// per c (scale bytes [c][r / 32]), batch b at b * out_bstride codes
+// (b * out_bstride / 32 scale bytes); with seg_off (the dispatched rows of a
+// table), segment-major: local expert l's rows [S, S + n) (S = seg_off[l],
+// n = seg_off[l+1] - S) form a [C][n] block at code C * S, scales [C][n / 32]
+// at byte C * S / 32, so the weight-gradient tiles of one expert read compact
+// rows.  Sources:
 //   bf16 rows src + r * ld (+ b * in_bstride), or, with phi, row r taken from
 //   source row part * Np + tok of phi[r] (padding rows zero);
 //   or MX codes srcq / srcs [R][C] (+ [R][C/32]), decoded exactly.
+// With wrow (bf16 sources), column codes are taken of bf16(value * wrow[r])
+// (an fp32 product rounded once, as the bf16 backward's dO_d w), and with rq
+// the same pass also writes the row codes of the unscaled values ([R][C],
+// scales rs [R][C/32]): one read of the source for both encodings.
 // Rows at or past *nrows (if given, else R) read as zero; only whole blocks
 // below the row count (rounded up to 32) are written.
 struct ColQArgs {
@@ -83,6 +84,10 @@ struct ColQArgs {
     int32_t Np;
     const uint8_t *srcq, *srcs;
     const int32_t *nrows;
+    const int32_t *seg_off;
+    int L;
+    const float *wrow;
+    uint8_t *rq, *rs;
     int64_t R;
     int C, batch;
     uint8_t *q, *s;
@@ -104,47 +109,103 @@ __device__ __forceinline__ void mx_colq_body(const ColQArgs &a, float *st) {
         const int c0 = (int)(in % ct) * kColqCols;
         __syncthreads();  // the previous tile's readers are done with st
         if (a.srcq) {
-            // 128 rows x 64 codes: 16 codes (one half block) per chunk
-            for (int k = t; k < kColqRows * 4; k += kColqThreads) {
-                const int row = k >> 2, cc = (k & 3) * 16;
-                float v[16];
-                const int64_t r = r0 + row;
-                if (r < rows && c0 + cc < a.C) {
-                    const u32x4 c = *reinterpret_cast<const u32x4 *>(a.srcq + r * a.C + c0 + cc);
-                    const uint32_t sb = a.srcs[r * (a.C / 32) + (c0 + cc) / 32];
+            // 128 rows x 64 codes: 16 codes (one half block) per chunk, two
+            // chunks per thread, both loads issued before either is decoded
+            constexpr int N = kColqRows * 4 / kColqThreads;
+            const int cc = (t & 3) * 16;
+            u32x4 x[N];
+            uint32_t sb[N];
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) v[j] = mx_decode((c[j >> 2] >> (8 * (j & 3))) & 0xffu, sb);
-                } else {
+            for (int i = 0; i < N; ++i) {
+                const int64_t r = r0 + (t >> 2) + i * (kColqThreads / 4);
+                const bool ok = r < rows && c0 + cc < a.C;
+                x[i] = ok ? *reinterpret_cast<const u32x4 *>(a.srcq + r * a.C + c0 + cc) : u32x4{0u, 0u, 0u, 0u};
+                sb[i] = ok ? a.srcs[r * (a.C / 32) + (c0 + cc) / 32] : 0u;
+            }
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) v[j] = 0.f;
-                }
+            for (int i = 0; i < N; ++i) {
+                const int row = (t >> 2) + i * (kColqThreads / 4);
 #pragma unroll
-                for (int j = 0; j < 16; ++j) st[(cc + j) * kColqLd + row] = v[j];
+                for (int j = 0; j < 16; ++j)
+                    st[(cc + j) * kColqLd + row] = mx_decode((x[i][j >> 2] >> (8 * (j & 3))) & 0xffu, sb[i]);
             }
         } else {
-            // 128 rows x 64 bf16: 8 values per 16-byte chunk
-            for (int k = t; k < kColqRows * 8; k += kColqThreads) {
-                const int row = k >> 3, cc = (k & 7) * 8;
-                const int64_t r = r0 + row;
-                const uint16_t *p = nullptr;
+            // 128 rows x 64 bf16: 8 values per 16-byte chunk, four chunks per
+            // thread (rows t/8 + 32 i, the same 8 columns); the row sources
+            // (a table lookup when gathered) and then all four loads are
+            // issued before any value is used
+            constexpr int N = kColqRows * 8 / kColqThreads;
+            const int cc = (t & 7) * 8;
+            const uint16_t *p[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int64_t r = r0 + (t >> 3) + i * (kColqThreads / 8);
+                p[i] = nullptr;
                 if (r < rows && c0 + cc < a.C) {
                     if (a.phi) {
                         const int2 e = reinterpret_cast<const int2 *>(a.phi)[r];
-                        if (e.x >= 0) p = a.src + ((int64_t)e.x * a.Np + e.y) * a.ld;
+                        if (e.x >= 0) p[i] = a.src + ((int64_t)e.x * a.Np + e.y) * a.ld + c0 + cc;
                     } else {
-                        p = a.src + b * a.in_bstride + r * a.ld;
+                        p[i] = a.src + b * a.in_bstride + r * a.ld + c0 + cc;
                     }
                 }
-                u32x4 x = {0u, 0u, 0u, 0u};
-                if (p) x = *reinterpret_cast<const u32x4 *>(p + c0 + cc);
+            }
+            u32x4 x[N];
+            float wr[N];
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                x[i] = p[i] ? *reinterpret_cast<const u32x4 *>(p[i]) : u32x4{0u, 0u, 0u, 0u};
+                const int64_t r = r0 + (t >> 3) + i * (kColqThreads / 8);
+                wr[i] = a.wrow && r < rows ? a.wrow[r] : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int row = (t >> 3) + i * (kColqThreads / 8);
+                const int64_t r = r0 + row;
+                float v[8];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    st[(cc + 2 * j) * kColqLd + row] = __uint_as_float(x[j] << 16);
-                    st[(cc + 2 * j + 1) * kColqLd + row] = __uint_as_float(x[j] & 0xffff0000u);
+                    v[2 * j] = __uint_as_float(x[i][j] << 16);
+                    v[2 * j + 1] = __uint_as_float(x[i][j] & 0xffff0000u);
                 }
+                if (a.rq) {
+                    // row codes: lanes with t & 3 = 0 .. 3 (adjacent lanes of
+                    // one wave) hold one 32-column block of the row
+                    float am = 0.f;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(v[j]));
+                    am = fmaxf(am, __shfl_xor(am, 1, 64));
+                    am = fmaxf(am, __shfl_xor(am, 2, 64));
+                    const int se = mx_block_exp(am);
+                    float y[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) y[j] = __builtin_amdgcn_ldexpf(v[j], -se);
+                    const uint32_t w0 = e4m3_encode4(y[0], y[1], y[2], y[3]);
+                    const uint32_t w1 = e4m3_encode4(y[4], y[5], y[6], y[7]);
+                    if (r < rows && c0 + cc < a.C) {
+                        *reinterpret_cast<uint2 *>(a.rq + r * a.C + c0 + cc) = make_uint2(w0, w1);
+                        if ((t & 3) == 0) a.rs[r * (a.C / 32) + (c0 + cc) / 32] = (uint8_t)(se + 127);
+                    }
+                }
+                if (a.wrow) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) v[j] = __uint_as_float((uint32_t)f2bf(v[j] * wr[i]) << 16);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) st[(cc + j) * kColqLd + row] = v[j];
             }
         }
         __syncthreads();
+        // where column c0 + c of rows [r0, r0 + 128) goes: a [C][ld] block at
+        // `base` whose first row is `first` (a tile lies inside one segment:
+        // segments are multiples of 256 rows)
+        int64_t base = b * a.out_bstride, ld = a.ldq, first = 0;
+        if (a.seg_off) {
+            const int l = expert_of(a.seg_off, a.L, (int)r0);
+            first = a.seg_off[l];
+            ld = a.seg_off[l + 1] - first;
+            base = (int64_t)a.C * first;
+        }
         // one 32-row block of one column per thread
         const int c = t >> 2, blk = t & 3;
         const int64_t rb = r0 + 32 * blk;
@@ -161,10 +222,10 @@ __device__ __forceinline__ void mx_colq_body(const ColQArgs &a, float *st) {
             }
             uint32_t w[8];
             const uint32_t sb = mx_quantize32(v, w);
-            uint8_t *out = a.q + b * a.out_bstride + (int64_t)(c0 + c) * a.ldq + rb;
-            reinterpret_cast<u32x4 *>(out)[0] = u32x4{w[0], w[1], w[2], w[3]};
-            reinterpret_cast<u32x4 *>(out)[1] = u32x4{w[4], w[5], w[6], w[7]};
-            a.s[b * (a.out_bstride / 32) + (int64_t)(c0 + c) * (a.ldq / 32) + rb / 32] = (uint8_t)sb;
+            const int64_t o = base + (int64_t)(c0 + c) * ld + (rb - first);
+            reinterpret_cast<u32x4 *>(a.q + o)[0] = u32x4{w[0], w[1], w[2], w[3]};
+            reinterpret_cast<u32x4 *>(a.q + o)[1] = u32x4{w[4], w[5], w[6], w[7]};
+            a.s[o / 32] = (uint8_t)sb;
         }
     }
 }
@@ -257,43 +318,35 @@ __device__ __forceinline__ void mx_bwd_gateup_phase(const MxBwdArgs &a, char *ld
     }
 }
 
-// B5 with MX operands: the column-quantized activations, stored transposed
-// with ld_t codes per row (ld_t a multiple of 512, so scale rows of ld_t / 32
-// bytes stay 16-byte aligned).
+// B5 with MX operands: the column-quantized activations, segment-major
+// (expert l: a [C][n_l] block of codes at C * seg_off[l], its scales
+// [C][n_l / 32] at C * seg_off[l] / 32).
 struct MxWgradArgs {
-    const uint8_t *dOwTq, *dOwTs;  // (w dO_d)^T: [H][ld_t]
-    const uint8_t *aTq, *aTs;      // a^T: [I][ld_t]
-    const uint8_t *dHUTq, *dHUTs;  // dHU^T: [2I][ld_t]
-    const uint8_t *XdTq, *XdTs;    // Xd^T: [H][ld_t]
-    int64_t ld_t;
+    const uint8_t *dOwTq, *dOwTs;  // (w dO_d)^T, C = H
+    const uint8_t *aTq, *aTs;      // a^T, C = I
+    const uint8_t *dHUTq, *dHUTs;  // dHU^T, C = 2I
+    const uint8_t *XdTq, *XdTs;    // Xd^T, C = H
     const int32_t *seg_off;
     float *dW13, *dW2;
     int L, H, I;
 };
 
-// One 256 x 256 output tile of dW2[l] (W2) or dW13[l] over the expert's rows
-// [seg_off[l], seg_off[l+1]) (a multiple of 256; the scale rows start at a
-// multiple of 8 bytes, hence 4-byte scale DMAs).
+// One 256 x 256 output tile of dW2[l] (W2) or dW13[l] over the expert's
+// kext rows (a multiple of 256; scale rows of kext / 32 bytes, a multiple of
+// 8, hence 4-byte scale DMAs).
 template <bool W2>
 __device__ __forceinline__ void mx_wgrad_tile(const MxWgradArgs &a, int l, int mt, int nt, char *lds) {
     const int H = a.H, I = a.I;
-    const int64_t ld = a.ld_t, lds_s = ld / 32;
-    const int S = a.seg_off[l], kext = a.seg_off[l + 1] - S;
-    const uint8_t *aq, *as_, *bq, *bs_;
-    int bhi;
-    if constexpr (W2) {
-        aq = a.dOwTq + (int64_t)mt * 256 * ld + S;
-        as_ = a.dOwTs + (int64_t)mt * 256 * lds_s + S / 32;
-        bq = a.aTq + (int64_t)nt * 256 * ld + S;
-        bs_ = a.aTs + (int64_t)nt * 256 * lds_s + S / 32;
-        bhi = I - nt * 256 > 128 ? 128 : 0;
-    } else {
-        aq = a.dHUTq + (int64_t)mt * 256 * ld + S;
-        as_ = a.dHUTs + (int64_t)mt * 256 * lds_s + S / 32;
-        bq = a.XdTq + (int64_t)nt * 256 * ld + S;
-        bs_ = a.XdTs + (int64_t)nt * 256 * lds_s + S / 32;
-        bhi = 128;
-    }
+    const int64_t S = a.seg_off[l];
+    const int kext = a.seg_off[l + 1] - (int)S;
+    const int64_t ld = kext, lds_s = kext / 32;
+    // an operand's row r: the expert's block (at C * S) plus r * kext
+    const int Ca = W2 ? H : 2 * I, Cb = W2 ? I : H;
+    const uint8_t *aq = (W2 ? a.dOwTq : a.dHUTq) + Ca * S + (int64_t)mt * 256 * ld;
+    const uint8_t *as_ = (W2 ? a.dOwTs : a.dHUTs) + Ca * S / 32 + (int64_t)mt * 256 * lds_s;
+    const uint8_t *bq = (W2 ? a.aTq : a.XdTq) + Cb * S + (int64_t)nt * 256 * ld;
+    const uint8_t *bs_ = (W2 ? a.aTs : a.XdTs) + Cb * S / 32 + (int64_t)nt * 256 * lds_s;
+    const int bhi = (W2 && I - nt * 256 <= 128) ? 0 : 128;
     const KOp ak{as_u16(aq), as_u16(aq + 128 * ld), ld / 2, nullptr, nullptr, 0};
     const SOp as{as_, as_ + 128 * lds_s, lds_s, nullptr, nullptr, 0};
     const KOp bk{as_u16(bq), as_u16(bq + bhi * ld), ld / 2, nullptr, nullptr, 0};

@@ -381,23 +381,29 @@ def alloc_bwd_mx(d: moe_desc, device) -> MxBwdGrads:
 def mx_bwd_views(d: moe_desc, ws: torch.Tensor) -> dict:
     """Views of moe_layer_bwd_mx's workspace buffers (the MOE_WS_MX_* fields):
     dHU bf16 [cap][2I]; row codes / scales (DO, DHU) [cap][C] / [cap][C/32];
-    column codes / scales (DOWT, AT, XDT, DHUT) [C][ldt] / [C][ldt/32]."""
+    the column codes (DOWT, AT, XDT, DHUT) as flat (codes, scales) byte
+    tensors, segment-major (mx_expert_block cuts one expert's block out)."""
     cap = capacity_rows(d)
-    ldt = (cap + 511) // 512 * 512
     H, I2 = d.H, 2 * d.I
 
-    def at(field, shape, dtype=torch.uint8):
+    def at(field, nbytes):
         off = workspace_field(d, MOE_OP_LAYER_BWD_MX, field)
-        n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
-        return ws[off:off + n].view(dtype).view(shape)
+        return ws[off:off + nbytes]
 
-    v = {"dHU": at(MOE_WS_MX_DHU, (cap, I2), torch.bfloat16)}
+    v = {"dHU": at(MOE_WS_MX_DHU, cap * I2 * 2).view(torch.bfloat16).view(cap, I2)}
     for nm, f, C in (("DO", MOE_WS_MX_DO_Q, H), ("DHU", MOE_WS_MX_DHU_Q, I2)):
-        v[nm] = (at(f, (cap, C)), at(f + 1, (cap, C // 32)))
+        v[nm] = (at(f, cap * C).view(cap, C), at(f + 1, cap * C // 32).view(cap, C // 32))
     for nm, f, C in (("DOWT", MOE_WS_MX_DOWT_Q, H), ("AT", MOE_WS_MX_AT_Q, d.I), ("XDT", MOE_WS_MX_XDT_Q, H),
                      ("DHUT", MOE_WS_MX_DHUT_Q, I2)):
-        v[nm] = (at(f, (C, ldt)), at(f + 1, (C, ldt // 32)))
+        v[nm] = (at(f, cap * C), at(f + 1, cap * C // 32), C)
     return v
+
+
+def mx_expert_block(view, S: int, n: int):
+    """(codes [C][n], scales [C][n/32]) of the expert whose rows are [S, S+n)
+    in a segment-major column-code view of mx_bwd_views."""
+    q, s, C = view
+    return q[C * S:C * (S + n)].view(C, n), s[C * S // 32:C * (S + n) // 32].view(C, n // 32)
 
 
 def layer_bwd_mx(d, dOut, w, X, fwd: MxFwdBuffers, W13t, W2t, g: MxBwdGrads, stream=None):

@@ -182,14 +182,13 @@ def test_mx_backward_arguments_and_workspace():
     assert lib.moe_quantize_mx_t(None, 0, 64, 64, None, None, None) == ops.MOE_OK
     d = kimi()
     cap = ops.capacity_rows(d)
-    wb = ops.workspace_bytes(d, ops.MOE_OP_LAYER_BWD)
     wm = ops.workspace_bytes(d, ops.MOE_OP_LAYER_BWD_MX)
     H, I = 7168, 2048
-    ldt = (cap + 511) // 512 * 512
-    # the bf16 backward's buffers, the row-quantized dO_d and dHU, the four
-    # transposed column-quantized operands; codes plus a scale byte per 32
-    assert wm - wb >= (cap * (H + 2 * I) + ldt * (2 * H + 3 * I)) * 33 // 32
-    assert wm - wb <= (cap * (H + 2 * I) + ldt * (2 * H + 3 * I)) * 33 // 32 + 12 * 256
+    # dXd and dHU (bf16), the row weights and dw partials (fp32), the row
+    # codes of dO_d and dHU and the four column-coded operands (C codes per
+    # dispatched row); codes plus a scale byte per 32
+    need = cap * (2 * H + 4 * I + 4 + 4 * (I // 256)) + cap * (3 * H + 5 * I) * 33 // 32
+    assert need <= wm <= need + 16 * 256
     bwd = p[:18]  # 17 operands and the workspace
     assert lib.moe_layer_bwd_mx(ctypes.byref(d), *bwd, wm - 1, None) == ops.MOE_ENOSPC
     for i in range(18):

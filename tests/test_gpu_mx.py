@@ -144,6 +144,44 @@ def test_quantize_bit_exact(K):
     np.testing.assert_array_equal(s.cpu().numpy(), s_ref)
 
 
+def test_quantize_every_bf16_value_at_unit_scale():
+    """Every bf16 value below 512 in magnitude (both signs, zeros and
+    subnormals included) through the device quantizer at block scale 1: each
+    32-element block holds the anchor 256 (scale exponent 0) and 31 of the
+    values, so every E4M3 rounding midpoint (all of them bf16 values), every
+    subnormal step and the saturation between 448 and 512 is met, in every
+    position of a packed code word.  Row codes (moe_quantize_mx) and column
+    codes (moe_quantize_mx_t) bit for bit against the oracle."""
+    pats = np.arange(0x8000, dtype=np.uint32)
+    vals = (pats << 16).view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) < 512)]
+    vals = np.concatenate([vals, -vals])
+    nblk = -(-vals.size // 31)
+    blocks = np.zeros((nblk, 32), np.float32)
+    flat = np.zeros(nblk * 31, np.float32)
+    flat[:vals.size] = vals
+    blocks[:, 1:] = flat.reshape(nblk, 31)
+    blocks[:, 0] = 256.0
+    shift = np.arange(nblk) % 32                        # the anchor in every position
+    blocks = blocks[np.arange(nblk)[:, None], (np.arange(32)[None, :] - shift[:, None]) % 32]
+    nrow = -(-nblk // 64 // 8) * 8  # a multiple of 8 columns for the transposed call
+    x = np.zeros((nrow * 64, 32), np.float32)
+    x[:nblk] = blocks
+    x[nblk:, 0] = 256.0
+    xb = bf16_bits(x.reshape(nrow, 64 * 32))
+    q_ref, s_ref = oracle.mx_quantize(xb)
+    assert (s_ref == 127).all()
+    q, s = ops.quantize_mx(up_bf16(xb))
+    np.testing.assert_array_equal(q.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(s.cpu().numpy(), s_ref)
+    # the same values as columns: [R = 2048][C = nrow] quantized along R
+    xt = np.ascontiguousarray(xb.T)
+    qt, st = ops.quantize_mx_t(up_bf16(xt))
+    qt_ref, st_ref = oracle.mx_transpose_quantize(xt)
+    np.testing.assert_array_equal(qt.cpu().numpy(), qt_ref)
+    np.testing.assert_array_equal(st.cpu().numpy(), st_ref)
+
+
 def test_quantize_large_bit_exact():
     rng = np.random.default_rng(9)
     xb = bf16_bits(rng.standard_normal((2048, 2048)).astype(np.float32))

@@ -149,7 +149,8 @@ def check_expert(c, l, sg, g, b, v):
     dhu_eff = code_diff(f"[mx bwd] dHU codes[{l}]", dhu_g, (sg["dHUq"], sg["dHUs"]))
 
     def col(t):
-        return t[0][:, r0:r1].cpu().numpy(), t[1][:, r0 // 32:r1 // 32].cpu().numpy()
+        q, sc = ops.mx_expert_block(t, r0, r1 - r0)
+        return q.cpu().numpy(), sc.cpu().numpy()
 
     for nm in ("XdT", "dOwT"):  # column codes of bf16 values both sides hold: bit for bit
         gq, gs = col(v[nm.upper()])
