@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kFwdThreads) void k_mx_bwd_gateup(MxBwdArgs a) {
 }
 
 __global__ __launch_bounds__(kFwdThreads) void k_mx_wgrad(MxWgradArgs a, WindowCombine c) {
-    __shared__ __attribute__((aligned(16))) char lds[kMxLds];
+    __shared__ __attribute__((aligned(16))) char lds[kMxLds + 256 * sizeof(int)];
     mx_wgrad_phase(a, c, lds);
 }
 

@@ -119,6 +119,14 @@ __device__ __attribute__((noinline)) const uint16_t *mx_dma_src(const KOp &op, i
     return dma_src_w<64, 3, NW>(op, i);
 }
 
+// The same for an operand read in place (never gathered), inline: the
+// out-of-line call takes the operand through scratch memory, and reading it
+// back waits for every vector-memory operation in flight.
+template <int NW>
+__device__ __forceinline__ const uint16_t *mx_dma_src_plain(const KOp &op, int i) {
+    return dma_src_w<64, 3, NW>(KOp{op.lo, op.hi, op.ld, nullptr, nullptr, 0}, i);
+}
+
 template <int OPSEL>
 __device__ __forceinline__ f32x16 mfma_mx(const i32x8 &a, const i32x8 &b, const f32x16 &c, uint32_t sa, uint32_t sb) {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, OPSEL, (int)sa, OPSEL, (int)sb);
@@ -208,17 +216,19 @@ __device__ __forceinline__ void mx_read_scales(char *lds, int kt, int arow, cons
     for (int ni = 0; ni < WaveGrid<WM, WN>::NI; ++ni) cb[ni] = swb[brow[ni] * SG + j] >> (8 * h);
 }
 
-// One 128-deep K step kt on stage `slot`: wait for the stage; on the first
-// step of an SG-step group that has a successor, fetch that group's scale
-// words (their buffer was last read in the previous group, which every wave
-// has left by this barrier); with FILL spread the next stage's DMA over
-// sub-step 0.  The scale fetch comes before the sub-steps so that its branch
-// does not split them: the MFMA / DMA interleave is pinned only within one
-// basic block.  ca / cb hold this step's scale words on entry when SG > 1
-// (read one step ahead, between the sub-steps: step kt + 1's group is in LDS
-// since step kt's barrier) and the next step's on return; with SG = 1 the
-// next group is this step's DMA, so the words are read after the barrier.
-template <int WM, int WN, int EVERY, int GH, int SG, bool FILL>
+// One 128-deep K step kt on stage `slot`: wait for the stage (TAIL: the
+// caller's prologue or the previous step did); on the first step of an
+// SG-step group that has a successor, fetch that group's scale words (their
+// buffer was last read in the previous group, which every wave has left by
+// that barrier); with FILL spread the next stage's DMA over sub-step 0 (and
+// with TAIL end with the wait and barrier for it).  The scale fetch comes
+// before the sub-steps so that its branch does not split them: the MFMA /
+// DMA interleave is pinned only within one basic block.  ca / cb hold this
+// step's scale words on entry when SG > 1 (read one step ahead, between the
+// sub-steps: step kt + 1's group is in LDS since step kt's barrier) and the
+// next step's on return; with SG = 1 the next group is this step's DMA, so
+// the words are read after the barrier.
+template <int WM, int WN, int EVERY, int GH, int SG, bool FILL, bool TAIL>
 __device__ __forceinline__ void mx_step(char *lds, int slot, int kt, int nk, int arow,
                                         const int (&brow)[WaveGrid<WM, WN>::NI], int h, const uint32_t *ssrc,
                                         uint32_t (&ca)[WaveGrid<WM, WN>::MI], uint32_t (&cb)[WaveGrid<WM, WN>::NI],
@@ -227,7 +237,7 @@ __device__ __forceinline__ void mx_step(char *lds, int slot, int kt, int nk, int
     using WG = WaveGrid<WM, WN>;
     constexpr int MI = WG::MI, NI = WG::NI;
     constexpr int stage_bytes = 2 * 256 * 128;
-    wait_vm_barrier<0>();
+    if constexpr (!TAIL) wait_vm_barrier<0>();
     if (FILL && kt % SG == 0 && kt + SG < nk) mx_scale_dma<SG>(ssrc, kt + SG, lds, (kt / SG + 1) & 1);
     char *dst = lds + (slot ^ 1) * stage_bytes;
     const char *stage = lds + slot * stage_bytes;
@@ -242,6 +252,10 @@ __device__ __forceinline__ void mx_step(char *lds, int slot, int kt, int nk, int
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) cb[ni] = nb[ni];
     }
+    if constexpr (FILL && TAIL) {
+        __builtin_amdgcn_sched_barrier(0);  // every MFMA of the step issued before the wave waits
+        wait_vm_barrier<0>();
+    }
 }
 
 // MX main loop: 256 x 256 tile, K steps of 128 codes (one [256][128]-byte
@@ -253,9 +267,21 @@ __device__ __forceinline__ void mx_step(char *lds, int slot, int kt, int nk, int
 // vector-memory requests of the operand tiles.  SG = 4 (16-byte lanes) needs
 // nk % 4 == 0 and 16-byte aligned scale rows, SG = 1 4-byte aligned ones.
 // Needs 8 waves (4 x 64 rows per operand); lds holds kMxLds bytes.
-template <int WM, int WN, int SG>
+//
+// PLAIN: both operands are read in place (no gathered rows): their DMA
+// addresses are computed inline, each step's wait sits at the end of the
+// step before it (the prologue's for step 0), and pre may be set.
+//
+// pre (PLAIN only): step 0's operand and scale DMAs were issued by
+// mx_prefetch_stage0, followed by at least 64 more vector-memory operations
+// of this wave (a previous tile's stores).  A wave's vector-memory
+// operations complete in issue order, so once no more than the last 63 are
+// in flight those DMAs have landed: the prologue waits for vmcnt 63, not for
+// the stores to be written.  Read in the prologue only, so the loop carries
+// no flag.
+template <int WM, int WN, int SG, bool PLAIN = false>
 __device__ __forceinline__ void gemm_mainloop_mx(const KOp &ak, const KOp &bk, const SOp &as, const SOp &bs, int nk,
-                                                 bool swiglu, char *lds, AccW<WM, WN> &acc) {
+                                                 bool swiglu, char *lds, AccW<WM, WN> &acc, bool pre = false) {
     using WG = WaveGrid<WM, WN>;
     constexpr int MI = WG::MI, NI = WG::NI, NW = WG::NW;
     static_assert(NW == 8, "one scale DMA per wave: waves 0-3 A rows, 4-7 B rows");
@@ -281,30 +307,56 @@ __device__ __forceinline__ void gemm_mainloop_mx(const KOp &ak, const KOp &bk, c
     const uint16_t *asrc[GH], *bsrc[GH];
 #pragma unroll
     for (int i = 0; i < GH; ++i) {
-        asrc[i] = mx_dma_src<NW>(ak, i);
-        bsrc[i] = mx_dma_src<NW>(bk, i);
+        asrc[i] = PLAIN ? mx_dma_src_plain<NW>(ak, i) : mx_dma_src<NW>(ak, i);
+        bsrc[i] = PLAIN ? mx_dma_src_plain<NW>(bk, i) : mx_dma_src<NW>(bk, i);
     }
     const uint32_t *ssrc = reinterpret_cast<const uint32_t *>(
         wave < 4 ? mx_scale_row(as, 64 * wave + lane) : mx_scale_row(bs, 64 * (wave - 4) + lane));
-    __syncthreads();  // the previous tile's epilogue may still read LDS
-    mx_scale_dma<SG>(ssrc, 0, lds, 0);
+    if (!(PLAIN && pre)) {
+        __syncthreads();  // the previous tile's epilogue may still read LDS
+        mx_scale_dma<SG>(ssrc, 0, lds, 0);
 #pragma unroll
-    for (int i = 0; i < GH; ++i) {
-        dma_blk_w<64, NW>(asrc[i], 0, lds, i);
-        dma_blk_w<64, NW>(bsrc[i], 0, lds + tile_bytes, i);
+        for (int i = 0; i < GH; ++i) {
+            dma_blk_w<64, NW>(asrc[i], 0, lds, i);
+            dma_blk_w<64, NW>(bsrc[i], 0, lds + tile_bytes, i);
+        }
+        if constexpr (PLAIN) wait_vm_barrier<0>();
+    } else {
+        wait_vm_barrier<63>();
     }
     uint32_t ca[MI], cb[NI];
     if constexpr (SG > 1) {  // step 0's words: wait for the first group
-        wait_vm_barrier<0>();
+        if constexpr (!PLAIN) wait_vm_barrier<0>();
         mx_read_scales<WM, WN, SG>(lds, 0, arow, brow, h, ca, cb);
     }
     int slot = 0;
     for (int kt = 0; kt + 1 < nk; ++kt) {
-        mx_step<WM, WN, EVERY, GH, SG, true>(lds, slot, kt, nk, arow, brow, h, ssrc, ca, cb, acc, asrc, bsrc);
+        mx_step<WM, WN, EVERY, GH, SG, true, PLAIN>(lds, slot, kt, nk, arow, brow, h, ssrc, ca, cb, acc, asrc, bsrc);
         slot ^= 1;
     }
-    mx_step<WM, WN, EVERY, GH, SG, false>(lds, slot, nk - 1, nk, arow, brow, h, ssrc, ca, cb, acc, asrc, bsrc);
+    mx_step<WM, WN, EVERY, GH, SG, false, PLAIN>(lds, slot, nk - 1, nk, arow, brow, h, ssrc, ca, cb, acc, asrc, bsrc);
     __syncthreads();
+}
+
+// Step 0's DMAs of an MX tile whose operands are read in place (operands and
+// scale words), issued ahead of gemm_mainloop_mx(..., pre = true) on the
+// same operands; LDS must be free (after a main loop's closing barrier, with
+// no LDS use since).
+template <int WM, int WN, int SG>
+__device__ __forceinline__ void mx_prefetch_stage0(const KOp &ak, const KOp &bk, const SOp &as, const SOp &bs,
+                                                   char *lds) {
+    constexpr int NW = WaveGrid<WM, WN>::NW;
+    constexpr int tile_bytes = 256 * 128;
+    constexpr int GH = tile_bytes / 1024 / NW;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint32_t *ssrc = reinterpret_cast<const uint32_t *>(
+        wave < 4 ? mx_scale_row(as, 64 * wave + lane) : mx_scale_row(bs, 64 * (wave - 4) + lane));
+    mx_scale_dma<SG>(ssrc, 0, lds, 0);
+#pragma unroll
+    for (int i = 0; i < GH; ++i) {
+        dma_blk_w<64, NW>(mx_dma_src_plain<NW>(ak, i), 0, lds, i);
+        dma_blk_w<64, NW>(mx_dma_src_plain<NW>(bk, i), 0, lds + tile_bytes, i);
+    }
 }
 
 // Gate/up tile -> a = silu(gate) * up (256 rows x 128 columns), MX-quantized

@@ -331,41 +331,110 @@ struct MxWgradArgs {
     int L, H, I;
 };
 
-// One 256 x 256 output tile of dW2[l] (W2) or dW13[l] over the expert's
-// kext rows (a multiple of 256; scale rows of kext / 32 bytes, a multiple of
-// 8, hence 4-byte scale DMAs).
-template <bool W2>
-__device__ __forceinline__ void mx_wgrad_tile(const MxWgradArgs &a, int l, int mt, int nt, char *lds) {
+// The operands of one 256 x 256 output tile of dW2[l] (w2) or dW13[l] over
+// the expert's kext rows (a multiple of 256; scale rows of kext / 32 bytes, a
+// multiple of 8, hence 4-byte scale DMAs).
+struct MxWgradTile {
+    KOp ak, bk;
+    SOp as, bs;
+    int nk;
+};
+
+// seg_off[l] for a uniform l by a scalar load: it adds nothing to the vector
+// memory counter, so reading it does not wait for the previous tile's stores.
+__device__ __forceinline__ int seg_uniform(const int32_t *seg_off, int l) {
+    using cint = __attribute__((address_space(4))) const int32_t;
+    return ((cint *)seg_off)[l];
+}
+
+__device__ __forceinline__ MxWgradTile mx_wgrad_operands(const MxWgradArgs &a, bool w2, int l, int mt, int nt) {
     const int H = a.H, I = a.I;
-    const int64_t S = a.seg_off[l];
-    const int kext = a.seg_off[l + 1] - (int)S;
+    const int64_t S = seg_uniform(a.seg_off, l);
+    const int kext = seg_uniform(a.seg_off, l + 1) - (int)S;
     const int64_t ld = kext, lds_s = kext / 32;
     // an operand's row r: the expert's block (at C * S) plus r * kext
-    const int Ca = W2 ? H : 2 * I, Cb = W2 ? I : H;
-    const uint8_t *aq = (W2 ? a.dOwTq : a.dHUTq) + Ca * S + (int64_t)mt * 256 * ld;
-    const uint8_t *as_ = (W2 ? a.dOwTs : a.dHUTs) + Ca * S / 32 + (int64_t)mt * 256 * lds_s;
-    const uint8_t *bq = (W2 ? a.aTq : a.XdTq) + Cb * S + (int64_t)nt * 256 * ld;
-    const uint8_t *bs_ = (W2 ? a.aTs : a.XdTs) + Cb * S / 32 + (int64_t)nt * 256 * lds_s;
-    const int bhi = (W2 && I - nt * 256 <= 128) ? 0 : 128;
-    const KOp ak{as_u16(aq), as_u16(aq + 128 * ld), ld / 2, nullptr, nullptr, 0};
-    const SOp as{as_, as_ + 128 * lds_s, lds_s, nullptr, nullptr, 0};
-    const KOp bk{as_u16(bq), as_u16(bq + bhi * ld), ld / 2, nullptr, nullptr, 0};
-    const SOp bs{bs_, bs_ + bhi * lds_s, lds_s, nullptr, nullptr, 0};
-    AccW<kFwdWM, kFwdWN> acc;
-    gemm_mainloop_mx<kFwdWM, kFwdWN, 1>(ak, bk, as, bs, kext / 128, false, lds, acc);
-    if constexpr (W2)
-        epilogue_store_f32_w<kFwdWM, kFwdWN>(acc, a.dW2 + (int64_t)l * H * I + (int64_t)mt * 256 * I + nt * 256, I, 256,
-                                             I - nt * 256);
+    const int Ca = w2 ? H : 2 * I, Cb = w2 ? I : H;
+    const uint8_t *aq = (w2 ? a.dOwTq : a.dHUTq) + Ca * S + (int64_t)mt * 256 * ld;
+    const uint8_t *as_ = (w2 ? a.dOwTs : a.dHUTs) + Ca * S / 32 + (int64_t)mt * 256 * lds_s;
+    const uint8_t *bq = (w2 ? a.aTq : a.XdTq) + Cb * S + (int64_t)nt * 256 * ld;
+    const uint8_t *bs_ = (w2 ? a.aTs : a.XdTs) + Cb * S / 32 + (int64_t)nt * 256 * lds_s;
+    const int bhi = (w2 && I - nt * 256 <= 128) ? 0 : 128;
+    return {KOp{as_u16(aq), as_u16(aq + 128 * ld), ld / 2, nullptr, nullptr, 0},
+            KOp{as_u16(bq), as_u16(bq + bhi * ld), ld / 2, nullptr, nullptr, 0},
+            SOp{as_, as_ + 128 * lds_s, lds_s, nullptr, nullptr, 0},
+            SOp{bs_, bs_ + bhi * lds_s, lds_s, nullptr, nullptr, 0}, kext / 128};
+}
+
+// Work item lid of the weight-gradient launch: a tile (w2, l, mt, nt) when
+// lid < L * per, else a reverse-dispatch item.
+struct MxWgradItem {
+    bool w2;
+    int l, mt, nt;
+};
+
+__device__ __forceinline__ MxWgradItem mx_wgrad_item(int64_t lid, int L, int per, int mt2, int nt2, int mt13, int nt13,
+                                                     const int *s_order) {
+    const int pos = (int)((uint32_t)lid / (uint32_t)per), in = (int)((uint32_t)lid - (uint32_t)pos * (uint32_t)per);
+    MxWgradItem t;
+    t.l = L <= 256 ? __builtin_amdgcn_readfirstlane(s_order[pos]) : pos;  // uniform: keep it scalar
+    t.w2 = in < mt2 * nt2;
+    if (t.w2)
+        grouped_mn<4>(in, mt2, nt2, t.mt, t.nt);
     else
-        epilogue_store_f32_w<kFwdWM, kFwdWN>(acc, a.dW13 + (int64_t)l * 2 * I * H + (int64_t)mt * 256 * H + nt * 256, H,
-                                             256, 256);
+        grouped_mn<4>(in - mt2 * nt2, mt13, nt13, t.mt, t.nt);
+    return t;
+}
+
+// One weight-gradient tile; pre: its first stage is in flight.  When the
+// block's next item (nlid, if nxt) is a tile, its first stage's DMAs go out
+// before this tile's stores; returns whether they did.
+template <bool W2>
+__device__ __forceinline__ bool mx_wgrad_tile(const MxWgradArgs &a, const MxWgradItem &t, bool pre, bool nxt,
+                                              int64_t nlid, int L, int per, int mt2, int nt2, int mt13, int nt13,
+                                              const int *s_order, char *lds) {
+    const int H = a.H, I = a.I;
+    AccW<kFwdWM, kFwdWN> acc;
+    {
+        const MxWgradTile o = mx_wgrad_operands(a, W2, t.l, t.mt, t.nt);
+        gemm_mainloop_mx<kFwdWM, kFwdWN, 1, true>(o.ak, o.bk, o.as, o.bs, o.nk, false, lds, acc, pre);
+    }
+    const int nvalid = W2 ? min(256, I - t.nt * 256) : 256;
+    bool issued = false;
+    if (nvalid == 256 && nxt) {
+        const MxWgradItem u = mx_wgrad_item(nlid, L, per, mt2, nt2, mt13, nt13, s_order);
+        const MxWgradTile o = mx_wgrad_operands(a, u.w2, u.l, u.mt, u.nt);
+        if (o.nk > 0) {
+            mx_prefetch_stage0<kFwdWM, kFwdWN, 1>(o.ak, o.bk, o.as, o.bs, lds);
+            issued = true;
+        }
+    }
+    if constexpr (W2)
+        epilogue_store_f32_w<kFwdWM, kFwdWN>(acc, a.dW2 + (int64_t)t.l * H * I + (int64_t)t.mt * 256 * I + t.nt * 256, I,
+                                             256, nvalid);
+    else
+        epilogue_store_f32_w<kFwdWM, kFwdWN>(
+            acc, a.dW13 + (int64_t)t.l * 2 * I * H + (int64_t)t.mt * 256 * H + t.nt * 256, H, 256, 256);
+    return issued;
 }
 
 // All weight-gradient tiles, longest experts first, then the reverse-dispatch
-// items of `c` (as the bf16 weight-gradient launch).
+// items of `c` (as the bf16 weight-gradient launch).  A tile's 256 KB of fp32
+// stores drain slowly (the workgroups write their tiles at about the same
+// time), and a wave's vector-memory operations complete in order, so a DMA
+// issued after the stores is seen to land only once they have drained.  When
+// the block's next item is a tile, its first stage's DMAs therefore go out
+// before this tile's stores (LDS is free after the main loop; the store
+// epilogue uses none): the next main loop starts once all but the last 63
+// stores have drained, and its first step's MFMAs overlap the rest.  Only
+// after a whole tile (128 stores per wave).  Nothing between the stores and
+// that wait may wait for the counter: the tile operands come from scalar
+// loads and inline address arithmetic, no vector loads or scratch.  The
+// expert order sits past the GEMM's LDS in the same array: with a second LDS
+// variable the compiler gives LDS accesses alias scopes and then waits for
+// every outstanding DMA before the scale and fragment reads of each step.
 __device__ __forceinline__ void mx_wgrad_phase(const MxWgradArgs &a, const WindowCombine &c, char *lds) {
     const int H = a.H, I = a.I, L = a.L;
-    __shared__ int s_order[256];
+    int *s_order = reinterpret_cast<int *>(lds + kMxLds);
     experts_by_rows(a.seg_off, L, 1, s_order);
     const int mt2 = H / 256, nt2 = (I + 255) / 256;  // dW2 [H][I]
     const int mt13 = 2 * I / 256, nt13 = H / 256;     // dW13 [2I][H]
@@ -373,6 +442,7 @@ __device__ __forceinline__ void mx_wgrad_phase(const MxWgradArgs &a, const Windo
     const int64_t ntiles = (int64_t)L * per;
     const int64_t ncb = c.Y ? (c.ntok + kCombineItem - 1) / kCombineItem : 0;
     const int64_t total = ntiles + ncb;
+    bool pre = false;  // this item's first stage is in flight
     for (int64_t it = blockIdx.x; it - blockIdx.x < total; it += gridDim.x) {
         const int64_t lid = logical_tile(it);
         if (lid >= total) continue;
@@ -382,16 +452,13 @@ __device__ __forceinline__ void mx_wgrad_phase(const MxWgradArgs &a, const Windo
                                          threadIdx.x / kWave, blockDim.x / kWave, c.tpp, c.tstride);
             continue;
         }
-        const int pos = (int)((uint32_t)lid / (uint32_t)per), in = (int)((uint32_t)lid - (uint32_t)pos * (uint32_t)per);
-        const int l = L <= 256 ? s_order[pos] : pos;
-        int mt, nt;
-        if (in < mt2 * nt2) {
-            grouped_mn<4>(in, mt2, nt2, mt, nt);
-            mx_wgrad_tile<true>(a, l, mt, nt, lds);
-        } else {
-            grouped_mn<4>(in - mt2 * nt2, mt13, nt13, mt, nt);
-            mx_wgrad_tile<false>(a, l, mt, nt, lds);
-        }
+        const MxWgradItem t = mx_wgrad_item(lid, L, per, mt2, nt2, mt13, nt13, s_order);
+        const int64_t nx = it + gridDim.x, nlid = logical_tile(nx);
+        const bool nxt = nx - blockIdx.x < total && nlid < ntiles;
+        if (t.w2)
+            pre = mx_wgrad_tile<true>(a, t, pre, nxt, nlid, L, per, mt2, nt2, mt13, nt13, s_order, lds);
+        else
+            pre = mx_wgrad_tile<false>(a, t, pre, nxt, nlid, L, per, mt2, nt2, mt13, nt13, s_order, lds);
     }
 }
 
