@@ -109,12 +109,12 @@ __global__ __launch_bounds__(kFwdThreads) void k_ring_gateup_combine(FfnArgs a, 
 
 __global__ __launch_bounds__(kFwdThreads) void k_ffn_gateup(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
-    ffn_gateup_phase(a, 0, a.seg_off[a.L], lds);
+    ffn_gateup_phase(a, lds);
 }
 
 __global__ __launch_bounds__(kFwdThreads) void k_ffn_down(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kGemmLds];
-    ffn_down_phase(a, 0, a.seg_off[a.L], lds);
+    ffn_down_phase(a, lds);
 }
 
 // Wide-tile down projection: 8 waves, all 160 KiB of LDS, one workgroup per CU.
