@@ -1485,8 +1485,15 @@ int moe_trace_enable(int max_records) {
     g_trace_used = 0;
     if (max_records <= 0) return MOE_OK;
     g_trace.resize(max_records);
+    // Timing events without the system-scope fence: the default release at
+    // each record writes the L2s back for the host (about 10 us between two
+    // traced launches); the host reads these events only through
+    // hipEventElapsedTime, after synchronizing.
+    constexpr unsigned flags = hipEventDefault | hipEventDisableSystemFence;
     for (auto &r : g_trace) {
-        if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) return MOE_EHIP;
+        if (hipEventCreateWithFlags(&r.start, flags) != hipSuccess ||
+            hipEventCreateWithFlags(&r.stop, flags) != hipSuccess)
+            return MOE_EHIP;
         r.name[0] = 0;
     }
     g_trace_cap = max_records;
