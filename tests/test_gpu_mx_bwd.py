@@ -51,6 +51,11 @@ CASES = {
     "hot_empty_base": dict(seed=12, P=2, Np=400, E=16, K=3, L=6, H=512, I=256, base=5, hot=True),
     # I % 256 = 128 with 2I = 768 (4-byte scale DMAs in the gate/up dgrad), top-1
     "k1_i384": dict(seed=13, P=1, Np=700, E=4, K=1, L=4, H=256, I=384),
+    # 512 weight-gradient tiles, so every workgroup of the launch takes two:
+    # a tile that issues the next one's first stage before its stores, next
+    # tiles of the other weight, with a half-width column (I % 256 = 128) or
+    # with no rows (an empty expert), and the reverse-dispatch items after them
+    "multi_tile": dict(seed=14, P=2, Np=512, E=16, K=2, L=8, H=2048, I=640, hot=True),
 }
 
 
