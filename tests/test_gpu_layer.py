@@ -106,6 +106,26 @@ def test_small_forward_multi_tile():
     check_fwd_full(lay, lay.fwd())
 
 
+def test_forward_large_experts():
+    """Experts of 11 and 9 M tiles next to small ones: the gate/up tiles of an
+    expert with more than 8 M tiles sweep the N tiles in groups of 4 aligned
+    to its first tile, the last group short (3, then 1); every row, output
+    and gradient against the oracle."""
+    print("[layer] forward + backward, experts of 11 and 9 M tiles", flush=True)
+    lay = Layer(12, 4, 700, 8, 2, 4, 256, 128, routing="uniform")
+    rt = lay.h["routes"].copy()
+    rt[:, :, 0] = 1                 # 2,800 rows: 11 tiles
+    rt[:3, :, 1] = 2                # 2,100 rows: 9 tiles
+    rt[3, :, 1] = np.where(rt[3, :, 1] < 3, 5, rt[3, :, 1])  # partition 3's second slot off experts 1 and 2
+    lay.h["routes"] = rt
+    lay.routes = up(rt)
+    s = lay.oracle_schedule()
+    assert list(np.diff(s.seg_off)[1:3] // 256) == [11, 9]
+    b = lay.fwd()
+    check_fwd_full(lay, b)
+    check_bwd_full(lay, lay.bwd(b))
+
+
 def test_forward_paths_agree_bitwise():
     lay = Layer(4, 4, 900, 16, 4, 8, 512, 384, routing="uniform")
     ref = lay.fwd()
