@@ -243,6 +243,10 @@ enum {
  * workgroups pass device-side barriers between stages ([MoK] section 5,
  * megakernel fusion); otherwise one launch per stage.  Both give bitwise the
  * same results.  chunk_rows as in moe_expert_ffn.
+ * Without MOE_PERSISTENT and with chunk_rows == 0, a token with exactly one
+ * local route has its output row written by the down GEMM's epilogue (the
+ * combine's one-term sum, same fp32 product and bf16 rounding) and the
+ * combine launch skips it; out is bitwise what the other paths write.
  * Xd may be NULL: the dispatch is then fused into the gate/up GEMM, whose
  * operand loads pull each row from X through phi ([MoK] section 2, pull
  * dispatch hidden behind the GEMM), and no dispatched copy is written; every

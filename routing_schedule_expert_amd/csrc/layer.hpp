@@ -45,6 +45,7 @@ struct FfnArgs {
     const uint16_t *X;
     const moe_src *phi;
     int32_t Np;
+    RowCombine rc;  // the wide down tiles' combine of single-route tokens (rc.out null: none)
 };
 
 __device__ __forceinline__ void ffn_gateup_tile(const FfnArgs &a, int mt, int nt, char *lds) {
@@ -121,7 +122,7 @@ __device__ __forceinline__ void wide_down_tile(const FfnArgs &a, int mt, int n0,
     const int l = expert_of(a.seg_off, a.L, m0);
     AccWide<BN> acc;
     wide_mainloop<BN>(a.A + (int64_t)m0 * I, I, a.W2 + ((int64_t)l * H + n0) * I, I, I / kWBK, lds, acc);
-    wide_epilogue_store<BN>(acc, lds, a.Y + (int64_t)m0 * H + n0, H);
+    wide_epilogue_store<BN>(acc, lds, a.Y + (int64_t)m0 * H + n0, H, a.rc, m0, n0);
 }
 
 // All wide tiles (groups of 4 M tiles sweep the N tiles), then the narrow ones.

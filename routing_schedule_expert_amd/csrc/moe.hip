@@ -59,10 +59,16 @@ __global__ __launch_bounds__(256) void k_gather_scaled(const uint16_t *src, cons
 
 __global__ __launch_bounds__(256) void k_combine(const uint16_t *Y, const int32_t *route_row, const float *w,
                                                  uint16_t *out, int K, int H, int64_t ntok, int tpp,
-                                                 int64_t tstride, const uint16_t *S) {
+                                                 int64_t tstride, const uint16_t *S, int skip_single) {
     const int waves = blockDim.x / kWave;
     combine_body(Y, route_row, w, out, K, H, 0, ntok, blockIdx.x * waves + threadIdx.x / kWave, gridDim.x * waves,
-                 tpp, tstride, S);
+                 tpp, tstride, S, skip_single != 0);
+}
+
+// sj (see single_slot_body) for every token of one table.
+__global__ __launch_bounds__(256) void k_single_slot(const int32_t *route_row, int32_t *sj, int K, int64_t ntok) {
+    for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < ntok; g += (int64_t)gridDim.x * blockDim.x)
+        single_slot_body(route_row, sj, K, g);
 }
 
 // The shared expert's table: row g < ntok pulls token g (partition g / Np,
@@ -309,6 +315,10 @@ int64_t sched_ws_bytes(const moe_desc *d) {
     return sched_ids8_offset(d) + ids;
 }
 
+// The forward's per-row slot table (k_single_slot): one int32 per row of
+// capacity, after the schedule's workspace.
+int64_t single_slot_bytes(const moe_desc *d) { return align256(cap_rows(d) * 4); }
+
 int bwd_nparts(const moe_desc *d) { return (d->I + 255) / 256; }  // one dw partial per 256-column tile
 
 // Backward workspace: dO_d, dXd, dO_d * w (bf16 [cap][H] each), dHU (bf16
@@ -459,13 +469,14 @@ int launch_gather(const moe_desc *d, const uint16_t *src, const moe_src *phi, co
 // [P][tstride] token array (route_row, w, out pointing at its first token).
 // S (nullable): the shared expert's output rows [P*Np][H], added per token.
 int launch_combine(const moe_desc *d, const uint16_t *Y, const int32_t *route_row, const float *w, uint16_t *out,
-                   hipStream_t s, const char *name, int64_t tstride = 0, const uint16_t *S = nullptr) {
+                   hipStream_t s, const char *name, int64_t tstride = 0, const uint16_t *S = nullptr,
+                   bool skip_single = false) {
     const int64_t ntok = (int64_t)d->P * d->Np;
     const int grid = (int)std::min<int64_t>((ntok + 3) / 4, 16ll * device_cus());
     const int tpp = tstride > d->Np ? d->Np : 0;
     TraceScope tr(name, s);
     hipLaunchKernelGGL(k_combine, dim3(grid), dim3(256), 0, s, Y, route_row, w, out, d->K, d->H, ntok, tpp,
-                       tpp ? tstride : (int64_t)0, S);
+                       tpp ? tstride : (int64_t)0, S, skip_single ? 1 : 0);
     return launch_status();
 }
 
@@ -488,6 +499,7 @@ FfnArgs make_ffn_args(const moe_desc *d, const uint16_t *Xd, const uint16_t *W13
     a.I = d->I;
     a.chunk_rows = chunk_rows;
     a.bar = bar;
+    a.rc = RowCombine{nullptr, nullptr, nullptr, nullptr, 0, 0};
     return a;
 }
 
@@ -603,7 +615,7 @@ int64_t moe_workspace_bytes(const moe_desc *d, int op) {
         case MOE_OP_LAYER_FWD: {
             moe_desc one = *d;
             one.num_batches = 1;
-            return kBarrierBytes + sched_ws_bytes(&one);
+            return kBarrierBytes + sched_ws_bytes(&one) + single_slot_bytes(d);
         }
         case MOE_OP_LAYER_BWD: return bwd_ws_bytes(d);
         case MOE_OP_LAYER_BWD_MX: return mx_bwd_ws_bytes(d);
@@ -766,9 +778,23 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
         if (rc != MOE_OK) return rc;
     }
     FfnArgs a = make_ffn_args(d, Xd, W13, W2, seg_off, HU, A, Y, chunk_rows, bar, X, phi);
+    // with the wide down tiles, the tokens that have one local route are
+    // combined in the down GEMM's epilogue and the combine launch skips them
+    const bool fused = chunk_rows <= 0;
+    if (fused) {
+        int32_t *sj = reinterpret_cast<int32_t *>(sched_ws + sched_ws_bytes(&one));
+        const int64_t ntok = (int64_t)d->P * d->Np;
+        {
+            TraceScope tr("single_slot", s);
+            const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((ntok + 255) / 256, 4ll * device_cus()));
+            hipLaunchKernelGGL(k_single_slot, dim3(grid), dim3(256), 0, s, route_row, sj, d->K, ntok);
+        }
+        if (launch_status() != MOE_OK) return MOE_EHIP;
+        a.rc = RowCombine{out, phi, sj, w, d->K, d->Np};
+    }
     rc = launch_ffn(d, a, s);
     if (rc != MOE_OK) return rc;
-    return launch_combine(d, Y, route_row, w, out, s, "combine");
+    return launch_combine(d, Y, route_row, w, out, s, "combine", 0, nullptr, fused);
 }
 
 }  // extern "C"
@@ -1467,7 +1493,7 @@ int moe_layer_bwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots,
             const int64_t ntok = rd.ntok;
             const int grid = (int)std::min<int64_t>((ntok + 3) / 4, 16ll * device_cus());
             hipLaunchKernelGGL(k_combine, dim3(grid), dim3(256), 0, s, rd.Y, rd.route_row, rd.w, rd.out, rd.K, rd.H,
-                               ntok, rd.tpp, rd.tstride, (const uint16_t *)nullptr);
+                               ntok, rd.tpp, rd.tstride, (const uint16_t *)nullptr, 0);
             if (launch_status() != MOE_OK) return MOE_EHIP;
         }
     }

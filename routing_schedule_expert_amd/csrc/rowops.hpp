@@ -109,15 +109,26 @@ __device__ void gather_rows_scaled_body(const uint16_t *__restrict__ src, const 
 // many waves per CU and U = kRowUnroll; a combine that runs inside a GEMM
 // kernel (eight waves per CU) takes U = kRowUnrollWide, a whole 7,168-wide
 // row per wave, so the CU still keeps enough row loads in flight.
+// skip_single: tokens with exactly one local route are left alone (the down
+// GEMM's epilogue wrote them: down_combine_rows).
 template <int U = kRowUnroll>
 __device__ void combine_body(const uint16_t *__restrict__ Y, const int32_t *__restrict__ route_row,
                              const float *__restrict__ w, uint16_t *__restrict__ out, int K, int H,
                              int64_t g_begin, int64_t g_end, int wave_global, int nwaves, int tpp = 0,
-                             int64_t tstride = 0, const uint16_t *__restrict__ S = nullptr) {
+                             int64_t tstride = 0, const uint16_t *__restrict__ S = nullptr,
+                             bool skip_single = false) {
     const int lane = lane_id();
     const int chunks = H / 8;
     for (int64_t gw = g_begin + wave_global; gw < g_end; gw += nwaves) {
         const int64_t g = window_token(gw, tpp, tstride);
+        if (skip_single) {
+            int n = 0;
+            for (int j0 = 0; j0 < K; j0 += kWave) {
+                const int j = j0 + lane;
+                n += __popcll(ballot(j < K && route_row[g * K + j] >= 0));
+            }
+            if (n == 1) continue;
+        }
         u32x4 *o = reinterpret_cast<u32x4 *>(out + g * (int64_t)H);
         for (int c0 = 0; c0 < chunks; c0 += U * kWave) {
             float acc[U][8];
@@ -165,6 +176,21 @@ __device__ void combine_body(const uint16_t *__restrict__ Y, const int32_t *__re
                                  pack_bf2(acc[u][4], acc[u][5]), pack_bf2(acc[u][6], acc[u][7])};
             }
         }
+    }
+}
+
+// sj[row] for the local routes of token g: the route's slot j when the token
+// has exactly one local route (its combine is then a single term, which the
+// down GEMM's epilogue computes: down_combine_rows), else -1.  Padding rows
+// are not written.
+__device__ void single_slot_body(const int32_t *__restrict__ route_row, int32_t *__restrict__ sj, int K,
+                                 int64_t g) {
+    int n = 0, jj = -1;
+    for (int j = 0; j < K; ++j)
+        if (route_row[g * K + j] >= 0) ++n, jj = j;
+    for (int j = 0; j < K; ++j) {
+        const int32_t r = route_row[g * K + j];
+        if (r >= 0) sj[r] = n == 1 ? jj : -1;
     }
 }
 
