@@ -246,7 +246,9 @@ enum {
  * Without MOE_PERSISTENT and with chunk_rows == 0, a token with exactly one
  * local route has its output row written by the down GEMM's epilogue (the
  * combine's one-term sum, same fp32 product and bf16 rounding) and the
- * combine launch skips it; out is bitwise what the other paths write.
+ * combine launch skips it; out is bitwise what the other paths write.  The
+ * table of such rows (one int32 per row of capacity) is rebuilt by every
+ * call, so nothing an earlier call left in ws is read.
  * Xd may be NULL: the dispatch is then fused into the gate/up GEMM, whose
  * operand loads pull each row from X through phi ([MoK] section 2, pull
  * dispatch hidden behind the GEMM), and no dispatched copy is written; every
@@ -343,7 +345,8 @@ int moe_quantize_mx(const uint16_t *src, int64_t rows, int32_t K, uint8_t *q, ui
  * accumulates in fp32 and in its epilogue computes a = silu(h) * u and
  * quantizes it (codes Aq [cap][I], scales As [cap][I/32]); the down GEMM
  * multiplies the MX codes of a and W2 into Y (bf16 [cap][H]); the combine is
- * moe_combine's.
+ * moe_combine's, with the tokens that have one local route written by the
+ * down GEMM's epilogue (as in moe_layer_fwd).
  *   W13q, W13s  MX codes [L][2I][H] and scales [L][2I][H/32] of W13 (rows
  *               [0,I) gate, [I,2I) up), e.g. from moe_quantize_mx
  *   W2q, W2s    MX codes [L][H][I] and scales [L][H][I/32] of W2

@@ -78,7 +78,8 @@ __device__ __forceinline__ void ffn_down_tile(const FfnArgs &a, int mt, int nt, 
     KOp bk{w, w + 128ll * I, I};
     AccW<kFwdWM, kFwdWN> acc;
     gemm_mainloop_x<kFwdWM, kFwdWN, false, false>(ak, bk, I / 64, false, lds, acc);
-    epilogue_store_bf16_w<kFwdWM, kFwdWN>(acc, lds, a.Y + (int64_t)m0 * H + nt * 256, H, 256);
+    epilogue_store_bf16_comb<kFwdWM, kFwdWN>(acc, lds, a.Y + (int64_t)m0 * H + nt * 256, H, a.rc, m0, nt * 256,
+                                             lds + kGemmLds);
 }
 
 // One persistent pass over the tiles of rows [r0, r1) (multiples of 256).
@@ -185,6 +186,7 @@ struct MxFfnArgs {
     uint16_t *HU;      // nullable: bf16 [cap][2I], h then u (saved for the backward)
     uint16_t *Y;       // bf16 [cap][H]
     int L, H, I;
+    RowCombine rc;  // the down tiles' combine of single-route tokens (rc.out null: none)
 };
 
 __device__ __forceinline__ const uint16_t *as_u16(const uint8_t *p) { return reinterpret_cast<const uint16_t *>(p); }
@@ -224,7 +226,8 @@ __device__ __forceinline__ void mx_down_tile(const MxFfnArgs &a, int mt, int nt,
     const SOp bs{ws, ws + 128ll * (I / 32), I / 32, nullptr, nullptr, 0};
     AccW<kFwdWM, kFwdWN> acc;
     gemm_mainloop_mx<kFwdWM, kFwdWN, SG>(ak, bk, as, bs, I / 128, false, lds, acc);
-    epilogue_store_bf16_w<kFwdWM, kFwdWN>(acc, lds, a.Y + (int64_t)m0 * H + nt * 256, H, 256);
+    epilogue_store_bf16_comb<kFwdWM, kFwdWN>(acc, lds, a.Y + (int64_t)m0 * H + nt * 256, H, a.rc, m0, nt * 256,
+                                             lds + kGemmLds);
 }
 
 template <int SG>

@@ -65,10 +65,15 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *Y, const int32_
                  tpp, tstride, S, skip_single != 0);
 }
 
-// sj (see single_slot_body) for every token of one table.
-__global__ __launch_bounds__(256) void k_single_slot(const int32_t *route_row, int32_t *sj, int K, int64_t ntok) {
-    for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < ntok; g += (int64_t)gridDim.x * blockDim.x)
-        single_slot_body(route_row, sj, K, g);
+// sq (see single_route_body) for every token of one table, -1 on its
+// padding rows.
+__global__ __launch_bounds__(256) void k_single_route(const int32_t *route_row, const moe_src *phi,
+                                                      const int32_t *npad_ptr, int32_t *sq, int K, int64_t ntok) {
+    const int64_t npad = *npad_ptr, stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < ntok || i < npad; i += stride) {
+        if (i < ntok) single_route_body(route_row, sq, K, i);
+        if (i < npad) single_route_pad(phi, sq, i);
+    }
 }
 
 // The shared expert's table: row g < ntok pulls token g (partition g / Np,
@@ -315,9 +320,9 @@ int64_t sched_ws_bytes(const moe_desc *d) {
     return sched_ids8_offset(d) + ids;
 }
 
-// The forward's per-row slot table (k_single_slot): one int32 per row of
+// The forward's per-row route table (k_single_route): one int32 per row of
 // capacity, after the schedule's workspace.
-int64_t single_slot_bytes(const moe_desc *d) { return align256(cap_rows(d) * 4); }
+int64_t single_route_bytes(const moe_desc *d) { return align256(cap_rows(d) * 4); }
 
 int bwd_nparts(const moe_desc *d) { return (d->I + 255) / 256; }  // one dw partial per 256-column tile
 
@@ -480,6 +485,19 @@ int launch_combine(const moe_desc *d, const uint16_t *Y, const int32_t *route_ro
     return launch_status();
 }
 
+// The per-row route table of the tokens with one local route (sq, in the
+// workspace after the schedule's part) and the epilogue arguments that use it.
+int launch_single_route(const moe_desc *d, const int32_t *route_row, const moe_src *phi, const int32_t *seg_off,
+                        const float *w, uint16_t *out, char *ws, hipStream_t s, RowCombine &rcomb) {
+    int32_t *sq = reinterpret_cast<int32_t *>(ws);
+    const int64_t ntok = (int64_t)d->P * d->Np, n = std::max<int64_t>(ntok, cap_rows(d));
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 4ll * device_cus()));
+    TraceScope tr("single_route", s);
+    hipLaunchKernelGGL(k_single_route, dim3(grid), dim3(256), 0, s, route_row, phi, seg_off + d->L, sq, d->K, ntok);
+    rcomb = RowCombine{out, sq, w, d->K};
+    return launch_status();
+}
+
 FfnArgs make_ffn_args(const moe_desc *d, const uint16_t *Xd, const uint16_t *W13, const uint16_t *W2,
                       const int32_t *seg_off, uint16_t *HU, uint16_t *A, uint16_t *Y, int32_t chunk_rows,
                       uint32_t *bar, const uint16_t *X = nullptr, const moe_src *phi = nullptr) {
@@ -499,7 +517,7 @@ FfnArgs make_ffn_args(const moe_desc *d, const uint16_t *Xd, const uint16_t *W13
     a.I = d->I;
     a.chunk_rows = chunk_rows;
     a.bar = bar;
-    a.rc = RowCombine{nullptr, nullptr, nullptr, nullptr, 0, 0};
+    a.rc = RowCombine{nullptr, nullptr, nullptr, 0};
     return a;
 }
 
@@ -615,7 +633,7 @@ int64_t moe_workspace_bytes(const moe_desc *d, int op) {
         case MOE_OP_LAYER_FWD: {
             moe_desc one = *d;
             one.num_batches = 1;
-            return kBarrierBytes + sched_ws_bytes(&one) + single_slot_bytes(d);
+            return kBarrierBytes + sched_ws_bytes(&one) + single_route_bytes(d);
         }
         case MOE_OP_LAYER_BWD: return bwd_ws_bytes(d);
         case MOE_OP_LAYER_BWD_MX: return mx_bwd_ws_bytes(d);
@@ -782,15 +800,8 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
     // combined in the down GEMM's epilogue and the combine launch skips them
     const bool fused = chunk_rows <= 0;
     if (fused) {
-        int32_t *sj = reinterpret_cast<int32_t *>(sched_ws + sched_ws_bytes(&one));
-        const int64_t ntok = (int64_t)d->P * d->Np;
-        {
-            TraceScope tr("single_slot", s);
-            const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((ntok + 255) / 256, 4ll * device_cus()));
-            hipLaunchKernelGGL(k_single_slot, dim3(grid), dim3(256), 0, s, route_row, sj, d->K, ntok);
-        }
-        if (launch_status() != MOE_OK) return MOE_EHIP;
-        a.rc = RowCombine{out, phi, sj, w, d->K, d->Np};
+        rc = launch_single_route(d, route_row, phi, seg_off, w, out, sched_ws + sched_ws_bytes(&one), s, a.rc);
+        if (rc != MOE_OK) return rc;
     }
     rc = launch_ffn(d, a, s);
     if (rc != MOE_OK) return rc;
@@ -1080,6 +1091,9 @@ int moe_layer_fwd_mx(const moe_desc *d, const int32_t *routes, const float *w, c
     a.L = d->L;
     a.H = d->H;
     a.I = d->I;
+    // the MX down tiles write the outputs of the tokens with one local route
+    rc = launch_single_route(d, route_row, phi, seg_off, w, out, sched_ws + sched_ws_bytes(&one), s, a.rc);
+    if (rc != MOE_OK) return rc;
     const int grid = gemm_grid();
     {
         TraceScope tr("mx_gateup", s);
@@ -1098,7 +1112,7 @@ int moe_layer_fwd_mx(const moe_desc *d, const int32_t *routes, const float *w, c
             hipLaunchKernelGGL(k_mx_down<1>, dim3(grid), dim3(kFwdThreads), 0, s, a);
     }
     if (launch_status() != MOE_OK) return MOE_EHIP;
-    return launch_combine(d, Y, route_row, w, out, s, "combine");
+    return launch_combine(d, Y, route_row, w, out, s, "combine", 0, nullptr, true);
 }
 
 }  // extern "C"

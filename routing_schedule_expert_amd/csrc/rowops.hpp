@@ -110,7 +110,7 @@ __device__ void gather_rows_scaled_body(const uint16_t *__restrict__ src, const 
 // kernel (eight waves per CU) takes U = kRowUnrollWide, a whole 7,168-wide
 // row per wave, so the CU still keeps enough row loads in flight.
 // skip_single: tokens with exactly one local route are left alone (the down
-// GEMM's epilogue wrote them: down_combine_rows).
+// GEMM's epilogue wrote them: RowCombine).
 template <int U = kRowUnroll>
 __device__ void combine_body(const uint16_t *__restrict__ Y, const int32_t *__restrict__ route_row,
                              const float *__restrict__ w, uint16_t *__restrict__ out, int K, int H,
@@ -179,19 +179,26 @@ __device__ void combine_body(const uint16_t *__restrict__ Y, const int32_t *__re
     }
 }
 
-// sj[row] for the local routes of token g: the route's slot j when the token
-// has exactly one local route (its combine is then a single term, which the
-// down GEMM's epilogue computes: down_combine_rows), else -1.  Padding rows
-// are not written.
-__device__ void single_slot_body(const int32_t *__restrict__ route_row, int32_t *__restrict__ sj, int K,
-                                 int64_t g) {
+// sq[row] for the local routes of token g: the route's index g K + j when
+// the token has exactly one local route (its combine is then a single term,
+// which the down GEMM's epilogue computes: RowCombine), else -1.  Padding
+// rows are marked by single_route_pad.
+__device__ void single_route_body(const int32_t *__restrict__ route_row, int32_t *__restrict__ sq, int K,
+                                  int64_t g) {
     int n = 0, jj = -1;
     for (int j = 0; j < K; ++j)
         if (route_row[g * K + j] >= 0) ++n, jj = j;
     for (int j = 0; j < K; ++j) {
         const int32_t r = route_row[g * K + j];
-        if (r >= 0) sj[r] = n == 1 ? jj : -1;
+        if (r >= 0) sq[r] = n == 1 ? (int32_t)(g * K + jj) : -1;
     }
+}
+
+// sq[row] = -1 for a padding row (phi partition < 0) below seg_off[L]: such
+// a row belongs to no token.
+__device__ __forceinline__ void single_route_pad(const moe_src *__restrict__ phi, int32_t *__restrict__ sq,
+                                                 int64_t row) {
+    if (phi[row].part < 0) sq[row] = -1;
 }
 
 // wrow[i] = router weight of the route placed at row i (0 on padding rows).

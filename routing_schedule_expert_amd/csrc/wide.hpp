@@ -196,19 +196,6 @@ __device__ __forceinline__ void wide_copy_out(const char *st, int rows, uint16_t
     }
 }
 
-// The combine of the tokens that have exactly one local route, done where
-// their one output row is written: out[g] = bf16(w_gj * Y[row]) for the
-// route (g, j) at the row, the same single fp32 product and rounding as the
-// combine's one-term sum (combine_body starts from 0 and adds w Y with one
-// fma).  out == nullptr: none.
-struct RowCombine {
-    uint16_t *out;       // [tokens][ld]
-    const moe_src *phi;  // row -> (partition, token); partition < 0 on padding rows
-    const int32_t *sj;   // row -> the route's slot if its token has one local route, else -1
-    const float *w;      // [tokens][K]
-    int K, Np;
-};
-
 // Rows [128 pass, 128 pass + 128) of the staged tile that belong to such
 // tokens, to out (columns [n0, n0 + NC)); ig / iw: each tile row's token
 // (-1: none) and weight.
@@ -222,23 +209,18 @@ __device__ __forceinline__ void wide_copy_combine(const char *st, const int *ig,
         if (g < 0) continue;
         const float wv = iw[128 * pass + row];
         const u32x4 v = *reinterpret_cast<const u32x4 *>(st + row * (NC * 2) + (c % CPR) * 16);
-        u32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            o[e] = pack_bf2(fmaf(wv, __uint_as_float(v[e] << 16), 0.f),
-                            fmaf(wv, __uint_as_float(v[e] & 0xffff0000u), 0.f));
-        *reinterpret_cast<u32x4 *>(out + (int64_t)g * ld + n0 + (c % CPR) * 8) = o;
+        *reinterpret_cast<u32x4 *>(out + (int64_t)g * ld + n0 + (c % CPR) * 8) = scale_bf16x8(v, wv);
     }
 }
 
 // Plain bf16 store of the 256 x BN tile, in two passes of 128 rows; with
 // rc.out, also the outputs of the tile's rows whose tokens have one local
 // route (rows m0 ..., columns n0 ...).  Their tokens and weights are looked up
-// during the first pass (the table lookups under the staging, the weight under
-// the first copy) and kept past the staged rows in LDS.
+// during the first pass (the table entries under the staging, the weights
+// under the first copy) and kept past the staged rows in LDS.
 template <int BN>
 __device__ __forceinline__ void wide_epilogue_store(AccWide<BN> &acc, char *lds, uint16_t *dst, int64_t ld,
-                                                    const RowCombine &rc, int m0, int n0) {
+                                                    const RowCombine &rc, int64_t m0, int n0) {
     constexpr int NI = BN / 64;
     const int t = opaque_tid(), wave = t >> 6, lane = t & 63, wm = wave >> 1, wn = wave & 1;
     uint16_t *st = reinterpret_cast<uint16_t *>(lds);  // [128][BN]
@@ -246,14 +228,8 @@ __device__ __forceinline__ void wide_epilogue_store(AccWide<BN> &acc, char *lds,
     float *iw = reinterpret_cast<float *>(ig + 256);
     const int r0 = (wm & 1) * 64 + 4 * (lane >> 5), c0 = wn * (NI * 32) + (lane & 31);
     const bool comb = rc.out != nullptr;
-    uint2 e{0u, 0u};
-    int32_t j = -1;
-    if (comb && t < 256) {
-        e = reinterpret_cast<const uint2 *>(rc.phi)[m0 + t];
-        j = rc.sj[m0 + t];
-    }
-    int64_t g = -1;
-    float wv = 0.f;
+    RowCombineRow rr;
+    if (comb && t < 256) rr.load(rc, m0 + t);
     for (int pass = 0; pass < 2; ++pass) {
         if (pass) __syncthreads();
         if ((wm >> 1) == pass) {  // rows [128 pass, 128 pass + 128)
@@ -267,17 +243,14 @@ __device__ __forceinline__ void wide_epilogue_store(AccWide<BN> &acc, char *lds,
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (comb && pass == 0 && t < 256 && (int32_t)e.x >= 0 && j >= 0) {
-            g = (int64_t)(int32_t)e.x * rc.Np + (int32_t)e.y;
-            wv = rc.w[g * rc.K + j];
-        }
+        if (comb && pass == 0 && t < 256) rr.resolve(rc);
         __syncthreads();
         wide_copy_out<BN>(lds, 128, dst + (int64_t)pass * 128 * ld, ld);
         if (comb) {
             if (pass == 0) {
                 if (t < 256) {
-                    ig[t] = (int)g;
-                    iw[t] = wv;
+                    ig[t] = rr.g;
+                    iw[t] = rr.wv;
                 }
                 __syncthreads();
             }

@@ -34,8 +34,10 @@ class Layer:
         self.W2 = up_bf16(self.h["W2"])
         self.dOut = up_bf16(self.h["dOut"]) if grad else None
 
-    def fwd(self, flags=0, chunk_rows=0, save_hu=True, save_xd=True):
+    def fwd(self, flags=0, chunk_rows=0, save_hu=True, save_xd=True, ws_fill=None):
         b = ops.alloc_fwd(self.d, dev(), save_hu=save_hu, save_xd=save_xd)
+        if ws_fill is not None:  # what an earlier call could have left there
+            b.ws.view(torch.int32).fill_(ws_fill)
         ops.layer_fwd(self.d, self.routes, self.w, self.X, self.W13, self.W2, b, flags=flags, chunk_rows=chunk_rows)
         torch.cuda.synchronize()
         return b
@@ -126,8 +128,19 @@ def test_forward_large_experts():
     check_bwd_full(lay, lay.bwd(b))
 
 
+def local_route_counts(lay):
+    r = lay.h["routes"].reshape(-1, lay.K).astype(np.int64)
+    return ((r >= lay.base) & (r < lay.base + lay.L)).sum(axis=1)
+
+
 def test_forward_paths_agree_bitwise():
+    """The multi-launch forward (whose down epilogue writes the outputs of the
+    tokens with one local route) against the persistent and chunked paths
+    (whose combine writes every token), on tokens with 0, 1 and several local
+    routes."""
     lay = Layer(4, 4, 900, 16, 4, 8, 512, 384, routing="uniform")
+    n = local_route_counts(lay)
+    assert (n == 0).any() and (n == 1).any() and (n >= 2).any()
     ref = lay.fwd()
     outs = [ref]
     for flags, chunk in ((ops.MOE_PERSISTENT, 0), (0, 256), (ops.MOE_PERSISTENT, 512), (0, 1024)):
@@ -139,6 +152,38 @@ def test_forward_paths_agree_bitwise():
         assert digest(b.out) == digest(ref.out)
         assert digest(b.Y[:npad], b.A[:npad], b.HU[:npad]) == digest(ref.Y[:npad], ref.A[:npad], ref.HU[:npad])
         assert digest(b.phi[:npad], b.route_row, b.seg_off) == digest(ref.phi[:npad], ref.route_row, ref.seg_off)
+
+
+def test_single_route_tokens():
+    """Every token with exactly one local route (top-1 routing): the
+    multi-launch forward writes every routed token's output from the down
+    GEMM's epilogue (one partly padded M tile per expert, two wide column
+    tiles and a narrow one; tokens routed elsewhere stay 0 from the combine) and
+    must match the oracle and, bitwise, the persistent path."""
+    lay = Layer(15, 3, 211, 6, 1, 4, 1024, 256, routing="uniform")
+    n = local_route_counts(lay)
+    assert (n == 1).any() and (n == 0).any() and n.max() == 1
+    b = lay.fwd()
+    check_fwd_full(lay, b)
+    p = lay.fwd(flags=ops.MOE_PERSISTENT)
+    assert digest(p.out) == digest(b.out)
+
+
+@pytest.mark.parametrize("fill", [0, 2, -5])
+def test_stale_workspace(fill):
+    """The forward must not depend on what the workspace held before the call:
+    filled with int32 words that name routes of tokens 0 and 1 (0, K), or
+    with a negative word, the multi-launch forward (whose down epilogue reads
+    a per-row table kept there, padding rows included) still matches the
+    oracle and, bitwise, the persistent path."""
+    print(f"[layer] stale workspace words {fill}", flush=True)
+    lay = Layer(16, 2, 300, 8, 2, 4, 256, 128, routing="uniform")
+    ref = lay.fwd(flags=ops.MOE_PERSISTENT)
+    assert int(ref.seg_off[-1]) > int((local_route_counts(lay)).sum())  # padding rows present
+    b = lay.fwd(ws_fill=fill)
+    assert digest(b.out) == digest(ref.out)
+    if fill == 0:
+        check_fwd_full(lay, b)
 
 
 @pytest.mark.parametrize("flags,chunk,save_xd", [(ops.MOE_PERSISTENT, 0, True), (0, 256, True),

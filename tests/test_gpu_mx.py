@@ -201,8 +201,10 @@ class MxLayer:
         self.W13q, self.W13s = ops.quantize_mx(up_bf16(self.h["W13"]))
         self.W2q, self.W2s = ops.quantize_mx(up_bf16(self.h["W2"]))
 
-    def fwd(self):
+    def fwd(self, ws_fill=None):
         b = ops.alloc_fwd_mx(self.d, dev())
+        if ws_fill is not None:  # what an earlier call could have left there
+            b.ws.view(torch.int32).fill_(ws_fill)
         ops.layer_fwd_mx(self.d, self.routes, self.w, self.X, self.W13q, self.W13s, self.W2q, self.W2s, b)
         torch.cuda.synchronize()
         return b
@@ -281,6 +283,20 @@ def test_mx_repeat_bitwise():
     assert torch.equal(a.out, b.out)
     assert torch.equal(a.Y[:npad], b.Y[:npad]) and torch.equal(a.Aq[:npad], b.Aq[:npad])
     assert torch.equal(a.As[:npad], b.As[:npad])
+
+
+def test_mx_stale_workspace():
+    """The MX down tiles write the outputs of single-route tokens from a
+    per-row table in the workspace: a workspace filled beforehand with words
+    that name routes of tokens 0 and 1 (0 and K) must not change the output
+    (bitwise a fresh workspace's, and within the oracle's bound)."""
+    lay = MxLayer(9, 2, 300, 8, 2, 4, 256, 128, routing="uniform")
+    ref = lay.fwd()
+    for fill in (0, lay.K):
+        print(f"[mx] stale workspace words {fill}", flush=True)
+        b = lay.fwd(ws_fill=fill)
+        assert torch.equal(b.out, ref.out)
+    check_mx_full(lay, b)
 
 
 def test_mx_kimi_sampled():
