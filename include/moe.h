@@ -247,8 +247,11 @@ enum {
  * local route has its output row written by the down GEMM's epilogue (the
  * combine's one-term sum, same fp32 product and bf16 rounding) and the
  * combine launch skips it; out is bitwise what the other paths write.  The
- * table of such rows (one int32 per row of capacity) is rebuilt by every
- * call, so nothing an earlier call left in ws is read.
+ * row of Y of such a route is then not written (nothing else reads it: the
+ * backward takes HU and A), so Y holds the rows of tokens with two or more
+ * local routes and the padding rows; the persistent and chunked paths write
+ * every row.  The table of such rows (one int32 per row of capacity) is
+ * rebuilt by every call, so nothing an earlier call left in ws is read.
  * Xd may be NULL: the dispatch is then fused into the gate/up GEMM, whose
  * operand loads pull each row from X through phi ([MoK] section 2, pull
  * dispatch hidden behind the GEMM), and no dispatched copy is written; every
@@ -282,7 +285,7 @@ int moe_layer_fwd(const moe_desc *d, const int32_t *routes, const float *w, cons
  * calls that overlap on one GPU (different streams, or different host
  * threads, not ordered by the caller) race and give undefined results.
  */
-#define MOE_NOALLOC_SCRATCH_BYTES (4 << 20)
+#define MOE_NOALLOC_SCRATCH_BYTES (8 << 20)
 int moe_layer_fwd_noalloc(const moe_desc *d, const int32_t *routes, const float *w, const uint16_t *X,
                           const uint16_t *W13, const uint16_t *W2, int32_t *counts, int32_t *seg_off, moe_src *phi,
                           int32_t *route_row, uint16_t *Xd, uint16_t *HU, uint16_t *A, uint16_t *Y, uint16_t *out,
@@ -346,7 +349,7 @@ int moe_quantize_mx(const uint16_t *src, int64_t rows, int32_t K, uint8_t *q, ui
  * quantizes it (codes Aq [cap][I], scales As [cap][I/32]); the down GEMM
  * multiplies the MX codes of a and W2 into Y (bf16 [cap][H]); the combine is
  * moe_combine's, with the tokens that have one local route written by the
- * down GEMM's epilogue (as in moe_layer_fwd).
+ * down GEMM's epilogue and their rows of Y not written (as in moe_layer_fwd).
  *   W13q, W13s  MX codes [L][2I][H] and scales [L][2I][H/32] of W13 (rows
  *               [0,I) gate, [I,2I) up), e.g. from moe_quantize_mx
  *   W2q, W2s    MX codes [L][H][I] and scales [L][H][I/32] of W2

@@ -560,16 +560,51 @@ struct PairStageW {
     }
 };
 
+// The combine of the tokens that have exactly one local route, done where
+// their one output row is written: out[g] = bf16(w * Y[row]) for the route of
+// token g placed at the row.  That is the same single fp32 product and
+// rounding as the combine's one-term sum (combine_body starts from 0 and adds
+// w Y with one fma), so out is bitwise what the combine would write.
+// out == nullptr: none.
+struct RowCombine {
+    uint16_t *out;    // [tokens][ld]
+    const int2 *tab;  // row -> (token, bits of its weight) if the token has one local route, else (-1, 0)
+};
+
+// One tile row's entry, loaded by thread t < 256 of the epilogue for row
+// m0 + t before the tile is staged and put in LDS (ig, iw) after.
+struct RowCombineRow {
+    int2 e = make_int2(-1, 0);
+    __device__ __forceinline__ void load(const RowCombine &rc, int64_t row) { e = rc.tab[row]; }
+    __device__ __forceinline__ void publish(int *ig, float *iw, int t) const {
+        ig[t] = e.x;
+        iw[t] = __int_as_float(e.y);
+    }
+};
+
+// 8 bf16 values times wv, each product rounded once to bf16.
+__device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float wv) {
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        o[e] = pack_bf2(fmaf(wv, __uint_as_float(v[e] << 16), 0.f), fmaf(wv, __uint_as_float(v[e] & 0xffff0000u), 0.f));
+    return o;
+}
+
 // Copy of a staged 256 x NC bf16 area (chunks placed as PairStageW writes
 // them, or in place with SWZ = false) to rows of dst; columns from ncols on
-// (a multiple of 8) are not written.  A thread keeps one 16-byte column chunk
+// (a multiple of 8) are not written.  With ig, a row whose ig[row] >= 0 goes
+// to out[ig[row]] (columns n0 ..., row stride ld) times iw[row] instead
+// (RowCombine).  A thread keeps one 16-byte column chunk
 // for all its rows and issues a batch of LDS reads before the batch's stores
 // (one LDS round trip per batch, not per chunk).  tt is the thread index
 // passed through an empty asm by the caller: the addresses, the same for
 // every tile, are then not hoisted out of the tile loop to stay live (and
 // spill) across the next tile's K loop.
 template <int NC, int THREADS, bool SWZ = true>
-__device__ __forceinline__ void copy_staged(const char *area, uint16_t *dst, int64_t ld, int ncols, int tt) {
+__device__ __forceinline__ void copy_staged(const char *area, uint16_t *dst, int64_t ld, int ncols, int tt,
+                                            const int *ig = nullptr, const float *iw = nullptr,
+                                            uint16_t *out = nullptr, int n0 = 0) {
     constexpr int CPR = NC / 8, RSTEP = THREADS / CPR, kIt = 256 / RSTEP, kBatch = 8;
     static_assert(kIt % kBatch == 0, "whole batches");
     const int q = tt % CPR, r0 = tt / CPR;
@@ -584,66 +619,15 @@ __device__ __forceinline__ void copy_staged(const char *area, uint16_t *dst, int
         }
         if (q * 8 < ncols) {
 #pragma unroll
-            for (int i = 0; i < kBatch; ++i)
-                *reinterpret_cast<u32x4 *>(dst + (int64_t)(r0 + (b + i) * RSTEP) * ld + q * 8) = v[i];
+            for (int i = 0; i < kBatch; ++i) {
+                const int row = r0 + (b + i) * RSTEP;
+                const int g = ig ? ig[row] : -1;
+                if (g < 0)
+                    *reinterpret_cast<u32x4 *>(dst + (int64_t)row * ld + q * 8) = v[i];
+                else
+                    *reinterpret_cast<u32x4 *>(out + (int64_t)g * ld + n0 + q * 8) = scale_bf16x8(v[i], iw[row]);
+            }
         }
-    }
-}
-
-// The combine of the tokens that have exactly one local route, done where
-// their one output row is written: out[g] = bf16(w_q * Y[row]) for the route
-// q = g K + j placed at the row.  That is the same single fp32 product and
-// rounding as the combine's one-term sum (combine_body starts from 0 and adds
-// w Y with one fma), so out is bitwise what the combine would write.
-// out == nullptr: none.
-struct RowCombine {
-    uint16_t *out;      // [tokens][ld]
-    const int32_t *sq;  // row -> its route's index g K + j if token g has one local route, else -1
-    const float *w;     // [tokens][K]
-    int K;
-};
-
-// One tile row's lookup, kept by thread t < 256 of the epilogue for row
-// m0 + t: the table entry is loaded before the tile is staged, the weight
-// once the entry is in (before the tile's copy), and both go to LDS (ig, iw)
-// after the copy.
-struct RowCombineRow {
-    int32_t q = -1;
-    int g = -1;
-    float wv = 0.f;
-    __device__ __forceinline__ void load(const RowCombine &rc, int64_t row) { q = rc.sq[row]; }
-    __device__ __forceinline__ void resolve(const RowCombine &rc) {
-        if (q >= 0) {
-            g = q / rc.K;
-            wv = rc.w[q];
-        }
-    }
-};
-
-// 8 bf16 values times wv, each product rounded once to bf16.
-__device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float wv) {
-    u32x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        o[e] = pack_bf2(fmaf(wv, __uint_as_float(v[e] << 16), 0.f), fmaf(wv, __uint_as_float(v[e] & 0xffff0000u), 0.f));
-    return o;
-}
-
-// The rows of a staged 256 x NC area (placed as copy_staged reads them) whose
-// token ig[row] >= 0, times iw[row], to out[ig[row]][n0 ...].
-template <int NC, int THREADS>
-__device__ __forceinline__ void copy_staged_combine(const char *area, const int *ig, const float *iw, uint16_t *out,
-                                                    int64_t ld, int n0, int tt) {
-    constexpr int CPR = NC / 8, RSTEP = THREADS / CPR, kIt = 256 / RSTEP;
-    const int q = tt % CPR, r0 = tt / CPR;
-#pragma unroll 4
-    for (int i = 0; i < kIt; ++i) {
-        const int row = r0 + i * RSTEP;
-        const int g = ig[row];
-        if (g < 0) continue;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(area + (row >> 7) * kStageBytes + (row & 127) * (NC * 2) +
-                                                         ((q ^ (4 * stage_swz(row))) << 4));
-        *reinterpret_cast<u32x4 *>(out + (int64_t)g * ld + n0 + q * 8) = scale_bf16x8(v, iw[row]);
     }
 }
 
@@ -709,9 +693,9 @@ __device__ __forceinline__ void epilogue_store_bf16_w(AccW<WM, WN> &acc, char *l
 }
 
 // epilogue_store_bf16_w of a whole 256 x 256 tile at rows m0 ..., columns
-// n0 ... of the row buffer, plus the outputs of its single-route tokens
-// (RowCombine); tab: 2 KiB of LDS past the staged tile for their tokens and
-// weights.
+// n0 ... of the row buffer, except that the rows of single-route tokens go to
+// those tokens' outputs (RowCombine) instead of dst; tab: 2 KiB of LDS past
+// the staged tile for their tokens and weights.
 template <int WM, int WN>
 __device__ __forceinline__ void epilogue_store_bf16_comb(AccW<WM, WN> &acc, char *lds, uint16_t *dst, int64_t ld,
                                                          const RowCombine &rc, int64_t m0, int n0, char *tab) {
@@ -730,19 +714,14 @@ __device__ __forceinline__ void epilogue_store_bf16_comb(AccW<WM, WN> &acc, char
             for (int e = 0; e < 16; e += 2) sg.put2(mi, e, ni * 32, acc[mi][ni][e], acc[mi][ni][e + 1]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (comb && t < 256) rr.resolve(rc);
+    int *ig = reinterpret_cast<int *>(tab);
+    float *iw = reinterpret_cast<float *>(tab + 1024);
+    if (comb && t < 256) rr.publish(ig, iw, t);
     __syncthreads();
-    copy_staged<256, WG::THREADS>(lds, dst, ld, 256, opaque_tid());
-    if (comb) {
-        int *ig = reinterpret_cast<int *>(tab);
-        float *iw = reinterpret_cast<float *>(tab + 1024);
-        if (t < 256) {
-            ig[t] = rr.g;
-            iw[t] = rr.wv;
-        }
-        __syncthreads();
-        copy_staged_combine<256, WG::THREADS>(lds, ig, iw, rc.out, ld, n0, opaque_tid());
-    }
+    if (comb)
+        copy_staged<256, WG::THREADS>(lds, dst, ld, 256, opaque_tid(), ig, iw, rc.out, n0);
+    else
+        copy_staged<256, WG::THREADS>(lds, dst, ld, 256, opaque_tid());
 }
 
 // fp32 tile store of the rows < mvalid and columns < nvalid; with accumulate

@@ -65,14 +65,14 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *Y, const int32_
                  tpp, tstride, S, skip_single != 0);
 }
 
-// sq (see single_route_body) for every token of one table, -1 on its
+// tab (see single_route_body) for every token of one table, (-1, 0) on its
 // padding rows.
-__global__ __launch_bounds__(256) void k_single_route(const int32_t *route_row, const moe_src *phi,
-                                                      const int32_t *npad_ptr, int32_t *sq, int K, int64_t ntok) {
+__global__ __launch_bounds__(256) void k_single_route(const int32_t *route_row, const float *w, const moe_src *phi,
+                                                      const int32_t *npad_ptr, int2 *tab, int K, int64_t ntok) {
     const int64_t npad = *npad_ptr, stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < ntok || i < npad; i += stride) {
-        if (i < ntok) single_route_body(route_row, sq, K, i);
-        if (i < npad) single_route_pad(phi, sq, i);
+        if (i < ntok) single_route_body(route_row, w, tab, K, i);
+        if (i < npad) single_route_pad(phi, tab, i);
     }
 }
 
@@ -320,9 +320,9 @@ int64_t sched_ws_bytes(const moe_desc *d) {
     return sched_ids8_offset(d) + ids;
 }
 
-// The forward's per-row route table (k_single_route): one int32 per row of
-// capacity, after the schedule's workspace.
-int64_t single_route_bytes(const moe_desc *d) { return align256(cap_rows(d) * 4); }
+// The forward's per-row table of single-route tokens (k_single_route): 8
+// bytes per row of capacity, after the schedule's workspace.
+int64_t single_route_bytes(const moe_desc *d) { return align256(cap_rows(d) * 8); }
 
 int bwd_nparts(const moe_desc *d) { return (d->I + 255) / 256; }  // one dw partial per 256-column tile
 
@@ -485,16 +485,17 @@ int launch_combine(const moe_desc *d, const uint16_t *Y, const int32_t *route_ro
     return launch_status();
 }
 
-// The per-row route table of the tokens with one local route (sq, in the
-// workspace after the schedule's part) and the epilogue arguments that use it.
+// The per-row table of the tokens with one local route (in the workspace
+// after the schedule's part) and the epilogue arguments that use it.
 int launch_single_route(const moe_desc *d, const int32_t *route_row, const moe_src *phi, const int32_t *seg_off,
                         const float *w, uint16_t *out, char *ws, hipStream_t s, RowCombine &rcomb) {
-    int32_t *sq = reinterpret_cast<int32_t *>(ws);
+    int2 *tab = reinterpret_cast<int2 *>(ws);
     const int64_t ntok = (int64_t)d->P * d->Np, n = std::max<int64_t>(ntok, cap_rows(d));
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 4ll * device_cus()));
     TraceScope tr("single_route", s);
-    hipLaunchKernelGGL(k_single_route, dim3(grid), dim3(256), 0, s, route_row, phi, seg_off + d->L, sq, d->K, ntok);
-    rcomb = RowCombine{out, sq, w, d->K};
+    hipLaunchKernelGGL(k_single_route, dim3(grid), dim3(256), 0, s, route_row, w, phi, seg_off + d->L, tab, d->K,
+                       ntok);
+    rcomb = RowCombine{out, tab};
     return launch_status();
 }
 
@@ -517,7 +518,7 @@ FfnArgs make_ffn_args(const moe_desc *d, const uint16_t *Xd, const uint16_t *W13
     a.I = d->I;
     a.chunk_rows = chunk_rows;
     a.bar = bar;
-    a.rc = RowCombine{nullptr, nullptr, nullptr, 0};
+    a.rc = RowCombine{nullptr, nullptr};
     return a;
 }
 

@@ -179,26 +179,27 @@ __device__ void combine_body(const uint16_t *__restrict__ Y, const int32_t *__re
     }
 }
 
-// sq[row] for the local routes of token g: the route's index g K + j when
-// the token has exactly one local route (its combine is then a single term,
-// which the down GEMM's epilogue computes: RowCombine), else -1.  Padding
-// rows are marked by single_route_pad.
-__device__ void single_route_body(const int32_t *__restrict__ route_row, int32_t *__restrict__ sq, int K,
-                                  int64_t g) {
+// tab[row] for the local routes of token g: (g, bits of w_gj) when the token
+// has exactly one local route, at slot j (its combine is then a single term,
+// which the down GEMM's epilogue computes: RowCombine), else (-1, 0).
+// Padding rows are marked by single_route_pad.
+__device__ void single_route_body(const int32_t *__restrict__ route_row, const float *__restrict__ w,
+                                  int2 *__restrict__ tab, int K, int64_t g) {
     int n = 0, jj = -1;
     for (int j = 0; j < K; ++j)
         if (route_row[g * K + j] >= 0) ++n, jj = j;
+    const int2 e = n == 1 ? make_int2((int)g, __float_as_int(w[g * K + jj])) : make_int2(-1, 0);
     for (int j = 0; j < K; ++j) {
         const int32_t r = route_row[g * K + j];
-        if (r >= 0) sq[r] = n == 1 ? (int32_t)(g * K + jj) : -1;
+        if (r >= 0) tab[r] = e;
     }
 }
 
-// sq[row] = -1 for a padding row (phi partition < 0) below seg_off[L]: such
-// a row belongs to no token.
-__device__ __forceinline__ void single_route_pad(const moe_src *__restrict__ phi, int32_t *__restrict__ sq,
+// tab[row] = (-1, 0) for a padding row (phi partition < 0) below seg_off[L]:
+// such a row belongs to no token.
+__device__ __forceinline__ void single_route_pad(const moe_src *__restrict__ phi, int2 *__restrict__ tab,
                                                  int64_t row) {
-    if (phi[row].part < 0) sq[row] = -1;
+    if (phi[row].part < 0) tab[row] = make_int2(-1, 0);
 }
 
 // wrow[i] = router weight of the route placed at row i (0 on padding rows).

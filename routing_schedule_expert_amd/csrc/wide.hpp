@@ -177,8 +177,12 @@ __device__ __forceinline__ void wide_mainloop(const uint16_t *a, int64_t lda, co
 // ---------------------------------------------------------------------------
 
 // Copy `rows` staged rows of NC bf16 (row stride NC) to dst (row stride ld).
+// With ig, a row whose ig[row] >= 0 goes to out[ig[row]] (columns n0 ...,
+// row stride ld) times iw[row] instead (RowCombine).
 template <int NC>
-__device__ __forceinline__ void wide_copy_out(const char *st, int rows, uint16_t *dst, int64_t ld) {
+__device__ __forceinline__ void wide_copy_out(const char *st, int rows, uint16_t *dst, int64_t ld,
+                                              const int *ig = nullptr, const float *iw = nullptr,
+                                              uint16_t *out = nullptr, int n0 = 0) {
     constexpr int CPR = NC / 8;
     const int total = rows * CPR;
     for (int c0 = opaque_tid(); c0 < total; c0 += 4 * kWideThreads) {
@@ -191,33 +195,23 @@ __device__ __forceinline__ void wide_copy_out(const char *st, int rows, uint16_t
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = c0 + i * kWideThreads;
-            if (c < total) *reinterpret_cast<u32x4 *>(dst + (int64_t)(c / CPR) * ld + (c % CPR) * 8) = v[i];
+            if (c >= total) continue;
+            const int g = ig ? ig[c / CPR] : -1;
+            if (g < 0)
+                *reinterpret_cast<u32x4 *>(dst + (int64_t)(c / CPR) * ld + (c % CPR) * 8) = v[i];
+            else
+                *reinterpret_cast<u32x4 *>(out + (int64_t)g * ld + n0 + (c % CPR) * 8) =
+                    scale_bf16x8(v[i], iw[c / CPR]);
         }
     }
 }
 
-// Rows [128 pass, 128 pass + 128) of the staged tile that belong to such
-// tokens, to out (columns [n0, n0 + NC)); ig / iw: each tile row's token
-// (-1: none) and weight.
-template <int NC>
-__device__ __forceinline__ void wide_copy_combine(const char *st, const int *ig, const float *iw, int pass,
-                                                  uint16_t *out, int64_t ld, int n0) {
-    constexpr int CPR = NC / 8;
-    for (int c = opaque_tid(); c < 128 * CPR; c += kWideThreads) {
-        const int row = c / CPR;
-        const int g = ig[128 * pass + row];
-        if (g < 0) continue;
-        const float wv = iw[128 * pass + row];
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(st + row * (NC * 2) + (c % CPR) * 16);
-        *reinterpret_cast<u32x4 *>(out + (int64_t)g * ld + n0 + (c % CPR) * 8) = scale_bf16x8(v, wv);
-    }
-}
-
-// Plain bf16 store of the 256 x BN tile, in two passes of 128 rows; with
-// rc.out, also the outputs of the tile's rows whose tokens have one local
-// route (rows m0 ..., columns n0 ...).  Their tokens and weights are looked up
-// during the first pass (the table entries under the staging, the weights
-// under the first copy) and kept past the staged rows in LDS.
+// Plain bf16 store of the 256 x BN tile, in two passes of 128 rows.  With
+// rc.out, the rows whose tokens have one local route (rows m0 ..., columns
+// n0 ...) go to those tokens' outputs instead (times the router weight), and
+// their rows of dst are not written: nothing else reads them.  Each row's
+// token and weight are loaded before the first pass is staged and kept past
+// the staged rows in LDS.
 template <int BN>
 __device__ __forceinline__ void wide_epilogue_store(AccWide<BN> &acc, char *lds, uint16_t *dst, int64_t ld,
                                                     const RowCombine &rc, int64_t m0, int n0) {
@@ -243,19 +237,13 @@ __device__ __forceinline__ void wide_epilogue_store(AccWide<BN> &acc, char *lds,
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (comb && pass == 0 && t < 256) rr.resolve(rc);
+        if (comb && pass == 0 && t < 256) rr.publish(ig, iw, t);
         __syncthreads();
-        wide_copy_out<BN>(lds, 128, dst + (int64_t)pass * 128 * ld, ld);
-        if (comb) {
-            if (pass == 0) {
-                if (t < 256) {
-                    ig[t] = rr.g;
-                    iw[t] = rr.wv;
-                }
-                __syncthreads();
-            }
-            wide_copy_combine<BN>(lds, ig, iw, pass, rc.out, ld, n0);
-        }
+        uint16_t *d = dst + (int64_t)pass * 128 * ld;
+        if (comb)
+            wide_copy_out<BN>(lds, 128, d, ld, ig + 128 * pass, iw + 128 * pass, rc.out, n0);
+        else
+            wide_copy_out<BN>(lds, 128, d, ld);
     }
 }
 

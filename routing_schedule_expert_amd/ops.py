@@ -36,7 +36,7 @@ EXPORTED = (
     "moe_ring_capacity_rows", "moe_ring_workspace_bytes", "moe_layer_fwd_ring", "moe_layer_bwd_ring",
     "moe_layer_fwd_shared", "moe_layer_fwd_noalloc",
 )
-MOE_NOALLOC_SCRATCH_BYTES = 4 << 20
+MOE_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class MoeError(RuntimeError):

@@ -101,3 +101,47 @@ def gpu_schedule(routes: np.ndarray, L: int, base: int = 0, pad: int = 256, E: i
     inv = ops.read_ws_words(ws, ops.workspace_field(d, ops.MOE_OP_SCHEDULE, ops.MOE_WS_INVALID_IDS), nb)
     return {"counts": counts.cpu().numpy(), "seg_off": seg_off.cpu().numpy(), "phi": phi.cpu().numpy(),
             "route_row": route_row.cpu().numpy(), "cap": cap, "invalid": inv, "E": E}
+
+
+def local_counts(routes: np.ndarray, L: int, base: int) -> np.ndarray:
+    """Local routes of every token (routes [..., K], flattened over tokens)."""
+    r = np.asarray(routes).reshape(-1, np.asarray(routes).shape[-1]).astype(np.int64)
+    return ((r >= base) & (r < base + L)).sum(axis=1)
+
+
+def row_tokens(phi: np.ndarray, Np: int) -> np.ndarray:
+    """Token index p * Np + t of every table row (-1 on padding rows)."""
+    phi = np.asarray(phi).reshape(-1, 2).astype(np.int64)
+    return np.where(phi[:, 0] >= 0, phi[:, 0] * Np + phi[:, 1], -1)
+
+
+def fused_y_rows(routes: np.ndarray, L: int, base: int, phi: np.ndarray) -> np.ndarray:
+    """Mask over the table rows of phi: the rows of the routed Y that the fused
+    forward (separate launches without chunks, and the MX forward) writes.
+    Those are the padding rows and the rows of tokens with two or more local
+    routes; a token with one local route gets its output straight from the
+    down GEMM's epilogue, and its Y row is not written."""
+    Np = np.asarray(routes).shape[-2]
+    g = row_tokens(phi, Np)
+    n = local_counts(routes, L, base)
+    return (g < 0) | (n[np.maximum(g, 0)] >= 2)
+
+
+def on_dev_mask(mask: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(mask)).to(dev())
+
+
+def single_route_terms(routes: np.ndarray, w: np.ndarray, L: int, base: int, phi: np.ndarray, rows: np.ndarray):
+    """For table rows `rows`: whether the row's token has exactly one local
+    route (then the fused forward writes w * Y[row] straight to out[token]),
+    the token index, and the router weight of that route."""
+    routes = np.asarray(routes)
+    K, Np = routes.shape[-1], routes.shape[-2]
+    g = row_tokens(phi, Np)[rows]
+    r = routes.reshape(-1, K).astype(np.int64)
+    local = (r >= base) & (r < base + L)
+    gg = np.maximum(g, 0)
+    single = (g >= 0) & (local[gg].sum(axis=1) == 1)
+    j = np.argmax(local[gg], axis=1)
+    wt = np.asarray(w).reshape(-1, K)[gg, j].astype(np.float64)
+    return single, g, wt

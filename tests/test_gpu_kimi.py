@@ -19,7 +19,7 @@ import torch
 
 import oracle
 from routing_schedule_expert_amd import inputs, ops
-from tests.helpers import assert_elems, assert_rows, dev, f64, rel_l2
+from tests.helpers import assert_elems, assert_rows, dev, f64, fused_y_rows, on_dev_mask, rel_l2, single_route_terms
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -60,6 +60,23 @@ def kimi_fwd():
     return k, b
 
 
+def check_routed_rows(label, k, b, s, rows, ref):
+    """HU and A of sampled table rows vs the oracle; Y where the forward
+    writes it, and for rows of tokens with one local route (whose Y row goes
+    straight to the output) the token's output against w times the oracle's
+    row."""
+    ridx = torch.from_numpy(rows).to(dev())
+    for name, t in (("HU", b.HU), ("A", b.A)):
+        assert_rows(f"{label} {name}", f64(t[ridx]), ref[name], TOL, rows)
+    single, g, wt = single_route_terms(k.h["routes"], k.h["w"], C["L"], 0, s.phi, rows)
+    if (~single).any():
+        sel = rows[~single]
+        assert_rows(f"{label} Y", f64(b.Y[torch.from_numpy(sel).to(dev())]), ref["Y"][~single], TOL, sel)
+    if single.any():
+        got = f64(b.out.view(-1, C["H"])[torch.from_numpy(g[single]).to(dev())])
+        assert_rows(f"{label} out of one-route rows", got, wt[single, None] * ref["Y"][single], TOL, rows[single])
+
+
 def test_kimi_schedule_bit_exact(kimi_fwd):
     k, b = kimi_fwd
     s = oracle.schedule(k.h["routes"], C["L"], 0, 256)
@@ -93,9 +110,7 @@ def test_kimi_forward_sampled(kimi_fwd):
         sample.append(rng.choice(real, 48, replace=False))
     rows = np.sort(np.concatenate(sample))
     ref = oracle.expert_ffn_rows(s.seg_off, Xd, W13, W2, rows=rows)
-    ridx = torch.from_numpy(rows).to(dev())
-    for name, t in (("HU", b.HU), ("A", b.A), ("Y", b.Y)):
-        assert_rows(f"[kimi] {name}", f64(t[ridx]), ref[name], TOL, rows)
+    check_routed_rows("[kimi]", k, b, s, rows, ref)
     # combined tokens
     toks = np.sort(rng.choice(C["P"] * C["Np"], 256, replace=False))
     out_ref = oracle.layer_fwd_tokens(k.h["routes"], k.h["w"], X, W13, W2, L=C["L"], tokens=toks)
@@ -106,10 +121,12 @@ def test_kimi_forward_sampled(kimi_fwd):
 def test_kimi_forward_repeatable_and_persistent_agrees(kimi_fwd):
     k, b = kimi_fwd
     npad = int(b.seg_off[-1])
-    ref = (int_checksum(b.out), int_checksum(b.Y[:npad]))
+    s = oracle.schedule(k.h["routes"], C["L"], 0, 256)
+    yw = on_dev_mask(fused_y_rows(k.h["routes"], C["L"], 0, s.phi))  # the Y rows the fused forward writes
+    ref = (int_checksum(b.out), int_checksum(b.Y[:npad][yw]))
     for flags, save_xd in ((0, True), (ops.MOE_PERSISTENT, True), (0, False)):
         b2 = k.fwd(flags=flags, save_xd=save_xd)
-        assert (int_checksum(b2.out), int_checksum(b2.Y[:npad])) == ref, (flags, save_xd)
+        assert (int_checksum(b2.out), int_checksum(b2.Y[:npad][yw])) == ref, (flags, save_xd)
         assert torch.equal(b.out, b2.out)
         del b2
 
@@ -151,9 +168,7 @@ def test_kimi_adversarial_forward_backward():
         sample.append(rng.choice(real, min(48, real.size), replace=False))
     rows = np.sort(np.concatenate(sample))
     ref = oracle.expert_ffn_rows(s.seg_off, Xd, W13, W2, rows=rows)
-    ridx = torch.from_numpy(rows).to(dev())
-    for name, t in (("HU", b.HU), ("A", b.A), ("Y", b.Y)):
-        assert_rows(f"[kimi adv] {name}", f64(t[ridx]), ref[name], TOL, rows)
+    check_routed_rows("[kimi adv]", k, b, s, rows, ref)
     del Xd
     toks = np.sort(rng.choice(c["P"] * c["Np"], 128, replace=False))
     out_ref = oracle.layer_fwd_tokens(k.h["routes"], k.h["w"], X, W13, W2, L=L, tokens=toks)

@@ -13,7 +13,8 @@ import torch
 
 import oracle
 from routing_schedule_expert_amd import inputs, ops
-from tests.helpers import assert_elems, assert_rows, bits, digest, dev, f64, rel_l2, up, up_bf16
+from tests.helpers import (assert_elems, assert_rows, bits, digest, dev, f64, fused_y_rows, on_dev_mask, rel_l2, up,
+                           up_bf16)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -34,10 +35,12 @@ class Layer:
         self.W2 = up_bf16(self.h["W2"])
         self.dOut = up_bf16(self.h["dOut"]) if grad else None
 
-    def fwd(self, flags=0, chunk_rows=0, save_hu=True, save_xd=True, ws_fill=None):
+    def fwd(self, flags=0, chunk_rows=0, save_hu=True, save_xd=True, ws_fill=None, y_fill=None):
         b = ops.alloc_fwd(self.d, dev(), save_hu=save_hu, save_xd=save_xd)
         if ws_fill is not None:  # what an earlier call could have left there
             b.ws.view(torch.int32).fill_(ws_fill)
+        if y_fill is not None:
+            b.Y.view(torch.int16).fill_(y_fill)
         ops.layer_fwd(self.d, self.routes, self.w, self.X, self.W13, self.W2, b, flags=flags, chunk_rows=chunk_rows)
         torch.cuda.synchronize()
         return b
@@ -64,6 +67,15 @@ def ws_word(lay: Layer, b: ops.FwdBuffers, field: int) -> int:
     return ops.read_ws_words(b.ws, ops.workspace_field(lay.d, ops.MOE_OP_LAYER_FWD, field))[0]
 
 
+def y_rows(lay, s, flags=0, chunk_rows=0):
+    """Rows of Y the forward writes: every row, except on the fused path
+    (separate launches, no chunks), where the rows of single-route tokens go
+    straight to out."""
+    if flags & ops.MOE_PERSISTENT or chunk_rows > 0:
+        return np.ones(s.npad, bool)
+    return fused_y_rows(lay.h["routes"], lay.L, lay.base, s.phi)
+
+
 def check_fwd_full(lay: Layer, b: ops.FwdBuffers, flags=0, chunk_rows=0):
     h = lay.h
     s = lay.oracle_schedule()
@@ -81,12 +93,14 @@ def check_fwd_full(lay: Layer, b: ops.FwdBuffers, flags=0, chunk_rows=0):
         Xd = oracle.dispatch(h["X"], s.phi)
     r = oracle.expert_ffn_rows(s.seg_off, Xd, h["W13"], h["W2"])
     real = s.phi[:, 0] >= 0
-    ids = np.nonzero(real)[0]
+    written = y_rows(lay, s, flags, chunk_rows)
     for name, t in (("HU", b.HU), ("A", b.A), ("Y", b.Y)):
         if t is not None:
-            assert_rows(name, f64(t[: s.npad])[real], r[name][real], TOL, ids)
+            sel = real & written if name == "Y" else real
+            if sel.any():  # selected on the device: unwritten rows of Y may hold any bits
+                assert_rows(name, f64(t[: s.npad][on_dev_mask(sel)]), r[name][sel], TOL, np.nonzero(sel)[0])
             # padding rows are exactly zero in every row output
-            assert not f64(t[: s.npad])[~real].any(), f"{name}: a padding row is not zero"
+            assert not f64(t[: s.npad][on_dev_mask(~real)]).any(), f"{name}: a padding row is not zero"
     out = oracle.layer_fwd_tokens(h["routes"], h["w"], h["X"], h["W13"], h["W2"], L=lay.L, base=lay.base)
     got = f64(b.out).reshape(out.shape)
     # every token, including those with no local slot, which must be exactly zero
@@ -142,6 +156,7 @@ def test_forward_paths_agree_bitwise():
     n = local_route_counts(lay)
     assert (n == 0).any() and (n == 1).any() and (n >= 2).any()
     ref = lay.fwd()
+    yw = on_dev_mask(y_rows(lay, lay.oracle_schedule()))
     outs = [ref]
     for flags, chunk in ((ops.MOE_PERSISTENT, 0), (0, 256), (ops.MOE_PERSISTENT, 512), (0, 1024)):
         print(f"[layer] forward flags={flags} chunk_rows={chunk}", flush=True)
@@ -150,7 +165,8 @@ def test_forward_paths_agree_bitwise():
     for (flags, chunk), b in zip(((ops.MOE_PERSISTENT, 0), (0, 256), (ops.MOE_PERSISTENT, 512), (0, 1024)), outs[1:]):
         assert ws_word(lay, b, ops.MOE_WS_BARRIER_STATUS) == 0, (flags, chunk)
         assert digest(b.out) == digest(ref.out)
-        assert digest(b.Y[:npad], b.A[:npad], b.HU[:npad]) == digest(ref.Y[:npad], ref.A[:npad], ref.HU[:npad])
+        assert digest(b.Y[:npad][yw], b.A[:npad], b.HU[:npad]) == digest(ref.Y[:npad][yw], ref.A[:npad],
+                                                                          ref.HU[:npad])
         assert digest(b.phi[:npad], b.route_row, b.seg_off) == digest(ref.phi[:npad], ref.route_row, ref.seg_off)
 
 
@@ -158,13 +174,19 @@ def test_single_route_tokens():
     """Every token with exactly one local route (top-1 routing): the
     multi-launch forward writes every routed token's output from the down
     GEMM's epilogue (one partly padded M tile per expert, two wide column
-    tiles and a narrow one; tokens routed elsewhere stay 0 from the combine) and
+    tiles and a narrow one; tokens routed elsewhere stay 0 from the combine),
+    leaves every real row of Y as it was and writes its padding rows, and
     must match the oracle and, bitwise, the persistent path."""
     lay = Layer(15, 3, 211, 6, 1, 4, 1024, 256, routing="uniform")
     n = local_route_counts(lay)
     assert (n == 1).any() and (n == 0).any() and n.max() == 1
-    b = lay.fwd()
+    sentinel = 0x7FC1  # a bf16 NaN no product yields
+    b = lay.fwd(y_fill=sentinel)
     check_fwd_full(lay, b)
+    s = lay.oracle_schedule()
+    real = s.phi[:, 0] >= 0
+    y = bits(b.Y[: s.npad])
+    assert (y[real] == sentinel).all() and (y[~real] == 0).all()
     p = lay.fwd(flags=ops.MOE_PERSISTENT)
     assert digest(p.out) == digest(b.out)
 
@@ -205,6 +227,7 @@ def test_forward_fused_dispatch_bitwise():
     lay = Layer(9, 4, 900, 16, 4, 8, 512, 384, routing="zipf", s=1.2)
     ref = lay.fwd()
     npad = int(ref.seg_off[-1])
+    yw = on_dev_mask(y_rows(lay, lay.oracle_schedule()))
     for flags, chunk in ((0, 0), (ops.MOE_PERSISTENT, 0), (0, 512), (ops.MOE_PERSISTENT, 256)):
         print(f"[layer] fused dispatch flags={flags} chunk_rows={chunk}", flush=True)
         b = lay.fwd(flags=flags, chunk_rows=chunk, save_xd=False)
@@ -212,7 +235,8 @@ def test_forward_fused_dispatch_bitwise():
         if flags or chunk:
             assert ws_word(lay, b, ops.MOE_WS_BARRIER_STATUS) == 0, (flags, chunk)
         assert digest(b.out) == digest(ref.out)
-        assert digest(b.Y[:npad], b.A[:npad], b.HU[:npad]) == digest(ref.Y[:npad], ref.A[:npad], ref.HU[:npad])
+        assert digest(b.Y[:npad][yw], b.A[:npad], b.HU[:npad]) == digest(ref.Y[:npad][yw], ref.A[:npad],
+                                                                          ref.HU[:npad])
         assert digest(b.phi[:npad], b.route_row, b.seg_off) == digest(ref.phi[:npad], ref.route_row, ref.seg_off)
 
 
@@ -225,8 +249,9 @@ def test_fused_dispatch_vs_oracle():
     r = oracle.expert_ffn_rows(s.seg_off, oracle.dispatch(h["X"], s.phi), h["W13"], h["W2"])
     real = s.phi[:, 0] >= 0
     assert_rows("A", f64(b.A[: s.npad])[real], r["A"][real], TOL, np.nonzero(real)[0])
-    assert_rows("Y", f64(b.Y[: s.npad])[real], r["Y"][real], TOL, np.nonzero(real)[0])
-    assert not f64(b.Y[: s.npad])[~real].any()  # padding rows read the zero row
+    sel = real & y_rows(lay, s)
+    assert_rows("Y", f64(b.Y[: s.npad][on_dev_mask(sel)]), r["Y"][sel], TOL, np.nonzero(sel)[0])
+    assert not f64(b.Y[: s.npad][on_dev_mask(~real)]).any()  # padding rows read the zero row
     out = oracle.layer_fwd_tokens(h["routes"], h["w"], h["X"], h["W13"], h["W2"], L=lay.L)
     assert_rows("out", f64(b.out).reshape(out.shape), out, TOL)
 
@@ -241,9 +266,10 @@ def test_fused_dispatch_widest_rows():
     b = lay.fwd(save_xd=False)
     s = lay.oracle_schedule()
     assert torch.equal(a.out, b.out)
-    assert torch.equal(a.Y[: s.npad], b.Y[: s.npad])
+    yw = on_dev_mask(y_rows(lay, s))
+    assert torch.equal(a.Y[: s.npad][yw], b.Y[: s.npad][yw])
     real = s.phi[:, 0] >= 0
-    assert (~real).any() and not f64(b.Y[: s.npad])[~real].any()
+    assert (~real).any() and not f64(b.Y[: s.npad][on_dev_mask(~real)]).any()
     h = lay.h
     out = oracle.layer_fwd_tokens(h["routes"], h["w"], h["X"], h["W13"], h["W2"], L=lay.L)
     assert_rows("out (H=32768)", f64(b.out).reshape(out.shape), out, TOL)
@@ -294,11 +320,12 @@ def test_small_backward_skewed():
 def test_repeat_runs_bitwise_identical():
     lay = Layer(8, 4, 800, 16, 4, 8, 512, 256, routing="zipf", s=1.2)
     hashes = set()
+    yw = on_dev_mask(y_rows(lay, lay.oracle_schedule()))
     for _ in range(3):
         b = lay.fwd()
         g = lay.bwd(b)
         npad = int(b.seg_off[-1])
-        hashes.add(digest(b.out, b.Y[:npad], g["dX"], g["dW13"], g["dW2"], g["dw"]))
+        hashes.add(digest(b.out, b.Y[:npad][yw], g["dX"], g["dW13"], g["dW2"], g["dw"]))
     assert len(hashes) == 1
 
 
@@ -317,8 +344,11 @@ def test_mid_forward_sampled():
     real = np.nonzero(s.phi[:, 0] >= 0)[0]
     rows = np.sort(rng.choice(real, 192, replace=False))
     r = oracle.expert_ffn_rows(s.seg_off, Xd, lay.h["W13"], lay.h["W2"], rows=rows)
+    yw = y_rows(lay, s)[rows]
+    assert yw.any() and (~yw).any()
     for name, t in (("HU", b.HU), ("A", b.A), ("Y", b.Y)):
-        assert_rows(name, f64(t[rows]), r[name], TOL, rows)
+        sel = yw if name == "Y" else np.ones(rows.size, bool)
+        assert_rows(name, f64(t[rows[sel]]), r[name][sel], TOL, rows[sel])
     toks = np.sort(rng.choice(lay.P * lay.Np, 96, replace=False))
     out = oracle.layer_fwd_tokens(lay.h["routes"], lay.h["w"], lay.h["X"], lay.h["W13"], lay.h["W2"], L=lay.L,
                                   tokens=toks)

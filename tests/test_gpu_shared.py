@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from routing_schedule_expert_amd import inputs, ops
-from tests.helpers import bits, dev, f64, rel_l2, up, up_bf16
+from tests.helpers import bits, dev, f64, fused_y_rows, on_dev_mask, rel_l2, up, up_bf16
 from tests.test_gpu_layer import Layer
 
 pytestmark = pytest.mark.gpu
@@ -34,6 +34,17 @@ def run_shared(lay: Layer, W13s, W2s, Is):
     return b, sh
 
 
+def assert_routed_rows_equal(b, std, routes, L, base):
+    """Routed HU, A and Y of the shared-expert forward against moe_layer_fwd's
+    (separate launches), bitwise; Y on the rows moe_layer_fwd writes (the rows
+    of tokens with one local route go straight to its output there)."""
+    npad = int(std.seg_off[-1])
+    yw = on_dev_mask(fused_y_rows(routes, L, base, std.phi[:npad].cpu().numpy()))
+    for name in ("HU", "A"):
+        assert torch.equal(getattr(b, name)[:npad], getattr(std, name)[:npad]), name
+    assert torch.equal(b.Y[:npad][yw], std.Y[:npad][yw]), "Y"
+
+
 @pytest.mark.parametrize("P,Np,Is", [(2, 200, 256), (3, 256, 128)])
 def test_shared_forward(P, Np, Is):
     print(f"[shared] P={P} Np={Np} Is={Is}", flush=True)
@@ -43,8 +54,7 @@ def test_shared_forward(P, Np, Is):
     b, sh = run_shared(lay, W13s, W2s, Is)
     std = lay.fwd(save_xd=False)
     npad = int(std.seg_off[-1])
-    for name in ("HU", "A", "Y"):
-        assert torch.equal(getattr(b, name)[:npad], getattr(std, name)[:npad]), name
+    assert_routed_rows_equal(b, std, lay.h["routes"], lay.L, lay.base)
     np.testing.assert_array_equal(b.phi[:npad].cpu().numpy(), std.phi[:npad].cpu().numpy())  # rows past Npad unwritten
     h = lay.h
     ntok = P * Np
@@ -75,8 +85,7 @@ def test_shared_nonzero_base_and_dropped_ids():
     b, sh = run_shared(lay, up_bf16(w13s), up_bf16(w2s), 128)
     std = lay.fwd(save_xd=False)
     npad = int(std.seg_off[-1])
-    for name in ("HU", "A", "Y"):
-        assert torch.equal(getattr(b, name)[:npad], getattr(std, name)[:npad]), name
+    assert_routed_rows_equal(b, std, lay.h["routes"], lay.L, lay.base)
     h = lay.h
     out = oracle.layer_fwd_tokens_shared(h["routes"], h["w"], h["X"], h["W13"], h["W2"], w13s, w2s, L=lay.L,
                                          base=lay.base)
@@ -116,8 +125,7 @@ def test_shared_kimi_sampled():
     ops.layer_fwd(d, routes, w, h["X"], h["W13"], h["W2"], std)
     torch.cuda.synchronize()
     npad = int(std.seg_off[-1])
-    for name in ("HU", "A", "Y"):
-        assert torch.equal(getattr(b, name)[:npad], getattr(std, name)[:npad]), name
+    assert_routed_rows_equal(b, std, h["routes"], c["L"], 0)
     rng = np.random.default_rng(4)
     toks = np.sort(rng.choice(c["P"] * c["Np"], 128, replace=False))
     X, W13, W2 = bits(h["X"]), bits(h["W13"]), bits(h["W2"])
