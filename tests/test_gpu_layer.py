@@ -191,6 +191,20 @@ def test_single_route_tokens():
     assert digest(p.out) == digest(b.out)
 
 
+def test_many_slots_per_token():
+    """K = 70 slots per token (more than one wave's lanes: the combine counts a
+    token's local routes in two ballots) with 2 local experts of 80, so
+    tokens have 0, 1 or 2 local routes: the multi-launch forward against the
+    oracle and, bitwise, the persistent path."""
+    lay = Layer(17, 2, 96, 80, 70, 2, 256, 128, routing="topk")
+    n = local_route_counts(lay)
+    assert (n == 0).any() and (n == 1).any() and (n == 2).any()
+    b = lay.fwd()
+    check_fwd_full(lay, b)
+    p = lay.fwd(flags=ops.MOE_PERSISTENT)
+    assert digest(p.out) == digest(b.out)
+
+
 @pytest.mark.parametrize("fill", [0, 2, -5])
 def test_stale_workspace(fill):
     """The forward must not depend on what the workspace held before the call:
