@@ -485,8 +485,11 @@ int64_t moe_ring_workspace_bytes(const moe_desc *d, int32_t mb_tokens, int32_t w
  * m = M-1, ..., 0: macrobatch m uses slot (M-1-m) % ring_slots; each step is
  * one launch holding the gate/up tiles of m (the dispatch fused into their
  * operand loads) together with the combine of m+1, then the down GEMM of m;
- * a last launch combines macrobatch 0.  On return slot (M-1-m) % ring_slots
- * holds macrobatch m for every m < min(ring_slots, M).
+ * a last launch combines macrobatch 0.  As in moe_layer_fwd, the down GEMM
+ * writes the outputs of the tokens with one local route itself (from a
+ * per-row table of the macrobatch, rebuilt before each down launch) and the
+ * combines skip them.  On return slot (M-1-m) % ring_slots holds macrobatch m
+ * for every m < min(ring_slots, M).
  */
 int moe_layer_fwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots, const int32_t *routes,
                        const float *w, const uint16_t *X, const uint16_t *W13, const uint16_t *W2, int32_t *counts,

@@ -317,6 +317,7 @@ struct WindowCombine {
     uint16_t *out;
     int K, H, tpp;
     int64_t ntok, tstride;
+    int skip_single;  // leave the tokens with one local route (the down epilogue wrote them)
 };
 
 constexpr int kCombineItem = 64;  // tokens per combine work item (8 per wave)
@@ -341,7 +342,7 @@ __device__ __forceinline__ void ring_gateup_combine_body(const FfnArgs &a, const
         } else {
             const int64_t g0 = (lid - ngu) * kCombineItem;
             combine_body<kRowUnrollWide>(c.Y, c.route_row, c.w, c.out, c.K, c.H, g0, min(g0 + kCombineItem, c.ntok),
-                         threadIdx.x / kWave, waves, c.tpp, c.tstride);
+                         threadIdx.x / kWave, waves, c.tpp, c.tstride, nullptr, c.skip_single != 0);
         }
     }
 }

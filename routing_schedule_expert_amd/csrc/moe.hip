@@ -67,11 +67,14 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t *Y, const int32_
 
 // tab (see single_route_body) for every token of one table, (-1, 0) on its
 // padding rows.
+// With tpp > 0 the tokens are a window of tpp tokens per partition,
+// partitions tstride apart (window_token).
 __global__ __launch_bounds__(256) void k_single_route(const int32_t *route_row, const float *w, const moe_src *phi,
-                                                      const int32_t *npad_ptr, int2 *tab, int K, int64_t ntok) {
+                                                      const int32_t *npad_ptr, int2 *tab, int K, int64_t ntok,
+                                                      int tpp, int64_t tstride) {
     const int64_t npad = *npad_ptr, stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < ntok || i < npad; i += stride) {
-        if (i < ntok) single_route_body(route_row, w, tab, K, i);
+        if (i < ntok) single_route_body(route_row, w, tab, K, window_token(i, tpp, tstride));
         if (i < npad) single_route_pad(phi, tab, i);
     }
 }
@@ -488,13 +491,15 @@ int launch_combine(const moe_desc *d, const uint16_t *Y, const int32_t *route_ro
 // The per-row table of the tokens with one local route (in the workspace
 // after the schedule's part) and the epilogue arguments that use it.
 int launch_single_route(const moe_desc *d, const int32_t *route_row, const moe_src *phi, const int32_t *seg_off,
-                        const float *w, uint16_t *out, char *ws, hipStream_t s, RowCombine &rcomb) {
+                        const float *w, uint16_t *out, char *ws, hipStream_t s, RowCombine &rcomb,
+                        int64_t tstride = 0) {
     int2 *tab = reinterpret_cast<int2 *>(ws);
     const int64_t ntok = (int64_t)d->P * d->Np, n = std::max<int64_t>(ntok, cap_rows(d));
+    const int tpp = tstride > d->Np ? d->Np : 0;
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 4ll * device_cus()));
     TraceScope tr("single_route", s);
     hipLaunchKernelGGL(k_single_route, dim3(grid), dim3(256), 0, s, route_row, w, phi, seg_off + d->L, tab, d->K,
-                       ntok);
+                       ntok, tpp, tpp ? tstride : (int64_t)0);
     rcomb = RowCombine{out, tab};
     return launch_status();
 }
@@ -1351,7 +1356,7 @@ int64_t moe_ring_workspace_bytes(const moe_desc *d, int32_t mb_tokens, int32_t w
     if (ring_check(d, mb_tokens, 1, dm, M) != MOE_OK) return -1;
     moe_desc d1 = dm;
     d1.num_batches = 1;
-    if (op == MOE_OP_LAYER_FWD) return kBarrierBytes + sched_ws_bytes(&dm);
+    if (op == MOE_OP_LAYER_FWD) return kBarrierBytes + sched_ws_bytes(&dm) + single_route_bytes(&d1);
     if (op != MOE_OP_LAYER_BWD || wgrad_group < 1 || wgrad_group > kMaxWgradGroup) return -1;
     return ring_bwd_bytes(&d1, std::min(wgrad_group, M));
 }
@@ -1378,6 +1383,7 @@ int moe_layer_fwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots,
     moe_desc d1 = dm;
     d1.num_batches = 1;
     const int64_t capm = cap_rows(&d1);
+    char *tab = wsb + kBarrierBytes + sched_ws_bytes(&dm);  // the single-route table of one macrobatch
     const int grid = gemm_grid();
     // reversed ring: the last macrobatch first, so the first ones stay resident
     for (int i = 0; i < M; ++i) {
@@ -1399,18 +1405,24 @@ int moe_layer_fwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots,
         wc.tpp = (int)B;
         wc.ntok = (int64_t)d->P * B;
         wc.tstride = Np;
+        wc.skip_single = 1;
         {
             TraceScope tr("ring_gateup_combine", s);
             hipLaunchKernelGGL(k_ring_gateup_combine, dim3(grid), dim3(kFwdThreads), 0, s, fa, wc);
         }
         if (launch_status() != MOE_OK) return MOE_EHIP;
+        // the down tiles write the outputs of this macrobatch's single-route tokens
+        const int64_t t0 = (int64_t)m * B;
+        rc = launch_single_route(&d1, route_row + t0 * K, phi + (int64_t)m * capm, seg_off + (int64_t)m * (L + 1),
+                                 w + t0 * K, out + t0 * H, tab, s, fa.rc, Np);
+        if (rc != MOE_OK) return rc;
         {
             TraceScope tr("ring_down", s);
             hipLaunchKernelGGL(k_ffn_down_w, dim3(grid), dim3(kWideThreads), 0, s, fa);
         }
         if (launch_status() != MOE_OK) return MOE_EHIP;
     }
-    return launch_combine(&d1, Y, route_row, w, out, s, "ring_combine", Np);  // macrobatch 0
+    return launch_combine(&d1, Y, route_row, w, out, s, "ring_combine", Np, nullptr, true);  // macrobatch 0
 }
 
 int moe_layer_bwd_ring(const moe_desc *d, int32_t mb_tokens, int32_t ring_slots, int32_t wgrad_group,
