@@ -153,6 +153,13 @@ enum {
     MOE_WS_MX_XDT_S = 12,  /*                                                  */
     MOE_WS_MX_DHUT_Q = 13, /* C = 2I: dHU column codes                         */
     MOE_WS_MX_DHUT_S = 14, /*                                                  */
+    /* inspection of moe_layer_fwd and moe_layer_fwd_mx (op MOE_OP_LAYER_FWD):
+     * int32 pairs [cap][2], rows below seg_off[L] written by a call that
+     * combines single-route tokens in its down GEMM (separate launches, no
+     * chunks): (token p * Np + t, bits of its fp32 weight) for a row whose
+     * token has exactly one local route, (-1, 0) for every other row and for
+     * padding rows. */
+    MOE_WS_SINGLE_ROUTE = 15,
 };
 int64_t moe_workspace_field(const moe_desc *d, int op, int field);
 

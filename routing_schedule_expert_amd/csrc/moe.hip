@@ -666,6 +666,12 @@ int64_t moe_workspace_field(const moe_desc *d, int op, int field) {
         if (op == MOE_OP_LAYER_FWD || op == MOE_OP_EXPERT_FFN) return 8;
         return -1;
     }
+    if (field == MOE_WS_SINGLE_ROUTE) {
+        if (op != MOE_OP_LAYER_FWD) return -1;
+        moe_desc one = *d;
+        one.num_batches = 1;
+        return kBarrierBytes + sched_ws_bytes(&one);
+    }
     if (op == MOE_OP_LAYER_BWD_MX) {
         // the bf16 backward's dHU follows dO_d, dXd and dO_d w
         if (field == MOE_WS_MX_DHU) return mx_dhu_offset(d);

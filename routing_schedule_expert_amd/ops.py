@@ -26,6 +26,7 @@ MOE_PERSISTENT = 1
 MOE_WS_INVALID_IDS, MOE_WS_BARRIER_STATUS = 0, 1
 (MOE_WS_MX_DHU, MOE_WS_MX_DO_Q, MOE_WS_MX_DO_S, MOE_WS_MX_DHU_Q, MOE_WS_MX_DHU_S, MOE_WS_MX_DOWT_Q, MOE_WS_MX_DOWT_S,
  MOE_WS_MX_AT_Q, MOE_WS_MX_AT_S, MOE_WS_MX_XDT_Q, MOE_WS_MX_XDT_S, MOE_WS_MX_DHUT_Q, MOE_WS_MX_DHUT_S) = range(2, 15)
+MOE_WS_SINGLE_ROUTE = 15
 
 EXPORTED = (
     "moe_strerror", "moe_capacity_rows", "moe_workspace_bytes", "moe_workspace_field", "moe_schedule",

@@ -145,3 +145,16 @@ def single_route_terms(routes: np.ndarray, w: np.ndarray, L: int, base: int, phi
     j = np.argmax(local[gg], axis=1)
     wt = np.asarray(w).reshape(-1, K)[gg, j].astype(np.float64)
     return single, g, wt
+
+
+def expected_single_route_table(routes: np.ndarray, w: np.ndarray, L: int, base: int, phi: np.ndarray) -> np.ndarray:
+    """The forward's per-row table of single-route tokens, as int32 pairs
+    [npad][2]: (token, bits of its fp32 weight) for a row whose token has
+    exactly one local route, (-1, 0) for every other row and padding."""
+    rows = np.arange(np.asarray(phi).shape[0])
+    single, g, wt = single_route_terms(routes, w, L, base, phi, rows)
+    tab = np.zeros((rows.size, 2), np.int32)
+    tab[:, 0] = -1
+    tab[single, 0] = g[single]
+    tab[single, 1] = wt[single].astype(np.float32).view(np.int32)
+    return tab

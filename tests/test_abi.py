@@ -254,6 +254,12 @@ def test_workspace_fields():
     for op in (ops.MOE_OP_SCHEDULE, ops.MOE_OP_LAYER_FWD):
         off = f(d, op, ops.MOE_WS_INVALID_IDS)
         assert 0 <= off and off + 4 <= ops.workspace_bytes(d, op)
+    # the forward's single-route table: 8 bytes per row of capacity, at the end
+    off = f(d, ops.MOE_OP_LAYER_FWD, ops.MOE_WS_SINGLE_ROUTE)
+    assert off > 256 and off % 256 == 0
+    assert off + 8 * ops.capacity_rows(d) <= ops.workspace_bytes(d, ops.MOE_OP_LAYER_FWD) < off + 8 * ops.capacity_rows(d) + 256
+    for op in (ops.MOE_OP_SCHEDULE, ops.MOE_OP_LAYER_FWD_SHARED, ops.MOE_OP_LAYER_BWD):
+        assert f(d, op, ops.MOE_WS_SINGLE_ROUTE) == -1
     bad = kimi()
     bad.P = 0
     assert f(bad, ops.MOE_OP_SCHEDULE, ops.MOE_WS_INVALID_IDS) == -1

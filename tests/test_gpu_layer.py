@@ -13,8 +13,8 @@ import torch
 
 import oracle
 from routing_schedule_expert_amd import inputs, ops
-from tests.helpers import (assert_elems, assert_rows, bits, digest, dev, f64, fused_y_rows, on_dev_mask, rel_l2, up,
-                           up_bf16)
+from tests.helpers import (assert_elems, assert_rows, bits, digest, dev, expected_single_route_table, f64, fused_y_rows,
+                           on_dev_mask, rel_l2, up, up_bf16)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -168,6 +168,26 @@ def test_forward_paths_agree_bitwise():
         assert digest(b.Y[:npad][yw], b.A[:npad], b.HU[:npad]) == digest(ref.Y[:npad][yw], ref.A[:npad],
                                                                           ref.HU[:npad])
         assert digest(b.phi[:npad], b.route_row, b.seg_off) == digest(ref.phi[:npad], ref.route_row, ref.seg_off)
+
+
+def single_route_table(lay, b, npad):
+    off = ops.workspace_field(lay.d, ops.MOE_OP_LAYER_FWD, ops.MOE_WS_SINGLE_ROUTE)
+    assert off >= 0
+    return np.array(ops.read_ws_words(b.ws, off, 2 * npad), np.int32).reshape(npad, 2)
+
+
+@pytest.mark.parametrize("fill", [None, 0])
+def test_single_route_table_bit_exact(fill):
+    """The per-row table the down epilogue reads, bit for bit against the one
+    computed on the host from the oracle's schedule: (token, weight bits) for
+    rows of tokens with one local route, (-1, 0) for the others and padding;
+    also over a workspace filled beforehand with words naming token 0."""
+    lay = Layer(4, 4, 900, 16, 4, 8, 512, 384, routing="uniform")
+    b = lay.fwd(ws_fill=fill)
+    s = lay.oracle_schedule()
+    ref = expected_single_route_table(lay.h["routes"], lay.h["w"], lay.L, lay.base, s.phi)
+    assert (ref[:, 0] >= 0).any() and (ref[:, 0] < 0).any()
+    np.testing.assert_array_equal(single_route_table(lay, b, s.npad), ref)
 
 
 def test_single_route_tokens():

@@ -19,7 +19,7 @@ import torch
 
 import oracle
 from routing_schedule_expert_amd import inputs, ops
-from tests.helpers import dev, f64, fused_y_rows, on_dev_mask, single_route_terms, up, up_bf16
+from tests.helpers import dev, expected_single_route_table, f64, fused_y_rows, on_dev_mask, single_route_terms, up, up_bf16
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -289,6 +289,19 @@ def test_mx_repeat_bitwise():
     assert torch.equal(a.out, b.out)
     assert torch.equal(a.Y[:npad][yw], b.Y[:npad][yw]) and torch.equal(a.Aq[:npad], b.Aq[:npad])
     assert torch.equal(a.As[:npad], b.As[:npad])
+
+
+def test_mx_single_route_table_bit_exact():
+    """The MX forward's per-row table of single-route tokens (the one its down
+    epilogue reads) bit for bit against the host's from the oracle schedule."""
+    lay = MxLayer(10, 4, 500, 16, 4, 8, 512, 256, routing="zipf")
+    b = lay.fwd(ws_fill=0)
+    s = oracle.schedule(lay.h["routes"], lay.L, lay.base, 256)
+    ref = expected_single_route_table(lay.h["routes"], lay.h["w"], lay.L, lay.base, s.phi)
+    assert (ref[:, 0] >= 0).any() and (ref[:, 0] < 0).any()
+    off = ops.workspace_field(lay.d, ops.MOE_OP_LAYER_FWD, ops.MOE_WS_SINGLE_ROUTE)
+    got = np.array(ops.read_ws_words(b.ws, off, 2 * s.npad), np.int32).reshape(s.npad, 2)
+    np.testing.assert_array_equal(got, ref)
 
 
 def test_mx_stale_workspace():
