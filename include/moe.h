@@ -130,7 +130,9 @@ int64_t moe_workspace_bytes(const moe_desc *d, int op);
  * moe_workspace_field returns the byte offset of `field` in the workspace of
  * operation `op` (moe_workspace_bytes), or -1 if d is invalid or op has no
  * such field.  moe_layer_fwd_mx uses MOE_OP_LAYER_FWD's offsets, and so does
- * moe_layer_fwd_ring (its workspace is laid out the same way).
+ * moe_layer_fwd_ring for the two status words (its single-route table sits
+ * after its M tables' schedule workspace, so MOE_WS_SINGLE_ROUTE does not
+ * apply to it).
  */
 enum {
     MOE_WS_INVALID_IDS = 0,
